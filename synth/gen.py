@@ -1,0 +1,184 @@
+"""Seeded generators.  Every function is a pure function of (config, indices)."""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import ndtri
+
+from .configs import Config
+
+# tensor ids that enter the Philox key
+_T_CTX_K, _T_CTX_V, _T_QLAST, _T_TQ, _T_TK, _T_TV, _T_WSID, _T_ITEMS, _T_SHAPES = range(1, 10)
+
+
+def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest even."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit pattern -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _make_table() -> np.ndarray:
+    u = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+    return _f32_to_bf16_bits(ndtri(u).astype(np.float32))
+
+
+#: bf16 bit patterns of the 65536 quantiles of N(0,1): a discretised normal.
+BF16_NORMAL_TABLE = _make_table()
+
+
+def _key(cfg: Config, tensor: int, a: int = 0, b: int = 0) -> int:
+    return ((cfg.seed & 0xFFFF) << 112) | (cfg.cfg_id << 96) | (tensor << 64) | ((a & 0xFFFFFFFF) << 32) | (b & 0xFFFFFFFF)
+
+
+def _philox(cfg: Config, tensor: int, a: int = 0, b: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=_key(cfg, tensor, a, b)))
+
+
+def _bf16_normal(gen: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    idx = np.frombuffer(gen.bytes(2 * n), dtype=np.uint16)
+    return BF16_NORMAL_TABLE[idx].reshape(shape)
+
+
+# ---------------------------------------------------------------- tiny fp32 config
+_TINY_CACHE: dict = {}
+
+
+def _tiny_all(cfg: Config) -> dict:
+    """The tiny fp32 config: one default_rng(seed) stream, fixed tensor order."""
+    key = cfg
+    if key in _TINY_CACHE:
+        return _TINY_CACHE[key]
+    rng = np.random.default_rng(cfg.seed)
+    V, lv = cfg.codebook, cfg.n_levels
+    flat = rng.choice(V ** lv, size=cfg.n_items, replace=False)
+    out = {"items": _decompose(np.sort(flat), V, lv)}
+    n = request_shapes(cfg)[0][0]
+    L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    out["ctx_k"] = rng.standard_normal((L, n, Hkv, d)).astype(np.float32)
+    out["ctx_v"] = rng.standard_normal((L, n, Hkv, d)).astype(np.float32)
+    out["q_last"] = rng.standard_normal((L, Hq, d)).astype(np.float32)
+    T = max(lv - 1, 0)
+    out["tq"] = rng.standard_normal((L, T, V, Hq, d)).astype(np.float32)
+    out["tk"] = rng.standard_normal((L, T, V, Hkv, d)).astype(np.float32)
+    out["tv"] = rng.standard_normal((L, T, V, Hkv, d)).astype(np.float32)
+    out["w_sid"] = (rng.standard_normal((lv, Hq * d, V)) * np.sqrt(1.0 / (Hq * d))).astype(np.float32)
+    _TINY_CACHE[key] = out
+    return out
+
+
+def _decompose(flat: np.ndarray, V: int, levels: int) -> np.ndarray:
+    out = np.empty((flat.shape[0], levels), dtype=np.int32)
+    x = flat.astype(np.int64)
+    for t in range(levels - 1, -1, -1):
+        out[:, t] = x % V
+        x //= V
+    return out
+
+
+# ---------------------------------------------------------------- public API
+def request_shapes(cfg: Config):
+    """[(ctx_len, beam_width)] per request."""
+    R = cfg.n_requests
+    if isinstance(cfg.ctx_len, int) and isinstance(cfg.beam_width, int):
+        return [(cfg.ctx_len, cfg.beam_width)] * R
+    g = _philox(cfg, _T_SHAPES)
+    if isinstance(cfg.ctx_len, int):
+        ns = np.full(R, cfg.ctx_len, dtype=np.int64)
+    else:
+        lo, hi = cfg.ctx_len
+        ns = g.integers(lo, hi + 1, size=R)
+    if isinstance(cfg.beam_width, int):
+        ws = np.full(R, cfg.beam_width, dtype=np.int64)
+    else:
+        ch = np.asarray(cfg.beam_width, dtype=np.int64)
+        ws = ch[g.integers(0, len(ch), size=R)]
+    return [(int(a), int(b)) for a, b in zip(ns, ws)]
+
+
+def ctx_kv_block(cfg: Config, r: int, l: int):
+    """Context K and V of request r, layer l, caller layout [N][Hkv][d].
+
+    bf16 configs return uint16 bit patterns, fp32 configs float32 arrays."""
+    n = request_shapes(cfg)[r][0]
+    shape = (n, cfg.n_kv_heads, cfg.head_dim)
+    if cfg.dtype == "f32":
+        t = _tiny_all(cfg)
+        return t["ctx_k"][l], t["ctx_v"][l]
+    return (_bf16_normal(_philox(cfg, _T_CTX_K, r, l), shape),
+            _bf16_normal(_philox(cfg, _T_CTX_V, r, l), shape))
+
+
+def q_last(cfg: Config, r: int):
+    """Query of the last context token, [L][Hq][d] (stands in for the prefill's last query)."""
+    if cfg.dtype == "f32":
+        return _tiny_all(cfg)["q_last"]
+    return _bf16_normal(_philox(cfg, _T_QLAST, r), (cfg.n_layers, cfg.n_q_heads, cfg.head_dim))
+
+
+def token_tables(cfg: Config):
+    """(TQ [L][lv-1][V][Hq][d], TK [L][lv-1][V][Hkv][d], TV same as TK).
+
+    Row (l, t, c) is the query/key/value at layer l of the token that feeds
+    code c of level t back into the model."""
+    if cfg.dtype == "f32":
+        t = _tiny_all(cfg)
+        return t["tq"], t["tk"], t["tv"]
+    L, T, V = cfg.n_layers, max(cfg.n_levels - 1, 0), cfg.codebook
+    tq = np.empty((L, T, V, cfg.n_q_heads, cfg.head_dim), dtype=np.uint16)
+    tk = np.empty((L, T, V, cfg.n_kv_heads, cfg.head_dim), dtype=np.uint16)
+    tv = np.empty_like(tk)
+    for l in range(L):
+        tq[l] = _bf16_normal(_philox(cfg, _T_TQ, l), tq.shape[1:])
+        tk[l] = _bf16_normal(_philox(cfg, _T_TK, l), tk.shape[1:])
+        tv[l] = _bf16_normal(_philox(cfg, _T_TV, l), tv.shape[1:])
+    return tq, tk, tv
+
+
+def w_sid(cfg: Config) -> np.ndarray:
+    """Codebook projection [levels][Hq*d][V] float32, N(0, 1/(Hq*d)) (variance)."""
+    if cfg.dtype == "f32":
+        return _tiny_all(cfg)["w_sid"]
+    rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, cfg.cfg_id, _T_WSID]))
+    H = cfg.n_q_heads * cfg.head_dim
+    return (rng.standard_normal((cfg.n_levels, H, cfg.codebook)) * np.sqrt(1.0 / H)).astype(np.float32)
+
+
+def items(cfg: Config) -> np.ndarray:
+    """Valid items, [n_items][levels] int32, distinct, big-endian codes."""
+    V, lv, n = cfg.codebook, cfg.n_levels, cfg.n_items
+    if cfg.dtype == "f32":
+        return _tiny_all(cfg)["items"]
+    if cfg.item_dist == "uniform":
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, cfg.cfg_id, _T_ITEMS]))
+        flat = rng.choice(V ** lv, size=n, replace=False)
+        return _decompose(np.sort(flat), V, lv)
+    if cfg.item_dist == "zipf":
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, cfg.cfg_id, _T_ITEMS]))
+        ranks = np.arange(1, V + 1, dtype=np.float64)
+        p = ranks ** (-cfg.zipf_a)
+        p /= p.sum()
+        perms = np.stack([rng.permutation(V) for _ in range(lv)])
+        seen = np.empty(0, dtype=np.int64)
+        first = np.empty(0, dtype=np.int64)    # draw position of each distinct tuple
+        drawn = 0
+        while seen.shape[0] < n:
+            m = max(n, 1 << 16)
+            codes = np.stack([perms[t][rng.choice(V, size=m, p=p)] for t in range(lv)], axis=1)
+            flat = np.zeros(m, dtype=np.int64)
+            for t in range(lv):
+                flat = flat * V + codes[:, t]
+            allf = np.concatenate([seen, flat])
+            pos = np.concatenate([first, drawn + np.arange(m, dtype=np.int64)])
+            uniq, idx = np.unique(allf, return_index=True)
+            order = np.argsort(pos[idx], kind="stable")
+            seen, first = uniq[order], pos[idx][order]
+            drawn += m
+        keep = seen[:n]
+        return _decompose(np.sort(keep), V, lv)
+    raise ValueError(cfg.item_dist)
