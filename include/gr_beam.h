@@ -1,0 +1,231 @@
+/*
+ * gr_beam.h -- C ABI of the semantic-ID beam-search decode step on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The calls follow the serving pattern of generative recommendation with
+ * semantic IDs as described in the zhiding.cn article on NVIDIA
+ * recsys-examples, section "语义ID生成式推荐专用推理框架" (semantic-ID
+ * generative-recommendation inference framework): a long user context that
+ * every beam shares (ContextKV), a short per-beam decode history (BeamKV), the
+ * logical ancestry of each beam (BeamPath), wide and dynamic beam widths, and
+ * item-constrained generation with an item-constrained top-K; and the
+ * multi-beam return of the paper-daily summary "Advancing Generative
+ * Recommendation Inference", section "Background" (return every surviving
+ * beam, not only the best one).
+ *
+ * Model stand-in.  The pages give no model for this step beyond naming
+ * Qwen3-1.7B.  The library computes, per decode step s of request r and beam j
+ * with code prefix c_0..c_{s-1}:
+ *   - per layer l and query head hq (kv head hq / (Hq/Hkv)):
+ *       query  q = q_last[r][l][hq]                 (s = 0)
+ *              q = tok_q[l][s-1][c_{s-1}][hq]       (s >= 1)
+ *       keys   the request's context keys, then tok_k[l][t][c_t] for t < s
+ *       values likewise; o_l = softmax(q K^T / sqrt(d)) V
+ *   - hidden h = sum_l o_l, head-major (hq*d + i), float32
+ *   - logits = h @ w_sid[s]   (float32)
+ *   - log-softmax over the codes that extend a valid item prefix (GR_NORM_VALID)
+ *     or over all codes (GR_NORM_FULL), keeping only valid codes
+ *   - candidate score = beam score + log-prob; the next beam set holds the
+ *     min(W, #valid candidates) best candidates over all beams x codes, ordered
+ *     by score descending, then by flat index j*V + c ascending.
+ * The context is stored once per request; a beam's own tokens are written
+ * once into BeamKV and found again through BeamPath, never copied on reorder.
+ *
+ * Conventions
+ *   - Every call returns gr_status; on failure gr_last_error() gives a
+ *     thread-local message.  No exception or abort crosses the ABI.
+ *   - After a HIP runtime error the engine is poisoned: later calls on it
+ *     return GR_E_DEVICE.
+ *   - "device" pointers are HIP device memory (e.g. torch CUDA tensors on
+ *     ROCm); "host" pointers are ordinary process memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All device work
+ *     of a call is enqueued on it; an engine must be used from one host thread
+ *     and one stream at a time.
+ *   - The caller owns every buffer it passes, including the workspace; the
+ *     engine sub-allocates the workspace and never calls hipMalloc/hipFree.
+ *     The only allocation the engine makes itself is a small ring of pinned
+ *     host buffers for per-step work descriptors (at bind time).
+ */
+#ifndef GR_BEAM_H
+#define GR_BEAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GR_OK = 0,
+  GR_E_INVALID_ARG = 1,   /* a bad argument; nothing was changed */
+  GR_E_OUT_OF_MEMORY = 2, /* workspace, request slots or context pool exhausted */
+  GR_E_BAD_STATE = 3,     /* call not valid in the object's current state */
+  GR_E_NOT_FOUND = 4,     /* unknown request id */
+  GR_E_DEVICE = 5,        /* a HIP runtime error; the engine is poisoned */
+  GR_E_UNSUPPORTED = 6    /* valid but unsupported shape (see limits below) */
+} gr_status;
+
+typedef enum { GR_DTYPE_F32 = 0, GR_DTYPE_BF16 = 1 } gr_dtype;
+
+/* Normalisation domain of the item-constrained log-softmax. */
+typedef enum {
+  GR_NORM_VALID = 0, /* over the codes that extend a valid item prefix (default) */
+  GR_NORM_FULL = 1   /* over the whole codebook, then restricted to valid codes */
+} gr_norm;
+
+typedef struct gr_engine gr_engine; /* opaque */
+
+/* Model description.  Limits: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
+ * 1 <= n_levels <= 8; 2 <= codebook_size <= 1024 and codebook_size**n_levels < 2**62.
+ * All table pointers are device memory owned by the caller and must outlive
+ * the engine.  Element type of tok_q/tok_k/tok_v is `dtype` (bf16 = raw 16-bit
+ * patterns, f32 = float). */
+typedef struct {
+  int32_t n_layers, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_levels, codebook_size;
+  int32_t dtype; /* gr_dtype: ContextKV, BeamKV and token tables */
+  int32_t norm;  /* gr_norm */
+  const void *tok_q;   /* device [L][n_levels-1][V][Hq][d]  */
+  const void *tok_k;   /* device [L][n_levels-1][V][Hkv][d] */
+  const void *tok_v;   /* device [L][n_levels-1][V][Hkv][d] */
+  const float *w_sid;  /* device [n_levels][Hq*d][V] float32 */
+} gr_model_desc;
+
+/* The valid items: distinct code tuples (duplicates are tolerated and merged).
+ * Host memory, read during gr_engine_create only. */
+typedef struct {
+  int64_t n_items;
+  const int32_t *codes; /* host [n_items][n_levels], each code in [0, V) */
+} gr_item_set;
+
+#define GR_ENGINE_DEBUG_ATTN 1u /* keep every layer's attention output for gr_debug_attn_out */
+
+typedef struct {
+  int32_t max_requests;   /* requests loaded at once (slots), >= 1 */
+  int32_t max_beam_width; /* largest beam width W of any request, 1..1024 */
+  int64_t max_ctx_tokens; /* context tokens the engine's own pool holds for copy loads
+                             (each request takes its length rounded up to 64);
+                             0 = only GR_LOAD_ADOPT loads */
+  int32_t max_splits;     /* split-K partial slots per (request, kv head); 0 = 16 */
+  uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN */
+} gr_engine_opts;
+
+/* ---- engine lifetime ------------------------------------------------------ */
+
+/* Validates the description, builds the item trie (per level: a bit mask of
+ * valid next codes and the index of the first child for every valid prefix)
+ * on the host.  Makes no HIP call.  *out receives the engine. */
+gr_status gr_engine_create(const gr_model_desc *model, const gr_item_set *items,
+                           const gr_engine_opts *opts, gr_engine **out);
+
+/* Bytes of device workspace the engine needs (trie, per-slot BeamKV,
+ * BeamPath, hidden/logit/partial buffers, context pool).  0 on a NULL engine. */
+size_t gr_engine_workspace_bytes(const gr_engine *eng);
+
+/* Hands the engine its workspace (device memory, 256-byte aligned, at least
+ * gr_engine_workspace_bytes bytes, owned by the caller and kept alive until
+ * gr_engine_destroy) and uploads the trie on `stream`.  Once per engine. */
+gr_status gr_engine_bind_workspace(gr_engine *eng, void *workspace, size_t bytes, void *stream);
+
+/* Synchronises the engine's last stream, frees host state and pinned buffers.
+ * Does not free the workspace or any caller buffer.  NULL is a no-op. */
+gr_status gr_engine_destroy(gr_engine *eng);
+
+/* Trie statistics (host): number of valid prefixes of length `level`
+ * (level 0 -> 1 root, level n_levels -> number of distinct items). */
+gr_status gr_engine_trie_nodes(const gr_engine *eng, int32_t level, int64_t *n_nodes);
+
+/* ---- requests ------------------------------------------------------------- */
+
+/* Context length padded for the native ContextKV layout (multiple of 64). */
+int32_t gr_ctx_padded_len(int32_t ctx_len);
+
+#define GR_LOAD_ADOPT 1u /* k/v already in the native layout: view them, copy nothing */
+
+/* Admits request `request_id` with its shared context and creates its root
+ * beam (empty prefix, score 0).
+ *   ctx_len    N >= 1 context tokens;  beam_width 1 <= W <= max_beam_width.
+ *   q_last     device [L][Hq][d] (dtype): query of the last context token,
+ *              used at decode step 0; copied.
+ *   flags = 0: k, v are device [L][N][Hkv][d] (dtype); copied and re-laid-out
+ *              into the engine's context pool (stream-ordered; the sources may be
+ *              freed once the stream has passed this call).
+ *   flags = GR_LOAD_ADOPT: k is K in the native layout [L][Hkv][Np][d] and v is
+ *              V transposed, [L][Hkv][d][Np], Np = gr_ctx_padded_len(N); tokens
+ *              N..Np-1 must be zero.  The engine only keeps the pointers: the
+ *              buffers must stay alive and unchanged until gr_request_release.
+ * Errors: GR_E_INVALID_ARG (bad sizes, duplicate id), GR_E_OUT_OF_MEMORY (no free
+ * slot or pool space), GR_E_BAD_STATE (workspace not bound). */
+gr_status gr_ctx_kv_load(gr_engine *eng, int64_t request_id, int32_t ctx_len, int32_t beam_width,
+                         const void *k, const void *v, const void *q_last, uint32_t flags,
+                         void *stream);
+
+/* Advances each listed request by one decode step (one semantic-ID level),
+ * whatever level each one is at: requests at different levels can share a
+ * call (continuous batching).  Enqueued on `stream`; returns without waiting.
+ * Errors: GR_E_INVALID_ARG (n_requests < 1, duplicate ids), GR_E_NOT_FOUND,
+ * GR_E_BAD_STATE (a request already decoded all levels); nothing is enqueued
+ * when an error is returned. */
+gr_status gr_beam_step(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, void *stream);
+
+/* Multi-beam return after all n_levels steps.  Writes n = min(W, #valid items
+ * reachable) beams, best first: codes host [capacity][n_levels], scores host
+ * [capacity] (cumulative log-probability).  Synchronises `stream`.
+ * Errors: GR_E_BAD_STATE before the last step, GR_E_INVALID_ARG when
+ * capacity < n (then *n_beams still receives n). */
+gr_status gr_beams_get(gr_engine *eng, int64_t request_id, int32_t capacity, int32_t *codes,
+                       float *scores, int32_t *n_beams, void *stream);
+
+/* Releases a request's slot and pool space (host bookkeeping only; later work
+ * on the same stream may reuse them).  Errors: GR_E_NOT_FOUND. */
+gr_status gr_request_release(gr_engine *eng, int64_t request_id);
+
+/* Rewinds a loaded request to its root beam (level 0, empty prefix, score 0),
+ * keeping its ContextKV and q_last: the next gr_beam_step decodes it again from
+ * the start.  Enqueued on `stream`.  Errors: GR_E_NOT_FOUND. */
+gr_status gr_request_reset(gr_engine *eng, int64_t request_id, void *stream);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char *gr_last_error(void);
+
+/* ---- item-constrained top-K, stand-alone ---------------------------------- */
+
+/* Selects the k best of n_rows*V candidate scores, cand device [n_rows][V]
+ * float32, -inf marking invalid candidates: order score descending, then flat
+ * index j*V+c ascending.  Writes out_flat device [k] int32 and out_score
+ * device [k] float32 in rank order and n_out device [1] int32 = min(k, number
+ * of candidates greater than -inf).  Enqueued on `stream`, does not wait.
+ * Limits: n_rows*V <= 2**26, 1 <= k <= 1024.  The same selection runs inside
+ * gr_beam_step. */
+gr_status gr_topk_select(const float *cand, int32_t n_rows, int32_t V, int32_t k, int32_t *out_flat,
+                         float *out_score, int32_t *n_out, void *stream);
+
+/* ---- inspection (tests and debugging; each synchronises `stream`) --------- */
+
+/* Current beam set B_s of a request: *level = s, *n = n_s; parent host [cap]
+ * (slot in B_{s-1}), codes host [cap][n_levels] (first s entries valid),
+ * scores host [cap]. */
+gr_status gr_debug_beam_state(gr_engine *eng, int64_t request_id, int32_t capacity, int32_t *parent,
+                              int32_t *codes, float *scores, int32_t *n, int32_t *level,
+                              void *stream);
+
+/* BeamPath ancestry of B_s: anc host [cap][n_levels]; anc[j][t] is the BeamKV slot of
+ * beam j's level-t token (t < s). */
+gr_status gr_debug_beam_path(gr_engine *eng, int64_t request_id, int32_t capacity, int32_t *anc,
+                             int32_t *n, void *stream);
+
+/* Hidden vectors of the beams of the last completed step, host [cap][Hq*d]
+ * float32, and the logits host [cap][V]; *n = number of beams of that step. */
+gr_status gr_debug_hidden(gr_engine *eng, int64_t request_id, int32_t capacity, float *hidden,
+                          float *logits, int32_t *n, void *stream);
+
+/* Attention output of layer `layer` for the beams of the last completed
+ * step, host [cap][Hq][d] float32.  Needs GR_ENGINE_DEBUG_ATTN. */
+gr_status gr_debug_attn_out(gr_engine *eng, int64_t request_id, int32_t layer, int32_t capacity,
+                            float *out, int32_t *n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GR_BEAM_H */

@@ -1,0 +1,221 @@
+"""ctypes binding of libgr_beam.so (argument marshalling only).
+
+Every function keeps the C name.  Tensors are passed as device pointers
+(``tensor.data_ptr()``) or host numpy arrays; streams as ``hipStream_t``
+handles (``torch.cuda.current_stream().cuda_stream``).  Every step of the
+decode runs in the library's HIP kernels; nothing here computes.
+A failing call raises GrError with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgr_beam.so")
+
+GR_OK, GR_E_INVALID_ARG, GR_E_OUT_OF_MEMORY, GR_E_BAD_STATE, GR_E_NOT_FOUND, GR_E_DEVICE, GR_E_UNSUPPORTED = range(7)
+GR_DTYPE_F32, GR_DTYPE_BF16 = 0, 1
+GR_NORM_VALID, GR_NORM_FULL = 0, 1
+GR_ENGINE_DEBUG_ATTN = 1
+GR_LOAD_ADOPT = 1
+
+STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "GR_E_BAD_STATE",
+                4: "GR_E_NOT_FOUND", 5: "GR_E_DEVICE", 6: "GR_E_UNSUPPORTED"}
+
+#: every symbol include/gr_beam.h declares
+EXPORTS = [
+    "gr_engine_create", "gr_engine_workspace_bytes", "gr_engine_bind_workspace", "gr_engine_destroy",
+    "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
+    "gr_request_release", "gr_request_reset", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
+    "gr_debug_hidden", "gr_debug_attn_out",
+]
+
+
+class GrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class gr_model_desc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("n_levels", C.c_int32), ("codebook_size", C.c_int32),
+                ("dtype", C.c_int32), ("norm", C.c_int32),
+                ("tok_q", C.c_void_p), ("tok_k", C.c_void_p), ("tok_v", C.c_void_p), ("w_sid", C.c_void_p)]
+
+
+class gr_item_set(C.Structure):
+    _fields_ = [("n_items", C.c_int64), ("codes", C.POINTER(C.c_int32))]
+
+
+class gr_engine_opts(C.Structure):
+    _fields_ = [("max_requests", C.c_int32), ("max_beam_width", C.c_int32), ("max_ctx_tokens", C.c_int64),
+                ("max_splits", C.c_int32), ("flags", C.c_uint32)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the HIP library (fails loudly if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # Load torch first: its bundled HIP runtime then satisfies the library's
+    # libamdhip64.so.7 dependency, so the library and torch share one runtime
+    # (two runtimes in one process do not share devices or memory).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with semantic_id_beam_amd/build.py "
+                          "(or __graft_entry__.build())")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, u32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_size_t
+    P = C.POINTER
+    sig = {
+        "gr_engine_create": (i32, [P(gr_model_desc), P(gr_item_set), P(gr_engine_opts), P(vp)]),
+        "gr_engine_workspace_bytes": (sz, [vp]),
+        "gr_engine_bind_workspace": (i32, [vp, vp, sz, vp]),
+        "gr_engine_destroy": (i32, [vp]),
+        "gr_engine_trie_nodes": (i32, [vp, i32, P(i64)]),
+        "gr_ctx_padded_len": (i32, [i32]),
+        "gr_ctx_kv_load": (i32, [vp, i64, i32, i32, vp, vp, vp, u32, vp]),
+        "gr_beam_step": (i32, [vp, P(i64), i32, vp]),
+        "gr_beams_get": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
+        "gr_request_release": (i32, [vp, i64]),
+        "gr_request_reset": (i32, [vp, i64, vp]),
+        "gr_last_error": (C.c_char_p, []),
+        "gr_topk_select": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
+        "gr_debug_beam_state": (i32, [vp, i64, i32, vp, vp, vp, P(i32), P(i32), vp]),
+        "gr_debug_beam_path": (i32, [vp, i64, i32, vp, P(i32), vp]),
+        "gr_debug_hidden": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
+        "gr_debug_attn_out": (i32, [vp, i64, i32, i32, vp, P(i32), vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(st: int):
+    if st != GR_OK:
+        raise GrError(st, lib().gr_last_error().decode())
+
+
+def _ptr(x) -> int | None:
+    """Device pointer of a torch tensor, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _host(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+# ---------------------------------------------------------------- same names as the C ABI
+def gr_engine_create(desc: gr_model_desc, items: np.ndarray, opts: gr_engine_opts) -> int:
+    items = np.ascontiguousarray(items, dtype=np.int32)
+    iset = gr_item_set(items.shape[0], items.ctypes.data_as(C.POINTER(C.c_int32)))
+    out = C.c_void_p()
+    _check(lib().gr_engine_create(C.byref(desc), C.byref(iset), C.byref(opts), C.byref(out)))
+    return out.value
+
+
+def gr_engine_workspace_bytes(eng: int) -> int:
+    return lib().gr_engine_workspace_bytes(eng)
+
+
+def gr_engine_bind_workspace(eng: int, ws, nbytes: int, stream: int = 0):
+    _check(lib().gr_engine_bind_workspace(eng, _ptr(ws), nbytes, stream))
+
+
+def gr_engine_destroy(eng: int):
+    _check(lib().gr_engine_destroy(eng))
+
+
+def gr_engine_trie_nodes(eng: int, level: int) -> int:
+    n = C.c_int64()
+    _check(lib().gr_engine_trie_nodes(eng, level, C.byref(n)))
+    return n.value
+
+
+def gr_ctx_padded_len(n: int) -> int:
+    return lib().gr_ctx_padded_len(n)
+
+
+def gr_ctx_kv_load(eng: int, rid: int, ctx_len: int, beam_width: int, k, v, q_last, flags: int = 0,
+                   stream: int = 0):
+    _check(lib().gr_ctx_kv_load(eng, rid, ctx_len, beam_width, _ptr(k), _ptr(v), _ptr(q_last), flags, stream))
+
+
+def gr_beam_step(eng: int, request_ids, stream: int = 0):
+    ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+    _check(lib().gr_beam_step(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), ids.shape[0], stream))
+
+
+def gr_beams_get(eng: int, rid: int, capacity: int, n_levels: int, stream: int = 0):
+    codes = np.zeros((max(capacity, 1), n_levels), dtype=np.int32)
+    scores = np.zeros(max(capacity, 1), dtype=np.float32)
+    n = C.c_int32()
+    _check(lib().gr_beams_get(eng, rid, capacity, _host(codes), _host(scores), C.byref(n), stream))
+    return codes[: n.value], scores[: n.value]
+
+
+def gr_request_release(eng: int, rid: int):
+    _check(lib().gr_request_release(eng, rid))
+
+
+def gr_request_reset(eng: int, rid: int, stream: int = 0):
+    _check(lib().gr_request_reset(eng, rid, stream))
+
+
+def gr_last_error() -> str:
+    return lib().gr_last_error().decode()
+
+
+def gr_topk_select(cand, n_rows: int, V: int, k: int, out_flat, out_score, n_out, stream: int = 0):
+    _check(lib().gr_topk_select(_ptr(cand), n_rows, V, k, _ptr(out_flat), _ptr(out_score), _ptr(n_out), stream))
+
+
+def gr_debug_beam_state(eng: int, rid: int, capacity: int, n_levels: int, stream: int = 0):
+    parent = np.zeros(capacity, dtype=np.int32)
+    codes = np.zeros((capacity, n_levels), dtype=np.int32)
+    scores = np.zeros(capacity, dtype=np.float32)
+    n, level = C.c_int32(), C.c_int32()
+    _check(lib().gr_debug_beam_state(eng, rid, capacity, _host(parent), _host(codes), _host(scores),
+                                     C.byref(n), C.byref(level), stream))
+    m = min(n.value, capacity)
+    return {"n": n.value, "level": level.value, "parent": parent[:m], "codes": codes[:m, : level.value],
+            "scores": scores[:m]}
+
+
+def gr_debug_beam_path(eng: int, rid: int, capacity: int, n_levels: int, stream: int = 0):
+    anc = np.zeros((capacity, n_levels), dtype=np.int32)
+    n = C.c_int32()
+    _check(lib().gr_debug_beam_path(eng, rid, capacity, _host(anc), C.byref(n), stream))
+    return anc[: min(n.value, capacity)]
+
+
+def gr_debug_hidden(eng: int, rid: int, capacity: int, hidden_dim: int, V: int, stream: int = 0):
+    h = np.zeros((capacity, hidden_dim), dtype=np.float32)
+    lg = np.zeros((capacity, V), dtype=np.float32)
+    n = C.c_int32()
+    _check(lib().gr_debug_hidden(eng, rid, capacity, _host(h), _host(lg), C.byref(n), stream))
+    m = min(n.value, capacity)
+    return h[:m], lg[:m]
+
+
+def gr_debug_attn_out(eng: int, rid: int, layer: int, capacity: int, Hq: int, d: int, stream: int = 0):
+    o = np.zeros((capacity, Hq, d), dtype=np.float32)
+    n = C.c_int32()
+    _check(lib().gr_debug_attn_out(eng, rid, layer, capacity, _host(o), C.byref(n), stream))
+    return o[: min(n.value, capacity)]

@@ -1,0 +1,669 @@
+// Host side of the semantic-ID beam-decode library: argument validation, the
+// item trie, workspace layout, request table, per-step work descriptors and the
+// C ABI declared in include/gr_beam.h.
+//
+// The split of the KV cache into a per-request ContextKV, a short per-beam
+// BeamKV and a BeamPath ancestry table, continuous batching of requests at
+// different levels, and the item-constrained top-K all follow the zhiding.cn
+// article on NVIDIA recsys-examples, section "语义ID生成式推荐专用推理框架".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "gr_beam.h"
+#include "gr_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+gr_status fail(gr_status st, const std::string &msg) {
+  g_err = msg;
+  return st;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kRing = 16;  // per-step descriptor buffers in flight
+
+}  // namespace
+
+struct gr_engine {
+  gr::Dims dm{};
+  gr::SlotLayout sl{};
+  gr::Dev dev{};
+  gr_model_desc model{};
+  gr_engine_opts opts{};
+  int elem = 2;
+
+  // trie, host copy: levels 0..n_levels-1 hold masks and first-child indices
+  std::vector<int64_t> nodes;  // nodes[t] = valid prefixes of length t, t = 0..n_levels
+  std::vector<uint32_t> h_mask;
+  std::vector<int32_t> h_child;
+  std::vector<int64_t> trie_off;
+
+  // workspace layout (byte offsets)
+  size_t off_mask = 0, off_child = 0, off_slots = 0, off_pool = 0, off_work = 0, ws_need = 0;
+  size_t work_bytes = 0;  // one ring entry
+  uint8_t *ws = nullptr;
+  bool bound = false;
+  bool poisoned = false;
+
+  // context pool: padded tokens, first fit
+  int64_t pool_tokens = 0;
+  size_t pool_tok_bytes = 0;
+  std::map<int64_t, int64_t> pool_free;  // offset -> length
+
+  struct Req {
+    int slot = -1;
+    int N = 0, Np = 0, W = 0, level = 0, n_bound = 1;
+    bool adopt = false;
+    int64_t pool_off = -1;
+    const void *k = nullptr, *vt = nullptr;
+  };
+  std::unordered_map<int64_t, Req> reqs;
+  std::vector<int> free_slots;
+
+  std::vector<gr::StepReq *> pinned;
+  std::vector<hipEvent_t> events;
+  std::vector<bool> event_used;
+  int ring = 0;
+};
+
+namespace {
+
+gr_status check_dev(gr_engine *e, hipError_t err, const char *what) {
+  if (err == hipSuccess) return GR_OK;
+  e->poisoned = true;
+  return fail(GR_E_DEVICE, std::string(what) + ": " + hipGetErrorString(err));
+}
+
+gr_status build_trie(gr_engine *e, const gr_item_set *items) {
+  const int lv = e->dm.levels, V = e->dm.V;
+  std::vector<uint64_t> keys((size_t)items->n_items);
+  for (int64_t i = 0; i < items->n_items; ++i) {
+    uint64_t k = 0;
+    for (int t = 0; t < lv; ++t) {
+      const int32_t c = items->codes[i * lv + t];
+      if (c < 0 || c >= V) return fail(GR_E_INVALID_ARG, "item code out of range [0, codebook_size)");
+      k = k * (uint64_t)V + (uint64_t)c;
+    }
+    keys[(size_t)i] = k;
+  }
+  std::sort(keys.begin(), keys.end());
+  keys.erase(std::unique(keys.begin(), keys.end()), keys.end());
+  std::vector<uint64_t> powv(lv + 1, 1);
+  for (int t = 1; t <= lv; ++t) powv[t] = powv[t - 1] * (uint64_t)V;
+  // count nodes per level
+  e->nodes.assign(lv + 1, 0);
+  e->nodes[0] = 1;
+  {
+    std::vector<uint64_t> last(lv + 1, ~0ull);
+    for (uint64_t k : keys)
+      for (int t = 1; t <= lv; ++t) {
+        const uint64_t p = k / powv[lv - t];
+        if (p != last[t]) {
+          last[t] = p;
+          e->nodes[t]++;
+        }
+      }
+  }
+  const int MW = e->dm.MW;
+  e->trie_off.assign(lv + 1, 0);
+  for (int t = 1; t <= lv; ++t) e->trie_off[t] = e->trie_off[t - 1] + e->nodes[t - 1];
+  const int64_t total = e->trie_off[lv];
+  e->h_mask.assign((size_t)total * MW, 0u);
+  e->h_child.assign((size_t)total, -1);
+  std::vector<uint64_t> last(lv + 1, ~0ull);
+  std::vector<int64_t> cnt(lv + 1, 0);
+  cnt[0] = 1;
+  for (uint64_t k : keys) {
+    for (int t = 1; t <= lv; ++t) {
+      const uint64_t p = k / powv[lv - t];
+      if (p == last[t]) continue;
+      last[t] = p;
+      const int64_t idx = cnt[t]++;
+      const int64_t parent = cnt[t - 1] - 1;  // keys are sorted: the parent is the newest node above
+      const int c = (int)(p % (uint64_t)V);
+      const int64_t prow = e->trie_off[t - 1] + parent;
+      e->h_mask[(size_t)prow * MW + (c >> 5)] |= 1u << (c & 31);
+      if (e->h_child[(size_t)prow] < 0) e->h_child[(size_t)prow] = (int32_t)idx;
+    }
+  }
+  return GR_OK;
+}
+
+void layout(gr_engine *e) {
+  const gr::Dims &d = e->dm;
+  const size_t A = 256;
+  const size_t W = d.W_max, el = e->elem;
+  gr::SlotLayout &s = e->sl;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o = align_up(o + bytes, A);
+    return r;
+  };
+  const size_t kv = (size_t)d.L * (d.levels - 1) * W * d.Hkv * d.d * el;
+  s.beamkv_k = take(kv);
+  s.beamkv_v = take(kv);
+  s.q_last = take((size_t)d.L * d.Hq * d.d * el);
+  s.h = take(W * d.Hq * d.d * 4);
+  s.logits = take(W * d.V * 4);
+  s.cand = take(W * d.V * 4);
+  s.part_o = take((size_t)d.Hkv * d.S_max * W * d.g * d.d * 4);
+  s.part_ml = take((size_t)d.Hkv * d.S_max * W * d.g * 8);
+  for (int b = 0; b < 2; ++b) {
+    s.codes[b] = take(W * d.levels * 4);
+    s.score[b] = take(W * 4);
+    s.node[b] = take(W * 4);
+    s.anc[b] = take(W * d.levels * 4);
+    s.parent[b] = take(W * 4);
+  }
+  s.n_live = take(8);
+  s.dbg_attn = d.debug_attn ? take((size_t)d.L * W * d.Hq * d.d * 4) : 0;
+  s.slot_bytes = align_up(o, A);
+
+  size_t w = 0;
+  e->off_mask = w;
+  w = align_up(w + e->h_mask.size() * 4, A);
+  e->off_child = w;
+  w = align_up(w + e->h_child.size() * 4, A);
+  e->off_slots = w;
+  w = align_up(w + s.slot_bytes * (size_t)e->opts.max_requests, A);
+  e->pool_tok_bytes = (size_t)2 * d.L * d.Hkv * d.d * el;
+  e->pool_tokens = e->opts.max_ctx_tokens;
+  e->off_pool = w;
+  w = align_up(w + (size_t)e->pool_tokens * e->pool_tok_bytes, A);
+  e->work_bytes = align_up(sizeof(gr::StepReq) * (size_t)e->opts.max_requests, A);
+  e->off_work = w;
+  w = align_up(w + e->work_bytes * kRing, A);
+  e->ws_need = w;
+}
+
+bool pool_alloc(gr_engine *e, int64_t n, int64_t *off) {
+  for (auto it = e->pool_free.begin(); it != e->pool_free.end(); ++it) {
+    if (it->second >= n) {
+      *off = it->first;
+      const int64_t rest = it->second - n, roff = it->first + n;
+      e->pool_free.erase(it);
+      if (rest > 0) e->pool_free[roff] = rest;
+      return true;
+    }
+  }
+  return false;
+}
+
+void pool_free(gr_engine *e, int64_t off, int64_t n) {
+  auto it = e->pool_free.emplace(off, n).first;
+  auto nx = std::next(it);
+  if (nx != e->pool_free.end() && it->first + it->second == nx->first) {
+    it->second += nx->second;
+    e->pool_free.erase(nx);
+  }
+  if (it != e->pool_free.begin()) {
+    auto pv = std::prev(it);
+    if (pv->first + pv->second == it->first) {
+      pv->second += it->second;
+      e->pool_free.erase(it);
+    }
+  }
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+extern "C" {
+
+const char *gr_last_error(void) { return g_err.c_str(); }
+
+int32_t gr_ctx_padded_len(int32_t ctx_len) {
+  if (ctx_len <= 0) return 0;
+  return (int32_t)align_up((size_t)ctx_len, gr::kTileTok);
+}
+
+gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, const gr_engine_opts *o,
+                           gr_engine **out) {
+  g_err.clear();
+  if (!m || !items || !o || !out) return fail(GR_E_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (m->n_layers < 1 || m->n_q_heads < 1 || m->n_kv_heads < 1)
+    return fail(GR_E_INVALID_ARG, "n_layers, n_q_heads and n_kv_heads must be >= 1");
+  if (m->n_q_heads % m->n_kv_heads != 0) return fail(GR_E_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (m->n_q_heads / m->n_kv_heads > gr::kMaxGroup)
+    return fail(GR_E_UNSUPPORTED, "more than 8 query heads per kv head");
+  if (m->head_dim != 64 && m->head_dim != 128) return fail(GR_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (m->n_levels < 1 || m->n_levels > gr::kMaxLevels) return fail(GR_E_INVALID_ARG, "n_levels must be in [1, 8]");
+  if (m->codebook_size < 2 || m->codebook_size > 1024) return fail(GR_E_INVALID_ARG, "codebook_size must be in [2, 1024]");
+  {
+    double bits = m->n_levels * std::log2((double)m->codebook_size);
+    if (bits >= 62.0) return fail(GR_E_UNSUPPORTED, "codebook_size**n_levels must be < 2**62");
+  }
+  if (m->dtype != GR_DTYPE_F32 && m->dtype != GR_DTYPE_BF16) return fail(GR_E_INVALID_ARG, "dtype");
+  if (m->norm != GR_NORM_VALID && m->norm != GR_NORM_FULL) return fail(GR_E_INVALID_ARG, "norm");
+  if (!m->w_sid) return fail(GR_E_INVALID_ARG, "w_sid is null");
+  if (m->n_levels > 1 && (!m->tok_q || !m->tok_k || !m->tok_v))
+    return fail(GR_E_INVALID_ARG, "token tables are null");
+  if (items->n_items < 1 || !items->codes) return fail(GR_E_INVALID_ARG, "empty item set");
+  if (o->max_requests < 1 || o->max_requests > 65536) return fail(GR_E_INVALID_ARG, "max_requests must be in [1, 65536]");
+  if (o->max_beam_width < 1 || o->max_beam_width > gr::kMaxBeam)
+    return fail(GR_E_INVALID_ARG, "max_beam_width must be in [1, 1024]");
+  if (o->max_ctx_tokens < 0) return fail(GR_E_INVALID_ARG, "max_ctx_tokens < 0");
+  if (o->max_splits < 0 || o->max_splits > 64) return fail(GR_E_INVALID_ARG, "max_splits must be in [0, 64]");
+
+  gr_engine *e = new gr_engine();
+  e->model = *m;
+  e->opts = *o;
+  if (e->opts.max_splits == 0) e->opts.max_splits = 16;
+  e->elem = m->dtype == GR_DTYPE_BF16 ? 2 : 4;
+  gr::Dims &d = e->dm;
+  d.L = m->n_layers;
+  d.Hq = m->n_q_heads;
+  d.Hkv = m->n_kv_heads;
+  d.g = d.Hq / d.Hkv;
+  d.d = m->head_dim;
+  d.levels = m->n_levels;
+  d.V = m->codebook_size;
+  d.MW = (d.V + 31) / 32;
+  d.W_max = o->max_beam_width;
+  d.S_max = e->opts.max_splits;
+  d.dtype = m->dtype == GR_DTYPE_BF16 ? 1 : 0;
+  d.norm = m->norm == GR_NORM_FULL ? 1 : 0;
+  d.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
+  d.debug_attn = (o->flags & GR_ENGINE_DEBUG_ATTN) ? 1 : 0;
+  gr_status st = build_trie(e, items);
+  if (st != GR_OK) {
+    delete e;
+    return st;
+  }
+  layout(e);
+  for (int s = e->opts.max_requests - 1; s >= 0; --s) e->free_slots.push_back(s);
+  if (e->pool_tokens > 0) e->pool_free[0] = e->pool_tokens;
+  *out = e;
+  return GR_OK;
+}
+
+size_t gr_engine_workspace_bytes(const gr_engine *e) { return e ? e->ws_need : 0; }
+
+gr_status gr_engine_trie_nodes(const gr_engine *e, int32_t level, int64_t *n) {
+  if (!e || !n) return fail(GR_E_INVALID_ARG, "null argument");
+  if (level < 0 || level > e->dm.levels) return fail(GR_E_INVALID_ARG, "level out of range");
+  *n = e->nodes[level];
+  return GR_OK;
+}
+
+gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *stream) {
+  if (!e || !ws) return fail(GR_E_INVALID_ARG, "null argument");
+  if (e->bound) return fail(GR_E_BAD_STATE, "workspace already bound");
+  if (bytes < e->ws_need) return fail(GR_E_OUT_OF_MEMORY, "workspace smaller than gr_engine_workspace_bytes");
+  if (((uintptr_t)ws & 255u) != 0) return fail(GR_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  e->ws = (uint8_t *)ws;
+  gr_status r;
+  if ((r = check_dev(e, hipMemcpyAsync(e->ws + e->off_mask, e->h_mask.data(), e->h_mask.size() * 4,
+                                       hipMemcpyHostToDevice, st), "trie upload")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, hipMemcpyAsync(e->ws + e->off_child, e->h_child.data(), e->h_child.size() * 4,
+                                       hipMemcpyHostToDevice, st), "trie upload")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "trie upload")) != GR_OK) return r;
+  e->pinned.assign(kRing, nullptr);
+  e->events.assign(kRing, nullptr);
+  e->event_used.assign(kRing, false);
+  for (int i = 0; i < kRing; ++i) {
+    if ((r = check_dev(e, hipHostMalloc((void **)&e->pinned[i], e->work_bytes, hipHostMallocDefault),
+                       "pinned descriptor ring")) != GR_OK)
+      return r;
+    if ((r = check_dev(e, hipEventCreateWithFlags(&e->events[i], hipEventDisableTiming), "event")) != GR_OK)
+      return r;
+  }
+  gr::Dev &dv = e->dev;
+  dv.dm = e->dm;
+  dv.sl = e->sl;
+  dv.slots = e->ws + e->off_slots;
+  dv.trie_mask = (const uint32_t *)(e->ws + e->off_mask);
+  dv.trie_child = (const int32_t *)(e->ws + e->off_child);
+  for (int t = 0; t <= e->dm.levels && t <= gr::kMaxLevels; ++t) dv.trie_off[t] = e->trie_off[t];
+  dv.tok_q = e->model.tok_q;
+  dv.tok_k = e->model.tok_k;
+  dv.tok_v = e->model.tok_v;
+  dv.w_sid = e->model.w_sid;
+  e->bound = true;
+  return GR_OK;
+}
+
+gr_status gr_engine_destroy(gr_engine *e) {
+  if (!e) return GR_OK;
+  if (e->bound) {
+    (void)hipDeviceSynchronize();
+    for (auto &ev : e->events)
+      if (ev) (void)hipEventDestroy(ev);
+    for (auto *p : e->pinned)
+      if (p) (void)hipHostFree(p);
+  }
+  delete e;
+  return GR_OK;
+}
+
+gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const void *k, const void *v,
+                         const void *q_last, uint32_t flags, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (!k || !v || !q_last) return fail(GR_E_INVALID_ARG, "null k, v or q_last");
+  if (N < 1) return fail(GR_E_INVALID_ARG, "ctx_len must be >= 1");
+  if (W < 1 || W > e->dm.W_max) return fail(GR_E_INVALID_ARG, "beam_width must be in [1, max_beam_width]");
+  if (flags & ~GR_LOAD_ADOPT) return fail(GR_E_INVALID_ARG, "unknown load flag");
+  if (e->reqs.count(rid)) return fail(GR_E_INVALID_ARG, "request id already loaded");
+  if (e->free_slots.empty()) return fail(GR_E_OUT_OF_MEMORY, "no free request slot (max_requests)");
+  const int Np = gr_ctx_padded_len(N);
+  gr_engine::Req R;
+  R.N = N;
+  R.Np = Np;
+  R.W = W;
+  hipStream_t st = (hipStream_t)stream;
+  gr_status r;
+  if (flags & GR_LOAD_ADOPT) {
+    R.adopt = true;
+    R.k = k;
+    R.vt = v;
+  } else {
+    int64_t off;
+    if (!pool_alloc(e, Np, &off)) return fail(GR_E_OUT_OF_MEMORY, "context pool exhausted (max_ctx_tokens)");
+    R.pool_off = off;
+    uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
+    uint8_t *dvt = dk + (size_t)e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
+    R.k = dk;
+    R.vt = dvt;
+    if ((r = check_dev(e, gr::launch_relayout(k, v, dk, dvt, e->dm.L, N, Np, e->dm.Hkv, e->dm.d, e->elem, st),
+                       "context relayout")) != GR_OK) {
+      pool_free(e, off, Np);
+      return r;
+    }
+  }
+  R.slot = e->free_slots.back();
+  uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
+  if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem,
+                                       hipMemcpyDeviceToDevice, st), "q_last copy")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, gr::launch_init_slot(e->dev, R.slot, st), "slot init")) != GR_OK) return r;
+  e->free_slots.pop_back();
+  e->reqs[rid] = R;
+  return GR_OK;
+}
+
+gr_status gr_request_release(gr_engine *e, int64_t rid) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  auto it = e->reqs.find(rid);
+  if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+  if (!it->second.adopt && it->second.pool_off >= 0) pool_free(e, it->second.pool_off, it->second.Np);
+  e->free_slots.push_back(it->second.slot);
+  e->reqs.erase(it);
+  return GR_OK;
+}
+
+gr_status gr_request_reset(gr_engine *e, int64_t rid, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  auto it = e->reqs.find(rid);
+  if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+  gr_status r;
+  if ((r = check_dev(e, gr::launch_init_slot(e->dev, it->second.slot, (hipStream_t)stream), "slot init")) != GR_OK)
+    return r;
+  it->second.level = 0;
+  it->second.n_bound = 1;
+  return GR_OK;
+}
+
+gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (!ids || n < 1) return fail(GR_E_INVALID_ARG, "need at least one request id");
+  if (n > e->opts.max_requests) return fail(GR_E_INVALID_ARG, "more ids than max_requests");
+  const gr::Dims &d = e->dm;
+  std::vector<gr_engine::Req *> rs((size_t)n);
+  {
+    std::unordered_set<int64_t> seen;
+    for (int i = 0; i < n; ++i) {
+      if (!seen.insert(ids[i]).second) return fail(GR_E_INVALID_ARG, "duplicate request id in one step");
+      auto it = e->reqs.find(ids[i]);
+      if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+      if (it->second.level >= d.levels) return fail(GR_E_BAD_STATE, "request already decoded every level");
+      rs[(size_t)i] = &it->second;
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  gr_status r;
+  // ---- work decomposition
+  int nw = 1;
+  if (d.dtype == 1) {
+    for (auto *R : rs) {
+      const int rows = R->n_bound * d.g;
+      nw = std::max(nw, rows <= 32 ? 1 : rows <= 64 ? 2 : 4);
+    }
+  }
+  const int rows_wg = gr::ctx_rows_per_wg(nw);
+  int64_t units = 0;
+  for (auto *R : rs) units += (int64_t)d.Hkv * ceil_div((int64_t)R->n_bound * d.g, rows_wg);
+  const int want = d.dtype == 1 ? (nw == 4 ? 512 : nw == 2 ? 1024 : 2048) : 256;
+  const int slot_i = e->ring;
+  e->ring = (e->ring + 1) % kRing;
+  if (e->event_used[slot_i]) {
+    if ((r = check_dev(e, hipEventSynchronize(e->events[slot_i]), "descriptor ring")) != GR_OK) return r;
+  }
+  gr::StepReq *hw = e->pinned[slot_i];
+  int wg_ctx = 0, wg_merge = 0, wg_logits = 0;
+  for (int i = 0; i < n; ++i) {
+    gr_engine::Req *R = rs[(size_t)i];
+    gr::StepReq &w = hw[i];
+    std::memset(&w, 0, sizeof(w));
+    w.ctx_k = R->k;
+    w.ctx_vt = R->vt;
+    w.ctx_lstride = (int64_t)d.Hkv * R->Np * d.d;
+    w.N = R->N;
+    w.Np = R->Np;
+    w.slot = R->slot;
+    w.level = R->level;
+    w.W = R->W;
+    w.n_bound = R->n_bound;
+    const int rows = R->n_bound * d.g;
+    w.row_blocks = ceil_div(rows, rows_wg);
+    int S = (int)std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1));
+    S = std::min(S, d.S_max);
+    S = std::min(S, std::max(1, ceil_div(R->N, 2 * gr::kTileTok)));
+    int tps = (int)align_up((size_t)ceil_div(R->N, S), gr::kTileTok);
+    S = ceil_div(R->N, tps);
+    w.splits = S;
+    w.tps = tps;
+    w.wg_ctx = wg_ctx;
+    if (d.dtype == 1)
+      wg_ctx += d.Hkv * w.row_blocks * S;
+    else
+      wg_ctx += ceil_div((int64_t)d.Hkv * rows * S, 4);
+    w.wg_merge = wg_merge;
+    wg_merge += ceil_div((int64_t)R->n_bound * d.Hkv, 4);
+    w.wg_logits = wg_logits;
+    wg_logits += ceil_div(R->n_bound, 32) * ceil_div(d.V, 64);
+  }
+  gr::StepReq *dw = (gr::StepReq *)(e->ws + e->off_work + e->work_bytes * (size_t)slot_i);
+  if ((r = check_dev(e, hipMemcpyAsync(dw, hw, sizeof(gr::StepReq) * (size_t)n, hipMemcpyHostToDevice, st),
+                     "descriptor upload")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, hipEventRecord(e->events[slot_i], st), "descriptor ring")) != GR_OK) return r;
+  e->event_used[slot_i] = true;
+  for (int l = 0; l < d.L; ++l) {
+    if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw, n, l, wg_ctx, nw, st), "context attention")) != GR_OK)
+      return r;
+    if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st), "beam attention/merge")) != GR_OK)
+      return r;
+  }
+  if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st), "logits")) != GR_OK) return r;
+  if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, st), "top-k")) != GR_OK) return r;
+  for (auto *R : rs) {
+    const int s = R->level;
+    int64_t nb = std::min<int64_t>((int64_t)R->W, (int64_t)R->n_bound * d.V);
+    nb = std::min<int64_t>(nb, e->nodes[s + 1]);
+    R->n_bound = (int)nb;
+    R->level = s + 1;
+  }
+  return GR_OK;
+}
+
+namespace {
+gr_status find_req(gr_engine *e, int64_t rid, gr_engine::Req **out) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  auto it = e->reqs.find(rid);
+  if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+  *out = &it->second;
+  return GR_OK;
+}
+uint8_t *slot_ptr(gr_engine *e, const gr_engine::Req *R) {
+  return e->ws + e->off_slots + (size_t)R->slot * e->sl.slot_bytes;
+}
+gr_status d2h(gr_engine *e, void *dst, const void *src, size_t bytes, hipStream_t st) {
+  return check_dev(e, hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st), "device to host copy");
+}
+}  // namespace
+
+gr_status gr_beams_get(gr_engine *e, int64_t rid, int32_t cap, int32_t *codes, float *scores, int32_t *n_beams,
+                       void *stream) {
+  gr_engine::Req *R;
+  gr_status r = find_req(e, rid, &R);
+  if (r != GR_OK) return r;
+  if (!n_beams || cap < 0 || (cap > 0 && (!codes || !scores))) return fail(GR_E_INVALID_ARG, "null output");
+  if (R->level != e->dm.levels) return fail(GR_E_BAD_STATE, "request has not decoded every level yet");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, R);
+  const int cur = R->level & 1, lv = e->dm.levels;
+  int32_t nl = 0;
+  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * cur, 4, st)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  *n_beams = nl;
+  if (nl > cap) return fail(GR_E_INVALID_ARG, "capacity smaller than the number of beams");
+  if (nl > 0) {
+    if ((r = d2h(e, codes, sb + e->sl.codes[cur], (size_t)nl * lv * 4, st)) != GR_OK) return r;
+    if ((r = d2h(e, scores, sb + e->sl.score[cur], (size_t)nl * 4, st)) != GR_OK) return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  }
+  return GR_OK;
+}
+
+gr_status gr_debug_beam_state(gr_engine *e, int64_t rid, int32_t cap, int32_t *parent, int32_t *codes,
+                              float *scores, int32_t *n, int32_t *level, void *stream) {
+  gr_engine::Req *R;
+  gr_status r = find_req(e, rid, &R);
+  if (r != GR_OK) return r;
+  if (!parent || !codes || !scores || !n || !level) return fail(GR_E_INVALID_ARG, "null output");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, R);
+  const int cur = R->level & 1, lv = e->dm.levels;
+  int32_t nl = 0;
+  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * cur, 4, st)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  *n = nl;
+  *level = R->level;
+  const int m = std::min(nl, cap);
+  if (m > 0) {
+    if ((r = d2h(e, parent, sb + e->sl.parent[cur], (size_t)m * 4, st)) != GR_OK) return r;
+    if ((r = d2h(e, codes, sb + e->sl.codes[cur], (size_t)m * lv * 4, st)) != GR_OK) return r;
+    if ((r = d2h(e, scores, sb + e->sl.score[cur], (size_t)m * 4, st)) != GR_OK) return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  }
+  return GR_OK;
+}
+
+gr_status gr_debug_beam_path(gr_engine *e, int64_t rid, int32_t cap, int32_t *anc, int32_t *n, void *stream) {
+  gr_engine::Req *R;
+  gr_status r = find_req(e, rid, &R);
+  if (r != GR_OK) return r;
+  if (!anc || !n) return fail(GR_E_INVALID_ARG, "null output");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, R);
+  const int cur = R->level & 1;
+  int32_t nl = 0;
+  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * cur, 4, st)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  *n = nl;
+  const int m = std::min(nl, cap);
+  if (m > 0) {
+    if ((r = d2h(e, anc, sb + e->sl.anc[cur], (size_t)m * e->dm.levels * 4, st)) != GR_OK) return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  }
+  return GR_OK;
+}
+
+gr_status gr_debug_hidden(gr_engine *e, int64_t rid, int32_t cap, float *hidden, float *logits, int32_t *n,
+                          void *stream) {
+  gr_engine::Req *R;
+  gr_status r = find_req(e, rid, &R);
+  if (r != GR_OK) return r;
+  if (!n) return fail(GR_E_INVALID_ARG, "null output");
+  if (R->level < 1) return fail(GR_E_BAD_STATE, "no step completed yet");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, R);
+  const int prev = (R->level - 1) & 1;
+  int32_t nl = 0;
+  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * prev, 4, st)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  *n = nl;
+  const int m = std::min(nl, cap);
+  const size_t H = (size_t)e->dm.Hq * e->dm.d;
+  if (m > 0) {
+    if (hidden && (r = d2h(e, hidden, sb + e->sl.h, (size_t)m * H * 4, st)) != GR_OK) return r;
+    if (logits && (r = d2h(e, logits, sb + e->sl.logits, (size_t)m * e->dm.V * 4, st)) != GR_OK) return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  }
+  return GR_OK;
+}
+
+gr_status gr_debug_attn_out(gr_engine *e, int64_t rid, int32_t layer, int32_t cap, float *out, int32_t *n,
+                            void *stream) {
+  gr_engine::Req *R;
+  gr_status r = find_req(e, rid, &R);
+  if (r != GR_OK) return r;
+  if (!e->dm.debug_attn) return fail(GR_E_BAD_STATE, "engine created without GR_ENGINE_DEBUG_ATTN");
+  if (!out || !n) return fail(GR_E_INVALID_ARG, "null output");
+  if (layer < 0 || layer >= e->dm.L) return fail(GR_E_INVALID_ARG, "layer out of range");
+  if (R->level < 1) return fail(GR_E_BAD_STATE, "no step completed yet");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, R);
+  const int prev = (R->level - 1) & 1;
+  int32_t nl = 0;
+  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * prev, 4, st)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  *n = nl;
+  const int m = std::min(nl, cap);
+  const size_t row = (size_t)e->dm.Hq * e->dm.d;
+  if (m > 0) {
+    if ((r = d2h(e, out, sb + e->sl.dbg_attn + (size_t)layer * e->dm.W_max * row * 4, (size_t)m * row * 4, st)) !=
+        GR_OK)
+      return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  }
+  return GR_OK;
+}
+
+gr_status gr_topk_select(const float *cand, int32_t n_rows, int32_t V, int32_t k, int32_t *out_flat,
+                         float *out_score, int32_t *n_out, void *stream) {
+  g_err.clear();
+  if (!cand || !out_flat || !out_score || !n_out) return fail(GR_E_INVALID_ARG, "null argument");
+  if (n_rows < 1 || V < 1) return fail(GR_E_INVALID_ARG, "n_rows and V must be >= 1");
+  if ((int64_t)n_rows * V > (int64_t)1 << 26) return fail(GR_E_UNSUPPORTED, "n_rows*V must be <= 2**26");
+  if (k < 1 || k > gr::kMaxBeam) return fail(GR_E_INVALID_ARG, "k must be in [1, 1024]");
+  hipError_t err = gr::launch_topk_select(cand, n_rows, V, k, out_flat, out_score, n_out, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(GR_E_DEVICE, std::string("top-k select: ") + hipGetErrorString(err));
+  return GR_OK;
+}
+
+}  // extern "C"

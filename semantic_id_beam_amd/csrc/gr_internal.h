@@ -1,0 +1,88 @@
+// Internal structures shared by the host engine (gr_engine.cpp) and the HIP
+// kernels (gr_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gr {
+
+constexpr int kMaxLevels = 8;
+constexpr int kMaxGroup = 8;      // query heads per kv head handled by the beam kernel
+constexpr int kTileTok = 64;      // context tokens per split granule / padding unit
+constexpr int kTopkThreads = 1024;
+constexpr int kMaxBeam = 1024;
+
+struct Dims {
+  int L, Hq, Hkv, g, d, levels, V, MW;  // MW = 32-bit words per trie mask row
+  int W_max, S_max;
+  int dtype;   // 0 f32, 1 bf16
+  int norm;    // 0 valid, 1 full
+  float scale_log2;  // log2(e) / sqrt(d)
+  int debug_attn;
+};
+
+// Byte offsets of the arrays inside one request slot; slots are slot_bytes apart.
+struct SlotLayout {
+  size_t slot_bytes;
+  size_t beamkv_k, beamkv_v;  // [L][levels-1][W_max][Hkv][d] elem
+  size_t q_last;              // [L][Hq][d] elem
+  size_t h;                   // [W_max][Hq*d] f32
+  size_t logits;              // [W_max][V] f32
+  size_t cand;                // [W_max][V] f32
+  size_t part_o;              // [Hkv][S_max][W_max*g][d] f32
+  size_t part_ml;             // [Hkv][S_max][W_max*g] float2 (m in log2 units, l)
+  size_t codes[2];            // [W_max][levels] i32   (double-buffered by level parity)
+  size_t score[2];            // [W_max] f32
+  size_t node[2];             // [W_max] i32  trie node of the beam's prefix
+  size_t anc[2];              // [W_max][levels] i32  BeamKV slot of each level's token
+  size_t parent[2];           // [W_max] i32
+  size_t n_live;              // i32[2]: n_live[s & 1] = beams of B_s
+  size_t dbg_attn;            // [L][W_max][Hq][d] f32 (only with debug_attn)
+};
+
+struct Dev {
+  Dims dm;
+  SlotLayout sl;
+  uint8_t *slots;
+  const uint32_t *trie_mask;       // concatenated levels: [nodes_t][MW]
+  const int32_t *trie_child;       // concatenated levels: [nodes_t]
+  int64_t trie_off[kMaxLevels + 1];  // node offset of level t
+  const void *tok_q, *tok_k, *tok_v;
+  const float *w_sid;
+};
+
+// One request of one gr_beam_step call.
+struct StepReq {
+  const void *ctx_k;    // native K [L][Hkv][Np][d]
+  const void *ctx_vt;   // native V^T [L][Hkv][d][Np]
+  int64_t ctx_lstride;  // elements per layer = Hkv*Np*d
+  int N, Np;
+  int slot, level, W;
+  int n_bound;          // upper bound of n_s known on the host (device holds the exact n_s)
+  int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
+  int row_blocks;       // context-attention row blocks per kv head
+  int wg_ctx, wg_merge, wg_logits;  // first workgroup of this request in each launch
+  int pad_;
+};
+
+// ---- launchers (gr_kernels.hip) ------------------------------------------
+// ctx_nw: waves per context workgroup (1, 2 or 4); 32 query rows per wave.
+hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
+                           int ctx_nw, hipStream_t st);
+hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
+                             hipStream_t st);
+hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st);
+hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st);
+hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N,
+                           int Np, int Hkv, int d, int elem_bytes, hipStream_t st);
+hipError_t launch_init_slot(const Dev &dev, int slot, hipStream_t st);
+hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
+                              float *out_score, int32_t *n_out_dev, hipStream_t st);
+
+// rows per context workgroup for a given wave count
+inline int ctx_rows_per_wg(int nw) { return nw * 32; }
+// tokens per LDS tile of the context kernel
+inline int ctx_tile_tokens(int nw) { return nw >= 4 ? 64 : 32; }
+
+}  // namespace gr

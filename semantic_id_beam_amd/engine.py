@@ -1,0 +1,109 @@
+"""BeamEngine: holds the torch-owned device buffers of one gr_engine and forwards to the C ABI.
+
+PyTorch only allocates device memory and supplies the stream; every step of
+the decode runs in libgr_beam.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import _lib as G
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(arr: np.ndarray, device="cuda"):
+    """numpy -> torch device tensor; uint16 arrays are bf16 bit patterns and become bfloat16."""
+    torch = _torch()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+class BeamEngine:
+    """One engine: model tables, item trie, workspace.
+
+    tok_q/tok_k/tok_v/w_sid are numpy arrays (bf16 bit patterns as uint16, or float32) or torch
+    device tensors; items is a [n_items][n_levels] integer array."""
+
+    def __init__(self, *, tok_q, tok_k, tok_v, w_sid, items, n_layers: int, n_q_heads: int, n_kv_heads: int,
+                 head_dim: int, dtype: str = "bf16", norm: str = "valid", max_requests: int = 1,
+                 max_beam_width: int = 256, max_ctx_tokens: int = 0, max_splits: int = 0,
+                 debug_attn: bool = False, device="cuda"):
+        torch = _torch()
+        self.device = device
+        self.dtype = dtype
+        conv = (lambda x: x) if isinstance(tok_q, torch.Tensor) else (lambda x: to_device(x, device))
+        self.tok_q, self.tok_k, self.tok_v = conv(tok_q), conv(tok_k), conv(tok_v)
+        self.w_sid = conv(np.asarray(w_sid, dtype=np.float32)) if not isinstance(w_sid, torch.Tensor) else w_sid
+        self.n_layers, self.n_levels, self.V = int(n_layers), int(self.w_sid.shape[0]), int(self.w_sid.shape[2])
+        self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
+        desc = G.gr_model_desc(self.n_layers, n_q_heads, n_kv_heads, head_dim, self.n_levels, self.V,
+                               G.GR_DTYPE_BF16 if dtype == "bf16" else G.GR_DTYPE_F32,
+                               G.GR_NORM_VALID if norm == "valid" else G.GR_NORM_FULL,
+                               self.tok_q.data_ptr(), self.tok_k.data_ptr(), self.tok_v.data_ptr(),
+                               self.w_sid.data_ptr())
+        opts = G.gr_engine_opts(max_requests, max_beam_width, max_ctx_tokens, max_splits,
+                                G.GR_ENGINE_DEBUG_ATTN if debug_attn else 0)
+        self.max_beam_width = max_beam_width
+        self.eng = G.gr_engine_create(desc, np.asarray(items), opts)
+        self.ws_bytes = G.gr_engine_workspace_bytes(self.eng)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        G.gr_engine_bind_workspace(self.eng, self.ws, self.ws_bytes, self.stream)
+        self._keep = {}
+
+    @property
+    def stream(self) -> int:
+        return _torch().cuda.current_stream().cuda_stream
+
+    def trie_nodes(self, level: int) -> int:
+        return G.gr_engine_trie_nodes(self.eng, level)
+
+    def load(self, rid: int, k, v, q_last, beam_width: int, adopt: bool = False, ctx_len: int | None = None):
+        """k, v: torch device tensors, [L][N][Hkv][d] (copy) or native K / V^T (adopt)."""
+        n = ctx_len if ctx_len is not None else (k.shape[1] if not adopt else None)
+        if n is None:
+            raise ValueError("ctx_len is required with adopt=True")
+        G.gr_ctx_kv_load(self.eng, rid, n, beam_width, k, v, q_last, G.GR_LOAD_ADOPT if adopt else 0, self.stream)
+        if adopt:
+            self._keep[rid] = (k, v)
+
+    def step(self, rids):
+        G.gr_beam_step(self.eng, rids, self.stream)
+
+    def beams(self, rid: int):
+        return G.gr_beams_get(self.eng, rid, self.max_beam_width, self.n_levels, self.stream)
+
+    def reset(self, rid: int):
+        G.gr_request_reset(self.eng, rid, self.stream)
+
+    def release(self, rid: int):
+        G.gr_request_release(self.eng, rid)
+        self._keep.pop(rid, None)
+
+    def state(self, rid: int):
+        return G.gr_debug_beam_state(self.eng, rid, self.max_beam_width, self.n_levels, self.stream)
+
+    def path(self, rid: int):
+        return G.gr_debug_beam_path(self.eng, rid, self.max_beam_width, self.n_levels, self.stream)
+
+    def hidden(self, rid: int):
+        return G.gr_debug_hidden(self.eng, rid, self.max_beam_width, self.Hq * self.d, self.V, self.stream)
+
+    def attn_out(self, rid: int, layer: int):
+        return G.gr_debug_attn_out(self.eng, rid, layer, self.max_beam_width, self.Hq, self.d, self.stream)
+
+    def close(self):
+        if getattr(self, "eng", None):
+            G.gr_engine_destroy(self.eng)
+            self.eng = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

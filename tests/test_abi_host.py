@@ -1,0 +1,143 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and validates arguments and builds the item trie without touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import semantic_id_beam_amd as sib
+from semantic_id_beam_amd import _lib as G
+from tests.oracle_inputs import dict_trie
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced on the host
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "gr_beam.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gr_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = sib.lib()
+    decl = _declared()
+    assert len(decl) >= 17
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(G.EXPORTS) == decl
+
+
+def _desc(L=1, Hq=4, Hkv=2, d=64, lv=3, V=16, dtype=G.GR_DTYPE_F32, norm=G.GR_NORM_VALID):
+    return G.gr_model_desc(L, Hq, Hkv, d, lv, V, dtype, norm, FAKE, FAKE, FAKE, FAKE)
+
+
+def _opts(R=1, W=4, ctx=64, S=0, flags=0):
+    return G.gr_engine_opts(R, W, ctx, S, flags)
+
+
+def _items(V=16, lv=3, n=200, seed=0):
+    rng = np.random.default_rng(seed)
+    flat = rng.choice(V ** lv, n, replace=False)
+    return np.stack(np.unravel_index(flat, (V,) * lv), axis=1).astype(np.int32)
+
+
+def test_create_and_trie_counts_match_dict_trie():
+    items = _items()
+    eng = G.gr_engine_create(_desc(), items, _opts())
+    t = dict_trie(items)
+    for s in range(4):
+        expect = len({tuple(x[:s]) for x in items.tolist()})
+        assert G.gr_engine_trie_nodes(eng, s) == expect
+    assert G.gr_engine_workspace_bytes(eng) > 0
+    assert len(t[()]) == G.gr_engine_trie_nodes(eng, 1)
+    G.gr_engine_destroy(eng)
+
+
+def test_duplicate_items_are_merged():
+    items = _items()
+    eng = G.gr_engine_create(_desc(), np.concatenate([items, items[:50]]), _opts())
+    assert G.gr_engine_trie_nodes(eng, 3) == 200
+    G.gr_engine_destroy(eng)
+
+
+def test_workspace_grows_with_slots_and_pool():
+    items = _items()
+    a = G.gr_engine_create(_desc(), items, _opts(R=1, ctx=64))
+    b = G.gr_engine_create(_desc(), items, _opts(R=4, ctx=64))
+    c = G.gr_engine_create(_desc(), items, _opts(R=1, ctx=6400))
+    wa, wb, wc = (G.gr_engine_workspace_bytes(x) for x in (a, b, c))
+    assert wb > wa and wc > wa
+    # pool: 2 (K,V) * L * Hkv * d * 4 bytes per padded token
+    assert wc - wa == pytest.approx((6400 - 64) * 2 * 1 * 2 * 64 * 4, abs=1024)
+    for x in (a, b, c):
+        G.gr_engine_destroy(x)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d=96), dict(Hq=3, Hkv=2), dict(lv=0), dict(lv=9), dict(V=1), dict(V=2000), dict(dtype=7), dict(norm=3),
+    dict(Hq=18, Hkv=1),
+])
+def test_create_rejects_bad_model(bad):
+    with pytest.raises(G.GrError) as ei:
+        G.gr_engine_create(_desc(**bad), _items(), _opts())
+    assert ei.value.status in (G.GR_E_INVALID_ARG, G.GR_E_UNSUPPORTED)
+    assert G.gr_last_error()
+
+
+@pytest.mark.parametrize("bad", [dict(R=0), dict(W=0), dict(W=2000), dict(ctx=-1), dict(S=100)])
+def test_create_rejects_bad_opts(bad):
+    with pytest.raises(G.GrError):
+        G.gr_engine_create(_desc(), _items(), _opts(**bad))
+
+
+def test_create_rejects_bad_items():
+    it = _items()
+    it[5, 1] = 16
+    with pytest.raises(G.GrError) as ei:
+        G.gr_engine_create(_desc(), it, _opts())
+    assert "code" in str(ei.value)
+    with pytest.raises(G.GrError):
+        G.gr_engine_create(_desc(), np.zeros((0, 3), np.int32), _opts())
+
+
+def test_codebook_overflow_is_unsupported():
+    with pytest.raises(G.GrError) as ei:
+        G.gr_engine_create(_desc(lv=8, V=1024), np.zeros((1, 8), np.int32), _opts())
+    assert ei.value.status == G.GR_E_UNSUPPORTED
+
+
+def test_calls_before_bind_are_bad_state():
+    eng = G.gr_engine_create(_desc(), _items(), _opts())
+    with pytest.raises(G.GrError) as ei:
+        G.gr_ctx_kv_load(eng, 1, 10, 4, FAKE, FAKE, FAKE)
+    assert ei.value.status == G.GR_E_BAD_STATE
+    with pytest.raises(G.GrError) as ei:
+        G.gr_beam_step(eng, [1])
+    assert ei.value.status == G.GR_E_BAD_STATE
+    with pytest.raises(G.GrError) as ei:
+        G.gr_request_release(eng, 1)
+    assert ei.value.status == G.GR_E_NOT_FOUND
+    with pytest.raises(G.GrError):
+        G.gr_engine_bind_workspace(eng, FAKE + 1, 1 << 40)       # misaligned
+    with pytest.raises(G.GrError) as ei:
+        G.gr_engine_bind_workspace(eng, FAKE, 16)                # too small
+    assert ei.value.status == G.GR_E_OUT_OF_MEMORY
+    G.gr_engine_destroy(eng)
+
+
+def test_padded_len_and_topk_args():
+    assert G.gr_ctx_padded_len(1) == 64 and G.gr_ctx_padded_len(64) == 64 and G.gr_ctx_padded_len(65) == 128
+    assert G.gr_ctx_padded_len(0) == 0
+    for args in [(0, 16, 4), (4, 16, 0), (4, 16, 2000), (1 << 14, 1 << 13, 4)]:
+        with pytest.raises(G.GrError):
+            G.gr_topk_select(FAKE, *args, FAKE, FAKE, FAKE)
+
+
+def test_null_engine_is_rejected():
+    L = sib.lib()
+    assert L.gr_beam_step(None, None, 0, None) == G.GR_E_INVALID_ARG
+    assert L.gr_engine_destroy(None) == G.GR_OK
+    assert L.gr_engine_workspace_bytes(None) == 0

@@ -1,0 +1,137 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_harness import (SCORE_TOL, TeacherForced, attn_tol, gpu_beams, load_request, make_engine, rel_err_rows,
+                               save_report)
+from tests.oracle_inputs import model_for, prefixes_for, request_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_checked(cfg, r=0, norm="valid", debug_attn=True, max_splits=0, check_attn_every=1, adopt=False):
+    """Full decode of request r, each step checked against the oracle (teacher-forced)."""
+    eng = make_engine(cfg, max_requests=1, debug_attn=debug_attn, norm=norm, max_splits=max_splits)
+    rid = load_request(eng, cfg, r, rid=7, adopt=adopt)
+    tf = TeacherForced(cfg, r, norm)
+    prev = [()]
+    tol = attn_tol(cfg)
+    attn_errs = []
+    for s in range(cfg.n_levels):
+        eng.step([rid])
+        after = gpu_beams(eng, rid)
+        if debug_attn and s % check_attn_every == 0:
+            for l in range(cfg.n_layers):
+                got = eng.attn_out(rid, l)
+                assert got.shape[0] == len(prev)
+                ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev])
+                err = rel_err_rows(got, ref)
+                attn_errs.append(err)
+                assert err <= tol, f"step {s} layer {l}: attention rel err {err}"
+            h, lg = eng.hidden(rid)
+            href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev])
+            assert rel_err_rows(h, href) <= tol * max(1, cfg.n_layers)
+        tf.check_step(prev, after)
+        prev = after[0]
+    codes, scores = eng.beams(rid)
+    assert [tuple(c) for c in codes.tolist()] == prev
+    eng.close()
+    save_report(cfg, tf.report, attn_err=max(attn_errs) if attn_errs else None)
+    return tf.report, codes, scores
+
+
+def test_tiny_f32_decode_matches_oracle():
+    cfg = synth.get_config("tiny_f32")
+    rep, codes, scores = _decode_checked(cfg)
+    # free-running comparison: the oracle's own search gives the same final beams
+    hist = oracle.beam_search(request_for(cfg, 0), model_for(cfg), prefixes_for(cfg), 4, "valid")
+    assert [p for p, _, _ in hist[-1]] == [tuple(c) for c in codes.tolist()]
+    np.testing.assert_allclose(scores, [s for _, s, _ in hist[-1]], atol=1e-5)
+    assert all(x["exact_order"] for x in rep)
+
+
+def test_tiny_f32_full_vocab_normalisation():
+    cfg = synth.get_config("tiny_f32")
+    _decode_checked(cfg, norm="full")
+
+
+def test_tiny_f32_wide_beam_is_exhaustive():
+    cfg = synth.get_config("tiny_f32", beam_width=256)
+    rep, codes, scores = _decode_checked(cfg, debug_attn=False)
+    assert codes.shape[0] == cfg.n_items
+
+
+def test_ctx1k_bf16_decode_matches_oracle():
+    cfg = synth.get_config("ctx1k_beam256")
+    rep, codes, scores = _decode_checked(cfg)
+    assert codes.shape[0] == 256
+    print("ctx1k report", rep)
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 129, 700])
+def test_ragged_context_lengths(N):
+    cfg = synth.get_config("ctx1k_beam256", ctx_len=N, beam_width=8, n_items=20000)
+    _decode_checked(cfg)
+
+
+@pytest.mark.parametrize("W", [1, 3, 33, 64, 100])
+def test_beam_widths(W):
+    cfg = synth.get_config("ctx1k_beam256", ctx_len=300, beam_width=W, n_items=20000)
+    _decode_checked(cfg)
+
+
+def test_two_layers_bf16_split_invariance():
+    cfg = synth.get_config("ctx1k_beam256", n_layers=2, ctx_len=1500, beam_width=32, n_items=20000)
+    _, c1, s1 = _decode_checked(cfg, max_splits=1)
+    _, c2, s2 = _decode_checked(cfg, max_splits=16)
+    # each run is within SCORE_TOL of the oracle, so they differ by at most twice that
+    np.testing.assert_allclose(s1, s2, atol=2 * SCORE_TOL)
+
+
+def test_adopt_equals_copy_bit_identical():
+    cfg = synth.get_config("ctx1k_beam256", ctx_len=500, beam_width=64, n_items=20000)
+    _, c1, s1 = _decode_checked(cfg, debug_attn=False)
+    _, c2, s2 = _decode_checked(cfg, debug_attn=False, adopt=True)
+    assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+def test_determinism_bit_identical():
+    cfg = synth.get_config("ctx1k_beam256", ctx_len=777, beam_width=128, n_items=50000)
+    eng = make_engine(cfg, max_requests=1)
+    rid = load_request(eng, cfg, 0)
+    runs = []
+    for _ in range(2):
+        eng.reset(rid)
+        for _ in range(cfg.n_levels):
+            eng.step([rid])
+        runs.append(eng.beams(rid))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+
+
+def test_topk_select_bit_exact_vs_lexsort():
+    import torch
+    import semantic_id_beam_amd as sib
+    rng = np.random.default_rng(5)
+    for n_rows, V, k in [(1, 16, 4), (7, 33, 20), (256, 256, 256), (30, 256, 30), (3, 1000, 1024), (64, 5, 300)]:
+        x = np.round(rng.standard_normal((n_rows, V)) * 2, 2).astype(np.float32)   # many ties
+        x[rng.random((n_rows, V)) < 0.3] = -np.inf
+        x[0, 0] = 0.0
+        x[-1, -1] = -0.0
+        cand = torch.from_numpy(x).cuda()
+        of = torch.empty(k, dtype=torch.int32, device="cuda")
+        os_ = torch.empty(k, dtype=torch.float32, device="cuda")
+        no = torch.zeros(1, dtype=torch.int32, device="cuda")
+        sib._lib.gr_topk_select(cand, n_rows, V, k, of, os_, no, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        flat = np.arange(n_rows * V)
+        xs = x.reshape(-1)
+        fin = np.isfinite(xs)
+        order = flat[fin][np.lexsort((flat[fin], -xs[fin].astype(np.float64)))]
+        kk = min(k, order.shape[0])
+        assert int(no.item()) == kk
+        assert of.cpu().numpy()[:kk].tolist() == order[:kk].tolist()
+        exp = xs[order[:kk]] + np.float32(0.0)          # -0 is reported as +0
+        assert np.array_equal(os_.cpu().numpy()[:kk].view(np.uint32), exp.view(np.uint32))
