@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the semantic-ID beam-decode step on one MI355X.
+
+A bench "step" is one full beam decode of the whole request batch: every
+request is rewound to its root beam, then n_levels gr_beam_step calls run over
+all requests (context attention, BeamKV gather + merge, codebook logits,
+trie-masked log-softmax, top-K and BeamPath update per level), then
+gr_beams_get returns every surviving beam of every request.  The ContextKV is
+resident in HBM before the timed region (it stands in for prefill, which is
+not part of the step).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "beam-decode req/s + step µs at ctx 5000, beam 256; % MFMA peak, HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def workload_text(cfg, shapes):
+    ns = sorted({n for n, _ in shapes})
+    ws = sorted({w for _, w in shapes})
+    return (f"{cfg.name}: {cfg.n_requests} requests x {cfg.n_layers} layers, ctx "
+            f"{ns[0] if len(ns) == 1 else f'{ns[0]}..{ns[-1]}'}, beam {ws[0] if len(ws) == 1 else ws}, "
+            f"{cfg.n_levels} levels x {cfg.codebook} codes, {cfg.n_items} items ({cfg.item_dist}), "
+            f"{cfg.n_q_heads} q / {cfg.n_kv_heads} kv heads, head_dim {cfg.head_dim}, {cfg.dtype}")
+
+
+def cpu_baseline(cfg, n_beams: int):
+    """The oracle, timed on the host cores on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from tests.oracle_inputs import model_for, prefixes_for, request_for
+
+    model, ps = model_for(cfg), prefixes_for(cfg)
+    req = request_for(cfg, 0)
+    for l in range(cfg.n_layers):          # regenerate + decode the context before timing
+        req.ctx(l)
+    root = ps.valid_codes(())
+    beams = [((int(c),), 0.0) for c in root[:n_beams]]
+    t0 = time.perf_counter()
+    oracle.step_candidates(req, model, ps, beams, "valid")
+    dt = time.perf_counter() - t0
+    per_beam = dt / len(beams)
+    # beam evaluations of one full decode of one request: 1 at level 0, then n_s per level
+    W = cfg.beam_width if isinstance(cfg.beam_width, int) else max(cfg.beam_width)
+    evals, n = 1, 1
+    for s in range(1, cfg.n_levels):
+        n = min(W, len(ps.levels[s]), n * cfg.codebook)
+        evals += n
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {
+        "value": 1.0 / (evals * per_beam),
+        "unit": "req/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"request 0, level 1, {len(beams)} beams, each recomputed as an independent "
+                   f"{cfg.n_layers}-layer sequence of ctx+1 tokens with logits, log-softmax and candidates "
+                   f"({dt:.1f} s); extrapolated to {evals} beam evaluations per request decode"),
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=None, help="workload name (default: the ctx-5000 beam-256 headline)")
+    ap.add_argument("--cpu-beams", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by request with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from synth.configs import HEADLINE
+    from semantic_id_beam_amd import _lib as G
+    from tests.engine_inputs import make_engine, request_tensors
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.get_config(args.config or HEADLINE)
+    shapes = synth.request_shapes(cfg)
+    R, lv = cfg.n_requests, cfg.n_levels
+    log("workload", workload_text(cfg, shapes))
+    t = time.time()
+    eng = make_engine(cfg, max_requests=R)
+    log(f"engine ready ({eng.ws_bytes / 2**30:.2f} GiB workspace, {time.time() - t:.1f} s)")
+    rids = list(range(R))
+    t = time.time()
+    for r in rids:
+        k, v, q = request_tensors(cfg, r)
+        eng.load(r, k, v, q, shapes[r][1])
+        del k, v, q
+        if r % 8 == 7 or r == R - 1:
+            torch.cuda.synchronize()
+            log(f"loaded {r + 1}/{R} contexts ({time.time() - t:.1f} s)")
+    torch.cuda.empty_cache()
+
+    # live beams per level, measured once
+    n_live = np.zeros((R, lv), dtype=np.int64)
+    for r in rids:
+        eng.reset(r)
+    n_live[:, 0] = 1
+    for s in range(lv):
+        eng.step(rids)
+        if s + 1 < lv:
+            for r in rids:
+                n_live[r, s + 1] = eng.state(r)["n"]
+    for r in rids:
+        eng.beams(r)
+
+    def decode_all():
+        for r in rids:
+            eng.reset(r)
+        for _ in range(lv):
+            eng.step(rids)
+        return [eng.beams(r) for r in rids]
+
+    for i in range(args.warmup):
+        decode_all()
+    torch.cuda.synchronize()
+    G.gr_engine_profile_reset(eng.eng)
+    G.gr_engine_set_profiling(eng.eng, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decode_all()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    G.gr_engine_set_profiling(eng.eng, False)
+    elapsed = t1 - t0
+    log(f"timed {args.steps} decodes in {elapsed:.3f} s")
+
+    # ---- per-kernel times (HIP events on the decode stream, timed region only)
+    prof = {}
+    for kind, name in [(G.GR_PROF_CTX_ATTN, "ctx_attn"), (G.GR_PROF_BEAM_MERGE, "beam_merge"),
+                       (G.GR_PROF_LOGITS, "logits"), (G.GR_PROF_TOPK, "topk"), (G.GR_PROF_STEP, "step")]:
+        prof[name] = {s: G.gr_engine_profile_read(eng.eng, kind, s) for s in range(lv)}
+
+    d, g, Hkv = cfg.head_dim, cfg.group, cfg.n_kv_heads
+    N = np.array([n for n, _ in shapes], dtype=np.float64)
+    el = 2 if cfg.dtype == "bf16" else 4
+
+    def ctx_flops(s):      # one launch = one layer, all requests
+        return float(np.sum(Hkv * n_live[:, s] * g * N * d * 4))
+
+    def ctx_bytes(s):      # K and V read once, queries read, one fp32 output row per (beam, head)
+        return float(np.sum(Hkv * N * d * 2 * el + Hkv * n_live[:, s] * g * d * (el + 4)))
+
+    levels_mfma = [s for s in range(lv) if np.all(n_live[:, s] * g >= 64)]
+    ms_m = sum(prof["ctx_attn"][s][0] for s in levels_mfma)
+    n_m = sum(prof["ctx_attn"][s][1] for s in levels_mfma)
+    fl_m = sum(ctx_flops(s) * prof["ctx_attn"][s][1] for s in levels_mfma)
+    achieved_tf = fl_m / (ms_m * 1e-3) / 1e12 if ms_m > 0 else 0.0
+    ms_0, n_0 = prof["ctx_attn"][0]
+    achieved_gbs0 = ctx_bytes(0) * n_0 / (ms_0 * 1e-3) / 1e9 if ms_0 > 0 else 0.0
+    step_us = {f"level{s}": 1e3 * prof["step"][s][0] / max(prof["step"][s][1], 1) for s in range(lv)}
+
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "kernel": "k_ctx_attn_bf16 (levels %s)" % levels_mfma, "launches": int(n_m),
+        "avg_launch_us": round(1e3 * ms_m / max(n_m, 1), 2),
+        "algorithmic_per_launch": f"{ctx_flops(levels_mfma[-1]) / 1e9:.2f} GFLOP" if levels_mfma else None,
+    }
+    kernels = {
+        "ctx_attn_level0": {"bound": "hbm", "achieved_GBs": round(achieved_gbs0, 1), "peak_GBs": PEAK_HBM_GBS,
+                            "frac": round(achieved_gbs0 / PEAK_HBM_GBS, 4),
+                            "avg_launch_us": round(1e3 * ms_0 / max(n_0, 1), 2),
+                            "algorithmic_MB_per_launch": round(ctx_bytes(0) / 1e6, 2)},
+    }
+    for name in ("beam_merge", "logits", "topk"):
+        tot = sum(prof[name][s][0] for s in range(lv))
+        n = sum(prof[name][s][1] for s in range(lv))
+        kernels[name] = {"avg_launch_us": round(1e3 * tot / max(n, 1), 2), "ms_per_decode": round(tot / args.steps, 3)}
+    kernels["ctx_attn"] = {"ms_per_decode": round(sum(prof["ctx_attn"][s][0] for s in range(lv)) / args.steps, 3)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(R * args.steps / elapsed, 2),
+        "unit": "req/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload_text(cfg, shapes), "requests": R, "layers": cfg.n_layers,
+                   "ctx_len": cfg.ctx_len, "beam_width": cfg.beam_width, "levels": lv,
+                   "codebook": cfg.codebook, "items": cfg.n_items, "live_beams_per_level": n_live[0].tolist()},
+        "step_us": {k: round(v, 1) for k, v in step_us.items()},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    eng.close()
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on {args.cpu_beams} beams ...")
+        cb = cpu_baseline(cfg, args.cpu_beams)
+        log(f"oracle sample took {cb.pop('seconds'):.1f} s")
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

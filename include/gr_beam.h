@@ -201,6 +201,32 @@ const char *gr_last_error(void);
 gr_status gr_topk_select(const float *cand, int32_t n_rows, int32_t V, int32_t k, int32_t *out_flat,
                          float *out_score, int32_t *n_out, void *stream);
 
+/* ---- profiling ------------------------------------------------------------ */
+
+/* Kernel kinds reported by gr_engine_profile_read. */
+typedef enum {
+  GR_PROF_CTX_ATTN = 0,   /* shared-context attention (one launch per layer) */
+  GR_PROF_BEAM_MERGE = 1, /* BeamKV append + beam attention + merge (one per layer) */
+  GR_PROF_LOGITS = 2,     /* codebook logits (one per step) */
+  GR_PROF_TOPK = 3,       /* constrained log-softmax + top-K + BeamPath update (one per step) */
+  GR_PROF_STEP = 4        /* a whole gr_beam_step, first launch to last */
+} gr_prof_kind;
+
+/* When enabled, gr_beam_step brackets each launch with HIP events recorded on
+ * its stream (a bounded pool; it waits for old events when the pool is full).
+ * Buckets are keyed by kind and by the decode level of the step (0..n_levels-1;
+ * steps whose requests are at different levels go to bucket n_levels). */
+gr_status gr_engine_set_profiling(gr_engine *eng, int32_t enable);
+
+/* Waits for every recorded event, folds the elapsed times into the buckets and
+ * returns one bucket: total milliseconds and number of launches.  level = -1
+ * sums every level. */
+gr_status gr_engine_profile_read(gr_engine *eng, int32_t kind, int32_t level, double *total_ms,
+                                 int64_t *launches);
+
+/* Clears every bucket (pending events are folded first). */
+gr_status gr_engine_profile_reset(gr_engine *eng);
+
 /* ---- inspection (tests and debugging; each synchronises `stream`) --------- */
 
 /* Current beam set B_s of a request: *level = s, *n = n_s; parent host [cap]

@@ -71,6 +71,14 @@ struct gr_engine {
   std::unordered_map<int64_t, Req> reqs;
   std::vector<int> free_slots;
 
+  // profiling: event pairs around launches, folded into [kind][level] buckets
+  bool prof = false;
+  std::vector<hipEvent_t> prof_ev;  // 2 per record
+  struct ProfRec { int kind, level; };
+  std::vector<ProfRec> prof_pending;
+  double prof_ms[5][gr::kMaxLevels + 1] = {};
+  int64_t prof_n[5][gr::kMaxLevels + 1] = {};
+
   std::vector<gr::StepReq *> pinned;
   std::vector<hipEvent_t> events;
   std::vector<bool> event_used;
@@ -83,6 +91,45 @@ gr_status check_dev(gr_engine *e, hipError_t err, const char *what) {
   if (err == hipSuccess) return GR_OK;
   e->poisoned = true;
   return fail(GR_E_DEVICE, std::string(what) + ": " + hipGetErrorString(err));
+}
+
+constexpr int kProfPool = 1024;  // event pairs
+
+gr_status prof_fold(gr_engine *e) {
+  for (size_t i = 0; i < e->prof_pending.size(); ++i) {
+    hipEvent_t a = e->prof_ev[2 * i], b = e->prof_ev[2 * i + 1];
+    gr_status r = check_dev(e, hipEventSynchronize(b), "profiling event");
+    if (r != GR_OK) return r;
+    float ms = 0.f;
+    if ((r = check_dev(e, hipEventElapsedTime(&ms, a, b), "profiling event")) != GR_OK) return r;
+    const auto &p = e->prof_pending[i];
+    e->prof_ms[p.kind][p.level] += ms;
+    e->prof_n[p.kind][p.level] += 1;
+  }
+  e->prof_pending.clear();
+  return GR_OK;
+}
+
+// Makes room for `count` records before a step starts (every pending record is
+// complete then, so folding is safe).  Returns false when profiling is off or
+// the step needs more records than the pool holds.
+bool prof_reserve(gr_engine *e, int count) {
+  if (!e->prof || count > kProfPool) return false;
+  if ((int)e->prof_pending.size() + count > kProfPool && prof_fold(e) != GR_OK) return false;
+  return true;
+}
+
+// Records the start event of a profiled launch; returns the record index or -1.
+int prof_begin(gr_engine *e, bool on, int kind, int level, hipStream_t st) {
+  if (!on) return -1;
+  const int i = (int)e->prof_pending.size();
+  if (hipEventRecord(e->prof_ev[2 * i], st) != hipSuccess) return -1;
+  e->prof_pending.push_back({kind, level});
+  return i;
+}
+
+void prof_end(gr_engine *e, int i, hipStream_t st) {
+  if (i >= 0) (void)hipEventRecord(e->prof_ev[2 * i + 1], st);
 }
 
 gr_status build_trie(gr_engine *e, const gr_item_set *items) {
@@ -325,6 +372,9 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
     if ((r = check_dev(e, hipEventCreateWithFlags(&e->events[i], hipEventDisableTiming), "event")) != GR_OK)
       return r;
   }
+  e->prof_ev.assign(2 * kProfPool, nullptr);
+  for (auto &ev : e->prof_ev)
+    if ((r = check_dev(e, hipEventCreate(&ev), "event")) != GR_OK) return r;
   gr::Dev &dv = e->dev;
   dv.dm = e->dm;
   dv.sl = e->sl;
@@ -345,6 +395,8 @@ gr_status gr_engine_destroy(gr_engine *e) {
   if (e->bound) {
     (void)hipDeviceSynchronize();
     for (auto &ev : e->events)
+      if (ev) (void)hipEventDestroy(ev);
+    for (auto &ev : e->prof_ev)
       if (ev) (void)hipEventDestroy(ev);
     for (auto *p : e->pinned)
       if (p) (void)hipHostFree(p);
@@ -500,14 +552,28 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     return r;
   if ((r = check_dev(e, hipEventRecord(e->events[slot_i], st), "descriptor ring")) != GR_OK) return r;
   e->event_used[slot_i] = true;
+  int plevel = rs[0]->level;
+  for (auto *R : rs)
+    if (R->level != plevel) plevel = d.levels;
+  const bool pon = prof_reserve(e, 2 * d.L + 3);
+  const int pstep = prof_begin(e, pon, GR_PROF_STEP, plevel, st);
   for (int l = 0; l < d.L; ++l) {
+    int pi = prof_begin(e, pon, GR_PROF_CTX_ATTN, plevel, st);
     if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw, n, l, wg_ctx, nw, st), "context attention")) != GR_OK)
       return r;
+    prof_end(e, pi, st);
+    pi = prof_begin(e, pon, GR_PROF_BEAM_MERGE, plevel, st);
     if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st), "beam attention/merge")) != GR_OK)
       return r;
+    prof_end(e, pi, st);
   }
+  int pi = prof_begin(e, pon, GR_PROF_LOGITS, plevel, st);
   if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st), "logits")) != GR_OK) return r;
+  prof_end(e, pi, st);
+  pi = prof_begin(e, pon, GR_PROF_TOPK, plevel, st);
   if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, st), "top-k")) != GR_OK) return r;
+  prof_end(e, pi, st);
+  prof_end(e, pstep, st);
   for (auto *R : rs) {
     const int s = R->level;
     int64_t nb = std::min<int64_t>((int64_t)R->W, (int64_t)R->n_bound * d.V);
@@ -651,6 +717,40 @@ gr_status gr_debug_attn_out(gr_engine *e, int64_t rid, int32_t layer, int32_t ca
       return r;
     if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
   }
+  return GR_OK;
+}
+
+gr_status gr_engine_set_profiling(gr_engine *e, int32_t enable) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  e->prof = enable != 0;
+  return GR_OK;
+}
+
+gr_status gr_engine_profile_read(gr_engine *e, int32_t kind, int32_t level, double *total_ms, int64_t *launches) {
+  if (!e || !total_ms || !launches) return fail(GR_E_INVALID_ARG, "null argument");
+  if (kind < 0 || kind > GR_PROF_STEP) return fail(GR_E_INVALID_ARG, "unknown profile kind");
+  if (level < -1 || level > e->dm.levels) return fail(GR_E_INVALID_ARG, "level out of range");
+  gr_status r = prof_fold(e);
+  if (r != GR_OK) return r;
+  double ms = 0.0;
+  int64_t n = 0;
+  for (int l = 0; l <= e->dm.levels; ++l)
+    if (level < 0 || l == level) {
+      ms += e->prof_ms[kind][l];
+      n += e->prof_n[kind][l];
+    }
+  *total_ms = ms;
+  *launches = n;
+  return GR_OK;
+}
+
+gr_status gr_engine_profile_reset(gr_engine *e) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  gr_status r = prof_fold(e);
+  if (r != GR_OK) return r;
+  std::memset(e->prof_ms, 0, sizeof(e->prof_ms));
+  std::memset(e->prof_n, 0, sizeof(e->prof_n));
   return GR_OK;
 }
 
