@@ -77,7 +77,8 @@ typedef enum {
 typedef struct gr_engine gr_engine; /* opaque */
 
 /* Model description.  Limits: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
- * 1 <= n_levels <= 8; 2 <= codebook_size <= 1024 and codebook_size**n_levels < 2**62.
+ * n_q_heads * head_dim a multiple of 128; 1 <= n_levels <= 8; 2 <= codebook_size <= 1024
+ * and codebook_size**n_levels < 2**62.
  * All table pointers are device memory owned by the caller and must outlive
  * the engine.  Element type of tok_q/tok_k/tok_v is `dtype` (bf16 = raw 16-bit
  * patterns, f32 = float). */
@@ -107,7 +108,8 @@ typedef struct {
   int64_t max_ctx_tokens; /* context tokens the engine's own pool holds for copy loads
                              (each request takes its length rounded up to 64);
                              0 = only GR_LOAD_ADOPT loads */
-  int32_t max_splits;     /* split-K partial slots per (request, kv head); 0 = 16 */
+  int32_t max_splits;     /* split-K partial slots per (request, kv head) at full beam width
+                             (narrower steps may use proportionally more); 0 = 4 */
   uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN */
 } gr_engine_opts;
 

@@ -204,6 +204,7 @@ void layout(gr_engine *e) {
   s.q_last = take((size_t)d.L * d.Hq * d.d * el);
   s.h = take(W * d.Hq * d.d * 4);
   s.logits = take(W * d.V * 4);
+  s.logits_part = take((size_t)gr::kLogitsKS * W * d.V * 4);
   s.cand = take(W * d.V * 4);
   s.part_o = take((size_t)d.Hkv * d.S_max * W * d.g * d.d * 4);
   s.part_ml = take((size_t)d.Hkv * d.S_max * W * d.g * 8);
@@ -288,6 +289,8 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   if (m->n_q_heads / m->n_kv_heads > gr::kMaxGroup)
     return fail(GR_E_UNSUPPORTED, "more than 8 query heads per kv head");
   if (m->head_dim != 64 && m->head_dim != 128) return fail(GR_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if ((m->n_q_heads * m->head_dim) % (32 * gr::kLogitsKS) != 0)
+    return fail(GR_E_UNSUPPORTED, "n_q_heads * head_dim must be a multiple of 128");
   if (m->n_levels < 1 || m->n_levels > gr::kMaxLevels) return fail(GR_E_INVALID_ARG, "n_levels must be in [1, 8]");
   if (m->codebook_size < 2 || m->codebook_size > 1024) return fail(GR_E_INVALID_ARG, "codebook_size must be in [2, 1024]");
   {
@@ -309,7 +312,7 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   gr_engine *e = new gr_engine();
   e->model = *m;
   e->opts = *o;
-  if (e->opts.max_splits == 0) e->opts.max_splits = 16;
+  if (e->opts.max_splits == 0) e->opts.max_splits = 4;
   e->elem = m->dtype == GR_DTYPE_BF16 ? 2 : 4;
   gr::Dims &d = e->dm;
   d.L = m->n_layers;
@@ -500,20 +503,21 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   if (d.dtype == 1) {
     for (auto *R : rs) {
       const int rows = R->n_bound * d.g;
-      nw = std::max(nw, rows <= 32 ? 1 : rows <= 64 ? 2 : 4);
+      nw = std::max(nw, rows <= 32 ? 1 : rows <= 64 ? 2 : rows <= 128 ? 4 : 8);
     }
   }
+  if (d.d == 64) nw = std::min(nw, 4);  // the head_dim-64 kernels have at most 4 waves
   const int rows_wg = gr::ctx_rows_per_wg(nw);
   int64_t units = 0;
   for (auto *R : rs) units += (int64_t)d.Hkv * ceil_div((int64_t)R->n_bound * d.g, rows_wg);
-  const int want = d.dtype == 1 ? (nw == 4 ? 512 : nw == 2 ? 1024 : 2048) : 256;
+  const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? 1024 : 2048) : 256;  // workgroups per launch
   const int slot_i = e->ring;
   e->ring = (e->ring + 1) % kRing;
   if (e->event_used[slot_i]) {
     if ((r = check_dev(e, hipEventSynchronize(e->events[slot_i]), "descriptor ring")) != GR_OK) return r;
   }
   gr::StepReq *hw = e->pinned[slot_i];
-  int wg_ctx = 0, wg_merge = 0, wg_logits = 0;
+  int wg_ctx = 0, wg_merge = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0;
   for (int i = 0; i < n; ++i) {
     gr_engine::Req *R = rs[(size_t)i];
     gr::StepReq &w = hw[i];
@@ -528,23 +532,30 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     w.W = R->W;
     w.n_bound = R->n_bound;
     const int rows = R->n_bound * d.g;
+    w.rows_b = rows;
     w.row_blocks = ceil_div(rows, rows_wg);
+    // split-K: enough workgroups to fill the chip, at least two tiles per range, and
+    // no more partial rows than the slot holds (Hkv * S_max * W_max * g)
     int S = (int)std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1));
-    S = std::min(S, d.S_max);
     S = std::min(S, std::max(1, ceil_div(R->N, 2 * gr::kTileTok)));
+    S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)d.S_max * d.W_max * d.g / rows));
+    S = std::min(S, 256);
     int tps = (int)align_up((size_t)ceil_div(R->N, S), gr::kTileTok);
     S = ceil_div(R->N, tps);
     w.splits = S;
     w.tps = tps;
     w.wg_ctx = wg_ctx;
     if (d.dtype == 1)
-      wg_ctx += d.Hkv * w.row_blocks * S;
+      wg_ctx += (int)align_up((size_t)d.Hkv * S, 8) * w.row_blocks;  // multiple of 8: XCD-aware order
     else
       wg_ctx += ceil_div((int64_t)d.Hkv * rows * S, 4);
     w.wg_merge = wg_merge;
-    wg_merge += ceil_div((int64_t)R->n_bound * d.Hkv, 4);
+    wg_merge += R->n_bound;
     w.wg_logits = wg_logits;
-    wg_logits += ceil_div(R->n_bound, 32) * ceil_div(d.V, 64);
+    wg_logits += ceil_div(R->n_bound, 64) * ceil_div(d.V, 64) * gr::kLogitsKS;
+    w.wg_lsm = wg_lsm;
+    wg_lsm += ceil_div(R->n_bound, 4);
+    max_cand = std::max(max_cand, R->n_bound * d.V);
   }
   gr::StepReq *dw = (gr::StepReq *)(e->ws + e->off_work + e->work_bytes * (size_t)slot_i);
   if ((r = check_dev(e, hipMemcpyAsync(dw, hw, sizeof(gr::StepReq) * (size_t)n, hipMemcpyHostToDevice, st),
@@ -571,7 +582,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st), "logits")) != GR_OK) return r;
   prof_end(e, pi, st);
   pi = prof_begin(e, pon, GR_PROF_TOPK, plevel, st);
-  if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, st), "top-k")) != GR_OK) return r;
+  if ((r = check_dev(e, gr::launch_lsm(e->dev, dw, n, wg_lsm, st), "log-softmax")) != GR_OK) return r;
+  if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, max_cand, st), "top-k")) != GR_OK) return r;
   prof_end(e, pi, st);
   prof_end(e, pstep, st);
   for (auto *R : rs) {

@@ -12,10 +12,13 @@ constexpr int kMaxGroup = 8;      // query heads per kv head handled by the beam
 constexpr int kTileTok = 64;      // context tokens per split granule / padding unit
 constexpr int kTopkThreads = 1024;
 constexpr int kMaxBeam = 1024;
+constexpr int kLogitsKS = 4;          // split of the hidden dimension in the logits GEMM
+constexpr int kSelectCPT = 64;        // candidates per thread kept in registers by the selection
+constexpr int kTieCap = 1024;         // candidates sharing the cut bin that the fast selection sorts
 
 struct Dims {
   int L, Hq, Hkv, g, d, levels, V, MW;  // MW = 32-bit words per trie mask row
-  int W_max, S_max;
+  int W_max, S_max;        // S_max: split slots at full beam width (part_rows = Hkv*S_max*W_max*g)
   int dtype;   // 0 f32, 1 bf16
   int norm;    // 0 valid, 1 full
   float scale_log2;  // log2(e) / sqrt(d)
@@ -29,9 +32,10 @@ struct SlotLayout {
   size_t q_last;              // [L][Hq][d] elem
   size_t h;                   // [W_max][Hq*d] f32
   size_t logits;              // [W_max][V] f32
+  size_t logits_part;         // [kLogitsKS][W_max][V] f32 split-K partial sums
   size_t cand;                // [W_max][V] f32
-  size_t part_o;              // [Hkv][S_max][W_max*g][d] f32
-  size_t part_ml;             // [Hkv][S_max][W_max*g] float2 (m in log2 units, l)
+  size_t part_o;              // [part_rows][d] f32, row ((h*splits + sp)*rows_b + row)
+  size_t part_ml;             // [part_rows] float2 (m in log2 units, l)
   size_t codes[2];            // [W_max][levels] i32   (double-buffered by level parity)
   size_t score[2];            // [W_max] f32
   size_t node[2];             // [W_max] i32  trie node of the beam's prefix
@@ -60,10 +64,10 @@ struct StepReq {
   int N, Np;
   int slot, level, W;
   int n_bound;          // upper bound of n_s known on the host (device holds the exact n_s)
+  int rows_b;           // n_bound * g: row stride of the split-K partials
   int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
   int row_blocks;       // context-attention row blocks per kv head
-  int wg_ctx, wg_merge, wg_logits;  // first workgroup of this request in each launch
-  int pad_;
+  int wg_ctx, wg_merge, wg_logits, wg_lsm;  // first workgroup of this request in each launch
 };
 
 // ---- launchers (gr_kernels.hip) ------------------------------------------
@@ -73,7 +77,9 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                              hipStream_t st);
 hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st);
-hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st);
+hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st);
+// max_cand: largest n_bound*V of the step (selects the register-resident or the streaming variant)
+hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st);
 hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N,
                            int Np, int Hkv, int d, int elem_bytes, hipStream_t st);
 hipError_t launch_init_slot(const Dev &dev, int slot, hipStream_t st);

@@ -10,17 +10,19 @@
 // published online-normaliser / flash-decoding method (Milakov & Gimelshein
 // 2018); it is not on the pages.
 //
-// Kernels per decode step (one launch sequence per layer, then logits/top-K):
+// Kernels per decode step (one launch pair per layer, then three per step):
 //   k_ctx_attn_bf16   shared-context attention on MFMA, one (request, kv head,
 //                     row block, token range) per workgroup -> (m, l, o) partials
 //   k_ctx_attn_f32    the same on the vector ALU for float32 models
 //   k_beam_merge      appends the new token to BeamKV, attends over the beam's
 //                     own tokens found through BeamPath, merges with the
 //                     context partials and adds the layer output to h
-//   k_logits          h @ w_sid[level]
-//   k_topk            trie-masked log-softmax, top-K over beams x codes,
-//                     BeamPath update
+//   k_logits          h @ w_sid[level], fp32 MFMA, split over the hidden dim
+//   k_lsm             sums the split logits, trie-masked log-softmax, candidates
+//   k_select          top-K over beams x codes, BeamPath update
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "gr_internal.h"
 
@@ -29,12 +31,26 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+#define GR_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Loads and stores through the global address space (global_load/store, counted by
+// vmcnt only, so waiting for LDS never waits for a prefetch in flight).  T is a scalar or
+// a clang vector type.
+template <typename T>
+__device__ __forceinline__ T gld(const void *p) {
+  return *(const GR_GLOBAL T *)(p);
+}
+template <typename T>
+__device__ __forceinline__ void gst(void *p, const T &v) {
+  *(GR_GLOBAL T *)(p) = v;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-__device__ __forceinline__ float ldf(const float *p, size_t i) { return p[i]; }
-__device__ __forceinline__ float ldf(const uint16_t *p, size_t i) { return bf2f(p[i]); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -46,20 +62,18 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
-__device__ __forceinline__ int wave_isum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Workgroup -> request: reqs[] is ordered by its first-workgroup field.
+// Workgroup -> request: reqs[] is ordered by each first-workgroup field.
 template <int FIELD>
 __device__ __forceinline__ int find_req(const StepReq *reqs, int n, int bid) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int first = FIELD == 0 ? reqs[mid].wg_ctx : FIELD == 1 ? reqs[mid].wg_merge : reqs[mid].wg_logits;
+    const int first = FIELD == 0   ? reqs[mid].wg_ctx
+                      : FIELD == 1 ? reqs[mid].wg_merge
+                      : FIELD == 2 ? reqs[mid].wg_logits
+                                   : reqs[mid].wg_lsm;
     if (first <= bid) lo = mid; else hi = mid - 1;
   }
   return lo;
@@ -69,16 +83,16 @@ __device__ __forceinline__ uint8_t *slot_base(const Dev &dev, int slot) {
   return dev.slots + (size_t)slot * dev.sl.slot_bytes;
 }
 
-// Row r of a 64-token K tile is stored at LDS row swap23(r) (bits 2 and 3 exchanged).
-// Lane l of the QK^T MFMA then reads LDS row l%32 and holds token swap23(l%32), which
-// makes the score accumulator's layout equal to the PV MFMA's B-operand layout with
-// 8 consecutive tokens per lane (no cross-lane shuffle between the two MFMAs).
+// Row r of a K tile is stored at LDS row swap23(r) (bits 2 and 3 exchanged).  Lane l of
+// the QK^T MFMA then reads LDS row l%32 and holds token swap23(l%32), which makes the
+// score accumulator's register layout equal to the PV MFMA's B-operand layout with 8
+// consecutive tokens per lane: no cross-lane shuffle between the two MFMAs.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // --------------------------------------------------------------------------------------
 // Shared-context attention, bf16 K/V, fp32 accumulate, MFMA 32x32x16.
 //
-// Workgroup = NW waves; wave w owns 32 query rows (beam j = row / g, head hq = h*g + row % g)
+// Workgroup = NW waves; wave w owns 32 query rows (beam j = row / g, head hq = h*g + row%g)
 // of one kv head h of one request; all waves share the K/V tiles of one token range,
 // double-buffered through LDS.  Per 32-token sub-tile and wave:
 //   S^T[32 tok][32 q] = K_tile * Q^T     (D/16 MFMAs, A = K from LDS, B = Q in registers)
@@ -86,9 +100,13 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 //   column's max grows by more than 8, so p <= 256; exact since m and l share it)
 //   O^T[D][32 q] += V^T_tile * P^T        (D/32 * 2 MFMAs, A = V^T from LDS, B = P as bf16)
 // Output: unnormalised o, the reference max m (log2 units) and l per row and token range.
+//
+// Workgroup order: the row blocks of one (kv head, token range) pair get workgroup ids
+// 8 apart, so (with workgroups dealt round-robin over the 8 XCDs) they run on one XCD
+// and share its L2 for the K/V tiles.
 template <int D, int NW, int TT>
-__global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepReq *__restrict__ reqs,
-                                                           int n_reqs, int layer) {
+__device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                              int layer) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int NSUB = TT / 32;
@@ -104,13 +122,14 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepRe
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
   const int ri = find_req<0>(reqs, n_reqs, blockIdx.x);
   const StepReq R = reqs[ri];
-  int local = blockIdx.x - R.wg_ctx;
-  const int sp = local % R.splits;
-  local /= R.splits;
-  const int rb = local % R.row_blocks;
-  const int h = local / R.row_blocks;
-
   const Dims &dm = dev.dm;
+  const int local = blockIdx.x - R.wg_ctx;
+  const int rest = local >> 3;
+  const int rb = rest % R.row_blocks;
+  const int pidx = (rest / R.row_blocks) * 8 + (local & 7);
+  if (pidx >= dm.Hkv * R.splits) return;  // padding workgroup
+  const int h = pidx / R.splits, sp = pidx % R.splits;
+
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
@@ -139,14 +158,8 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepRe
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (row_ok) {
-        const uint4 u = *(const uint4 *)(qsrc + kb * 16 + 8 * hh);
-        qf[kb] = __builtin_bit_cast(bf16x8_t, u);
-      } else {
-        qf[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-      }
-    }
+    for (int kb = 0; kb < KB; ++kb)
+      qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
   }
 
   const int t0 = sp * R.tps;
@@ -155,17 +168,17 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepRe
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
 
-  uint4 rk[KPT], rv[VPT];
+  u32x4_t rk[KPT], rv[VPT];
   auto gload = [&](int tb) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NT, r = c / (D / 8), cc = c % (D / 8);
-      rk[i] = *(const uint4 *)(gK + (size_t)(tb + r) * D + cc * 8);
+      rk[i] = gld<u32x4_t>(gK + (size_t)(tb + r) * D + cc * 8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + i * NT, dd = c / (TT / 8), tc = c % (TT / 8);
-      rv[i] = *(const uint4 *)(gV + (size_t)dd * R.Np + tb + tc * 8);
+      rv[i] = gld<u32x4_t>(gV + (size_t)dd * R.Np + tb + tc * 8);
     }
   };
   auto lstore = [&](int buf) {
@@ -187,6 +200,54 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepRe
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
 
+  // one 32-token sub-tile; MASK handles the tokens >= t1 of the last tile
+  auto subtile = [&](int buf, int sub, int tb, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8_t kf = sK[buf][sub * 32 + (lane & 31)][kb * 2 + hh];
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], sacc, 0, 0, 0);
+    }
+    // accumulator register i of lane (col q, half hh) holds token tb + sub*32 + 16*(i/8) + 8*hh + (i%8)
+    if constexpr (MASK) {
+      const int tbase = tb + sub * 32 + 8 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (tbase + 16 * (i >> 3) + (i & 7) >= t1) sacc[i] = kNegInf;
+    }
+    float mx = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxs = mx * c2;
+    if (__ballot(mxs > M + 8.f) != 0ull) {
+      const float Mn = fmaxf(M, mxs);
+      const float f = fast_exp2(M - Mn);
+      l *= f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= f;
+      M = Mn;
+    }
+    float ls = 0.f;
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sacc[i], c2, -M));
+      ls += p;
+      pf[i >> 3][i & 7] = (__bf16)p;
+    }
+    l += ls;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const bf16x8_t vf = sV[buf][db * 32 + (lane & 31)][sub * 4 + pp * 2 + hh];
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pp], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
   gload(t0);
   lstore(0);
   __syncthreads();
@@ -195,52 +256,13 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepRe
     const int tb = t0 + it * TT;
     if (it + 1 < ntiles) gload(tb + TT);
     if (wave_active) {
+      if (tb + TT <= t1) {
 #pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub) {
-        if (tb + sub * 32 >= t1) break;
-        f32x16_t sacc = f32x16_t{};
+        for (int sub = 0; sub < NSUB; ++sub) subtile(buf, sub, tb, std::false_type{});
+      } else {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8_t kf = sK[buf][sub * 32 + (lane & 31)][kb * 2 + hh];
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], sacc, 0, 0, 0);
-        }
-        // accumulator register i of lane (col q, half hh) holds token
-        // tb + sub*32 + 16*(i/8) + 8*hh + (i%8)
-        float mx = kNegInf;
-        const int tbase = tb + sub * 32 + 8 * hh;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = tbase + 16 * (i >> 3) + (i & 7);
-          if (tok >= t1) sacc[i] = kNegInf;
-          mx = fmaxf(mx, sacc[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mxs = mx * c2;
-        if (__ballot(mxs > M + 8.f) != 0ull) {
-          const float Mn = fmaxf(M, mxs);
-          const float f = fast_exp2(M - Mn);
-          l *= f;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= f;
-          M = Mn;
-        }
-        float ls = 0.f;
-        bf16x8_t pf[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[i], c2, -M));
-          ls += p;
-          pf[i >> 3][i & 7] = (__bf16)p;
-        }
-        l += ls;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const bf16x8_t vf = sV[buf][db * 32 + (lane & 31)][sub * 4 + pp * 2 + hh];
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pp], oacc[db], 0, 0, 0);
-          }
-        }
+        for (int sub = 0; sub < NSUB; ++sub)
+          if (tb + sub * 32 < t1) subtile(buf, sub, tb, std::true_type{});
       }
     }
     if (it + 1 < ntiles) lstore(buf ^ 1);
@@ -249,19 +271,32 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16(Dev dev, const StepRe
 
   const float ltot = l + __shfl_xor(l, 32);
   if (wave_active && row_ok) {
-    const size_t prow = ((size_t)h * dm.S_max + sp) * ((size_t)dm.W_max * dm.g) + q_row;
-    if (hh == 0) ((float2 *)(slot + dev.sl.part_ml))[prow] = make_float2(M, ltot);
+    const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
+    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml) + prow, f32x2_t{M, ltot});
     float *po = (float *)(slot + dev.sl.part_o) + prow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = db * 32 + 8 * a + 4 * hh;
-        *(float4 *)(po + d0) =
-            make_float4(oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]);
+        gst<f32x4_t>(po + d0, f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
+                                      oacc[db][4 * a + 3]});
       }
     }
   }
+}
+
+// Wide steps (many query rows): two waves per SIMD so one wave's softmax overlaps the
+// other's MFMAs.  Narrow steps are HBM-bound and keep their staging registers instead.
+template <int D, int NW, int TT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_ctx_attn_bf16(
+    Dev dev, const StepReq *__restrict__ reqs, int n_reqs, int layer) {
+  ctx_attn_body<D, NW, TT>(dev, reqs, n_reqs, layer);
+}
+template <int D, int NW, int TT>
+__global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16_narrow(Dev dev, const StepReq *__restrict__ reqs,
+                                                                  int n_reqs, int layer) {
+  ctx_attn_body<D, NW, TT>(dev, reqs, n_reqs, layer);
 }
 
 // --------------------------------------------------------------------------------------
@@ -277,11 +312,10 @@ __global__ __launch_bounds__(256) void k_ctx_attn_f32(Dev dev, const StepReq *__
   const StepReq R = reqs[ri];
   const Dims &dm = dev.dm;
   int lw = (blockIdx.x - R.wg_ctx) * 4 + w;
-  const int rows_b = R.n_bound * dm.g;
   const int sp = lw % R.splits;
   lw /= R.splits;
-  const int q_row = lw % rows_b;
-  const int h = lw / rows_b;
+  const int q_row = lw % R.rows_b;
+  const int h = lw / R.rows_b;
   if (h >= dm.Hkv) return;
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
@@ -324,7 +358,7 @@ __global__ __launch_bounds__(256) void k_ctx_attn_f32(Dev dev, const StepReq *__
       for (int e = 0; e < DPL; ++e) o[e] = fmaf(pt, gV[(size_t)(lane + 64 * e) * R.Np + tb + tt], o[e]);
     }
   }
-  const size_t prow = ((size_t)h * dm.S_max + sp) * ((size_t)dm.W_max * dm.g) + q_row;
+  const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
   if (lane == 0) ((float2 *)(slot + dev.sl.part_ml))[prow] = make_float2(M, l);
   float *po = (float *)(slot + dev.sl.part_o) + prow * D;
 #pragma unroll
@@ -332,203 +366,304 @@ __global__ __launch_bounds__(256) void k_ctx_attn_f32(Dev dev, const StepReq *__
 }
 
 // --------------------------------------------------------------------------------------
-// BeamKV append + beam-token attention + split-K merge + layer sum.  One wave per
-// (request, beam j, kv head h), covering the g query heads of h.
+// 8 consecutive elements of a bf16 or f32 row: raw copy and float conversion.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const uint16_t *p) { u = gld<u32x4_t>(p); }
+  __device__ __forceinline__ void store(uint16_t *p) const { gst<u32x4_t>(p, u); }
+  __device__ __forceinline__ void to_float(float *f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = gld<f32x4_t>(p);
+    b = gld<f32x4_t>(p + 4);
+  }
+  __device__ __forceinline__ void store(float *p) const {
+    gst<f32x4_t>(p, a);
+    gst<f32x4_t>(p + 4, b);
+  }
+  __device__ __forceinline__ void to_float(float *f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = a[i];
+      f[4 + i] = b[i];
+    }
+  }
+};
+
+// BeamKV append + beam-token attention + split-K merge + layer sum.  One workgroup per
+// (request, beam j); thread = (query head hq, 8-feature chunk), C8 = D/8 threads per head.
 //   step s >= 1: the new token's k/v (code c_{s-1}) are written to BeamKV slot
 //   [layer][s-1][j]; the beam's earlier tokens t < s-1 are read from BeamKV slot
-//   anc[j][t] (BeamPath) -- the beam never re-reads the tables for them.
+//   anc[j][t] (BeamPath) -- never re-looked-up from the tables.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void k_beam_merge(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                     int layer) {
-  constexpr int DPL = D / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int C8 = D / 8;
+  const int tid = threadIdx.x;
   const int ri = find_req<1>(reqs, n_reqs, blockIdx.x);
   const StepReq R = reqs[ri];
   const Dims &dm = dev.dm;
-  const int lw = (blockIdx.x - R.wg_merge) * 4 + w;
-  const int j = lw / dm.Hkv, h = lw % dm.Hkv;
+  const int j = blockIdx.x - R.wg_merge;
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
   if (j >= n_live) return;
   const int g = dm.g, lvl = dm.levels;
   const float c2 = dm.scale_log2;
-
-  float Mb[kMaxGroup], lb[kMaxGroup], ob[kMaxGroup][DPL];
-#pragma unroll
-  for (int gi = 0; gi < kMaxGroup; ++gi) {
-    Mb[gi] = kNegInf;
-    lb[gi] = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) ob[gi][e] = 0.f;
-  }
-
-  if (s > 0) {
-    const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
-    const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
-    const int code = codes[j * lvl + (s - 1)];
-    const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code;
-    const T *kn = (const T *)dev.tok_k + (trow * dm.Hkv + h) * D;
-    const T *vn = (const T *)dev.tok_v + (trow * dm.Hkv + h) * D;
-    T *bk = (T *)(slot + dev.sl.beamkv_k);
-    T *bv = (T *)(slot + dev.sl.beamkv_v);
-    const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
-    const size_t lvstride = (size_t)dm.W_max * wstride;
-    const size_t base_l = (size_t)layer * (lvl - 1) * lvstride;
-    // append: BeamKV[layer][s-1][j][h]
-    T kraw[DPL], vraw[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      kraw[e] = kn[lane * DPL + e];
-      vraw[e] = vn[lane * DPL + e];
-      bk[base_l + (size_t)(s - 1) * lvstride + j * wstride + (size_t)h * D + lane * DPL + e] = kraw[e];
-      bv[base_l + (size_t)(s - 1) * lvstride + j * wstride + (size_t)h * D + lane * DPL + e] = vraw[e];
-    }
-    float q[kMaxGroup][DPL];
-#pragma unroll
-    for (int gi = 0; gi < kMaxGroup; ++gi) {
-      if (gi < g) {
-        const T *qp = (const T *)dev.tok_q + (trow * dm.Hq + h * g + gi) * D;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) q[gi][e] = ldf(qp, lane * DPL + e);
-      }
-    }
-    for (int t = 0; t < s; ++t) {
-      float kt[DPL], vt[DPL];
-      if (t == s - 1) {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          kt[e] = ldf(kraw, e);
-          vt[e] = ldf(vraw, e);
-        }
-      } else {
-        const int a = anc[j * lvl + t];
-        const size_t off = base_l + (size_t)t * lvstride + a * wstride + (size_t)h * D + lane * DPL;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          kt[e] = ldf(bk, off + e);
-          vt[e] = ldf(bv, off + e);
-        }
-      }
-#pragma unroll
-      for (int gi = 0; gi < kMaxGroup; ++gi) {
-        if (gi < g) {
-          float acc = 0.f;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc = fmaf(q[gi][e], kt[e], acc);
-          const float u = wave_sum(acc) * c2;
-          const float Mn = fmaxf(Mb[gi], u);
-          const float f = fast_exp2(Mb[gi] - Mn);
-          const float p = fast_exp2(u - Mn);
-          lb[gi] = lb[gi] * f + p;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) ob[gi][e] = fmaf(p, vt[e], ob[gi][e] * f);
-          Mb[gi] = Mn;
-        }
-      }
-    }
-  }
-
+  const int nchunk = dm.Hq * C8;  // a multiple of C8: a head's lanes are all active or all idle
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml);
   const float *po = (const float *)(slot + dev.sl.part_o);
   float *hbuf = (float *)(slot + dev.sl.h);
-  const size_t wg = (size_t)dm.W_max * g;
+  for (int e = tid; e < nchunk; e += 256) {
+    const int hq = e / C8, c8 = e % C8, kv = hq / g, gi = hq % g;
+    float Mb = kNegInf, lb = 0.f, ob[8];
 #pragma unroll
-  for (int gi = 0; gi < kMaxGroup; ++gi) {
-    if (gi >= g) break;
+    for (int i = 0; i < 8; ++i) ob[i] = 0.f;
+    if (s > 0) {
+      const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
+      const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
+      const int code = codes[j * lvl + (s - 1)];
+      const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code;
+      float q[8];
+      {
+        Raw8<T> rq;
+        rq.load((const T *)dev.tok_q + (trow * dm.Hq + hq) * D + c8 * 8);
+        rq.to_float(q);
+      }
+      Raw8<T> kn, vn;
+      kn.load((const T *)dev.tok_k + (trow * dm.Hkv + kv) * D + c8 * 8);
+      vn.load((const T *)dev.tok_v + (trow * dm.Hkv + kv) * D + c8 * 8);
+      T *bk = (T *)(slot + dev.sl.beamkv_k);
+      T *bv = (T *)(slot + dev.sl.beamkv_v);
+      const size_t wstride = (size_t)dm.Hkv * D;       // one BeamKV slot
+      const size_t lvstride = (size_t)dm.W_max * wstride;
+      const size_t base = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D + c8 * 8;
+      if (gi == 0) {
+        kn.store(bk + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
+        vn.store(bv + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
+      }
+      for (int t = 0; t < s; ++t) {
+        float kt[8], vt[8];
+        if (t == s - 1) {
+          kn.to_float(kt);
+          vn.to_float(vt);
+        } else {
+          const size_t off = base + (size_t)t * lvstride + (size_t)anc[j * lvl + t] * wstride;
+          Raw8<T> a, b;
+          a.load(bk + off);
+          b.load(bv + off);
+          a.to_float(kt);
+          b.to_float(vt);
+        }
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf(q[i], kt[i], dot);
+#pragma unroll
+        for (int o = C8 / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+        const float u = dot * c2;
+        const float Mn = fmaxf(Mb, u);
+        const float f = fast_exp2(Mb - Mn);
+        const float p = fast_exp2(u - Mn);
+        lb = lb * f + p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ob[i] = fmaf(p, vt[i], ob[i] * f);
+        Mb = Mn;
+      }
+    }
     const int row = j * g + gi;
-    float Ms = Mb[gi];
-    for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, pml[((size_t)h * dm.S_max + sp) * wg + row].x);
-    const float fb = fast_exp2(Mb[gi] - Ms);
-    float Ls = lb[gi] * fb, O[DPL];
+    const size_t pbase = (size_t)kv * R.splits * R.rows_b + row;
+    float Ms = Mb;
+    for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
+    const float fb = fast_exp2(Mb - Ms);
+    float Ls = lb * fb, O[8];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) O[e] = ob[gi][e] * fb;
+    for (int i = 0; i < 8; ++i) O[i] = ob[i] * fb;
     for (int sp = 0; sp < R.splits; ++sp) {
-      const size_t prow = ((size_t)h * dm.S_max + sp) * wg + row;
-      const float2 ml = pml[prow];
-      const float f = fast_exp2(ml.x - Ms);
-      Ls = fmaf(ml.y, f, Ls);
+      const size_t prow = pbase + (size_t)sp * R.rows_b;
+      const f32x2_t ml = gld<f32x2_t>(pml + prow);
+      const float f = fast_exp2(ml[0] - Ms);
+      Ls = fmaf(ml[1], f, Ls);
+      const f32x4_t a = gld<f32x4_t>(po + prow * D + c8 * 8);
+      const f32x4_t b = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) O[e] = fmaf(po[prow * D + lane * DPL + e], f, O[e]);
+      for (int i = 0; i < 4; ++i) {
+        O[i] = fmaf(a[i], f, O[i]);
+        O[4 + i] = fmaf(b[i], f, O[4 + i]);
+      }
     }
     const float inv = 1.f / Ls;
-    const int hq = h * g + gi;
-    float *hr = hbuf + ((size_t)j * dm.Hq + hq) * D + lane * DPL;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float o = O[e] * inv;
-      hr[e] = (layer == 0 ? 0.f : hr[e]) + o;
-      if (dm.debug_attn)
-        ((float *)(slot + dev.sl.dbg_attn))[(((size_t)layer * dm.W_max + j) * dm.Hq + hq) * D + lane * DPL + e] = o;
+    for (int i = 0; i < 8; ++i) O[i] *= inv;
+    float *hr = hbuf + ((size_t)j * dm.Hq + hq) * D + c8 * 8;
+    f32x4_t a = f32x4_t{O[0], O[1], O[2], O[3]}, b = f32x4_t{O[4], O[5], O[6], O[7]};
+    if (dm.debug_attn) {
+      float *dg = (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j) * dm.Hq + hq) * D + c8 * 8;
+      gst<f32x4_t>(dg, a);
+      gst<f32x4_t>(dg + 4, b);
     }
+    if (layer > 0) {
+      a += gld<f32x4_t>(hr);
+      b += gld<f32x4_t>(hr + 4);
+    }
+    gst<f32x4_t>(hr, a);
+    gst<f32x4_t>(hr + 4, b);
   }
 }
 
 // --------------------------------------------------------------------------------------
-// logits[j][c] = h[j] . w_sid[level][:, c]   (fp32, LDS-tiled, 32 rows x 64 codes per workgroup)
+// logits_part[ks][j][c] = sum over the ks-th quarter of the hidden dim of h[j][k] w_sid[level][k][c]
+// fp32 MFMA 32x32x2 (exact fp32 products, fp32 accumulate).  Workgroup: 64 beams x 64 codes
+// of one hidden-dim slice; wave w owns the 32x32 block (w/2, w%2).  Tiles of 32 hidden
+// features are double-buffered through LDS.
 __global__ __launch_bounds__(256) void k_logits(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ri = find_req<2>(reqs, n_reqs, blockIdx.x);
   const StepReq R = reqs[ri];
   const Dims &dm = dev.dm;
-  const int V = dm.V, H = dm.Hq * dm.d;
+  const int V = dm.V, H = dm.Hq * dm.d, KSL = H / kLogitsKS;
   const int nct = (V + 63) / 64;
-  const int local = blockIdx.x - R.wg_logits;
-  const int rt = local / nct, ct = local % nct;
+  int local = blockIdx.x - R.wg_logits;
+  const int ks = local % kLogitsKS;
+  local /= kLogitsKS;
+  const int ct = local % nct, rt = local / nct;
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
-  const int row0 = rt * 32;
+  const int row0 = rt * 64;
   if (row0 >= n_live) return;
   const float *hb = (const float *)(slot + dev.sl.h);
-  const float *W = dev.w_sid + (size_t)s * H * V;
-  float *out = (float *)(slot + dev.sl.logits);
-  __shared__ float sh[32][33];
-  __shared__ float sw[32][65];
-  const int ty = tid >> 4, tx = tid & 15;
-  float acc[2][4] = {};
-  for (int k0 = 0; k0 < H; k0 += 32) {
+  const float *Wt = dev.w_sid + (size_t)s * H * V;
+  const int k0 = ks * KSL;
+  __shared__ float sA[2][64][33];
+  __shared__ float sB[2][32][65];
+  float ra[8], rbv[8];
+  const int ar = tid >> 2, ak = (tid & 3) * 8;   // A tile: 64 rows x 32 features
+  const int br = tid >> 3, bc = (tid & 7) * 8;   // B tile: 32 features x 64 codes
+  auto gl = [&](int kc) {
+    if (row0 + ar < n_live) {
+      const f32x4_t a = gld<f32x4_t>(hb + (size_t)(row0 + ar) * H + k0 + kc + ak);
+      const f32x4_t b = gld<f32x4_t>(hb + (size_t)(row0 + ar) * H + k0 + kc + ak + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * 256, r = e >> 5, kk = e & 31;
-      sh[r][kk] = (row0 + r < n_live) ? hb[(size_t)(row0 + r) * H + k0 + kk] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = a[i];
+        ra[4 + i] = b[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ra[i] = 0.f;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int e = tid + i * 256, kk = e >> 6, cc = e & 63;
-      const int col = ct * 64 + cc;
-      sw[kk][cc] = col < V ? W[(size_t)(k0 + kk) * V + col] : 0.f;
+      const int col = ct * 64 + bc + i;
+      rbv[i] = col < V ? gld<float>(Wt + (size_t)(k0 + kc + br) * V + col) : 0.f;
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      const float a0 = sh[ty * 2][kk], a1 = sh[ty * 2 + 1][kk];
+  };
+  auto ls = [&](int buf) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float b = sw[kk][tx * 4 + c];
-        acc[0][c] = fmaf(a0, b, acc[0][c]);
-        acc[1][c] = fmaf(a1, b, acc[1][c]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      sA[buf][ar][ak + i] = ra[i];
+      sB[buf][br][bc + i] = rbv[i];
     }
+  };
+  const int rbk = w >> 1, cbk = w & 1;
+  f32x16_t acc = f32x16_t{};
+  gl(0);
+  ls(0);
+  __syncthreads();
+  for (int kc = 0, it = 0; kc < KSL; kc += 32, ++it) {
+    const int buf = it & 1;
+    if (kc + 32 < KSL) gl(kc + 32);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float a = sA[buf][rbk * 32 + (lane & 31)][kk * 2 + (lane >> 5)];
+      const float b = sB[buf][kk * 2 + (lane >> 5)][cbk * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    if (kc + 32 < KSL) ls(buf ^ 1);
     __syncthreads();
   }
+  float *out = (float *)(slot + dev.sl.logits_part) + (size_t)ks * dm.W_max * V;
+  const int col = ct * 64 + cbk * 32 + (lane & 31);
+  if (col < V) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = row0 + ty * 2 + r;
-    if (row >= n_live) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int col = ct * 64 + tx * 4 + c;
-      if (col < V) out[(size_t)row * V + col] = acc[r][c];
+    for (int i = 0; i < 16; ++i) {
+      const int row = row0 + rbk * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (row < n_live) gst<float>(out + (size_t)row * V + col, acc[i]);
     }
   }
 }
 
 // --------------------------------------------------------------------------------------
-// Top-K over a candidate array by radix select on unique 64-bit keys
+// Per beam row (one wave): logits = sum of the split partials (fixed order), trie mask of
+// the beam's node, log-softmax over the valid codes (or the whole codebook), candidates
+// cand[j][c] = score_j + logit - lse (valid) or -inf.
+__global__ __launch_bounds__(256) void k_lsm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  constexpr int MAXC = 1024 / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ri = find_req<3>(reqs, n_reqs, blockIdx.x);
+  const StepReq R = reqs[ri];
+  const Dims &dm = dev.dm;
+  const int j = (blockIdx.x - R.wg_lsm) * 4 + w;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int s = R.level, cur = s & 1, V = dm.V;
+  const int n = ((const int *)(slot + dev.sl.n_live))[cur];
+  if (j >= n) return;
+  const uint32_t *mrow = dev.trie_mask + (dev.trie_off[s] + ((const int *)(slot + dev.sl.node[cur]))[j]) * dm.MW;
+  const float sc = ((const float *)(slot + dev.sl.score[cur]))[j];
+  const float *part = (const float *)(slot + dev.sl.logits_part);
+  const size_t pstride = (size_t)dm.W_max * V;
+  float *logits = (float *)(slot + dev.sl.logits);
+  float *cand = (float *)(slot + dev.sl.cand);
+  float xs[MAXC];
+  uint32_t vbits = 0;
+  float mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < MAXC; ++e) {
+    const int c = lane + 64 * e;
+    xs[e] = 0.f;
+    if (c < V) {
+      float x = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kLogitsKS; ++ks) x += gld<float>(part + ks * pstride + (size_t)j * V + c);
+      xs[e] = x;
+      gst<float>(logits + (size_t)j * V + c, x);
+      const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
+      vbits |= (uint32_t)valid << e;
+      if (dm.norm == 1 || valid) mx = fmaxf(mx, x);
+    }
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < MAXC; ++e) {
+    const int c = lane + 64 * e;
+    if (c < V && (dm.norm == 1 || ((vbits >> e) & 1u))) sum += expf(xs[e] - mx);
+  }
+  sum = wave_sum(sum);
+  const float lse = mx + logf(sum);
+#pragma unroll
+  for (int e = 0; e < MAXC; ++e) {
+    const int c = lane + 64 * e;
+    if (c < V) gst<float>(cand + (size_t)j * V + c, ((vbits >> e) & 1u) ? sc + (xs[e] - lse) : kNegInf);
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// Top-K selection over a candidate array.  Keys are unique 64-bit integers
 //   key = order-preserving bits of the score << 32 | (0xFFFFFFFF - flat index)
-// so "larger key" = higher score, then lower flat index.  The k largest keys are
-// gathered and bitonic-sorted in LDS (descending).  1024 threads.
+// so "larger key" = higher score, then lower flat index; -0 is folded to +0 first.
 __device__ __forceinline__ uint32_t f2ord(float v) {
   const uint32_t b = __float_as_uint(v);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -537,22 +672,177 @@ __device__ __forceinline__ float ord2f(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 __device__ __forceinline__ uint64_t cand_key(float v, uint32_t i) {
-  const float vc = (v == 0.f) ? 0.f : v;  // -0 ranks equal to +0
+  const float vc = (v == 0.f) ? 0.f : v;
   return ((uint64_t)f2ord(vc) << 32) | (uint64_t)(0xFFFFFFFFu - i);
 }
 
+constexpr int kBins = 2048;
+
 struct SelectSmem {
   uint64_t sel[kMaxBeam];
-  int hist[256];
+  uint64_t tie[kTieCap];
+  int hist[kBins];
+  int wsum[kTopkThreads / 64];
+  int wcnt[kTopkThreads / 64];
+  float wmin[kTopkThreads / 64], wmax[kTopkThreads / 64];
   uint64_t prefix;
-  int need;
-  int cnt;
-  int nvalid;
+  int need, cut, cnt, tcnt, nvalid;
+  float vmin, vmax;
 };
 
-// Leaves the k largest keys, sorted descending, in sm.sel[0..k).  k >= 1, k <= kMaxBeam,
-// and at least k finite candidates.
-__device__ void wg_select(const float *__restrict__ cand, int n_total, int k, SelectSmem &sm) {
+__device__ void select_stream(const float *__restrict__ cand, int n_total, int k, SelectSmem &sm);
+
+// Sorts a[0..n) descending (n <= 1024); every thread of the workgroup calls it.
+__device__ void block_sort_desc(uint64_t *a, int n) {
+  const int tid = threadIdx.x;
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = n + tid; i < P; i += kTopkThreads) a[i] = 0ull;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += kTopkThreads) {
+        const int pj = i ^ stride;
+        if (pj > i) {
+          const uint64_t x = a[i], y = a[pj];
+          const bool desc = (i & size) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[pj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ void scan_cands(const float *__restrict__ cand, int total, SelectSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int cnt = 0;
+  float mn = __builtin_inff(), mx = kNegInf;
+  for (int i = tid; i < total; i += kTopkThreads) {
+    const float v = gld<float>(cand + i);
+    if (v > kNegInf) {
+      ++cnt;
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cnt += __shfl_xor(cnt, o);
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) {
+    sm.wcnt[w] = cnt;
+    sm.wmin[w] = mn;
+    sm.wmax[w] = mx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0;
+    float a = __builtin_inff(), b = kNegInf;
+    for (int i = 0; i < kTopkThreads / 64; ++i) {
+      c += sm.wcnt[i];
+      a = fminf(a, sm.wmin[i]);
+      b = fmaxf(b, sm.wmax[i]);
+    }
+    sm.nvalid = c;
+    sm.vmin = a;
+    sm.vmax = b;
+  }
+  __syncthreads();
+}
+
+// Top-k of cand[0..total), total <= 1024*CPT (second pass; scan_cands ran first and
+// 1 <= k <= nvalid).  A monotone linear map of the score to 2048 bins is kept in
+// registers as packed 16-bit bin numbers; the histogram picks the bin holding the k-th
+// best, everything above it is selected, and the candidates of that bin are ordered
+// exactly by their 64-bit keys.  When the cut bin holds more than kTieCap candidates
+// the exact streaming radix select runs instead.  Leaves the k best keys, sorted
+// descending, in sm.sel[0..k).
+template <int CPT>
+__device__ void select_bins(const float *__restrict__ cand, int total, int k, SelectSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float vmin = sm.vmin, span = sm.vmax - sm.vmin;
+  float scale = (float)(kBins - 1) / span;
+  if (!(scale > 0.f) || !(scale < 3.0e38f)) scale = 0.f;
+  for (int b = tid; b < kBins; b += kTopkThreads) sm.hist[b] = 0;
+  __syncthreads();
+  uint32_t pb[CPT / 2];  // bin of candidate tid + 1024*m in half m%2 of pb[m/2]; 0xFFFF = invalid
+#pragma unroll
+  for (int m2 = 0; m2 < CPT / 2; ++m2) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int hsel = 0; hsel < 2; ++hsel) {
+      const int i = tid + kTopkThreads * (2 * m2 + hsel);
+      const float v = i < total ? gld<float>(cand + i) : kNegInf;
+      uint32_t b = 0xFFFFu;
+      if (v > kNegInf) {
+        b = (uint32_t)min(kBins - 1, (int)((v - vmin) * scale));
+        atomicAdd(&sm.hist[b], 1);
+      }
+      packed |= b << (16 * hsel);
+    }
+    pb[m2] = packed;
+  }
+  __syncthreads();
+  // suffix sums: thread t owns bins 2t and 2t+1
+  const int h0 = sm.hist[2 * tid], h1 = sm.hist[2 * tid + 1];
+  const int loc = h0 + h1;
+  int suf = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(suf, o);
+    if (lane + o < 64) suf += y;
+  }
+  if (lane == 0) sm.wsum[w] = suf;
+  __syncthreads();
+  int above = suf - loc;
+  for (int ww = w + 1; ww < kTopkThreads / 64; ++ww) above += sm.wsum[ww];
+  if (above < k && k <= above + h1) {
+    sm.cut = 2 * tid + 1;
+    sm.need = k - above;
+  } else if (above + h1 < k && k <= above + h1 + h0) {
+    sm.cut = 2 * tid;
+    sm.need = k - above - h1;
+  }
+  if (tid == 0) {
+    sm.cnt = 0;
+    sm.tcnt = 0;
+  }
+  __syncthreads();
+  const int cut = sm.cut, need = sm.need, cutcnt = sm.hist[cut];
+  __syncthreads();  // every thread has read hist[cut] before anything reuses hist
+  if (cutcnt > kTieCap) {  // uniform branch
+    select_stream(cand, total, k, sm);
+    return;
+  }
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int b = (int)((pb[m >> 1] >> (16 * (m & 1))) & 0xFFFFu);
+    if (b != 0xFFFF && b >= cut) {
+      const int i = tid + kTopkThreads * m;
+      const uint64_t key = cand_key(gld<float>(cand + i), (uint32_t)i);
+      if (b > cut)
+        sm.sel[atomicAdd(&sm.cnt, 1)] = key;
+      else
+        sm.tie[atomicAdd(&sm.tcnt, 1)] = key;
+    }
+  }
+  __syncthreads();
+  const int ntie = sm.tcnt, base = sm.cnt;  // base == k - need
+  if (ntie > 1) block_sort_desc(sm.tie, ntie);
+  for (int i = tid; i < need; i += kTopkThreads) sm.sel[base + i] = sm.tie[i];
+  __syncthreads();
+  block_sort_desc(sm.sel, k);
+}
+
+// Streaming variant for candidate arrays larger than the registers hold: exact radix
+// select reading the array from memory each pass.  Leaves the k largest keys sorted.
+__device__ void select_stream(const float *__restrict__ cand, int n_total, int k, SelectSmem &sm) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   int need = k;
@@ -584,90 +874,40 @@ __device__ void wg_select(const float *__restrict__ cand, int n_total, int k, Se
     need = sm.need;
     __syncthreads();
   }
-  const uint64_t kstar = prefix;
   if (tid == 0) sm.cnt = 0;
   __syncthreads();
   for (int i = tid; i < n_total; i += kTopkThreads) {
     const float v = cand[i];
     if (!(v > kNegInf)) continue;
     const uint64_t key = cand_key(v, (uint32_t)i);
-    if (key >= kstar) {
-      const int pos = atomicAdd(&sm.cnt, 1);
-      sm.sel[pos] = key;
-    }
+    if (key >= prefix) sm.sel[atomicAdd(&sm.cnt, 1)] = key;
   }
   __syncthreads();
-  int P = 1;
-  while (P < k) P <<= 1;
-  for (int i = tid; i < P; i += kTopkThreads)
-    if (i >= k) sm.sel[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P; i += kTopkThreads) {
-        const int pj = i ^ stride;
-        if (pj > i) {
-          const uint64_t a = sm.sel[i], b = sm.sel[pj];
-          const bool desc = (i & size) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            sm.sel[i] = b;
-            sm.sel[pj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  block_sort_desc(sm.sel, k);
 }
 
-// Trie-masked log-softmax, top-K over beams x codes, BeamPath update.  One workgroup
-// per request.
-__global__ __launch_bounds__(kTopkThreads) void k_topk(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+// Top-K over beams x codes + BeamPath update.  One workgroup per request.
+template <bool REGS>
+__global__ __launch_bounds__(kTopkThreads) void k_select(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
   __shared__ SelectSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   const StepReq R = reqs[blockIdx.x];
   const Dims &dm = dev.dm;
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level, V = dm.V, lvl = dm.levels, MW = dm.MW;
   const int cur = s & 1, nxt = cur ^ 1;
   const int n = ((const int *)(slot + dev.sl.n_live))[cur];
-  const float *logits = (const float *)(slot + dev.sl.logits);
-  float *cand = (float *)(slot + dev.sl.cand);
-  const int *node_cur = (const int *)(slot + dev.sl.node[cur]);
-  const float *score_cur = (const float *)(slot + dev.sl.score[cur]);
-  const uint32_t *mask = dev.trie_mask + dev.trie_off[s] * MW;
-  const int32_t *child = dev.trie_child + dev.trie_off[s];
-  if (tid == 0) sm.nvalid = 0;
-  __syncthreads();
-  for (int j = w; j < n; j += kTopkThreads / 64) {
-    const uint32_t *mrow = mask + (size_t)node_cur[j] * MW;
-    const float sc = score_cur[j];
-    float mx = kNegInf;
-    for (int c = lane; c < V; c += 64) {
-      const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
-      if (dm.norm == 1 || valid) mx = fmaxf(mx, logits[(size_t)j * V + c]);
-    }
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int c = lane; c < V; c += 64) {
-      const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
-      if (dm.norm == 1 || valid) sum += expf(logits[(size_t)j * V + c] - mx);
-    }
-    sum = wave_sum(sum);
-    const float lse = mx + logf(sum);
-    int cnt = 0;
-    for (int c = lane; c < V; c += 64) {
-      const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
-      cand[(size_t)j * V + c] = valid ? sc + (logits[(size_t)j * V + c] - lse) : kNegInf;
-      cnt += valid;
-    }
-    cnt = wave_isum(cnt);
-    if (lane == 0) atomicAdd(&sm.nvalid, cnt);
+  const float *cand = (const float *)(slot + dev.sl.cand);
+  scan_cands(cand, n * V, sm);
+  const int k = min(R.W, sm.nvalid);
+  if (k > 0) {
+    if constexpr (REGS)
+      select_bins<kSelectCPT>(cand, n * V, k, sm);
+    else
+      select_stream(cand, n * V, k, sm);
   }
   __syncthreads();
-  const int k = min(R.W, sm.nvalid);
-  if (k > 0) wg_select(cand, n * V, k, sm);
-  __syncthreads();
+  const int *node_cur = (const int *)(slot + dev.sl.node[cur]);
   const int *codes_cur = (const int *)(slot + dev.sl.codes[cur]);
   const int *anc_cur = (const int *)(slot + dev.sl.anc[cur]);
   int *codes_nxt = (int *)(slot + dev.sl.codes[nxt]);
@@ -675,6 +915,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dev dev, const StepReq *_
   float *score_nxt = (float *)(slot + dev.sl.score[nxt]);
   int *node_nxt = (int *)(slot + dev.sl.node[nxt]);
   int *parent_nxt = (int *)(slot + dev.sl.parent[nxt]);
+  const uint32_t *mask = dev.trie_mask + dev.trie_off[s] * MW;
+  const int32_t *child = dev.trie_child + dev.trie_off[s];
   for (int i = tid; i < k; i += kTopkThreads) {
     const uint64_t key = sm.sel[i];
     const uint32_t flat = 0xFFFFFFFFu - (uint32_t)key;
@@ -697,20 +939,21 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dev dev, const StepReq *_
   if (tid == 0) ((int *)(slot + dev.sl.n_live))[nxt] = k;
 }
 
+template <bool REGS>
 __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float *__restrict__ cand, int n_rows, int V,
                                                               int k, int32_t *out_flat, float *out_score,
                                                               int32_t *n_out) {
   __shared__ SelectSmem sm;
   const int tid = threadIdx.x;
   const int n_total = n_rows * V;
-  if (tid == 0) sm.nvalid = 0;
-  __syncthreads();
-  int cnt = 0;
-  for (int i = tid; i < n_total; i += kTopkThreads) cnt += (cand[i] > kNegInf) ? 1 : 0;
-  atomicAdd(&sm.nvalid, cnt);
-  __syncthreads();
+  scan_cands(cand, n_total, sm);
   const int ke = min(k, sm.nvalid);
-  if (ke > 0) wg_select(cand, n_total, ke, sm);
+  if (ke > 0) {
+    if constexpr (REGS)
+      select_bins<kSelectCPT>(cand, n_total, ke, sm);
+    else
+      select_stream(cand, n_total, ke, sm);
+  }
   __syncthreads();
   for (int i = tid; i < ke; i += kTopkThreads) {
     const uint64_t key = sm.sel[i];
@@ -777,20 +1020,23 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
       hipLaunchKernelGGL(k_ctx_attn_f32<128>, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
     return hipGetLastError();
   }
+  const dim3 blk(ctx_nw * 64), grid(total_wgs);
   if (dev.dm.d == 128) {
-    if (ctx_nw == 4)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 4, 64>), dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+    if (ctx_nw == 8)
+      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+    else if (ctx_nw == 4)
+      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else if (ctx_nw == 2)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 2, 32>), dim3(total_wgs), dim3(128), 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 1, 32>), dim3(total_wgs), dim3(64), 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 1, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
   } else {
-    if (ctx_nw == 4)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<64, 4, 64>), dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+    if (ctx_nw >= 4)
+      hipLaunchKernelGGL((k_ctx_attn_bf16<64, 4, 64>), grid, dim3(256), 0, st, dev, reqs, n_reqs, layer);
     else if (ctx_nw == 2)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<64, 2, 32>), dim3(total_wgs), dim3(128), 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_ctx_attn_bf16<64, 1, 32>), dim3(total_wgs), dim3(64), 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 1, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
   }
   return hipGetLastError();
 }
@@ -818,16 +1064,29 @@ hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int to
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st) {
+hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st) {
+  if (total_wgs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lsm, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st) {
   if (n_reqs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk, dim3(n_reqs), dim3(kTopkThreads), 0, st, dev, reqs, n_reqs);
+  if (max_cand <= kTopkThreads * kSelectCPT)
+    hipLaunchKernelGGL(k_select<true>, dim3(n_reqs), dim3(kTopkThreads), 0, st, dev, reqs, n_reqs);
+  else
+    hipLaunchKernelGGL(k_select<false>, dim3(n_reqs), dim3(kTopkThreads), 0, st, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat, float *out_score,
                               int32_t *n_out_dev, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk_select, dim3(1), dim3(kTopkThreads), 0, st, cand, n_rows, V, k, out_flat, out_score,
-                     n_out_dev);
+  if ((int64_t)n_rows * V <= (int64_t)kTopkThreads * kSelectCPT)
+    hipLaunchKernelGGL(k_topk_select<true>, dim3(1), dim3(kTopkThreads), 0, st, cand, n_rows, V, k, out_flat,
+                       out_score, n_out_dev);
+  else
+    hipLaunchKernelGGL(k_topk_select<false>, dim3(1), dim3(kTopkThreads), 0, st, cand, n_rows, V, k, out_flat,
+                       out_score, n_out_dev);
   return hipGetLastError();
 }
 

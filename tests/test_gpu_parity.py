@@ -115,8 +115,16 @@ def test_topk_select_bit_exact_vs_lexsort():
     import torch
     import semantic_id_beam_amd as sib
     rng = np.random.default_rng(5)
-    for n_rows, V, k in [(1, 16, 4), (7, 33, 20), (256, 256, 256), (30, 256, 30), (3, 1000, 1024), (64, 5, 300)]:
-        x = np.round(rng.standard_normal((n_rows, V)) * 2, 2).astype(np.float32)   # many ties
+    cases = [(1, 16, 4, "r"), (7, 33, 20, "r"), (256, 256, 256, "r"), (30, 256, 30, "r"), (3, 1000, 1024, "r"),
+             (64, 5, 300, "r"), (300, 256, 100, "r"),         # > 65536 candidates: streaming select
+             (40, 128, 50, "eq"), (256, 256, 256, "n"), (1, 1024, 1024, "n")]
+    for n_rows, V, k, kind in cases:
+        if kind == "eq":                                     # one value: every candidate ties
+            x = np.full((n_rows, V), -1.5, dtype=np.float32)
+        elif kind == "n":                                    # continuous scores
+            x = (rng.standard_normal((n_rows, V)) - 8).astype(np.float32)
+        else:                                                # rounded: many exact ties
+            x = np.round(rng.standard_normal((n_rows, V)) * 2, 2).astype(np.float32)
         x[rng.random((n_rows, V)) < 0.3] = -np.inf
         x[0, 0] = 0.0
         x[-1, -1] = -0.0
