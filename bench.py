@@ -86,7 +86,19 @@ def main():
     ap.add_argument("--config", default=None, help="workload name (default: the ctx-5000 beam-256 headline)")
     ap.add_argument("--cpu-beams", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step shards by request with no exchange; see the design notes)", file=sys.stderr)

@@ -202,12 +202,15 @@ void layout(gr_engine *e) {
   s.beamkv_k = take(kv);
   s.beamkv_v = take(kv);
   s.q_last = take((size_t)d.L * d.Hq * d.d * el);
+  s.knmax = take((size_t)d.L * d.Hkv * 4);
   s.h = take(W * d.Hq * d.d * 4);
   s.logits = take(W * d.V * 4);
   s.logits_part = take((size_t)gr::kLogitsKS * W * d.V * 4);
   s.cand = take(W * d.V * 4);
-  s.part_o = take((size_t)d.Hkv * d.S_max * W * d.g * d.d * 4);
-  s.part_ml = take((size_t)d.Hkv * d.S_max * W * d.g * 8);
+  for (int b = 0; b < 2; ++b) {
+    s.part_o[b] = take((size_t)d.Hkv * d.S_max * W * d.g * d.d * 4);
+    s.part_ml[b] = take((size_t)d.Hkv * d.S_max * W * d.g * 8);
+  }
   for (int b = 0; b < 2; ++b) {
     s.codes[b] = take(W * d.levels * 4);
     s.score[b] = take(W * 4);
@@ -446,6 +449,9 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
   }
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
+  if ((r = check_dev(e, gr::launch_key_norm_max(R.k, e->dm.L, e->dm.Hkv, N, Np, e->dm.d, e->elem,
+                                                (float *)(sb + e->sl.knmax), st), "key norms")) != GR_OK)
+    return r;
   if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem,
                                        hipMemcpyDeviceToDevice, st), "q_last copy")) != GR_OK)
     return r;
@@ -573,10 +579,15 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw, n, l, wg_ctx, nw, st), "context attention")) != GR_OK)
       return r;
     prof_end(e, pi, st);
-    pi = prof_begin(e, pon, GR_PROF_BEAM_MERGE, plevel, st);
-    if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st), "beam attention/merge")) != GR_OK)
-      return r;
-    prof_end(e, pi, st);
+    // float32: finish every layer separately; bf16: layer l is finished inside layer l+1's
+    // context kernel, and the last layer here
+    if (d.dtype == 0 || l == d.L - 1) {
+      pi = prof_begin(e, pon, GR_PROF_BEAM_MERGE, plevel, st);
+      if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st), "beam attention/merge")) !=
+          GR_OK)
+        return r;
+      prof_end(e, pi, st);
+    }
   }
   int pi = prof_begin(e, pon, GR_PROF_LOGITS, plevel, st);
   if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st), "logits")) != GR_OK) return r;

@@ -30,12 +30,13 @@ struct SlotLayout {
   size_t slot_bytes;
   size_t beamkv_k, beamkv_v;  // [L][levels-1][W_max][Hkv][d] elem
   size_t q_last;              // [L][Hq][d] elem
+  size_t knmax;               // [L][Hkv] f32: largest context-key norm (bounds the scores)
   size_t h;                   // [W_max][Hq*d] f32
   size_t logits;              // [W_max][V] f32
   size_t logits_part;         // [kLogitsKS][W_max][V] f32 split-K partial sums
   size_t cand;                // [W_max][V] f32
-  size_t part_o;              // [part_rows][d] f32, row ((h*splits + sp)*rows_b + row)
-  size_t part_ml;             // [part_rows] float2 (m in log2 units, l)
+  size_t part_o[2];           // [part_rows][d] f32, row ((h*splits + sp)*rows_b + row); by layer parity
+  size_t part_ml[2];          // [part_rows] float2 (m in log2 units, l)
   size_t codes[2];            // [W_max][levels] i32   (double-buffered by level parity)
   size_t score[2];            // [W_max] f32
   size_t node[2];             // [W_max] i32  trie node of the beam's prefix
@@ -83,6 +84,9 @@ hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_
 hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N,
                            int Np, int Hkv, int d, int elem_bytes, hipStream_t st);
 hipError_t launch_init_slot(const Dev &dev, int slot, hipStream_t st);
+// largest key norm per (layer, kv head) of native K [L][Hkv][Np][d] -> out [L][Hkv]
+hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int Np, int d, int elem_bytes,
+                               float *out, hipStream_t st);
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
 

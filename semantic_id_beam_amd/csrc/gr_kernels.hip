@@ -30,6 +30,7 @@ namespace gr {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -89,6 +90,13 @@ __device__ __forceinline__ uint8_t *slot_base(const Dev &dev, int slot) {
 // consecutive tokens per lane: no cross-lane shuffle between the two MFMAs.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+template <int D, typename T>
+__device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
+                                           int gi, int kv, int c8);
+template <int D>
+__device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int kv,
+                                            int r0, int r1, int tid, int nthreads);
+
 // --------------------------------------------------------------------------------------
 // Shared-context attention, bf16 K/V, fp32 accumulate, MFMA 32x32x16.
 //
@@ -104,7 +112,7 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 // Workgroup order: the row blocks of one (kv head, token range) pair get workgroup ids
 // 8 apart, so (with workgroups dealt round-robin over the 8 XCDs) they run on one XCD
 // and share its L2 for the K/V tiles.
-template <int D, int NW, int TT>
+template <int D, int NW, int TT, bool HILO>
 __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__restrict__ reqs, int n_reqs,
                                               int layer) {
   constexpr int KB = D / 16;
@@ -200,9 +208,36 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
 
+  // Score bound (Cauchy-Schwarz): u = q.k*log2(e)/sqrt(d) <= B = |q| max|k| log2(e)/sqrt(d).
+  // When every row of the workgroup has B <= 60, the fixed reference M = B - 60 keeps every
+  // p = 2^(u - M) <= 2^60 and the row's largest p >= 2^(-2B+60) >= 2^-60: no running max and
+  // no rescale are needed (m and l share M, so the result is exact).  Otherwise the loop
+  // tracks a running max with a lazy rescale.
+  __shared__ float sBound[NW];
+  {
+    float qn = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
+    qn += __shfl_xor(qn, 32);
+    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
+    const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
+    M = B - 60.f;
+    const float bw = wave_max(B);
+    if (lane == 0) sBound[w] = bw;
+  }
+  __syncthreads();
+  float bmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) bmax = fmaxf(bmax, sBound[i]);
+  const bool fixed_ref = bmax <= 60.f;  // uniform over the workgroup
+  if (!fixed_ref) M = kNegInf;
+
   // one 32-token sub-tile; MASK handles the tokens >= t1 of the last tile
-  auto subtile = [&](int buf, int sub, int tb, auto mask_tag) {
+  auto subtile = [&](int buf, int sub, int tb, auto mask_tag, auto fixed_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIXED = decltype(fixed_tag)::value;
     f32x16_t sacc = f32x16_t{};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -216,64 +251,97 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
       for (int i = 0; i < 16; ++i)
         if (tbase + 16 * (i >> 3) + (i & 7) >= t1) sacc[i] = kNegInf;
     }
-    float mx = sacc[0];
+    if constexpr (!FIXED) {
+      float mx = sacc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * c2;
-    if (__ballot(mxs > M + 8.f) != 0ull) {
-      const float Mn = fmaxf(M, mxs);
-      const float f = fast_exp2(M - Mn);
-      l *= f;
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxs = mx * c2;
+      if (__ballot(mxs > M + 8.f) != 0ull) {
+        const float Mn = fmaxf(M, mxs);
+        const float f = fast_exp2(M - Mn);
+        l *= f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= f;
-      M = Mn;
+        for (int db = 0; db < DB; ++db) oacc[db] *= f;
+        M = Mn;
+      }
     }
-    float ls = 0.f;
-    bf16x8_t pf[2];
+    bf16x8_t pf[2], pl[2];
+    if constexpr (HILO) {
+      // p = p_hi + p_lo, both bf16 (relative error ~2^-17); l sums p in fp32
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(sacc[i], c2, -M));
-      ls += p;
-      pf[i >> 3][i & 7] = (__bf16)p;
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sacc[i], c2, -M));
+        const __bf16 ph = (__bf16)p;
+        pf[i >> 3][i & 7] = ph;
+        pl[i >> 3][i & 7] = (__bf16)(p - (float)ph);
+        l += p;
+      }
+    } else {
+      // p rounded to bf16 feeds the PV MFMA; l sums exactly those rounded values (dot2
+      // with (1, 1)), so the output is an exact convex combination of the value rows.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (__bf16)fast_exp2(fmaf(sacc[i], c2, -M));
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 0, 1), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 2, 3), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 4, 5), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 6, 7), ones, l, false);
+      }
     }
-    l += ls;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         const bf16x8_t vf = sV[buf][db * 32 + (lane & 31)][sub * 4 + pp * 2 + hh];
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pp], oacc[db], 0, 0, 0);
+        if constexpr (HILO) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[pp], oacc[db], 0, 0, 0);
       }
     }
   };
 
-  gload(t0);
-  lstore(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int tb = t0 + it * TT;
-    if (it + 1 < ntiles) gload(tb + TT);
-    if (wave_active) {
-      if (tb + TT <= t1) {
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) subtile(buf, sub, tb, std::false_type{});
-      } else {
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
-          if (tb + sub * 32 < t1) subtile(buf, sub, tb, std::true_type{});
-      }
+  auto run = [&](auto fixed_tag) {
+    gload(t0);
+    if (layer > 0) {
+      // finish the previous layer for this workgroup's share of the row block (its split
+      // partials are complete: that layer's kernel has ended)
+      const int nr = min(rows, row0 + NW * 32) - row0;
+      const int per = (nr + R.splits - 1) / R.splits;
+      const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
+      finish_rows<D>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
+    lstore(0);
     __syncthreads();
-  }
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = it & 1;
+      const int tb = t0 + it * TT;
+      if (it + 1 < ntiles) gload(tb + TT);
+      if (wave_active) {
+        if (tb + TT <= t1) {
+#pragma unroll
+          for (int sub = 0; sub < NSUB; ++sub) subtile(buf, sub, tb, std::false_type{}, fixed_tag);
+        } else {
+#pragma unroll
+          for (int sub = 0; sub < NSUB; ++sub)
+            if (tb + sub * 32 < t1) subtile(buf, sub, tb, std::true_type{}, fixed_tag);
+        }
+      }
+      if (it + 1 < ntiles) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  };
+  if (fixed_ref)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   const float ltot = l + __shfl_xor(l, 32);
   if (wave_active && row_ok) {
     const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml) + prow, f32x2_t{M, ltot});
-    float *po = (float *)(slot + dev.sl.part_o) + prow * D;
+    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[layer & 1]) + prow, f32x2_t{M, ltot});
+    float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -284,19 +352,22 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
       }
     }
   }
+
 }
 
-// Wide steps (many query rows): two waves per SIMD so one wave's softmax overlaps the
-// other's MFMAs.  Narrow steps are HBM-bound and keep their staging registers instead.
+// Wide steps (many query rows, MFMA-bound): two waves per SIMD so one wave's softmax
+// overlaps the other's MFMAs; P is rounded once to bf16.  Narrow steps (HBM- or
+// latency-bound) keep their staging registers and spend the idle MFMA time on a second
+// bf16 term of P.
 template <int D, int NW, int TT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_ctx_attn_bf16(
     Dev dev, const StepReq *__restrict__ reqs, int n_reqs, int layer) {
-  ctx_attn_body<D, NW, TT>(dev, reqs, n_reqs, layer);
+  ctx_attn_body<D, NW, TT, false>(dev, reqs, n_reqs, layer);
 }
 template <int D, int NW, int TT>
 __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16_narrow(Dev dev, const StepReq *__restrict__ reqs,
                                                                   int n_reqs, int layer) {
-  ctx_attn_body<D, NW, TT>(dev, reqs, n_reqs, layer);
+  ctx_attn_body<D, NW, TT, true>(dev, reqs, n_reqs, layer);
 }
 
 // --------------------------------------------------------------------------------------
@@ -359,8 +430,8 @@ __global__ __launch_bounds__(256) void k_ctx_attn_f32(Dev dev, const StepReq *__
     }
   }
   const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-  if (lane == 0) ((float2 *)(slot + dev.sl.part_ml))[prow] = make_float2(M, l);
-  float *po = (float *)(slot + dev.sl.part_o) + prow * D;
+  if (lane == 0) ((float2 *)(slot + dev.sl.part_ml[layer & 1]))[prow] = make_float2(M, l);
+  float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) po[lane + 64 * e] = o[e];
 }
@@ -402,123 +473,145 @@ struct Raw8<float> {
   }
 };
 
-// BeamKV append + beam-token attention + split-K merge + layer sum.  One workgroup per
-// (request, beam j); thread = (query head hq, 8-feature chunk), C8 = D/8 threads per head.
+// One (beam j, query head h*g+gi, 8-feature chunk c8) element of the per-layer finish:
 //   step s >= 1: the new token's k/v (code c_{s-1}) are written to BeamKV slot
-//   [layer][s-1][j]; the beam's earlier tokens t < s-1 are read from BeamKV slot
-//   anc[j][t] (BeamPath) -- never re-looked-up from the tables.
+//   [layer][s-1][j] (by gi == 0); the beam's earlier tokens t < s-1 are read from BeamKV
+//   slot anc[j][t] (BeamPath) -- never re-looked-up from the tables -- and attended to;
+//   then the split-K context partials are merged in split order with that beam partial and
+//   the layer output is added to h (written at layer 0).
+// The D/8 lanes of one (j, head) must be consecutive and active together (their dot
+// products are reduced with lane shuffles).
+template <int D, typename T>
+__device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
+                                           int gi, int kv, int c8) {
+  constexpr int C8 = D / 8;
+  const Dims &dm = dev.dm;
+  const int s = R.level, g = dm.g, lvl = dm.levels, hq = kv * g + gi;
+  const float c2 = dm.scale_log2;
+  float Mb = kNegInf, lb = 0.f, ob[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ob[i] = 0.f;
+  if (s > 0) {
+    const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
+    const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
+    const int code = codes[j * lvl + (s - 1)];
+    const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code;
+    float q[8];
+    {
+      Raw8<T> rq;
+      rq.load((const T *)dev.tok_q + (trow * dm.Hq + hq) * D + c8 * 8);
+      rq.to_float(q);
+    }
+    Raw8<T> kn, vn;
+    kn.load((const T *)dev.tok_k + (trow * dm.Hkv + kv) * D + c8 * 8);
+    vn.load((const T *)dev.tok_v + (trow * dm.Hkv + kv) * D + c8 * 8);
+    T *bk = (T *)(slot + dev.sl.beamkv_k);
+    T *bv = (T *)(slot + dev.sl.beamkv_v);
+    const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
+    const size_t lvstride = (size_t)dm.W_max * wstride;
+    const size_t base = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D + c8 * 8;
+    if (gi == 0) {
+      kn.store(bk + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
+      vn.store(bv + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
+    }
+    for (int t = 0; t < s; ++t) {
+      float kt[8], vt[8];
+      if (t == s - 1) {
+        kn.to_float(kt);
+        vn.to_float(vt);
+      } else {
+        const size_t off = base + (size_t)t * lvstride + (size_t)anc[j * lvl + t] * wstride;
+        Raw8<T> a, b;
+        a.load(bk + off);
+        b.load(bv + off);
+        a.to_float(kt);
+        b.to_float(vt);
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot = fmaf(q[i], kt[i], dot);
+#pragma unroll
+      for (int o = C8 / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+      const float u = dot * c2;
+      const float Mn = fmaxf(Mb, u);
+      const float f = fast_exp2(Mb - Mn);
+      const float p = fast_exp2(u - Mn);
+      lb = lb * f + p;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ob[i] = fmaf(p, vt[i], ob[i] * f);
+      Mb = Mn;
+    }
+  }
+  const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[layer & 1]);
+  const float *po = (const float *)(slot + dev.sl.part_o[layer & 1]);
+  const int row = j * g + gi;
+  const size_t pbase = (size_t)kv * R.splits * R.rows_b + row;
+  float Ms = Mb;
+  for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
+  const float fb = fast_exp2(Mb - Ms);
+  float Ls = lb * fb, O[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] = ob[i] * fb;
+  for (int sp = 0; sp < R.splits; ++sp) {
+    const size_t prow = pbase + (size_t)sp * R.rows_b;
+    const f32x2_t ml = gld<f32x2_t>(pml + prow);
+    const float f = fast_exp2(ml[0] - Ms);
+    Ls = fmaf(ml[1], f, Ls);
+    const f32x4_t a = gld<f32x4_t>(po + prow * D + c8 * 8);
+    const f32x4_t b = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      O[i] = fmaf(a[i], f, O[i]);
+      O[4 + i] = fmaf(b[i], f, O[4 + i]);
+    }
+  }
+  const float inv = 1.f / Ls;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] *= inv;
+  float *hr = (float *)(slot + dev.sl.h) + ((size_t)j * dm.Hq + hq) * D + c8 * 8;
+  f32x4_t a = f32x4_t{O[0], O[1], O[2], O[3]}, b = f32x4_t{O[4], O[5], O[6], O[7]};
+  if (dm.debug_attn) {
+    float *dg = (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j) * dm.Hq + hq) * D + c8 * 8;
+    gst<f32x4_t>(dg, a);
+    gst<f32x4_t>(dg + 4, b);
+  }
+  if (layer > 0) {
+    a += gld<f32x4_t>(hr);
+    b += gld<f32x4_t>(hr + 4);
+  }
+  gst<f32x4_t>(hr, a);
+  gst<f32x4_t>(hr + 4, b);
+}
+
+// Finishes rows [r0, r1) of kv head kv for `layer` (bf16 caches); thread = (row, chunk).
+template <int D>
+__device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int kv,
+                                            int r0, int r1, int tid, int nthreads) {
+  constexpr int C8 = D / 8;
+  for (int e = tid; e < (r1 - r0) * C8; e += nthreads) {
+    const int row = r0 + e / C8;
+    merge_elem<D, uint16_t>(dev, R, slot, layer, row / dev.dm.g, row % dev.dm.g, kv, e % C8);
+  }
+}
+
+// Separate finish kernel: the float32 path after every layer, the bf16 path after the last
+// layer.  One workgroup per (request, beam j); thread = (query head, 8-feature chunk).
+// thread = (query head, 8-feature chunk).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void k_beam_merge(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                     int layer) {
   constexpr int C8 = D / 8;
-  const int tid = threadIdx.x;
   const int ri = find_req<1>(reqs, n_reqs, blockIdx.x);
   const StepReq R = reqs[ri];
   const Dims &dm = dev.dm;
   const int j = blockIdx.x - R.wg_merge;
   uint8_t *slot = slot_base(dev, R.slot);
-  const int s = R.level;
-  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[R.level & 1];
   if (j >= n_live) return;
-  const int g = dm.g, lvl = dm.levels;
-  const float c2 = dm.scale_log2;
   const int nchunk = dm.Hq * C8;  // a multiple of C8: a head's lanes are all active or all idle
-  const float2 *pml = (const float2 *)(slot + dev.sl.part_ml);
-  const float *po = (const float *)(slot + dev.sl.part_o);
-  float *hbuf = (float *)(slot + dev.sl.h);
-  for (int e = tid; e < nchunk; e += 256) {
-    const int hq = e / C8, c8 = e % C8, kv = hq / g, gi = hq % g;
-    float Mb = kNegInf, lb = 0.f, ob[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ob[i] = 0.f;
-    if (s > 0) {
-      const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
-      const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
-      const int code = codes[j * lvl + (s - 1)];
-      const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code;
-      float q[8];
-      {
-        Raw8<T> rq;
-        rq.load((const T *)dev.tok_q + (trow * dm.Hq + hq) * D + c8 * 8);
-        rq.to_float(q);
-      }
-      Raw8<T> kn, vn;
-      kn.load((const T *)dev.tok_k + (trow * dm.Hkv + kv) * D + c8 * 8);
-      vn.load((const T *)dev.tok_v + (trow * dm.Hkv + kv) * D + c8 * 8);
-      T *bk = (T *)(slot + dev.sl.beamkv_k);
-      T *bv = (T *)(slot + dev.sl.beamkv_v);
-      const size_t wstride = (size_t)dm.Hkv * D;       // one BeamKV slot
-      const size_t lvstride = (size_t)dm.W_max * wstride;
-      const size_t base = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D + c8 * 8;
-      if (gi == 0) {
-        kn.store(bk + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
-        vn.store(bv + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
-      }
-      for (int t = 0; t < s; ++t) {
-        float kt[8], vt[8];
-        if (t == s - 1) {
-          kn.to_float(kt);
-          vn.to_float(vt);
-        } else {
-          const size_t off = base + (size_t)t * lvstride + (size_t)anc[j * lvl + t] * wstride;
-          Raw8<T> a, b;
-          a.load(bk + off);
-          b.load(bv + off);
-          a.to_float(kt);
-          b.to_float(vt);
-        }
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dot = fmaf(q[i], kt[i], dot);
-#pragma unroll
-        for (int o = C8 / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-        const float u = dot * c2;
-        const float Mn = fmaxf(Mb, u);
-        const float f = fast_exp2(Mb - Mn);
-        const float p = fast_exp2(u - Mn);
-        lb = lb * f + p;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ob[i] = fmaf(p, vt[i], ob[i] * f);
-        Mb = Mn;
-      }
-    }
-    const int row = j * g + gi;
-    const size_t pbase = (size_t)kv * R.splits * R.rows_b + row;
-    float Ms = Mb;
-    for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
-    const float fb = fast_exp2(Mb - Ms);
-    float Ls = lb * fb, O[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) O[i] = ob[i] * fb;
-    for (int sp = 0; sp < R.splits; ++sp) {
-      const size_t prow = pbase + (size_t)sp * R.rows_b;
-      const f32x2_t ml = gld<f32x2_t>(pml + prow);
-      const float f = fast_exp2(ml[0] - Ms);
-      Ls = fmaf(ml[1], f, Ls);
-      const f32x4_t a = gld<f32x4_t>(po + prow * D + c8 * 8);
-      const f32x4_t b = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        O[i] = fmaf(a[i], f, O[i]);
-        O[4 + i] = fmaf(b[i], f, O[4 + i]);
-      }
-    }
-    const float inv = 1.f / Ls;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) O[i] *= inv;
-    float *hr = hbuf + ((size_t)j * dm.Hq + hq) * D + c8 * 8;
-    f32x4_t a = f32x4_t{O[0], O[1], O[2], O[3]}, b = f32x4_t{O[4], O[5], O[6], O[7]};
-    if (dm.debug_attn) {
-      float *dg = (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j) * dm.Hq + hq) * D + c8 * 8;
-      gst<f32x4_t>(dg, a);
-      gst<f32x4_t>(dg + 4, b);
-    }
-    if (layer > 0) {
-      a += gld<f32x4_t>(hr);
-      b += gld<f32x4_t>(hr + 4);
-    }
-    gst<f32x4_t>(hr, a);
-    gst<f32x4_t>(hr + 4, b);
+  for (int e = threadIdx.x; e < nchunk; e += 256) {
+    const int hq = e / C8;
+    merge_elem<D, T>(dev, R, slot, layer, j, hq % dm.g, hq / dm.g, e % C8);
   }
 }
 
@@ -992,6 +1085,29 @@ __global__ void k_relayout_vt(const T *__restrict__ src, T *__restrict__ dst, in
   }
 }
 
+// Largest L2 norm of the context keys of each (layer, kv head): one workgroup per pair,
+// one wave per key row at a time.
+template <typename T>
+__global__ __launch_bounds__(256) void k_key_norm_max(const T *__restrict__ k, int N, int Np, int d,
+                                                      float *__restrict__ out) {
+  __shared__ float smax[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const T *base = k + (size_t)blockIdx.x * Np * d;
+  float best = 0.f;
+  for (int t = w; t < N; t += 4) {
+    float acc = 0.f;
+    for (int e = lane; e < d; e += 64) {
+      const float x = (float)(sizeof(T) == 2 ? __uint_as_float(((uint32_t)(uint16_t)base[(size_t)t * d + e]) << 16)
+                                             : (float)base[(size_t)t * d + e]);
+      acc = fmaf(x, x, acc);
+    }
+    best = fmaxf(best, wave_sum(acc));
+  }
+  if (lane == 0) smax[w] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+}
+
 __global__ void k_init_slot(Dev dev, int slot) {
   uint8_t *sb = slot_base(dev, slot);
   if (threadIdx.x == 0) {
@@ -1025,7 +1141,7 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
     if (ctx_nw == 8)
       hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else if (ctx_nw == 4)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else if (ctx_nw == 2)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else
@@ -1105,6 +1221,17 @@ hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, vo
     hipLaunchKernelGGL(k_relayout_vt<float>, dim3(blocks), dim3(256), 0, st, (const float *)src_v, (float *)dst_vt,
                        L, N, Np, Hkv, d);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int Np, int d, int elem_bytes,
+                               float *out, hipStream_t st) {
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_key_norm_max<uint16_t>, dim3(L * Hkv), dim3(256), 0, st, (const uint16_t *)k_native, N, Np,
+                       d, out);
+  else
+    hipLaunchKernelGGL(k_key_norm_max<float>, dim3(L * Hkv), dim3(256), 0, st, (const float *)k_native, N, Np, d,
+                       out);
   return hipGetLastError();
 }
 
