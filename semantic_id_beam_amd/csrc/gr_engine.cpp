@@ -504,64 +504,77 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   }
   hipStream_t st = (hipStream_t)stream;
   gr_status r;
-  // ---- work decomposition
-  int nw = 1;
-  if (d.dtype == 1) {
-    for (auto *R : rs) {
-      const int rows = R->n_bound * d.g;
-      nw = std::max(nw, rows <= 32 ? 1 : rows <= 64 ? 2 : rows <= 128 ? 4 : 8);
-    }
+  // ---- work decomposition: requests grouped by context-attention variant (one launch per
+  // group); within a group, enough split-K token ranges to fill the chip
+  std::vector<int> kind((size_t)n);
+  for (int i = 0; i < n; ++i)
+    kind[(size_t)i] = d.dtype == 1 ? gr::ctx_kind_for(rs[(size_t)i]->n_bound * d.g, rs[(size_t)i]->N, d.d) : 0;
+  std::vector<int> order((size_t)n);
+  for (int i = 0; i < n; ++i) order[(size_t)i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kind[(size_t)a] < kind[(size_t)b]; });
+  struct Group { int kind, start, count, wgs; };
+  std::vector<Group> groups;
+  for (int i = 0; i < n; ++i) {
+    const int k = kind[(size_t)order[(size_t)i]];
+    if (groups.empty() || groups.back().kind != k) groups.push_back({k, i, 0, 0});
+    groups.back().count++;
   }
-  if (d.d == 64) nw = std::min(nw, 4);  // the head_dim-64 kernels have at most 4 waves
-  const int rows_wg = gr::ctx_rows_per_wg(nw);
-  int64_t units = 0;
-  for (auto *R : rs) units += (int64_t)d.Hkv * ceil_div((int64_t)R->n_bound * d.g, rows_wg);
-  const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? 1024 : 2048) : 256;  // workgroups per launch
   const int slot_i = e->ring;
   e->ring = (e->ring + 1) % kRing;
   if (e->event_used[slot_i]) {
     if ((r = check_dev(e, hipEventSynchronize(e->events[slot_i]), "descriptor ring")) != GR_OK) return r;
   }
   gr::StepReq *hw = e->pinned[slot_i];
-  int wg_ctx = 0, wg_merge = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0;
-  for (int i = 0; i < n; ++i) {
-    gr_engine::Req *R = rs[(size_t)i];
-    gr::StepReq &w = hw[i];
-    std::memset(&w, 0, sizeof(w));
-    w.ctx_k = R->k;
-    w.ctx_vt = R->vt;
-    w.ctx_lstride = (int64_t)d.Hkv * R->Np * d.d;
-    w.N = R->N;
-    w.Np = R->Np;
-    w.slot = R->slot;
-    w.level = R->level;
-    w.W = R->W;
-    w.n_bound = R->n_bound;
-    const int rows = R->n_bound * d.g;
-    w.rows_b = rows;
-    w.row_blocks = ceil_div(rows, rows_wg);
-    // split-K: enough workgroups to fill the chip, at least two tiles per range, and
-    // no more partial rows than the slot holds (Hkv * S_max * W_max * g)
-    int S = (int)std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1));
-    S = std::min(S, std::max(1, ceil_div(R->N, 2 * gr::kTileTok)));
-    S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)d.S_max * d.W_max * d.g / rows));
-    S = std::min(S, 256);
-    int tps = (int)align_up((size_t)ceil_div(R->N, S), gr::kTileTok);
-    S = ceil_div(R->N, tps);
-    w.splits = S;
-    w.tps = tps;
-    w.wg_ctx = wg_ctx;
-    if (d.dtype == 1)
-      wg_ctx += (int)align_up((size_t)d.Hkv * S, 8) * w.row_blocks;  // multiple of 8: XCD-aware order
-    else
-      wg_ctx += ceil_div((int64_t)d.Hkv * rows * S, 4);
-    w.wg_merge = wg_merge;
-    wg_merge += R->n_bound;
-    w.wg_logits = wg_logits;
-    wg_logits += ceil_div(R->n_bound, 64) * ceil_div(d.V, 64) * gr::kLogitsKS;
-    w.wg_lsm = wg_lsm;
-    wg_lsm += ceil_div(R->n_bound, 4);
-    max_cand = std::max(max_cand, R->n_bound * d.V);
+  int wg_merge = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0;
+  for (Group &G : groups) {
+    const int nw = G.kind & 0xFF;
+    const int rows_wg = d.dtype == 1 ? gr::ctx_rows_per_wg(G.kind) : 32;
+    // workgroups per launch: about two per compute unit of 4 waves, fewer when wider
+    const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? 1024 : 2048) : 256;
+    int64_t units = 0;
+    for (int i = G.start; i < G.start + G.count; ++i)
+      units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)order[(size_t)i]]->n_bound * d.g, rows_wg);
+    int wg_ctx = 0;
+    for (int i = G.start; i < G.start + G.count; ++i) {
+      gr_engine::Req *R = rs[(size_t)order[(size_t)i]];
+      gr::StepReq &w = hw[i];
+      std::memset(&w, 0, sizeof(w));
+      w.ctx_k = R->k;
+      w.ctx_vt = R->vt;
+      w.ctx_lstride = (int64_t)d.Hkv * R->Np * d.d;
+      w.N = R->N;
+      w.Np = R->Np;
+      w.slot = R->slot;
+      w.level = R->level;
+      w.W = R->W;
+      w.n_bound = R->n_bound;
+      const int rows = R->n_bound * d.g;
+      w.rows_b = rows;
+      w.row_blocks = ceil_div(rows, rows_wg);
+      // split-K: enough workgroups, at least two tiles per range, and no more partial rows
+      // than the slot holds (Hkv * S_max * W_max * g)
+      int S = (int)std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1));
+      S = std::min(S, std::max(1, ceil_div(R->N, 2 * gr::kTileTok)));
+      S = (int)std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)d.S_max * d.W_max * d.g / rows));
+      S = std::min(S, 256);
+      int tps = (int)align_up((size_t)ceil_div(R->N, S), gr::kTileTok);
+      S = ceil_div(R->N, tps);
+      w.splits = S;
+      w.tps = tps;
+      w.wg_ctx = wg_ctx;
+      if (d.dtype == 1)
+        wg_ctx += (int)align_up((size_t)d.Hkv * S, 8) * w.row_blocks;  // multiple of 8: XCD-aware order
+      else
+        wg_ctx += ceil_div((int64_t)d.Hkv * rows * S, 4);
+      w.wg_merge = wg_merge;
+      wg_merge += R->n_bound;
+      w.wg_logits = wg_logits;
+      wg_logits += ceil_div(R->n_bound, 64) * ceil_div(d.V, 64) * gr::kLogitsKS;
+      w.wg_lsm = wg_lsm;
+      wg_lsm += ceil_div(R->n_bound, 4);
+      max_cand = std::max(max_cand, R->n_bound * d.V);
+    }
+    G.wgs = wg_ctx;
   }
   gr::StepReq *dw = (gr::StepReq *)(e->ws + e->off_work + e->work_bytes * (size_t)slot_i);
   if ((r = check_dev(e, hipMemcpyAsync(dw, hw, sizeof(gr::StepReq) * (size_t)n, hipMemcpyHostToDevice, st),
@@ -576,8 +589,10 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   const int pstep = prof_begin(e, pon, GR_PROF_STEP, plevel, st);
   for (int l = 0; l < d.L; ++l) {
     int pi = prof_begin(e, pon, GR_PROF_CTX_ATTN, plevel, st);
-    if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw, n, l, wg_ctx, nw, st), "context attention")) != GR_OK)
-      return r;
+    for (const Group &G : groups)
+      if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, st),
+                         "context attention")) != GR_OK)
+        return r;
     prof_end(e, pi, st);
     // float32: finish every layer separately; bf16: layer l is finished inside layer l+1's
     // context kernel, and the last layer here

@@ -72,9 +72,13 @@ struct StepReq {
 };
 
 // ---- launchers (gr_kernels.hip) ------------------------------------------
-// ctx_nw: waves per context workgroup (1, 2 or 4); 32 query rows per wave.
+// Context-attention variants: waves per workgroup (1, 2, 4 or 8; 32 query rows per wave)
+// in the low byte, kCtxHiLo when P is split into two bf16 terms.  1, 2 and 4 waves always
+// use the split (narrow steps: HBM- or latency-bound); 8 waves only for short contexts.
+constexpr int kCtxHiLo = 0x100;
+constexpr int kCtxLongContext = 4096;  // wide steps at least this long round P once to bf16
 hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
-                           int ctx_nw, hipStream_t st);
+                           int ctx_kind, hipStream_t st);
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                              hipStream_t st);
 hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st);
@@ -90,9 +94,15 @@ hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int 
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
 
-// rows per context workgroup for a given wave count
-inline int ctx_rows_per_wg(int nw) { return nw * 32; }
-// tokens per LDS tile of the context kernel
-inline int ctx_tile_tokens(int nw) { return nw >= 4 ? 64 : 32; }
+// rows per context workgroup for a given variant
+inline int ctx_rows_per_wg(int kind) { return (kind & 0xFF) * 32; }
+
+// Variant for one request of a step (bf16 path).
+inline int ctx_kind_for(int rows, int N, int d) {
+  if (rows <= 32) return 1 | kCtxHiLo;
+  if (rows <= 64 || d == 64) return (rows <= 64 ? 2 : 4) | kCtxHiLo;
+  if (rows <= 128) return 4 | kCtxHiLo;
+  return N >= kCtxLongContext ? 8 : (8 | kCtxHiLo);
+}
 
 }  // namespace gr

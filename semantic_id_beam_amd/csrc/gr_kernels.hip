@@ -359,10 +359,10 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
 // overlaps the other's MFMAs; P is rounded once to bf16.  Narrow steps (HBM- or
 // latency-bound) keep their staging registers and spend the idle MFMA time on a second
 // bf16 term of P.
-template <int D, int NW, int TT>
+template <int D, int NW, int TT, bool HILO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_ctx_attn_bf16(
     Dev dev, const StepReq *__restrict__ reqs, int n_reqs, int layer) {
-  ctx_attn_body<D, NW, TT, false>(dev, reqs, n_reqs, layer);
+  ctx_attn_body<D, NW, TT, HILO>(dev, reqs, n_reqs, layer);
 }
 template <int D, int NW, int TT>
 __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16_narrow(Dev dev, const StepReq *__restrict__ reqs,
@@ -1126,7 +1126,7 @@ __global__ void k_init_slot(Dev dev, int slot) {
 }  // namespace
 
 // ---------------------------------------------------------------------------- launchers
-hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs, int ctx_nw,
+hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs, int ctx_kind,
                            hipStream_t st) {
   if (total_wgs <= 0) return hipSuccess;
   if (dev.dm.dtype == 0) {
@@ -1136,20 +1136,24 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
       hipLaunchKernelGGL(k_ctx_attn_f32<128>, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
     return hipGetLastError();
   }
-  const dim3 blk(ctx_nw * 64), grid(total_wgs);
+  const int nw = ctx_kind & 0xFF;
+  const bool hilo = (ctx_kind & kCtxHiLo) != 0;
+  const dim3 blk(nw * 64), grid(total_wgs);
   if (dev.dm.d == 128) {
-    if (ctx_nw == 8)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
-    else if (ctx_nw == 4)
+    if (nw == 8 && hilo)
+      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64, true>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+    else if (nw == 8)
+      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64, false>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+    else if (nw == 4)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
-    else if (ctx_nw == 2)
+    else if (nw == 2)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 1, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
   } else {
-    if (ctx_nw >= 4)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<64, 4, 64>), grid, dim3(256), 0, st, dev, reqs, n_reqs, layer);
-    else if (ctx_nw == 2)
+    if (nw == 4)
+      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+    else if (nw == 2)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 1, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);

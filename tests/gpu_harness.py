@@ -90,6 +90,17 @@ def save_report(cfg, steps, **extra):
         f.write(json.dumps({"test": test, "config": cfg.name, "steps": steps, **extra}) + "\n")
 
 
+def progress(msg: str):
+    """Append a progress line to $GR_REPORT_DIR/progress.log when that is set (long GPU tests)."""
+    import os
+    import time
+    d = os.environ.get("GR_REPORT_DIR")
+    if d:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "progress.log"), "a") as f:
+            f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+
+
 def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
     """max over rows of max|got-ref| / max|ref| (rows = last axis)."""
     num = np.max(np.abs(got - ref), axis=-1)
