@@ -529,8 +529,10 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   for (Group &G : groups) {
     const int nw = G.kind & 0xFF;
     const int rows_wg = d.dtype == 1 ? gr::ctx_rows_per_wg(G.kind) : 32;
-    // workgroups per launch: about two per compute unit of 4 waves, fewer when wider
-    const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? 1024 : 2048) : 256;
+    // workgroups per launch: one per compute unit for the 8-wave kernel, two per unit for the
+    // one-wave streaming kernel (head_dim 128; its LDS ring allows two), else about two per
+    // compute unit of 4 waves
+    const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? 1024 : d.d == 128 ? 512 : 2048) : 256;
     int64_t units = 0;
     for (int i = G.start; i < G.start + G.count; ++i)
       units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)order[(size_t)i]]->n_bound * d.g, rows_wg);

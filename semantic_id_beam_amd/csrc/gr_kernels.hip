@@ -371,6 +371,579 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16_narrow(Dev dev, const
 }
 
 // --------------------------------------------------------------------------------------
+// Shared-context attention for wide steps, head_dim 128: 8 waves (two per SIMD), 32 query
+// rows each, 256 rows per workgroup; the arithmetic is that of ctx_attn_body, the schedule
+// is built for a long MFMA-bound token loop:
+//   * K and V^T tiles go from global memory straight into LDS (global_load_lds_dwordx4,
+//     1 KB of consecutive LDS per wave instruction): no staging registers, no LDS stores.
+//     A ring of NST stages of 64 tokens keeps NST-2 tiles in flight.
+//   * LDS rows are XOR-swizzled instead of padded: 16-byte column c of K row r sits at
+//     c ^ (r & 15), of V^T row r (half as long) at c ^ (r & 7) ^ ((r >> 3) & 1), so the
+//     operand reads of 16 consecutive lanes (16 consecutive rows) cover all 64 banks once.
+//   * QK^T of the next 32-token sub-tile is interleaved by hand with the softmax and PV of
+//     the current one, so the exponentials issue while the matrix core works.
+// One barrier per tile, placed before the first QK^T of tile it: tile it has landed in LDS
+// and every wave is past its last read of tile it-2, whose stage then receives tile
+// it+NST-2.  The barrier is a bare s_barrier behind an explicit vmcnt wait (a full
+// workgroup fence would wait for the tiles still in flight).
+// The copy is issued from inline assembly: the compiler then neither orders later LDS reads
+// behind it nor counts it; the explicit vmcnt waits below do both.  lds_addr is the byte
+// address in LDS and must be uniform over the wave (it goes through M0; one wait state
+// between the M0 write and the LDS-DMA instruction).
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0 || N == 4 || N == 8, "unsupported wait");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if constexpr (N == 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  else static_assert(N % 16 == 0 && N <= 48, "unsupported wait");
+}
+
+// --------------------------------------------------------------------------------------
+// Shared-context attention for narrow steps (at most 32 query rows per kv head, head_dim
+// 128), which stream the context once and are bound by HBM.  One wave per workgroup, so no
+// barrier: the wave's own vmcnt says when a tile has landed.  32-token tiles go from global
+// memory straight into a ring of NST LDS stages (NST-1 tiles in flight per wave); P is split
+// into two bf16 terms.  V^T rows are 64 bytes here: 16-byte column c of row r sits at
+// c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps 16 consecutive operand rows on 64 banks.
+template <int NST>
+__global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                        int layer) {
+  constexpr int D = 128, TT = 32, KB = D / 16, DB = D / 32;
+  constexpr int P = NST - 1;
+  constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
+  constexpr int KI = KCH / 64, VI = VCH / 64, LPT = KI + VI;
+  static_assert(LPT == 16 && NST >= 2 && NST <= 4, "wait immediates assume 16 copies per tile");
+  __shared__ bf16x8_t sK[NST][KCH];
+  __shared__ bf16x8_t sV[NST][VCH];
+
+  const int lane = threadIdx.x, hh = lane >> 5;
+  const int kx = lane & 15, vx = ((lane >> 1) ^ (lane >> 3)) & 3;
+  const int ri = find_req<0>(reqs, n_reqs, blockIdx.x);
+  const StepReq R = reqs[ri];
+  const Dims &dm = dev.dm;
+  const int local = blockIdx.x - R.wg_ctx;
+  const int rest = local >> 3;
+  const int rb = rest % R.row_blocks;
+  const int pidx = (rest / R.row_blocks) * 8 + (local & 7);
+  if (pidx >= dm.Hkv * R.splits) return;  // padding workgroup
+  const int h = pidx / R.splits, sp = pidx % R.splits;
+
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int s = R.level;
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  const int rows = n_live * dm.g;
+  const int row0 = rb * 32;
+  if (row0 >= rows) return;
+  const int q_row = row0 + (lane & 31);
+  const bool row_ok = q_row < rows;
+
+  const int t0 = sp * R.tps;
+  const int t1 = min(R.N, t0 + R.tps);
+  const int ntiles = (t1 - t0 + TT - 1) / TT;
+  const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
+  const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
+  uint32_t koff[KI], voff[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int p = i * 64 + lane, rl = p >> 4, c = (p & 15) ^ (rl & 15);
+    koff[i] = (uint32_t)(swap23(rl) * D + c * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int p = i * 64 + lane, row = p >> 2, c = (p & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    voff[i] = (uint32_t)row * (uint32_t)R.Np + (uint32_t)(c * 8);
+  }
+  const uint32_t kdst = lds_addr(&sK[0][0]), vdst = lds_addr(&sV[0][0]);
+  auto issue = [&](int tile) {
+    const int st = tile % NST, tb = t0 + tile * TT;
+    const uint16_t *kb = gK + (size_t)tb * D;
+    const uint16_t *vb = gV + tb;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) dma16(kb + koff[i], kdst + st * (KCH * 16) + i * 1024);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + i * 1024);
+  };
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+    if (k < ntiles) issue(k);
+
+  bf16x8_t qf[KB];
+  {
+    const uint16_t *qsrc = nullptr;
+    if (row_ok) {
+      const int j = q_row / dm.g, hq = h * dm.g + q_row % dm.g;
+      if (s == 0) {
+        qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq) * D;
+      } else {
+        const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
+        const int code = codes[j * dm.levels + (s - 1)];
+        qsrc = (const uint16_t *)dev.tok_q +
+               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
+  }
+  const float c2 = dm.scale_log2;
+  float M, l = 0.f;
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  float bmax;
+  {
+    float qn = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
+    qn += __shfl_xor(qn, 32);
+    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
+    const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
+    M = B - 60.f;
+    bmax = wave_max(B);
+  }
+  if (layer > 0) {
+    const int nr = min(rows, row0 + 32) - row0;
+    const int per = (nr + R.splits - 1) / R.splits;
+    const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
+    finish_rows<D>(dev, R, slot, layer - 1, h, r0, r1, lane, 64);
+  }
+  const bool fixed_ref = bmax <= 60.f;
+  if (!fixed_ref) M = kNegInf;
+
+  auto tile_step = [&](int it, auto mask_tag, auto fixed_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIXED = decltype(fixed_tag)::value;
+    const int st = it % NST;
+    const bf16x8_t *kr = &sK[st][(lane & 31) * (D / 8)];
+    const bf16x8_t *vr = &sV[st][(lane & 31) * (TT / 8)];
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[(kb * 2 + hh) ^ kx], qf[kb], sacc, 0, 0, 0);
+    if constexpr (MASK) {
+      const int tbase = t0 + it * TT + 8 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (tbase + 16 * (i >> 3) + (i & 7) >= t1) sacc[i] = kNegInf;
+    }
+    if constexpr (!FIXED) {
+      float mx = sacc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxs = mx * c2;
+      if (__ballot(mxs > M + 8.f) != 0ull) {
+        const float Mn = fmaxf(M, mxs);
+        const float f = fast_exp2(M - Mn);
+        l *= f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= f;
+        M = Mn;
+      }
+    }
+    bf16x8_t pf[2], pl[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sacc[i], c2, -M));
+      const __bf16 ph = (__bf16)p;
+      pf[i >> 3][i & 7] = ph;
+      pl[i >> 3][i & 7] = (__bf16)(p - (float)ph);
+      l += p;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const bf16x8_t vf = vr[db * 32 * (TT / 8) + ((pp * 2 + hh) ^ vx)];
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pp], oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[pp], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto run = [&](auto fixed_tag) {
+    using F = decltype(fixed_tag);
+    const bool partial = ((t1 - t0) % TT) != 0;
+    for (int it = 0; it < ntiles; ++it) {
+      // tile it has landed once at most the copies of the later tiles already issued remain
+      const int ahead = min(P - 1, ntiles - 1 - it);
+      if (ahead >= 2) vm_wait<2 * LPT>();
+      else if (ahead == 1) vm_wait<LPT>();
+      else vm_wait<0>();
+      if (it + P < ntiles) issue(it + P);  // into the stage of tile it-1, read by now
+      if (it + 1 < ntiles || !partial)
+        tile_step(it, std::false_type{}, F{});
+      else
+        tile_step(it, std::true_type{}, F{});
+    }
+  };
+  if (fixed_ref)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  const float ltot = l + __shfl_xor(l, 32);
+  if (row_ok) {
+    const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
+    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[layer & 1]) + prow, f32x2_t{M, ltot});
+    float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = db * 32 + 8 * a + 4 * hh;
+        gst<f32x4_t>(po + d0, f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
+                                      oacc[db][4 * a + 3]});
+      }
+    }
+  }
+}
+
+template <int NST, bool HILO>
+__global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                       int layer) {
+  constexpr int D = 128, NW = 8, TT = 64, KB = D / 16, DB = D / 32, NT = NW * 64;
+  constexpr int P = NST - 2;                          // tiles in flight beyond the one in use
+  constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
+  constexpr int KI = KCH / NT, VI = VCH / NT;        // DMA instructions per wave and tile
+  constexpr int LPT = KI + VI;
+  static_assert(NST >= 3 && NST <= 4, "ring of three or four stages");
+  static_assert(TT == kTileTok, "tiles never cross the zero-padded end of the context");
+  __shared__ bf16x8_t sK[NST][KCH];   // [token row swap23(r)][column c ^ (row & 15)]
+  __shared__ bf16x8_t sV[NST][VCH];   // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
+  __shared__ float sBound[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
+  const int kx = lane & 15, vx = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of this lane's operand row
+  const int ri = find_req<0>(reqs, n_reqs, blockIdx.x);
+  const StepReq R = reqs[ri];
+  const Dims &dm = dev.dm;
+  const int local = blockIdx.x - R.wg_ctx;
+  const int rest = local >> 3;
+  const int rb = rest % R.row_blocks;
+  const int pidx = (rest / R.row_blocks) * 8 + (local & 7);
+  if (pidx >= dm.Hkv * R.splits) return;  // padding workgroup
+  const int h = pidx / R.splits, sp = pidx % R.splits;
+
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int s = R.level;
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  const int rows = n_live * dm.g;
+  const int row0 = rb * (NW * 32);
+  if (row0 >= rows) return;  // whole workgroup idle
+
+  const int wrow = row0 + w * 32;
+  const bool wave_active = wrow < rows;
+  const int q_row = wrow + (lane & 31);
+  const bool row_ok = q_row < rows;
+
+  const int t0 = sp * R.tps;
+  const int t1 = min(R.N, t0 + R.tps);
+  const int ntiles = (t1 - t0 + TT - 1) / TT;
+  const int nsub = (t1 - t0 + 31) / 32;
+  const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
+  const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
+
+  // per-lane DMA sources (elements from the tile's first token) for this wave's chunks
+  uint32_t koff[KI], voff[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int p = (w * KI + i) * 64 + lane, rl = p >> 4, c = (p & 15) ^ (rl & 15);
+    koff[i] = (uint32_t)(swap23(rl) * D + c * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int p = (w * VI + i) * 64 + lane, row = p >> 3, c = (p & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+    voff[i] = (uint32_t)row * (uint32_t)R.Np + (uint32_t)(c * 8);
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t kdst = lds_addr(&sK[0][0]) + wu * KI * 1024, vdst = lds_addr(&sV[0][0]) + wu * VI * 1024;
+  auto issue = [&](int tile) {
+    const int st = tile % NST, tb = t0 + tile * TT;
+    const uint16_t *kb = gK + (size_t)tb * D;
+    const uint16_t *vb = gV + tb;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) dma16(kb + koff[i], kdst + st * (KCH * 16) + i * 1024);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + i * 1024);
+  };
+  // the tiles the ring holds ahead of the first one go out before anything else
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+    if (k < ntiles) issue(k);
+
+  // ---- query fragments (B operand of QK^T): lane holds Q[q_row][kb*16 + 8*hh .. +8]
+  bf16x8_t qf[KB];
+  {
+    const uint16_t *qsrc = nullptr;
+    if (row_ok) {
+      const int j = q_row / dm.g, hq = h * dm.g + q_row % dm.g;
+      if (s == 0) {
+        qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq) * D;
+      } else {
+        const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
+        const int code = codes[j * dm.levels + (s - 1)];
+        qsrc = (const uint16_t *)dev.tok_q +
+               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
+  }
+
+  const float c2 = dm.scale_log2;
+  float M, l = 0.f;
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  // fixed score reference from the Cauchy-Schwarz bound, as in ctx_attn_body
+  {
+    float qn = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
+    qn += __shfl_xor(qn, 32);
+    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
+    const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
+    M = B - 60.f;
+    const float bw = wave_max(B);
+    if (lane == 0) sBound[w] = bw;
+  }
+  if (layer > 0) {
+    // finish the previous layer for this workgroup's share of the row block
+    const int nr = min(rows, row0 + NW * 32) - row0;
+    const int per = (nr + R.splits - 1) / R.splits;
+    const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
+    finish_rows<D>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
+  }
+  // the first P tiles have landed (explicitly: the compiler does not count the copies) and
+  // sBound is visible
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float bmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) bmax = fmaxf(bmax, sBound[i]);
+  const bool fixed_ref = bmax <= 60.f;  // uniform over the workgroup
+  if (!fixed_ref) M = kNegInf;
+
+  auto qk = [&](int tile, int sub) {
+    const bf16x8_t *kr = &sK[tile % NST][(sub * 32 + (lane & 31)) * (D / 8)];
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[(kb * 2 + hh) ^ kx], qf[kb], acc, 0, 0, 0);
+    return acc;
+  };
+  // softmax of sub-tile u (first token t0 + 32u) and PV with its tile's V^T
+  auto soft_pv = [&](f32x16_t sacc, int u, auto mask_tag, auto fixed_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIXED = decltype(fixed_tag)::value;
+    if constexpr (MASK) {
+      const int tbase = t0 + u * 32 + 8 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (tbase + 16 * (i >> 3) + (i & 7) >= t1) sacc[i] = kNegInf;
+    }
+    if constexpr (!FIXED) {
+      float mx = sacc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxs = mx * c2;
+      if (__ballot(mxs > M + 8.f) != 0ull) {
+        const float Mn = fmaxf(M, mxs);
+        const float f = fast_exp2(M - Mn);
+        l *= f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= f;
+        M = Mn;
+      }
+    }
+    bf16x8_t pf[2], pl[2];
+    if constexpr (HILO) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sacc[i], c2, -M));
+        const __bf16 ph = (__bf16)p;
+        pf[i >> 3][i & 7] = ph;
+        pl[i >> 3][i & 7] = (__bf16)(p - (float)ph);
+        l += p;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (__bf16)fast_exp2(fmaf(sacc[i], c2, -M));
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 0, 1), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 2, 3), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 4, 5), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 6, 7), ones, l, false);
+      }
+    }
+    const int tile = u >> 1, sub = u & 1;
+    const bf16x8_t *vr = &sV[tile % NST][(lane & 31) * (TT / 8)];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const bf16x8_t vf = vr[db * 32 * (TT / 8) + ((sub * 4 + pp * 2 + hh) ^ vx)];
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pp], oacc[db], 0, 0, 0);
+        if constexpr (HILO) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[pp], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+  // Steady-state step with the fixed reference, sub-tile u unmasked: QK^T of sub-tile u+1
+  // and softmax + PV of sub-tile u, interleaved by hand.  Issue is in order within a wave and
+  // the two waves of a SIMD do not overlap each other's exponentials with their MFMAs, so the
+  // softmax is spread over this wave's own MFMAs: element k (k < 8) after the k-th QK^T MFMA,
+  // elements 8..15 two at a time after the first four PV MFMAs (those use the first eight
+  // only).  LDS operands are fetched two MFMAs ahead; sched_barrier keeps the order.
+  auto block_fixed = [&](int u, const f32x16_t &sc) {
+    const int tq = (u + 1) >> 1, sq = (u + 1) & 1, tp = u >> 1, spv = u & 1;
+    const bf16x8_t *kr = &sK[tq % NST][(sq * 32 + (lane & 31)) * (D / 8)];
+    const bf16x8_t *vr = &sV[tp % NST][(lane & 31) * (TT / 8)];
+    auto kfrag = [&](int kb) { return kr[(kb * 2 + hh) ^ kx]; };
+    auto vfrag = [&](int j) {  // j = pp*4 + db
+      return vr[(j & 3) * 32 * (TT / 8) + ((spv * 4 + (j >> 2) * 2 + hh) ^ vx)];
+    };
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8_t kf[3], vf[3], pf[2], pl[2];
+    float pr[8];
+    // the pair (i, i+1) of P: bf16 term(s) and its share of l
+    auto pair = [&](float p0, float p1, int i) {
+      const bf16x2_t h2 = {(__bf16)p0, (__bf16)p1};
+      pf[i >> 3][i & 7] = h2[0];
+      pf[i >> 3][(i + 1) & 7] = h2[1];
+      if constexpr (HILO) {
+        pl[i >> 3][i & 7] = (__bf16)(p0 - (float)h2[0]);
+        pl[i >> 3][(i + 1) & 7] = (__bf16)(p1 - (float)h2[1]);
+        l += p0 + p1;
+      } else {
+        l = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, l, false);
+      }
+    };
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb + 2 < KB) kf[(kb + 2) % 3] = kfrag(kb + 2);
+      else vf[(kb + 2 - KB) % 3] = vfrag(kb + 2 - KB);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 3], qf[kb], acc, 0, 0, 0);
+      pr[kb] = fast_exp2(fmaf(sc[kb], c2, -M));
+      if (kb & 1) pair(pr[kb - 1], pr[kb], kb - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + 2 < 8) vf[(j + 2) % 3] = vfrag(j + 2);
+      oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % 3], pf[j >> 2], oacc[j & 3], 0, 0, 0);
+      if constexpr (HILO)
+        oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % 3], pl[j >> 2], oacc[j & 3], 0, 0, 0);
+      if (j < 4)
+        pair(fast_exp2(fmaf(sc[8 + 2 * j], c2, -M)), fast_exp2(fmaf(sc[9 + 2 * j], c2, -M)), 8 + 2 * j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+  static_assert(KB == 8, "the interleave assumes eight QK^T MFMAs per sub-tile");
+
+  // before the first QK^T of tile it (it >= 1): tile it landed, then the barrier, then tile
+  // it+P goes into the stage of tile it-2
+  auto advance = [&](int it) {
+    const int ahead = min(P - 1, ntiles - 1 - it);  // own tiles issued after tile it
+    if (P == 2 && ahead > 0) vm_wait_barrier<LPT>();
+    else vm_wait_barrier<0>();
+    if (it + P < ntiles) issue(it + P);
+  };
+
+  auto run = [&](auto fixed_tag) {
+    using F = decltype(fixed_tag);
+    if (P < ntiles) issue(P);  // stage P was never used
+    // s0 holds the scores of even sub-tiles, s1 of odd ones
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+    if (wave_active) s0 = qk(0, 0);
+    // steady state: both sub-tiles of tile it are unmasked and tile it+1 exists
+    int it = 0;
+    for (; 2 * it + 2 < nsub; ++it) {
+      if (wave_active) {
+        if constexpr (F::value) {
+          s1 = block_fixed(2 * it, s0);
+        } else {
+          s1 = qk(it, 1);
+          soft_pv(s0, 2 * it, std::false_type{}, F{});
+        }
+      }
+      advance(it + 1);
+      if (wave_active) {
+        if constexpr (F::value) {
+          s0 = block_fixed(2 * it + 1, s1);
+        } else {
+          s0 = qk(it + 1, 0);
+          soft_pv(s1, 2 * it + 1, std::false_type{}, F{});
+        }
+      }
+    }
+    // tail: one or two sub-tiles of the last tile; only the very last one can be partial
+    const bool partial = ((t1 - t0) & 31) != 0;
+    if (wave_active) {
+      if (2 * it + 1 < nsub) {
+        s1 = qk(it, 1);
+        soft_pv(s0, 2 * it, std::false_type{}, F{});
+        if (partial)
+          soft_pv(s1, nsub - 1, std::true_type{}, F{});
+        else
+          soft_pv(s1, nsub - 1, std::false_type{}, F{});
+      } else if (partial) {
+        soft_pv(s0, nsub - 1, std::true_type{}, F{});
+      } else {
+        soft_pv(s0, nsub - 1, std::false_type{}, F{});
+      }
+    }
+  };
+  if (fixed_ref)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  const float ltot = l + __shfl_xor(l, 32);
+  if (wave_active && row_ok) {
+    const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
+    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[layer & 1]) + prow, f32x2_t{M, ltot});
+    float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = db * 32 + 8 * a + 4 * hh;
+        gst<f32x4_t>(po + d0, f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
+                                      oacc[db][4 * a + 3]});
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------
 // Shared-context attention for float32 models (vector ALU).  One wave per
 // (request, kv head, query row, token range); lane = token for the scores,
 // lane = feature for the output.
@@ -1141,15 +1714,15 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
   const dim3 blk(nw * 64), grid(total_wgs);
   if (dev.dm.d == 128) {
     if (nw == 8 && hilo)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64, true>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_wide<4, true>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else if (nw == 8)
-      hipLaunchKernelGGL((k_ctx_attn_bf16<128, 8, 64, false>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_wide<4, false>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else if (nw == 4)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else if (nw == 2)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 1, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      hipLaunchKernelGGL((k_ctx_attn_stream<4>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
   } else {
     if (nw == 4)
       hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
