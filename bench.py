@@ -27,6 +27,29 @@ METRIC = "beam-decode req/s + step µs at ctx 5000, beam 256; % MFMA peak, HBM G
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM bytes per launch of the context-attention kernels on this workload, from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
+# the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000);
+# profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel source they were taken
+# on: with any other gr_kernels.hip the traffic is reported as null.
+MEASURED_TRAFFIC = {
+    "workload": "ctx5k_beam256_r8",
+    "source_sha256": "591b0c6d640bffe6723e0c48a764d834939b4f7276d236f6c49a3a0af62865cf",
+    "k_ctx_attn_wide": {"read": 222776469, "written": 58345765},
+    "k_ctx_attn_stream": {"read": 166318020, "written": 603867},
+}
+
+
+def measured_traffic(cfg, kernel):
+    import hashlib
+    src = os.path.join(ROOT, "semantic_id_beam_amd", "csrc", "gr_kernels.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if cfg.name != MEASURED_TRAFFIC["workload"] or sha != MEASURED_TRAFFIC["source_sha256"]:
+        return None
+    t = MEASURED_TRAFFIC[kernel]
+    return t["read"] + t["written"]
+
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -66,10 +89,17 @@ def cpu_baseline(cfg, n_beams: int):
         n = min(W, len(ps.levels[s]), n * cfg.codebook)
         evals += n
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {
         "value": 1.0 / (evals * per_beam),
         "unit": "req/s",
         "cores": int(threads),
+        "cpu": cpu,
         "kind": "oracle",
         "sample": (f"request 0, level 1, {len(beams)} beams, each recomputed as an independent "
                    f"{cfg.n_layers}-layer sequence of ctx+1 tokens with logits, log-softmax and candidates "
@@ -157,11 +187,15 @@ def main():
     G.gr_engine_profile_reset(eng.eng)
     G.gr_engine_set_profiling(eng.eng, True)
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(args.steps):
         decode_all()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    decode_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     G.gr_engine_set_profiling(eng.eng, False)
     elapsed = t1 - t0
     log(f"timed {args.steps} decodes in {elapsed:.3f} s")
@@ -191,18 +225,26 @@ def main():
     achieved_gbs0 = ctx_bytes(0) * n_0 / (ms_0 * 1e-3) / 1e9 if ms_0 > 0 else 0.0
     step_us = {f"level{s}": 1e3 * prof["step"][s][0] / max(prof["step"][s][1], 1) for s in range(lv)}
 
+    # the launch of layer l also finishes layer l-1 (BeamKV append, beam tokens, split merge,
+    # h += o): its time is in the denominator, its bytes are not in the algorithmic count
+    wide = cfg.dtype == "bf16" and cfg.head_dim == 128
     roofline = {
         "bound": "mfma", "achieved": round(achieved_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(achieved_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-        "kernel": "k_ctx_attn_bf16 (levels %s)" % levels_mfma, "launches": int(n_m),
+        "frac": round(achieved_tf / PEAK_BF16_TFLOPS, 4),
+        "traffic": measured_traffic(cfg, "k_ctx_attn_wide") if wide else None,
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+        "kernel": ("k_ctx_attn_wide" if wide else "k_ctx_attn") + " (levels %s)" % levels_mfma,
+        "launches": int(n_m),
         "avg_launch_us": round(1e3 * ms_m / max(n_m, 1), 2),
         "algorithmic_per_launch": f"{ctx_flops(levels_mfma[-1]) / 1e9:.2f} GFLOP" if levels_mfma else None,
     }
     kernels = {
-        "ctx_attn_level0": {"bound": "hbm", "achieved_GBs": round(achieved_gbs0, 1), "peak_GBs": PEAK_HBM_GBS,
+        "ctx_attn_level0": {"kernel": "k_ctx_attn_stream" if wide else "k_ctx_attn",
+                            "bound": "hbm", "achieved_GBs": round(achieved_gbs0, 1), "peak_GBs": PEAK_HBM_GBS,
                             "frac": round(achieved_gbs0 / PEAK_HBM_GBS, 4),
                             "avg_launch_us": round(1e3 * ms_0 / max(n_0, 1), 2),
-                            "algorithmic_MB_per_launch": round(ctx_bytes(0) / 1e6, 2)},
+                            "algorithmic_MB_per_launch": round(ctx_bytes(0) / 1e6, 2),
+                            "traffic": measured_traffic(cfg, "k_ctx_attn_stream") if wide else None},
     }
     for name in ("beam_merge", "logits", "topk"):
         tot = sum(prof[name][s][0] for s in range(lv))
@@ -227,6 +269,9 @@ def main():
                    "ctx_len": cfg.ctx_len, "beam_width": cfg.beam_width, "levels": lv,
                    "codebook": cfg.codebook, "items": cfg.n_items, "live_beams_per_level": n_live[0].tolist()},
         "step_us": {k: round(v, 1) for k, v in step_us.items()},
+        "decode_ms": {"p10": round(float(np.percentile(decode_ms, 10)), 3),
+                      "p50": round(float(np.percentile(decode_ms, 50)), 3),
+                      "p90": round(float(np.percentile(decode_ms, 90)), 3)},
         "roofline": roofline,
         "kernels": kernels,
     }
