@@ -179,7 +179,7 @@ def main():
             eng.reset(r)
         for _ in range(lv):
             eng.step(rids)
-        return [eng.beams(r) for r in rids]
+        return eng.beams_batch(rids)
 
     for i in range(args.warmup):
         decode_all()

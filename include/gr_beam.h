@@ -179,6 +179,20 @@ gr_status gr_beam_step(gr_engine *eng, const int64_t *request_ids, int32_t n_req
 gr_status gr_beams_get(gr_engine *eng, int64_t request_id, int32_t capacity, int32_t *codes,
                        float *scores, int32_t *n_beams, void *stream);
 
+/* gr_beams_get for several requests at once (the same multi-beam return, [GR]
+ * continuous batching): one small gather kernel, one device-to-host copy
+ * through engine-owned pinned memory and one synchronisation of `stream` for
+ * the whole batch.  Request i (request_ids[i]) fills codes host
+ * [n_requests][capacity][n_levels] at row block i, scores host
+ * [n_requests][capacity] at row i and n_beams host [n_requests] at i; rows past
+ * n_beams[i] are left untouched.  Errors: GR_E_INVALID_ARG (n_requests outside
+ * 1..max_requests, null outputs, or some request with more beams than capacity:
+ * every n_beams[i] is still written, and the rows of requests that fit),
+ * GR_E_NOT_FOUND, GR_E_BAD_STATE before a request's last step; nothing is
+ * copied when an id is unknown or unfinished. */
+gr_status gr_beams_get_batch(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, int32_t capacity,
+                             int32_t *codes, float *scores, int32_t *n_beams, void *stream);
+
 /* Releases a request's slot and pool space (host bookkeeping only; later work
  * on the same stream may reuse them).  Errors: GR_E_NOT_FOUND. */
 gr_status gr_request_release(gr_engine *eng, int64_t request_id);
@@ -214,8 +228,10 @@ typedef enum {
   GR_PROF_STEP = 4        /* a whole gr_beam_step, first launch to last */
 } gr_prof_kind;
 
-/* When enabled, gr_beam_step brackets each launch with HIP events recorded on
- * its stream (a bounded pool; it waits for old events when the pool is full).
+/* When enabled, gr_beam_step times each launch with HIP events carried by the
+ * dispatch itself (hipExtLaunchKernel start/stop events: no marker packets are
+ * inserted between kernels, so the timed stream runs as it does unprofiled).  The
+ * events come from a bounded pool; a step waits for old events when it is full.
  * Buckets are keyed by kind and by the decode level of the step (0..n_levels-1;
  * steps whose requests are at different levels go to bucket n_levels). */
 gr_status gr_engine_set_profiling(gr_engine *eng, int32_t enable);

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "
 EXPORTS = [
     "gr_engine_create", "gr_engine_workspace_bytes", "gr_engine_bind_workspace", "gr_engine_destroy",
     "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
-    "gr_request_release", "gr_request_reset", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
+    "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
     "gr_engine_profile_reset",
 ]
@@ -89,6 +89,7 @@ def lib() -> C.CDLL:
         "gr_ctx_kv_load": (i32, [vp, i64, i32, i32, vp, vp, vp, u32, vp]),
         "gr_beam_step": (i32, [vp, P(i64), i32, vp]),
         "gr_beams_get": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
+        "gr_beams_get_batch": (i32, [vp, P(i64), i32, i32, vp, vp, vp, vp]),
         "gr_request_release": (i32, [vp, i64]),
         "gr_request_reset": (i32, [vp, i64, vp]),
         "gr_last_error": (C.c_char_p, []),
@@ -173,6 +174,18 @@ def gr_beams_get(eng: int, rid: int, capacity: int, n_levels: int, stream: int =
     n = C.c_int32()
     _check(lib().gr_beams_get(eng, rid, capacity, _host(codes), _host(scores), C.byref(n), stream))
     return codes[: n.value], scores[: n.value]
+
+
+def gr_beams_get_batch(eng: int, request_ids, capacity: int, n_levels: int, stream: int = 0):
+    """[(codes [n_i][n_levels], scores [n_i]) for each id], one synchronisation for all."""
+    ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+    n = ids.shape[0]
+    codes = np.zeros((n, max(capacity, 1), n_levels), dtype=np.int32)
+    scores = np.zeros((n, max(capacity, 1)), dtype=np.float32)
+    nb = np.zeros(n, dtype=np.int32)
+    _check(lib().gr_beams_get_batch(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), n, capacity, _host(codes),
+                                    _host(scores), _host(nb), stream))
+    return [(codes[i, : nb[i]], scores[i, : nb[i]]) for i in range(n)]
 
 
 def gr_request_release(eng: int, rid: int):

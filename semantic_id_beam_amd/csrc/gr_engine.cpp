@@ -15,6 +15,7 @@
 #include <string>
 #include <unordered_map>
 #include <unordered_set>
+#include <utility>
 #include <vector>
 
 #include "gr_beam.h"
@@ -50,8 +51,10 @@ struct gr_engine {
   std::vector<int64_t> trie_off;
 
   // workspace layout (byte offsets)
-  size_t off_mask = 0, off_child = 0, off_slots = 0, off_pool = 0, off_work = 0, ws_need = 0;
+  size_t off_mask = 0, off_child = 0, off_slots = 0, off_pool = 0, off_work = 0, off_out = 0, ws_need = 0;
   size_t work_bytes = 0;  // one ring entry
+  size_t out_bytes = 0;   // results of one request in the staging area (gr_beams_get_batch)
+  uint8_t *out_host = nullptr;  // pinned copy of the staging area
   uint8_t *ws = nullptr;
   bool bound = false;
   bool poisoned = false;
@@ -71,10 +74,12 @@ struct gr_engine {
   std::unordered_map<int64_t, Req> reqs;
   std::vector<int> free_slots;
 
-  // profiling: event pairs around launches, folded into [kind][level] buckets
+  // profiling: timing events carried by the launches themselves (no marker packets between
+  // kernels), folded into [kind][level] buckets.  A record spans two events of the pool.
   bool prof = false;
-  std::vector<hipEvent_t> prof_ev;  // 2 per record
-  struct ProfRec { int kind, level; };
+  std::vector<hipEvent_t> prof_ev;
+  int prof_next = 0;  // next unused event of the pool
+  struct ProfRec { int kind, level, a, b; };
   std::vector<ProfRec> prof_pending;
   double prof_ms[5][gr::kMaxLevels + 1] = {};
   int64_t prof_n[5][gr::kMaxLevels + 1] = {};
@@ -93,43 +98,49 @@ gr_status check_dev(gr_engine *e, hipError_t err, const char *what) {
   return fail(GR_E_DEVICE, std::string(what) + ": " + hipGetErrorString(err));
 }
 
-constexpr int kProfPool = 1024;  // event pairs
+constexpr int kProfPool = 2048;  // events
 
 gr_status prof_fold(gr_engine *e) {
-  for (size_t i = 0; i < e->prof_pending.size(); ++i) {
-    hipEvent_t a = e->prof_ev[2 * i], b = e->prof_ev[2 * i + 1];
+  for (const auto &p : e->prof_pending) {
+    hipEvent_t a = e->prof_ev[(size_t)p.a], b = e->prof_ev[(size_t)p.b];
     gr_status r = check_dev(e, hipEventSynchronize(b), "profiling event");
     if (r != GR_OK) return r;
     float ms = 0.f;
     if ((r = check_dev(e, hipEventElapsedTime(&ms, a, b), "profiling event")) != GR_OK) return r;
-    const auto &p = e->prof_pending[i];
     e->prof_ms[p.kind][p.level] += ms;
     e->prof_n[p.kind][p.level] += 1;
   }
   e->prof_pending.clear();
+  e->prof_next = 0;
   return GR_OK;
 }
 
-// Makes room for `count` records before a step starts (every pending record is
-// complete then, so folding is safe).  Returns false when profiling is off or
-// the step needs more records than the pool holds.
+// Makes room for `count` events before a step starts (every pending record is complete
+// then, so folding is safe).  Returns false when profiling is off or the step needs more
+// events than the pool holds.
 bool prof_reserve(gr_engine *e, int count) {
   if (!e->prof || count > kProfPool) return false;
-  if ((int)e->prof_pending.size() + count > kProfPool && prof_fold(e) != GR_OK) return false;
+  if (e->prof_next + count > kProfPool && prof_fold(e) != GR_OK) return false;
   return true;
 }
 
-// Records the start event of a profiled launch; returns the record index or -1.
-int prof_begin(gr_engine *e, bool on, int kind, int level, hipStream_t st) {
-  if (!on) return -1;
-  const int i = (int)e->prof_pending.size();
-  if (hipEventRecord(e->prof_ev[2 * i], st) != hipSuccess) return -1;
-  e->prof_pending.push_back({kind, level});
-  return i;
+// A fresh (start, stop) event pair for a profiled launch; {-1, -1} when off.
+std::pair<int, int> prof_pair(gr_engine *e, bool on) {
+  if (!on) return {-1, -1};
+  const int a = e->prof_next;
+  e->prof_next += 2;
+  return {a, a + 1};
 }
 
-void prof_end(gr_engine *e, int i, hipStream_t st) {
-  if (i >= 0) (void)hipEventRecord(e->prof_ev[2 * i + 1], st);
+gr::LaunchEv prof_ev(gr_engine *e, int a, int b) {
+  gr::LaunchEv ev;
+  if (a >= 0) ev.start = e->prof_ev[(size_t)a];
+  if (b >= 0) ev.stop = e->prof_ev[(size_t)b];
+  return ev;
+}
+
+void prof_record(gr_engine *e, int kind, int level, std::pair<int, int> ab) {
+  if (ab.first >= 0) e->prof_pending.push_back({kind, level, ab.first, ab.second});
 }
 
 gr_status build_trie(gr_engine *e, const gr_item_set *items) {
@@ -236,6 +247,10 @@ void layout(gr_engine *e) {
   e->work_bytes = align_up(sizeof(gr::StepReq) * (size_t)e->opts.max_requests, A);
   e->off_work = w;
   w = align_up(w + e->work_bytes * kRing, A);
+  // result staging: per request n_live (16-byte header), codes [W][levels], scores [W]
+  e->out_bytes = align_up(16 + W * d.levels * 4 + W * 4, A);
+  e->off_out = w;
+  w = align_up(w + e->out_bytes * (size_t)e->opts.max_requests, A);
   e->ws_need = w;
 }
 
@@ -368,6 +383,9 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
                                        hipMemcpyHostToDevice, st), "trie upload")) != GR_OK)
     return r;
   if ((r = check_dev(e, hipStreamSynchronize(st), "trie upload")) != GR_OK) return r;
+  if ((r = check_dev(e, hipHostMalloc((void **)&e->out_host, e->out_bytes * (size_t)e->opts.max_requests,
+                                      hipHostMallocDefault), "pinned result staging")) != GR_OK)
+    return r;
   e->pinned.assign(kRing, nullptr);
   e->events.assign(kRing, nullptr);
   e->event_used.assign(kRing, false);
@@ -378,7 +396,7 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
     if ((r = check_dev(e, hipEventCreateWithFlags(&e->events[i], hipEventDisableTiming), "event")) != GR_OK)
       return r;
   }
-  e->prof_ev.assign(2 * kProfPool, nullptr);
+  e->prof_ev.assign(kProfPool, nullptr);
   for (auto &ev : e->prof_ev)
     if ((r = check_dev(e, hipEventCreate(&ev), "event")) != GR_OK) return r;
   gr::Dev &dv = e->dev;
@@ -406,6 +424,7 @@ gr_status gr_engine_destroy(gr_engine *e) {
       if (ev) (void)hipEventDestroy(ev);
     for (auto *p : e->pinned)
       if (p) (void)hipHostFree(p);
+    if (e->out_host) (void)hipHostFree(e->out_host);
   }
   delete e;
   return GR_OK;
@@ -587,33 +606,41 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   int plevel = rs[0]->level;
   for (auto *R : rs)
     if (R->level != plevel) plevel = d.levels;
-  const bool pon = prof_reserve(e, 2 * d.L + 3);
-  const int pstep = prof_begin(e, pon, GR_PROF_STEP, plevel, st);
+  const bool pon = prof_reserve(e, 2 * (2 * d.L + 2));
+  int step_start = -1;
   for (int l = 0; l < d.L; ++l) {
-    int pi = prof_begin(e, pon, GR_PROF_CTX_ATTN, plevel, st);
-    for (const Group &G : groups)
-      if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, st),
+    const auto pc = prof_pair(e, pon);
+    if (l == 0) step_start = pc.first;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group &G = groups[gi];
+      const gr::LaunchEv ev = prof_ev(e, gi == 0 ? pc.first : -1, gi + 1 == groups.size() ? pc.second : -1);
+      if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, st, ev),
                          "context attention")) != GR_OK)
         return r;
-    prof_end(e, pi, st);
+    }
+    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc);
     // float32: finish every layer separately; bf16: layer l is finished inside layer l+1's
     // context kernel, and the last layer here
     if (d.dtype == 0 || l == d.L - 1) {
-      pi = prof_begin(e, pon, GR_PROF_BEAM_MERGE, plevel, st);
-      if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st), "beam attention/merge")) !=
-          GR_OK)
+      const auto pm = prof_pair(e, pon);
+      if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st, prof_ev(e, pm.first, pm.second)),
+                         "beam attention/merge")) != GR_OK)
         return r;
-      prof_end(e, pi, st);
+      prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
     }
   }
-  int pi = prof_begin(e, pon, GR_PROF_LOGITS, plevel, st);
-  if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st), "logits")) != GR_OK) return r;
-  prof_end(e, pi, st);
-  pi = prof_begin(e, pon, GR_PROF_TOPK, plevel, st);
-  if ((r = check_dev(e, gr::launch_lsm(e->dev, dw, n, wg_lsm, st), "log-softmax")) != GR_OK) return r;
-  if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, max_cand, st), "top-k")) != GR_OK) return r;
-  prof_end(e, pi, st);
-  prof_end(e, pstep, st);
+  const auto pl = prof_pair(e, pon);
+  if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st, prof_ev(e, pl.first, pl.second)),
+                     "logits")) != GR_OK)
+    return r;
+  prof_record(e, GR_PROF_LOGITS, plevel, pl);
+  const auto pt = prof_pair(e, pon);
+  if ((r = check_dev(e, gr::launch_lsm(e->dev, dw, n, wg_lsm, st, prof_ev(e, pt.first, -1)), "log-softmax")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, max_cand, st, prof_ev(e, -1, pt.second)), "top-k")) != GR_OK)
+    return r;
+  prof_record(e, GR_PROF_TOPK, plevel, pt);
+  prof_record(e, GR_PROF_STEP, plevel, {step_start, pt.second});
   for (auto *R : rs) {
     const int s = R->level;
     int64_t nb = std::min<int64_t>((int64_t)R->W, (int64_t)R->n_bound * d.V);
@@ -642,27 +669,58 @@ gr_status d2h(gr_engine *e, void *dst, const void *src, size_t bytes, hipStream_
 }
 }  // namespace
 
+gr_status gr_beams_get_batch(gr_engine *e, const int64_t *ids, int32_t n, int32_t cap, int32_t *codes,
+                             float *scores, int32_t *n_beams, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (!ids || n < 1 || n > e->opts.max_requests) return fail(GR_E_INVALID_ARG, "need 1..max_requests ids");
+  if (!n_beams || cap < 0 || (cap > 0 && (!codes || !scores))) return fail(GR_E_INVALID_ARG, "null output");
+  const int lv = e->dm.levels;
+  std::vector<int32_t> slots((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    auto it = e->reqs.find(ids[i]);
+    if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+    if (it->second.level != lv) return fail(GR_E_BAD_STATE, "request has not decoded every level yet");
+    slots[(size_t)i] = it->second.slot;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *dst = e->ws + e->off_out;
+  gr_status r;
+  for (int i0 = 0; i0 < n; i0 += gr::kGatherMax) {
+    const int m = std::min(gr::kGatherMax, n - i0);
+    if ((r = check_dev(e, gr::launch_gather_results(e->dev, slots.data() + i0, m, lv & 1, dst + e->out_bytes * i0,
+                                                    e->out_bytes, st),
+                       "result gather")) != GR_OK)
+      return r;
+  }
+  if ((r = check_dev(e, hipMemcpyAsync(e->out_host, dst, e->out_bytes * (size_t)n, hipMemcpyDeviceToHost, st),
+                     "result copy")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  bool over = false;
+  const size_t W = (size_t)e->dm.W_max;
+  for (int i = 0; i < n; ++i) {
+    const uint8_t *src = e->out_host + e->out_bytes * (size_t)i;
+    int32_t nl;
+    std::memcpy(&nl, src, 4);
+    n_beams[i] = nl;
+    if (nl > cap) {
+      over = true;
+      continue;
+    }
+    if (nl > 0) {
+      std::memcpy(codes + (size_t)i * cap * lv, src + 16, (size_t)nl * lv * 4);
+      std::memcpy(scores + (size_t)i * cap, src + 16 + W * lv * 4, (size_t)nl * 4);
+    }
+  }
+  if (over) return fail(GR_E_INVALID_ARG, "capacity smaller than the number of beams");
+  return GR_OK;
+}
+
 gr_status gr_beams_get(gr_engine *e, int64_t rid, int32_t cap, int32_t *codes, float *scores, int32_t *n_beams,
                        void *stream) {
-  gr_engine::Req *R;
-  gr_status r = find_req(e, rid, &R);
-  if (r != GR_OK) return r;
-  if (!n_beams || cap < 0 || (cap > 0 && (!codes || !scores))) return fail(GR_E_INVALID_ARG, "null output");
-  if (R->level != e->dm.levels) return fail(GR_E_BAD_STATE, "request has not decoded every level yet");
-  hipStream_t st = (hipStream_t)stream;
-  uint8_t *sb = slot_ptr(e, R);
-  const int cur = R->level & 1, lv = e->dm.levels;
-  int32_t nl = 0;
-  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * cur, 4, st)) != GR_OK) return r;
-  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
-  *n_beams = nl;
-  if (nl > cap) return fail(GR_E_INVALID_ARG, "capacity smaller than the number of beams");
-  if (nl > 0) {
-    if ((r = d2h(e, codes, sb + e->sl.codes[cur], (size_t)nl * lv * 4, st)) != GR_OK) return r;
-    if ((r = d2h(e, scores, sb + e->sl.score[cur], (size_t)nl * 4, st)) != GR_OK) return r;
-    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
-  }
-  return GR_OK;
+  return gr_beams_get_batch(e, &rid, 1, cap, codes, scores, n_beams, stream);
 }
 
 gr_status gr_debug_beam_state(gr_engine *e, int64_t rid, int32_t cap, int32_t *parent, int32_t *codes,

@@ -72,22 +72,37 @@ struct StepReq {
 };
 
 // ---- launchers (gr_kernels.hip) ------------------------------------------
+// Optional timing events carried by a dispatch itself (hipExtLaunchKernel): `start` is
+// stamped when the first launch of a launcher begins, `stop` when its last one ends.  They
+// add no marker packets between kernels; both null means a plain launch.
+struct LaunchEv {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
 // Context-attention variants: waves per workgroup (1, 2, 4 or 8; 32 query rows per wave)
 // in the low byte, kCtxHiLo when P is split into two bf16 terms.  1, 2 and 4 waves always
 // use the split (narrow steps: HBM- or latency-bound); 8 waves only for short contexts.
 constexpr int kCtxHiLo = 0x100;
 constexpr int kCtxLongContext = 4096;  // wide steps at least this long round P once to bf16
 hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
-                           int ctx_kind, hipStream_t st);
+                           int ctx_kind, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
-                             hipStream_t st);
-hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st);
-hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st);
+                             hipStream_t st, LaunchEv ev = {});
+hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
+                         LaunchEv ev = {});
+hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
+                      LaunchEv ev = {});
 // max_cand: largest n_bound*V of the step (selects the register-resident or the streaming variant)
-hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st);
+hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st,
+                       LaunchEv ev = {});
 hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N,
                            int Np, int Hkv, int d, int elem_bytes, hipStream_t st);
 hipError_t launch_init_slot(const Dev &dev, int slot, hipStream_t st);
+// Copies n_live, codes and scores of level parity `parity` of up to kGatherMax slots into a
+// staging area: request i at out + i*out_bytes (n_live at 0, codes at 16, scores after
+// W_max*levels codes).
+constexpr int kGatherMax = 64;
+hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, int parity, uint8_t *out,
+                                 size_t out_bytes, hipStream_t st);
 // largest key norm per (layer, kv head) of native K [L][Hkv][Np][d] -> out [L][Hkv]
 hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int Np, int d, int elem_bytes,
                                float *out, hipStream_t st);

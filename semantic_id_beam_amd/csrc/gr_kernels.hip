@@ -20,6 +20,7 @@
 //   k_logits          h @ w_sid[level], fp32 MFMA, split over the hidden dim
 //   k_lsm             sums the split logits, trie-masked log-softmax, candidates
 //   k_select          top-K over beams x codes, BeamPath update
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
   constexpr int P = NST - 1;
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
   constexpr int KI = KCH / 64, VI = VCH / 64, LPT = KI + VI;
-  static_assert(LPT == 16 && NST >= 2 && NST <= 4, "wait immediates assume 16 copies per tile");
+  static_assert(LPT == 16 && NST >= 2 && NST <= 5, "wait immediates assume 16 copies per tile");
   __shared__ bf16x8_t sK[NST][KCH];
   __shared__ bf16x8_t sV[NST][VCH];
 
@@ -585,7 +586,8 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     for (int it = 0; it < ntiles; ++it) {
       // tile it has landed once at most the copies of the later tiles already issued remain
       const int ahead = min(P - 1, ntiles - 1 - it);
-      if (ahead >= 2) vm_wait<2 * LPT>();
+      if (ahead >= 3) vm_wait<3 * LPT>();
+      else if (ahead == 2) vm_wait<2 * LPT>();
       else if (ahead == 1) vm_wait<LPT>();
       else vm_wait<0>();
       if (it + P < ntiles) issue(it + P);  // into the stage of tile it-1, read by now
@@ -625,11 +627,13 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
   constexpr int KI = KCH / NT, VI = VCH / NT;        // DMA instructions per wave and tile
   constexpr int LPT = KI + VI;
-  static_assert(NST >= 3 && NST <= 4, "ring of three or four stages");
+  static_assert(NST >= 3 && NST <= 5, "ring of three to five stages");
   static_assert(TT == kTileTok, "tiles never cross the zero-padded end of the context");
   __shared__ bf16x8_t sK[NST][KCH];   // [token row swap23(r)][column c ^ (row & 15)]
   __shared__ bf16x8_t sV[NST][VCH];   // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
-  __shared__ float sBound[NW];
+  // per-wave score bounds, read right after the prologue barrier; the last K stage receives
+  // its first tile only after the next barrier
+  float *sBound = (float *)&sK[NST - 1][0];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
   const int kx = lane & 15, vx = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of this lane's operand row
@@ -872,7 +876,8 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   // it+P goes into the stage of tile it-2
   auto advance = [&](int it) {
     const int ahead = min(P - 1, ntiles - 1 - it);  // own tiles issued after tile it
-    if (P == 2 && ahead > 0) vm_wait_barrier<LPT>();
+    if (ahead >= 2) vm_wait_barrier<2 * LPT>();
+    else if (ahead == 1) vm_wait_barrier<LPT>();
     else vm_wait_barrier<0>();
     if (it + P < ntiles) issue(it + P);
   };
@@ -1696,79 +1701,113 @@ __global__ void k_init_slot(Dev dev, int slot) {
   }
 }
 
+struct GatherSlots {
+  int32_t slot[kGatherMax];
+};
+// one workgroup per request: final n_live, codes and scores into the staging area
+__global__ __launch_bounds__(256) void k_gather_results(Dev dev, GatherSlots gs, int n, int parity, uint8_t *out,
+                                                        size_t out_bytes) {
+  const int i = blockIdx.x;
+  if (i >= n) return;
+  const uint8_t *sb = slot_base(dev, gs.slot[i]);
+  const int lv = dev.dm.levels;
+  const int nl = ((const int *)(sb + dev.sl.n_live))[parity];
+  uint8_t *o = out + (size_t)i * out_bytes;
+  if (threadIdx.x == 0) *(int32_t *)o = nl;
+  int32_t *oc = (int32_t *)(o + 16);
+  float *os = (float *)(o + 16 + (size_t)dev.dm.W_max * lv * 4);
+  const int32_t *codes = (const int32_t *)(sb + dev.sl.codes[parity]);
+  const float *score = (const float *)(sb + dev.sl.score[parity]);
+  for (int e = threadIdx.x; e < nl * lv; e += blockDim.x) oc[e] = codes[e];
+  for (int e = threadIdx.x; e < nl; e += blockDim.x) os[e] = score[e];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------- launchers
+namespace {
+template <typename K, typename... Args>
+void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, LaunchEv ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+}  // namespace
+
 hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs, int ctx_kind,
-                           hipStream_t st) {
+                           hipStream_t st, LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
+  const dim3 grid(total_wgs);
   if (dev.dm.dtype == 0) {
     if (dev.dm.d == 64)
-      hipLaunchKernelGGL(k_ctx_attn_f32<64>, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_f32<64>, grid, dim3(256), st, ev, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL(k_ctx_attn_f32<128>, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_f32<128>, grid, dim3(256), st, ev, dev, reqs, n_reqs, layer);
     return hipGetLastError();
   }
   const int nw = ctx_kind & 0xFF;
   const bool hilo = (ctx_kind & kCtxHiLo) != 0;
-  const dim3 blk(nw * 64), grid(total_wgs);
+  const dim3 blk(nw * 64);
   if (dev.dm.d == 128) {
     if (nw == 8 && hilo)
-      hipLaunchKernelGGL((k_ctx_attn_wide<4, true>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_wide<4, true>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 8)
-      hipLaunchKernelGGL((k_ctx_attn_wide<4, false>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_wide<4, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 4)
-      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_bf16_narrow<128, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 2)
-      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<128, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_bf16_narrow<128, 2, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_ctx_attn_stream<4>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_stream<4>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   } else {
     if (nw == 4)
-      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 4, 64>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_bf16_narrow<64, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 2)
-      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 2, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_bf16_narrow<64, 2, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_ctx_attn_bf16_narrow<64, 1, 32>), grid, blk, 0, st, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_bf16_narrow<64, 1, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
-                             hipStream_t st) {
+                             hipStream_t st, LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
+  const dim3 grid(total_wgs), blk(256);
   if (dev.dm.dtype == 0) {
     if (dev.dm.d == 64)
-      hipLaunchKernelGGL((k_beam_merge<64, float>), dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<64, float>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_beam_merge<128, float>), dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<128, float>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   } else {
     if (dev.dm.d == 64)
-      hipLaunchKernelGGL((k_beam_merge<64, uint16_t>), dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<64, uint16_t>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else
-      hipLaunchKernelGGL((k_beam_merge<128, uint16_t>), dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<128, uint16_t>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st) {
+hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
+                         LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_logits, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs);
+  launch(k_logits, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
-hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st) {
+hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st, LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lsm, dim3(total_wgs), dim3(256), 0, st, dev, reqs, n_reqs);
+  launch(k_lsm, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st) {
+hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st, LaunchEv ev) {
   if (n_reqs <= 0) return hipSuccess;
   if (max_cand <= kTopkThreads * kSelectCPT)
-    hipLaunchKernelGGL(k_select<true>, dim3(n_reqs), dim3(kTopkThreads), 0, st, dev, reqs, n_reqs);
+    launch(k_select<true>, dim3(n_reqs), dim3(kTopkThreads), st, ev, dev, reqs, n_reqs);
   else
-    hipLaunchKernelGGL(k_select<false>, dim3(n_reqs), dim3(kTopkThreads), 0, st, dev, reqs, n_reqs);
+    launch(k_select<false>, dim3(n_reqs), dim3(kTopkThreads), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
@@ -1809,6 +1848,15 @@ hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int 
   else
     hipLaunchKernelGGL(k_key_norm_max<float>, dim3(L * Hkv), dim3(256), 0, st, (const float *)k_native, N, Np, d,
                        out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, int parity, uint8_t *out,
+                                 size_t out_bytes, hipStream_t st) {
+  if (n <= 0 || n > kGatherMax) return hipErrorInvalidValue;
+  GatherSlots gs{};
+  for (int i = 0; i < n; ++i) gs.slot[i] = slots[i];
+  hipLaunchKernelGGL(k_gather_results, dim3(n), dim3(256), 0, st, dev, gs, n, parity, out, out_bytes);
   return hipGetLastError();
 }
 

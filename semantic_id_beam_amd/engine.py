@@ -78,6 +78,9 @@ class BeamEngine:
     def beams(self, rid: int):
         return G.gr_beams_get(self.eng, rid, self.max_beam_width, self.n_levels, self.stream)
 
+    def beams_batch(self, rids):
+        return G.gr_beams_get_batch(self.eng, rids, self.max_beam_width, self.n_levels, self.stream)
+
     def reset(self, rid: int):
         G.gr_request_reset(self.eng, rid, self.stream)
 

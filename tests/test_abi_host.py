@@ -120,6 +120,9 @@ def test_calls_before_bind_are_bad_state():
     with pytest.raises(G.GrError) as ei:
         G.gr_request_release(eng, 1)
     assert ei.value.status == G.GR_E_NOT_FOUND
+    with pytest.raises(G.GrError) as ei:
+        G.gr_beams_get_batch(eng, [1], 4, 3)
+    assert ei.value.status == G.GR_E_BAD_STATE
     with pytest.raises(G.GrError):
         G.gr_engine_bind_workspace(eng, FAKE + 1, 1 << 40)       # misaligned
     with pytest.raises(G.GrError) as ei:
@@ -139,5 +142,6 @@ def test_padded_len_and_topk_args():
 def test_null_engine_is_rejected():
     L = sib.lib()
     assert L.gr_beam_step(None, None, 0, None) == G.GR_E_INVALID_ARG
+    assert L.gr_beams_get_batch(None, None, 1, 4, None, None, None, None) == G.GR_E_INVALID_ARG
     assert L.gr_engine_destroy(None) == G.GR_OK
     assert L.gr_engine_workspace_bytes(None) == 0

@@ -111,6 +111,32 @@ def test_determinism_bit_identical():
     assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
 
 
+def test_beams_get_batch_equals_single_calls():
+    """The batched result path returns, bit for bit, what one gr_beams_get per request does."""
+    import semantic_id_beam_amd._lib as G
+    cfg = synth.get_config("ctx1k_beam256", ctx_len=300, beam_width=48, n_items=5000)
+    eng = make_engine(cfg, max_requests=3, max_ctx_tokens=3 * 320)
+    rids = [load_request(eng, cfg, 0, rid=10), load_request(eng, cfg, 0, rid=11), load_request(eng, cfg, 0, rid=12)]
+    eng.reset(rids[2])
+    with pytest.raises(G.GrError) as ei:                        # nothing decoded yet
+        eng.beams_batch(rids)
+    assert ei.value.status == G.GR_E_BAD_STATE
+    for _ in range(cfg.n_levels):
+        eng.step(rids)
+    single = [eng.beams(r) for r in rids]
+    batch = eng.beams_batch(rids[::-1])[::-1]
+    for (c1, s1), (c2, s2) in zip(single, batch):
+        assert c1.shape[0] == cfg.beam_width
+        assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    with pytest.raises(G.GrError) as ei:                        # capacity below the beam count
+        G.gr_beams_get_batch(eng.eng, rids, cfg.beam_width - 1, cfg.n_levels, eng.stream)
+    assert ei.value.status == G.GR_E_INVALID_ARG
+    with pytest.raises(G.GrError) as ei:
+        G.gr_beams_get_batch(eng.eng, [10, 99], cfg.beam_width, cfg.n_levels, eng.stream)
+    assert ei.value.status == G.GR_E_NOT_FOUND
+    eng.close()
+
+
 def test_topk_select_bit_exact_vs_lexsort():
     import torch
     import semantic_id_beam_amd as sib
