@@ -94,7 +94,7 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 template <int D, typename T>
 __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
                                            int gi, int kv, int c8);
-template <int D>
+template <int D, int E>
 __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int kv,
                                             int r0, int r1, int tid, int nthreads);
 
@@ -311,7 +311,7 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
       const int nr = min(rows, row0 + NW * 32) - row0;
       const int per = (nr + R.splits - 1) / R.splits;
       const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
-      finish_rows<D>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
+      finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
     }
     lstore(0);
     __syncthreads();
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     const int nr = min(rows, row0 + 32) - row0;
     const int per = (nr + R.splits - 1) / R.splits;
     const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
-    finish_rows<D>(dev, R, slot, layer - 1, h, r0, r1, lane, 64);
+    finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, lane, 64);
   }
   const bool fixed_ref = bmax <= 60.f;
   if (!fixed_ref) M = kNegInf;
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     const int nr = min(rows, row0 + NW * 32) - row0;
     const int per = (nr + R.splits - 1) / R.splits;
     const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
-    finish_rows<D>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
+    finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
   }
   // the first P tiles have landed (explicitly: the compiler does not count the copies) and
   // sBound is visible
@@ -1161,14 +1161,197 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
   gst<f32x4_t>(hr + 4, b);
 }
 
-// Finishes rows [r0, r1) of kv head kv for `layer` (bf16 caches); thread = (row, chunk).
-template <int D>
+// Finishes rows [r0, r1) of kv head kv for `layer` (bf16 caches); thread = (row, 8-feature
+// chunk).  The arithmetic is merge_elem's, in the same order; the memory accesses are arranged
+// for parallelism, E elements of a thread at a time: first every load that needs only indices
+// (the beam's code, the first two splits' partials, h), then the token-table and BeamKV loads
+// that need the code or the ancestry, then the arithmetic and the stores.  The finish is
+// bound by these round trips, not by bandwidth: its data sits in the L2 / Infinity Cache.
+template <int D, int E>
 __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int kv,
                                             int r0, int r1, int tid, int nthreads) {
   constexpr int C8 = D / 8;
-  for (int e = tid; e < (r1 - r0) * C8; e += nthreads) {
-    const int row = r0 + e / C8;
-    merge_elem<D, uint16_t>(dev, R, slot, layer, row / dev.dm.g, row % dev.dm.g, kv, e % C8);
+  const Dims &dm = dev.dm;
+  const int s = R.level, g = dm.g, lvl = dm.levels, S = R.splits;
+  const float c2 = dm.scale_log2;
+  const int total = (r1 - r0) * C8;
+  const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[layer & 1]);
+  const float *po = (const float *)(slot + dev.sl.part_o[layer & 1]);
+  const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
+  const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
+  uint16_t *bk = (uint16_t *)(slot + dev.sl.beamkv_k);
+  uint16_t *bv = (uint16_t *)(slot + dev.sl.beamkv_v);
+  float *hb = (float *)(slot + dev.sl.h);
+  const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
+  const size_t lvstride = (size_t)dm.W_max * wstride;
+  const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
+  for (int e0 = tid; e0 < total; e0 += E * nthreads) {
+    int j[E], gi[E], c8[E], code[E];
+    bool ok[E];
+    size_t pbase[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const int e = e0 + k * nthreads;
+      ok[k] = e < total;  // uniform over the C8 lanes of a row
+      const int row = r0 + (ok[k] ? e / C8 : 0);
+      j[k] = row / g;
+      gi[k] = row % g;
+      c8[k] = e % C8;
+      pbase[k] = (size_t)kv * S * R.rows_b + row;
+    }
+    // ---- phase 1: index-only loads
+    f32x2_t ml0[E], ml1[E];
+    f32x4_t pa0[E], pb0[E], pa1[E], pb1[E], ha[E], hc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      if (!ok[k]) continue;
+      code[k] = s > 0 ? codes[j[k] * lvl + (s - 1)] : 0;
+      const float *p0 = po + pbase[k] * D + c8[k] * 8;
+      ml0[k] = gld<f32x2_t>(pml + pbase[k]);
+      pa0[k] = gld<f32x4_t>(p0);
+      pb0[k] = gld<f32x4_t>(p0 + 4);
+      if (S > 1) {
+        const float *p1 = p0 + (size_t)R.rows_b * D;
+        ml1[k] = gld<f32x2_t>(pml + pbase[k] + R.rows_b);
+        pa1[k] = gld<f32x4_t>(p1);
+        pb1[k] = gld<f32x4_t>(p1 + 4);
+      }
+      if (layer > 0) {
+        const float *hr = hb + ((size_t)j[k] * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8;
+        ha[k] = gld<f32x4_t>(hr);
+        hc[k] = gld<f32x4_t>(hr + 4);
+      }
+    }
+    // ---- phase 2: the beam's own tokens (step s >= 1)
+    float Mb[E], lb[E], ob[E][8];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      Mb[k] = kNegInf;
+      lb[k] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ob[k][i] = 0.f;
+    }
+    if (s > 0) {
+      Raw8<uint16_t> rq[E], kn[E], vn[E];
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        if (!ok[k]) continue;
+        const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code[k];
+        rq[k].load((const uint16_t *)dev.tok_q + (trow * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8);
+        kn[k].load((const uint16_t *)dev.tok_k + (trow * dm.Hkv + kv) * D + c8[k] * 8);
+        vn[k].load((const uint16_t *)dev.tok_v + (trow * dm.Hkv + kv) * D + c8[k] * 8);
+      }
+      float q[E][8];
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        rq[k].to_float(q[k]);
+        if (ok[k] && gi[k] == 0) {
+          const size_t dst = lbase + (size_t)(s - 1) * lvstride + (size_t)j[k] * wstride + c8[k] * 8;
+          kn[k].store(bk + dst);
+          vn[k].store(bv + dst);
+        }
+      }
+      for (int t = 0; t < s; ++t) {
+        float kt[E][8], vt[E][8];
+        if (t == s - 1) {
+#pragma unroll
+          for (int k = 0; k < E; ++k) {
+            kn[k].to_float(kt[k]);
+            vn[k].to_float(vt[k]);
+          }
+        } else {
+          Raw8<uint16_t> a[E], b[E];
+#pragma unroll
+          for (int k = 0; k < E; ++k) {
+            if (!ok[k]) continue;
+            const size_t off = lbase + (size_t)t * lvstride + (size_t)anc[j[k] * lvl + t] * wstride + c8[k] * 8;
+            a[k].load(bk + off);
+            b[k].load(bv + off);
+          }
+#pragma unroll
+          for (int k = 0; k < E; ++k) {
+            a[k].to_float(kt[k]);
+            b[k].to_float(vt[k]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = fmaf(q[k][i], kt[k][i], dot);
+#pragma unroll
+          for (int o = C8 / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+          const float u = dot * c2;
+          const float Mn = fmaxf(Mb[k], u);
+          const float f = fast_exp2(Mb[k] - Mn);
+          const float p = fast_exp2(u - Mn);
+          lb[k] = lb[k] * f + p;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ob[k][i] = fmaf(p, vt[k][i], ob[k][i] * f);
+          Mb[k] = Mn;
+        }
+      }
+    }
+    // ---- phase 3: merge the splits in order with the beam partial, h += o
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      if (!ok[k]) continue;
+      float Ms = fmaxf(Mb[k], ml0[k][0]);
+      if (S > 1) Ms = fmaxf(Ms, ml1[k][0]);
+      for (int sp = 2; sp < S; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase[k] + (size_t)sp * R.rows_b)[0]);
+      const float fb = fast_exp2(Mb[k] - Ms);
+      float Ls = lb[k] * fb, O[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) O[i] = ob[k][i] * fb;
+      {
+        const float f = fast_exp2(ml0[k][0] - Ms);
+        Ls = fmaf(ml0[k][1], f, Ls);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          O[i] = fmaf(pa0[k][i], f, O[i]);
+          O[4 + i] = fmaf(pb0[k][i], f, O[4 + i]);
+        }
+      }
+      if (S > 1) {
+        const float f = fast_exp2(ml1[k][0] - Ms);
+        Ls = fmaf(ml1[k][1], f, Ls);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          O[i] = fmaf(pa1[k][i], f, O[i]);
+          O[4 + i] = fmaf(pb1[k][i], f, O[4 + i]);
+        }
+      }
+      for (int sp = 2; sp < S; ++sp) {
+        const size_t prow = pbase[k] + (size_t)sp * R.rows_b;
+        const f32x2_t ml = gld<f32x2_t>(pml + prow);
+        const float f = fast_exp2(ml[0] - Ms);
+        Ls = fmaf(ml[1], f, Ls);
+        const f32x4_t a = gld<f32x4_t>(po + prow * D + c8[k] * 8);
+        const f32x4_t b = gld<f32x4_t>(po + prow * D + c8[k] * 8 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          O[i] = fmaf(a[i], f, O[i]);
+          O[4 + i] = fmaf(b[i], f, O[4 + i]);
+        }
+      }
+      const float inv = 1.f / Ls;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) O[i] *= inv;
+      const int hq = kv * g + gi[k];
+      float *hr = hb + ((size_t)j[k] * dm.Hq + hq) * D + c8[k] * 8;
+      f32x4_t a = f32x4_t{O[0], O[1], O[2], O[3]}, b = f32x4_t{O[4], O[5], O[6], O[7]};
+      if (dm.debug_attn) {
+        float *dg = (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j[k]) * dm.Hq + hq) * D + c8[k] * 8;
+        gst<f32x4_t>(dg, a);
+        gst<f32x4_t>(dg + 4, b);
+      }
+      if (layer > 0) {
+        a += ha[k];
+        b += hc[k];
+      }
+      gst<f32x4_t>(hr, a);
+      gst<f32x4_t>(hr + 4, b);
+    }
   }
 }
 
