@@ -66,6 +66,20 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum over each aligned group of 16 lanes without LDS permutes (DPP: swap neighbours, swap
+// pairs, mirror within 8, mirror within 16); every lane of the group gets the sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                                   false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_add<0xB1>(v);      // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);      // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);     // row_half_mirror
+  return dpp_add<0x140>(v);  // row_mirror
+}
+
 // Workgroup -> request: reqs[] is ordered by each first-workgroup field.
 template <int FIELD>
 __device__ __forceinline__ int find_req(const StepReq *reqs, int n, int bid) {
@@ -1279,8 +1293,12 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
           float dot = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) dot = fmaf(q[k][i], kt[k][i], dot);
+          if constexpr (C8 == 16) {
+            dot = row16_sum(dot);
+          } else {
 #pragma unroll
-          for (int o = C8 / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+            for (int o = C8 / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+          }
           const float u = dot * c2;
           const float Mn = fmaxf(Mb[k], u);
           const float f = fast_exp2(Mb[k] - Mn);
