@@ -175,8 +175,7 @@ def main():
         eng.beams(r)
 
     def decode_all():
-        for r in rids:
-            eng.reset(r)
+        eng.reset_batch(rids)
         for _ in range(lv):
             eng.step(rids)
         return eng.beams_batch(rids)

@@ -202,6 +202,10 @@ gr_status gr_request_release(gr_engine *eng, int64_t request_id);
  * the start.  Enqueued on `stream`.  Errors: GR_E_NOT_FOUND. */
 gr_status gr_request_reset(gr_engine *eng, int64_t request_id, void *stream);
 
+/* gr_request_reset for several requests with one launch.  Errors: GR_E_INVALID_ARG
+ * (n_requests < 1), GR_E_NOT_FOUND (nothing is reset then). */
+gr_status gr_request_reset_batch(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, void *stream);
+
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char *gr_last_error(void);
 

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "
 EXPORTS = [
     "gr_engine_create", "gr_engine_workspace_bytes", "gr_engine_bind_workspace", "gr_engine_destroy",
     "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
-    "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
+    "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
     "gr_engine_profile_reset",
 ]
@@ -92,6 +92,7 @@ def lib() -> C.CDLL:
         "gr_beams_get_batch": (i32, [vp, P(i64), i32, i32, vp, vp, vp, vp]),
         "gr_request_release": (i32, [vp, i64]),
         "gr_request_reset": (i32, [vp, i64, vp]),
+        "gr_request_reset_batch": (i32, [vp, P(i64), i32, vp]),
         "gr_last_error": (C.c_char_p, []),
         "gr_topk_select": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "gr_debug_beam_state": (i32, [vp, i64, i32, vp, vp, vp, P(i32), P(i32), vp]),
@@ -194,6 +195,11 @@ def gr_request_release(eng: int, rid: int):
 
 def gr_request_reset(eng: int, rid: int, stream: int = 0):
     _check(lib().gr_request_reset(eng, rid, stream))
+
+
+def gr_request_reset_batch(eng: int, request_ids, stream: int = 0):
+    ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+    _check(lib().gr_request_reset_batch(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), ids.shape[0], stream))
 
 
 def gr_last_error() -> str:

@@ -474,7 +474,7 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
   if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem,
                                        hipMemcpyDeviceToDevice, st), "q_last copy")) != GR_OK)
     return r;
-  if ((r = check_dev(e, gr::launch_init_slot(e->dev, R.slot, st), "slot init")) != GR_OK) return r;
+  if ((r = check_dev(e, gr::launch_init_slots(e->dev, &R.slot, 1, st), "slot init")) != GR_OK) return r;
   e->free_slots.pop_back();
   e->reqs[rid] = R;
   return GR_OK;
@@ -490,17 +490,34 @@ gr_status gr_request_release(gr_engine *e, int64_t rid) {
   return GR_OK;
 }
 
-gr_status gr_request_reset(gr_engine *e, int64_t rid, void *stream) {
+gr_status gr_request_reset_batch(gr_engine *e, const int64_t *ids, int32_t n, void *stream) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
-  auto it = e->reqs.find(rid);
-  if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+  if (!ids || n < 1) return fail(GR_E_INVALID_ARG, "need at least one request id");
+  std::vector<gr_engine::Req *> rs((size_t)n);
+  std::vector<int32_t> slots((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    auto it = e->reqs.find(ids[i]);
+    if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+    rs[(size_t)i] = &it->second;
+    slots[(size_t)i] = it->second.slot;
+  }
   gr_status r;
-  if ((r = check_dev(e, gr::launch_init_slot(e->dev, it->second.slot, (hipStream_t)stream), "slot init")) != GR_OK)
-    return r;
-  it->second.level = 0;
-  it->second.n_bound = 1;
+  for (int i0 = 0; i0 < n; i0 += gr::kGatherMax) {
+    const int m = std::min(gr::kGatherMax, n - i0);
+    if ((r = check_dev(e, gr::launch_init_slots(e->dev, slots.data() + i0, m, (hipStream_t)stream), "slot init")) !=
+        GR_OK)
+      return r;
+  }
+  for (auto *R : rs) {
+    R->level = 0;
+    R->n_bound = 1;
+  }
   return GR_OK;
+}
+
+gr_status gr_request_reset(gr_engine *e, int64_t rid, void *stream) {
+  return gr_request_reset_batch(e, &rid, 1, stream);
 }
 
 gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream) {

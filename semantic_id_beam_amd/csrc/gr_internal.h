@@ -15,6 +15,7 @@ constexpr int kMaxBeam = 1024;
 constexpr int kLogitsKS = 4;          // split of the hidden dimension in the logits GEMM
 constexpr int kSelectCPT = 64;        // candidates per thread kept in registers by the selection
 constexpr int kTieCap = 1024;         // candidates sharing the cut bin that the fast selection sorts
+constexpr int kGatherMax = 64;        // slots per result-gather / root-beam launch
 
 struct Dims {
   int L, Hq, Hkv, g, d, levels, V, MW;  // MW = 32-bit words per trie mask row
@@ -96,11 +97,11 @@ hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_
                        LaunchEv ev = {});
 hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N,
                            int Np, int Hkv, int d, int elem_bytes, hipStream_t st);
-hipError_t launch_init_slot(const Dev &dev, int slot, hipStream_t st);
+// root beam (level 0, empty prefix, score 0) in up to kGatherMax slots
+hipError_t launch_init_slots(const Dev &dev, const int32_t *slots, int n, hipStream_t st);
 // Copies n_live, codes and scores of level parity `parity` of up to kGatherMax slots into a
 // staging area: request i at out + i*out_bytes (n_live at 0, codes at 16, scores after
 // W_max*levels codes).
-constexpr int kGatherMax = 64;
 hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, int parity, uint8_t *out,
                                  size_t out_bytes, hipStream_t st);
 // largest key norm per (layer, kv head) of native K [L][Hkv][Np][d] -> out [L][Hkv]

@@ -112,6 +112,18 @@ template <int D, int E>
 __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int kv,
                                             int r0, int r1, int tid, int nthreads);
 
+// Rows [r0, r1) of a row block's nr rows that split sp finishes.  The rows go to as few splits
+// as one batch per workgroup allows (batch = rows one workgroup finishes at once), taken from
+// the last split down: the last token range is the shortest, so a small finish (one beam at the
+// first level) lands where it lengthens the launch least.
+__device__ __forceinline__ void finish_share(int row0, int nr, int splits, int sp, int batch_rows, int &r0, int &r1) {
+  const int k = min(splits, max(1, (nr + batch_rows - 1) / batch_rows));
+  const int idx = splits - 1 - sp;
+  const int per = (nr + k - 1) / k;
+  r0 = row0 + min(nr, idx < k ? idx * per : nr);
+  r1 = row0 + min(nr, idx < k ? (idx + 1) * per : nr);
+}
+
 // --------------------------------------------------------------------------------------
 // Shared-context attention, bf16 K/V, fp32 accumulate, MFMA 32x32x16.
 //
@@ -322,9 +334,8 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
     if (layer > 0) {
       // finish the previous layer for this workgroup's share of the row block (its split
       // partials are complete: that layer's kernel has ended)
-      const int nr = min(rows, row0 + NW * 32) - row0;
-      const int per = (nr + R.splits - 1) / R.splits;
-      const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
+      int r0, r1;
+      finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, NT / (D / 8), r0, r1);
       finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
     }
     lstore(0);
@@ -536,9 +547,8 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     bmax = wave_max(B);
   }
   if (layer > 0) {
-    const int nr = min(rows, row0 + 32) - row0;
-    const int per = (nr + R.splits - 1) / R.splits;
-    const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
+    int r0, r1;
+    finish_share(row0, min(rows, row0 + 32) - row0, R.splits, sp, 64 / (D / 8), r0, r1);
     finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, lane, 64);
   }
   const bool fixed_ref = bmax <= 60.f;
@@ -749,9 +759,8 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   }
   if (layer > 0) {
     // finish the previous layer for this workgroup's share of the row block
-    const int nr = min(rows, row0 + NW * 32) - row0;
-    const int per = (nr + R.splits - 1) / R.splits;
-    const int r0 = row0 + min(nr, sp * per), r1 = row0 + min(nr, (sp + 1) * per);
+    int r0, r1;
+    finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
     finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
   }
   // the first P tiles have landed (explicitly: the compiler does not count the copies) and
@@ -1887,8 +1896,14 @@ __global__ __launch_bounds__(256) void k_key_norm_max(const T *__restrict__ k, i
   if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
 }
 
-__global__ void k_init_slot(Dev dev, int slot) {
-  uint8_t *sb = slot_base(dev, slot);
+struct GatherSlots {
+  int32_t slot[kGatherMax];
+};
+
+// one workgroup per listed slot: the root beam (level 0, empty prefix, score 0)
+__global__ void k_init_slot(Dev dev, GatherSlots gs, int n) {
+  if ((int)blockIdx.x >= n) return;
+  uint8_t *sb = slot_base(dev, gs.slot[blockIdx.x]);
   if (threadIdx.x == 0) {
     ((int *)(sb + dev.sl.n_live))[0] = 1;
     ((int *)(sb + dev.sl.n_live))[1] = 0;
@@ -1902,9 +1917,6 @@ __global__ void k_init_slot(Dev dev, int slot) {
   }
 }
 
-struct GatherSlots {
-  int32_t slot[kGatherMax];
-};
 // one workgroup per request: final n_live, codes and scores into the staging area
 __global__ __launch_bounds__(256) void k_gather_results(Dev dev, GatherSlots gs, int n, int parity, uint8_t *out,
                                                         size_t out_bytes) {
@@ -2061,8 +2073,11 @@ hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, in
   return hipGetLastError();
 }
 
-hipError_t launch_init_slot(const Dev &dev, int slot, hipStream_t st) {
-  hipLaunchKernelGGL(k_init_slot, dim3(1), dim3(64), 0, st, dev, slot);
+hipError_t launch_init_slots(const Dev &dev, const int32_t *slots, int n, hipStream_t st) {
+  if (n <= 0 || n > kGatherMax) return hipErrorInvalidValue;
+  GatherSlots gs{};
+  for (int i = 0; i < n; ++i) gs.slot[i] = slots[i];
+  hipLaunchKernelGGL(k_init_slot, dim3(n), dim3(64), 0, st, dev, gs, n);
   return hipGetLastError();
 }
 

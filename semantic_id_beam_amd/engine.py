@@ -84,6 +84,9 @@ class BeamEngine:
     def reset(self, rid: int):
         G.gr_request_reset(self.eng, rid, self.stream)
 
+    def reset_batch(self, rids):
+        G.gr_request_reset_batch(self.eng, rids, self.stream)
+
     def release(self, rid: int):
         G.gr_request_release(self.eng, rid)
         self._keep.pop(rid, None)

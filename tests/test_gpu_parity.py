@@ -112,7 +112,8 @@ def test_determinism_bit_identical():
 
 
 def test_beams_get_batch_equals_single_calls():
-    """The batched result path returns, bit for bit, what one gr_beams_get per request does."""
+    """The batched result path returns, bit for bit, what one gr_beams_get per request does;
+    a batched reset rewinds every request to its root beam."""
     import semantic_id_beam_amd._lib as G
     cfg = synth.get_config("ctx1k_beam256", ctx_len=300, beam_width=48, n_items=5000)
     eng = make_engine(cfg, max_requests=3, max_ctx_tokens=3 * 320)
@@ -127,6 +128,12 @@ def test_beams_get_batch_equals_single_calls():
     batch = eng.beams_batch(rids[::-1])[::-1]
     for (c1, s1), (c2, s2) in zip(single, batch):
         assert c1.shape[0] == cfg.beam_width
+        assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    eng.reset_batch(rids)                                       # rewind all at once, decode again
+    for _ in range(cfg.n_levels):
+        eng.step(rids)
+    again = eng.beams_batch(rids)
+    for (c1, s1), (c2, s2) in zip(single, again):
         assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
     with pytest.raises(G.GrError) as ei:                        # capacity below the beam count
         G.gr_beams_get_batch(eng.eng, rids, cfg.beam_width - 1, cfg.n_levels, eng.stream)
