@@ -79,7 +79,7 @@ struct gr_engine {
   bool prof = false;
   std::vector<hipEvent_t> prof_ev;
   int prof_next = 0;  // next unused event of the pool
-  struct ProfRec { int kind, level, a, b; };
+  struct ProfRec { int kind, level, a, b, count; };  // count: launches the record stands for
   std::vector<ProfRec> prof_pending;
   double prof_ms[5][gr::kMaxLevels + 1] = {};
   int64_t prof_n[5][gr::kMaxLevels + 1] = {};
@@ -108,7 +108,7 @@ gr_status prof_fold(gr_engine *e) {
     float ms = 0.f;
     if ((r = check_dev(e, hipEventElapsedTime(&ms, a, b), "profiling event")) != GR_OK) return r;
     e->prof_ms[p.kind][p.level] += ms;
-    e->prof_n[p.kind][p.level] += 1;
+    e->prof_n[p.kind][p.level] += p.count;
   }
   e->prof_pending.clear();
   e->prof_next = 0;
@@ -139,8 +139,8 @@ gr::LaunchEv prof_ev(gr_engine *e, int a, int b) {
   return ev;
 }
 
-void prof_record(gr_engine *e, int kind, int level, std::pair<int, int> ab) {
-  if (ab.first >= 0) e->prof_pending.push_back({kind, level, ab.first, ab.second});
+void prof_record(gr_engine *e, int kind, int level, std::pair<int, int> ab, int count = 1) {
+  if (ab.first >= 0) e->prof_pending.push_back({kind, level, ab.first, ab.second, count});
 }
 
 gr_status build_trie(gr_engine *e, const gr_item_set *items) {
@@ -542,6 +542,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   gr_status r;
   // ---- work decomposition: requests grouped by context-attention variant (one launch per
   // group); within a group, enough split-K token ranges to fill the chip
+  // A first-level step (every request at level 0) runs all layers' context attention in one
+  // launch: each layer's query is an input there.  Needs room for every layer's partials in
+  // one partial buffer and for the per-layer outputs in the other.
+  bool first_fused = d.dtype == 1 && d.d == 128 && d.L > 1 && (int64_t)d.L <= (int64_t)d.S_max * d.W_max;
+  for (int i = 0; i < n && first_fused; ++i) first_fused = rs[(size_t)i]->level == 0;
   std::vector<int> kind((size_t)n);
   for (int i = 0; i < n; ++i)
     kind[(size_t)i] = d.dtype == 1 ? gr::ctx_kind_for(rs[(size_t)i]->n_bound * d.g, rs[(size_t)i]->N, d.d) : 0;
@@ -595,6 +600,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       S = std::min(S, std::max(1, ceil_div(R->N, 2 * gr::kTileTok)));
       S = (int)std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)d.S_max * d.W_max * d.g / rows));
       S = std::min(S, 256);
+      if (first_fused) S = std::max(1, std::min<int>(S, (int)((int64_t)d.S_max * d.W_max * d.g / ((int64_t)d.L * rows))));
       int tps = (int)align_up((size_t)ceil_div(R->N, S), gr::kTileTok);
       S = ceil_div(R->N, tps);
       w.splits = S;
@@ -625,7 +631,21 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     if (R->level != plevel) plevel = d.levels;
   const bool pon = prof_reserve(e, 2 * (2 * d.L + 2));
   int step_start = -1;
-  for (int l = 0; l < d.L; ++l) {
+  if (first_fused) {
+    const auto pc = prof_pair(e, pon);
+    step_start = pc.first;
+    if ((r = check_dev(e, gr::launch_ctx_attn_first_level(e->dev, dw, n, groups[0].wgs, st,
+                                                          prof_ev(e, pc.first, pc.second)),
+                       "context attention")) != GR_OK)
+      return r;
+    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L);
+    const auto pm = prof_pair(e, pon);
+    if ((r = check_dev(e, gr::launch_finish_first_level(e->dev, dw, n, st, prof_ev(e, pm.first, pm.second)),
+                       "first-level finish")) != GR_OK)
+      return r;
+    prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
+  }
+  for (int l = 0; l < (first_fused ? 0 : d.L); ++l) {
     const auto pc = prof_pair(e, pon);
     if (l == 0) step_start = pc.first;
     for (size_t gi = 0; gi < groups.size(); ++gi) {

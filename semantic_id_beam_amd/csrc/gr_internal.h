@@ -88,6 +88,13 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
                            int ctx_kind, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                              hipStream_t st, LaunchEv ev = {});
+// A first-level step of head_dim-128 bf16 requests with every layer in one launch (grid
+// [total_wgs][L], partials of layer l at row offset l*Hkv*splits*rows_b of buffer 0), and its
+// finish: per-layer outputs into buffer 1, then h = sum over layers in order.
+hipError_t launch_ctx_attn_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs,
+                                       hipStream_t st, LaunchEv ev = {});
+hipError_t launch_finish_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st,
+                                     LaunchEv ev = {});
 hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
                          LaunchEv ev = {});
 hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,

@@ -448,9 +448,14 @@ __device__ __forceinline__ void vm_wait() {
 // memory straight into a ring of NST LDS stages (NST-1 tiles in flight per wave); P is split
 // into two bf16 terms.  V^T rows are 64 bytes here: 16-byte column c of row r sits at
 // c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps 16 consecutive operand rows on 64 banks.
-template <int NST>
+// FUSED: every layer of a first-level step in one launch (blockIdx.y = layer).  At the first
+// level each layer's query is an input (q_last), so no layer waits for another; layer l's
+// partials go to partial buffer 0 at row offset l*Hkv*splits*rows_b, and the finish of all
+// layers runs afterwards (k_finish_first_level).
+template <int NST, bool FUSED>
 __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
-                                                        int layer) {
+                                                        int layer_arg) {
+  const int layer = FUSED ? (int)blockIdx.y : layer_arg;
   constexpr int D = 128, TT = 32, KB = D / 16, DB = D / 32;
   constexpr int P = NST - 1;
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     M = B - 60.f;
     bmax = wave_max(B);
   }
-  if (layer > 0) {
+  if (!FUSED && layer > 0) {
     int r0, r1;
     finish_share(row0, min(rows, row0 + 32) - row0, R.splits, sp, 64 / (D / 8), r0, r1);
     finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, lane, 64);
@@ -628,9 +633,11 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
 
   const float ltot = l + __shfl_xor(l, 32);
   if (row_ok) {
-    const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[layer & 1]) + prow, f32x2_t{M, ltot});
-    float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
+    const size_t lofs = FUSED ? (size_t)layer * dm.Hkv * R.splits * R.rows_b : 0;
+    const int pb = FUSED ? 0 : layer & 1;
+    const size_t prow = lofs + ((size_t)h * R.splits + sp) * R.rows_b + q_row;
+    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[pb]) + prow, f32x2_t{M, ltot});
+    float *po = (float *)(slot + dev.sl.part_o[pb]) + prow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -1403,6 +1410,72 @@ __global__ __launch_bounds__(256) void k_beam_merge(Dev dev, const StepReq *__re
   }
 }
 
+// Finish of a first-level step whose layers ran in one launch (k_ctx_attn_stream<.., true>).
+// The first level has one live beam and no beam tokens, so a layer's output is the merge of
+// its split partials.  k_finish_first_level: workgroup (request, layer), thread = (query
+// head, 8-feature chunk); the layer's output goes to the scratch rows [layer][Hq*d] of
+// partial buffer 1 (unused by the fused launch).  k_sum_layers then forms h = sum over layers
+// in layer order, the additions of the per-layer finish.
+template <int D>
+__global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  constexpr int C8 = D / 8;
+  const StepReq R = reqs[blockIdx.x];
+  const int layer = blockIdx.y;
+  const Dims &dm = dev.dm;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[0]);
+  const float *po = (const float *)(slot + dev.sl.part_o[0]);
+  float *tmp = (float *)(slot + dev.sl.part_o[1]);
+  const size_t lofs = (size_t)layer * dm.Hkv * R.splits * R.rows_b;
+  for (int e = threadIdx.x; e < dm.Hq * C8; e += blockDim.x) {
+    const int hq = e / C8, c8 = e % C8, kv = hq / dm.g, row = hq % dm.g;  // beam 0: row = gi
+    const size_t pbase = lofs + (size_t)kv * R.splits * R.rows_b + row;
+    float Ms = kNegInf;
+    for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
+    float Ls = 0.f, O[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) O[i] = 0.f;
+    for (int sp = 0; sp < R.splits; ++sp) {
+      const size_t prow = pbase + (size_t)sp * R.rows_b;
+      const f32x2_t ml = gld<f32x2_t>(pml + prow);
+      const float f = fast_exp2(ml[0] - Ms);
+      Ls = fmaf(ml[1], f, Ls);
+      const f32x4_t a = gld<f32x4_t>(po + prow * D + c8 * 8);
+      const f32x4_t b = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        O[i] = fmaf(a[i], f, O[i]);
+        O[4 + i] = fmaf(b[i], f, O[4 + i]);
+      }
+    }
+    const float inv = 1.f / Ls;
+    const f32x4_t a = f32x4_t{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
+    const f32x4_t b = f32x4_t{O[4] * inv, O[5] * inv, O[6] * inv, O[7] * inv};
+    float *t = tmp + ((size_t)layer * dm.Hq + hq) * D + c8 * 8;
+    gst<f32x4_t>(t, a);
+    gst<f32x4_t>(t + 4, b);
+    if (dm.debug_attn) {
+      float *dg = (float *)(slot + dev.sl.dbg_attn) + ((size_t)layer * dm.W_max * dm.Hq + hq) * D + c8 * 8;
+      gst<f32x4_t>(dg, a);
+      gst<f32x4_t>(dg + 4, b);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sum_layers(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  const StepReq R = reqs[blockIdx.x];
+  const Dims &dm = dev.dm;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const float *tmp = (const float *)(slot + dev.sl.part_o[1]);
+  float *hb = (float *)(slot + dev.sl.h);
+  const int n = dm.Hq * dm.d;
+  for (int e = blockIdx.y * blockDim.x + threadIdx.x; e < n; e += gridDim.y * blockDim.x) {
+    float acc = tmp[e];
+    for (int l = 1; l < dm.L; ++l) acc = tmp[(size_t)l * n + e] + acc;
+    hb[e] = acc;
+  }
+}
+
 // --------------------------------------------------------------------------------------
 // logits_part[ks][j][c] = sum over the ks-th quarter of the hidden dim of h[j][k] w_sid[level][k][c]
 // fp32 MFMA 32x32x2 (exact fp32 products, fp32 accumulate).  Workgroup: 64 beams x 64 codes
@@ -1972,7 +2045,7 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
     else if (nw == 2)
       launch(k_ctx_attn_bf16_narrow<128, 2, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else
-      launch(k_ctx_attn_stream<4>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_stream<4, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   } else {
     if (nw == 4)
       launch(k_ctx_attn_bf16_narrow<64, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
@@ -1981,6 +2054,21 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
     else
       launch(k_ctx_attn_bf16_narrow<64, 1, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ctx_attn_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs,
+                                       hipStream_t st, LaunchEv ev) {
+  if (total_wgs <= 0) return hipSuccess;
+  launch(k_ctx_attn_stream<4, true>, dim3(total_wgs, dev.dm.L), dim3(64), st, ev, dev, reqs, n_reqs, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st, LaunchEv ev) {
+  if (n_reqs <= 0) return hipSuccess;
+  launch(k_finish_first_level<128>, dim3(n_reqs, dev.dm.L), dim3(256), st, LaunchEv{ev.start, nullptr}, dev, reqs,
+         n_reqs);
+  launch(k_sum_layers, dim3(n_reqs, 8), dim3(256), st, LaunchEv{nullptr, ev.stop}, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
