@@ -34,9 +34,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # on: with any other gr_kernels.hip the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "591b0c6d640bffe6723e0c48a764d834939b4f7276d236f6c49a3a0af62865cf",
-    "k_ctx_attn_wide": {"read": 222776469, "written": 58345765},
-    "k_ctx_attn_stream": {"read": 166318020, "written": 603867},
+    "source_sha256": "65d1ccb6c2cc703c9de79c0c77491f427553a14f0140a3c0e2eb509b7eab0c01",
+    "k_ctx_attn_wide": {"read": 206565218, "written": 42213704},
+    "k_ctx_attn_stream": {"read": 166484369, "written": 278784},   # per layer of the fused launch
 }
 
 

@@ -214,6 +214,7 @@ void layout(gr_engine *e) {
   s.beamkv_v = take(kv);
   s.q_last = take((size_t)d.L * d.Hq * d.d * el);
   s.knmax = take((size_t)d.L * d.Hkv * 4);
+  s.vscale = take((size_t)d.L * d.Hkv * 4);
   s.h = take(W * d.Hq * d.d * 4);
   s.logits = take(W * d.V * 4);
   s.logits_part = take((size_t)gr::kLogitsKS * W * d.V * 4);
@@ -468,8 +469,9 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
   }
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
-  if ((r = check_dev(e, gr::launch_key_norm_max(R.k, e->dm.L, e->dm.Hkv, N, Np, e->dm.d, e->elem,
-                                                (float *)(sb + e->sl.knmax), st), "key norms")) != GR_OK)
+  if ((r = check_dev(e, gr::launch_key_norm_max(R.k, R.vt, e->dm.L, e->dm.Hkv, N, Np, e->dm.d, e->elem,
+                                                (float *)(sb + e->sl.knmax), (float *)(sb + e->sl.vscale), st),
+                     "key norms and value scales")) != GR_OK)
     return r;
   if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem,
                                        hipMemcpyDeviceToDevice, st), "q_last copy")) != GR_OK)

@@ -32,11 +32,12 @@ struct SlotLayout {
   size_t beamkv_k, beamkv_v;  // [L][levels-1][W_max][Hkv][d] elem
   size_t q_last;              // [L][Hq][d] elem
   size_t knmax;               // [L][Hkv] f32: largest context-key norm (bounds the scores)
+  size_t vscale;              // [L][Hkv] f32: power of two above the context's largest |v|
   size_t h;                   // [W_max][Hq*d] f32
   size_t logits;              // [W_max][V] f32
   size_t logits_part;         // [kLogitsKS][W_max][V] f32 split-K partial sums
   size_t cand;                // [W_max][V] f32
-  size_t part_o[2];           // [part_rows][d] f32, row ((h*splits + sp)*rows_b + row); by layer parity
+  size_t part_o[2];           // [part_rows][d] fp16 o/l*2^-e (bf16) or f32 o, row ((h*splits + sp)*rows_b + row); by layer parity
   size_t part_ml[2];          // [part_rows] float2 (m in log2 units, l)
   size_t codes[2];            // [W_max][levels] i32   (double-buffered by level parity)
   size_t score[2];            // [W_max] f32
@@ -111,9 +112,11 @@ hipError_t launch_init_slots(const Dev &dev, const int32_t *slots, int n, hipStr
 // W_max*levels codes).
 hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, int parity, uint8_t *out,
                                  size_t out_bytes, hipStream_t st);
-// largest key norm per (layer, kv head) of native K [L][Hkv][Np][d] -> out [L][Hkv]
-hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int Np, int d, int elem_bytes,
-                               float *out, hipStream_t st);
+// Per (layer, kv head) of a context (native K [L][Hkv][Np][d], V^T [L][Hkv][d][Np]; first N
+// tokens): the largest key norm -> out [L][Hkv], and the value scale, the power of two 2^e
+// with max |v| < 2^e -> out_vscale [L][Hkv].
+hipError_t launch_key_norm_max(const void *k_native, const void *vt_native, int L, int Hkv, int N, int Np, int d,
+                               int elem_bytes, float *out, float *out_vscale, hipStream_t st);
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
 

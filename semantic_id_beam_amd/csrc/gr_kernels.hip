@@ -36,6 +36,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 #define GR_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kNegInf = -__builtin_inff();
@@ -104,6 +106,47 @@ __device__ __forceinline__ uint8_t *slot_base(const Dev &dev, int slot) {
 // score accumulator's register layout equal to the PV MFMA's B-operand layout with 8
 // consecutive tokens per lane: no cross-lane shuffle between the two MFMAs.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Split partials of bf16 models: (m, l) in fp32, and the row's o divided by its own l in fp16.
+// o/l is a convex combination of value rows, so |o/l| <= max |v| of the context head; it is
+// stored times 2^-e, where 2^e is the head's value scale (vscale: the power of two just above
+// max |v|), which keeps it below 1 in magnitude whatever the values' range, with no rounding
+// from the scale.  fp16 rounds it to 2^-11 relative, an order below the bf16 rounding of P,
+// and halves the partials' traffic.  A reader weights split sp by exp2(m_sp - M) * l_sp * 2^e.
+// Lane (row, hh) of an MFMA output tile holds features db*32 + 8a + 4hh .. +4.
+template <int DB>
+__device__ __forceinline__ void store_partial(uint8_t *slot, const SlotLayout &sl, int buf, size_t prow, float M,
+                                              float ltot, int hh, float vscale, const f32x16_t (&oacc)[DB]) {
+  constexpr int D = DB * 32;
+  if (hh == 0) gst<f32x2_t>((float2 *)(slot + sl.part_ml[buf]) + prow, f32x2_t{M, ltot});
+  uint16_t *po = (uint16_t *)(slot + sl.part_o[buf]) + prow * D;
+  const float inv = (1.f / ltot) * (1.f / vscale);  // 1/vscale: exact, a power of two
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f16x2_t lo = {(_Float16)(oacc[db][4 * a] * inv), (_Float16)(oacc[db][4 * a + 1] * inv)};
+      const f16x2_t hi = {(_Float16)(oacc[db][4 * a + 2] * inv), (_Float16)(oacc[db][4 * a + 3] * inv)};
+      gst<u32x2_t>(po + db * 32 + 8 * a + 4 * hh,
+                   u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
+    }
+  }
+}
+__device__ __forceinline__ float head_vscale(const Dev &dev, const uint8_t *slot, int layer, int kv) {
+  return ((const float *)(slot + dev.sl.vscale))[layer * dev.dm.Hkv + kv];
+}
+
+// 8 features of a bf16 model's fp16 partial row
+// Each half is cut out of its word with integer ops before the conversion: per-element bit
+// casts of the loaded vector were folded into one 32-bit load that fed all eight features.
+__device__ __forceinline__ void f16x8_to_float(const u32x4_t &u, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = u[i];
+    f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+    f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+}
 
 template <int D, typename T>
 __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
@@ -366,17 +409,7 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
   const float ltot = l + __shfl_xor(l, 32);
   if (wave_active && row_ok) {
     const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[layer & 1]) + prow, f32x2_t{M, ltot});
-    float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = db * 32 + 8 * a + 4 * hh;
-        gst<f32x4_t>(po + d0, f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
-                                      oacc[db][4 * a + 3]});
-      }
-    }
+    store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
   }
 
 }
@@ -636,17 +669,7 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     const size_t lofs = FUSED ? (size_t)layer * dm.Hkv * R.splits * R.rows_b : 0;
     const int pb = FUSED ? 0 : layer & 1;
     const size_t prow = lofs + ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[pb]) + prow, f32x2_t{M, ltot});
-    float *po = (float *)(slot + dev.sl.part_o[pb]) + prow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = db * 32 + 8 * a + 4 * hh;
-        gst<f32x4_t>(po + d0, f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
-                                      oacc[db][4 * a + 3]});
-      }
-    }
+    store_partial<DB>(slot, dev.sl, pb, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
   }
 }
 
@@ -964,17 +987,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const float ltot = l + __shfl_xor(l, 32);
   if (wave_active && row_ok) {
     const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    if (hh == 0) gst<f32x2_t>((float2 *)(slot + dev.sl.part_ml[layer & 1]) + prow, f32x2_t{M, ltot});
-    float *po = (float *)(slot + dev.sl.part_o[layer & 1]) + prow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = db * 32 + 8 * a + 4 * hh;
-        gst<f32x4_t>(po + d0, f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
-                                      oacc[db][4 * a + 3]});
-      }
-    }
+    store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
   }
 }
 
@@ -1150,10 +1163,13 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
       Mb = Mn;
     }
   }
+  // partials: fp16 o/l for bf16 models (weight exp2(m - Ms) * l), fp32 o for fp32 models
+  constexpr bool F16 = std::is_same<T, uint16_t>::value;
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[layer & 1]);
-  const float *po = (const float *)(slot + dev.sl.part_o[layer & 1]);
+  const uint8_t *po = slot + dev.sl.part_o[layer & 1];
   const int row = j * g + gi;
   const size_t pbase = (size_t)kv * R.splits * R.rows_b + row;
+  const float vs = F16 ? head_vscale(dev, slot, layer, kv) : 1.f;
   float Ms = Mb;
   for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
   const float fb = fast_exp2(Mb - Ms);
@@ -1165,13 +1181,21 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
     const f32x2_t ml = gld<f32x2_t>(pml + prow);
     const float f = fast_exp2(ml[0] - Ms);
     Ls = fmaf(ml[1], f, Ls);
-    const f32x4_t a = gld<f32x4_t>(po + prow * D + c8 * 8);
-    const f32x4_t b = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
+    float a[8];
+    if constexpr (F16) {
+      f16x8_to_float(gld<u32x4_t>((const uint16_t *)po + prow * D + c8 * 8), a);
+    } else {
+      const f32x4_t x = gld<f32x4_t>((const float *)po + prow * D + c8 * 8);
+      const f32x4_t y = gld<f32x4_t>((const float *)po + prow * D + c8 * 8 + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      O[i] = fmaf(a[i], f, O[i]);
-      O[4 + i] = fmaf(b[i], f, O[4 + i]);
+      for (int i = 0; i < 4; ++i) {
+        a[i] = x[i];
+        a[4 + i] = y[i];
+      }
     }
+    const float wgt = F16 ? f * ml[1] * vs : f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], wgt, O[i]);
   }
   const float inv = 1.f / Ls;
 #pragma unroll
@@ -1206,7 +1230,8 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
   const float c2 = dm.scale_log2;
   const int total = (r1 - r0) * C8;
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[layer & 1]);
-  const float *po = (const float *)(slot + dev.sl.part_o[layer & 1]);
+  const uint16_t *po = (const uint16_t *)(slot + dev.sl.part_o[layer & 1]);  // fp16 o/l * 2^-e
+  const float vs = head_vscale(dev, slot, layer, kv);
   const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
   const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
   uint16_t *bk = (uint16_t *)(slot + dev.sl.beamkv_k);
@@ -1231,20 +1256,18 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
     }
     // ---- phase 1: index-only loads
     f32x2_t ml0[E], ml1[E];
-    f32x4_t pa0[E], pb0[E], pa1[E], pb1[E], ha[E], hc[E];
+    u32x4_t pa0[E], pa1[E];
+    f32x4_t ha[E], hc[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
       if (!ok[k]) continue;
       code[k] = s > 0 ? codes[j[k] * lvl + (s - 1)] : 0;
-      const float *p0 = po + pbase[k] * D + c8[k] * 8;
+      const uint16_t *p0 = po + pbase[k] * D + c8[k] * 8;
       ml0[k] = gld<f32x2_t>(pml + pbase[k]);
-      pa0[k] = gld<f32x4_t>(p0);
-      pb0[k] = gld<f32x4_t>(p0 + 4);
+      pa0[k] = gld<u32x4_t>(p0);
       if (S > 1) {
-        const float *p1 = p0 + (size_t)R.rows_b * D;
         ml1[k] = gld<f32x2_t>(pml + pbase[k] + R.rows_b);
-        pa1[k] = gld<f32x4_t>(p1);
-        pb1[k] = gld<f32x4_t>(p1 + 4);
+        pa1[k] = gld<u32x4_t>(p0 + (size_t)R.rows_b * D);
       }
       if (layer > 0) {
         const float *hr = hb + ((size_t)j[k] * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8;
@@ -1340,33 +1363,28 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
       {
         const float f = fast_exp2(ml0[k][0] - Ms);
         Ls = fmaf(ml0[k][1], f, Ls);
+        float a[8];
+        f16x8_to_float(pa0[k], a);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          O[i] = fmaf(pa0[k][i], f, O[i]);
-          O[4 + i] = fmaf(pb0[k][i], f, O[4 + i]);
-        }
+        for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml0[k][1] * vs, O[i]);
       }
       if (S > 1) {
         const float f = fast_exp2(ml1[k][0] - Ms);
         Ls = fmaf(ml1[k][1], f, Ls);
+        float a[8];
+        f16x8_to_float(pa1[k], a);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          O[i] = fmaf(pa1[k][i], f, O[i]);
-          O[4 + i] = fmaf(pb1[k][i], f, O[4 + i]);
-        }
+        for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml1[k][1] * vs, O[i]);
       }
       for (int sp = 2; sp < S; ++sp) {
         const size_t prow = pbase[k] + (size_t)sp * R.rows_b;
         const f32x2_t ml = gld<f32x2_t>(pml + prow);
         const float f = fast_exp2(ml[0] - Ms);
         Ls = fmaf(ml[1], f, Ls);
-        const f32x4_t a = gld<f32x4_t>(po + prow * D + c8[k] * 8);
-        const f32x4_t b = gld<f32x4_t>(po + prow * D + c8[k] * 8 + 4);
+        float a[8];
+        f16x8_to_float(gld<u32x4_t>(po + prow * D + c8[k] * 8), a);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          O[i] = fmaf(a[i], f, O[i]);
-          O[4 + i] = fmaf(b[i], f, O[4 + i]);
-        }
+        for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml[1] * vs, O[i]);
       }
       const float inv = 1.f / Ls;
 #pragma unroll
@@ -1424,7 +1442,7 @@ __global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepR
   const Dims &dm = dev.dm;
   uint8_t *slot = slot_base(dev, R.slot);
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[0]);
-  const float *po = (const float *)(slot + dev.sl.part_o[0]);
+  const uint16_t *po = (const uint16_t *)(slot + dev.sl.part_o[0]);  // fp16 o/l * 2^-e
   float *tmp = (float *)(slot + dev.sl.part_o[1]);
   const size_t lofs = (size_t)layer * dm.Hkv * R.splits * R.rows_b;
   for (int e = threadIdx.x; e < dm.Hq * C8; e += blockDim.x) {
@@ -1432,6 +1450,7 @@ __global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepR
     const size_t pbase = lofs + (size_t)kv * R.splits * R.rows_b + row;
     float Ms = kNegInf;
     for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
+    const float vs = head_vscale(dev, slot, layer, kv);
     float Ls = 0.f, O[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) O[i] = 0.f;
@@ -1440,13 +1459,10 @@ __global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepR
       const f32x2_t ml = gld<f32x2_t>(pml + prow);
       const float f = fast_exp2(ml[0] - Ms);
       Ls = fmaf(ml[1], f, Ls);
-      const f32x4_t a = gld<f32x4_t>(po + prow * D + c8 * 8);
-      const f32x4_t b = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
+      float a[8];
+      f16x8_to_float(gld<u32x4_t>(po + prow * D + c8 * 8), a);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        O[i] = fmaf(a[i], f, O[i]);
-        O[4 + i] = fmaf(b[i], f, O[4 + i]);
-      }
+      for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml[1] * vs, O[i]);
     }
     const float inv = 1.f / Ls;
     const f32x4_t a = f32x4_t{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
@@ -1949,11 +1965,21 @@ __global__ void k_relayout_vt(const T *__restrict__ src, T *__restrict__ dst, in
 // Largest L2 norm of the context keys of each (layer, kv head): one workgroup per pair,
 // one wave per key row at a time.
 template <typename T>
-__global__ __launch_bounds__(256) void k_key_norm_max(const T *__restrict__ k, int N, int Np, int d,
-                                                      float *__restrict__ out) {
-  __shared__ float smax[4];
+__global__ __launch_bounds__(256) void k_key_norm_max(const T *__restrict__ k, const T *__restrict__ vt, int N,
+                                                      int Np, int d, float *__restrict__ out,
+                                                      float *__restrict__ out_vscale) {
+  __shared__ float smax[4], svmax[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const T *base = k + (size_t)blockIdx.x * Np * d;
+  // largest |v| of the head's first N tokens (V^T rows of Np tokens)
+  float vmax = 0.f;
+  for (int e = w; e < d; e += 4)
+    for (int t = lane; t < N; t += 64) {
+      const T x = vt[((size_t)blockIdx.x * d + e) * Np + t];
+      vmax = fmaxf(vmax, fabsf(sizeof(T) == 2 ? __uint_as_float(((uint32_t)(uint16_t)x) << 16) : (float)x));
+    }
+  vmax = wave_max(vmax);
+  if (lane == 0) svmax[w] = vmax;
   float best = 0.f;
   for (int t = w; t < N; t += 4) {
     float acc = 0.f;
@@ -1966,7 +1992,13 @@ __global__ __launch_bounds__(256) void k_key_norm_max(const T *__restrict__ k, i
   }
   if (lane == 0) smax[w] = best;
   __syncthreads();
-  if (threadIdx.x == 0) out[blockIdx.x] = sqrtf(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+  if (threadIdx.x == 0) {
+    out[blockIdx.x] = sqrtf(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+    // value scale 2^e with max|v| < 2^e (frexp: max|v| = m 2^e, m in [0.5, 1)), kept a normal float
+    int ex = 0;
+    (void)frexpf(fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3])), &ex);
+    out_vscale[blockIdx.x] = ldexpf(1.f, min(max(ex, -126), 127));
+  }
 }
 
 struct GatherSlots {
@@ -2060,7 +2092,7 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
 hipError_t launch_ctx_attn_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs,
                                        hipStream_t st, LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
-  launch(k_ctx_attn_stream<4, true>, dim3(total_wgs, dev.dm.L), dim3(64), st, ev, dev, reqs, n_reqs, 0);
+  launch(k_ctx_attn_stream<3, true>, dim3(total_wgs, dev.dm.L), dim3(64), st, ev, dev, reqs, n_reqs, 0);
   return hipGetLastError();
 }
 
@@ -2141,14 +2173,14 @@ hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, vo
   return hipGetLastError();
 }
 
-hipError_t launch_key_norm_max(const void *k_native, int L, int Hkv, int N, int Np, int d, int elem_bytes,
-                               float *out, hipStream_t st) {
+hipError_t launch_key_norm_max(const void *k_native, const void *vt_native, int L, int Hkv, int N, int Np, int d,
+                               int elem_bytes, float *out, float *out_vscale, hipStream_t st) {
   if (elem_bytes == 2)
-    hipLaunchKernelGGL(k_key_norm_max<uint16_t>, dim3(L * Hkv), dim3(256), 0, st, (const uint16_t *)k_native, N, Np,
-                       d, out);
+    hipLaunchKernelGGL(k_key_norm_max<uint16_t>, dim3(L * Hkv), dim3(256), 0, st, (const uint16_t *)k_native,
+                       (const uint16_t *)vt_native, N, Np, d, out, out_vscale);
   else
-    hipLaunchKernelGGL(k_key_norm_max<float>, dim3(L * Hkv), dim3(256), 0, st, (const float *)k_native, N, Np, d,
-                       out);
+    hipLaunchKernelGGL(k_key_norm_max<float>, dim3(L * Hkv), dim3(256), 0, st, (const float *)k_native,
+                       (const float *)vt_native, N, Np, d, out, out_vscale);
   return hipGetLastError();
 }
 

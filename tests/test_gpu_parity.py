@@ -97,6 +97,44 @@ def test_adopt_equals_copy_bit_identical():
     assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
 
 
+def _bf16_times_pow2(bits: np.ndarray, k: int) -> np.ndarray:
+    """bf16 bit patterns times 2^k (exact: only the exponent moves)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
+    out = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((out.astype(np.uint32) << 16).view(np.float32), f)
+    return out
+
+
+def test_value_range_power_of_two_scaling():
+    """Attention is linear in V and the logits are h @ w_sid, so scaling every value row (context
+    and beam tokens) by 2^k and w_sid by 2^-k leaves the search unchanged; in floating point the
+    scaling is exact and commutes with every rounding, so the decode is bit-identical.  2^17
+    takes |v| past fp16's range and 2^-30 far below its normal range: the split partials must
+    hold both (16-bit o/l carries a per-head power-of-two scale)."""
+    import semantic_id_beam_amd as sib
+    from tests.engine_inputs import request_tensors
+    cfg = synth.get_config("ctx1k_beam256", n_layers=2, ctx_len=700, beam_width=128, n_items=50000)
+    _decode_checked(cfg, debug_attn=False)                 # the unscaled search is the oracle's
+    tq, tk, tv = synth.token_tables(cfg)
+    w = synth.w_sid(cfg)
+    N, W = synth.request_shapes(cfg)[0]
+    runs = []
+    for k in (0, 17, -30):
+        eng = sib.BeamEngine(tok_q=tq, tok_k=tk, tok_v=_bf16_times_pow2(tv, k), w_sid=w * np.float32(2.0 ** -k),
+                             items=synth.items(cfg), n_layers=cfg.n_layers, n_q_heads=cfg.n_q_heads,
+                             n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, dtype=cfg.dtype, max_requests=1,
+                             max_beam_width=W, max_ctx_tokens=sib._lib.lib().gr_ctx_padded_len(N))
+        kc, vc, q = request_tensors(cfg, 0)
+        eng.load(3, kc, vc * (2.0 ** k), q, W)
+        for _ in range(cfg.n_levels):
+            eng.step([3])
+        runs.append(eng.beams(3))
+        eng.close()
+    for c, sc in runs[1:]:
+        assert np.array_equal(c, runs[0][0])
+        assert np.array_equal(sc.view(np.uint32), runs[0][1].view(np.uint32))
+
+
 def test_determinism_bit_identical():
     cfg = synth.get_config("ctx1k_beam256", ctx_len=777, beam_width=128, n_items=50000)
     eng = make_engine(cfg, max_requests=1)
