@@ -552,14 +552,27 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   std::vector<int> kind((size_t)n);
   for (int i = 0; i < n; ++i)
     kind[(size_t)i] = d.dtype == 1 ? gr::ctx_kind_for(rs[(size_t)i]->n_bound * d.g, rs[(size_t)i]->N, d.d) : 0;
+  // A wide step (every request on the 8-wave variant) whose row blocks fill the chip over at
+  // most min(L, S_max) layers per launch runs without split partials: each workgroup covers the
+  // whole context of one layer and finishes it, the layers of a launch go to separate
+  // hidden-vector partials (in the room of the split partials), summed into h at the end.
+  const int lg_max = std::min(d.L, d.S_max);
+  bool layered = d.dtype == 1 && d.d == 128 && !first_fused;
+  int64_t wide_units = 0;
+  for (int i = 0; i < n && layered; ++i) {
+    layered = (kind[(size_t)i] & 0xFF) == 8;
+    wide_units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)i]->n_bound * d.g, gr::ctx_rows_per_wg(kind[(size_t)i]));
+  }
+  layered = layered && wide_units * lg_max >= 192;
+  bool any_hparts = false;
   std::vector<int> order((size_t)n);
   for (int i = 0; i < n; ++i) order[(size_t)i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kind[(size_t)a] < kind[(size_t)b]; });
-  struct Group { int kind, start, count, wgs; };
+  struct Group { int kind, start, count, wgs, lgroups; };
   std::vector<Group> groups;
   for (int i = 0; i < n; ++i) {
     const int k = kind[(size_t)order[(size_t)i]];
-    if (groups.empty() || groups.back().kind != k) groups.push_back({k, i, 0, 0});
+    if (groups.empty() || groups.back().kind != k) groups.push_back({k, i, 0, 0, 0});
     groups.back().count++;
   }
   const int slot_i = e->ring;
@@ -579,6 +592,12 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     int64_t units = 0;
     for (int i = G.start; i < G.start + G.count; ++i)
       units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)order[(size_t)i]]->n_bound * d.g, rows_wg);
+    int lgroups = 0;
+    if (layered) {
+      lgroups = (int)std::min<int64_t>(lg_max, std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1)));
+      G.lgroups = lgroups;
+      any_hparts = any_hparts || lgroups > 1;
+    }
     int wg_ctx = 0;
     for (int i = G.start; i < G.start + G.count; ++i) {
       gr_engine::Req *R = rs[(size_t)order[(size_t)i]];
@@ -598,7 +617,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       w.row_blocks = ceil_div(rows, rows_wg);
       // split-K: enough workgroups, at least two tiles per range, and no more partial rows
       // than the slot holds (Hkv * S_max * W_max * g)
-      int S = (int)std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1));
+      int S = layered ? 1 : (int)std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1));
       S = std::min(S, std::max(1, ceil_div(R->N, 2 * gr::kTileTok)));
       S = (int)std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)d.S_max * d.W_max * d.g / rows));
       S = std::min(S, 256);
@@ -607,8 +626,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       S = ceil_div(R->N, tps);
       w.splits = S;
       w.tps = tps;
+      w.lgroups = lgroups;
       w.wg_ctx = wg_ctx;
-      if (d.dtype == 1)
+      if (layered)
+        wg_ctx += (int)align_up((size_t)d.Hkv * lgroups, 8) * w.row_blocks;
+      else if (d.dtype == 1)
         wg_ctx += (int)align_up((size_t)d.Hkv * S, 8) * w.row_blocks;  // multiple of 8: XCD-aware order
       else
         wg_ctx += ceil_div((int64_t)d.Hkv * rows * S, 4);
@@ -647,7 +669,29 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       return r;
     prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
   }
-  for (int l = 0; l < (first_fused ? 0 : d.L); ++l) {
+  if (layered) {
+    const auto pc = prof_pair(e, pon);
+    step_start = pc.first;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group &G = groups[gi];
+      for (int l0 = 0; l0 < d.L; l0 += G.lgroups) {
+        const bool first = gi == 0 && l0 == 0, last = gi + 1 == groups.size() && l0 + G.lgroups >= d.L;
+        const gr::LaunchEv ev = prof_ev(e, first ? pc.first : -1, last ? pc.second : -1);
+        if ((r = check_dev(e, gr::launch_ctx_attn_layered(e->dev, dw + G.start, G.count, l0, G.wgs, G.kind, st, ev),
+                           "context attention")) != GR_OK)
+          return r;
+      }
+    }
+    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L);
+    if (any_hparts) {
+      const auto pm = prof_pair(e, pon);
+      if ((r = check_dev(e, gr::launch_sum_hparts(e->dev, dw, n, st, prof_ev(e, pm.first, pm.second)),
+                         "layer-group sum")) != GR_OK)
+        return r;
+      prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
+    }
+  }
+  for (int l = 0; l < (first_fused || layered ? 0 : d.L); ++l) {
     const auto pc = prof_pair(e, pon);
     if (l == 0) step_start = pc.first;
     for (size_t gi = 0; gi < groups.size(); ++gi) {

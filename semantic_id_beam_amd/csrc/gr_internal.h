@@ -69,6 +69,7 @@ struct StepReq {
   int n_bound;          // upper bound of n_s known on the host (device holds the exact n_s)
   int rows_b;           // n_bound * g: row stride of the split-K partials
   int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
+  int lgroups;          // full-context wide steps: layers per launch = hidden-vector partials (else 0)
   int row_blocks;       // context-attention row blocks per kv head
   int wg_ctx, wg_merge, wg_logits, wg_lsm;  // first workgroup of this request in each launch
 };
@@ -94,6 +95,14 @@ hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, in
 // finish: per-layer outputs into buffer 1, then h = sum over layers in order.
 hipError_t launch_ctx_attn_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs,
                                        hipStream_t st, LaunchEv ev = {});
+// A wide step (8-wave variant, head_dim 128, bf16) without split partials: one launch covers
+// layers layer0 .. layer0 + lgroups - 1, workgroup (row block, kv head, g) owns layer layer0 + g
+// over the whole context and finishes it; layer layer0 + g goes into h when lgroups == 1, else
+// into partial g at part_o[0] + g*W_max*Hq*d floats (stored by the launch with layer0 == 0,
+// added to by the later ones), which launch_sum_hparts adds into h in order.
+hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_reqs, int layer0, int total_wgs,
+                                   int ctx_kind, hipStream_t st, LaunchEv ev = {});
+hipError_t launch_sum_hparts(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_finish_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st,
                                      LaunchEv ev = {});
 hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,

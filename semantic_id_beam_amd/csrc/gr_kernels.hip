@@ -673,9 +673,133 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
   }
 }
 
-template <int NST, bool HILO>
+// The beam's own tokens t < s for the lane's query row (beam j, head of kv head kv) in the
+// layered wide kernel, merged online into (M, l, o) before the context loop: the newest token
+// from the token tables (appended to BeamKV by the gi == 0 row of the beam), older ones from
+// BeamKV at the beam's ancestry.  qf holds the lane's features kb*16 + 8hh .. +8; oacc[db][4a + c]
+// is feature db*32 + 8a + 4hh + c.  A row's two lanes compute the same scores, and only the
+// hh == 0 lane counts p in l (l of the two lanes is summed at the end).  Lanes of rows past the
+// live beams load nothing but take part in the shuffles.
+template <int D>
+__device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                                int j, int gi, int code, int hh, float c2,
+                                                const bf16x8_t (&qf)[D / 16], float &M, float &l,
+                                                f32x16_t (&oacc)[D / 32], bool append) {
+  constexpr int KB = D / 16, DB = D / 32;
+  const Dims &dm = dev.dm;
+  const int lvl = dm.levels;
+  uint16_t *bk = (uint16_t *)(slot + dev.sl.beamkv_k);
+  uint16_t *bv = (uint16_t *)(slot + dev.sl.beamkv_v);
+  const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
+  const size_t lvstride = (size_t)dm.W_max * wstride;
+  const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
+  const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
+  for (int t = 0; t < s; ++t) {
+    const uint16_t *kp = nullptr, *vp = nullptr;
+    if (row_ok) {
+      if (t == s - 1) {
+        const size_t trow = (((size_t)layer * (lvl - 1) + t) * dm.V + code) * dm.Hkv + kv;
+        kp = (const uint16_t *)dev.tok_k + trow * D;
+        vp = (const uint16_t *)dev.tok_v + trow * D;
+      } else {
+        const size_t off = lbase + (size_t)t * lvstride + (size_t)anc[j * lvl + t] * wstride;
+        kp = bk + off;
+        vp = bv + off;
+      }
+    }
+    const bool app = append && t == s - 1 && row_ok && gi == 0;
+    const size_t dst = lbase + (size_t)t * lvstride + (size_t)j * wstride;
+    float dot = 0.f;
+    {
+      u32x4_t kr[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kr[kb] = row_ok ? gld<u32x4_t>(kp + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot = fmaf((float)qf[kb][2 * e], __uint_as_float(kr[kb][e] << 16), dot);
+          dot = fmaf((float)qf[kb][2 * e + 1], __uint_as_float(kr[kb][e] & 0xFFFF0000u), dot);
+        }
+        if (app) gst<u32x4_t>(bk + dst + kb * 16 + 8 * hh, kr[kb]);
+      }
+    }
+    dot += __shfl_xor(dot, 32);
+    const float u = dot * c2;
+    const float Mn = fmaxf(M, u);
+    const float f = fast_exp2(M - Mn);  // M = -inf before the first token of the lazy path: f = 0
+    const float p = fast_exp2(u - Mn);
+    l = fmaf(l, f, hh == 0 ? p : 0.f);
+    // values in two halves of DB/2 feature blocks (fewer live registers)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x2_t vr[DB * 2];
+#pragma unroll
+      for (int q = 0; q < DB * 2; ++q) {
+        const int qq = half * DB * 2 + q;
+        vr[q] = row_ok ? gld<u32x2_t>(vp + (qq >> 2) * 32 + 8 * (qq & 3) + 4 * hh) : u32x2_t{0, 0};
+      }
+#pragma unroll
+      for (int dbl = 0; dbl < DB / 2; ++dbl) {
+        const int db = half * (DB / 2) + dbl;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t wv = vr[dbl * 4 + (i >> 2)][(i & 3) >> 1];
+          const float v = __uint_as_float((i & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+          oacc[db][i] = fmaf(p, v, oacc[db][i] * f);
+        }
+      }
+      if (app) {
+#pragma unroll
+        for (int q = 0; q < DB * 2; ++q) {
+          const int qq = half * DB * 2 + q;
+          gst<u32x2_t>(bv + dst + (qq >> 2) * 32 + 8 * (qq & 3) + 4 * hh, vr[q]);
+        }
+      }
+    }
+    M = Mn;
+  }
+}
+
+// Layer output o/l of the lane's query row in the layered wide kernel: to the debug rows, and
+// added to the layer group's hidden-vector partial (stored for the group's first layer).
+template <int D>
+__device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
+                                                 int hq, int hh, float ltot, const f32x16_t (&oacc)[D / 32],
+                                                 bool first, int lg) {
+  constexpr int DB = D / 32;
+  const Dims &dm = dev.dm;
+  const float inv = 1.f / ltot;
+  float *hp = (R.lgroups > 1 ? (float *)(slot + dev.sl.part_o[0]) + (size_t)lg * dm.W_max * dm.Hq * D
+                             : (float *)(slot + dev.sl.h)) +
+              ((size_t)j * dm.Hq + hq) * D;
+  float *dg = dm.debug_attn ? (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j) * dm.Hq + hq) * D
+                            : nullptr;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int f0 = db * 32 + 8 * a + 4 * hh;
+      f32x4_t o = f32x4_t{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv, oacc[db][4 * a + 2] * inv,
+                          oacc[db][4 * a + 3] * inv};
+      if (dg) gst<f32x4_t>(dg + f0, o);
+      if (!first) o += gld<f32x4_t>(hp + f0);
+      gst<f32x4_t>(hp + f0, o);
+    }
+}
+
+// LAYERED: a launch covers layers layer_arg .. layer_arg + lgroups - 1, and a workgroup owns its
+// row block over the whole context of one of them, layer_arg + g (every layer's query comes
+// from the token tables or the request, never from another layer's output).  It then finishes
+// its rows itself, with no split partials: the beam's own tokens are merged into (m, l, o) in
+// the prologue (the newest one appended to BeamKV), the context loop continues from that
+// state, and o/l is added to hidden-vector partial g (h itself when lgroups == 1; otherwise
+// k_sum_hparts adds the partials in order at the end).  Layer g of every launch goes to
+// partial g, so no two workgroups of a launch update one row.  Otherwise: one layer, one
+// token range, split partials out, and the previous layer finished in the prologue.
+template <int NST, bool HILO, bool LAYERED>
 __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
-                                                       int layer) {
+                                                       int layer_arg) {
   constexpr int D = 128, NW = 8, TT = 64, KB = D / 16, DB = D / 32, NT = NW * 64;
   constexpr int P = NST - 2;                          // tiles in flight beyond the one in use
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
@@ -685,9 +809,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   static_assert(TT == kTileTok, "tiles never cross the zero-padded end of the context");
   __shared__ bf16x8_t sK[NST][KCH];   // [token row swap23(r)][column c ^ (row & 15)]
   __shared__ bf16x8_t sV[NST][VCH];   // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
-  // per-wave score bounds, read right after the prologue barrier; the last K stage receives
-  // its first tile only after the next barrier
-  float *sBound = (float *)&sK[NST - 1][0];
+  __shared__ float sBound[NW];        // per-wave score bounds of the current layer
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
   const int kx = lane & 15, vx = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of this lane's operand row
@@ -698,8 +820,9 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const int rest = local >> 3;
   const int rb = rest % R.row_blocks;
   const int pidx = (rest / R.row_blocks) * 8 + (local & 7);
-  if (pidx >= dm.Hkv * R.splits) return;  // padding workgroup
-  const int h = pidx / R.splits, sp = pidx % R.splits;
+  const int nparts = LAYERED ? R.lgroups : R.splits;  // layer groups, or token ranges
+  if (pidx >= dm.Hkv * nparts) return;  // padding workgroup
+  const int h = pidx / nparts, sp = pidx % nparts;
 
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
@@ -713,12 +836,13 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const int q_row = wrow + (lane & 31);
   const bool row_ok = q_row < rows;
 
-  const int t0 = sp * R.tps;
-  const int t1 = min(R.N, t0 + R.tps);
+  const int t0 = LAYERED ? 0 : sp * R.tps;
+  const int t1 = LAYERED ? R.N : min(R.N, t0 + R.tps);
   const int ntiles = (t1 - t0 + TT - 1) / TT;
   const int nsub = (t1 - t0 + 31) / 32;
-  const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
-  const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
+  const int layer = layer_arg + (LAYERED ? sp : 0);
+  if (layer >= dm.L) return;  // past the last layer of the last launch
+  const uint16_t *gK = nullptr, *gV = nullptr;  // the current layer's K and V^T of kv head h
 
   // per-lane DMA sources (elements from the tile's first token) for this wave's chunks
   uint32_t koff[KI], voff[VI];
@@ -743,64 +867,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 #pragma unroll
     for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + i * 1024);
   };
-  // the tiles the ring holds ahead of the first one go out before anything else
-#pragma unroll
-  for (int k = 0; k < P; ++k)
-    if (k < ntiles) issue(k);
-
-  // ---- query fragments (B operand of QK^T): lane holds Q[q_row][kb*16 + 8*hh .. +8]
-  bf16x8_t qf[KB];
-  {
-    const uint16_t *qsrc = nullptr;
-    if (row_ok) {
-      const int j = q_row / dm.g, hq = h * dm.g + q_row % dm.g;
-      if (s == 0) {
-        qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq) * D;
-      } else {
-        const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
-        const int code = codes[j * dm.levels + (s - 1)];
-        qsrc = (const uint16_t *)dev.tok_q +
-               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
-  }
-
   const float c2 = dm.scale_log2;
-  float M, l = 0.f;
+  bf16x8_t qf[KB];  // B operand of QK^T: lane holds Q[q_row][kb*16 + 8*hh .. +8]
+  float M, l;
   f32x16_t oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
-  // fixed score reference from the Cauchy-Schwarz bound, as in ctx_attn_body
-  {
-    float qn = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
-    qn += __shfl_xor(qn, 32);
-    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
-    const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
-    M = B - 60.f;
-    const float bw = wave_max(B);
-    if (lane == 0) sBound[w] = bw;
-  }
-  if (layer > 0) {
-    // finish the previous layer for this workgroup's share of the row block
-    int r0, r1;
-    finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
-    finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
-  }
-  // the first P tiles have landed (explicitly: the compiler does not count the copies) and
-  // sBound is visible
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  float bmax = 0.f;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) bmax = fmaxf(bmax, sBound[i]);
-  const bool fixed_ref = bmax <= 60.f;  // uniform over the workgroup
-  if (!fixed_ref) M = kNegInf;
 
   auto qk = [&](int tile, int sub) {
     const bf16x8_t *kr = &sK[tile % NST][(sub * 32 + (lane & 31)) * (D / 8)];
@@ -979,15 +1049,86 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
       }
     }
   };
-  if (fixed_ref)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+  {
+    gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
+    gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
+    // the tiles the ring holds ahead of the first one go out before anything else
+#pragma unroll
+    for (int k = 0; k < P; ++k)
+      if (k < ntiles) issue(k);
+    // the row's beam j, query head hq and latest code (its query token at steps s >= 1)
+    const int j_row = q_row / dm.g, gi_row = q_row % dm.g, hq_row = h * dm.g + gi_row;
+    const int code_row =
+        (row_ok && s > 0) ? ((const int *)(slot + dev.sl.codes[s & 1]))[j_row * dm.levels + (s - 1)] : 0;
+    {
+      const uint16_t *qsrc = nullptr;
+      if (row_ok)
+        qsrc = s == 0 ? (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq_row) * D
+                      : (const uint16_t *)dev.tok_q +
+                            ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code_row) * dm.Hq + hq_row) * D;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
+    }
+    l = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+    // fixed score reference from the Cauchy-Schwarz bound, as in ctx_attn_body
+    {
+      float qn = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
+      qn += __shfl_xor(qn, 32);
+      const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
+      const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
+      M = B - 60.f;
+      const float bw = wave_max(B);
+      if (lane == 0) sBound[w] = bw;
+    }
+    if (LAYERED) {
+      // the beam's own tokens, against the fixed reference (redone below if the workgroup
+      // takes the lazy path)
+      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, true);
+    }
+    if (!LAYERED && layer > 0) {
+      // finish the previous layer for this workgroup's share of the row block
+      int r0, r1;
+      finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
+      finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
+    }
+    // the first P tiles have landed (explicitly: the compiler does not count the copies) and
+    // sBound is visible
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float bmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) bmax = fmaxf(bmax, sBound[i]);
+    const bool fixed_ref = bmax <= 60.f;  // uniform over the workgroup
+    if (!fixed_ref) {
+      M = kNegInf;
+      if (LAYERED) {
+        l = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+        wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, false);
+      }
+    }
 
-  const float ltot = l + __shfl_xor(l, 32);
-  if (wave_active && row_ok) {
-    const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
+    if (fixed_ref)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+
+    float ltot = l + __shfl_xor(l, 32);
+    if constexpr (!LAYERED) {
+      if (wave_active && row_ok) {
+        const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
+        store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
+      }
+    } else {
+      if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, layer_arg == 0, sp);
+    }
   }
 }
 
@@ -1489,6 +1630,25 @@ __global__ __launch_bounds__(256) void k_sum_layers(Dev dev, const StepReq *__re
     float acc = tmp[e];
     for (int l = 1; l < dm.L; ++l) acc = tmp[(size_t)l * n + e] + acc;
     hb[e] = acc;
+  }
+}
+
+// h = sum of the layer groups' hidden-vector partials of the layered wide kernel, in group
+// order, over the live beams (requests with one group wrote h directly).
+__global__ __launch_bounds__(256) void k_sum_hparts(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  const StepReq R = reqs[blockIdx.y];
+  if (R.lgroups <= 1) return;
+  const Dims &dm = dev.dm;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[R.level & 1];
+  const size_t n4 = (size_t)n_live * dm.Hq * dm.d / 4;
+  const size_t gstride = (size_t)dm.W_max * dm.Hq * dm.d / 4;
+  const f32x4_t *hp = (const f32x4_t *)(slot + dev.sl.part_o[0]);
+  f32x4_t *hb = (f32x4_t *)(slot + dev.sl.h);
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (size_t)gridDim.x * blockDim.x) {
+    f32x4_t acc = gld<f32x4_t>(hp + e);
+    for (int g = 1; g < R.lgroups; ++g) acc = acc + gld<f32x4_t>(hp + g * gstride + e);
+    gst<f32x4_t>(hb + e, acc);
   }
 }
 
@@ -2069,9 +2229,9 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
   const dim3 blk(nw * 64);
   if (dev.dm.d == 128) {
     if (nw == 8 && hilo)
-      launch(k_ctx_attn_wide<4, true>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_wide<4, true, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 8)
-      launch(k_ctx_attn_wide<4, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_wide<4, false, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 4)
       launch(k_ctx_attn_bf16_narrow<128, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 2)
@@ -2086,6 +2246,23 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
     else
       launch(k_ctx_attn_bf16_narrow<64, 1, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_reqs, int layer0, int total_wgs,
+                                   int ctx_kind, hipStream_t st, LaunchEv ev) {
+  if (total_wgs <= 0) return hipSuccess;
+  if (dev.dm.dtype != 1 || dev.dm.d != 128 || (ctx_kind & 0xFF) != 8) return hipErrorInvalidValue;
+  if (ctx_kind & kCtxHiLo)
+    launch(k_ctx_attn_wide<4, true, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
+  else
+    launch(k_ctx_attn_wide<4, false, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_hparts(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st, LaunchEv ev) {
+  if (n_reqs <= 0) return hipSuccess;
+  launch(k_sum_hparts, dim3(64, n_reqs), dim3(256), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 

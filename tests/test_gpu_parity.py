@@ -97,6 +97,39 @@ def test_adopt_equals_copy_bit_identical():
     assert np.array_equal(c1, c2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
 
 
+def test_layered_wide_steps_match_oracle():
+    """Wide steps of several requests without split partials: 4 requests x 2 row blocks (200
+    beams x 2 query heads per kv head; the second block partly empty) x 8 kv heads x 4 layers
+    per launch fill the chip, each workgroup over the whole context of one layer, whose last tile
+    is ragged; the second launch holds only layers 4 and 5 (its other workgroups stand idle).
+    Two requests are checked teacher-forced, with every layer's attention output of every beam
+    (written by the kernel's own finish) and the hidden vector (the sum of the four partials)."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=4, n_layers=6, ctx_len=700, beam_width=200, n_items=50000)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
+    checked = {0: TeacherForced(cfg, 0), 3: TeacherForced(cfg, 3)}
+    prev = {r: [()] for r in checked}
+    tol = attn_tol(cfg)
+    errs = []
+    for s in range(cfg.n_levels):
+        eng.step(rids)
+        for r, tf in checked.items():
+            after = gpu_beams(eng, r)
+            for l in range(cfg.n_layers):
+                got = eng.attn_out(r, l)
+                assert got.shape[0] == len(prev[r])
+                ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev[r]])
+                errs.append(rel_err_rows(got, ref))
+                assert errs[-1] <= tol, f"request {r} step {s} layer {l}: attention rel err {errs[-1]}"
+            h, _ = eng.hidden(r)
+            href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev[r]])
+            assert rel_err_rows(h, href) <= tol * cfg.n_layers
+            tf.check_step(prev[r], after)
+            prev[r] = after[0]
+    eng.close()
+    save_report(cfg, checked[0].report + checked[3].report, attn_err=max(errs))
+
+
 def _bf16_times_pow2(bits: np.ndarray, k: int) -> np.ndarray:
     """bf16 bit patterns times 2^k (exact: only the exponent moves)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
