@@ -27,25 +27,38 @@ METRIC = "beam-decode req/s + step µs at ctx 5000, beam 256; % MFMA peak, HBM G
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-# HBM bytes per launch of the context-attention kernels on this workload, from rocprofv3
+# HBM bytes per layer of the context-attention kernels on this workload, from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
-# the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000);
-# profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel source they were taken
-# on: with any other gr_kernels.hip the traffic is reported as null.
+# the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000), and
+# divided by the layers one dispatch covers (two for the wide kernel here, all 28 for the
+# first-level launch); profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel
+# code they were taken on (source_digest of gr_kernels.hip: comments excluded); with any
+# other code the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "65d1ccb6c2cc703c9de79c0c77491f427553a14f0140a3c0e2eb509b7eab0c01",
-    "k_ctx_attn_wide": {"read": 206565218, "written": 42213704},
-    "k_ctx_attn_stream": {"read": 166484369, "written": 278784},   # per layer of the fused launch
+    "source_sha256": "a9fc8ac7391a805bb7fc889c7ca241e18b4be6f940773bce350515b186e94fd6",
+    "k_ctx_attn_wide": {"read": 189519227, "written": 31902755},
+    "k_ctx_attn_stream": {"read": 166464200, "written": 278786},
 }
 
 
-def measured_traffic(cfg, kernel):
+def source_digest(path):
+    """SHA-256 of a C/HIP source with its // comments and blank lines removed (a comment edit
+    does not change the code the counters ran)."""
     import hashlib
+    import re
+    lines = []
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            line = re.sub(r"\s*//.*$", "", line.rstrip("\n")).rstrip()
+            if line:
+                lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
+def measured_traffic(cfg, kernel):
     src = os.path.join(ROOT, "semantic_id_beam_amd", "csrc", "gr_kernels.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if cfg.name != MEASURED_TRAFFIC["workload"] or sha != MEASURED_TRAFFIC["source_sha256"]:
+    if cfg.name != MEASURED_TRAFFIC["workload"] or source_digest(src) != MEASURED_TRAFFIC["source_sha256"]:
         return None
     t = MEASURED_TRAFFIC[kernel]
     return t["read"] + t["written"]
@@ -224,25 +237,32 @@ def main():
     achieved_gbs0 = ctx_bytes(0) * n_0 / (ms_0 * 1e-3) / 1e9 if ms_0 > 0 else 0.0
     step_us = {f"level{s}": 1e3 * prof["step"][s][0] / max(prof["step"][s][1], 1) for s in range(lv)}
 
-    # the launch of layer l also finishes layer l-1 (BeamKV append, beam tokens, split merge,
-    # h += o): its time is in the denominator, its bytes are not in the algorithmic count
+    # the unit is one layer of one step over every request: a dispatch covers one or more of them
+    # (two per dispatch for the wide kernel on the headline workload).  The kernel also finishes
+    # each layer (beam tokens, BeamKV append, h += o): that time is in the denominator, those
+    # bytes are not in the algorithmic count.
     wide = cfg.dtype == "bf16" and cfg.head_dim == 128
+    d_m = sum(G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, s) for s in levels_mfma)
+    d_0 = G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, 0)
     roofline = {
         "bound": "mfma", "achieved": round(achieved_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved_tf / PEAK_BF16_TFLOPS, 4),
         "traffic": measured_traffic(cfg, "k_ctx_attn_wide") if wide else None,
-        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+        "traffic_unit": "HBM bytes per layer (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
         "kernel": ("k_ctx_attn_wide" if wide else "k_ctx_attn") + " (levels %s)" % levels_mfma,
-        "launches": int(n_m),
-        "avg_launch_us": round(1e3 * ms_m / max(n_m, 1), 2),
-        "algorithmic_per_launch": f"{ctx_flops(levels_mfma[-1]) / 1e9:.2f} GFLOP" if levels_mfma else None,
+        "layers": int(n_m),
+        "avg_us_per_layer": round(1e3 * ms_m / max(n_m, 1), 2),
+        "dispatches": int(d_m),
+        "avg_us_per_dispatch": round(1e3 * ms_m / max(d_m, 1), 2),
+        "algorithmic_per_layer": f"{ctx_flops(levels_mfma[-1]) / 1e9:.2f} GFLOP" if levels_mfma else None,
     }
     kernels = {
         "ctx_attn_level0": {"kernel": "k_ctx_attn_stream" if wide else "k_ctx_attn",
                             "bound": "hbm", "achieved_GBs": round(achieved_gbs0, 1), "peak_GBs": PEAK_HBM_GBS,
                             "frac": round(achieved_gbs0 / PEAK_HBM_GBS, 4),
-                            "avg_launch_us": round(1e3 * ms_0 / max(n_0, 1), 2),
-                            "algorithmic_MB_per_launch": round(ctx_bytes(0) / 1e6, 2),
+                            "avg_us_per_layer": round(1e3 * ms_0 / max(n_0, 1), 2),
+                            "avg_us_per_dispatch": round(1e3 * ms_0 / max(d_0, 1), 2),
+                            "algorithmic_MB_per_layer": round(ctx_bytes(0) / 1e6, 2),
                             "traffic": measured_traffic(cfg, "k_ctx_attn_stream") if wide else None},
     }
     for name in ("beam_merge", "logits", "topk"):

@@ -225,8 +225,8 @@ gr_status gr_topk_select(const float *cand, int32_t n_rows, int32_t V, int32_t k
 
 /* Kernel kinds reported by gr_engine_profile_read. */
 typedef enum {
-  GR_PROF_CTX_ATTN = 0,   /* shared-context attention (one launch per layer) */
-  GR_PROF_BEAM_MERGE = 1, /* BeamKV append + beam attention + merge (one per layer) */
+  GR_PROF_CTX_ATTN = 0,   /* shared-context attention (per layer, or one launch for a group of layers) */
+  GR_PROF_BEAM_MERGE = 1, /* BeamKV append + beam attention + merge, or the sum of hidden-vector partials */
   GR_PROF_LOGITS = 2,     /* codebook logits (one per step) */
   GR_PROF_TOPK = 3,       /* constrained log-softmax + top-K + BeamPath update (one per step) */
   GR_PROF_STEP = 4        /* a whole gr_beam_step, first launch to last */
@@ -241,10 +241,15 @@ typedef enum {
 gr_status gr_engine_set_profiling(gr_engine *eng, int32_t enable);
 
 /* Waits for every recorded event, folds the elapsed times into the buckets and
- * returns one bucket: total milliseconds and number of launches.  level = -1
- * sums every level. */
+ * returns one bucket: total milliseconds and number of launches, where a launch that
+ * covers several layers counts once per layer (so total_ms / launches is the time per
+ * layer).  level = -1 sums every level. */
 gr_status gr_engine_profile_read(gr_engine *eng, int32_t kind, int32_t level, double *total_ms,
                                  int64_t *launches);
+
+/* The same bucket's number of kernel dispatches (total_ms / dispatches is the time per
+ * dispatch, comparable with a kernel trace). */
+gr_status gr_engine_profile_dispatches(gr_engine *eng, int32_t kind, int32_t level, int64_t *dispatches);
 
 /* Clears every bucket (pending events are folded first). */
 gr_status gr_engine_profile_reset(gr_engine *eng);

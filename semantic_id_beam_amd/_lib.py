@@ -31,7 +31,7 @@ EXPORTS = [
     "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
     "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
-    "gr_engine_profile_reset",
+    "gr_engine_profile_dispatches", "gr_engine_profile_reset",
 ]
 GR_PROF_CTX_ATTN, GR_PROF_BEAM_MERGE, GR_PROF_LOGITS, GR_PROF_TOPK, GR_PROF_STEP = range(5)
 
@@ -101,6 +101,7 @@ def lib() -> C.CDLL:
         "gr_debug_attn_out": (i32, [vp, i64, i32, i32, vp, P(i32), vp]),
         "gr_engine_set_profiling": (i32, [vp, i32]),
         "gr_engine_profile_read": (i32, [vp, i32, i32, P(C.c_double), P(i64)]),
+        "gr_engine_profile_dispatches": (i32, [vp, i32, i32, P(i64)]),
         "gr_engine_profile_reset": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
@@ -253,6 +254,12 @@ def gr_engine_profile_read(eng: int, kind: int, level: int = -1):
     ms, n = C.c_double(), C.c_int64()
     _check(lib().gr_engine_profile_read(eng, kind, level, C.byref(ms), C.byref(n)))
     return ms.value, n.value
+
+
+def gr_engine_profile_dispatches(eng: int, kind: int, level: int = -1) -> int:
+    n = C.c_int64()
+    _check(lib().gr_engine_profile_dispatches(eng, kind, level, C.byref(n)))
+    return n.value
 
 
 def gr_engine_profile_reset(eng: int):

@@ -79,10 +79,11 @@ struct gr_engine {
   bool prof = false;
   std::vector<hipEvent_t> prof_ev;
   int prof_next = 0;  // next unused event of the pool
-  struct ProfRec { int kind, level, a, b, count; };  // count: launches the record stands for
+  struct ProfRec { int kind, level, a, b, count, disp; };  // count: layer steps, disp: kernel dispatches
   std::vector<ProfRec> prof_pending;
   double prof_ms[5][gr::kMaxLevels + 1] = {};
   int64_t prof_n[5][gr::kMaxLevels + 1] = {};
+  int64_t prof_d[5][gr::kMaxLevels + 1] = {};
 
   std::vector<gr::StepReq *> pinned;
   std::vector<hipEvent_t> events;
@@ -109,6 +110,7 @@ gr_status prof_fold(gr_engine *e) {
     if ((r = check_dev(e, hipEventElapsedTime(&ms, a, b), "profiling event")) != GR_OK) return r;
     e->prof_ms[p.kind][p.level] += ms;
     e->prof_n[p.kind][p.level] += p.count;
+    e->prof_d[p.kind][p.level] += p.disp;
   }
   e->prof_pending.clear();
   e->prof_next = 0;
@@ -139,8 +141,8 @@ gr::LaunchEv prof_ev(gr_engine *e, int a, int b) {
   return ev;
 }
 
-void prof_record(gr_engine *e, int kind, int level, std::pair<int, int> ab, int count = 1) {
-  if (ab.first >= 0) e->prof_pending.push_back({kind, level, ab.first, ab.second, count});
+void prof_record(gr_engine *e, int kind, int level, std::pair<int, int> ab, int count = 1, int disp = 1) {
+  if (ab.first >= 0) e->prof_pending.push_back({kind, level, ab.first, ab.second, count, disp});
 }
 
 gr_status build_trie(gr_engine *e, const gr_item_set *items) {
@@ -672,9 +674,10 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   if (layered) {
     const auto pc = prof_pair(e, pon);
     step_start = pc.first;
+    int disp = 0;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group &G = groups[gi];
-      for (int l0 = 0; l0 < d.L; l0 += G.lgroups) {
+      for (int l0 = 0; l0 < d.L; l0 += G.lgroups, ++disp) {
         const bool first = gi == 0 && l0 == 0, last = gi + 1 == groups.size() && l0 + G.lgroups >= d.L;
         const gr::LaunchEv ev = prof_ev(e, first ? pc.first : -1, last ? pc.second : -1);
         if ((r = check_dev(e, gr::launch_ctx_attn_layered(e->dev, dw + G.start, G.count, l0, G.wgs, G.kind, st, ev),
@@ -682,7 +685,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
           return r;
       }
     }
-    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L);
+    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, disp);
     if (any_hparts) {
       const auto pm = prof_pair(e, pon);
       if ((r = check_dev(e, gr::launch_sum_hparts(e->dev, dw, n, st, prof_ev(e, pm.first, pm.second)),
@@ -701,7 +704,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
                          "context attention")) != GR_OK)
         return r;
     }
-    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc);
+    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, 1, (int)groups.size());
     // float32: finish every layer separately; bf16: layer l is finished inside layer l+1's
     // context kernel, and the last layer here
     if (d.dtype == 0 || l == d.L - 1) {
@@ -926,12 +929,26 @@ gr_status gr_engine_profile_read(gr_engine *e, int32_t kind, int32_t level, doub
   return GR_OK;
 }
 
+gr_status gr_engine_profile_dispatches(gr_engine *e, int32_t kind, int32_t level, int64_t *dispatches) {
+  if (!e || !dispatches) return fail(GR_E_INVALID_ARG, "null argument");
+  if (kind < 0 || kind > GR_PROF_STEP) return fail(GR_E_INVALID_ARG, "unknown profile kind");
+  if (level < -1 || level > e->dm.levels) return fail(GR_E_INVALID_ARG, "level out of range");
+  gr_status r = prof_fold(e);
+  if (r != GR_OK) return r;
+  int64_t n = 0;
+  for (int l = 0; l <= e->dm.levels; ++l)
+    if (level < 0 || l == level) n += e->prof_d[kind][l];
+  *dispatches = n;
+  return GR_OK;
+}
+
 gr_status gr_engine_profile_reset(gr_engine *e) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   gr_status r = prof_fold(e);
   if (r != GR_OK) return r;
   std::memset(e->prof_ms, 0, sizeof(e->prof_ms));
   std::memset(e->prof_n, 0, sizeof(e->prof_n));
+  std::memset(e->prof_d, 0, sizeof(e->prof_d));
   return GR_OK;
 }
 

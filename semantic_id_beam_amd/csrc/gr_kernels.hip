@@ -10,13 +10,21 @@
 // published online-normaliser / flash-decoding method (Milakov & Gimelshein
 // 2018); it is not on the pages.
 //
-// Kernels per decode step (one launch pair per layer, then three per step):
-//   k_ctx_attn_bf16   shared-context attention on MFMA, one (request, kv head,
-//                     row block, token range) per workgroup -> (m, l, o) partials
-//   k_ctx_attn_f32    the same on the vector ALU for float32 models
-//   k_beam_merge      appends the new token to BeamKV, attends over the beam's
-//                     own tokens found through BeamPath, merges with the
-//                     context partials and adds the layer output to h
+// Kernels of a decode step:
+//   shared-context attention on MFMA (bf16 K/V), in one of three shapes:
+//     k_ctx_attn_stream<3, true>  first level (one beam): every layer in one launch,
+//                                 split partials, then k_finish_first_level and
+//                                 k_sum_layers form h
+//     k_ctx_attn_wide<.., true>   wide steps that fill the chip: a workgroup owns one
+//                                 layer's row block over the whole context, merges the
+//                                 beam's own tokens (BeamKV through BeamPath) and adds o/l
+//                                 to a hidden partial; k_sum_hparts forms h
+//     split-K per layer           k_ctx_attn_wide<.., false>, k_ctx_attn_bf16_narrow,
+//                                 k_ctx_attn_stream<4, false>: (m, l, o) partials per
+//                                 token range; the next layer's launch finishes the layer
+//                                 (BeamKV append, beam tokens, merge, h += o) and
+//                                 k_beam_merge the last one
+//   k_ctx_attn_f32    split-K context attention on the vector ALU for float32 models
 //   k_logits          h @ w_sid[level], fp32 MFMA, split over the hidden dim
 //   k_lsm             sums the split logits, trie-masked log-softmax, candidates
 //   k_select          top-K over beams x codes, BeamPath update
