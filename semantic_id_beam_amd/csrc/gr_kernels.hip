@@ -953,10 +953,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   // softmax is spread over this wave's own MFMAs: element k (k < 8) after the k-th QK^T MFMA,
   // elements 8..15 two at a time after the first four PV MFMAs (those use the first eight
   // only).  LDS operands are fetched two MFMAs ahead; sched_barrier keeps the order.
-  auto block_fixed = [&](int u, const f32x16_t &sc) {
-    const int tq = (u + 1) >> 1, sq = (u + 1) & 1, tp = u >> 1, spv = u & 1;
-    const bf16x8_t *kr = &sK[tq % NST][(sq * 32 + (lane & 31)) * (D / 8)];
-    const bf16x8_t *vr = &sV[tp % NST][(lane & 31) * (TT / 8)];
+  // kr: the K rows of the QK^T sub-tile, vr: the V^T tile of the PV sub-tile spv.  With
+  // compile-time stages (block_fixed_st) every operand address is a per-lane register plus
+  // an immediate offset.
+  auto block_fixed_p = [&](const bf16x8_t *kr, const bf16x8_t *vr, int spv, const f32x16_t &sc) {
     auto kfrag = [&](int kb) { return kr[(kb * 2 + hh) ^ kx]; };
     auto vfrag = [&](int j) {  // j = pp*4 + db
       return vr[(j & 3) * 32 * (TT / 8) + ((spv * 4 + (j >> 2) * 2 + hh) ^ vx)];
@@ -1001,6 +1001,17 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     }
     return acc;
   };
+  auto block_fixed = [&](int u, const f32x16_t &sc) {
+    const int tq = (u + 1) >> 1, sq = (u + 1) & 1, tp = u >> 1;
+    return block_fixed_p(&sK[tq % NST][(sq * 32 + (lane & 31)) * (D / 8)], &sV[tp % NST][(lane & 31) * (TT / 8)], u & 1,
+                         sc);
+  };
+  // sub-tile u = 2*it + SPV with it % NST == ST (QK^T of sub-tile u+1, PV of sub-tile u)
+  auto block_fixed_st = [&](auto st_tag, auto spv_tag, const f32x16_t &sc) {
+    constexpr int ST = decltype(st_tag)::value, SPV = decltype(spv_tag)::value;
+    constexpr int KST = SPV ? (ST + 1) % NST : ST, SQ = SPV ? 0 : 1;
+    return block_fixed_p(&sK[KST][(SQ * 32 + (lane & 31)) * (D / 8)], &sV[ST][(lane & 31) * (TT / 8)], SPV, sc);
+  };
   static_assert(KB == 8, "the interleave assumes eight QK^T MFMAs per sub-tile");
 
   // before the first QK^T of tile it (it >= 1): tile it landed, then the barrier, then tile
@@ -1019,8 +1030,24 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     // s0 holds the scores of even sub-tiles, s1 of odd ones
     f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
     if (wave_active) s0 = qk(0, 0);
-    // steady state: both sub-tiles of tile it are unmasked and tile it+1 exists
+    // steady state: both sub-tiles of tile it are unmasked and tile it+1 exists; NST tiles
+    // at a time with compile-time stages on the fixed path, then one at a time
     int it = 0;
+    if constexpr (F::value) {
+      auto step = [&](auto st_tag) {
+        if (wave_active) s1 = block_fixed_st(st_tag, std::integral_constant<int, 0>{}, s0);
+        advance(it + 1);
+        if (wave_active) s0 = block_fixed_st(st_tag, std::integral_constant<int, 1>{}, s1);
+        ++it;
+      };
+      static_assert(NST == 4, "the unrolled steady loop walks a ring of four stages");
+      while (2 * (it + NST - 1) + 2 < nsub) {
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+      }
+    }
     for (; 2 * it + 2 < nsub; ++it) {
       if (wave_active) {
         if constexpr (F::value) {
