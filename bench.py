@@ -30,15 +30,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # HBM bytes per layer of the context-attention kernels on this workload, from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
 # the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000), and
-# divided by the layers one dispatch covers (two for the wide kernel here, all 28 for the
+# divided by the layers one dispatch covers (four for the wide kernel here, all 28 for the
 # first-level launch); profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel
 # code they were taken on (source_digest of gr_kernels.hip: comments excluded); with any
 # other code the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "a9fc8ac7391a805bb7fc889c7ca241e18b4be6f940773bce350515b186e94fd6",
-    "k_ctx_attn_wide": {"read": 189519227, "written": 31902755},
-    "k_ctx_attn_stream": {"read": 166464200, "written": 278786},
+    "source_sha256": "23949d4a19ff85a6bbadf429391b9ce45bab203ac09b36a82b65dd7a3db088a7",
+    "k_ctx_attn_wide": {"read": 190791856, "written": 31466399},
+    "k_ctx_attn_stream": {"read": 166498766, "written": 278781},
 }
 
 

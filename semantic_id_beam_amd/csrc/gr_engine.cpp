@@ -596,7 +596,9 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)order[(size_t)i]]->n_bound * d.g, rows_wg);
     int lgroups = 0;
     if (layered) {
-      lgroups = (int)std::min<int64_t>(lg_max, std::max<int64_t>(1, (want + units - 1) / std::max<int64_t>(units, 1)));
+      // two rounds of workgroups per launch: the second round starts on the units the first
+      // one frees, and the launches (and their ends) are half as many
+      lgroups = (int)std::min<int64_t>(lg_max, std::max<int64_t>(1, (2 * want + units - 1) / std::max<int64_t>(units, 1)));
       G.lgroups = lgroups;
       any_hparts = any_hparts || lgroups > 1;
     }

@@ -948,11 +948,12 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     }
   };
   // Steady-state step with the fixed reference, sub-tile u unmasked: QK^T of sub-tile u+1
-  // and softmax + PV of sub-tile u, interleaved by hand.  Issue is in order within a wave and
-  // the two waves of a SIMD do not overlap each other's exponentials with their MFMAs, so the
-  // softmax is spread over this wave's own MFMAs: element k (k < 8) after the k-th QK^T MFMA,
-  // elements 8..15 two at a time after the first four PV MFMAs (those use the first eight
-  // only).  LDS operands are fetched two MFMAs ahead; sched_barrier keeps the order.
+  // and softmax + PV of sub-tile u, interleaved by hand.  Issue is in order within a wave, so
+  // the softmax is spread over this wave's own MFMAs, giving each wave independent VALU work
+  // between its MFMAs (the two waves of a SIMD then keep the matrix core fed): element k
+  // (k < 8) after the k-th QK^T MFMA, elements 8..15 two at a time after the first four PV
+  // MFMAs (those use the first eight only).  LDS operands are fetched two MFMAs ahead (a
+  // deeper prefetch measured no faster); sched_barrier keeps the order.
   // kr: the K rows of the QK^T sub-tile, vr: the V^T tile of the PV sub-tile spv.  With
   // compile-time stages (block_fixed_st) every operand address is a per-lane register plus
   // an immediate offset.
