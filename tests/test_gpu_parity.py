@@ -130,6 +130,36 @@ def test_layered_wide_steps_match_oracle():
     save_report(cfg, checked[0].report + checked[3].report, attn_err=max(errs))
 
 
+def test_max_beam_width_1024():
+    """The largest beam width the engine takes: at the last step 1024 beams x 2 query heads =
+    8 row blocks per kv head on the full-context wide path (2 requests x 2 layers), and the
+    selection over 1024 x 256 candidates takes the streaming select.  Two requests, checked
+    teacher-forced with every layer's attention output."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=2, n_layers=2, ctx_len=300, beam_width=1024,
+                           n_items=200000)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
+    tfs = {r: TeacherForced(cfg, r) for r in rids}
+    prev = {r: [()] for r in rids}
+    tol = attn_tol(cfg)
+    errs = []
+    for s in range(cfg.n_levels):
+        eng.step(rids)
+        for r, tf in tfs.items():
+            after = gpu_beams(eng, r)
+            for l in range(cfg.n_layers):
+                got = eng.attn_out(r, l)
+                assert got.shape[0] == len(prev[r])
+                ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev[r]])
+                errs.append(rel_err_rows(got, ref))
+                assert errs[-1] <= tol, f"request {r} step {s} layer {l}: attention rel err {errs[-1]}"
+            tf.check_step(prev[r], after)
+            prev[r] = after[0]
+    assert max(len(p) for p in prev.values()) == 1024
+    eng.close()
+    save_report(cfg, tfs[0].report + tfs[1].report, attn_err=max(errs))
+
+
 def _bf16_times_pow2(bits: np.ndarray, k: int) -> np.ndarray:
     """bf16 bit patterns times 2^k (exact: only the exponent moves)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
