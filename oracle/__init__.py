@@ -21,6 +21,9 @@ What it computes (one request, one beam-search decode):
   constrained log-softmax and an exhaustive sort, nothing shared across beams.
 * Item-constrained generation (same section): only codes that extend a
   valid item prefix are candidates.
+* Candidate scoring (paper-daily article, section "Background": given
+  candidates are ranked by the model): an item's log-probability is the sum
+  of its per-level constrained log-probabilities at its own prefixes.
 
 Readings where the pages are silent (each is a choice, see ``beam.py``):
 query of step 0 is the last context token's query; a fed-back code's q/k/v
@@ -45,6 +48,7 @@ from .beam import (  # noqa: F401
     beam_search,
     codebook_logits,
     constrained_log_softmax,
+    score_items,
     select_topk,
     step_candidates,
 )

@@ -212,6 +212,38 @@ def select_topk(scores: np.ndarray, j: np.ndarray, c: np.ndarray, W: int, V: int
     return order[: min(W, scores.shape[0])]
 
 
+def score_items(req: Request, model: Model, prefixes: PrefixSet, items, norm: str = "valid") -> np.ndarray:
+    """Log-probability of each given item under the item-constrained decode: the candidates
+    are given and the model ranks them (paper-daily article, section "Background"), here by
+    its own outputs (zhiding.cn article, section "语义ID": ranking via output logits).
+
+    For item (c_0 .. c_{T-1}): sum over t of log p(c_t | c_0 .. c_{t-1}), each term the
+    constrained log-softmax at the item's own prefix, added in level order; -inf from the
+    first level whose code is not a valid child (the tuple is not an item)."""
+    items = np.asarray(items, dtype=np.int64)
+    out = np.empty(items.shape[0])
+    memo = {}
+    for i in range(items.shape[0]):
+        total = 0.0
+        for t in range(items.shape[1]):
+            prefix = tuple(int(c) for c in items[i, :t])
+            if prefix not in memo:
+                valid = prefixes.valid_codes(prefix)
+                if valid.shape[0] == 0:
+                    memo[prefix] = {}
+                else:
+                    h = beam_hidden(req, model, prefix)
+                    lp = constrained_log_softmax(codebook_logits(model, h, t), valid, norm)
+                    memo[prefix] = dict(zip(valid.tolist(), lp.tolist()))
+            lp_t = memo[prefix].get(int(items[i, t]))
+            if lp_t is None:
+                total = -np.inf
+                break
+            total = total + lp_t
+        out[i] = total
+    return out
+
+
 def beam_search(req: Request, model: Model, prefixes: PrefixSet, W: int, norm: str = "valid"):
     """Full decode of one request: n_levels steps from the empty prefix ([BG]).
 

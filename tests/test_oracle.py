@@ -298,3 +298,53 @@ def test_beam_invariants_tiny(W):
         scores = [b[1] for b in beams]
         assert all(a >= b for a, b in zip(scores, scores[1:]))
         prev = [(p, sc) for p, sc, _ in beams]
+
+
+# ----------------------------------------------------------------- candidate scoring
+@pytest.mark.parametrize("norm,key", [("valid", "R2"), ("full", "R1")])
+def test_worked_example_item_scores(norm, key):
+    """The hand-derived example's three items score their closed-form log-probabilities
+    (under R2: log 1/2, log 1/3, log 1/6), and a tuple outside the item set scores -inf."""
+    g, m, req, ps = _worked()
+    exp = {tuple(p): _ev(s) for p, s, _ in g["expected"]["valid"][key]["W3"]}
+    items = [list(k) for k in exp] + [[1, 0]]
+    got = oracle.score_items(req, m, ps, items, norm)
+    np.testing.assert_allclose(got[:-1], list(exp.values()), rtol=0, atol=1e-14)
+    assert got[-1] == -np.inf
+
+
+def test_item_probabilities_sum_to_one_under_r2():
+    """R2 normalises every level over the valid children, so the items' probabilities form a
+    distribution over the item set; R1 spends mass on invalid codes and never scores higher."""
+    cfg, m, req, ps = _tiny_cfg_inputs()
+    items = [np.unravel_index(x, (cfg.codebook,) * cfg.n_levels) for x in ps.levels[-1]]
+    r2 = oracle.score_items(req, m, ps, items, "valid")
+    r1 = oracle.score_items(req, m, ps, items, "full")
+    assert len(items) == cfg.n_items
+    assert abs(np.exp(r2).sum() - 1.0) < 1e-12
+    assert np.all(r1 <= r2 + 1e-15) and np.exp(r1).sum() <= 1.0 + 1e-12
+
+
+@pytest.mark.parametrize("norm", ["valid", "full"])
+def test_item_scores_equal_exhaustive_beam_scores(norm):
+    """W >= every level's prefix count: the search keeps every item, and its cumulative score
+    is the item's score (same terms, same order)."""
+    cfg, m, req, ps = _tiny_cfg_inputs()
+    final = oracle.beam_search(req, m, ps, 256, norm)[-1]
+    got = oracle.score_items(req, m, ps, [p for p, _, _ in final], norm)
+    assert np.array_equal(got, np.array([s for _, s, _ in final]))
+
+
+def test_tuples_outside_the_item_set_score_minus_inf():
+    cfg, m, req, ps = _tiny_cfg_inputs()
+    V = cfg.codebook
+    item = np.unravel_index(int(ps.levels[-1][0]), (V,) * cfg.n_levels)
+    pre = tuple(int(c) for c in item[:-1])
+    bad_last = next(c for c in range(V) if c not in set(ps.valid_codes(pre).tolist()))
+    bad_first = next(c for c in range(V) if c not in set(ps.valid_codes(()).tolist())) \
+        if len(ps.valid_codes(())) < V else None
+    tuples = [list(pre) + [bad_last]]
+    if bad_first is not None:
+        tuples.append([bad_first] + [0] * (cfg.n_levels - 1))
+    got = oracle.score_items(req, m, ps, tuples + [list(item)], "valid")
+    assert np.all(got[:-1] == -np.inf) and np.isfinite(got[-1])
