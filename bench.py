@@ -77,6 +77,38 @@ def workload_text(cfg, shapes):
             f"{cfg.n_q_heads} q / {cfg.n_kv_heads} kv heads, head_dim {cfg.head_dim}, {cfg.dtype}")
 
 
+def scoring_leg(cfg, args):
+    """Candidate scoring on the same context: 500 given items per call (the pages' scoring
+    workload), items of the set drawn with repeats; one request's context, calls timed end to
+    end (each call synchronises)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from tests.engine_inputs import make_engine, request_tensors
+    n_cand, n_calls = 500, max(4, args.steps // 2)
+    eng = make_engine(cfg, max_requests=1, max_beam_width=512)
+    k, v, q = request_tensors(cfg, 0)
+    eng.load(0, k, v, q, synth.request_shapes(cfg)[0][1])
+    del k, v, q
+    items = synth.items(cfg)
+    cands = items[np.random.default_rng(11).integers(0, items.shape[0], size=n_cand)].astype(np.int32)
+    for _ in range(2):
+        eng.score_items(0, cands)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        sc = eng.score_items(0, cands)
+    dt = time.perf_counter() - t0
+    eng.close()
+    log(f"scoring: {n_calls} calls of {n_cand} candidates in {dt:.3f} s")
+    assert np.all(np.isfinite(sc))
+    return {"candidates_per_call": n_cand, "calls": n_calls, "ms_per_call": round(1e3 * dt / n_calls, 3),
+            "candidates_per_s": round(n_cand * n_calls / dt, 1),
+            "context": "request 0 of the workload (ctx %d, %d layers)" % (synth.request_shapes(cfg)[0][0],
+                                                                      cfg.n_layers)}
+
+
 def cpu_baseline(cfg, n_beams: int):
     """The oracle, timed on the host cores on a bounded sample of the same workload."""
     import numpy as np
@@ -295,6 +327,8 @@ def main():
         "kernels": kernels,
     }
     eng.close()
+    del eng
+    out["scoring"] = scoring_leg(cfg, args)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_beams} beams ...")
         cb = cpu_baseline(cfg, args.cpu_beams)

@@ -193,6 +193,23 @@ gr_status gr_beams_get(gr_engine *eng, int64_t request_id, int32_t capacity, int
 gr_status gr_beams_get_batch(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, int32_t capacity,
                              int32_t *codes, float *scores, int32_t *n_beams, void *stream);
 
+/* Candidate scoring over a loaded request's context (the pages' second task, [TRT]
+ * "Background": candidates are given and the model ranks them; here, as in [GR]
+ * section "语义ID", by the model's own outputs).  Each of the n items (host
+ * [n][n_levels] codes) gets its log-probability under the item-constrained decode:
+ * the sum over levels of the constrained log-softmax of its code given its own
+ * prefix.  The n_levels steps run as in gr_beam_step, with the candidates' codes
+ * forced instead of selected (same attention kernels, BeamKV and BeamPath): level 0
+ * expands the root to every candidate, beam i then carries candidate i.  scores host
+ * [n], in candidate order; -inf for a code tuple that leaves the item trie.  The
+ * request is rewound first and stays at its last level afterwards (gr_beams_get then
+ * returns the candidates in the same order; gr_request_reset returns it to beam
+ * search).  Synchronises `stream`.  Errors: GR_E_INVALID_ARG (null arrays, n outside
+ * 1..max_beam_width, a code outside the codebook), GR_E_NOT_FOUND, GR_E_BAD_STATE
+ * (workspace not bound). */
+gr_status gr_score_items(gr_engine *eng, int64_t request_id, const int32_t *items, int32_t n, float *scores,
+                         void *stream);
+
 /* Releases a request's slot and pool space (host bookkeeping only; later work
  * on the same stream may reuse them).  Errors: GR_E_NOT_FOUND. */
 gr_status gr_request_release(gr_engine *eng, int64_t request_id);

@@ -67,6 +67,7 @@ struct gr_engine {
   struct Req {
     int slot = -1;
     int N = 0, Np = 0, W = 0, level = 0, n_bound = 1;
+    int n_items = 0;  // > 0 while the request scores given items (gr_score_items)
     bool adopt = false;
     int64_t pool_off = -1;
     const void *k = nullptr, *vt = nullptr;
@@ -233,6 +234,7 @@ void layout(gr_engine *e) {
     s.parent[b] = take(W * 4);
   }
   s.n_live = take(8);
+  s.items = take(W * d.levels * 4);
   s.dbg_attn = d.debug_attn ? take((size_t)d.L * W * d.Hq * d.d * 4) : 0;
   s.slot_bytes = align_up(o, A);
 
@@ -516,6 +518,7 @@ gr_status gr_request_reset_batch(gr_engine *e, const int64_t *ids, int32_t n, vo
   for (auto *R : rs) {
     R->level = 0;
     R->n_bound = 1;
+    R->n_items = 0;
   }
   return GR_OK;
 }
@@ -614,6 +617,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       w.Np = R->Np;
       w.slot = R->slot;
       w.level = R->level;
+      w.n_items = R->n_items;
       w.W = R->W;
       w.n_bound = R->n_bound;
       const int rows = R->n_bound * d.g;
@@ -733,6 +737,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     const int s = R->level;
     int64_t nb = std::min<int64_t>((int64_t)R->W, (int64_t)R->n_bound * d.V);
     nb = std::min<int64_t>(nb, e->nodes[s + 1]);
+    if (R->n_items > 0) nb = R->n_items;  // scoring: one beam per candidate
     R->n_bound = (int)nb;
     R->level = s + 1;
   }
@@ -809,6 +814,35 @@ gr_status gr_beams_get_batch(gr_engine *e, const int64_t *ids, int32_t n, int32_
 gr_status gr_beams_get(gr_engine *e, int64_t rid, int32_t cap, int32_t *codes, float *scores, int32_t *n_beams,
                        void *stream) {
   return gr_beams_get_batch(e, &rid, 1, cap, codes, scores, n_beams, stream);
+}
+
+gr_status gr_score_items(gr_engine *e, int64_t rid, const int32_t *items, int32_t n, float *scores, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (!items || !scores) return fail(GR_E_INVALID_ARG, "null items or scores");
+  if (n < 1 || n > e->dm.W_max) return fail(GR_E_INVALID_ARG, "n_items must be in [1, max_beam_width]");
+  auto it = e->reqs.find(rid);
+  if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+  const int lv = e->dm.levels;
+  for (int64_t i = 0; i < (int64_t)n * lv; ++i)
+    if (items[i] < 0 || items[i] >= e->dm.V) return fail(GR_E_INVALID_ARG, "item code outside the codebook");
+  gr_engine::Req &R = it->second;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, &R);
+  gr_status r;
+  if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.items, items, (size_t)n * lv * sizeof(int32_t),
+                                       hipMemcpyHostToDevice, st), "items upload")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, gr::launch_init_slots(e->dev, &R.slot, 1, st), "slot init")) != GR_OK) return r;
+  R.level = 0;
+  R.n_bound = 1;
+  R.n_items = n;
+  for (int s = 0; s < lv; ++s)
+    if ((r = gr_beam_step(e, &rid, 1, stream)) != GR_OK) return r;
+  std::vector<int32_t> codes((size_t)n * lv);
+  int32_t nb = 0;
+  return gr_beams_get_batch(e, &rid, 1, n, codes.data(), scores, &nb, stream);
 }
 
 gr_status gr_debug_beam_state(gr_engine *e, int64_t rid, int32_t cap, int32_t *parent, int32_t *codes,

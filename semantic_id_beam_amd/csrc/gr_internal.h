@@ -45,6 +45,7 @@ struct SlotLayout {
   size_t anc[2];              // [W_max][levels] i32  BeamKV slot of each level's token
   size_t parent[2];           // [W_max] i32
   size_t n_live;              // i32[2]: n_live[s & 1] = beams of B_s
+  size_t items;               // [W_max][levels] i32: the candidates of a scoring request
   size_t dbg_attn;            // [L][W_max][Hq][d] f32 (only with debug_attn)
 };
 
@@ -70,6 +71,7 @@ struct StepReq {
   int rows_b;           // n_bound * g: row stride of the split-K partials
   int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
   int lgroups;          // full-context wide steps: layers per launch = hidden-vector partials (else 0)
+  int n_items;          // > 0: scoring request, its n_items candidates' codes are forced (no top-K)
   int row_blocks;       // context-attention row blocks per kv head
   int wg_ctx, wg_merge, wg_logits, wg_lsm;  // first workgroup of this request in each launch
 };

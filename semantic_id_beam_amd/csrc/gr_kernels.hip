@@ -2052,7 +2052,51 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, int k
   block_sort_desc(sm.sel, k);
 }
 
-// Top-K over beams x codes + BeamPath update.  One workgroup per request.
+// Scoring step: candidate i (of the n_items given) takes its own code at level s instead of a
+// top-K choice.  At level 0 every candidate extends the root beam; later, beam i is candidate
+// i's prefix.  Its score is the candidate array's entry (previous score + log-prob, -inf when
+// the code is not a valid child of the prefix); an invalid prefix keeps -inf and continues
+// from the first trie node of the next level, so every index stays in range.
+__device__ void force_codes(const Dev &dev, const StepReq &R, uint8_t *slot) {
+  const Dims &dm = dev.dm;
+  const int s = R.level, V = dm.V, lvl = dm.levels, MW = dm.MW, n = R.n_items;
+  const int cur = s & 1, nxt = cur ^ 1;
+  const float *cand = (const float *)(slot + dev.sl.cand);
+  const int *items = (const int *)(slot + dev.sl.items);
+  const int *node_cur = (const int *)(slot + dev.sl.node[cur]);
+  const int *codes_cur = (const int *)(slot + dev.sl.codes[cur]);
+  const int *anc_cur = (const int *)(slot + dev.sl.anc[cur]);
+  int *codes_nxt = (int *)(slot + dev.sl.codes[nxt]);
+  int *anc_nxt = (int *)(slot + dev.sl.anc[nxt]);
+  float *score_nxt = (float *)(slot + dev.sl.score[nxt]);
+  int *node_nxt = (int *)(slot + dev.sl.node[nxt]);
+  int *parent_nxt = (int *)(slot + dev.sl.parent[nxt]);
+  const uint32_t *mask = dev.trie_mask + dev.trie_off[s] * MW;
+  const int32_t *child = dev.trie_child + dev.trie_off[s];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int j = s == 0 ? 0 : i;  // parent beam
+    const int c = items[i * lvl + s];
+    for (int t = 0; t < s; ++t) {
+      codes_nxt[i * lvl + t] = codes_cur[j * lvl + t];
+      anc_nxt[i * lvl + t] = anc_cur[j * lvl + t];
+    }
+    codes_nxt[i * lvl + s] = c;
+    anc_nxt[i * lvl + s] = i;
+    parent_nxt[i] = j;
+    const int nj = node_cur[j];
+    const uint32_t *mrow = mask + (size_t)nj * MW;
+    const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
+    score_nxt[i] = valid ? cand[(size_t)j * V + c] : kNegInf;
+    int below = 0;
+    for (int wd = 0; wd < (c >> 5); ++wd) below += __popc(mrow[wd]);
+    below += __popc(mrow[c >> 5] & ((1u << (c & 31)) - 1u));
+    node_nxt[i] = valid ? child[nj] + below : 0;
+  }
+  if (threadIdx.x == 0) ((int *)(slot + dev.sl.n_live))[nxt] = n;
+}
+
+// Top-K over beams x codes + BeamPath update (or the forced codes of a scoring request).  One
+// workgroup per request.
 template <bool REGS>
 __global__ __launch_bounds__(kTopkThreads) void k_select(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
   __shared__ SelectSmem sm;
@@ -2060,6 +2104,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_select(Dev dev, const StepReq 
   const StepReq R = reqs[blockIdx.x];
   const Dims &dm = dev.dm;
   uint8_t *slot = slot_base(dev, R.slot);
+  if (R.n_items > 0) {
+    force_codes(dev, R, slot);
+    return;
+  }
   const int s = R.level, V = dm.V, lvl = dm.levels, MW = dm.MW;
   const int cur = s & 1, nxt = cur ^ 1;
   const int n = ((const int *)(slot + dev.sl.n_live))[cur];

@@ -81,6 +81,10 @@ class BeamEngine:
     def beams_batch(self, rids):
         return G.gr_beams_get_batch(self.eng, rids, self.max_beam_width, self.n_levels, self.stream)
 
+    def score_items(self, rid: int, items):
+        """Log-probability of each given item (its code tuple) over the request's context."""
+        return G.gr_score_items(self.eng, rid, items, self.stream)
+
     def reset(self, rid: int):
         G.gr_request_reset(self.eng, rid, self.stream)
 

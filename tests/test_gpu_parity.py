@@ -160,6 +160,63 @@ def test_max_beam_width_1024():
     save_report(cfg, tfs[0].report + tfs[1].report, attn_err=max(errs))
 
 
+def _candidates(cfg, n, n_bad, seed):
+    """n candidates: items of the set (with repeats), n_bad code tuples outside it, shuffled."""
+    rng = np.random.default_rng(seed)
+    items = synth.items(cfg)
+    ps = prefixes_for(cfg)
+    good = items[rng.integers(0, items.shape[0], size=n - n_bad)]
+    bad = []
+    while len(bad) < n_bad:
+        t = rng.integers(0, cfg.codebook, size=cfg.n_levels)
+        if not ps.contains(tuple(int(c) for c in t)):
+            bad.append(t)
+    cands = np.concatenate([good, np.array(bad, dtype=good.dtype).reshape(-1, cfg.n_levels)])
+    return cands[rng.permutation(cands.shape[0])].astype(np.int32)
+
+
+def test_score_items_matches_oracle():
+    """Candidate scoring: 500 given items (repeats and 20 tuples outside the item set among
+    them) over one request's context, against the oracle's item log-probabilities; then the
+    request's own beam search, whose final beams scored as candidates give their beam scores."""
+    cfg = synth.get_config("ctx1k_beam256", n_layers=2, ctx_len=700, beam_width=64, n_items=50000)
+    eng = make_engine(cfg, max_requests=1, max_beam_width=512)
+    rid = load_request(eng, cfg, 0)
+    cands = _candidates(cfg, 500, 20, seed=3)
+    got = eng.score_items(rid, cands)
+    ref = oracle.score_items(request_for(cfg, 0), model_for(cfg), prefixes_for(cfg), cands, "valid")
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin) and fin.sum() == 480
+    err = float(np.max(np.abs(got[fin] - ref[fin])))
+    assert err <= SCORE_TOL, err
+    codes, scores = eng.beams(rid)                       # the candidates, in the given order
+    assert np.array_equal(codes, cands) and np.array_equal(scores.view(np.uint32), got.view(np.uint32))
+    eng.reset(rid)                                       # back to beam search on the same context
+    for _ in range(cfg.n_levels):
+        eng.step([rid])
+    bcodes, bscores = eng.beams(rid)
+    again = eng.score_items(rid, bcodes)
+    np.testing.assert_allclose(again, bscores, rtol=0, atol=2 * SCORE_TOL)
+    eng.close()
+    save_report(cfg, [], score_err=err)
+
+
+def test_score_all_items_is_a_distribution():
+    """Under R2 the item probabilities sum to one: every item of the tiny float32 model scored
+    on the GPU in one call."""
+    cfg = synth.get_config("tiny_f32")
+    eng = make_engine(cfg, max_requests=1, max_beam_width=256)
+    rid = load_request(eng, cfg, 0)
+    ps = prefixes_for(cfg)
+    items = np.array([np.unravel_index(int(x), (cfg.codebook,) * cfg.n_levels) for x in ps.levels[-1]],
+                     dtype=np.int32)
+    got = eng.score_items(rid, items)
+    ref = oracle.score_items(request_for(cfg, 0), model_for(cfg), ps, items, "valid")
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
+    assert abs(float(np.exp(got.astype(np.float64)).sum()) - 1.0) < 1e-5
+    eng.close()
+
+
 def _bf16_times_pow2(bits: np.ndarray, k: int) -> np.ndarray:
     """bf16 bit patterns times 2^k (exact: only the exponent moves)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
