@@ -78,35 +78,38 @@ def workload_text(cfg, shapes):
 
 
 def scoring_leg(cfg, args):
-    """Candidate scoring on the same context: 500 given items per call (the pages' scoring
-    workload), items of the set drawn with repeats; one request's context, calls timed end to
-    end (each call synchronises)."""
+    """Candidate scoring on the same contexts: 500 given items per request per call (the pages'
+    scoring workload), items of the set drawn with repeats; every request of the workload in
+    one call (gr_score_items_batch), calls timed end to end (each call synchronises)."""
     import numpy as np
     import torch
 
     import synth
     from tests.engine_inputs import make_engine, request_tensors
     n_cand, n_calls = 500, max(4, args.steps // 2)
-    eng = make_engine(cfg, max_requests=1, max_beam_width=512)
-    k, v, q = request_tensors(cfg, 0)
-    eng.load(0, k, v, q, synth.request_shapes(cfg)[0][1])
-    del k, v, q
+    R = cfg.n_requests
+    eng = make_engine(cfg, max_requests=R, max_beam_width=512)
+    for r in range(R):
+        k, v, q = request_tensors(cfg, r)
+        eng.load(r, k, v, q, synth.request_shapes(cfg)[r][1])
+        del k, v, q
     items = synth.items(cfg)
-    cands = items[np.random.default_rng(11).integers(0, items.shape[0], size=n_cand)].astype(np.int32)
+    rng = np.random.default_rng(11)
+    cands = np.stack([items[rng.integers(0, items.shape[0], size=n_cand)] for _ in range(R)]).astype(np.int32)
+    rids = list(range(R))
     for _ in range(2):
-        eng.score_items(0, cands)
+        eng.score_items_batch(rids, cands)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(n_calls):
-        sc = eng.score_items(0, cands)
+        sc = eng.score_items_batch(rids, cands)
     dt = time.perf_counter() - t0
     eng.close()
-    log(f"scoring: {n_calls} calls of {n_cand} candidates in {dt:.3f} s")
+    log(f"scoring: {n_calls} calls of {R} x {n_cand} candidates in {dt:.3f} s")
     assert np.all(np.isfinite(sc))
-    return {"candidates_per_call": n_cand, "calls": n_calls, "ms_per_call": round(1e3 * dt / n_calls, 3),
-            "candidates_per_s": round(n_cand * n_calls / dt, 1),
-            "context": "request 0 of the workload (ctx %d, %d layers)" % (synth.request_shapes(cfg)[0][0],
-                                                                      cfg.n_layers)}
+    return {"requests_per_call": R, "candidates_per_request": n_cand, "calls": n_calls,
+            "ms_per_call": round(1e3 * dt / n_calls, 3),
+            "candidates_per_s": round(R * n_cand * n_calls / dt, 1)}
 
 
 def cpu_baseline(cfg, n_beams: int):

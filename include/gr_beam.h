@@ -210,6 +210,13 @@ gr_status gr_beams_get_batch(gr_engine *eng, const int64_t *request_ids, int32_t
 gr_status gr_score_items(gr_engine *eng, int64_t request_id, const int32_t *items, int32_t n, float *scores,
                          void *stream);
 
+/* gr_score_items for several requests in the same steps (continuous batching): request
+ * i (request_ids[i]) scores the n items at items host [n_requests][n][n_levels] row
+ * block i into scores host [n_requests][n] row i.  Errors: as gr_score_items, plus
+ * GR_E_INVALID_ARG for n_requests outside 1..max_requests or a duplicate id. */
+gr_status gr_score_items_batch(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, const int32_t *items,
+                               int32_t n, float *scores, void *stream);
+
 /* Releases a request's slot and pool space (host bookkeeping only; later work
  * on the same stream may reuse them).  Errors: GR_E_NOT_FOUND. */
 gr_status gr_request_release(gr_engine *eng, int64_t request_id);

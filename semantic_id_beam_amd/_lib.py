@@ -31,7 +31,7 @@ EXPORTS = [
     "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
     "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
-    "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items",
+    "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
 ]
 GR_PROF_CTX_ATTN, GR_PROF_BEAM_MERGE, GR_PROF_LOGITS, GR_PROF_TOPK, GR_PROF_STEP = range(5)
 
@@ -103,6 +103,7 @@ def lib() -> C.CDLL:
         "gr_engine_profile_read": (i32, [vp, i32, i32, P(C.c_double), P(i64)]),
         "gr_engine_profile_dispatches": (i32, [vp, i32, i32, P(i64)]),
         "gr_score_items": (i32, [vp, i64, vp, i32, vp, vp]),
+        "gr_score_items_batch": (i32, [vp, vp, i32, vp, i32, vp, vp]),
         "gr_engine_profile_reset": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
@@ -197,6 +198,16 @@ def gr_score_items(eng: int, rid: int, items, stream: int = 0) -> np.ndarray:
     scores = np.zeros(max(it.shape[0], 1), dtype=np.float32)
     _check(lib().gr_score_items(eng, rid, _host(it), it.shape[0], _host(scores), stream))
     return scores[: it.shape[0]]
+
+
+def gr_score_items_batch(eng: int, request_ids, items, stream: int = 0) -> np.ndarray:
+    """[n_requests][n] log-probabilities of items [n_requests][n][n_levels], one set of steps."""
+    ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+    it = np.ascontiguousarray(items, dtype=np.int32)
+    scores = np.zeros((ids.shape[0], it.shape[1]), dtype=np.float32)
+    _check(lib().gr_score_items_batch(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), ids.shape[0], _host(it),
+                                      it.shape[1], _host(scores), stream))
+    return scores
 
 
 def gr_request_release(eng: int, rid: int):

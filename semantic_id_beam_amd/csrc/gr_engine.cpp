@@ -816,33 +816,53 @@ gr_status gr_beams_get(gr_engine *e, int64_t rid, int32_t cap, int32_t *codes, f
   return gr_beams_get_batch(e, &rid, 1, cap, codes, scores, n_beams, stream);
 }
 
-gr_status gr_score_items(gr_engine *e, int64_t rid, const int32_t *items, int32_t n, float *scores, void *stream) {
+gr_status gr_score_items_batch(gr_engine *e, const int64_t *ids, int32_t n_req, const int32_t *items, int32_t n,
+                               float *scores, void *stream) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
-  if (!items || !scores) return fail(GR_E_INVALID_ARG, "null items or scores");
+  if (!ids || !items || !scores) return fail(GR_E_INVALID_ARG, "null ids, items or scores");
+  if (n_req < 1 || n_req > e->opts.max_requests) return fail(GR_E_INVALID_ARG, "need 1..max_requests ids");
   if (n < 1 || n > e->dm.W_max) return fail(GR_E_INVALID_ARG, "n_items must be in [1, max_beam_width]");
-  auto it = e->reqs.find(rid);
-  if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
   const int lv = e->dm.levels;
-  for (int64_t i = 0; i < (int64_t)n * lv; ++i)
+  for (int64_t i = 0; i < (int64_t)n_req * n * lv; ++i)
     if (items[i] < 0 || items[i] >= e->dm.V) return fail(GR_E_INVALID_ARG, "item code outside the codebook");
-  gr_engine::Req &R = it->second;
+  std::vector<gr_engine::Req *> rs((size_t)n_req);
+  std::vector<int32_t> slots((size_t)n_req);
+  {
+    std::unordered_set<int64_t> seen;
+    for (int i = 0; i < n_req; ++i) {
+      if (!seen.insert(ids[i]).second) return fail(GR_E_INVALID_ARG, "duplicate request id");
+      auto it = e->reqs.find(ids[i]);
+      if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
+      rs[(size_t)i] = &it->second;
+      slots[(size_t)i] = it->second.slot;
+    }
+  }
   hipStream_t st = (hipStream_t)stream;
-  uint8_t *sb = slot_ptr(e, &R);
   gr_status r;
-  if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.items, items, (size_t)n * lv * sizeof(int32_t),
-                                       hipMemcpyHostToDevice, st), "items upload")) != GR_OK)
-    return r;
-  if ((r = check_dev(e, gr::launch_init_slots(e->dev, &R.slot, 1, st), "slot init")) != GR_OK) return r;
-  R.level = 0;
-  R.n_bound = 1;
-  R.n_items = n;
+  const size_t bytes = (size_t)n * lv * sizeof(int32_t);
+  for (int i = 0; i < n_req; ++i)
+    if ((r = check_dev(e, hipMemcpyAsync(slot_ptr(e, rs[(size_t)i]) + e->sl.items, items + (size_t)i * n * lv, bytes,
+                                         hipMemcpyHostToDevice, st), "items upload")) != GR_OK)
+      return r;
+  for (int i0 = 0; i0 < n_req; i0 += gr::kGatherMax)
+    if ((r = check_dev(e, gr::launch_init_slots(e->dev, slots.data() + i0, std::min(gr::kGatherMax, n_req - i0), st),
+                       "slot init")) != GR_OK)
+      return r;
+  for (auto *R : rs) {
+    R->level = 0;
+    R->n_bound = 1;
+    R->n_items = n;
+  }
   for (int s = 0; s < lv; ++s)
-    if ((r = gr_beam_step(e, &rid, 1, stream)) != GR_OK) return r;
-  std::vector<int32_t> codes((size_t)n * lv);
-  int32_t nb = 0;
-  return gr_beams_get_batch(e, &rid, 1, n, codes.data(), scores, &nb, stream);
+    if ((r = gr_beam_step(e, ids, n_req, stream)) != GR_OK) return r;
+  std::vector<int32_t> codes((size_t)n_req * n * lv), nb((size_t)n_req);
+  return gr_beams_get_batch(e, ids, n_req, n, codes.data(), scores, nb.data(), stream);
+}
+
+gr_status gr_score_items(gr_engine *e, int64_t rid, const int32_t *items, int32_t n, float *scores, void *stream) {
+  return gr_score_items_batch(e, &rid, 1, items, n, scores, stream);
 }
 
 gr_status gr_debug_beam_state(gr_engine *e, int64_t rid, int32_t cap, int32_t *parent, int32_t *codes,

@@ -85,6 +85,10 @@ class BeamEngine:
         """Log-probability of each given item (its code tuple) over the request's context."""
         return G.gr_score_items(self.eng, rid, items, self.stream)
 
+    def score_items_batch(self, rids, items):
+        """[len(rids)][n] log-probabilities; items [len(rids)][n][n_levels]."""
+        return G.gr_score_items_batch(self.eng, rids, items, self.stream)
+
     def reset(self, rid: int):
         G.gr_request_reset(self.eng, rid, self.stream)
 

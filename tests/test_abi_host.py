@@ -144,5 +144,7 @@ def test_null_engine_is_rejected():
     assert L.gr_beam_step(None, None, 0, None) == G.GR_E_INVALID_ARG
     assert L.gr_beams_get_batch(None, None, 1, 4, None, None, None, None) == G.GR_E_INVALID_ARG
     assert L.gr_engine_profile_dispatches(None, 0, -1, None) == G.GR_E_INVALID_ARG
+    assert L.gr_score_items(None, 0, None, 1, None, None) == G.GR_E_INVALID_ARG
+    assert L.gr_score_items_batch(None, None, 1, None, 1, None, None) == G.GR_E_INVALID_ARG
     assert L.gr_engine_destroy(None) == G.GR_OK
     assert L.gr_engine_workspace_bytes(None) == 0

@@ -201,6 +201,28 @@ def test_score_items_matches_oracle():
     save_report(cfg, [], score_err=err)
 
 
+def test_score_items_batch_matches_oracle_and_single_calls():
+    """Four requests' candidates scored in the same steps (full-context wide path at 300 beams
+    x 2 layers): two requests against the oracle, all four against one call each."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=4, n_layers=2, ctx_len=700, beam_width=64, n_items=50000)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, max_beam_width=512)
+    rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
+    cands = np.stack([_candidates(cfg, 300, 10, seed=20 + r) for r in rids])
+    got = eng.score_items_batch(rids, cands)
+    assert got.shape == (4, 300)
+    for r in (0, 3):
+        ref = oracle.score_items(request_for(cfg, r), model_for(cfg), prefixes_for(cfg), cands[r], "valid")
+        fin = np.isfinite(ref)
+        assert np.array_equal(np.isfinite(got[r]), fin)
+        assert float(np.max(np.abs(got[r][fin] - ref[fin]))) <= SCORE_TOL
+    for r in rids:
+        one = eng.score_items(r, cands[r])
+        fin = np.isfinite(one)
+        assert np.array_equal(np.isfinite(got[r]), fin)
+        np.testing.assert_allclose(got[r][fin], one[fin], rtol=0, atol=2 * SCORE_TOL)
+    eng.close()
+
+
 def test_score_all_items_is_a_distribution():
     """Under R2 the item probabilities sum to one: every item of the tiny float32 model scored
     on the GPU in one call."""
