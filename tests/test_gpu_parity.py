@@ -82,6 +82,16 @@ def test_beam_widths(W):
     _decode_checked(cfg)
 
 
+@pytest.mark.parametrize("hq,hkv,d,W", [(8, 8, 128, 96), (16, 4, 128, 64), (16, 8, 64, 64), (32, 4, 64, 16)])
+def test_head_geometries(hq, hkv, d, W):
+    """Query-head groups of 1, 4 and 8 and head_dim 64 in bf16 (the other workloads all use 16
+    query / 8 kv heads of 128): g*W rows per kv head decide the context kernel (96 and 256
+    rows at d = 128 take the 4- and 8-wave kernels, d = 64 the narrow ones)."""
+    cfg = synth.get_config("ctx1k_beam256", n_q_heads=hq, n_kv_heads=hkv, head_dim=d, n_layers=2, ctx_len=500,
+                           beam_width=W, n_items=20000)
+    _decode_checked(cfg)
+
+
 def test_two_layers_bf16_split_invariance():
     cfg = synth.get_config("ctx1k_beam256", n_layers=2, ctx_len=1500, beam_width=32, n_items=20000)
     _, c1, s1 = _decode_checked(cfg, max_splits=1)
