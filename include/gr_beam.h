@@ -157,8 +157,12 @@ int32_t gr_ctx_padded_len(int32_t ctx_len);
  *              V transposed, [L][Hkv][d][Np], Np = gr_ctx_padded_len(N); tokens
  *              N..Np-1 must be zero.  The engine only keeps the pointers: the
  *              buffers must stay alive and unchanged until gr_request_release.
- * Errors: GR_E_INVALID_ARG (bad sizes, duplicate id), GR_E_OUT_OF_MEMORY (no free
- * slot or pool space), GR_E_BAD_STATE (workspace not bound). */
+ *   k and v are 16-byte aligned in both cases.  Either way one pass over the
+ *   context also takes, per (layer, kv head), the largest key norm and the
+ *   largest |v| (bounds that the attention kernels use).
+ * Errors: GR_E_INVALID_ARG (bad sizes, duplicate id, misaligned k or v),
+ * GR_E_OUT_OF_MEMORY (no free slot or pool space), GR_E_BAD_STATE (workspace not
+ * bound). */
 gr_status gr_ctx_kv_load(gr_engine *eng, int64_t request_id, int32_t ctx_len, int32_t beam_width,
                          const void *k, const void *v, const void *q_last, uint32_t flags,
                          void *stream);

@@ -441,6 +441,7 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
   if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
   if (!k || !v || !q_last) return fail(GR_E_INVALID_ARG, "null k, v or q_last");
+  if (((uintptr_t)k | (uintptr_t)v) & 15u) return fail(GR_E_INVALID_ARG, "k and v must be 16-byte aligned");
   if (N < 1) return fail(GR_E_INVALID_ARG, "ctx_len must be >= 1");
   if (W < 1 || W > e->dm.W_max) return fail(GR_E_INVALID_ARG, "beam_width must be in [1, max_beam_width]");
   if (flags & ~GR_LOAD_ADOPT) return fail(GR_E_INVALID_ARG, "unknown load flag");
@@ -453,7 +454,8 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
   R.W = W;
   hipStream_t st = (hipStream_t)stream;
   gr_status r;
-  if (flags & GR_LOAD_ADOPT) {
+  const bool adopt = (flags & GR_LOAD_ADOPT) != 0;
+  if (adopt) {
     R.adopt = true;
     R.k = k;
     R.vt = v;
@@ -462,21 +464,19 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
     if (!pool_alloc(e, Np, &off)) return fail(GR_E_OUT_OF_MEMORY, "context pool exhausted (max_ctx_tokens)");
     R.pool_off = off;
     uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
-    uint8_t *dvt = dk + (size_t)e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
     R.k = dk;
-    R.vt = dvt;
-    if ((r = check_dev(e, gr::launch_relayout(k, v, dk, dvt, e->dm.L, N, Np, e->dm.Hkv, e->dm.d, e->elem, st),
-                       "context relayout")) != GR_OK) {
-      pool_free(e, off, Np);
-      return r;
-    }
+    R.vt = dk + (size_t)e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
   }
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
-  if ((r = check_dev(e, gr::launch_key_norm_max(R.k, R.vt, e->dm.L, e->dm.Hkv, N, Np, e->dm.d, e->elem,
-                                                (float *)(sb + e->sl.knmax), (float *)(sb + e->sl.vscale), st),
-                     "key norms and value scales")) != GR_OK)
+  // native layout (unless adopted), key-norm bounds and value scales in one pass over the context
+  if ((r = check_dev(e, gr::launch_load_ctx(k, v, const_cast<void *>(R.k), const_cast<void *>(R.vt), !adopt,
+                                            e->dm.L, e->dm.Hkv, N, Np, e->dm.d, e->elem, (float *)(sb + e->sl.knmax),
+                                            (float *)(sb + e->sl.vscale), st),
+                     "context load")) != GR_OK) {
+    if (!adopt) pool_free(e, R.pool_off, Np);
     return r;
+  }
   if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem,
                                        hipMemcpyDeviceToDevice, st), "q_last copy")) != GR_OK)
     return r;

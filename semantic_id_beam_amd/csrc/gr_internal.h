@@ -114,8 +114,6 @@ hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total
 // max_cand: largest n_bound*V of the step (selects the register-resident or the streaming variant)
 hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_cand, hipStream_t st,
                        LaunchEv ev = {});
-hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N,
-                           int Np, int Hkv, int d, int elem_bytes, hipStream_t st);
 // root beam (level 0, empty prefix, score 0) in up to kGatherMax slots
 hipError_t launch_init_slots(const Dev &dev, const int32_t *slots, int n, hipStream_t st);
 // Copies n_live, codes and scores of level parity `parity` of up to kGatherMax slots into a
@@ -123,11 +121,12 @@ hipError_t launch_init_slots(const Dev &dev, const int32_t *slots, int n, hipStr
 // W_max*levels codes).
 hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, int parity, uint8_t *out,
                                  size_t out_bytes, hipStream_t st);
-// Per (layer, kv head) of a context (native K [L][Hkv][Np][d], V^T [L][Hkv][d][Np]; first N
-// tokens): the largest key norm -> out [L][Hkv], and the value scale, the power of two 2^e
-// with max |v| < 2^e -> out_vscale [L][Hkv].
-hipError_t launch_key_norm_max(const void *k_native, const void *vt_native, int L, int Hkv, int N, int Np, int d,
-                               int elem_bytes, float *out, float *out_vscale, hipStream_t st);
+// Context loading.  copy: caller K, V [L][N][Hkv][d] -> native K nk [L][Hkv][Np][d] and V^T nvt
+// [L][Hkv][d][Np] (padding zero); else nk / nvt already hold the native layout and are only
+// read.  Both: per (layer, kv head) the largest key norm -> knmax [L][Hkv] and the value
+// scale, the power of two 2^e with max |v| < 2^e over the first N tokens -> vscale [L][Hkv].
+hipError_t launch_load_ctx(const void *src_k, const void *src_v, void *nk, void *nvt, bool copy, int L, int Hkv,
+                           int N, int Np, int d, int elem_bytes, float *knmax, float *vscale, hipStream_t st);
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
 

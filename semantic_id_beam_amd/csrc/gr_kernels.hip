@@ -2178,70 +2178,149 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float *__res
 }
 
 // --------------------------------------------------------------------------------------
-// caller layout [L][N][Hkv][d] -> native K [L][Hkv][Np][d] and V^T [L][Hkv][d][Np], zero pad.
+// Context loading: one workgroup per (layer, kv head, 64-token tile), 16-byte chunks.
+// COPY: the caller's K and V [L][N][Hkv][d] go to native K [L][Hkv][Np][d] (a permutation of
+// whole token rows, copied chunk for chunk) and V^T [L][Hkv][d][Np] (transposed through
+// LDS), padding tokens N..Np-1 zero.  Otherwise the native arrays are only read.  Either
+// way the tile's tokens t < N are folded into the maxima of its (layer, kv head): squared
+// key norm and |v|, kept as float bits (non-negative floats order like their bit patterns)
+// by an atomic max into kn_bits / vm_bits, which k_load_finish turns into the key-norm bound
+// and the value scale.
+template <int S> struct UIntOf;
+template <> struct UIntOf<2> { using type = uint16_t; };
+template <> struct UIntOf<4> { using type = uint32_t; };
+
+// element i of a 16-byte chunk as float (bf16 or f32 payload)
 template <typename T>
-__global__ void k_relayout_k(const T *__restrict__ src, T *__restrict__ dst, int L, int N, int Np, int Hkv, int d) {
-  const size_t total = (size_t)L * Hkv * Np * d;
-  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-    const int dd = e % d;
-    const size_t r = e / d;
-    const int t = r % Np;
-    const size_t r2 = r / Np;
-    const int h = r2 % Hkv;
-    const int l = r2 / Hkv;
-    dst[e] = t < N ? src[(((size_t)l * N + t) * Hkv + h) * d + dd] : T(0);
-  }
+__device__ __forceinline__ float chunk_elem(const u32x4_t &x, int i) {
+  if (sizeof(T) == 2) return __uint_as_float((i & 1) ? (x[i >> 1] & 0xFFFF0000u) : (x[i >> 1] << 16));
+  return __uint_as_float(x[i]);
 }
-template <typename T>
-__global__ void k_relayout_vt(const T *__restrict__ src, T *__restrict__ dst, int L, int N, int Np, int Hkv, int d) {
-  const size_t total = (size_t)L * Hkv * d * Np;
-  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-    const int t = e % Np;
-    const size_t r = e / Np;
-    const int dd = r % d;
-    const size_t r2 = r / d;
-    const int h = r2 % Hkv;
-    const int l = r2 / Hkv;
-    dst[e] = t < N ? src[(((size_t)l * N + t) * Hkv + h) * d + dd] : T(0);
+
+constexpr int kLoadTile = 64;
+
+template <typename T, int D, bool COPY>
+__global__ __launch_bounds__(256) void k_load_ctx(const T *__restrict__ src_k, const T *__restrict__ src_v,
+                                                  T *__restrict__ nk, T *__restrict__ nvt, int N, int Np, int Hkv,
+                                                  uint32_t *__restrict__ kn_bits, uint32_t *__restrict__ vm_bits) {
+  using U = typename UIntOf<sizeof(T)>::type;
+  constexpr int EPC = 16 / sizeof(T);          // elements per chunk
+  constexpr int TT = kLoadTile;
+  constexpr int CPR = D / EPC;                 // chunks per token row: 8, 16 or 32, divides 64
+  constexpr int CPT = TT / EPC;                // chunks per V^T row segment of the tile
+  constexpr int NI = TT * CPR / 256;           // token-row chunks per thread
+  constexpr int NO = D * CPT / 256;            // V^T chunks per thread
+  static_assert(NI * 256 == TT * CPR && NO * 256 == D * CPT && 64 % CPR == 0, "tile shape");
+  __shared__ U sv[COPY ? D : 1][TT + 4 / sizeof(T)];  // one dword of padding per row
+  const int tid = threadIdx.x;
+  const int n_tiles = Np / TT;
+  const int lh = blockIdx.x / n_tiles, t0 = (blockIdx.x - lh * n_tiles) * TT;
+  const int l = lh / Hkv, h = lh - l * Hkv;
+  T *krows = nk + ((size_t)lh * Np + t0) * D;  // the tile's native K rows are contiguous
+  const size_t src_row = (size_t)Hkv * D;      // caller layout: token stride
+  const size_t src0 = ((size_t)l * N * Hkv + h) * D;
+  constexpr int GI = NI < 4 ? NI : 4, GO = NO < 4 ? NO : 4;  // chunks in flight per thread per group
+  float kmax = 0.f, vmax = 0.f;
+#pragma unroll 1
+  for (int i0 = 0; i0 < NI; i0 += GI) {
+    u32x4_t xk[GI], xv[COPY ? GI : 1];
+    // every load of the group is issued before the first use
+#pragma unroll
+    for (int j = 0; j < GI; ++j) {
+      const int c = tid + 256 * (i0 + j), r = c / CPR, q = c % CPR, t = t0 + r;
+      xk[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (COPY) {
+        xv[j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (t < N) {
+          xk[j] = gld<u32x4_t>(src_k + src0 + (size_t)t * src_row + q * EPC);
+          xv[j] = gld<u32x4_t>(src_v + src0 + (size_t)t * src_row + q * EPC);
+        }
+      } else if (t < N) {
+        xk[j] = gld<u32x4_t>(krows + (size_t)r * D + q * EPC);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GI; ++j) {
+      const int c = tid + 256 * (i0 + j), r = c / CPR, q = c % CPR;
+      if (COPY) gst<u32x4_t>(krows + (size_t)r * D + q * EPC, xk[j]);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float x = chunk_elem<T>(xk[j], e);
+        ss = fmaf(x, x, ss);
+      }
+#pragma unroll
+      for (int o = CPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);  // the row's lanes are aligned
+      kmax = fmaxf(kmax, ss);
+      if (COPY) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const float x = chunk_elem<T>(xv[j], e);
+          vmax = fmaxf(vmax, fabsf(x));
+          sv[q * EPC + e][r] = (U)(sizeof(T) == 2 ? (__float_as_uint(x) >> 16) : __float_as_uint(x));
+        }
+      }
+    }
+  }
+  if (COPY) __syncthreads();
+#pragma unroll 1
+  for (int i0 = 0; i0 < NO; i0 += GO) {
+    u32x4_t y[GO];
+#pragma unroll
+    for (int j = 0; j < GO; ++j) {
+      const int c = tid + 256 * (i0 + j), dd = c / CPT, q = c % CPT, tb = t0 + q * EPC;
+      if (COPY) {
+        const uint32_t *p = (const uint32_t *)&sv[dd][0] + q * 4;
+        y[j] = u32x4_t{p[0], p[1], p[2], p[3]};
+      } else {
+        y[j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (tb < N) y[j] = gld<u32x4_t>(nvt + ((size_t)lh * D + dd) * Np + tb);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GO; ++j) {
+      const int c = tid + 256 * (i0 + j), dd = c / CPT, q = c % CPT, tb = t0 + q * EPC;
+      if (COPY) {
+        gst<u32x4_t>(nvt + ((size_t)lh * D + dd) * Np + tb, y[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (tb + e < N) vmax = fmaxf(vmax, fabsf(chunk_elem<T>(y[j], e)));
+      }
+    }
+  }
+  // one atomic pair per workgroup: atomics of many workgroups on the same few lines serialise
+  __shared__ float sred[2][4];
+  kmax = wave_max(kmax);
+  vmax = wave_max(vmax);
+  if ((tid & 63) == 0) {
+    sred[0][tid >> 6] = kmax;
+    sred[1][tid >> 6] = vmax;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    atomicMax(kn_bits + lh, __float_as_uint(fmaxf(fmaxf(sred[0][0], sred[0][1]), fmaxf(sred[0][2], sred[0][3]))));
+    atomicMax(vm_bits + lh, __float_as_uint(fmaxf(fmaxf(sred[1][0], sred[1][1]), fmaxf(sred[1][2], sred[1][3]))));
   }
 }
 
-// Largest L2 norm of the context keys of each (layer, kv head): one workgroup per pair,
-// one wave per key row at a time.
-template <typename T>
-__global__ __launch_bounds__(256) void k_key_norm_max(const T *__restrict__ k, const T *__restrict__ vt, int N,
-                                                      int Np, int d, float *__restrict__ out,
-                                                      float *__restrict__ out_vscale) {
-  __shared__ float smax[4], svmax[4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const T *base = k + (size_t)blockIdx.x * Np * d;
-  // largest |v| of the head's first N tokens (V^T rows of Np tokens)
-  float vmax = 0.f;
-  for (int e = w; e < d; e += 4)
-    for (int t = lane; t < N; t += 64) {
-      const T x = vt[((size_t)blockIdx.x * d + e) * Np + t];
-      vmax = fmaxf(vmax, fabsf(sizeof(T) == 2 ? __uint_as_float(((uint32_t)(uint16_t)x) << 16) : (float)x));
-    }
-  vmax = wave_max(vmax);
-  if (lane == 0) svmax[w] = vmax;
-  float best = 0.f;
-  for (int t = w; t < N; t += 4) {
-    float acc = 0.f;
-    for (int e = lane; e < d; e += 64) {
-      const float x = (float)(sizeof(T) == 2 ? __uint_as_float(((uint32_t)(uint16_t)base[(size_t)t * d + e]) << 16)
-                                             : (float)base[(size_t)t * d + e]);
-      acc = fmaf(x, x, acc);
-    }
-    best = fmaxf(best, wave_sum(acc));
+__global__ void k_load_init(uint32_t *kn_bits, uint32_t *vm_bits, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    kn_bits[i] = 0u;
+    vm_bits[i] = 0u;
   }
-  if (lane == 0) smax[w] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    out[blockIdx.x] = sqrtf(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
-    // value scale 2^e with max|v| < 2^e (frexp: max|v| = m 2^e, m in [0.5, 1)), kept a normal float
+}
+
+// In place: kn = sqrt(largest squared key norm); vs = 2^e with max|v| < 2^e (frexp: max|v| =
+// m 2^e, m in [0.5, 1)), kept a normal float.
+__global__ void k_load_finish(float *kn, float *vs, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    kn[i] = sqrtf(__uint_as_float(((const uint32_t *)kn)[i]));
     int ex = 0;
-    (void)frexpf(fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3])), &ex);
-    out_vscale[blockIdx.x] = ldexpf(1.f, min(max(ex, -126), 127));
+    (void)frexpf(__uint_as_float(((const uint32_t *)vs)[i]), &ex);
+    vs[i] = ldexpf(1.f, min(max(ex, -126), 127));
   }
 }
 
@@ -2416,32 +2495,34 @@ hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32
   return hipGetLastError();
 }
 
-hipError_t launch_relayout(const void *src_k, const void *src_v, void *dst_k, void *dst_vt, int L, int N, int Np,
-                           int Hkv, int d, int elem_bytes, hipStream_t st) {
-  const size_t total = (size_t)L * Hkv * Np * d;
-  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+hipError_t launch_load_ctx(const void *src_k, const void *src_v, void *nk, void *nvt, bool copy, int L, int Hkv,
+                           int N, int Np, int d, int elem_bytes, float *knmax, float *vscale, hipStream_t st) {
+  if (Np % kLoadTile != 0 || N < 1 || N > Np || (d != 64 && d != 128) || (elem_bytes != 2 && elem_bytes != 4))
+    return hipErrorInvalidValue;
+  const int n = L * Hkv;
+  uint32_t *kb = (uint32_t *)knmax, *vb = (uint32_t *)vscale;
+  hipLaunchKernelGGL(k_load_init, dim3((n + 255) / 256), dim3(256), 0, st, kb, vb, n);
+  const dim3 grid((unsigned)((size_t)n * (Np / kLoadTile)));
+  auto go = [&](auto tag, auto dtag) {
+    using T = decltype(tag);
+    constexpr int D = decltype(dtag)::value;
+    if (copy)
+      hipLaunchKernelGGL((k_load_ctx<T, D, true>), grid, dim3(256), 0, st, (const T *)src_k, (const T *)src_v,
+                         (T *)nk, (T *)nvt, N, Np, Hkv, kb, vb);
+    else
+      hipLaunchKernelGGL((k_load_ctx<T, D, false>), grid, dim3(256), 0, st, nullptr, nullptr, (T *)nk, (T *)nvt, N,
+                         Np, Hkv, kb, vb);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (elem_bytes == 2) {
-    hipLaunchKernelGGL(k_relayout_k<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t *)src_k,
-                       (uint16_t *)dst_k, L, N, Np, Hkv, d);
-    hipLaunchKernelGGL(k_relayout_vt<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t *)src_v,
-                       (uint16_t *)dst_vt, L, N, Np, Hkv, d);
+    if (d == 64) go(uint16_t{}, D64{});
+    else go(uint16_t{}, D128{});
   } else {
-    hipLaunchKernelGGL(k_relayout_k<float>, dim3(blocks), dim3(256), 0, st, (const float *)src_k, (float *)dst_k, L,
-                       N, Np, Hkv, d);
-    hipLaunchKernelGGL(k_relayout_vt<float>, dim3(blocks), dim3(256), 0, st, (const float *)src_v, (float *)dst_vt,
-                       L, N, Np, Hkv, d);
+    if (d == 64) go(float{}, D64{});
+    else go(float{}, D128{});
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_key_norm_max(const void *k_native, const void *vt_native, int L, int Hkv, int N, int Np, int d,
-                               int elem_bytes, float *out, float *out_vscale, hipStream_t st) {
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(k_key_norm_max<uint16_t>, dim3(L * Hkv), dim3(256), 0, st, (const uint16_t *)k_native,
-                       (const uint16_t *)vt_native, N, Np, d, out, out_vscale);
-  else
-    hipLaunchKernelGGL(k_key_norm_max<float>, dim3(L * Hkv), dim3(256), 0, st, (const float *)k_native,
-                       (const float *)vt_native, N, Np, d, out, out_vscale);
+  hipLaunchKernelGGL(k_load_finish, dim3((n + 255) / 256), dim3(256), 0, st, knmax, vscale, n);
   return hipGetLastError();
 }
 
