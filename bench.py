@@ -112,6 +112,80 @@ def scoring_leg(cfg, args):
             "candidates_per_s": round(R * n_cand * n_calls / dt, 1)}
 
 
+def workload_leg(name: str, reps: int = 3):
+    """Another workload of the decode step, its requests admitted as the workload prescribes
+    (all at once, or in admission waves interleaved with the earlier waves' steps).  The first
+    pass loads the contexts (loads timed apart with events); the timed passes replay the same
+    schedule with the contexts resident, a wave's admission being the reset of its requests
+    to the root beam.  Requests per second of decode wall time, every beam set fetched."""
+    import numpy as np
+    import torch
+
+    import synth
+    from tests.engine_inputs import make_engine, request_tensors
+    cfg = synth.get_config(name)
+    shapes = synth.request_shapes(cfg)
+    R, lv = cfg.n_requests, cfg.n_levels
+    waves = getattr(cfg, "waves", 0) or 1
+    per = R // waves
+    schedule = [list(range(w * per, (w + 1) * per)) for w in range(waves)]
+    eng = make_engine(cfg, max_requests=R)
+    load_ms = [0.0]
+    batch_sizes = []
+
+    def run(first):
+        level, active = {}, []
+        for k in range(waves + lv - 1):
+            if k < waves:
+                wave = schedule[k]
+                if first:
+                    tens = [request_tensors(cfg, r) for r in wave]
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for r, (kk, vv, qq) in zip(wave, tens):
+                        eng.load(r, kk, vv, qq, shapes[r][1])
+                    e1.record()
+                    torch.cuda.synchronize()
+                    load_ms[0] += e0.elapsed_time(e1)
+                    del tens
+                else:
+                    eng.reset_batch(wave)
+                for r in wave:
+                    level[r] = 0
+                active += wave
+            step = [r for r in active if level[r] < lv]
+            if first:
+                batch_sizes.append(len(step))
+            eng.step(step)
+            fin = []
+            for r in step:
+                level[r] += 1
+                if level[r] == lv:
+                    fin.append(r)
+            if fin:
+                eng.beams_batch(fin)
+
+    run(True)
+    torch.cuda.empty_cache()
+    run(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run(False)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    eng.close()
+    el = 2 if cfg.dtype == "bf16" else 4
+    load_bytes = sum(2 * cfg.n_layers * cfg.n_kv_heads * cfg.head_dim * el * (n + (n + 63) // 64 * 64)
+                     for n, _ in shapes)
+    log(f"{name}: {reps} schedules in {dt:.3f} s")
+    return {"workload": workload_text(cfg, shapes), "req_per_s": round(R * reps / dt, 1),
+            "ms_per_schedule": round(1e3 * dt / reps, 3), "batched_steps": batch_sizes,
+            "ctx_load_ms_per_request": round(load_ms[0] / R, 3),
+            "ctx_load_GBs": round(load_bytes / (load_ms[0] * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(cfg, n_beams: int):
     """The oracle, timed on the host cores on a bounded sample of the same workload."""
     import numpy as np
@@ -164,6 +238,8 @@ def main():
     ap.add_argument("--config", default=None, help="workload name (default: the ctx-5000 beam-256 headline)")
     ap.add_argument("--cpu-beams", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other two workloads (64 x ctx 2000 beam 30; ragged 128 in four waves)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -354,6 +430,8 @@ def main():
     eng.close()
     del eng
     out["scoring"] = scoring_leg(cfg, args)
+    if not args.no_workloads:
+        out["workloads"] = {w: workload_leg(w) for w in ("ctx2k_beam30_r64", "ragged_r128")}
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_beams} beams ...")
         cb = cpu_baseline(cfg, args.cpu_beams)

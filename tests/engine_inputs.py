@@ -24,9 +24,15 @@ def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm=
                           debug_attn=debug_attn)
 
 
-def request_tensors(cfg, r: int, device="cuda"):
-    """Context K, V [L][N][Hkv][d] and q_last [L][Hq][d] of request r as device tensors."""
+def request_tensors(cfg, r: int, device="cuda", host=False):
+    """Context K, V [L][N][Hkv][d] and q_last [L][Hq][d] of request r as device tensors.
+
+    bf16 workloads are generated on the device (synth.device: the host generators' values)
+    unless `host`; fp32 ones on the host."""
     from semantic_id_beam_amd import to_device
+    if cfg.dtype == "bf16" and not host and str(device).startswith("cuda"):
+        from synth import device as synth_device
+        return synth_device.request_tensors(cfg, r, device)
     ks, vs = [], []
     for l in range(cfg.n_layers):
         k, v = synth.ctx_kv_block(cfg, r, l)
