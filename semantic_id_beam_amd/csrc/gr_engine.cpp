@@ -36,6 +36,8 @@ constexpr int kRing = 16;  // per-step descriptor buffers in flight
 
 }  // namespace
 
+constexpr int kAuxStreams = 3;
+
 struct gr_engine {
   gr::Dims dm{};
   gr::SlotLayout sl{};
@@ -86,6 +88,11 @@ struct gr_engine {
   int64_t prof_n[5][gr::kMaxLevels + 1] = {};
   int64_t prof_d[5][gr::kMaxLevels + 1] = {};
 
+  // split-K steps with several variant groups: each group's chain of layer launches depends
+  // only on itself, so groups 1..3 (mod 4) run on their own streams, forked from and joined
+  // into the caller's stream (default priority, created at the first such step)
+  hipStream_t aux[kAuxStreams] = {};
+  hipEvent_t fork_ev = nullptr, join_ev[kAuxStreams] = {};
   std::vector<gr::StepReq *> pinned;
   std::vector<hipEvent_t> events;
   std::vector<bool> event_used;
@@ -427,6 +434,11 @@ gr_status gr_engine_destroy(gr_engine *e) {
       if (ev) (void)hipEventDestroy(ev);
     for (auto &ev : e->prof_ev)
       if (ev) (void)hipEventDestroy(ev);
+    for (int i = 0; i < kAuxStreams; ++i) {
+      if (e->aux[i]) (void)hipStreamDestroy(e->aux[i]);
+      if (e->join_ev[i]) (void)hipEventDestroy(e->join_ev[i]);
+    }
+    if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
     for (auto *p : e->pinned)
       if (p) (void)hipHostFree(p);
     if (e->out_host) (void)hipHostFree(e->out_host);
@@ -572,7 +584,12 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   bool any_hparts = false;
   std::vector<int> order((size_t)n);
   for (int i = 0; i < n; ++i) order[(size_t)i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kind[(size_t)a] < kind[(size_t)b]; });
+  // within a variant, longest context first: workgroups are dealt out in order as compute
+  // units free up, so the long ones start first and the short ones fill the end
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    if (kind[(size_t)a] != kind[(size_t)b]) return kind[(size_t)a] < kind[(size_t)b];
+    return rs[(size_t)a]->N > rs[(size_t)b]->N;
+  });
   struct Group { int kind, start, count, wgs, lgroups; };
   std::vector<Group> groups;
   for (int i = 0; i < n; ++i) {
@@ -591,9 +608,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     const int nw = G.kind & 0xFF;
     const int rows_wg = d.dtype == 1 ? gr::ctx_rows_per_wg(G.kind) : 32;
     // workgroups per launch: one per compute unit for the 8-wave kernel, two per unit for the
-    // one-wave streaming kernel (head_dim 128; its LDS ring allows two), else about two per
-    // compute unit of 4 waves
-    const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? 1024 : d.d == 128 ? 512 : 2048) : 256;
+    // one- and two-wave streaming kernels (head_dim 128; their LDS ring allows two), else
+    // about two per compute unit of 4 waves
+    const int want = d.dtype == 1 ? (nw == 8 ? 256 : nw == 4 ? 512 : nw == 2 ? (d.d == 128 ? 512 : 1024)
+                                                                           : d.d == 128 ? 512 : 2048)
+                                  : 256;
     int64_t units = 0;
     for (int i = G.start; i < G.start + G.count; ++i)
       units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)order[(size_t)i]]->n_bound * d.g, rows_wg);
@@ -700,7 +719,49 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
     }
   }
-  for (int l = 0; l < (first_fused || layered ? 0 : d.L); ++l) {
+  const bool multi = !first_fused && !layered && d.dtype == 1 && groups.size() > 1;
+  if (multi) {
+    if (!e->fork_ev) {
+      for (int i = 0; i < kAuxStreams; ++i) {
+        if ((r = check_dev(e, hipStreamCreateWithFlags(&e->aux[i], hipStreamNonBlocking), "stream create")) != GR_OK)
+          return r;
+        if ((r = check_dev(e, hipEventCreateWithFlags(&e->join_ev[i], hipEventDisableTiming), "event create")) != GR_OK)
+          return r;
+      }
+      if ((r = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
+        return r;
+    }
+    const int ns = (int)std::min<size_t>(kAuxStreams + 1, groups.size());
+    const auto pc = prof_pair(e, pon);
+    step_start = pc.first;
+    if (pc.first >= 0 && (r = check_dev(e, hipEventRecord(e->prof_ev[(size_t)pc.first], st), "profiling event")) != GR_OK)
+      return r;
+    if ((r = check_dev(e, hipEventRecord(e->fork_ev, st), "stream fork")) != GR_OK) return r;
+    for (int i = 0; i + 1 < ns; ++i)
+      if ((r = check_dev(e, hipStreamWaitEvent(e->aux[i], e->fork_ev, 0), "stream fork")) != GR_OK) return r;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group &G = groups[gi];
+      hipStream_t sg = gi % (kAuxStreams + 1) == 0 ? st : e->aux[gi % (kAuxStreams + 1) - 1];
+      for (int l = 0; l < d.L; ++l)
+        if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, sg),
+                           "context attention")) != GR_OK)
+          return r;
+    }
+    for (int i = 0; i + 1 < ns; ++i) {
+      if ((r = check_dev(e, hipEventRecord(e->join_ev[i], e->aux[i]), "stream join")) != GR_OK) return r;
+      if ((r = check_dev(e, hipStreamWaitEvent(st, e->join_ev[i], 0), "stream join")) != GR_OK) return r;
+    }
+    if (pc.second >= 0 && (r = check_dev(e, hipEventRecord(e->prof_ev[(size_t)pc.second], st), "profiling event")) != GR_OK)
+      return r;
+    prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, d.L * (int)groups.size());
+    // the last layer of every request (layer l is finished inside layer l+1's launch)
+    const auto pm = prof_pair(e, pon);
+    if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, d.L - 1, wg_merge, st, prof_ev(e, pm.first, pm.second)),
+                       "beam attention/merge")) != GR_OK)
+      return r;
+    prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
+  }
+  for (int l = 0; l < (first_fused || layered || multi ? 0 : d.L); ++l) {
     const auto pc = prof_pair(e, pon);
     if (l == 0) step_start = pc.first;
     for (size_t gi = 0; gi < groups.size(); ++gi) {

@@ -483,29 +483,44 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 // --------------------------------------------------------------------------------------
-// Shared-context attention for narrow steps (at most 32 query rows per kv head, head_dim
-// 128), which stream the context once and are bound by HBM.  One wave per workgroup, so no
-// barrier: the wave's own vmcnt says when a tile has landed.  32-token tiles go from global
-// memory straight into a ring of NST LDS stages (NST-1 tiles in flight per wave); P is split
-// into two bf16 terms.  V^T rows are 64 bytes here: 16-byte column c of row r sits at
+// Shared-context attention for narrow steps (at most 32 query rows per wave, head_dim 128),
+// which stream the context once and are bound by HBM.  32-token tiles go from global memory
+// straight into a ring of NST LDS stages (NST-1 tiles in flight); P is split into two bf16
+// terms.  NW = 1: one wave per workgroup, no barrier (the wave's own vmcnt says when a tile has
+// landed).  NW = 2: two waves (rows 0-31, 32-63 of the block) share the ring, each issues half
+// of every tile's copies, and one barrier per tile (behind the wave's own vmcnt wait) says that
+// the tile has landed and that every wave is done with the stage the next copy overwrites.
+// V^T rows are 64 bytes here: 16-byte column c of row r sits at
 // c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps 16 consecutive operand rows on 64 banks.
-// FUSED: every layer of a first-level step in one launch (blockIdx.y = layer).  At the first
-// level each layer's query is an input (q_last), so no layer waits for another; layer l's
+// FUSED (NW = 1): every layer of a first-level step in one launch (blockIdx.y = layer).  At the
+// first level each layer's query is an input (q_last), so no layer waits for another; layer l's
 // partials go to partial buffer 0 at row offset l*Hkv*splits*rows_b, and the finish of all
 // layers runs afterwards (k_finish_first_level).
-template <int NST, bool FUSED>
-__global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
-                                                        int layer_arg) {
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier8() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  else static_assert(N % 8 == 0 && N <= 24, "unsupported wait");
+}
+
+template <int NST, bool FUSED, int NW = 1>
+__global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                             int layer_arg) {
+  static_assert(NW == 1 || (NW == 2 && !FUSED), "one wave, or two waves per split-K workgroup");
   const int layer = FUSED ? (int)blockIdx.y : layer_arg;
   constexpr int D = 128, TT = 32, KB = D / 16, DB = D / 32;
   constexpr int P = NST - 1;
+  constexpr int NT = NW * 64;
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
-  constexpr int KI = KCH / 64, VI = VCH / 64, LPT = KI + VI;
-  static_assert(LPT == 16 && NST >= 2 && NST <= 5, "wait immediates assume 16 copies per tile");
+  constexpr int KI = KCH / NT, VI = VCH / NT, LPT = KI + VI;  // copies per tile and wave
+  static_assert(LPT * NW == 16 && NST >= 2 && NST <= 5, "wait immediates assume 16 copies per tile");
   __shared__ bf16x8_t sK[NST][KCH];
   __shared__ bf16x8_t sV[NST][VCH];
 
-  const int lane = threadIdx.x, hh = lane >> 5;
+  // the wave index is uniform over the wave (it enters the copies' LDS address, an SGPR)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), hh = lane >> 5;
   const int kx = lane & 15, vx = ((lane >> 1) ^ (lane >> 3)) & 3;
   const int ri = find_req<0>(reqs, n_reqs, blockIdx.x);
   const StepReq R = reqs[ri];
@@ -521,9 +536,11 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
   const int s = R.level;
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
   const int rows = n_live * dm.g;
-  const int row0 = rb * 32;
-  if (row0 >= rows) return;
-  const int q_row = row0 + (lane & 31);
+  const int row0 = rb * (NW * 32);
+  if (row0 >= rows) return;  // whole workgroup idle
+  const int wrow = row0 + w * 32;
+  const bool wave_active = wrow < rows;  // an idle wave still copies its share and meets the barriers
+  const int q_row = wrow + (lane & 31);
   const bool row_ok = q_row < rows;
 
   const int t0 = sp * R.tps;
@@ -531,15 +548,16 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
   const int ntiles = (t1 - t0 + TT - 1) / TT;
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
+  // copy i of wave w fills the 1 KB of the stage at (i * NW + w) * 1024: chunk p of the stage
   uint32_t koff[KI], voff[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
-    const int p = i * 64 + lane, rl = p >> 4, c = (p & 15) ^ (rl & 15);
+    const int p = (i * NW + w) * 64 + lane, rl = p >> 4, c = (p & 15) ^ (rl & 15);
     koff[i] = (uint32_t)(swap23(rl) * D + c * 8);
   }
 #pragma unroll
   for (int i = 0; i < VI; ++i) {
-    const int p = i * 64 + lane, row = p >> 2, c = (p & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    const int p = (i * NW + w) * 64 + lane, row = p >> 2, c = (p & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
     voff[i] = (uint32_t)row * (uint32_t)R.Np + (uint32_t)(c * 8);
   }
   const uint32_t kdst = lds_addr(&sK[0][0]), vdst = lds_addr(&sV[0][0]);
@@ -548,9 +566,9 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     const uint16_t *kb = gK + (size_t)tb * D;
     const uint16_t *vb = gV + tb;
 #pragma unroll
-    for (int i = 0; i < KI; ++i) dma16(kb + koff[i], kdst + st * (KCH * 16) + i * 1024);
+    for (int i = 0; i < KI; ++i) dma16(kb + koff[i], kdst + st * (KCH * 16) + (i * NW + w) * 1024);
 #pragma unroll
-    for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + i * 1024);
+    for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + (i * NW + w) * 1024);
   };
 #pragma unroll
   for (int k = 0; k < P; ++k)
@@ -594,9 +612,10 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
   }
   if (!FUSED && layer > 0) {
     int r0, r1;
-    finish_share(row0, min(rows, row0 + 32) - row0, R.splits, sp, 64 / (D / 8), r0, r1);
-    finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, lane, 64);
+    finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, NT / (D / 8), r0, r1);
+    finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
   }
+  // per wave: both branches meet the same barriers, once per tile
   const bool fixed_ref = bmax <= 60.f;
   if (!fixed_ref) M = kNegInf;
 
@@ -656,11 +675,20 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     for (int it = 0; it < ntiles; ++it) {
       // tile it has landed once at most the copies of the later tiles already issued remain
       const int ahead = min(P - 1, ntiles - 1 - it);
-      if (ahead >= 3) vm_wait<3 * LPT>();
-      else if (ahead == 2) vm_wait<2 * LPT>();
-      else if (ahead == 1) vm_wait<LPT>();
-      else vm_wait<0>();
+      if constexpr (NW == 1) {
+        if (ahead >= 3) vm_wait<3 * LPT>();
+        else if (ahead == 2) vm_wait<2 * LPT>();
+        else if (ahead == 1) vm_wait<LPT>();
+        else vm_wait<0>();
+      } else {
+        // every wave's copies of tile it have landed, and every wave is past tile it-1
+        if (ahead >= 3) vm_wait_barrier8<3 * LPT>();
+        else if (ahead == 2) vm_wait_barrier8<2 * LPT>();
+        else if (ahead == 1) vm_wait_barrier8<LPT>();
+        else vm_wait_barrier8<0>();
+      }
       if (it + P < ntiles) issue(it + P);  // into the stage of tile it-1, read by now
+      if (!wave_active) continue;
       if (it + 1 < ntiles || !partial)
         tile_step(it, std::false_type{}, F{});
       else
@@ -673,7 +701,7 @@ __global__ __launch_bounds__(64) void k_ctx_attn_stream(Dev dev, const StepReq *
     run(std::false_type{});
 
   const float ltot = l + __shfl_xor(l, 32);
-  if (row_ok) {
+  if (wave_active && row_ok) {
     const size_t lofs = FUSED ? (size_t)layer * dm.Hkv * R.splits * R.rows_b : 0;
     const int pb = FUSED ? 0 : layer & 1;
     const size_t prow = lofs + ((size_t)h * R.splits + sp) * R.rows_b + q_row;
@@ -2398,7 +2426,7 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
     else if (nw == 4)
       launch(k_ctx_attn_bf16_narrow<128, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 2)
-      launch(k_ctx_attn_bf16_narrow<128, 2, 32>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_stream<4, false, 2>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else
       launch(k_ctx_attn_stream<4, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
   } else {

@@ -33,6 +33,7 @@ class Config:
     zipf_a: float = 1.1
     waves: int = 1                   # admission waves (continuous batching)
     seed: int = 0
+    shapes: Tuple[Tuple[int, int], ...] = ()   # explicit (ctx_len, beam_width) per request
     notes: str = field(default="", compare=False)
 
     @property

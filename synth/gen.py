@@ -85,6 +85,9 @@ def _decompose(flat: np.ndarray, V: int, levels: int) -> np.ndarray:
 def request_shapes(cfg: Config):
     """[(ctx_len, beam_width)] per request."""
     R = cfg.n_requests
+    if cfg.shapes:
+        assert len(cfg.shapes) == R
+        return [(int(a), int(b)) for a, b in cfg.shapes]
     if isinstance(cfg.ctx_len, int) and isinstance(cfg.beam_width, int):
         return [(cfg.ctx_len, cfg.beam_width)] * R
     g = _philox(cfg, _T_SHAPES)

@@ -140,6 +140,52 @@ def test_layered_wide_steps_match_oracle():
     save_report(cfg, checked[0].report + checked[3].report, attn_err=max(errs))
 
 
+def test_mixed_variant_steps_match_oracle():
+    """Continuous batching over every context-attention variant at once: six requests whose
+    (context, beam width) pick the one-wave and two-wave streaming kernels, the four-wave
+    narrow kernel, and the wide kernel with two-term and single-term P; the second half is
+    admitted one step later, so the middle steps mix levels and variants (five groups, each
+    group's chain of layer launches on its own stream, the fifth sharing the first's).  Each
+    request is checked teacher-forced after each of its steps, with every layer's attention
+    output of every beam and the hidden vector."""
+    shapes = ((700, 8), (1500, 30), (900, 50), (2000, 100), (4100, 66), (600, 200))
+    cfg = synth.get_config("ragged_r128", n_requests=6, n_layers=3, shapes=shapes, n_items=60000, waves=2)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
+    tfs = {r: TeacherForced(cfg, r) for r in rids}
+    prev = {r: [()] for r in rids}
+    level = {r: 0 for r in rids}
+    tol = attn_tol(cfg)
+    errs, report = [], []
+    admitted = [0, 2, 4]
+    for k in range(cfg.n_levels + 1):
+        if k == 1:
+            admitted += [1, 3, 5]
+        step = [r for r in admitted if level[r] < cfg.n_levels]
+        eng.step(step)
+        for r in step:
+            after = gpu_beams(eng, r)
+            tf = tfs[r]
+            for l in range(cfg.n_layers):
+                got = eng.attn_out(r, l)
+                assert got.shape[0] == len(prev[r])
+                ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev[r]])
+                errs.append(rel_err_rows(got, ref))
+                assert errs[-1] <= tol, f"request {r} level {level[r]} layer {l}: attention rel err {errs[-1]}"
+            h, _ = eng.hidden(r)
+            href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev[r]])
+            assert rel_err_rows(h, href) <= tol * cfg.n_layers
+            tf.check_step(prev[r], after)
+            prev[r] = after[0]
+            level[r] += 1
+    for r in rids:
+        codes, _ = eng.beams(r)
+        assert [tuple(c) for c in codes.tolist()] == prev[r]
+        report += tfs[r].report
+    eng.close()
+    save_report(cfg, report, attn_err=max(errs))
+
+
 def test_max_beam_width_1024():
     """The largest beam width the engine takes: at the last step 1024 beams x 2 query heads =
     8 row blocks per kv head on the full-context wide path (2 requests x 2 layers), and the
