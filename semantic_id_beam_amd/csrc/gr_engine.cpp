@@ -569,18 +569,21 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   std::vector<int> kind((size_t)n);
   for (int i = 0; i < n; ++i)
     kind[(size_t)i] = d.dtype == 1 ? gr::ctx_kind_for(rs[(size_t)i]->n_bound * d.g, rs[(size_t)i]->N, d.d) : 0;
-  // A wide step (every request on the 8-wave variant) whose row blocks fill the chip over at
-  // most min(L, S_max) layers per launch runs without split partials: each workgroup covers the
+  // A step whose requests all run on the 8-wave wide kernel or the two-wave stream kernel, and
+  // whose row blocks fill the chip (three quarters of the resident workgroups) over at most
+  // min(L, S_max) layers per launch, runs without split partials: each workgroup covers the
   // whole context of one layer and finishes it, the layers of a launch go to separate
   // hidden-vector partials (in the room of the split partials), summed into h at the end.
   const int lg_max = std::min(d.L, d.S_max);
   bool layered = d.dtype == 1 && d.d == 128 && !first_fused;
-  int64_t wide_units = 0;
+  double fill = 0.0;  // resident-workgroup rounds the step's row blocks fill over lg_max layers
   for (int i = 0; i < n && layered; ++i) {
-    layered = (kind[(size_t)i] & 0xFF) == 8;
-    wide_units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)i]->n_bound * d.g, gr::ctx_rows_per_wg(kind[(size_t)i]));
+    const int nw = kind[(size_t)i] & 0xFF;
+    layered = nw == 8 || nw == 2;
+    const int64_t units = (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)i]->n_bound * d.g, gr::ctx_rows_per_wg(kind[(size_t)i]));
+    fill += (double)units * lg_max / (nw == 8 ? 256.0 : 512.0);
   }
-  layered = layered && wide_units * lg_max >= 192;
+  layered = layered && fill >= 0.75;
   bool any_hparts = false;
   std::vector<int> order((size_t)n);
   for (int i = 0; i < n; ++i) order[(size_t)i] = i;
@@ -696,20 +699,56 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       return r;
     prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
   }
+  // several variant groups: each group's launches depend only on that group's earlier ones,
+  // so group gi runs on stream gi mod 4 (the caller's stream or an engine-owned one), forked
+  // from and joined into the caller's stream; a span record then uses marker events on it
+  const int nstreams = d.dtype == 1 && !first_fused ? (int)std::min<size_t>(kAuxStreams + 1, groups.size()) : 1;
+  auto group_stream = [&](size_t gi) { return gi % (kAuxStreams + 1) == 0 ? st : e->aux[gi % (kAuxStreams + 1) - 1]; };
+  auto fork = [&]() -> gr_status {
+    gr_status q;
+    if (!e->fork_ev) {
+      for (int i = 0; i < kAuxStreams; ++i) {
+        if ((q = check_dev(e, hipStreamCreateWithFlags(&e->aux[i], hipStreamNonBlocking), "stream create")) != GR_OK)
+          return q;
+        if ((q = check_dev(e, hipEventCreateWithFlags(&e->join_ev[i], hipEventDisableTiming), "event create")) != GR_OK)
+          return q;
+      }
+      if ((q = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
+        return q;
+    }
+    if ((q = check_dev(e, hipEventRecord(e->fork_ev, st), "stream fork")) != GR_OK) return q;
+    for (int i = 0; i + 1 < nstreams; ++i)
+      if ((q = check_dev(e, hipStreamWaitEvent(e->aux[i], e->fork_ev, 0), "stream fork")) != GR_OK) return q;
+    return GR_OK;
+  };
+  auto join = [&]() -> gr_status {
+    gr_status q;
+    for (int i = 0; i + 1 < nstreams; ++i) {
+      if ((q = check_dev(e, hipEventRecord(e->join_ev[i], e->aux[i]), "stream join")) != GR_OK) return q;
+      if ((q = check_dev(e, hipStreamWaitEvent(st, e->join_ev[i], 0), "stream join")) != GR_OK) return q;
+    }
+    return GR_OK;
+  };
+  auto marker = [&](int ev) -> gr_status {
+    return ev >= 0 ? check_dev(e, hipEventRecord(e->prof_ev[(size_t)ev], st), "profiling event") : GR_OK;
+  };
   if (layered) {
     const auto pc = prof_pair(e, pon);
     step_start = pc.first;
+    if (nstreams > 1 && ((r = marker(pc.first)) != GR_OK || (r = fork()) != GR_OK)) return r;
     int disp = 0;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group &G = groups[gi];
       for (int l0 = 0; l0 < d.L; l0 += G.lgroups, ++disp) {
         const bool first = gi == 0 && l0 == 0, last = gi + 1 == groups.size() && l0 + G.lgroups >= d.L;
-        const gr::LaunchEv ev = prof_ev(e, first ? pc.first : -1, last ? pc.second : -1);
-        if ((r = check_dev(e, gr::launch_ctx_attn_layered(e->dev, dw + G.start, G.count, l0, G.wgs, G.kind, st, ev),
+        const gr::LaunchEv ev = nstreams > 1 ? gr::LaunchEv{} : prof_ev(e, first ? pc.first : -1, last ? pc.second : -1);
+        if ((r = check_dev(e, gr::launch_ctx_attn_layered(e->dev, dw + G.start, G.count, l0, G.wgs, G.kind,
+                                                          group_stream(gi), ev),
                            "context attention")) != GR_OK)
           return r;
       }
     }
+    if (nstreams > 1 && ((r = join()) != GR_OK || (r = marker(pc.second)) != GR_OK)) return r;
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, disp);
     if (any_hparts) {
       const auto pm = prof_pair(e, pon);
@@ -719,42 +758,22 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
     }
   }
-  const bool multi = !first_fused && !layered && d.dtype == 1 && groups.size() > 1;
+  // split-K steps with several groups: the same streams; layer l of a group is finished inside
+  // the group's launch of layer l+1, the last layer of every request after the join
+  const bool multi = !first_fused && !layered && nstreams > 1;
   if (multi) {
-    if (!e->fork_ev) {
-      for (int i = 0; i < kAuxStreams; ++i) {
-        if ((r = check_dev(e, hipStreamCreateWithFlags(&e->aux[i], hipStreamNonBlocking), "stream create")) != GR_OK)
-          return r;
-        if ((r = check_dev(e, hipEventCreateWithFlags(&e->join_ev[i], hipEventDisableTiming), "event create")) != GR_OK)
-          return r;
-      }
-      if ((r = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
-        return r;
-    }
-    const int ns = (int)std::min<size_t>(kAuxStreams + 1, groups.size());
     const auto pc = prof_pair(e, pon);
     step_start = pc.first;
-    if (pc.first >= 0 && (r = check_dev(e, hipEventRecord(e->prof_ev[(size_t)pc.first], st), "profiling event")) != GR_OK)
-      return r;
-    if ((r = check_dev(e, hipEventRecord(e->fork_ev, st), "stream fork")) != GR_OK) return r;
-    for (int i = 0; i + 1 < ns; ++i)
-      if ((r = check_dev(e, hipStreamWaitEvent(e->aux[i], e->fork_ev, 0), "stream fork")) != GR_OK) return r;
+    if ((r = marker(pc.first)) != GR_OK || (r = fork()) != GR_OK) return r;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group &G = groups[gi];
-      hipStream_t sg = gi % (kAuxStreams + 1) == 0 ? st : e->aux[gi % (kAuxStreams + 1) - 1];
       for (int l = 0; l < d.L; ++l)
-        if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, sg),
+        if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, group_stream(gi)),
                            "context attention")) != GR_OK)
           return r;
     }
-    for (int i = 0; i + 1 < ns; ++i) {
-      if ((r = check_dev(e, hipEventRecord(e->join_ev[i], e->aux[i]), "stream join")) != GR_OK) return r;
-      if ((r = check_dev(e, hipStreamWaitEvent(st, e->join_ev[i], 0), "stream join")) != GR_OK) return r;
-    }
-    if (pc.second >= 0 && (r = check_dev(e, hipEventRecord(e->prof_ev[(size_t)pc.second], st), "profiling event")) != GR_OK)
-      return r;
+    if ((r = join()) != GR_OK || (r = marker(pc.second)) != GR_OK) return r;
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, d.L * (int)groups.size());
-    // the last layer of every request (layer l is finished inside layer l+1's launch)
     const auto pm = prof_pair(e, pon);
     if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, d.L - 1, wg_merge, st, prof_ev(e, pm.first, pm.second)),
                        "beam attention/merge")) != GR_OK)

@@ -505,11 +505,24 @@ __device__ __forceinline__ void vm_wait_barrier8() {
   else static_assert(N % 8 == 0 && N <= 24, "unsupported wait");
 }
 
-template <int NST, bool FUSED, int NW = 1>
+template <int D>
+__device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                                int j, int gi, int code, int hh, float c2,
+                                                const bf16x8_t (&qf)[D / 16], float &M, float &l,
+                                                f32x16_t (&oacc)[D / 32], bool append);
+template <int D>
+__device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
+                                                 int hq, int hh, float ltot, const f32x16_t (&oacc)[D / 32],
+                                                 bool first, int lg);
+
+// LAYERED (NW = 2): as in the layered wide kernel, a launch covers layers layer_arg ..
+// layer_arg + lgroups - 1 and a workgroup owns its rows over the whole context of one of them;
+// the beam's own tokens are merged in the prologue and o/l goes to hidden-vector partial g.
+template <int NST, bool FUSED, int NW = 1, bool LAYERED = false>
 __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                              int layer_arg) {
-  static_assert(NW == 1 || (NW == 2 && !FUSED), "one wave, or two waves per split-K workgroup");
-  const int layer = FUSED ? (int)blockIdx.y : layer_arg;
+  static_assert(NW == 1 || (NW == 2 && !FUSED), "one wave, or two waves per split-K or layered workgroup");
+  static_assert(!(FUSED && LAYERED), "first-level fusion or layer slots, not both");
   constexpr int D = 128, TT = 32, KB = D / 16, DB = D / 32;
   constexpr int P = NST - 1;
   constexpr int NT = NW * 64;
@@ -529,8 +542,11 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
   const int rest = local >> 3;
   const int rb = rest % R.row_blocks;
   const int pidx = (rest / R.row_blocks) * 8 + (local & 7);
-  if (pidx >= dm.Hkv * R.splits) return;  // padding workgroup
-  const int h = pidx / R.splits, sp = pidx % R.splits;
+  const int nparts = LAYERED ? R.lgroups : R.splits;  // layer slots, or token ranges
+  if (pidx >= dm.Hkv * nparts) return;  // padding workgroup
+  const int h = pidx / nparts, sp = pidx % nparts;
+  const int layer = FUSED ? (int)blockIdx.y : layer_arg + (LAYERED ? sp : 0);
+  if (LAYERED && layer >= dm.L) return;  // past the last layer of the last launch
 
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
@@ -543,8 +559,8 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
   const int q_row = wrow + (lane & 31);
   const bool row_ok = q_row < rows;
 
-  const int t0 = sp * R.tps;
-  const int t1 = min(R.N, t0 + R.tps);
+  const int t0 = LAYERED ? 0 : sp * R.tps;
+  const int t1 = LAYERED ? R.N : min(R.N, t0 + R.tps);
   const int ntiles = (t1 - t0 + TT - 1) / TT;
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
@@ -575,17 +591,20 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
     if (k < ntiles) issue(k);
 
   bf16x8_t qf[KB];
+  int j_row = 0, gi_row = 0, hq_row = 0, code_row = 0;  // the lane's query row
   {
     const uint16_t *qsrc = nullptr;
     if (row_ok) {
-      const int j = q_row / dm.g, hq = h * dm.g + q_row % dm.g;
+      j_row = q_row / dm.g;
+      gi_row = q_row % dm.g;
+      hq_row = h * dm.g + gi_row;
       if (s == 0) {
-        qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq) * D;
+        qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq_row) * D;
       } else {
         const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
-        const int code = codes[j * dm.levels + (s - 1)];
+        code_row = codes[j_row * dm.levels + (s - 1)];
         qsrc = (const uint16_t *)dev.tok_q +
-               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
+               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code_row) * dm.Hq + hq_row) * D;
       }
     }
 #pragma unroll
@@ -610,14 +629,25 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
     M = B - 60.f;
     bmax = wave_max(B);
   }
-  if (!FUSED && layer > 0) {
+  // the beam's own tokens, against the fixed reference (redone below on the lazy path)
+  if (LAYERED && wave_active)
+    wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, true);
+  if (!FUSED && !LAYERED && layer > 0) {
     int r0, r1;
     finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, NT / (D / 8), r0, r1);
     finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
   }
   // per wave: both branches meet the same barriers, once per tile
   const bool fixed_ref = bmax <= 60.f;
-  if (!fixed_ref) M = kNegInf;
+  if (!fixed_ref) {
+    M = kNegInf;
+    if (LAYERED && wave_active) {
+      l = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, false);
+    }
+  }
 
   auto tile_step = [&](int it, auto mask_tag, auto fixed_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -701,7 +731,10 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
     run(std::false_type{});
 
   const float ltot = l + __shfl_xor(l, 32);
-  if (wave_active && row_ok) {
+  if (LAYERED) {
+    if (wave_active && row_ok)
+      wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, layer_arg == 0, sp);
+  } else if (wave_active && row_ok) {
     const size_t lofs = FUSED ? (size_t)layer * dm.Hkv * R.splits * R.rows_b : 0;
     const int pb = FUSED ? 0 : layer & 1;
     const size_t prow = lofs + ((size_t)h * R.splits + sp) * R.rows_b + q_row;
@@ -2443,7 +2476,12 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
 hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_reqs, int layer0, int total_wgs,
                                    int ctx_kind, hipStream_t st, LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
-  if (dev.dm.dtype != 1 || dev.dm.d != 128 || (ctx_kind & 0xFF) != 8) return hipErrorInvalidValue;
+  if (dev.dm.dtype != 1 || dev.dm.d != 128) return hipErrorInvalidValue;
+  if ((ctx_kind & 0xFF) == 2) {
+    launch(k_ctx_attn_stream<4, false, 2, true>, dim3(total_wgs), dim3(128), st, ev, dev, reqs, n_reqs, layer0);
+    return hipGetLastError();
+  }
+  if ((ctx_kind & 0xFF) != 8) return hipErrorInvalidValue;
   if (ctx_kind & kCtxHiLo)
     launch(k_ctx_attn_wide<4, true, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
   else

@@ -140,6 +140,47 @@ def test_layered_wide_steps_match_oracle():
     save_report(cfg, checked[0].report + checked[3].report, attn_err=max(errs))
 
 
+def test_layered_stream_steps_match_oracle():
+    """Steps without split partials on two kernels at once: twelve narrow requests (30 beams x
+    2 query heads = 60 rows per kv head) on the two-wave stream kernel, 8 kv heads x 4 layer
+    slots per launch, and two wide ones (150 beams) on the wide kernel, each group's launches
+    on its own stream.  Each workgroup covers the whole (ragged, 333-token) context of one
+    layer and merges the beam's own tokens (up to four, from BeamKV through the ancestry) in
+    its prologue; the second launch of each group holds layer 4 alone.  Three requests are
+    checked teacher-forced at every level with every layer's attention output and the hidden
+    vector; the dispatch count shows the path."""
+    from semantic_id_beam_amd import _lib as G
+    shapes = ((333, 30),) * 12 + ((333, 150),) * 2
+    cfg = synth.get_config("ctx2k_beam30_r64", n_requests=14, n_layers=5, shapes=shapes, n_items=50000)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
+    checked = {1: TeacherForced(cfg, 1), 10: TeacherForced(cfg, 10), 13: TeacherForced(cfg, 13)}
+    prev = {r: [()] for r in checked}
+    tol = attn_tol(cfg)
+    errs = []
+    G.gr_engine_set_profiling(eng.eng, True)
+    for s in range(cfg.n_levels):
+        eng.step(rids)
+        for r, tf in checked.items():
+            after = gpu_beams(eng, r)
+            for l in range(cfg.n_layers):
+                got = eng.attn_out(r, l)
+                assert got.shape[0] == len(prev[r])
+                ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev[r]])
+                errs.append(rel_err_rows(got, ref))
+                assert errs[-1] <= tol, f"request {r} step {s} layer {l}: attention rel err {errs[-1]}"
+            h, _ = eng.hidden(r)
+            href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev[r]])
+            assert rel_err_rows(h, href) <= tol * cfg.n_layers
+            tf.check_step(prev[r], after)
+            prev[r] = after[0]
+    G.gr_engine_set_profiling(eng.eng, False)
+    for s in range(1, cfg.n_levels):   # level 0: one first-level launch; then 2 + 2 launches of 4 layer slots
+        assert G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, s) == 4, s
+    eng.close()
+    save_report(cfg, checked[1].report + checked[10].report + checked[13].report, attn_err=max(errs))
+
+
 def test_mixed_variant_steps_match_oracle():
     """Continuous batching over every context-attention variant at once: six requests whose
     (context, beam width) pick the one-wave and two-wave streaming kernels, the four-wave
