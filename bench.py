@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # other code the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "23949d4a19ff85a6bbadf429391b9ce45bab203ac09b36a82b65dd7a3db088a7",
-    "k_ctx_attn_wide": {"read": 190791856, "written": 31466399},
-    "k_ctx_attn_stream": {"read": 166498766, "written": 278781},
+    "source_sha256": "cd4093c5560bb6ab51701641fdbf64d79543adbeebc5f32fac642ad51db5b314",
+    "k_ctx_attn_wide": {"read": 190796875, "written": 31303171},
+    "k_ctx_attn_stream": {"read": 166473138, "written": 278602},
 }
 
 
