@@ -505,9 +505,46 @@ __device__ __forceinline__ void vm_wait_barrier8() {
   else static_assert(N % 8 == 0 && N <= 24, "unsupported wait");
 }
 
+// The beam's own tokens in the full-context kernels.  A row of beam j at level s attends to
+// s tokens of its own besides the context: level t < s-1 from BeamKV slot anc[j][t], level s-1
+// (its query token) from the token tables at the code chosen at level s-1.
+// Index loads first (issued before the live-beam count is known; j is clamped so that rows
+// past the live beams load in bounds, and their values are never used): the code and the
+// first ancestor slot (older ones are loaded when their token is).  Unsigned, so that
+// widening them to 64 bits waits for nothing.
+struct BeamIdx {
+  uint32_t code, anc0;
+};
+template <bool ANC>
+__device__ __forceinline__ BeamIdx load_beam_idx(const Dev &dev, const uint8_t *slot, int s, int j) {
+  BeamIdx b{0u, 0u};
+  const int lvl = dev.dm.levels, jj = min(j, dev.dm.W_max - 1);
+  if (s > 0) b.code = ((const uint32_t *)(slot + dev.sl.codes[s & 1]))[jj * lvl + (s - 1)];
+  if constexpr (ANC) {
+    if (s > 1) b.anc0 = ((const uint32_t *)(slot + dev.sl.anc[s & 1]))[jj * lvl];
+  }
+  return b;
+}
+// Keys and values of two own tokens (t0, t0+1) of the lane's row, loaded before any arithmetic
+// so that a pair costs one memory round trip.  A lane without the token (row past the live
+// beams, or t >= s) reads the token table's first row instead: no branch around the loads,
+// and its values are never used.
+template <int D, int NTOK = 1>
+struct TailPair {
+  u32x4_t kr[NTOK][D / 16];
+  u32x2_t vr[NTOK][D / 8];
+};
+template <int D, int NTOK>
+__device__ __forceinline__ void tail_load_pair(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                               int j, const BeamIdx &bi, int hh, int t0, TailPair<D, NTOK> &tp);
+template <int D, int NTOK>
+__device__ __forceinline__ void tail_merge_pair(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                                int j, int gi, int hh, float c2, int t0, const TailPair<D, NTOK> &tp,
+                                                const bf16x8_t (&qf)[D / 16], float &M, float &l,
+                                                f32x16_t (&oacc)[D / 32], bool append, bool fresh = false);
 template <int D>
 __device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
-                                                int j, int gi, int code, int hh, float c2,
+                                                int j, int gi, const BeamIdx &bi, int hh, float c2, bool fresh,
                                                 const bf16x8_t (&qf)[D / 16], float &M, float &l,
                                                 f32x16_t (&oacc)[D / 32], bool append);
 template <int D>
@@ -550,13 +587,17 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
 
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
+  const int row0 = rb * (NW * 32);
+  const int wrow = row0 + w * 32;
+  const int q_row = wrow + (lane & 31);
+  // the lane's query row: beam j_row, query head hq_row; its index loads go out before the
+  // live-beam count is known
+  const int j_row = q_row / dm.g, gi_row = q_row % dm.g, hq_row = h * dm.g + gi_row;
+  const BeamIdx bi = load_beam_idx<LAYERED>(dev, slot, s, j_row);
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
   const int rows = n_live * dm.g;
-  const int row0 = rb * (NW * 32);
   if (row0 >= rows) return;  // whole workgroup idle
-  const int wrow = row0 + w * 32;
   const bool wave_active = wrow < rows;  // an idle wave still copies its share and meets the barriers
-  const int q_row = wrow + (lane & 31);
   const bool row_ok = q_row < rows;
 
   const int t0 = LAYERED ? 0 : sp * R.tps;
@@ -586,36 +627,28 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
 #pragma unroll
     for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + (i * NW + w) * 1024);
   };
-#pragma unroll
-  for (int k = 0; k < P; ++k)
-    if (k < ntiles) issue(k);
-
   bf16x8_t qf[KB];
-  int j_row = 0, gi_row = 0, hq_row = 0, code_row = 0;  // the lane's query row
+  const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
   {
-    const uint16_t *qsrc = nullptr;
-    if (row_ok) {
-      j_row = q_row / dm.g;
-      gi_row = q_row % dm.g;
-      hq_row = h * dm.g + gi_row;
-      if (s == 0) {
-        qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq_row) * D;
-      } else {
-        const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
-        code_row = codes[j_row * dm.levels + (s - 1)];
-        qsrc = (const uint16_t *)dev.tok_q +
-               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code_row) * dm.Hq + hq_row) * D;
-      }
-    }
+    // a row past the live beams reads the request's own q_last row and is zeroed
+    const uint16_t *qsrc = (const uint16_t *)(slot + dev.sl.q_last) + (size_t)layer * dm.Hq * D;
+    if (row_ok)
+      qsrc = s == 0 ? qsrc + (size_t)hq_row * D
+                    : (const uint16_t *)dev.tok_q +
+                          ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
+    u32x4_t qr[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
+    for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
+    // the tiles the ring holds ahead of the first one, in flight with the query
+#pragma unroll
+    for (int k = 0; k < P; ++k)
+      if (k < ntiles) issue(k);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? qr[kb] : u32x4_t{0, 0, 0, 0});
   }
   const float c2 = dm.scale_log2;
   float M, l = 0.f;
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  f32x16_t oacc[DB];  // zero, or set by the first own token
   float bmax;
   {
     float qn = 0.f;
@@ -624,14 +657,17 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
 #pragma unroll
       for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
     qn += __shfl_xor(qn, 32);
-    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
     const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
     M = B - 60.f;
     bmax = wave_max(B);
   }
   // the beam's own tokens, against the fixed reference (redone below on the lazy path)
-  if (LAYERED && wave_active)
-    wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, true);
+  if (LAYERED && wave_active && s > 0) {
+    wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, true, qf, M, l, oacc, true);
+  } else {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  }
   if (!FUSED && !LAYERED && layer > 0) {
     int r0, r1;
     finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, NT / (D / 8), r0, r1);
@@ -645,7 +681,7 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
       l = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
-      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, false);
+      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, false, qf, M, l, oacc, false);
     }
   }
 
@@ -749,84 +785,106 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
 // is feature db*32 + 8a + 4hh + c.  A row's two lanes compute the same scores, and only the
 // hh == 0 lane counts p in l (l of the two lanes is summed at the end).  Lanes of rows past the
 // live beams load nothing but take part in the shuffles.
-template <int D>
-__device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
-                                                int j, int gi, int code, int hh, float c2,
+template <int D, int NTOK>
+__device__ __forceinline__ void tail_load_pair(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                               int j, const BeamIdx &bi, int hh, int t0, TailPair<D, NTOK> &tp) {
+  constexpr int KB = D / 16;
+  const Dims &dm = dev.dm;
+  const int lvl = dm.levels;
+  const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
+  const size_t lvstride = (size_t)dm.W_max * wstride;
+  const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
+  const size_t tbase = (size_t)layer * (lvl - 1) * dm.V * dm.Hkv + kv;  // token-table row, level 0, code 0
+#pragma unroll
+  for (int e = 0; e < NTOK; ++e) {
+    const int t = t0 + e;
+    // element offset into tok_k/tok_v, or into BeamKV when `own`; selected without branches
+    const bool valid = row_ok && t < s, table = t == s - 1;
+    uint32_t a = bi.anc0;
+    if (t > 0 && t < s - 1)  // uniform: an older own token beyond the first
+      a = valid ? ((const uint32_t *)(slot + dev.sl.anc[s & 1]))[j * lvl + t] : 0u;
+    const size_t krow_tab = (tbase + ((size_t)t * dm.V + bi.code) * dm.Hkv) * D;
+    const size_t krow_own = lbase + (size_t)t * lvstride + (size_t)a * wstride;
+    const bool own = valid && !table;
+    const size_t krow = own ? krow_own : valid ? krow_tab : tbase * D;
+    const uint16_t *kp = (own ? (const uint16_t *)(slot + dev.sl.beamkv_k) : (const uint16_t *)dev.tok_k) + krow;
+    const uint16_t *vp = (own ? (const uint16_t *)(slot + dev.sl.beamkv_v) : (const uint16_t *)dev.tok_v) + krow;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) tp.kr[e][kb] = gld<u32x4_t>(kp + kb * 16 + 8 * hh);
+#pragma unroll
+    for (int q = 0; q < D / 8; ++q) tp.vr[e][q] = gld<u32x2_t>(vp + (q >> 2) * 32 + 8 * (q & 3) + 4 * hh);
+  }
+}
+
+// Online-softmax update of (M, l, oacc) with the pair's tokens, in level order, against the
+// running reference M; the row with gi == 0 appends its query token's key and value to BeamKV.
+// fresh: l and oacc are still zero (and M finite or -inf), so the first token sets them, which
+// is what the update gives (f <= 1), without reading zero accumulators.
+template <int D, int NTOK>
+__device__ __forceinline__ void tail_merge_pair(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                                int j, int gi, int hh, float c2, int t0, const TailPair<D, NTOK> &tp,
                                                 const bf16x8_t (&qf)[D / 16], float &M, float &l,
-                                                f32x16_t (&oacc)[D / 32], bool append) {
+                                                f32x16_t (&oacc)[D / 32], bool append, bool fresh) {
   constexpr int KB = D / 16, DB = D / 32;
   const Dims &dm = dev.dm;
   const int lvl = dm.levels;
   uint16_t *bk = (uint16_t *)(slot + dev.sl.beamkv_k);
   uint16_t *bv = (uint16_t *)(slot + dev.sl.beamkv_v);
-  const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
+  const size_t wstride = (size_t)dm.Hkv * D;
   const size_t lvstride = (size_t)dm.W_max * wstride;
   const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
-  const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
-  for (int t = 0; t < s; ++t) {
-    const uint16_t *kp = nullptr, *vp = nullptr;
-    if (row_ok) {
-      if (t == s - 1) {
-        const size_t trow = (((size_t)layer * (lvl - 1) + t) * dm.V + code) * dm.Hkv + kv;
-        kp = (const uint16_t *)dev.tok_k + trow * D;
-        vp = (const uint16_t *)dev.tok_v + trow * D;
-      } else {
-        const size_t off = lbase + (size_t)t * lvstride + (size_t)anc[j * lvl + t] * wstride;
-        kp = bk + off;
-        vp = bv + off;
-      }
-    }
+#pragma unroll
+  for (int e = 0; e < NTOK; ++e) {
+    const int t = t0 + e;
+    if (t >= s) break;
     const bool app = append && t == s - 1 && row_ok && gi == 0;
     const size_t dst = lbase + (size_t)t * lvstride + (size_t)j * wstride;
     float dot = 0.f;
-    {
-      u32x4_t kr[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[kb] = row_ok ? gld<u32x4_t>(kp + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dot = fmaf((float)qf[kb][2 * e], __uint_as_float(kr[kb][e] << 16), dot);
-          dot = fmaf((float)qf[kb][2 * e + 1], __uint_as_float(kr[kb][e] & 0xFFFF0000u), dot);
-        }
-        if (app) gst<u32x4_t>(bk + dst + kb * 16 + 8 * hh, kr[kb]);
+      for (int x = 0; x < 4; ++x) {
+        dot = fmaf((float)qf[kb][2 * x], __uint_as_float(tp.kr[e][kb][x] << 16), dot);
+        dot = fmaf((float)qf[kb][2 * x + 1], __uint_as_float(tp.kr[e][kb][x] & 0xFFFF0000u), dot);
       }
+      if (app) gst<u32x4_t>(bk + dst + kb * 16 + 8 * hh, tp.kr[e][kb]);
     }
     dot += __shfl_xor(dot, 32);
     const float u = dot * c2;
     const float Mn = fmaxf(M, u);
     const float f = fast_exp2(M - Mn);  // M = -inf before the first token of the lazy path: f = 0
     const float p = fast_exp2(u - Mn);
-    l = fmaf(l, f, hh == 0 ? p : 0.f);
-    // values in two halves of DB/2 feature blocks (fewer live registers)
+    const bool first = fresh && e == 0;
+    l = first ? (hh == 0 ? p : 0.f) : fmaf(l, f, hh == 0 ? p : 0.f);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x2_t vr[DB * 2];
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int q = 0; q < DB * 2; ++q) {
-        const int qq = half * DB * 2 + q;
-        vr[q] = row_ok ? gld<u32x2_t>(vp + (qq >> 2) * 32 + 8 * (qq & 3) + 4 * hh) : u32x2_t{0, 0};
-      }
-#pragma unroll
-      for (int dbl = 0; dbl < DB / 2; ++dbl) {
-        const int db = half * (DB / 2) + dbl;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t wv = vr[dbl * 4 + (i >> 2)][(i & 3) >> 1];
-          const float v = __uint_as_float((i & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
-          oacc[db][i] = fmaf(p, v, oacc[db][i] * f);
-        }
-      }
-      if (app) {
-#pragma unroll
-        for (int q = 0; q < DB * 2; ++q) {
-          const int qq = half * DB * 2 + q;
-          gst<u32x2_t>(bv + dst + (qq >> 2) * 32 + 8 * (qq & 3) + 4 * hh, vr[q]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t wv = tp.vr[e][db * 4 + (i >> 2)][(i & 3) >> 1];
+        const float v = __uint_as_float((i & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+        oacc[db][i] = first ? p * v : fmaf(p, v, oacc[db][i] * f);
       }
     }
+    if (app) {
+#pragma unroll
+      for (int q = 0; q < DB * 4; ++q) gst<u32x2_t>(bv + dst + (q >> 2) * 32 + 8 * (q & 3) + 4 * hh, tp.vr[e][q]);
+    }
     M = Mn;
+  }
+}
+
+// The own tokens in level order, each key and value in one round trip; the first of them
+// sets l and oacc when fresh (both still zero).
+template <int D>
+__device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, int layer, int kv, int s, bool row_ok,
+                                                int j, int gi, const BeamIdx &bi, int hh, float c2, bool fresh,
+                                                const bf16x8_t (&qf)[D / 16], float &M, float &l,
+                                                f32x16_t (&oacc)[D / 32], bool append) {
+  for (int t = 0; t < s; ++t) {
+    TailPair<D, 1> tp;
+    tail_load_pair<D, 1>(dev, slot, layer, kv, s, row_ok, j, bi, hh, t, tp);
+    tail_merge_pair<D, 1>(dev, slot, layer, kv, s, row_ok, j, gi, hh, c2, t, tp, qf, M, l, oacc, append,
+                          fresh && t == 0);
   }
 }
 
@@ -895,14 +953,18 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 
   uint8_t *slot = slot_base(dev, R.slot);
   const int s = R.level;
+  const int row0 = rb * (NW * 32);
+  const int wrow = row0 + w * 32;
+  const int q_row = wrow + (lane & 31);
+  // the row's beam j, query head hq and latest code (its query token at steps s >= 1), and
+  // the BeamKV slots of its older tokens: loaded before the live-beam count is known
+  const int j_row = q_row / dm.g, gi_row = q_row % dm.g, hq_row = h * dm.g + gi_row;
+  const BeamIdx bi = load_beam_idx<LAYERED>(dev, slot, s, j_row);
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
   const int rows = n_live * dm.g;
-  const int row0 = rb * (NW * 32);
   if (row0 >= rows) return;  // whole workgroup idle
 
-  const int wrow = row0 + w * 32;
   const bool wave_active = wrow < rows;
-  const int q_row = wrow + (lane & 31);
   const bool row_ok = q_row < rows;
 
   const int t0 = LAYERED ? 0 : sp * R.tps;
@@ -1149,27 +1211,25 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   {
     gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
     gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
-    // the tiles the ring holds ahead of the first one go out before anything else
-#pragma unroll
-    for (int k = 0; k < P; ++k)
-      if (k < ntiles) issue(k);
-    // the row's beam j, query head hq and latest code (its query token at steps s >= 1)
-    const int j_row = q_row / dm.g, gi_row = q_row % dm.g, hq_row = h * dm.g + gi_row;
-    const int code_row =
-        (row_ok && s > 0) ? ((const int *)(slot + dev.sl.codes[s & 1]))[j_row * dm.levels + (s - 1)] : 0;
+    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
     {
-      const uint16_t *qsrc = nullptr;
+      // a row past the live beams reads the request's own q_last row and is zeroed
+      const uint16_t *qsrc = (const uint16_t *)(slot + dev.sl.q_last) + (size_t)layer * dm.Hq * D;
       if (row_ok)
-        qsrc = s == 0 ? (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq_row) * D
+        qsrc = s == 0 ? qsrc + (size_t)hq_row * D
                       : (const uint16_t *)dev.tok_q +
-                            ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code_row) * dm.Hq + hq_row) * D;
+                            ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
+      u32x4_t qr[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? gld<u32x4_t>(qsrc + kb * 16 + 8 * hh) : u32x4_t{0, 0, 0, 0});
+      for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
+      // the tiles the ring holds ahead of the first one, in flight with the query
+#pragma unroll
+      for (int k = 0; k < P; ++k)
+        if (k < ntiles) issue(k);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? qr[kb] : u32x4_t{0, 0, 0, 0});
     }
-    l = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+    l = 0.f;  // oacc: zero, or set by the first own token
     // fixed score reference from the Cauchy-Schwarz bound, as in ctx_attn_body
     {
       float qn = 0.f;
@@ -1178,16 +1238,18 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 #pragma unroll
         for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
       qn += __shfl_xor(qn, 32);
-      const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
       const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
       M = B - 60.f;
       const float bw = wave_max(B);
       if (lane == 0) sBound[w] = bw;
     }
-    if (LAYERED) {
+    if (LAYERED && s > 0) {
       // the beam's own tokens, against the fixed reference (redone below if the workgroup
       // takes the lazy path)
-      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, true);
+      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, true, qf, M, l, oacc, true);
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
     }
     if (!LAYERED && layer > 0) {
       // finish the previous layer for this workgroup's share of the row block
@@ -1208,7 +1270,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
         l = 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
-        wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, code_row, hh, c2, qf, M, l, oacc, false);
+        wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, false, qf, M, l, oacc, false);
       }
     }
 
