@@ -243,6 +243,9 @@ void layout(gr_engine *e) {
   s.n_live = take(8);
   s.items = take(W * d.levels * 4);
   s.dbg_attn = d.debug_attn ? take((size_t)d.L * W * d.Hq * d.d * 4) : 0;
+  const bool full_ctx = d.dtype == 1 && d.d == 128;  // full-context (layered) steps possible
+  s.hl = full_ctx ? take((size_t)d.L * W * d.Hq * d.d * 2) : 0;
+  s.hl_scale = full_ctx ? take((size_t)d.L * W * d.Hq * 4) : 0;
   s.slot_bytes = align_up(o, A);
 
   size_t w = 0;
@@ -625,7 +628,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       // one frees, and the launches (and their ends) are half as many
       lgroups = (int)std::min<int64_t>(lg_max, std::max<int64_t>(1, (2 * want + units - 1) / std::max<int64_t>(units, 1)));
       G.lgroups = lgroups;
-      any_hparts = any_hparts || lgroups > 1;
+      any_hparts = true;  // every layer's output goes to its own partial
     }
     int wg_ctx = 0;
     for (int i = G.start; i < G.start + G.count; ++i) {

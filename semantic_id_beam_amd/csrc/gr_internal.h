@@ -47,6 +47,8 @@ struct SlotLayout {
   size_t n_live;              // i32[2]: n_live[s & 1] = beams of B_s
   size_t items;               // [W_max][levels] i32: the candidates of a scoring request
   size_t dbg_attn;            // [L][W_max][Hq][d] f32 (only with debug_attn)
+  size_t hl;                  // full-context steps: [L][W_max][Hq][d] fp16 o/l of each layer, times 2^-e of its row
+  size_t hl_scale;            // [L][W_max][Hq] f32: the row's 2^e (0 when bf16 head_dim-128 steps are impossible)
 };
 
 struct Dev {
@@ -70,7 +72,7 @@ struct StepReq {
   int n_bound;          // upper bound of n_s known on the host (device holds the exact n_s)
   int rows_b;           // n_bound * g: row stride of the split-K partials
   int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
-  int lgroups;          // full-context wide steps: layers per launch = hidden-vector partials (else 0)
+  int lgroups;          // full-context steps: layers per launch (else 0)
   int n_items;          // > 0: scoring request, its n_items candidates' codes are forced (no top-K)
   int row_blocks;       // context-attention row blocks per kv head
   int wg_ctx, wg_merge, wg_logits, wg_lsm;  // first workgroup of this request in each launch
@@ -99,9 +101,8 @@ hipError_t launch_ctx_attn_first_level(const Dev &dev, const StepReq *reqs, int 
                                        hipStream_t st, LaunchEv ev = {});
 // A wide step (8-wave variant, head_dim 128, bf16) without split partials: one launch covers
 // layers layer0 .. layer0 + lgroups - 1, workgroup (row block, kv head, g) owns layer layer0 + g
-// over the whole context and finishes it; layer layer0 + g goes into h when lgroups == 1, else
-// into partial g at part_o[0] + g*W_max*Hq*d floats (stored by the launch with layer0 == 0,
-// added to by the later ones), which launch_sum_hparts adds into h in order.
+// over the whole context and finishes it; its o/l goes to the layer's fp16 hidden partial (hl,
+// hl_scale), which launch_sum_hparts adds into h in layer order.
 hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_reqs, int layer0, int total_wgs,
                                    int ctx_kind, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_sum_hparts(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st, LaunchEv ev = {});

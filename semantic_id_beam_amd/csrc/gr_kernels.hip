@@ -17,8 +17,9 @@
 //                                 k_sum_layers form h
 //     k_ctx_attn_wide<.., true>   wide steps that fill the chip: a workgroup owns one
 //                                 layer's row block over the whole context, merges the
-//                                 beam's own tokens (BeamKV through BeamPath) and adds o/l
-//                                 to a hidden partial; k_sum_hparts forms h
+//                                 beam's own tokens (BeamKV through BeamPath) and stores
+//                                 o/l as the layer's fp16 hidden partial; k_sum_hparts
+//                                 adds the layers into h
 //     split-K per layer           k_ctx_attn_wide<.., false>, k_ctx_attn_bf16_narrow,
 //                                 k_ctx_attn_stream<4, false>: (m, l, o) partials per
 //                                 token range; the next layer's launch finishes the layer
@@ -550,11 +551,11 @@ __device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, i
 template <int D>
 __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
                                                  int hq, int hh, float ltot, const f32x16_t (&oacc)[D / 32],
-                                                 bool first, int lg);
+                                                 bool row_ok);
 
 // LAYERED (NW = 2): as in the layered wide kernel, a launch covers layers layer_arg ..
 // layer_arg + lgroups - 1 and a workgroup owns its rows over the whole context of one of them;
-// the beam's own tokens are merged in the prologue and o/l goes to hidden-vector partial g.
+// the beam's own tokens are merged in the prologue and o/l goes to the layer's hidden partial.
 template <int NST, bool FUSED, int NW = 1, bool LAYERED = false>
 __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                              int layer_arg) {
@@ -769,7 +770,7 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
   const float ltot = l + __shfl_xor(l, 32);
   if (LAYERED) {
     if (wave_active && row_ok)
-      wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, layer_arg == 0, sp);
+      wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, true);
   } else if (wave_active && row_ok) {
     const size_t lofs = FUSED ? (size_t)layer * dm.Hkv * R.splits * R.rows_b : 0;
     const int pb = FUSED ? 0 : layer & 1;
@@ -888,20 +889,32 @@ __device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, i
   }
 }
 
-// Layer output o/l of the lane's query row in the layered wide kernel: to the debug rows, and
-// added to the layer group's hidden-vector partial (stored for the group's first layer).
+// Layer output o/l of the lane's query row in the full-context kernels: to the debug rows, and
+// stored (never read back here) as the layer's fp16 partial of the hidden vector.  The row is
+// scaled by 2^-e, 2^e the power of two just above its largest |o/l| (kept beside it in fp32),
+// so the stored values lie in (-1, 1) for any value range and fp16 rounds them to 2^-11
+// relative; k_sum_hparts adds the layers' rows in layer order.  Lanes (row, hh) and
+// (row, hh ^ 1) hold the two halves of the row's features.
 template <int D>
 __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
                                                  int hq, int hh, float ltot, const f32x16_t (&oacc)[D / 32],
-                                                 bool first, int lg) {
+                                                 bool row_ok) {
   constexpr int DB = D / 32;
   const Dims &dm = dev.dm;
   const float inv = 1.f / ltot;
-  float *hp = (R.lgroups > 1 ? (float *)(slot + dev.sl.part_o[0]) + (size_t)lg * dm.W_max * dm.Hq * D
-                             : (float *)(slot + dev.sl.h)) +
-              ((size_t)j * dm.Hq + hq) * D;
-  float *dg = dm.debug_attn ? (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j) * dm.Hq + hq) * D
-                            : nullptr;
+  float mx = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(oacc[db][i] * inv));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (!row_ok) return;
+  int e = 0;
+  (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1); e = 0 for mx = 0
+  const size_t row = ((size_t)layer * dm.W_max + j) * dm.Hq + hq;
+  uint32_t *hp = (uint32_t *)(slot + dev.sl.hl) + row * (D / 2);
+  if (hh == 0) ((float *)(slot + dev.sl.hl_scale))[row] = ldexpf(1.f, e);
+  float *dg = dm.debug_attn ? (float *)(slot + dev.sl.dbg_attn) + row * D : nullptr;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -910,8 +923,9 @@ __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &
       f32x4_t o = f32x4_t{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv, oacc[db][4 * a + 2] * inv,
                           oacc[db][4 * a + 3] * inv};
       if (dg) gst<f32x4_t>(dg + f0, o);
-      if (!first) o += gld<f32x4_t>(hp + f0);
-      gst<f32x4_t>(hp + f0, o);
+      const f16x2_t h01 = {(_Float16)ldexpf(o[0], -e), (_Float16)ldexpf(o[1], -e)};
+      const f16x2_t h23 = {(_Float16)ldexpf(o[2], -e), (_Float16)ldexpf(o[3], -e)};
+      gst<u32x2_t>(hp + f0 / 2, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
     }
 }
 
@@ -920,10 +934,9 @@ __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &
 // from the token tables or the request, never from another layer's output).  It then finishes
 // its rows itself, with no split partials: the beam's own tokens are merged into (m, l, o) in
 // the prologue (the newest one appended to BeamKV), the context loop continues from that
-// state, and o/l is added to hidden-vector partial g (h itself when lgroups == 1; otherwise
-// k_sum_hparts adds the partials in order at the end).  Layer g of every launch goes to
-// partial g, so no two workgroups of a launch update one row.  Otherwise: one layer, one
-// token range, split partials out, and the previous layer finished in the prologue.
+// state, and o/l is stored as the layer's fp16 hidden partial (k_sum_hparts adds the layers
+// in order at the end).  Otherwise: one layer, one token range, split partials out, and the
+// previous layer finished in the prologue.
 template <int NST, bool HILO, bool LAYERED>
 __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                        int layer_arg) {
@@ -1286,7 +1299,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
         store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
       }
     } else {
-      if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, layer_arg == 0, sp);
+      if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, true);
     }
   }
 }
@@ -1792,22 +1805,35 @@ __global__ __launch_bounds__(256) void k_sum_layers(Dev dev, const StepReq *__re
   }
 }
 
-// h = sum of the layer groups' hidden-vector partials of the layered wide kernel, in group
-// order, over the live beams (requests with one group wrote h directly).
+// h of every live beam after a full-context step: the sum over layers, in layer order, of the
+// rows' stored fp16 o/l times their 2^e (an exact product).  One thread per 8 features of a
+// (beam, query head) row.
 __global__ __launch_bounds__(256) void k_sum_hparts(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
   const StepReq R = reqs[blockIdx.y];
-  if (R.lgroups <= 1) return;
+  if (R.lgroups < 1) return;
   const Dims &dm = dev.dm;
   uint8_t *slot = slot_base(dev, R.slot);
   const int n_live = ((const int *)(slot + dev.sl.n_live))[R.level & 1];
-  const size_t n4 = (size_t)n_live * dm.Hq * dm.d / 4;
-  const size_t gstride = (size_t)dm.W_max * dm.Hq * dm.d / 4;
-  const f32x4_t *hp = (const f32x4_t *)(slot + dev.sl.part_o[0]);
+  const int per_row = dm.d / 8;
+  const size_t n8 = (size_t)n_live * dm.Hq * per_row;
+  const size_t lrows = (size_t)dm.W_max * dm.Hq;  // rows per layer
+  const u32x4_t *hp = (const u32x4_t *)(slot + dev.sl.hl);
+  const float *sc = (const float *)(slot + dev.sl.hl_scale);
   f32x4_t *hb = (f32x4_t *)(slot + dev.sl.h);
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (size_t)gridDim.x * blockDim.x) {
-    f32x4_t acc = gld<f32x4_t>(hp + e);
-    for (int g = 1; g < R.lgroups; ++g) acc = acc + gld<f32x4_t>(hp + g * gstride + e);
-    gst<f32x4_t>(hb + e, acc);
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t row = e / per_row;
+    f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+#pragma unroll 4
+    for (int l = 0; l < dm.L; ++l) {
+      const u32x4_t v = gld<u32x4_t>(hp + (size_t)l * lrows * per_row + e);
+      const float w = sc[(size_t)l * lrows + row];
+      float f[8];
+      f16x8_to_float(v, f);
+      a0 += w * f32x4_t{f[0], f[1], f[2], f[3]};
+      a1 += w * f32x4_t{f[4], f[5], f[6], f[7]};
+    }
+    gst<f32x4_t>(hb + 2 * e, a0);
+    gst<f32x4_t>(hb + 2 * e + 1, a1);
   }
 }
 
@@ -2553,7 +2579,7 @@ hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_re
 
 hipError_t launch_sum_hparts(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st, LaunchEv ev) {
   if (n_reqs <= 0) return hipSuccess;
-  launch(k_sum_hparts, dim3(64, n_reqs), dim3(256), st, ev, dev, reqs, n_reqs);
+  launch(k_sum_hparts, dim3(128, n_reqs), dim3(256), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
