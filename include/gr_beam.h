@@ -111,6 +111,9 @@ typedef struct {
   int32_t max_splits;     /* split-K partial slots per (request, kv head) at full beam width
                              (narrower steps may use proportionally more); 0 = 4 */
   uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN */
+  int32_t max_layers_per_launch; /* full-context steps: at most this many layers per
+                             context-attention launch; 0 = automatic (about seven rounds of
+                             workgroups per launch, layers split evenly over the launches) */
 } gr_engine_opts;
 
 /* ---- engine lifetime ------------------------------------------------------ */

@@ -55,7 +55,7 @@ class gr_item_set(C.Structure):
 
 class gr_engine_opts(C.Structure):
     _fields_ = [("max_requests", C.c_int32), ("max_beam_width", C.c_int32), ("max_ctx_tokens", C.c_int64),
-                ("max_splits", C.c_int32), ("flags", C.c_uint32)]
+                ("max_splits", C.c_int32), ("flags", C.c_uint32), ("max_layers_per_launch", C.c_int32)]
 
 
 _lib = None

@@ -341,6 +341,7 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
     return fail(GR_E_INVALID_ARG, "max_beam_width must be in [1, 1024]");
   if (o->max_ctx_tokens < 0) return fail(GR_E_INVALID_ARG, "max_ctx_tokens < 0");
   if (o->max_splits < 0 || o->max_splits > 64) return fail(GR_E_INVALID_ARG, "max_splits must be in [0, 64]");
+  if (o->max_layers_per_launch < 0) return fail(GR_E_INVALID_ARG, "max_layers_per_launch must be >= 0");
 
   gr_engine *e = new gr_engine();
   e->model = *m;
@@ -573,10 +574,10 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   for (int i = 0; i < n; ++i)
     kind[(size_t)i] = d.dtype == 1 ? gr::ctx_kind_for(rs[(size_t)i]->n_bound * d.g, rs[(size_t)i]->N, d.d) : 0;
   // A step whose requests all run on the 8-wave wide kernel or the two-wave stream kernel, and
-  // whose row blocks fill the chip (three quarters of the resident workgroups) over at most
-  // min(L, S_max) layers per launch, runs without split partials: each workgroup covers the
-  // whole context of one layer and finishes it, the layers of a launch go to separate
-  // hidden-vector partials (in the room of the split partials), summed into h at the end.
+  // whose row blocks fill the chip (three quarters of the resident workgroups) over
+  // min(L, S_max) layers, runs without split partials: each workgroup covers the whole context
+  // of one layer and finishes it, every layer's output goes to its own fp16 hidden partial,
+  // and the partials are summed into h at the end.
   const int lg_max = std::min(d.L, d.S_max);
   bool layered = d.dtype == 1 && d.d == 128 && !first_fused;
   double fill = 0.0;  // resident-workgroup rounds the step's row blocks fill over lg_max layers
@@ -624,9 +625,15 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       units += (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)order[(size_t)i]]->n_bound * d.g, rows_wg);
     int lgroups = 0;
     if (layered) {
-      // two rounds of workgroups per launch: the second round starts on the units the first
-      // one frees, and the launches (and their ends) are half as many
-      lgroups = (int)std::min<int64_t>(lg_max, std::max<int64_t>(1, (2 * want + units - 1) / std::max<int64_t>(units, 1)));
+      // about seven rounds of workgroups per launch (later rounds start on the units the
+      // earlier ones free), the layers split as evenly as possible over the launches: few
+      // launch ends, and no short last launch.  Same-box, headline workload: 83.9 us per layer
+      // with two rounds, 82.5-83.2 with seven or fourteen; 8+8+8+4 layers measured 95.2.
+      int64_t target =
+          std::min<int64_t>(d.L, std::max<int64_t>(1, (7 * want + units - 1) / std::max<int64_t>(units, 1)));
+      if (e->opts.max_layers_per_launch > 0) target = std::min<int64_t>(target, e->opts.max_layers_per_launch);
+      const int64_t launches = (d.L + target - 1) / target;
+      lgroups = (int)((d.L + launches - 1) / launches);
       G.lgroups = lgroups;
       any_hparts = true;  // every layer's output goes to its own partial
     }

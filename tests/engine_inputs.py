@@ -9,7 +9,7 @@ import synth
 
 
 def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm="valid", max_ctx_tokens=None,
-                max_beam_width=None):
+                max_beam_width=None, max_layers_per_launch=0):
     import semantic_id_beam_amd as sib
     tq, tk, tv = synth.token_tables(cfg)
     shapes = synth.request_shapes(cfg)
@@ -21,7 +21,7 @@ def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm=
                           n_layers=cfg.n_layers, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                           head_dim=cfg.head_dim, dtype=cfg.dtype, norm=norm, max_requests=R,
                           max_beam_width=W, max_ctx_tokens=max_ctx_tokens, max_splits=max_splits,
-                          debug_attn=debug_attn)
+                          debug_attn=debug_attn, max_layers_per_launch=max_layers_per_launch)
 
 
 def request_tensors(cfg, r: int, device="cuda", host=False):

@@ -111,11 +111,13 @@ def test_layered_wide_steps_match_oracle():
     """Wide steps of several requests without split partials: 4 requests x 2 row blocks (200
     beams x 2 query heads per kv head; the second block partly empty) x 8 kv heads x 4 layers
     per launch fill the chip, each workgroup over the whole context of one layer, whose last tile
-    is ragged; the second launch holds only layers 4 and 5 (its other workgroups stand idle).
-    Two requests are checked teacher-forced, with every layer's attention output of every beam
-    (written by the kernel's own finish) and the hidden vector (the sum of the four partials)."""
+    is ragged; with at most four layers per launch, the second launch holds only layers 4 and 5
+    (its other workgroups stand idle).  Two requests are checked teacher-forced, with every
+    layer's attention output of every beam (written by the kernel's own finish) and the hidden
+    vector (the sum of the layers' fp16 partials).  The same step with every layer in one launch
+    (the automatic choice here) gives the same beams, scores and hidden vectors bit for bit."""
     cfg = synth.get_config("ctx1k_beam256", n_requests=4, n_layers=6, ctx_len=700, beam_width=200, n_items=50000)
-    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True, max_layers_per_launch=4)
     rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
     checked = {0: TeacherForced(cfg, 0), 3: TeacherForced(cfg, 3)}
     prev = {r: [()] for r in checked}
@@ -136,15 +138,28 @@ def test_layered_wide_steps_match_oracle():
             assert rel_err_rows(h, href) <= tol * cfg.n_layers
             tf.check_step(prev[r], after)
             prev[r] = after[0]
+    def final(e, r):
+        st = e.state(r)
+        return st["codes"].copy(), st["scores"].copy(), e.hidden(r)[0].copy()
+
+    split = {r: final(eng, r) for r in rids}
     eng.close()
+    one = make_engine(cfg, max_requests=cfg.n_requests)
+    for r in range(cfg.n_requests):
+        load_request(one, cfg, r)
+    for s in range(cfg.n_levels):
+        one.step(rids)
+    for r in rids:
+        assert all(np.array_equal(a, b) for a, b in zip(split[r], final(one, r))), r
+    one.close()
     save_report(cfg, checked[0].report + checked[3].report, attn_err=max(errs))
 
 
 def test_layered_stream_steps_match_oracle():
     """Steps without split partials on two kernels at once: twelve narrow requests (30 beams x
     2 query heads = 60 rows per kv head) on the two-wave stream kernel, 8 kv heads x 4 layer
-    slots per launch, and two wide ones (150 beams) on the wide kernel, each group's launches
-    on its own stream.  Each workgroup covers the whole (ragged, 333-token) context of one
+    slots per launch (at most four layers per launch), and two wide ones (150 beams) on the
+    wide kernel, each group's launches on its own stream.  Each workgroup covers the whole (ragged, 333-token) context of one
     layer and merges the beam's own tokens (up to four, from BeamKV through the ancestry) in
     its prologue; the second launch of each group holds layer 4 alone.  Three requests are
     checked teacher-forced at every level with every layer's attention output and the hidden
@@ -152,7 +167,7 @@ def test_layered_stream_steps_match_oracle():
     from semantic_id_beam_amd import _lib as G
     shapes = ((333, 30),) * 12 + ((333, 150),) * 2
     cfg = synth.get_config("ctx2k_beam30_r64", n_requests=14, n_layers=5, shapes=shapes, n_items=50000)
-    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True, max_layers_per_launch=4)
     rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
     checked = {1: TeacherForced(cfg, 1), 10: TeacherForced(cfg, 10), 13: TeacherForced(cfg, 13)}
     prev = {r: [()] for r in checked}
