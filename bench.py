@@ -30,15 +30,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # HBM bytes per layer of the context-attention kernels on this workload, from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
 # the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000), and
-# divided by the layers one dispatch covers (four for the wide kernel here, all 28 for the
+# divided by the layers one dispatch covers (14 for the wide kernel here, all 28 for the
 # first-level launch); profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel
 # code they were taken on (source_digest of gr_kernels.hip: comments excluded); with any
 # other code the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "cd4093c5560bb6ab51701641fdbf64d79543adbeebc5f32fac642ad51db5b314",
-    "k_ctx_attn_wide": {"read": 190796875, "written": 31303171},
-    "k_ctx_attn_stream": {"read": 166473138, "written": 278602},
+    "source_sha256": "90bfd0e04caa54ba0b831cae298cea72923ca568068aeba5af2f98bf0803d227",
+    "k_ctx_attn_wide": {"read": 181442610, "written": 21535100},
+    "k_ctx_attn_stream": {"read": 166635735, "written": 278607},
 }
 
 
@@ -365,7 +365,7 @@ def main():
     step_us = {f"level{s}": 1e3 * prof["step"][s][0] / max(prof["step"][s][1], 1) for s in range(lv)}
 
     # the unit is one layer of one step over every request: a dispatch covers one or more of them
-    # (two per dispatch for the wide kernel on the headline workload).  The kernel also finishes
+    # (14 per dispatch for the wide kernel on the headline workload).  The kernel also finishes
     # each layer (beam tokens, BeamKV append, h += o): that time is in the denominator, those
     # bytes are not in the algorithmic count.
     wide = cfg.dtype == "bf16" and cfg.head_dim == 128
