@@ -186,6 +186,74 @@ def workload_leg(name: str, reps: int = 3):
             "ctx_load_GBs": round(load_bytes / (load_ms[0] * 1e-3) / 1e9, 1)}
 
 
+def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 4000, 5000, 6000),
+                n_req: int = 1000, max_active: int = 64, seed: int = 0):
+    """Latency against offered load through the continuous-batching scheduler (gr_sched_*):
+    Poisson arrivals at each offered rate, n_req requests per rate, at most max_active decoding
+    at once, the way the paper-daily TensorRT-LLM summary reads its beam-search chart
+    ("Performance": where latency turns sharply upward; "Limitations": 1,000 requests per rate
+    point, a concurrency cap of 64).  Each request is admitted when it arrives, decoded in the
+    shared batched steps and timed until the host holds its beams.  Its context is already in
+    the native layout, as a prefill would leave it (GR_LOAD_ADOPT: the load only takes the
+    key-norm and value-scale bounds); the workload's 64 seeded contexts serve the requests
+    round-robin."""
+    import numpy as np
+    import torch
+
+    import semantic_id_beam_amd as sib
+    import synth
+    from tests.engine_inputs import make_engine, native_layout, request_tensors
+    cfg = synth.get_config(name)
+    shapes = synth.request_shapes(cfg)
+    tens = []
+    for r in range(cfg.n_requests):
+        k, v, q = request_tensors(cfg, r)
+        kn, vn, _ = native_layout(k, v)
+        del k, v
+        tens.append((kn, vn, q))
+    eng = make_engine(cfg, max_requests=max_active + 2, max_ctx_tokens=0)
+    torch.cuda.synchronize()
+    points, base = [], 0
+    for lam in rates:
+        sched = sib.Scheduler(eng, max_active)
+        arrival = np.cumsum(np.random.default_rng(seed + lam).exponential(1.0 / lam, n_req))
+        done = np.full(n_req, np.nan)
+        sizes = []
+        i = n_done = 0
+        t0 = time.perf_counter()
+        while n_done < n_req:
+            now = time.perf_counter() - t0
+            while i < n_req and arrival[i] <= now:
+                r = i % cfg.n_requests
+                sched.submit(base + i, *tens[r], shapes[r][1], ctx_len=shapes[r][0], adopt=True)
+                i += 1
+            c = sched.counts()
+            if c["queued"] + c["active"] == 0 and i - n_done - c["done"] == 0:
+                continue                                   # idle until the next arrival
+            sizes.append(c["active"] + min(c["queued"], max_active - c["active"]))
+            sched.advance()
+            for rid in sched.completed():
+                sched.result(int(rid))
+                done[int(rid) - base] = time.perf_counter() - t0
+                n_done += 1
+        sched.close()
+        lat = (done - arrival) * 1e3
+        span = float(np.max(done) - arrival[0])
+        points.append({"offered_rps": lam, "achieved_rps": round(n_req / span, 1),
+                       "p50_ms": round(float(np.percentile(lat, 50)), 2),
+                       "p90_ms": round(float(np.percentile(lat, 90)), 2),
+                       "p99_ms": round(float(np.percentile(lat, 99)), 2),
+                       "mean_batch": round(float(np.mean(sizes)), 1)})
+        log(f"serving {lam} req/s offered: {points[-1]}")
+        base += n_req
+    eng.close()
+    del tens
+    torch.cuda.empty_cache()
+    return {"workload": workload_text(cfg, shapes[:1] * 1).replace(f"{cfg.n_requests} requests", "requests"),
+            "requests_per_rate": n_req, "max_active": max_active, "contexts": cfg.n_requests,
+            "points": points}
+
+
 def cpu_baseline(cfg, n_beams: int):
     """The oracle, timed on the host cores on a bounded sample of the same workload."""
     import numpy as np
@@ -432,6 +500,7 @@ def main():
     out["scoring"] = scoring_leg(cfg, args)
     if not args.no_workloads:
         out["workloads"] = {w: workload_leg(w) for w in ("ctx2k_beam30_r64", "ragged_r128")}
+        out["serving"] = serving_leg()
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_beams} beams ...")
         cb = cpu_baseline(cfg, args.cpu_beams)

@@ -240,6 +240,64 @@ gr_status gr_request_reset_batch(gr_engine *eng, const int64_t *request_ids, int
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char *gr_last_error(void);
 
+/* ---- continuous batching: host scheduler ---------------------------------- */
+/* A scheduler drives one engine on one stream in the continuous-batching pattern of the
+ * zhiding.cn article's semantic-ID inference framework (section "语义ID生成式推荐专用推理
+ * 框架": requests join and leave the running batch between decode steps) and prepares the
+ * next step while the GPU runs the current one: the overlap scheduling of the paper-daily
+ * TensorRT-LLM summary, section "Moving all three into TensorRT-LLM" (the GPU keeps working
+ * while the CPU prepares the next step).  Requests wait in a FIFO queue until a slot frees;
+ * each gr_sched_advance then
+ *   1. loads queued requests (gr_ctx_kv_load) while fewer than max_active decode,
+ *   2. enqueues one gr_beam_step over every decoding request (each at its own level),
+ *   3. enqueues the result gather and a copy into pinned host memory for the requests that
+ *      this step finished, and releases their slots (later work on the stream reuses them
+ *      only after the gather),
+ *   4. waits for the copy enqueued by the PREVIOUS call (the GPU meanwhile runs this call's
+ *      step) and moves those results into the scheduler's result store.
+ * So the host stays one step ahead and never waits for the step it just enqueued.  A
+ * request's result is available from the call after the one whose step finished it (or
+ * after gr_sched_flush).  Not thread-safe; one scheduler per engine, and nothing else may
+ * load, step or release requests of that engine while the scheduler is in use. */
+typedef struct gr_sched gr_sched; /* opaque */
+
+/* max_active: requests decoding at once, 1..max_requests of the engine.  Allocates the
+ * scheduler's two pinned result buffers (outside any hot path).  stream: hipStream_t every
+ * call of the scheduler enqueues on. */
+gr_status gr_sched_create(gr_engine *eng, int32_t max_active, void *stream, gr_sched **out);
+
+/* Waits for the stream, frees the pinned buffers.  Requests still queued or decoding are
+ * released from the engine. */
+gr_status gr_sched_destroy(gr_sched *sched);
+
+/* Queues a request: the arguments of gr_ctx_kv_load (k, v, q_last device or host memory as
+ * there; with device sources they must stay valid until the request's load has run on the
+ * stream, i.e. until a later gr_sched_advance returns).  GR_E_INVALID_ARG for an id that is
+ * queued, decoding or holds an unfetched result; the load's own checks run at admission. */
+gr_status gr_sched_submit(gr_sched *sched, int64_t request_id, int32_t ctx_len, int32_t beam_width,
+                          const void *k, const void *v, const void *q_last, uint32_t load_flags);
+
+/* One scheduling round (above).  *n_completed = results that became available in this call
+ * (those of the previous call's step).  With nothing queued or decoding it only collects. */
+gr_status gr_sched_advance(gr_sched *sched, int32_t *n_completed);
+
+/* Collects every result still in flight (synchronises the stream); *n_completed as above. */
+gr_status gr_sched_flush(gr_sched *sched, int32_t *n_completed);
+
+/* Ids of available results, oldest first, up to `capacity` (host [capacity]);
+ * *n = how many are available in all. */
+gr_status gr_sched_completed(gr_sched *sched, int32_t capacity, int64_t *request_ids, int32_t *n);
+
+/* Takes a request's result out of the store: as gr_beams_get (codes host [capacity][n_levels],
+ * scores host [capacity], sorted by score).  GR_E_NOT_FOUND if the id holds no result (yet);
+ * GR_E_INVALID_ARG (result kept) if capacity < its beam count. */
+gr_status gr_sched_result(gr_sched *sched, int64_t request_id, int32_t capacity, int32_t *codes,
+                          float *scores, int32_t *n_beams);
+
+/* Requests queued, decoding, and holding unfetched results; batched steps enqueued so far. */
+gr_status gr_sched_counts(const gr_sched *sched, int32_t *queued, int32_t *active, int32_t *done,
+                          int64_t *steps);
+
 /* ---- item-constrained top-K, stand-alone ---------------------------------- */
 
 /* Selects the k best of n_rows*V candidate scores, cand device [n_rows][V]

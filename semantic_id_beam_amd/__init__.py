@@ -8,4 +8,4 @@ not built.
 """
 from . import _lib  # noqa: F401
 from ._lib import GrError, lib  # noqa: F401
-from .engine import BeamEngine, to_device  # noqa: F401
+from .engine import BeamEngine, Scheduler, to_device  # noqa: F401

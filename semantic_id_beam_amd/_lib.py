@@ -32,6 +32,8 @@ EXPORTS = [
     "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
     "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
+    "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
+    "gr_sched_completed", "gr_sched_result", "gr_sched_counts",
 ]
 GR_PROF_CTX_ATTN, GR_PROF_BEAM_MERGE, GR_PROF_LOGITS, GR_PROF_TOPK, GR_PROF_STEP = range(5)
 
@@ -105,6 +107,14 @@ def lib() -> C.CDLL:
         "gr_score_items": (i32, [vp, i64, vp, i32, vp, vp]),
         "gr_score_items_batch": (i32, [vp, vp, i32, vp, i32, vp, vp]),
         "gr_engine_profile_reset": (i32, [vp]),
+        "gr_sched_create": (i32, [vp, i32, vp, P(vp)]),
+        "gr_sched_destroy": (i32, [vp]),
+        "gr_sched_submit": (i32, [vp, i64, i32, i32, vp, vp, vp, u32]),
+        "gr_sched_advance": (i32, [vp, P(i32)]),
+        "gr_sched_flush": (i32, [vp, P(i32)]),
+        "gr_sched_completed": (i32, [vp, i32, vp, P(i32)]),
+        "gr_sched_result": (i32, [vp, i64, i32, vp, vp, P(i32)]),
+        "gr_sched_counts": (i32, [vp, P(i32), P(i32), P(i32), P(i64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -284,3 +294,51 @@ def gr_engine_profile_dispatches(eng: int, kind: int, level: int = -1) -> int:
 
 def gr_engine_profile_reset(eng: int):
     _check(lib().gr_engine_profile_reset(eng))
+
+
+# ---------------------------------------------------------------- continuous-batching scheduler
+def gr_sched_create(eng: int, max_active: int, stream: int = 0) -> int:
+    out = C.c_void_p()
+    _check(lib().gr_sched_create(eng, max_active, stream, C.byref(out)))
+    return out.value
+
+
+def gr_sched_destroy(sched: int):
+    _check(lib().gr_sched_destroy(sched))
+
+
+def gr_sched_submit(sched: int, rid: int, ctx_len: int, beam_width: int, k, v, q_last, flags: int = 0):
+    _check(lib().gr_sched_submit(sched, rid, ctx_len, beam_width, _ptr(k), _ptr(v), _ptr(q_last), flags))
+
+
+def gr_sched_advance(sched: int) -> int:
+    n = C.c_int32()
+    _check(lib().gr_sched_advance(sched, C.byref(n)))
+    return n.value
+
+
+def gr_sched_flush(sched: int) -> int:
+    n = C.c_int32()
+    _check(lib().gr_sched_flush(sched, C.byref(n)))
+    return n.value
+
+
+def gr_sched_completed(sched: int, capacity: int) -> np.ndarray:
+    ids = np.zeros(max(capacity, 1), dtype=np.int64)
+    n = C.c_int32()
+    _check(lib().gr_sched_completed(sched, capacity, _host(ids), C.byref(n)))
+    return ids[: min(n.value, capacity)]
+
+
+def gr_sched_result(sched: int, rid: int, capacity: int, n_levels: int):
+    codes = np.zeros((max(capacity, 1), n_levels), dtype=np.int32)
+    scores = np.zeros(max(capacity, 1), dtype=np.float32)
+    n = C.c_int32()
+    _check(lib().gr_sched_result(sched, rid, capacity, _host(codes), _host(scores), C.byref(n)))
+    return codes[: n.value], scores[: n.value]
+
+
+def gr_sched_counts(sched: int):
+    q, a, d, st = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64()
+    _check(lib().gr_sched_counts(sched, C.byref(q), C.byref(a), C.byref(d), C.byref(st)))
+    return {"queued": q.value, "active": a.value, "done": d.value, "steps": st.value}

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <deque>
 #include <map>
 #include <string>
 #include <unordered_map>
@@ -1107,6 +1108,243 @@ gr_status gr_topk_select(const float *cand, int32_t n_rows, int32_t V, int32_t k
   if (k < 1 || k > gr::kMaxBeam) return fail(GR_E_INVALID_ARG, "k must be in [1, 1024]");
   hipError_t err = gr::launch_topk_select(cand, n_rows, V, k, out_flat, out_score, n_out, (hipStream_t)stream);
   if (err != hipSuccess) return fail(GR_E_DEVICE, std::string("top-k select: ") + hipGetErrorString(err));
+  return GR_OK;
+}
+
+
+// ---- continuous batching: host scheduler ---------------------------------------------------
+// FIFO admission into free slots, one batched step per call over every decoding request, and a
+// one-step lag on results: the call that enqueues step t waits only for the result copy of step
+// t-1, which the GPU finished before starting step t.  Result buffers alternate between two
+// pinned areas; the device staging area of the engine is reused in stream order.
+}  // extern "C"
+
+struct gr_sched {
+  gr_engine *e = nullptr;
+  hipStream_t st = nullptr;
+  int max_active = 1;
+  struct Pending {
+    int64_t rid;
+    int32_t N, W;
+    const void *k, *v, *q;
+    uint32_t flags;
+  };
+  std::deque<Pending> queue;
+  std::vector<int64_t> active;        // loaded and decoding, in admission order
+  std::unordered_set<int64_t> known;  // ids queued, decoding or holding a result
+  struct Batch {
+    std::vector<int64_t> ids;
+    uint8_t *host = nullptr;  // pinned, out_bytes per request
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  Batch batch[2];
+  int cur = 0;  // the batch this call fills; the other one belongs to the previous call
+  struct Result {
+    int32_t n = 0;
+    std::vector<int32_t> codes;
+    std::vector<float> scores;
+  };
+  std::unordered_map<int64_t, Result> done;
+  std::deque<int64_t> done_order;  // may hold ids already taken (skipped)
+  int64_t steps = 0;
+};
+
+namespace {
+
+// Results of a finished batch into the store (waits for its copy).
+gr_status sched_collect(gr_sched *s, gr_sched::Batch &B, int32_t *n_completed) {
+  if (!B.pending) return GR_OK;
+  gr_engine *e = s->e;
+  gr_status r;
+  if ((r = check_dev(e, hipEventSynchronize(B.ev), "result copy")) != GR_OK) return r;
+  const int lv = e->dm.levels;
+  const size_t W = (size_t)e->dm.W_max;
+  for (size_t i = 0; i < B.ids.size(); ++i) {
+    const uint8_t *src = B.host + e->out_bytes * i;
+    gr_sched::Result R;
+    std::memcpy(&R.n, src, 4);
+    R.codes.resize((size_t)R.n * lv);
+    R.scores.resize((size_t)R.n);
+    if (R.n > 0) {
+      std::memcpy(R.codes.data(), src + 16, (size_t)R.n * lv * 4);
+      std::memcpy(R.scores.data(), src + 16 + W * lv * 4, (size_t)R.n * 4);
+    }
+    s->done[B.ids[i]] = std::move(R);
+    s->done_order.push_back(B.ids[i]);
+  }
+  if (n_completed) *n_completed += (int32_t)B.ids.size();
+  B.ids.clear();
+  B.pending = false;
+  return GR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gr_status gr_sched_create(gr_engine *e, int32_t max_active, void *stream, gr_sched **out) {
+  g_err.clear();
+  if (!e || !out) return fail(GR_E_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (max_active < 1 || max_active > e->opts.max_requests)
+    return fail(GR_E_INVALID_ARG, "max_active must be in [1, max_requests]");
+  auto *s = new gr_sched();
+  s->e = e;
+  s->st = (hipStream_t)stream;
+  s->max_active = max_active;
+  gr_status r = GR_OK;
+  for (auto &B : s->batch) {
+    if (r == GR_OK)
+      r = check_dev(e, hipHostMalloc((void **)&B.host, e->out_bytes * (size_t)e->opts.max_requests,
+                                     hipHostMallocDefault), "pinned scheduler results");
+    if (r == GR_OK) r = check_dev(e, hipEventCreateWithFlags(&B.ev, hipEventDisableTiming), "event");
+  }
+  if (r != GR_OK) {
+    (void)gr_sched_destroy(s);
+    return r;
+  }
+  *out = s;
+  return GR_OK;
+}
+
+gr_status gr_sched_destroy(gr_sched *s) {
+  if (!s) return GR_OK;
+  if (s->e && s->e->bound) (void)hipStreamSynchronize(s->st);
+  for (int64_t rid : s->active) (void)gr_request_release(s->e, rid);
+  for (auto &B : s->batch) {
+    if (B.ev) (void)hipEventDestroy(B.ev);
+    if (B.host) (void)hipHostFree(B.host);
+  }
+  delete s;
+  return GR_OK;
+}
+
+gr_status gr_sched_submit(gr_sched *s, int64_t rid, int32_t N, int32_t W, const void *k, const void *v,
+                          const void *q_last, uint32_t flags) {
+  g_err.clear();
+  if (!s) return fail(GR_E_INVALID_ARG, "null scheduler");
+  if (!k || !v || !q_last) return fail(GR_E_INVALID_ARG, "null k, v or q_last");
+  if (s->known.count(rid) || s->e->reqs.count(rid))
+    return fail(GR_E_INVALID_ARG, "request id queued, decoding or holding a result");
+  s->queue.push_back({rid, N, W, k, v, q_last, flags});
+  s->known.insert(rid);
+  return GR_OK;
+}
+
+gr_status gr_sched_advance(gr_sched *s, int32_t *n_completed) {
+  g_err.clear();
+  if (!s || !n_completed) return fail(GR_E_INVALID_ARG, "null argument");
+  *n_completed = 0;
+  gr_engine *e = s->e;
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  gr_status r;
+  // 1. admissions, in arrival order, while a slot, pool room and the concurrency cap allow
+  while (!s->queue.empty() && (int)s->active.size() < s->max_active && !e->free_slots.empty()) {
+    const gr_sched::Pending P = s->queue.front();
+    r = gr_ctx_kv_load(e, P.rid, P.N, P.W, P.k, P.v, P.q, P.flags, s->st);
+    if (r == GR_E_OUT_OF_MEMORY && !s->active.empty()) break;  // the pool frees as requests finish
+    if (r != GR_OK) {  // dropped with the load's error
+      s->queue.pop_front();
+      s->known.erase(P.rid);
+      return r;
+    }
+    s->queue.pop_front();
+    s->active.push_back(P.rid);
+  }
+  gr_sched::Batch &B = s->batch[s->cur];
+  if ((r = sched_collect(s, B, n_completed)) != GR_OK) return r;  // never pending here; kept safe
+  // 2. one batched step over every decoding request, each at its own level
+  if (!s->active.empty()) {
+    if ((r = gr_beam_step(e, s->active.data(), (int32_t)s->active.size(), s->st)) != GR_OK) return r;
+    ++s->steps;
+    // 3. the requests this step finished: gather, copy to pinned memory, release the slots
+    const int lv = e->dm.levels;
+    std::vector<int64_t> still;
+    std::vector<int32_t> slots;
+    for (int64_t rid : s->active) {
+      const gr_engine::Req &R = e->reqs.at(rid);
+      if (R.level == lv) {
+        B.ids.push_back(rid);
+        slots.push_back(R.slot);
+      } else {
+        still.push_back(rid);
+      }
+    }
+    s->active.swap(still);
+    if (!B.ids.empty()) {
+      uint8_t *dst = e->ws + e->off_out;
+      const int n = (int)B.ids.size();
+      for (int i0 = 0; i0 < n; i0 += gr::kGatherMax) {
+        const int m = std::min(gr::kGatherMax, n - i0);
+        if ((r = check_dev(e, gr::launch_gather_results(e->dev, slots.data() + i0, m, lv & 1,
+                                                        dst + e->out_bytes * i0, e->out_bytes, s->st),
+                           "result gather")) != GR_OK)
+          return r;
+      }
+      if ((r = check_dev(e, hipMemcpyAsync(B.host, dst, e->out_bytes * (size_t)n, hipMemcpyDeviceToHost, s->st),
+                         "result copy")) != GR_OK)
+        return r;
+      if ((r = check_dev(e, hipEventRecord(B.ev, s->st), "event")) != GR_OK) return r;
+      B.pending = true;
+      for (int64_t rid : B.ids)
+        if ((r = gr_request_release(e, rid)) != GR_OK) return r;
+    }
+  }
+  // 4. the previous call's results: its copy ran before this call's step
+  if ((r = sched_collect(s, s->batch[s->cur ^ 1], n_completed)) != GR_OK) return r;
+  s->cur ^= 1;
+  return GR_OK;
+}
+
+gr_status gr_sched_flush(gr_sched *s, int32_t *n_completed) {
+  g_err.clear();
+  if (!s || !n_completed) return fail(GR_E_INVALID_ARG, "null argument");
+  *n_completed = 0;
+  gr_status r;
+  // the older batch first
+  if ((r = sched_collect(s, s->batch[s->cur], n_completed)) != GR_OK) return r;
+  return sched_collect(s, s->batch[s->cur ^ 1], n_completed);
+}
+
+gr_status gr_sched_completed(gr_sched *s, int32_t cap, int64_t *ids, int32_t *n) {
+  g_err.clear();
+  if (!s || !n || cap < 0 || (cap > 0 && !ids)) return fail(GR_E_INVALID_ARG, "null argument");
+  int32_t k = 0;
+  for (int64_t rid : s->done_order) {
+    if (k >= cap) break;
+    if (s->done.count(rid)) ids[k++] = rid;
+  }
+  *n = (int32_t)s->done.size();
+  return GR_OK;
+}
+
+gr_status gr_sched_result(gr_sched *s, int64_t rid, int32_t cap, int32_t *codes, float *scores, int32_t *n_beams) {
+  g_err.clear();
+  if (!s || !n_beams || cap < 0 || (cap > 0 && (!codes || !scores))) return fail(GR_E_INVALID_ARG, "null output");
+  auto it = s->done.find(rid);
+  if (it == s->done.end()) return fail(GR_E_NOT_FOUND, "no result for this request id (yet)");
+  const gr_sched::Result &R = it->second;
+  *n_beams = R.n;
+  if (R.n > cap) return fail(GR_E_INVALID_ARG, "capacity smaller than the number of beams");
+  if (R.n > 0) {
+    std::memcpy(codes, R.codes.data(), R.codes.size() * 4);
+    std::memcpy(scores, R.scores.data(), R.scores.size() * 4);
+  }
+  s->done.erase(it);
+  s->known.erase(rid);
+  while (!s->done_order.empty() && !s->done.count(s->done_order.front())) s->done_order.pop_front();
+  return GR_OK;
+}
+
+gr_status gr_sched_counts(const gr_sched *s, int32_t *queued, int32_t *active, int32_t *done, int64_t *steps) {
+  g_err.clear();
+  if (!s) return fail(GR_E_INVALID_ARG, "null scheduler");
+  if (queued) *queued = (int32_t)s->queue.size();
+  if (active) *active = (int32_t)s->active.size();
+  if (done) *done = (int32_t)s->done.size();
+  if (steps) *steps = s->steps;
   return GR_OK;
 }
 

@@ -121,3 +121,50 @@ class BeamEngine:
             self.close()
         except Exception:
             pass
+
+
+class Scheduler:
+    """Continuous batching over one BeamEngine (gr_sched_*): FIFO admission up to max_active
+    decoding requests, one batched step per advance(), results one step later."""
+
+    def __init__(self, engine: BeamEngine, max_active: int):
+        self.engine = engine
+        self.sched = G.gr_sched_create(engine.eng, max_active, engine.stream)
+        self._keep = {}
+
+    def submit(self, rid: int, k, v, q_last, beam_width: int, ctx_len: int | None = None, adopt: bool = False):
+        """Queue a request (k, v, q_last as for BeamEngine.load; kept alive until admitted)."""
+        n = ctx_len if ctx_len is not None else k.shape[1]
+        G.gr_sched_submit(self.sched, rid, n, beam_width, k, v, q_last, G.GR_LOAD_ADOPT if adopt else 0)
+        self._keep[rid] = (k, v, q_last)
+
+    def advance(self) -> int:
+        """One scheduling round; returns the number of results that became available."""
+        return G.gr_sched_advance(self.sched)
+
+    def flush(self) -> int:
+        return G.gr_sched_flush(self.sched)
+
+    def completed(self, capacity: int = 1 << 16):
+        return G.gr_sched_completed(self.sched, capacity)
+
+    def result(self, rid: int):
+        """(codes [n][n_levels], scores [n]) of a finished request, taken out of the store."""
+        out = G.gr_sched_result(self.sched, rid, self.engine.max_beam_width, self.engine.n_levels)
+        self._keep.pop(rid, None)
+        return out
+
+    def counts(self):
+        return G.gr_sched_counts(self.sched)
+
+    def close(self):
+        if getattr(self, "sched", None):
+            G.gr_sched_destroy(self.sched)
+            self.sched = None
+        self._keep.clear()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

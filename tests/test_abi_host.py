@@ -34,8 +34,8 @@ def _desc(L=1, Hq=4, Hkv=2, d=64, lv=3, V=16, dtype=G.GR_DTYPE_F32, norm=G.GR_NO
     return G.gr_model_desc(L, Hq, Hkv, d, lv, V, dtype, norm, FAKE, FAKE, FAKE, FAKE)
 
 
-def _opts(R=1, W=4, ctx=64, S=0, flags=0):
-    return G.gr_engine_opts(R, W, ctx, S, flags)
+def _opts(R=1, W=4, ctx=64, S=0, flags=0, lpl=0):
+    return G.gr_engine_opts(R, W, ctx, S, flags, lpl)
 
 
 def _items(V=16, lv=3, n=200, seed=0):
@@ -87,7 +87,7 @@ def test_create_rejects_bad_model(bad):
     assert G.gr_last_error()
 
 
-@pytest.mark.parametrize("bad", [dict(R=0), dict(W=0), dict(W=2000), dict(ctx=-1), dict(S=100)])
+@pytest.mark.parametrize("bad", [dict(R=0), dict(W=0), dict(W=2000), dict(ctx=-1), dict(S=100), dict(lpl=-1)])
 def test_create_rejects_bad_opts(bad):
     with pytest.raises(G.GrError):
         G.gr_engine_create(_desc(), _items(), _opts(**bad))
@@ -148,3 +148,24 @@ def test_null_engine_is_rejected():
     assert L.gr_score_items_batch(None, None, 1, None, 1, None, None) == G.GR_E_INVALID_ARG
     assert L.gr_engine_destroy(None) == G.GR_OK
     assert L.gr_engine_workspace_bytes(None) == 0
+
+
+def test_scheduler_host_checks():
+    """The scheduler needs a bound engine and a concurrency cap within max_requests; null
+    handles and outputs are rejected without touching a GPU."""
+    L = sib.lib()
+    eng = G.gr_engine_create(_desc(), _items(), _opts(R=4))
+    with pytest.raises(G.GrError) as ei:
+        G.gr_sched_create(eng, 2)
+    assert ei.value.status == G.GR_E_BAD_STATE
+    G.gr_engine_destroy(eng)
+    out = C.c_void_p()
+    assert L.gr_sched_create(None, 1, None, C.byref(out)) == G.GR_E_INVALID_ARG
+    n = C.c_int32()
+    assert L.gr_sched_advance(None, C.byref(n)) == G.GR_E_INVALID_ARG
+    assert L.gr_sched_flush(None, C.byref(n)) == G.GR_E_INVALID_ARG
+    assert L.gr_sched_submit(None, 1, 10, 4, FAKE, FAKE, FAKE, 0) == G.GR_E_INVALID_ARG
+    assert L.gr_sched_result(None, 1, 4, None, None, C.byref(n)) == G.GR_E_INVALID_ARG
+    assert L.gr_sched_completed(None, 0, None, C.byref(n)) == G.GR_E_INVALID_ARG
+    assert L.gr_sched_counts(None, None, None, None, None) == G.GR_E_INVALID_ARG
+    assert L.gr_sched_destroy(None) == G.GR_OK
