@@ -574,21 +574,24 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   std::vector<int> kind((size_t)n);
   for (int i = 0; i < n; ++i)
     kind[(size_t)i] = d.dtype == 1 ? gr::ctx_kind_for(rs[(size_t)i]->n_bound * d.g, rs[(size_t)i]->N, d.d) : 0;
-  // A step whose requests all run on the 8-wave wide kernel or the two-wave stream kernel, and
-  // whose row blocks fill the chip (three quarters of the resident workgroups) over
-  // min(L, S_max) layers, runs without split partials: each workgroup covers the whole context
+  // A step whose row blocks fill the chip (three quarters of the resident workgroups) over
+  // min(L, S_max) layers runs without split partials: each workgroup covers the whole context
   // of one layer and finishes it, every layer's output goes to its own fp16 hidden partial,
-  // and the partials are summed into h at the end.
+  // and the partials are summed into h at the end.  Wide requests run on the 8-wave kernel;
+  // every narrower one (level-0 beams included) on the two-wave stream kernel in 64-row
+  // blocks, so a step that mixes levels (continuous batching) stays on this path.
   const int lg_max = std::min(d.L, d.S_max);
+  auto full_ctx_kind = [](int k) { return (k & 0xFF) == 8 ? k : (2 | gr::kCtxHiLo); };
   bool layered = d.dtype == 1 && d.d == 128 && !first_fused;
   double fill = 0.0;  // resident-workgroup rounds the step's row blocks fill over lg_max layers
   for (int i = 0; i < n && layered; ++i) {
-    const int nw = kind[(size_t)i] & 0xFF;
-    layered = nw == 8 || nw == 2;
-    const int64_t units = (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)i]->n_bound * d.g, gr::ctx_rows_per_wg(kind[(size_t)i]));
-    fill += (double)units * lg_max / (nw == 8 ? 256.0 : 512.0);
+    const int k = full_ctx_kind(kind[(size_t)i]);
+    const int64_t units = (int64_t)d.Hkv * ceil_div((int64_t)rs[(size_t)i]->n_bound * d.g, gr::ctx_rows_per_wg(k));
+    fill += (double)units * lg_max / ((k & 0xFF) == 8 ? 256.0 : 512.0);
   }
   layered = layered && fill >= 0.75;
+  if (layered)
+    for (int i = 0; i < n; ++i) kind[(size_t)i] = full_ctx_kind(kind[(size_t)i]);
   bool any_hparts = false;
   std::vector<int> order((size_t)n);
   for (int i = 0; i < n; ++i) order[(size_t)i] = i;

@@ -242,6 +242,64 @@ def test_mixed_variant_steps_match_oracle():
     save_report(cfg, report, attn_err=max(errs))
 
 
+def test_full_context_steps_mixing_levels_match_oracle():
+    """Continuous batching on the full-context path: three admission waves of eight requests,
+    one wave per step, so the middle steps hold requests at levels 0, 1 and 2 together (and
+    the first step, all at level 0, runs the fused first level).  Beams of up to 128 rows
+    (level-0 beams, 5, 30 and 50 beams) run on the two-wave stream kernel in 64-row blocks, the
+    200-beam ones on the wide kernel, each workgroup over a whole (ragged, down to one-token)
+    context; the dispatch count shows one launch per kernel and step instead of one per layer.
+    Four requests (a narrow, a level-0-at-the-time, a two-block and a wide one) are checked
+    teacher-forced after each of their steps, with every layer's attention output of every
+    beam and the hidden vector."""
+    from semantic_id_beam_amd import _lib as G
+    wave = ((300, 30), (129, 5), (700, 50), (64, 30), (1, 30), (257, 5), (450, 200), (333, 30))
+    shapes = wave + tuple((n + 37, w) for n, w in wave) + tuple((max(1, n - 20), w) for n, w in wave)
+    cfg = synth.get_config("ragged_r128", n_requests=len(shapes), n_layers=4, shapes=shapes, n_items=60000,
+                           waves=3)
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True)
+    rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
+    checked = (1, 10, 18, 22)
+    tfs = {r: TeacherForced(cfg, r) for r in checked}
+    prev = {r: [()] for r in rids}
+    level = {r: 0 for r in rids}
+    tol = attn_tol(cfg)
+    errs, report, admitted, mixed = [], [], [], 0
+    G.gr_engine_set_profiling(eng.eng, True)
+    for k in range(3 + cfg.n_levels - 1):
+        if k < 3:
+            admitted += list(range(8 * k, 8 * k + 8))
+        step = [r for r in admitted if level[r] < cfg.n_levels]
+        mixed += len({level[r] for r in step}) > 1
+        eng.step(step)
+        for r in step:
+            if r in tfs:
+                after = gpu_beams(eng, r)
+                tf = tfs[r]
+                for l in range(cfg.n_layers):
+                    got = eng.attn_out(r, l)
+                    assert got.shape[0] == len(prev[r])
+                    ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev[r]])
+                    errs.append(rel_err_rows(got, ref))
+                    assert errs[-1] <= tol, f"request {r} level {level[r]} layer {l}: attention rel err {errs[-1]}"
+                h, _ = eng.hidden(r)
+                href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev[r]])
+                assert rel_err_rows(h, href) <= tol * cfg.n_layers
+                tf.check_step(prev[r], after)
+                prev[r] = after[0]
+            level[r] += 1
+    G.gr_engine_set_profiling(eng.eng, False)
+    assert mixed == 3
+    # mixed-level steps are profiled under level n_levels: two kernels, all four layers each
+    assert G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, cfg.n_levels) == 2 * mixed
+    for r in checked:
+        codes, _ = eng.beams(r)
+        assert [tuple(c) for c in codes.tolist()] == prev[r]
+        report += tfs[r].report
+    eng.close()
+    save_report(cfg, report, attn_err=max(errs))
+
+
 def test_max_beam_width_1024():
     """The largest beam width the engine takes: at the last step 1024 beams x 2 query heads =
     8 row blocks per kv head on the full-context wide path (2 requests x 2 layers), and the
