@@ -2008,28 +2008,24 @@ struct SelectSmem {
 __device__ void select_stream(const float *__restrict__ cand, int n_total, int k, SelectSmem &sm);
 
 // Sorts a[0..n) descending (n <= 1024); every thread of the workgroup calls it.
+static_assert(kMaxBeam <= kTopkThreads && kTieCap <= kTopkThreads, "one key per thread");
 __device__ void block_sort_desc(uint64_t *a, int n) {
+  // n <= kTopkThreads distinct keys (each holds its candidate's flat index): a key's place in
+  // descending order is the number of keys above it, so the places form a permutation.  Every
+  // thread reads the same a[j] at once (an LDS broadcast); two barriers in all.
   const int tid = threadIdx.x;
-  int P = 1;
-  while (P < n) P <<= 1;
-  for (int i = n + tid; i < P; i += kTopkThreads) a[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P; i += kTopkThreads) {
-        const int pj = i ^ stride;
-        if (pj > i) {
-          const uint64_t x = a[i], y = a[pj];
-          const bool desc = (i & size) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            a[i] = y;
-            a[pj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  uint64_t key = 0;
+  int rank = 0;
+  if (tid < n) {
+    key = a[tid];
+    int j = 0;
+    for (; j + 4 <= n; j += 4)
+      rank += (int)(a[j] > key) + (int)(a[j + 1] > key) + (int)(a[j + 2] > key) + (int)(a[j + 3] > key);
+    for (; j < n; ++j) rank += (int)(a[j] > key);
   }
+  __syncthreads();
+  if (tid < n) a[rank] = key;
+  __syncthreads();
 }
 
 __device__ void scan_cands(const float *__restrict__ cand, int total, SelectSmem &sm) {
