@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # other code the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "90bfd0e04caa54ba0b831cae298cea72923ca568068aeba5af2f98bf0803d227",
-    "k_ctx_attn_wide": {"read": 181442610, "written": 21535100},
-    "k_ctx_attn_stream": {"read": 166635735, "written": 278607},
+    "source_sha256": "f1d6bdc3eb22b130a9eb529ffe81b5297ef79a44b9b0e97c9e9e01fecf4fc08a",
+    "k_ctx_attn_wide": {"read": 181454927, "written": 21535287},
+    "k_ctx_attn_stream": {"read": 166624539, "written": 278601},
 }
 
 
