@@ -200,6 +200,27 @@ gr_status gr_beams_get(gr_engine *eng, int64_t request_id, int32_t capacity, int
 gr_status gr_beams_get_batch(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, int32_t capacity,
                              int32_t *codes, float *scores, int32_t *n_beams, void *stream);
 
+/* gr_beams_get_batch without the synchronisation, for a host that keeps enqueueing while
+ * results travel (the overlap scheduling of [TRT] section "Moving all three into
+ * TensorRT-LLM"): enqueues the gather and an asynchronous copy of request i's record into
+ * out_host + i * gr_beams_result_bytes(eng) on `stream` and returns.  out_host: caller-owned
+ * host memory of n_requests records, pinned (hipHostMalloc) for the copy to overlap.  Once
+ * the stream has passed the copy (an event recorded after this call), gr_beams_unpack reads
+ * the records.  The engine's staging area is reused in stream order, so later calls on the
+ * same stream may follow at once; out_host must not be read before the copy is done nor
+ * reused before it has been read.  Errors as gr_beams_get_batch (nothing enqueued). */
+gr_status gr_beams_get_batch_async(gr_engine *eng, const int64_t *request_ids, int32_t n_requests,
+                                   void *out_host, void *stream);
+
+/* Bytes of one request's record for gr_beams_get_batch_async (0 on a NULL engine). */
+size_t gr_beams_result_bytes(const gr_engine *eng);
+
+/* Record i of a completed gr_beams_get_batch_async copy: *n_beams, then (if it fits
+ * `capacity`) codes host [capacity][n_levels] and scores host [capacity] as gr_beams_get.
+ * GR_E_INVALID_ARG if capacity < *n_beams (n_beams still written). */
+gr_status gr_beams_unpack(const gr_engine *eng, const void *out_host, int32_t i, int32_t capacity, int32_t *codes,
+                          float *scores, int32_t *n_beams);
+
 /* Candidate scoring over a loaded request's context (the pages' second task, [TRT]
  * "Background": candidates are given and the model ranks them; here, as in [GR]
  * section "语义ID", by the model's own outputs).  Each of the n items (host

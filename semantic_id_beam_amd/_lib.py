@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "
 EXPORTS = [
     "gr_engine_create", "gr_engine_workspace_bytes", "gr_engine_bind_workspace", "gr_engine_destroy",
     "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
-    "gr_beams_get_batch", "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
+    "gr_beams_get_batch", "gr_beams_get_batch_async", "gr_beams_result_bytes", "gr_beams_unpack",
+    "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
     "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
     "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
@@ -92,6 +93,9 @@ def lib() -> C.CDLL:
         "gr_beam_step": (i32, [vp, P(i64), i32, vp]),
         "gr_beams_get": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
         "gr_beams_get_batch": (i32, [vp, P(i64), i32, i32, vp, vp, vp, vp]),
+        "gr_beams_get_batch_async": (i32, [vp, P(i64), i32, vp, vp]),
+        "gr_beams_result_bytes": (sz, [vp]),
+        "gr_beams_unpack": (i32, [vp, vp, i32, i32, vp, vp, P(i32)]),
         "gr_request_release": (i32, [vp, i64]),
         "gr_request_reset": (i32, [vp, i64, vp]),
         "gr_request_reset_batch": (i32, [vp, P(i64), i32, vp]),
@@ -200,6 +204,27 @@ def gr_beams_get_batch(eng: int, request_ids, capacity: int, n_levels: int, stre
     _check(lib().gr_beams_get_batch(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), n, capacity, _host(codes),
                                     _host(scores), _host(nb), stream))
     return [(codes[i, : nb[i]], scores[i, : nb[i]]) for i in range(n)]
+
+
+def gr_beams_get_batch_async(eng: int, request_ids, out_host: int, stream: int = 0) -> None:
+    """Enqueue the gather of each request's beams into records at out_host (caller-owned pinned
+    host memory, n * gr_beams_result_bytes bytes); returns without synchronising."""
+    ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+    _check(lib().gr_beams_get_batch_async(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), ids.shape[0],
+                                          out_host, stream))
+
+
+def gr_beams_result_bytes(eng: int) -> int:
+    return int(lib().gr_beams_result_bytes(eng))
+
+
+def gr_beams_unpack(eng: int, out_host: int, i: int, capacity: int, n_levels: int):
+    """(codes [n][n_levels], scores [n]) of record i of a completed gr_beams_get_batch_async copy."""
+    codes = np.zeros((max(capacity, 1), n_levels), dtype=np.int32)
+    scores = np.zeros(max(capacity, 1), dtype=np.float32)
+    nb = C.c_int32(0)
+    _check(lib().gr_beams_unpack(eng, out_host, i, capacity, _host(codes), _host(scores), C.byref(nb)))
+    return codes[: nb.value], scores[: nb.value]
 
 
 def gr_score_items(eng: int, rid: int, items, stream: int = 0) -> np.ndarray:

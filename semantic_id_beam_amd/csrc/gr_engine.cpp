@@ -856,13 +856,12 @@ gr_status d2h(gr_engine *e, void *dst, const void *src, size_t bytes, hipStream_
 }
 }  // namespace
 
-gr_status gr_beams_get_batch(gr_engine *e, const int64_t *ids, int32_t n, int32_t cap, int32_t *codes,
-                             float *scores, int32_t *n_beams, void *stream) {
+gr_status gr_beams_get_batch_async(gr_engine *e, const int64_t *ids, int32_t n, void *out_host, void *stream) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
   if (!ids || n < 1 || n > e->opts.max_requests) return fail(GR_E_INVALID_ARG, "need 1..max_requests ids");
-  if (!n_beams || cap < 0 || (cap > 0 && (!codes || !scores))) return fail(GR_E_INVALID_ARG, "null output");
+  if (!out_host) return fail(GR_E_INVALID_ARG, "null output");
   const int lv = e->dm.levels;
   std::vector<int32_t> slots((size_t)n);
   for (int i = 0; i < n; ++i) {
@@ -881,25 +880,44 @@ gr_status gr_beams_get_batch(gr_engine *e, const int64_t *ids, int32_t n, int32_
                        "result gather")) != GR_OK)
       return r;
   }
-  if ((r = check_dev(e, hipMemcpyAsync(e->out_host, dst, e->out_bytes * (size_t)n, hipMemcpyDeviceToHost, st),
-                     "result copy")) != GR_OK)
-    return r;
-  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
-  bool over = false;
+  return check_dev(e, hipMemcpyAsync(out_host, dst, e->out_bytes * (size_t)n, hipMemcpyDeviceToHost, st),
+                   "result copy");
+}
+
+size_t gr_beams_result_bytes(const gr_engine *e) { return e ? e->out_bytes : 0; }
+
+gr_status gr_beams_unpack(const gr_engine *e, const void *out_host, int32_t i, int32_t cap, int32_t *codes,
+                          float *scores, int32_t *n_beams) {
+  if (!e || !out_host || !n_beams || i < 0 || cap < 0 || (cap > 0 && (!codes || !scores)))
+    return fail(GR_E_INVALID_ARG, "null argument");
+  const int lv = e->dm.levels;
   const size_t W = (size_t)e->dm.W_max;
+  const uint8_t *src = (const uint8_t *)out_host + e->out_bytes * (size_t)i;
+  int32_t nl;
+  std::memcpy(&nl, src, 4);
+  *n_beams = nl;
+  if (nl < 0 || (size_t)nl > W) return fail(GR_E_INVALID_ARG, "not a completed result record");
+  if (nl > cap) return fail(GR_E_INVALID_ARG, "capacity smaller than the number of beams");
+  if (nl > 0) {
+    std::memcpy(codes, src + 16, (size_t)nl * lv * 4);
+    std::memcpy(scores, src + 16 + W * lv * 4, (size_t)nl * 4);
+  }
+  return GR_OK;
+}
+
+gr_status gr_beams_get_batch(gr_engine *e, const int64_t *ids, int32_t n, int32_t cap, int32_t *codes,
+                             float *scores, int32_t *n_beams, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (!n_beams || cap < 0 || (cap > 0 && (!codes || !scores))) return fail(GR_E_INVALID_ARG, "null output");
+  gr_status r;
+  if ((r = gr_beams_get_batch_async(e, ids, n, e->out_host, stream)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize((hipStream_t)stream), "sync")) != GR_OK) return r;
+  const int lv = e->dm.levels;
+  bool over = false;
   for (int i = 0; i < n; ++i) {
-    const uint8_t *src = e->out_host + e->out_bytes * (size_t)i;
-    int32_t nl;
-    std::memcpy(&nl, src, 4);
-    n_beams[i] = nl;
-    if (nl > cap) {
+    if (gr_beams_unpack(e, e->out_host, i, cap, codes + (size_t)i * cap * lv, scores + (size_t)i * cap,
+                        n_beams + i) != GR_OK)
       over = true;
-      continue;
-    }
-    if (nl > 0) {
-      std::memcpy(codes + (size_t)i * cap * lv, src + 16, (size_t)nl * lv * 4);
-      std::memcpy(scores + (size_t)i * cap, src + 16 + W * lv * 4, (size_t)nl * 4);
-    }
   }
   if (over) return fail(GR_E_INVALID_ARG, "capacity smaller than the number of beams");
   return GR_OK;
@@ -1162,17 +1180,12 @@ gr_status sched_collect(gr_sched *s, gr_sched::Batch &B, int32_t *n_completed) {
   gr_status r;
   if ((r = check_dev(e, hipEventSynchronize(B.ev), "result copy")) != GR_OK) return r;
   const int lv = e->dm.levels;
-  const size_t W = (size_t)e->dm.W_max;
   for (size_t i = 0; i < B.ids.size(); ++i) {
-    const uint8_t *src = B.host + e->out_bytes * i;
     gr_sched::Result R;
-    std::memcpy(&R.n, src, 4);
+    std::memcpy(&R.n, B.host + e->out_bytes * i, 4);
     R.codes.resize((size_t)R.n * lv);
     R.scores.resize((size_t)R.n);
-    if (R.n > 0) {
-      std::memcpy(R.codes.data(), src + 16, (size_t)R.n * lv * 4);
-      std::memcpy(R.scores.data(), src + 16 + W * lv * 4, (size_t)R.n * 4);
-    }
+    if ((r = gr_beams_unpack(e, B.host, (int32_t)i, R.n, R.codes.data(), R.scores.data(), &R.n)) != GR_OK) return r;
     s->done[B.ids[i]] = std::move(R);
     s->done_order.push_back(B.ids[i]);
   }
@@ -1265,30 +1278,17 @@ gr_status gr_sched_advance(gr_sched *s, int32_t *n_completed) {
     // 3. the requests this step finished: gather, copy to pinned memory, release the slots
     const int lv = e->dm.levels;
     std::vector<int64_t> still;
-    std::vector<int32_t> slots;
     for (int64_t rid : s->active) {
       const gr_engine::Req &R = e->reqs.at(rid);
       if (R.level == lv) {
         B.ids.push_back(rid);
-        slots.push_back(R.slot);
       } else {
         still.push_back(rid);
       }
     }
     s->active.swap(still);
     if (!B.ids.empty()) {
-      uint8_t *dst = e->ws + e->off_out;
-      const int n = (int)B.ids.size();
-      for (int i0 = 0; i0 < n; i0 += gr::kGatherMax) {
-        const int m = std::min(gr::kGatherMax, n - i0);
-        if ((r = check_dev(e, gr::launch_gather_results(e->dev, slots.data() + i0, m, lv & 1,
-                                                        dst + e->out_bytes * i0, e->out_bytes, s->st),
-                           "result gather")) != GR_OK)
-          return r;
-      }
-      if ((r = check_dev(e, hipMemcpyAsync(B.host, dst, e->out_bytes * (size_t)n, hipMemcpyDeviceToHost, s->st),
-                         "result copy")) != GR_OK)
-        return r;
+      if ((r = gr_beams_get_batch_async(e, B.ids.data(), (int32_t)B.ids.size(), B.host, s->st)) != GR_OK) return r;
       if ((r = check_dev(e, hipEventRecord(B.ev, s->st), "event")) != GR_OK) return r;
       B.pending = true;
       for (int64_t rid : B.ids)

@@ -81,6 +81,30 @@ class BeamEngine:
     def beams_batch(self, rids):
         return G.gr_beams_get_batch(self.eng, rids, self.max_beam_width, self.n_levels, self.stream)
 
+    @property
+    def result_bytes(self) -> int:
+        """Bytes of one request's record in a beams_batch_async buffer."""
+        return G.gr_beams_result_bytes(self.eng)
+
+    def result_buffer(self, n: int):
+        """Pinned host buffer for n records of beams_batch_async."""
+        return _torch().empty(max(n, 1) * self.result_bytes, dtype=_torch().uint8, pin_memory=True)
+
+    def beams_batch_async(self, rids, buf):
+        """Enqueue the gather and copy of rids' beams into pinned `buf` on the current stream and
+        return an event recorded after it; unpack(buf, i) once the event has completed."""
+        n = len(rids)
+        if buf.numel() < n * self.result_bytes or not buf.is_pinned():
+            raise ValueError("buf must be pinned host memory of len(rids) * result_bytes bytes")
+        G.gr_beams_get_batch_async(self.eng, rids, buf.data_ptr(), self.stream)
+        ev = _torch().cuda.Event()
+        ev.record()
+        return ev
+
+    def unpack(self, buf, i: int):
+        """(codes [n][n_levels], scores [n]) of record i of a completed beams_batch_async."""
+        return G.gr_beams_unpack(self.eng, buf.data_ptr(), i, self.max_beam_width, self.n_levels)
+
     def score_items(self, rid: int, items):
         """Log-probability of each given item (its code tuple) over the request's context."""
         return G.gr_score_items(self.eng, rid, items, self.stream)

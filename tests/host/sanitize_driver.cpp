@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <random>
 #include <vector>
 
@@ -104,6 +105,23 @@ int main() {
     EXPECT(gr_request_release(e, rid) == GR_E_NOT_FOUND);
     gr_sched *s = nullptr;
     EXPECT(gr_sched_create(e, 1, nullptr, &s) == GR_E_BAD_STATE && s == nullptr);
+    // a result record unpacked from host memory: full, empty, over capacity, not a record
+    {
+      const size_t rb = gr_beams_result_bytes(e);
+      const int lv = c.m.n_levels;
+      std::vector<uint8_t> rec(rb, 0);
+      int32_t nl = c.W;
+      std::memcpy(rec.data(), &nl, 4);
+      std::vector<int32_t> codes((size_t)c.W * lv);
+      std::vector<float> scores((size_t)c.W);
+      int32_t got = -1;
+      EXPECT(gr_beams_unpack(e, rec.data(), 0, c.W, codes.data(), scores.data(), &got) == GR_OK && got == c.W);
+      EXPECT(gr_beams_unpack(e, rec.data(), 0, c.W - 1, codes.data(), scores.data(), &got) == GR_E_INVALID_ARG);
+      nl = c.W + 1;
+      std::memcpy(rec.data(), &nl, 4);
+      EXPECT(gr_beams_unpack(e, rec.data(), 0, c.W + 8, codes.data(), scores.data(), &got) == GR_E_INVALID_ARG);
+      EXPECT(gr_beams_get_batch_async(e, &rid, 1, rec.data(), nullptr) == GR_E_BAD_STATE);
+    }
     EXPECT(gr_engine_bind_workspace(e, const_cast<void *>(kFake), 16, nullptr) == GR_E_OUT_OF_MEMORY);
     EXPECT(gr_engine_destroy(e) == GR_OK);
   }

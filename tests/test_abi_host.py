@@ -169,3 +169,42 @@ def test_scheduler_host_checks():
     assert L.gr_sched_completed(None, 0, None, C.byref(n)) == G.GR_E_INVALID_ARG
     assert L.gr_sched_counts(None, None, None, None, None) == G.GR_E_INVALID_ARG
     assert L.gr_sched_destroy(None) == G.GR_OK
+
+
+def test_result_records_unpack_and_async_checks():
+    """gr_beams_unpack reads a record (beam count, then codes [W_max][n_levels], then scores
+    [W_max]) from host memory without a GPU; it refuses a capacity below the beam count and a
+    count that no gather writes; the asynchronous gather needs a bound engine."""
+    L = sib.lib()
+    W, lv = 4, 3
+    eng = G.gr_engine_create(_desc(), _items(), _opts(R=2, W=W))
+    rb = G.gr_beams_result_bytes(eng)
+    assert rb >= 16 + W * lv * 4 + W * 4 and rb % 16 == 0
+    assert L.gr_beams_result_bytes(None) == 0
+    buf = np.zeros(2 * rb, dtype=np.uint8)
+    codes = np.arange(W * lv, dtype=np.int32).reshape(W, lv) + 100
+    scores = -np.arange(1, W + 1, dtype=np.float32)
+    rec = buf[rb:]
+    rec[:4] = np.array([3], dtype=np.int32).view(np.uint8)
+    rec[16:16 + codes.nbytes] = codes.view(np.uint8).ravel()
+    rec[16 + codes.nbytes:16 + codes.nbytes + scores.nbytes] = scores.view(np.uint8)
+    c, s = G.gr_beams_unpack(eng, buf.ctypes.data, 1, W, lv)
+    np.testing.assert_array_equal(c, codes[:3])
+    np.testing.assert_array_equal(s, scores[:3])
+    c, s = G.gr_beams_unpack(eng, buf.ctypes.data, 0, W, lv)
+    assert c.shape == (0, lv) and s.shape == (0,)
+    n = C.c_int32()
+    assert L.gr_beams_unpack(eng, buf.ctypes.data, 1, 2, G._host(np.zeros((2, lv), np.int32)),
+                             G._host(np.zeros(2, np.float32)), C.byref(n)) == G.GR_E_INVALID_ARG
+    assert n.value == 3
+    rec[:4] = np.array([W + 1], dtype=np.int32).view(np.uint8)
+    with pytest.raises(G.GrError):
+        G.gr_beams_unpack(eng, buf.ctypes.data, 1, 64, lv)
+    assert L.gr_beams_unpack(None, buf.ctypes.data, 0, 0, None, None, C.byref(n)) == G.GR_E_INVALID_ARG
+    with pytest.raises(G.GrError) as ei:
+        G.gr_beams_get_batch_async(eng, [0], buf.ctypes.data)
+    assert ei.value.status == G.GR_E_BAD_STATE
+    G.gr_engine_destroy(eng)
+    ids = np.zeros(1, np.int64)
+    assert L.gr_beams_get_batch_async(None, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1, buf.ctypes.data,
+                                      None) == G.GR_E_INVALID_ARG

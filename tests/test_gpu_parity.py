@@ -494,6 +494,37 @@ def test_beams_get_batch_equals_single_calls():
     eng.close()
 
 
+def test_beams_get_batch_async_equals_sync():
+    """The asynchronous gather (two pinned buffers, waited on with events) returns, bit for bit,
+    what the synchronising batch call does, across more requests than one gather launch covers,
+    while the next decode of the same requests is already enqueued behind it."""
+    cfg = synth.get_config("ctx1k_beam256", ctx_len=65, beam_width=16, n_items=5000, n_layers=2)
+    R = 70
+    eng = make_engine(cfg, max_requests=R, max_ctx_tokens=R * 64 * 2)
+    rids = [load_request(eng, cfg, 0, rid=100 + i) for i in range(R)]
+    for _ in range(cfg.n_levels):
+        eng.step(rids)
+    ref = eng.beams_batch(rids)
+    assert ref[0][0].shape[0] == cfg.beam_width
+    bufs = [eng.result_buffer(R) for _ in range(2)]
+    done0 = eng.beams_batch_async(rids, bufs[0])
+    sub = rids[::-3]
+    eng.reset_batch(sub)                                  # enqueued behind the first gather
+    for _ in range(cfg.n_levels):
+        eng.step(sub)
+    done1 = eng.beams_batch_async(sub, bufs[1])
+    done0.synchronize()
+    for i in range(R):
+        c, s = eng.unpack(bufs[0], i)
+        assert np.array_equal(c, ref[i][0]) and np.array_equal(s.view(np.uint32), ref[i][1].view(np.uint32)), i
+    done1.synchronize()
+    for j, r in enumerate(sub):
+        c, s = eng.unpack(bufs[1], j)
+        c0, s0 = ref[r - 100]
+        assert np.array_equal(c, c0) and np.array_equal(s.view(np.uint32), s0.view(np.uint32)), r
+    eng.close()
+
+
 def test_topk_select_bit_exact_vs_lexsort():
     import torch
     import semantic_id_beam_amd as sib
