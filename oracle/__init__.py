@@ -33,8 +33,13 @@ GQA (kv = hq // g); log-softmax normalised over the valid codes (R2) or the
 whole codebook (R1); ties broken by flat index j*V + c ascending; the beam
 count after a step is min(W, number of valid candidates).
 
-Parity status per function: every function in ``beam.py`` is pinned by tests
-in ``tests/test_oracle.py`` (closed forms, a hand-derived worked example,
+* Prefill (``prefill.py``): the context K/V and first query from context
+  token ids, one position optionally a soft token projected from a user
+  vector (paper-daily article, section "Getting the user vector into the
+  prompt: three approaches").
+
+Parity status per function: every function in ``beam.py`` and ``prefill.py`` is pinned by tests
+in ``tests/test_oracle.py`` and ``tests/test_oracle_prefill.py`` (closed forms, a hand-derived worked example,
 library cross-checks, brute-force enumeration, greedy special case,
 invariants).  No function is "parity unpinned".
 """
@@ -52,3 +57,4 @@ from .beam import (  # noqa: F401
     select_topk,
     step_candidates,
 )
+from .prefill import prefill_context, soft_embedding, soft_qkv  # noqa: F401

@@ -35,8 +35,12 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     ctx_kv_block,
     items,
+    prefill_tables,
+    prefill_tokens,
     q_last,
     request_shapes,
+    soft_token_weights,
     token_tables,
+    user_vector,
     w_sid,
 )

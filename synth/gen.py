@@ -185,3 +185,46 @@ def items(cfg: Config) -> np.ndarray:
         keep = seen[:n]
         return _decompose(np.sort(keep), V, lv)
     raise ValueError(cfg.item_dist)
+
+
+# ---------------------------------------------------------------- prefill inputs
+_T_PF_TAB, _T_PF_TOK, _T_PF_USER, _T_PF_PROJ, _T_PF_W = range(10, 15)
+
+
+def _normal(cfg: Config, gen: np.random.Generator, shape, scale: float = 1.0):
+    """bf16 bit patterns of N(0, scale^2) for bf16 configs (scale 1 only), float32 otherwise."""
+    if cfg.dtype == "bf16" and scale == 1.0:
+        return _bf16_normal(gen, shape)
+    return (gen.standard_normal(shape) * scale).astype(np.float32)
+
+
+def prefill_tables(cfg: Config, vocab: int):
+    """(TQ [L][Vc][Hq][d], TK [L][Vc][Hkv][d], TV same as TK): per-layer rows of the
+    context tokens, N(0, 1) in the model dtype (bf16 bit patterns or float32)."""
+    L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    return (_normal(cfg, _philox(cfg, _T_PF_TAB, 0), (L, vocab, Hq, d)),
+            _normal(cfg, _philox(cfg, _T_PF_TAB, 1), (L, vocab, Hkv, d)),
+            _normal(cfg, _philox(cfg, _T_PF_TAB, 2), (L, vocab, Hkv, d)))
+
+
+def prefill_tokens(cfg: Config, r: int, vocab: int, n: int | None = None) -> np.ndarray:
+    """Context token ids of request r, [N] int32, uniform over [0, vocab)."""
+    if n is None:
+        n = request_shapes(cfg)[r][0]
+    return _philox(cfg, _T_PF_TOK, r).integers(0, vocab, n, dtype=np.int32)
+
+
+def user_vector(cfg: Config, r: int, user_dim: int) -> np.ndarray:
+    """User vector of request r, [user_dim] float32, N(0, 1)."""
+    return _philox(cfg, _T_PF_USER, r).standard_normal(user_dim).astype(np.float32)
+
+
+def soft_token_weights(cfg: Config, user_dim: int, embed_dim: int):
+    """(proj [user_dim][embed_dim] with variance 1/user_dim, w_q [L][embed_dim][Hq*d], w_k and
+    w_v [L][embed_dim][Hkv*d] with variance 1/embed_dim), float32: projected entries come out
+    about N(0, 1) like the table rows."""
+    L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    g = lambda i, shape, var: (_philox(cfg, _T_PF_W, i).standard_normal(shape) * np.sqrt(var)).astype(np.float32)
+    proj = (_philox(cfg, _T_PF_PROJ).standard_normal((user_dim, embed_dim)) * np.sqrt(1.0 / user_dim)).astype(np.float32)
+    return (proj, g(0, (L, embed_dim, Hq * d), 1.0 / embed_dim), g(1, (L, embed_dim, Hkv * d), 1.0 / embed_dim),
+            g(2, (L, embed_dim, Hkv * d), 1.0 / embed_dim))
