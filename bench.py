@@ -112,6 +112,61 @@ def scoring_leg(cfg, args):
             "candidates_per_s": round(R * n_cand * n_calls / dt, 1)}
 
 
+def prefill_leg(cfg, args, vocab: int = 32768, user_dim: int = 256, embed_dim: int = 2048, reps: int = 5):
+    """Prefill (gr_ctx_prefill) of the workload's requests from context token ids: per-layer
+    token tables of a 32,768-token vocabulary, a soft token at position 0 (a 256-float user
+    vector through one linear layer to a 2048-float embedding, Qwen3-1.7B's hidden size, then
+    projected to q/k/v per layer with float32 weights).  Each pass prefills every request into
+    the engine's pool (HIP events around the pass on the stream it runs on), then releases
+    them."""
+    import numpy as np
+    import torch
+
+    import synth
+    from semantic_id_beam_amd import _lib as G
+    from tests.engine_inputs import make_engine
+    R, L, Hq, Hkv, d = cfg.n_requests, cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    shapes = synth.request_shapes(cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed * 1000 + 17)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    tabs = [torch.randn((L, vocab, h, d), generator=g, device="cuda", dtype=dt) for h in (Hq, Hkv, Hkv)]
+    proj = torch.randn((user_dim, embed_dim), generator=g, device="cuda") * (1.0 / user_dim) ** 0.5
+    ws = [torch.randn((L, embed_dim, h * d), generator=g, device="cuda") * (1.0 / embed_dim) ** 0.5
+          for h in (Hq, Hkv, Hkv)]
+    users = torch.randn((R, user_dim), generator=g, device="cuda")
+    toks = [synth.prefill_tokens(cfg, r, vocab) for r in range(R)]
+    eng = make_engine(cfg, max_requests=R)
+    eng.set_prefill(*tabs, proj, *ws)
+    res = {}
+    for soft in (0, -1):
+        ms = []
+        for rep in range(reps + 1):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(R):
+                eng.prefill(r, toks[r], shapes[r][1], soft_pos=soft, user_vec=users[r] if soft >= 0 else None)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep:
+                ms.append(e0.elapsed_time(e1))
+            for r in range(R):
+                eng.release(r)
+        res[soft] = float(np.median(ms)) / R
+    eng.close()
+    el = 2 if cfg.dtype == "bf16" else 4
+    ctx_b = sum(L * Hkv * d * 2 * el * (n + 2 * G.gr_ctx_padded_len(n)) for n, _ in shapes) / R
+    soft_b = 4 * (L * embed_dim * (Hq + 2 * Hkv) * d + user_dim * embed_dim)
+    log(f"prefill: {res[0]:.3f} ms per request with the soft token, {res[-1]:.3f} without")
+    return {"vocab": vocab, "user_dim": user_dim, "embed_dim": embed_dim, "soft_pos": 0,
+            "ms_per_request": round(res[0], 3), "ms_per_request_no_soft": round(res[-1], 3),
+            "algorithmic_MB_per_request": round((ctx_b + soft_b) / 1e6, 1),
+            "context_MB_per_request": round(ctx_b / 1e6, 1), "soft_weights_MB": round(soft_b / 1e6, 1),
+            "achieved_GBs": round((ctx_b + soft_b) / (res[0] * 1e-3) / 1e9, 1),
+            "achieved_GBs_no_soft": round(ctx_b / (res[-1] * 1e-3) / 1e9, 1)}
+
+
 def workload_leg(name: str, reps: int = 3):
     """Another workload of the decode step, its requests admitted as the workload prescribes
     (all at once, or in admission waves interleaved with the earlier waves' steps).  The first
@@ -498,6 +553,7 @@ def main():
     eng.close()
     del eng
     out["scoring"] = scoring_leg(cfg, args)
+    out["prefill"] = prefill_leg(cfg, args)
     if not args.no_workloads:
         out["workloads"] = {w: workload_leg(w) for w in ("ctx2k_beam30_r64", "ragged_r128")}
         out["serving"] = serving_leg()

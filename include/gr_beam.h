@@ -170,6 +170,56 @@ gr_status gr_ctx_kv_load(gr_engine *eng, int64_t request_id, int32_t ctx_len, in
                          const void *k, const void *v, const void *q_last, uint32_t flags,
                          void *stream);
 
+/* Prefill: the step before the decode, producing a request's ContextKV from context token
+ * ids, with one position optionally replaced by a soft token ([TRT] section "Getting the
+ * user vector into the prompt: three approaches", the third approach: a user vector mapped
+ * by one linear layer to a token-sized embedding and put in place of a placeholder position
+ * before the first forward pass).  Under the model stand-in above, a context token's query,
+ * key and value at layer l are rows of per-layer tables indexed by token id (standing in for
+ * the projections of its embedding, as tok_q/tok_k/tok_v do for fed-back codes).  The soft
+ * token has no table row: its embedding e = u * proj (u: user vector [user_dim], proj:
+ * [user_dim][embed_dim]) is projected per layer, q = e * w_q[l], k = e * w_k[l],
+ * v = e * w_v[l] (head-major columns hq*d + i), in float32, then rounded to the model dtype
+ * (round to nearest even).  Tables are device memory that must stay valid while the engine
+ * uses them.  Limits: vocab >= 1; user_dim = 0 (no soft token) or 1..8192 with embed_dim
+ * 1..8192 and every projection pointer set. */
+typedef struct {
+  int32_t vocab;            /* context-token vocabulary size Vc */
+  const void *tok_q;        /* device [L][Vc][Hq][d], model dtype */
+  const void *tok_k;        /* device [L][Vc][Hkv][d], model dtype */
+  const void *tok_v;        /* device [L][Vc][Hkv][d], model dtype */
+  int32_t user_dim;         /* length of the user vector; 0 = no soft token */
+  int32_t embed_dim;        /* soft embedding size */
+  const float *proj;        /* device [user_dim][embed_dim] */
+  const float *w_q;         /* device [L][embed_dim][Hq*d] */
+  const float *w_k;         /* device [L][embed_dim][Hkv*d] */
+  const float *w_v;         /* device [L][embed_dim][Hkv*d] */
+} gr_prefill_desc;
+
+/* Sets (or replaces) the prefill tables of the engine.  Allocates the engine's prefill
+ * staging (a pinned token buffer and a small device area; outside any hot path).  Errors:
+ * GR_E_INVALID_ARG (limits above, null pointers), GR_E_OUT_OF_MEMORY. */
+gr_status gr_engine_set_prefill(gr_engine *eng, const gr_prefill_desc *desc);
+
+/* Admits request `request_id` like gr_ctx_kv_load, its context made from tokens host
+ * [ctx_len] (each in [0, vocab) except at soft_pos, whose entry is ignored).  soft_pos = -1:
+ * no soft token; else 0 <= soft_pos < ctx_len takes the soft token of user_vec device
+ * [user_dim] float32.  q_last is the last position's query (a table row, or the soft
+ * token's q when soft_pos = ctx_len - 1).
+ *   k_native, vt_native both NULL: the context goes into the engine's pool (as a copy load);
+ *   both set: it is written to these caller buffers in the native layout of GR_LOAD_ADOPT
+ *     (K [L][Hkv][Np][d], V^T [L][Hkv][d][Np], padding zero) and the request keeps them
+ *     (alive and unchanged until gr_request_release), 16-byte aligned.
+ * q_last_out: optional device [L][Hq][d] copy of the last query.  Stream-ordered; the
+ * engine's prefill staging is shared, so prefills of one engine run on one stream.
+ * Errors: GR_E_BAD_STATE (workspace not bound, no prefill tables, soft_pos >= 0 without
+ * a soft projection), GR_E_INVALID_ARG (a token id out of range, bad soft_pos, null
+ * tokens or user_vec, one of k_native / vt_native set, an id already loaded, ctx_len < 1,
+ * beam_width outside [1, max_beam_width]), GR_E_OUT_OF_MEMORY (no free slot or pool space). */
+gr_status gr_ctx_prefill(gr_engine *eng, int64_t request_id, const int32_t *tokens, int32_t ctx_len,
+                         int32_t soft_pos, const float *user_vec, int32_t beam_width, void *k_native,
+                         void *vt_native, void *q_last_out, void *stream);
+
 /* Advances each listed request by one decode step (one semantic-ID level),
  * whatever level each one is at: requests at different levels can share a
  * call (continuous batching).  Enqueued on `stream`; returns without waiting.

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "
 #: every symbol include/gr_beam.h declares
 EXPORTS = [
     "gr_engine_create", "gr_engine_workspace_bytes", "gr_engine_bind_workspace", "gr_engine_destroy",
-    "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_beam_step", "gr_beams_get",
+    "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_engine_set_prefill", "gr_ctx_prefill",
+    "gr_beam_step", "gr_beams_get",
     "gr_beams_get_batch", "gr_beams_get_batch_async", "gr_beams_result_bytes", "gr_beams_unpack",
     "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
@@ -61,6 +62,12 @@ class gr_engine_opts(C.Structure):
                 ("max_splits", C.c_int32), ("flags", C.c_uint32), ("max_layers_per_launch", C.c_int32)]
 
 
+class gr_prefill_desc(C.Structure):
+    _fields_ = [("vocab", C.c_int32), ("tok_q", C.c_void_p), ("tok_k", C.c_void_p), ("tok_v", C.c_void_p),
+                ("user_dim", C.c_int32), ("embed_dim", C.c_int32), ("proj", C.c_void_p), ("w_q", C.c_void_p),
+                ("w_k", C.c_void_p), ("w_v", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -90,6 +97,8 @@ def lib() -> C.CDLL:
         "gr_engine_trie_nodes": (i32, [vp, i32, P(i64)]),
         "gr_ctx_padded_len": (i32, [i32]),
         "gr_ctx_kv_load": (i32, [vp, i64, i32, i32, vp, vp, vp, u32, vp]),
+        "gr_engine_set_prefill": (i32, [vp, P(gr_prefill_desc)]),
+        "gr_ctx_prefill": (i32, [vp, i64, vp, i32, i32, vp, i32, vp, vp, vp, vp]),
         "gr_beam_step": (i32, [vp, P(i64), i32, vp]),
         "gr_beams_get": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
         "gr_beams_get_batch": (i32, [vp, P(i64), i32, i32, vp, vp, vp, vp]),
@@ -179,6 +188,18 @@ def gr_ctx_padded_len(n: int) -> int:
 def gr_ctx_kv_load(eng: int, rid: int, ctx_len: int, beam_width: int, k, v, q_last, flags: int = 0,
                    stream: int = 0):
     _check(lib().gr_ctx_kv_load(eng, rid, ctx_len, beam_width, _ptr(k), _ptr(v), _ptr(q_last), flags, stream))
+
+
+def gr_engine_set_prefill(eng: int, desc: gr_prefill_desc):
+    _check(lib().gr_engine_set_prefill(eng, C.byref(desc)))
+
+
+def gr_ctx_prefill(eng: int, rid: int, tokens, soft_pos: int, user_vec, beam_width: int, k_native=None,
+                   vt_native=None, q_last_out=None, stream: int = 0):
+    """tokens: host int32 [N]; user_vec, k_native, vt_native, q_last_out: device pointers or None."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    _check(lib().gr_ctx_prefill(eng, rid, _host(tok), tok.shape[0], soft_pos, _ptr(user_vec), beam_width,
+                                _ptr(k_native), _ptr(vt_native), _ptr(q_last_out), stream))
 
 
 def gr_beam_step(eng: int, request_ids, stream: int = 0):

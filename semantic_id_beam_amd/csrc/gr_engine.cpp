@@ -98,6 +98,17 @@ struct gr_engine {
   std::vector<hipEvent_t> events;
   std::vector<bool> event_used;
   int ring = 0;
+
+  // prefill (gr_engine_set_prefill): the tables, a pinned token buffer and its device copy
+  // (grown on demand; an event guards the pinned buffer until its upload has run), and the
+  // soft token's embedding and partial projections
+  gr_prefill_desc pf{};
+  bool has_pf = false;
+  int32_t *pf_tok_host = nullptr, *pf_tok_dev = nullptr;
+  int64_t pf_tok_cap = 0;
+  float *pf_soft = nullptr;
+  hipEvent_t pf_ev = nullptr;
+  bool pf_ev_used = false;
 };
 
 namespace {
@@ -448,7 +459,143 @@ gr_status gr_engine_destroy(gr_engine *e) {
       if (p) (void)hipHostFree(p);
     if (e->out_host) (void)hipHostFree(e->out_host);
   }
+  if (e->pf_tok_host || e->pf_tok_dev || e->pf_soft || e->pf_ev) {
+    (void)hipDeviceSynchronize();
+    if (e->pf_tok_host) (void)hipHostFree(e->pf_tok_host);
+    if (e->pf_tok_dev) (void)hipFree(e->pf_tok_dev);
+    if (e->pf_soft) (void)hipFree(e->pf_soft);
+    if (e->pf_ev) (void)hipEventDestroy(e->pf_ev);
+  }
   delete e;
+  return GR_OK;
+}
+
+gr_status gr_engine_set_prefill(gr_engine *e, const gr_prefill_desc *p) {
+  if (!e || !p) return fail(GR_E_INVALID_ARG, "null engine or prefill description");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (p->vocab < 1 || !p->tok_q || !p->tok_k || !p->tok_v) return fail(GR_E_INVALID_ARG, "need vocab >= 1 and three tables");
+  if (p->user_dim < 0 || p->user_dim > 8192) return fail(GR_E_INVALID_ARG, "user_dim must be in [0, 8192]");
+  if (p->user_dim > 0 && (p->embed_dim < 1 || p->embed_dim > 8192 || !p->proj || !p->w_q || !p->w_k || !p->w_v))
+    return fail(GR_E_INVALID_ARG, "a soft token needs embed_dim in [1, 8192] and proj, w_q, w_k, w_v");
+  if (((uintptr_t)p->tok_k | (uintptr_t)p->tok_v) & 15u) return fail(GR_E_INVALID_ARG, "tables must be 16-byte aligned");
+  gr_status r;
+  if (!e->pf_ev && (r = check_dev(e, hipEventCreateWithFlags(&e->pf_ev, hipEventDisableTiming), "event")) != GR_OK)
+    return r;
+  if (e->pf_soft) {
+    if ((r = check_dev(e, hipDeviceSynchronize(), "sync")) != GR_OK) return r;
+    (void)hipFree(e->pf_soft);
+    e->pf_soft = nullptr;
+  }
+  if (p->user_dim > 0) {
+    const size_t ct = (size_t)(e->dm.Hq + 2 * e->dm.Hkv) * e->dm.d;
+    const size_t n = (size_t)p->embed_dim + (size_t)gr::kSoftSplit * e->dm.L * ct;
+    if (hipMalloc((void **)&e->pf_soft, n * sizeof(float)) != hipSuccess) {
+      e->pf_soft = nullptr;
+      (void)hipGetLastError();
+      return fail(GR_E_OUT_OF_MEMORY, "soft-token staging");
+    }
+  }
+  e->pf = *p;
+  e->has_pf = true;
+  return GR_OK;
+}
+
+gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32_t N, int32_t soft_pos,
+                         const float *u, int32_t W, void *kn, void *vtn, void *q_out, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (!e->has_pf) return fail(GR_E_BAD_STATE, "no prefill tables (gr_engine_set_prefill)");
+  if (!tokens) return fail(GR_E_INVALID_ARG, "null tokens");
+  if (N < 1) return fail(GR_E_INVALID_ARG, "ctx_len must be >= 1");
+  if (W < 1 || W > e->dm.W_max) return fail(GR_E_INVALID_ARG, "beam_width must be in [1, max_beam_width]");
+  if (soft_pos < -1 || soft_pos >= N) return fail(GR_E_INVALID_ARG, "soft_pos must be -1 or in [0, ctx_len)");
+  if (soft_pos >= 0 && e->pf.user_dim < 1) return fail(GR_E_BAD_STATE, "no soft-token projection set");
+  if (soft_pos >= 0 && !u) return fail(GR_E_INVALID_ARG, "null user vector");
+  if ((kn == nullptr) != (vtn == nullptr)) return fail(GR_E_INVALID_ARG, "k_native and vt_native go together");
+  if (((uintptr_t)kn | (uintptr_t)vtn) & 15u) return fail(GR_E_INVALID_ARG, "k_native and vt_native must be 16-byte aligned");
+  if (e->reqs.count(rid)) return fail(GR_E_INVALID_ARG, "request id already loaded");
+  if (e->free_slots.empty()) return fail(GR_E_OUT_OF_MEMORY, "no free request slot (max_requests)");
+  for (int32_t n = 0; n < N; ++n)
+    if (n != soft_pos && (tokens[n] < 0 || tokens[n] >= e->pf.vocab))
+      return fail(GR_E_INVALID_ARG, "token id outside [0, vocab)");
+  const int Np = gr_ctx_padded_len(N);
+  hipStream_t st = (hipStream_t)stream;
+  gr_status r;
+  // token staging: the pinned buffer is reused once its last upload has run
+  if (e->pf_ev_used && (r = check_dev(e, hipEventSynchronize(e->pf_ev), "prefill staging")) != GR_OK) return r;
+  if (N > e->pf_tok_cap) {
+    const int64_t cap = std::max<int64_t>(N, 2 * e->pf_tok_cap);
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+    if (e->pf_tok_host) (void)hipHostFree(e->pf_tok_host);
+    if (e->pf_tok_dev) (void)hipFree(e->pf_tok_dev);
+    e->pf_tok_host = nullptr;
+    e->pf_tok_dev = nullptr;
+    e->pf_tok_cap = 0;
+    if (hipHostMalloc((void **)&e->pf_tok_host, (size_t)cap * 4, hipHostMallocDefault) != hipSuccess ||
+        hipMalloc((void **)&e->pf_tok_dev, (size_t)cap * 4) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(GR_E_OUT_OF_MEMORY, "prefill token staging");
+    }
+    e->pf_tok_cap = cap;
+  }
+  std::memcpy(e->pf_tok_host, tokens, (size_t)N * 4);
+  if (soft_pos >= 0) e->pf_tok_host[soft_pos] = 0;
+  gr_engine::Req R;
+  R.N = N;
+  R.Np = Np;
+  R.W = W;
+  if (kn) {
+    R.adopt = true;
+    R.k = kn;
+    R.vt = vtn;
+  } else {
+    int64_t off;
+    if (!pool_alloc(e, Np, &off)) return fail(GR_E_OUT_OF_MEMORY, "context pool exhausted (max_ctx_tokens)");
+    R.pool_off = off;
+    uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
+    R.k = dk;
+    R.vt = dk + (size_t)e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
+  }
+  R.slot = e->free_slots.back();
+  uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
+  const int L = e->dm.L, Hq = e->dm.Hq, Hkv = e->dm.Hkv, d = e->dm.d;
+  float *part = e->pf_soft ? e->pf_soft + e->pf.embed_dim : nullptr;
+  auto run = [&]() -> gr_status {
+    gr_status q;
+    if ((q = check_dev(e, hipMemcpyAsync(e->pf_tok_dev, e->pf_tok_host, (size_t)N * 4, hipMemcpyHostToDevice, st),
+                       "token upload")) != GR_OK)
+      return q;
+    if ((q = check_dev(e, hipEventRecord(e->pf_ev, st), "prefill staging")) != GR_OK) return q;
+    e->pf_ev_used = true;
+    if (soft_pos >= 0 &&
+        (q = check_dev(e, gr::launch_soft_token(u, e->pf.proj, e->pf.user_dim, e->pf.embed_dim, e->pf.w_q, e->pf.w_k,
+                                                e->pf.w_v, L, Hq * d, Hkv * d, e->pf_soft, part, st),
+                       "soft token")) != GR_OK)
+      return q;
+    if ((q = check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, e->pf_tok_dev, N, Np, soft_pos,
+                                                 part, L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
+                                                 const_cast<void *>(R.vt), st),
+                       "prefill")) != GR_OK)
+      return q;
+    // key-norm bounds and value scales: the load kernel's read-only pass over the native layout
+    if ((q = check_dev(e, gr::launch_load_ctx(nullptr, nullptr, const_cast<void *>(R.k), const_cast<void *>(R.vt),
+                                              false, L, Hkv, N, Np, d, e->elem, (float *)(sb + e->sl.knmax),
+                                              (float *)(sb + e->sl.vscale), st),
+                       "context bounds")) != GR_OK)
+      return q;
+    const int last = (soft_pos == N - 1) ? -1 : tokens[N - 1];
+    return check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, last, part, L, Hq, Hkv, d, e->pf.vocab,
+                                             sb + e->sl.q_last, q_out, st),
+                     "prefill query");
+  };
+  if ((r = run()) != GR_OK) {
+    if (!R.adopt) pool_free(e, R.pool_off, Np);
+    return r;
+  }
+  if ((r = check_dev(e, gr::launch_init_slots(e->dev, &R.slot, 1, st), "slot init")) != GR_OK) return r;
+  e->free_slots.pop_back();
+  e->reqs[rid] = R;
   return GR_OK;
 }
 

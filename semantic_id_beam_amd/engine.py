@@ -72,6 +72,33 @@ class BeamEngine:
         if adopt:
             self._keep[rid] = (k, v)
 
+    def set_prefill(self, tok_q, tok_k, tok_v, proj=None, w_q=None, w_k=None, w_v=None):
+        """Context-token tables [L][Vc][H][d] (model dtype) and, for a soft token, the projection
+        proj [user_dim][embed_dim] and w_q/w_k/w_v [L][embed_dim][H*d], float32.  numpy arrays are
+        uploaded; torch device tensors are used in place.  The engine keeps them alive."""
+        torch = _torch()
+        dev = (lambda x: x) if isinstance(tok_k, torch.Tensor) else (lambda x: to_device(x, self.device))
+        tabs = [dev(t) for t in (tok_q, tok_k, tok_v)]
+        soft = []
+        if proj is not None:
+            f32 = lambda x: x if isinstance(x, torch.Tensor) else to_device(np.asarray(x, dtype=np.float32), self.device)
+            soft = [f32(x) for x in (proj, w_q, w_k, w_v)]
+        desc = G.gr_prefill_desc(int(tabs[1].shape[1]), *(t.data_ptr() for t in tabs),
+                                 int(soft[0].shape[0]) if soft else 0, int(soft[0].shape[1]) if soft else 0,
+                                 *((x.data_ptr() for x in soft) if soft else (None,) * 4))
+        G.gr_engine_set_prefill(self.eng, desc)
+        self._keep_pf = (tabs, soft)
+
+    def prefill(self, rid: int, tokens, beam_width: int, soft_pos: int = -1, user_vec=None, k_native=None,
+                vt_native=None, q_last_out=None):
+        """Admit rid with its context made from token ids (host int array), one position
+        optionally a soft token of user_vec (device float32 [user_dim]); with k_native/vt_native
+        (device, native layout) the context goes there and the request keeps them."""
+        G.gr_ctx_prefill(self.eng, rid, tokens, soft_pos, user_vec, beam_width, k_native, vt_native, q_last_out,
+                         self.stream)
+        if k_native is not None:
+            self._keep[rid] = (k_native, vt_native)
+
     def step(self, rids):
         G.gr_beam_step(self.eng, rids, self.stream)
 

@@ -31,6 +31,11 @@ GR_STUB(launch_gather_results, const Dev &, const int32_t *, int, int, uint8_t *
 GR_STUB(launch_load_ctx, const void *, const void *, void *, void *, bool, int, int, int, int, int, int, float *,
         float *, hipStream_t)
 GR_STUB(launch_topk_select, const float *, int, int, int, int32_t *, float *, int32_t *, hipStream_t)
+GR_STUB(launch_soft_token, const float *, const float *, int, int, const float *, const float *, const float *, int,
+        int, int, float *, float *, hipStream_t)
+GR_STUB(launch_prefill_ctx, int, const void *, const void *, const int32_t *, int, int, int, const float *, int, int,
+        int, int, int, void *, void *, hipStream_t)
+GR_STUB(launch_prefill_q, int, const void *, int, const float *, int, int, int, int, int, void *, void *, hipStream_t)
 #undef GR_STUB
 }  // namespace gr
 
@@ -103,6 +108,18 @@ int main() {
     EXPECT(gr_ctx_kv_load(e, rid, 10, 4, kFake, kFake, kFake, 0, nullptr) == GR_E_BAD_STATE);
     EXPECT(gr_beam_step(e, &rid, 1, nullptr) == GR_E_BAD_STATE);
     EXPECT(gr_request_release(e, rid) == GR_E_NOT_FOUND);
+    // prefill before a workspace or tables, and a description the engine refuses
+    {
+      const int32_t toks[3] = {0, 1, 2};
+      EXPECT(gr_ctx_prefill(e, rid, toks, 3, -1, nullptr, 1, nullptr, nullptr, nullptr, nullptr) == GR_E_BAD_STATE);
+      gr_prefill_desc pd{};
+      EXPECT(gr_engine_set_prefill(e, &pd) == GR_E_INVALID_ARG);
+      pd.vocab = 4;
+      pd.tok_q = pd.tok_k = pd.tok_v = kFake;
+      pd.user_dim = 3;
+      EXPECT(gr_engine_set_prefill(e, &pd) == GR_E_INVALID_ARG);
+      EXPECT(gr_engine_set_prefill(nullptr, &pd) == GR_E_INVALID_ARG);
+    }
     gr_sched *s = nullptr;
     EXPECT(gr_sched_create(e, 1, nullptr, &s) == GR_E_BAD_STATE && s == nullptr);
     // a result record unpacked from host memory: full, empty, over capacity, not a record
