@@ -156,7 +156,7 @@ def prefill_leg(cfg, args, vocab: int = 32768, user_dim: int = 256, embed_dim: i
         res[soft] = float(np.median(ms)) / R
     eng.close()
     el = 2 if cfg.dtype == "bf16" else 4
-    ctx_b = sum(L * Hkv * d * 2 * el * (n + 2 * G.gr_ctx_padded_len(n)) for n, _ in shapes) / R
+    ctx_b = sum(L * Hkv * d * 2 * el * (n + G.gr_ctx_padded_len(n)) for n, _ in shapes) / R
     soft_b = 4 * (L * embed_dim * (Hq + 2 * Hkv) * d + user_dim * embed_dim)
     log(f"prefill: {res[0]:.3f} ms per request with the soft token, {res[-1]:.3f} without")
     return {"vocab": vocab, "user_dim": user_dim, "embed_dim": embed_dim, "soft_pos": 0,

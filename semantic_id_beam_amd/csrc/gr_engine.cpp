@@ -488,7 +488,7 @@ gr_status gr_engine_set_prefill(gr_engine *e, const gr_prefill_desc *p) {
   }
   if (p->user_dim > 0) {
     const size_t ct = (size_t)(e->dm.Hq + 2 * e->dm.Hkv) * e->dm.d;
-    const size_t n = (size_t)p->embed_dim + (size_t)gr::kSoftSplit * e->dm.L * ct;
+    const size_t n = (size_t)gr::kSoftSplit * (p->embed_dim + e->dm.L * ct);
     if (hipMalloc((void **)&e->pf_soft, n * sizeof(float)) != hipSuccess) {
       e->pf_soft = nullptr;
       (void)hipGetLastError();
@@ -560,7 +560,7 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
   const int L = e->dm.L, Hq = e->dm.Hq, Hkv = e->dm.Hkv, d = e->dm.d;
-  float *part = e->pf_soft ? e->pf_soft + e->pf.embed_dim : nullptr;
+  float *part = e->pf_soft ? e->pf_soft + (size_t)gr::kSoftSplit * e->pf.embed_dim : nullptr;
   auto run = [&]() -> gr_status {
     gr_status q;
     if ((q = check_dev(e, hipMemcpyAsync(e->pf_tok_dev, e->pf_tok_host, (size_t)N * 4, hipMemcpyHostToDevice, st),
@@ -573,16 +573,12 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
                                                 e->pf.w_v, L, Hq * d, Hkv * d, e->pf_soft, part, st),
                        "soft token")) != GR_OK)
       return q;
+    // the context in the native layout, with its key-norm bounds and value scales
     if ((q = check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, e->pf_tok_dev, N, Np, soft_pos,
                                                  part, L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
-                                                 const_cast<void *>(R.vt), st),
+                                                 const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
+                                                 (float *)(sb + e->sl.vscale), st),
                        "prefill")) != GR_OK)
-      return q;
-    // key-norm bounds and value scales: the load kernel's read-only pass over the native layout
-    if ((q = check_dev(e, gr::launch_load_ctx(nullptr, nullptr, const_cast<void *>(R.k), const_cast<void *>(R.vt),
-                                              false, L, Hkv, N, Np, d, e->elem, (float *)(sb + e->sl.knmax),
-                                              (float *)(sb + e->sl.vscale), st),
-                       "context bounds")) != GR_OK)
       return q;
     const int last = (soft_pos == N - 1) ? -1 : tokens[N - 1];
     return check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, last, part, L, Hq, Hkv, d, e->pf.vocab,

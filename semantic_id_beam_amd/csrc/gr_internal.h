@@ -128,7 +128,8 @@ hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, in
 // scale, the power of two 2^e with max |v| < 2^e over the first N tokens -> vscale [L][Hkv].
 hipError_t launch_load_ctx(const void *src_k, const void *src_v, void *nk, void *nvt, bool copy, int L, int Hkv,
                            int N, int Np, int d, int elem_bytes, float *knmax, float *vscale, hipStream_t st);
-// Prefill (gr_prefill.hip).  Soft token: e = u * proj [du][de] into e_buf [de], then the
+// Prefill (gr_prefill.hip).  Soft token: e = u * proj [du][de] as kSoftSplit partial sums
+// over the user vector in e_buf [kSoftSplit][de], then the
 // per-layer projections of e in kSoftSplit partial sums over the embedding dimension,
 // part [kSoftSplit][L][cq + 2 ckv] (q columns, then k, then v; cq = Hq d, ckv = Hkv d),
 // summed in order by their readers.
@@ -137,10 +138,11 @@ hipError_t launch_soft_token(const float *u, const float *proj, int du, int de, 
                              const float *wv, int L, int cq, int ckv, float *e_buf, float *part, hipStream_t st);
 // Context K, V of tokens tok device [N] (table rows of tk / tv [L][vocab][Hkv][d]; position
 // soft_pos from part) written in the native layout nk [L][Hkv][Np][d], nvt [L][Hkv][d][Np],
-// padding zero.  Token ids must be in [0, vocab) (checked by the caller).
+// padding zero, with knmax / vscale [L][Hkv] as launch_load_ctx computes them.  Token ids
+// must be in [0, vocab) (checked by the caller).
 hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, const int32_t *tok, int N, int Np,
                               int soft_pos, const float *part, int L, int Hq, int Hkv, int d, int vocab, void *nk,
-                              void *nvt, hipStream_t st);
+                              void *nvt, float *knmax, float *vscale, hipStream_t st);
 // Query of the last position, [L][Hq][d]: row last_tok of tq [L][vocab][Hq][d], or the soft
 // token's q (last_tok < 0), into q_slot and (if set) q_out.
 hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const float *part, int L, int Hq, int Hkv,

@@ -9,12 +9,13 @@
 // placeholder's place before the first forward pass; here that embedding is projected to
 // the soft position's query, key and value per layer.
 //
-//   k_soft_embed    e = u * proj                       (one thread per embedding element)
+//   k_soft_embed    e = u * proj, split in kSoftSplit ranges of the user vector
 //   k_soft_proj     e * w_{q,k,v}[l], split in kSoftSplit ranges of the embedding
 //                   dimension (partial sums, added in order by the readers)
 //   k_prefill_ctx   table rows (or the soft row, rounded to the model dtype) into the
 //                   native layout: K rows copied as 16-byte chunks, V transposed through
-//                   LDS; padding tokens zero
+//                   LDS; padding tokens zero; the key-norm and |v| maxima of each (layer,
+//                   kv head) folded in (k_pf_bounds_init / k_pf_bounds_finish around it)
 //   k_prefill_q     the last position's query into the request's slot
 //
 // All of it is HBM-bound gather and GEMV work: no matrix cores.
@@ -51,13 +52,18 @@ __device__ inline float soft_col(const float *part, int L, int ct, int l, int c)
   return a;
 }
 
+// grid (ceil(de / 256), kSoftSplit): partial sums of e over kSoftSplit ranges of the user
+// vector, e_part [kSoftSplit][de], added in order by k_soft_proj
 __global__ __launch_bounds__(256) void k_soft_embed(const float *__restrict__ u, const float *__restrict__ proj,
-                                                    int du, int de, float *__restrict__ e) {
+                                                    int du, int de, float *__restrict__ e_part) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= de) return;
+  const int chunk = (du + kSoftSplit - 1) / kSoftSplit;
+  const int i0 = blockIdx.y * chunk, i1 = min(du, i0 + chunk);
   float a = 0.f;
-  for (int i = 0; i < du; ++i) a = fmaf(u[i], proj[(size_t)i * de + j], a);
-  e[j] = a;
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) a = fmaf(u[i], proj[(size_t)i * de + j], a);
+  e_part[(size_t)blockIdx.y * de + j] = a;
 }
 
 // grid (ceil(ct / 256), L, kSoftSplit): thread = one output column of one layer over one
@@ -68,7 +74,12 @@ __global__ __launch_bounds__(256) void k_soft_proj(const float *__restrict__ e, 
   __shared__ float se[kMaxEmbed / kSoftSplit];
   const int chunk = (de + kSoftSplit - 1) / kSoftSplit;
   const int i0 = blockIdx.z * chunk, i1 = min(de, i0 + chunk);
-  for (int i = i0 + (int)threadIdx.x; i < i1; i += 256) se[i - i0] = e[i];
+  for (int i = i0 + (int)threadIdx.x; i < i1; i += 256) {
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < kSoftSplit; ++s) a += e[(size_t)s * de + i];
+    se[i - i0] = a;
+  }
   __syncthreads();
   const int l = blockIdx.y, ct = cq + 2 * ckv;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -94,18 +105,57 @@ __global__ __launch_bounds__(256) void k_soft_proj(const float *__restrict__ e, 
   part[((size_t)blockIdx.z * L + l) * ct + c] = a;
 }
 
-// grid (Np / 64, Hkv, L), 256 threads
+// element e of a 16-byte chunk as float (bf16 or f32 payload)
+template <typename T>
+__device__ inline float chunk_f32(const uint4 &x, int e) {
+  const uint32_t w = e / (int)(4 / sizeof(T)) == 0 ? x.x : e / (int)(4 / sizeof(T)) == 1 ? x.y
+                   : e / (int)(4 / sizeof(T)) == 2 ? x.z : x.w;
+  if (sizeof(T) == 2) return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  return __uint_as_float(w);
+}
+
+__global__ void k_pf_bounds_init(uint32_t *kn_bits, uint32_t *vm_bits, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    kn_bits[i] = 0u;
+    vm_bits[i] = 0u;
+  }
+}
+
+// In place, per (layer, kv head): kn = sqrt(largest squared key norm), vs = 2^e with
+// max|v| < 2^e (max|v| = m 2^e, m in [0.5, 1)), kept a normal float.  The decode's fixed
+// softmax reference and value scaling read these; they are the same as a load computes.
+__global__ void k_pf_bounds_finish(float *kn, float *vs, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    kn[i] = sqrtf(__uint_as_float(((const uint32_t *)kn)[i]));
+    int ex = 0;
+    (void)frexpf(__uint_as_float(((const uint32_t *)vs)[i]), &ex);
+    vs[i] = ldexpf(1.f, min(max(ex, -126), 127));
+  }
+}
+
+// grid (Np / 64, Hkv, L), 256 threads.  Besides the copy, each workgroup folds its tokens
+// into the (layer, kv head) maxima of the squared key norm and of |v| (float bits, atomic
+// max: non-negative floats order like their bit patterns).  A row's squared norm is summed
+// per 16-byte chunk in element order, then over the row's chunks (consecutive lanes) by an
+// xor-shuffle tree.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prefill_ctx(const T *__restrict__ tk, const T *__restrict__ tv,
                                                      const int32_t *__restrict__ tok, int N, int Np, int soft_pos,
                                                      const float *__restrict__ part, int L, int cq, int Hkv, int d,
-                                                     int vocab, T *__restrict__ nk, T *__restrict__ nvt) {
+                                                     int vocab, T *__restrict__ nk, T *__restrict__ nvt,
+                                                     uint32_t *__restrict__ kn_bits, uint32_t *__restrict__ vm_bits) {
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int PITCH = 128 + EPC;          // LDS row pitch (elements), 16-byte multiple
   __shared__ __align__(16) T sv[kPfTile * PITCH];
+  __shared__ float sred[2][4];
   const int tile = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int cpr = d / EPC, ckv = Hkv * d, ct = cq + 2 * ckv;
   const size_t head = (size_t)l * Hkv + h;
+  float kmax = 0.f, vmax = 0.f;
+  // kPfTile * cpr is a multiple of 256 for every supported (d, dtype): all lanes run every
+  // iteration, so the shuffles below see whole rows
   for (int idx = threadIdx.x; idx < kPfTile * cpr; idx += 256) {
     const int t = idx / cpr, ch = idx - t * cpr;
     const int n = tile * kPfTile + t;
@@ -129,8 +179,29 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(const T *__restrict__ tk, c
     }
     *reinterpret_cast<uint4 *>(nk + (head * Np + n) * d + (size_t)ch * EPC) = kc;
     *reinterpret_cast<uint4 *>(sv + t * PITCH + ch * EPC) = vc;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const float x = chunk_f32<T>(kc, e);
+      ss = fmaf(x, x, ss);
+      vmax = fmaxf(vmax, fabsf(chunk_f32<T>(vc, e)));
+    }
+    for (int o = cpr / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    kmax = fmaxf(kmax, ss);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    kmax = fmaxf(kmax, __shfl_xor(kmax, o));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sred[0][threadIdx.x >> 6] = kmax;
+    sred[1][threadIdx.x >> 6] = vmax;
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicMax(kn_bits + head, __float_as_uint(fmaxf(fmaxf(sred[0][0], sred[0][1]), fmaxf(sred[0][2], sred[0][3]))));
+    atomicMax(vm_bits + head, __float_as_uint(fmaxf(fmaxf(sred[1][0], sred[1][1]), fmaxf(sred[1][2], sred[1][3]))));
+  }
   // V^T: row c of this head holds the tile's 64 tokens; a thread writes EPC of them
   constexpr int GPR = kPfTile / EPC;
   for (int idx = threadIdx.x; idx < d * GPR; idx += 256) {
@@ -163,7 +234,8 @@ __global__ __launch_bounds__(256) void k_prefill_q(const T *__restrict__ tq, int
 hipError_t launch_soft_token(const float *u, const float *proj, int du, int de, const float *wq, const float *wk,
                              const float *wv, int L, int cq, int ckv, float *e_buf, float *part, hipStream_t st) {
   if (du < 1 || de < 1 || de > kMaxEmbed || L < 1 || cq < 1 || ckv < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_soft_embed, dim3((unsigned)((de + 255) / 256)), dim3(256), 0, st, u, proj, du, de, e_buf);
+  hipLaunchKernelGGL(k_soft_embed, dim3((unsigned)((de + 255) / 256), kSoftSplit), dim3(256), 0, st, u, proj, du, de,
+                     e_buf);
   const int ct = cq + 2 * ckv;
   hipLaunchKernelGGL(k_soft_proj, dim3((unsigned)((ct + 255) / 256), (unsigned)L, kSoftSplit), dim3(256), 0, st,
                      e_buf, wq, wk, wv, de, L, cq, ckv, part);
@@ -172,17 +244,21 @@ hipError_t launch_soft_token(const float *u, const float *proj, int du, int de, 
 
 hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, const int32_t *tok, int N, int Np,
                               int soft_pos, const float *part, int L, int Hq, int Hkv, int d, int vocab, void *nk,
-                              void *nvt, hipStream_t st) {
+                              void *nvt, float *knmax, float *vscale, hipStream_t st) {
   if (N < 1 || Np % kPfTile != 0 || N > Np || (d != 64 && d != 128) || (elem_bytes != 2 && elem_bytes != 4) ||
       soft_pos >= N || (soft_pos >= 0 && !part))
     return hipErrorInvalidValue;
+  const int n = L * Hkv;
+  uint32_t *kb = (uint32_t *)knmax, *vb = (uint32_t *)vscale;
+  hipLaunchKernelGGL(k_pf_bounds_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, kb, vb, n);
   const dim3 grid((unsigned)(Np / kPfTile), (unsigned)Hkv, (unsigned)L);
   if (elem_bytes == 2)
     hipLaunchKernelGGL(k_prefill_ctx<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)tk, (const uint16_t *)tv,
-                       tok, N, Np, soft_pos, part, L, Hq * d, Hkv, d, vocab, (uint16_t *)nk, (uint16_t *)nvt);
+                       tok, N, Np, soft_pos, part, L, Hq * d, Hkv, d, vocab, (uint16_t *)nk, (uint16_t *)nvt, kb, vb);
   else
     hipLaunchKernelGGL(k_prefill_ctx<float>, grid, dim3(256), 0, st, (const float *)tk, (const float *)tv, tok, N,
-                       Np, soft_pos, part, L, Hq * d, Hkv, d, vocab, (float *)nk, (float *)nvt);
+                       Np, soft_pos, part, L, Hq * d, Hkv, d, vocab, (float *)nk, (float *)nvt, kb, vb);
+  hipLaunchKernelGGL(k_pf_bounds_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, knmax, vscale, n);
   return hipGetLastError();
 }
 
