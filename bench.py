@@ -359,7 +359,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=None, help="workload name (default: the ctx-5000 beam-256 headline)")
-    ap.add_argument("--cpu-beams", type=int, default=16)
+    ap.add_argument("--cpu-beams", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other two workloads (64 x ctx 2000 beam 30; ragged 128 in four waves)")
