@@ -42,9 +42,12 @@
  *     of a call is enqueued on it; an engine must be used from one host thread
  *     and one stream at a time.
  *   - The caller owns every buffer it passes, including the workspace; the
- *     engine sub-allocates the workspace and never calls hipMalloc/hipFree.
- *     The only allocation the engine makes itself is a small ring of pinned
- *     host buffers for per-step work descriptors (at bind time).
+ *     engine sub-allocates the workspace.  Its own allocations are a small ring
+ *     of pinned host buffers for per-step work descriptors (at bind time), the
+ *     prefill staging of gr_engine_set_prefill (a pinned token buffer, grown by
+ *     gr_ctx_prefill when a longer context comes, and a small device area for
+ *     the soft token), and a scheduler's pinned result buffers (gr_sched_create).
+ *     No decode-step call allocates.
  */
 #ifndef GR_BEAM_H
 #define GR_BEAM_H
@@ -180,7 +183,8 @@ gr_status gr_ctx_kv_load(gr_engine *eng, int64_t request_id, int32_t ctx_len, in
  * token has no table row: its embedding e = u * proj (u: user vector [user_dim], proj:
  * [user_dim][embed_dim]) is projected per layer, q = e * w_q[l], k = e * w_k[l],
  * v = e * w_v[l] (head-major columns hq*d + i), in float32, then rounded to the model dtype
- * (round to nearest even).  Tables are device memory that must stay valid while the engine
+ * (round to nearest even).  Tables are device memory (tok_k and tok_v 16-byte aligned)
+ * that must stay valid while the engine
  * uses them.  Limits: vocab >= 1; user_dim = 0 (no soft token) or 1..8192 with embed_dim
  * 1..8192 and every projection pointer set. */
 typedef struct {
