@@ -185,7 +185,57 @@ def test_prefill_argument_checks():
         with pytest.raises(sib.GrError) as ei:
             eng.prefill(1, **args)
         assert ei.value.status == sib._lib.GR_E_INVALID_ARG, kw
+    kn, vn, _ = _native(cfg, 300)
+    with pytest.raises(sib.GrError) as ei:                   # one native buffer without the other
+        eng.prefill(1, toks, 8, k_native=kn)
+    assert ei.value.status == sib._lib.GR_E_INVALID_ARG
     eng.prefill(1, toks, 8)
     with pytest.raises(sib.GrError):                          # id already loaded
         eng.prefill(1, toks, 8)
+    with pytest.raises(sib.GrError) as ei:                   # the pool holds one 300-token context
+        eng.prefill(2, toks, 8)
+    assert ei.value.status == sib._lib.GR_E_OUT_OF_MEMORY
+    eng.prefill(2, toks, 8, k_native=kn, vt_native=vn)       # caller buffers need no pool
+    eng.release(1)
+    eng.release(2)
+    eng.prefill(3, toks, 8)                                   # the released space is reused
+    eng.close()
+
+
+def test_prefill_full_size_sampled():
+    """The headline shapes in the launch configuration the bench times (28 layers, 16/8
+    heads of 128, a 5000-token context, the soft token first, user vector 256 -> embedding
+    2048; vocabulary 4,096 here to keep the host tables small): sampled positions against the
+    oracle, which computes a position from its own token alone, so it is given the sampled
+    tokens' table rows only."""
+    import torch
+    cfg = synth.get_config("ctx5k_beam256_r8")
+    vocab, du, de = 4096, 256, 2048
+    N = synth.request_shapes(cfg)[0][0]
+    tabs = synth.prefill_tables(cfg, vocab)
+    soft = synth.soft_token_weights(cfg, du, de)
+    eng = make_engine(cfg, max_requests=1)
+    eng.set_prefill(*tabs, *soft)
+    toks = synth.prefill_tokens(cfg, 0, vocab)
+    u = synth.user_vector(cfg, 0, du)
+    kn, vn, qo = _native(cfg, N)
+    eng.prefill(0, toks, 256, soft_pos=0, user_vec=torch.from_numpy(u).cuda(), k_native=kn, vt_native=vn,
+                q_last_out=qo)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    pos = np.unique(np.concatenate([[0, 1, 63, 64, 2047, 2048, N - 1], rng.integers(1, N, 25)]))
+    uniq, inv = np.unique(toks[pos[1:]], return_inverse=True)
+    sub = [t[:, uniq] for t in tabs]
+    # position 0 is the soft token; the rest are the sampled tokens, in order
+    K, V, q = oracle.prefill_context(*sub, np.concatenate([[0], inv]), 0, u, *soft)
+    Kd = _to_f64(kn[:, :, torch.from_numpy(pos).cuda(), :].permute(0, 2, 1, 3).contiguous())
+    Vd = _to_f64(vn[:, :, :, torch.from_numpy(pos).cuda()].permute(0, 3, 1, 2).contiguous())
+    np.testing.assert_array_equal(Kd[:, 1:], K[:, 1:])
+    np.testing.assert_array_equal(Vd[:, 1:], V[:, 1:])
+    _check_soft(Kd[:, 0], K[:, 0], _soft_bound(u, soft, cfg, "k"), "bf16")
+    _check_soft(Vd[:, 0], V[:, 0], _soft_bound(u, soft, cfg, "v"), "bf16")
+    np.testing.assert_array_equal(_to_f64(qo), q)      # the last position is a token
+    Np = kn.shape[2]
+    assert not kn[:, :, N:, :].float().abs().sum().item() and not vn[:, :, :, N:].float().abs().sum().item()
+    assert Np == 5056
     eng.close()
