@@ -573,17 +573,19 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
                                                 e->pf.w_v, L, Hq * d, Hkv * d, e->pf_soft, part, st),
                        "soft token")) != GR_OK)
       return q;
-    // the context in the native layout, with its key-norm bounds and value scales
-    if ((q = check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, e->pf_tok_dev, N, Np, soft_pos,
-                                                 part, L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
-                                                 const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
-                                                 (float *)(sb + e->sl.vscale), st),
-                       "prefill")) != GR_OK)
-      return q;
+    // the last query first: its launch also clears the maxima the context launch folds into
     const int last = (soft_pos == N - 1) ? -1 : tokens[N - 1];
-    return check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, last, part, L, Hq, Hkv, d, e->pf.vocab,
-                                             sb + e->sl.q_last, q_out, st),
-                     "prefill query");
+    if ((q = check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, last, part, L, Hq, Hkv, d, e->pf.vocab,
+                                               sb + e->sl.q_last, q_out, (float *)(sb + e->sl.knmax),
+                                               (float *)(sb + e->sl.vscale), st),
+                       "prefill query")) != GR_OK)
+      return q;
+    // the context in the native layout, with its key-norm bounds and value scales
+    return check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, e->pf_tok_dev, N, Np, soft_pos,
+                                               part, L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
+                                               const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
+                                               (float *)(sb + e->sl.vscale), st),
+                     "prefill");
   };
   if ((r = run()) != GR_OK) {
     if (!R.adopt) pool_free(e, R.pool_off, Np);

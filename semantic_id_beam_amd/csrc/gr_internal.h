@@ -138,15 +138,17 @@ hipError_t launch_soft_token(const float *u, const float *proj, int du, int de, 
                              const float *wv, int L, int cq, int ckv, float *e_buf, float *part, hipStream_t st);
 // Context K, V of tokens tok device [N] (table rows of tk / tv [L][vocab][Hkv][d]; position
 // soft_pos from part) written in the native layout nk [L][Hkv][Np][d], nvt [L][Hkv][d][Np],
-// padding zero, with knmax / vscale [L][Hkv] as launch_load_ctx computes them.  Token ids
-// must be in [0, vocab) (checked by the caller).
+// padding zero, with knmax / vscale [L][Hkv] as launch_load_ctx computes them; it must follow
+// launch_prefill_q on the same stream (which clears the maxima).  Token ids must be in
+// [0, vocab) (checked by the caller).
 hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, const int32_t *tok, int N, int Np,
                               int soft_pos, const float *part, int L, int Hq, int Hkv, int d, int vocab, void *nk,
                               void *nvt, float *knmax, float *vscale, hipStream_t st);
 // Query of the last position, [L][Hq][d]: row last_tok of tq [L][vocab][Hq][d], or the soft
-// token's q (last_tok < 0), into q_slot and (if set) q_out.
+// token's q (last_tok < 0), into q_slot and (if set) q_out; clears knmax / vscale [L][Hkv]
+// for the launch_prefill_ctx that follows.
 hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const float *part, int L, int Hq, int Hkv,
-                            int d, int vocab, void *q_slot, void *q_out, hipStream_t st);
+                            int d, int vocab, void *q_slot, void *q_out, float *knmax, float *vscale, hipStream_t st);
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
 

@@ -15,7 +15,8 @@
 //   k_prefill_ctx   table rows (or the soft row, rounded to the model dtype) into the
 //                   native layout: K rows copied as 16-byte chunks, V transposed through
 //                   LDS; padding tokens zero; the key-norm and |v| maxima of each (layer,
-//                   kv head) folded in (k_pf_bounds_init / k_pf_bounds_finish around it)
+//                   kv head) folded in (cleared by k_prefill_q before it, turned into the
+//                   bounds by k_pf_bounds_finish after it)
 //   k_prefill_q     the last position's query into the request's slot
 //
 // All of it is HBM-bound gather and GEMV work: no matrix cores.
@@ -114,14 +115,6 @@ __device__ inline float chunk_f32(const uint4 &x, int e) {
   return __uint_as_float(w);
 }
 
-__global__ void k_pf_bounds_init(uint32_t *kn_bits, uint32_t *vm_bits, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) {
-    kn_bits[i] = 0u;
-    vm_bits[i] = 0u;
-  }
-}
-
 // In place, per (layer, kv head): kn = sqrt(largest squared key norm), vs = 2^e with
 // max|v| < 2^e (max|v| = m 2^e, m in [0.5, 1)), kept a normal float.  The decode's fixed
 // softmax reference and value scaling read these; they are the same as a load computes.
@@ -215,12 +208,18 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(const T *__restrict__ tk, c
   }
 }
 
+// Also clears the key-norm / |v| maxima that k_prefill_ctx (launched after it) folds into.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prefill_q(const T *__restrict__ tq, int last_tok,
                                                    const float *__restrict__ part, int L, int Hq, int Hkv, int d,
-                                                   int vocab, T *__restrict__ q_slot, T *__restrict__ q_out) {
+                                                   int vocab, T *__restrict__ q_slot, T *__restrict__ q_out,
+                                                   uint32_t *__restrict__ kn_bits, uint32_t *__restrict__ vm_bits) {
   const int cq = Hq * d, ct = cq + 2 * Hkv * d;
   const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < L * Hkv) {
+    kn_bits[i] = 0u;
+    vm_bits[i] = 0u;
+  }
   if (i >= L * cq) return;
   const int l = i / cq, c = i - l * cq;
   const T v = last_tok >= 0 ? tq[((size_t)l * vocab + (size_t)last_tok) * cq + c]
@@ -250,7 +249,6 @@ hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, co
     return hipErrorInvalidValue;
   const int n = L * Hkv;
   uint32_t *kb = (uint32_t *)knmax, *vb = (uint32_t *)vscale;
-  hipLaunchKernelGGL(k_pf_bounds_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, kb, vb, n);
   const dim3 grid((unsigned)(Np / kPfTile), (unsigned)Hkv, (unsigned)L);
   if (elem_bytes == 2)
     hipLaunchKernelGGL(k_prefill_ctx<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)tk, (const uint16_t *)tv,
@@ -263,15 +261,17 @@ hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, co
 }
 
 hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const float *part, int L, int Hq, int Hkv,
-                            int d, int vocab, void *q_slot, void *q_out, hipStream_t st) {
-  if (last_tok >= vocab || (last_tok < 0 && !part) || (elem_bytes != 2 && elem_bytes != 4)) return hipErrorInvalidValue;
+                            int d, int vocab, void *q_slot, void *q_out, float *knmax, float *vscale, hipStream_t st) {
+  if (last_tok >= vocab || (last_tok < 0 && !part) || (elem_bytes != 2 && elem_bytes != 4) || Hkv > Hq * d)
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((size_t)L * Hq * d + 255) / 256));
+  uint32_t *kb = (uint32_t *)knmax, *vb = (uint32_t *)vscale;
   if (elem_bytes == 2)
     hipLaunchKernelGGL(k_prefill_q<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)tq, last_tok, part, L, Hq,
-                       Hkv, d, vocab, (uint16_t *)q_slot, (uint16_t *)q_out);
+                       Hkv, d, vocab, (uint16_t *)q_slot, (uint16_t *)q_out, kb, vb);
   else
     hipLaunchKernelGGL(k_prefill_q<float>, grid, dim3(256), 0, st, (const float *)tq, last_tok, part, L, Hq, Hkv, d,
-                       vocab, (float *)q_slot, (float *)q_out);
+                       vocab, (float *)q_slot, (float *)q_out, kb, vb);
   return hipGetLastError();
 }
 

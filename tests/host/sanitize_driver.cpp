@@ -35,7 +35,8 @@ GR_STUB(launch_soft_token, const float *, const float *, int, int, const float *
         int, int, float *, float *, hipStream_t)
 GR_STUB(launch_prefill_ctx, int, const void *, const void *, const int32_t *, int, int, int, const float *, int, int,
         int, int, int, void *, void *, float *, float *, hipStream_t)
-GR_STUB(launch_prefill_q, int, const void *, int, const float *, int, int, int, int, int, void *, void *, hipStream_t)
+GR_STUB(launch_prefill_q, int, const void *, int, const float *, int, int, int, int, int, void *, void *, float *,
+        float *, hipStream_t)
 #undef GR_STUB
 }  // namespace gr
 
