@@ -30,15 +30,17 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # HBM bytes per layer of the context-attention kernels on this workload, from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
 # the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000), and
-# divided by the layers one dispatch covers (14 for the wide kernel here, all 28 for the
-# first-level launch); profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel
-# code they were taken on (source_digest of gr_kernels.hip: comments excluded); with any
-# other code the traffic is reported as null.
+# divided by the layers one dispatch covers (one with one layer per launch; 14 for the wide
+# kernel and all 28 for the first-level launch of the multi-layer variant);
+# profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel code they were taken on
+# (source_digest of gr_kernels.hip: comments excluded); with any other code, or a variant not
+# measured, the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
     "source_sha256": "f1d6bdc3eb22b130a9eb529ffe81b5297ef79a44b9b0e97c9e9e01fecf4fc08a",
-    "k_ctx_attn_wide": {"read": 181454927, "written": 21535287},
-    "k_ctx_attn_stream": {"read": 166624539, "written": 278601},
+    "fused": {"k_ctx_attn_wide": {"read": 181454927, "written": 21535287},
+              "k_ctx_attn_stream": {"read": 166624539, "written": 278601}},
+    "per_layer": {},
 }
 
 
@@ -56,12 +58,12 @@ def source_digest(path):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def measured_traffic(cfg, kernel):
+def measured_traffic(cfg, kernel, variant):
     src = os.path.join(ROOT, "semantic_id_beam_amd", "csrc", "gr_kernels.hip")
     if cfg.name != MEASURED_TRAFFIC["workload"] or source_digest(src) != MEASURED_TRAFFIC["source_sha256"]:
         return None
-    t = MEASURED_TRAFFIC[kernel]
-    return t["read"] + t["written"]
+    t = MEASURED_TRAFFIC.get(variant, {}).get(kernel)
+    return None if t is None else t["read"] + t["written"]
 
 
 def log(*a):
@@ -77,7 +79,7 @@ def workload_text(cfg, shapes):
             f"{cfg.n_q_heads} q / {cfg.n_kv_heads} kv heads, head_dim {cfg.head_dim}, {cfg.dtype}")
 
 
-def scoring_leg(cfg, args):
+def scoring_leg(cfg, args, per_layer=True):
     """Candidate scoring on the same contexts: 500 given items per request per call (the pages'
     scoring workload), items of the set drawn with repeats; every request of the workload in
     one call (gr_score_items_batch), calls timed end to end (each call synchronises)."""
@@ -85,10 +87,10 @@ def scoring_leg(cfg, args):
     import torch
 
     import synth
-    from tests.engine_inputs import make_engine, request_tensors
+    from semantic_id_beam_amd.workloads import make_engine, request_tensors
     n_cand, n_calls = 500, max(4, args.steps // 2)
     R = cfg.n_requests
-    eng = make_engine(cfg, max_requests=R, max_beam_width=512)
+    eng = make_engine(cfg, max_requests=R, max_beam_width=512, per_layer=per_layer)
     for r in range(R):
         k, v, q = request_tensors(cfg, r)
         eng.load(r, k, v, q, synth.request_shapes(cfg)[r][1])
@@ -124,7 +126,7 @@ def prefill_leg(cfg, args, vocab: int = 32768, user_dim: int = 256, embed_dim: i
 
     import synth
     from semantic_id_beam_amd import _lib as G
-    from tests.engine_inputs import make_engine
+    from semantic_id_beam_amd.workloads import make_engine
     R, L, Hq, Hkv, d = cfg.n_requests, cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     shapes = synth.request_shapes(cfg)
     g = torch.Generator(device="cuda")
@@ -167,7 +169,7 @@ def prefill_leg(cfg, args, vocab: int = 32768, user_dim: int = 256, embed_dim: i
             "achieved_GBs_no_soft": round(ctx_b / (res[-1] * 1e-3) / 1e9, 1)}
 
 
-def workload_leg(name: str, reps: int = 3):
+def workload_leg(name: str, reps: int = 3, per_layer: bool = True):
     """Another workload of the decode step, its requests admitted as the workload prescribes
     (all at once, or in admission waves interleaved with the earlier waves' steps).  The first
     pass loads the contexts (loads timed apart with events); the timed passes replay the same
@@ -177,14 +179,14 @@ def workload_leg(name: str, reps: int = 3):
     import torch
 
     import synth
-    from tests.engine_inputs import make_engine, request_tensors
+    from semantic_id_beam_amd.workloads import make_engine, request_tensors
     cfg = synth.get_config(name)
     shapes = synth.request_shapes(cfg)
     R, lv = cfg.n_requests, cfg.n_levels
     waves = getattr(cfg, "waves", 0) or 1
     per = R // waves
     schedule = [list(range(w * per, (w + 1) * per)) for w in range(waves)]
-    eng = make_engine(cfg, max_requests=R)
+    eng = make_engine(cfg, max_requests=R, per_layer=per_layer)
     load_ms = [0.0]
     batch_sizes = []
 
@@ -242,7 +244,7 @@ def workload_leg(name: str, reps: int = 3):
 
 
 def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 4000, 5000, 6000),
-                n_req: int = 1000, max_active: int = 64, seed: int = 0):
+                n_req: int = 1000, max_active: int = 64, seed: int = 0, per_layer: bool = True):
     """Latency against offered load through the continuous-batching scheduler (gr_sched_*):
     Poisson arrivals at each offered rate, n_req requests per rate, at most max_active decoding
     at once, the way the paper-daily TensorRT-LLM summary reads its beam-search chart
@@ -257,7 +259,7 @@ def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 40
 
     import semantic_id_beam_amd as sib
     import synth
-    from tests.engine_inputs import make_engine, native_layout, request_tensors
+    from semantic_id_beam_amd.workloads import make_engine, native_layout, request_tensors
     cfg = synth.get_config(name)
     shapes = synth.request_shapes(cfg)
     tens = []
@@ -266,7 +268,7 @@ def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 40
         kn, vn, _ = native_layout(k, v)
         del k, v
         tens.append((kn, vn, q))
-    eng = make_engine(cfg, max_requests=max_active + 2, max_ctx_tokens=0)
+    eng = make_engine(cfg, max_requests=max_active + 2, max_ctx_tokens=0, per_layer=per_layer)
     torch.cuda.synchronize()
     points, base = [], 0
     for lam in rates:
@@ -315,7 +317,7 @@ def cpu_baseline(cfg, n_beams: int):
     from threadpoolctl import threadpool_info
 
     import oracle
-    from tests.oracle_inputs import model_for, prefixes_for, request_for
+    from oracle.inputs import model_for, prefixes_for, request_for
 
     model, ps = model_for(cfg), prefixes_for(cfg)
     req = request_for(cfg, 0)
@@ -353,50 +355,22 @@ def cpu_baseline(cfg, n_beams: int):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default=None, help="workload name (default: the ctx-5000 beam-256 headline)")
-    ap.add_argument("--cpu-beams", type=int, default=64)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-workloads", action="store_true",
-                    help="skip the other two workloads (64 x ctx 2000 beam 30; ragged 128 in four waves)")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
-    args = ap.parse_args()
-    if args.copy_probe:
-        import torch
-        n = args.copy_probe << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n}))
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode step shards by request with no exchange; see the design notes)", file=sys.stderr)
-        sys.exit(2)
-
+def decode_leg(cfg, args, per_layer: bool):
+    """The timed decode of the workload's requests (contexts resident), with per-kernel times
+    from HIP events carried by the dispatches on the decode stream."""
     import numpy as np
     import torch
 
     import synth
-    from synth.configs import HEADLINE
     from semantic_id_beam_amd import _lib as G
-    from tests.engine_inputs import make_engine, request_tensors
+    from semantic_id_beam_amd.workloads import make_engine, request_tensors
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = synth.get_config(args.config or HEADLINE)
     shapes = synth.request_shapes(cfg)
     R, lv = cfg.n_requests, cfg.n_levels
-    log("workload", workload_text(cfg, shapes))
     t = time.time()
-    eng = make_engine(cfg, max_requests=R)
-    log(f"engine ready ({eng.ws_bytes / 2**30:.2f} GiB workspace, {time.time() - t:.1f} s)")
+    eng = make_engine(cfg, max_requests=R, per_layer=per_layer)
+    log(f"engine ready ({'one layer per launch' if per_layer else 'several layers per launch'}, "
+        f"{eng.ws_bytes / 2**30:.2f} GiB workspace, {time.time() - t:.1f} s)")
     rids = list(range(R))
     t = time.time()
     # contexts are generated in HBM eight at a time; the loads (re-layout, key-norm bounds,
@@ -472,7 +446,7 @@ def main():
     N = np.array([n for n, _ in shapes], dtype=np.float64)
     el = 2 if cfg.dtype == "bf16" else 4
 
-    def ctx_flops(s):      # one launch = one layer, all requests
+    def ctx_flops(s):      # one layer, all requests
         return float(np.sum(Hkv * n_live[:, s] * g * N * d * 4))
 
     def ctx_bytes(s):      # K and V read once, queries read, one fp32 output row per (beam, head)
@@ -487,17 +461,18 @@ def main():
     achieved_gbs0 = ctx_bytes(0) * n_0 / (ms_0 * 1e-3) / 1e9 if ms_0 > 0 else 0.0
     step_us = {f"level{s}": 1e3 * prof["step"][s][0] / max(prof["step"][s][1], 1) for s in range(lv)}
 
-    # the unit is one layer of one step over every request: a dispatch covers one or more of them
-    # (14 per dispatch for the wide kernel on the headline workload).  The kernel also finishes
-    # each layer (beam tokens, BeamKV append, h += o): that time is in the denominator, those
-    # bytes are not in the algorithmic count.
+    # the unit is one layer of one step over every request: a dispatch covers one layer (one layer
+    # per launch) or several.  The kernel also finishes a layer (beam tokens, BeamKV append, the
+    # split merge, h += o): that time is in the denominator, those bytes are not in the
+    # algorithmic count.
     wide = cfg.dtype == "bf16" and cfg.head_dim == 128
     d_m = sum(G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, s) for s in levels_mfma)
     d_0 = G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, 0)
+    variant = "per_layer" if per_layer else "fused"
     roofline = {
         "bound": "mfma", "achieved": round(achieved_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved_tf / PEAK_BF16_TFLOPS, 4),
-        "traffic": measured_traffic(cfg, "k_ctx_attn_wide") if wide else None,
+        "traffic": measured_traffic(cfg, "k_ctx_attn_wide", variant) if wide else None,
         "traffic_unit": "HBM bytes per layer (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
         "kernel": ("k_ctx_attn_wide" if wide else "k_ctx_attn") + " (levels %s)" % levels_mfma,
         "layers": int(n_m),
@@ -512,8 +487,9 @@ def main():
                             "frac": round(achieved_gbs0 / PEAK_HBM_GBS, 4),
                             "avg_us_per_layer": round(1e3 * ms_0 / max(n_0, 1), 2),
                             "avg_us_per_dispatch": round(1e3 * ms_0 / max(d_0, 1), 2),
+                            "dispatches": int(d_0),
                             "algorithmic_MB_per_layer": round(ctx_bytes(0) / 1e6, 2),
-                            "traffic": measured_traffic(cfg, "k_ctx_attn_stream") if wide else None},
+                            "traffic": measured_traffic(cfg, "k_ctx_attn_stream", variant) if wide else None},
     }
     for name in ("beam_merge", "logits", "topk"):
         tot = sum(prof[name][s][0] for s in range(lv))
@@ -526,23 +502,13 @@ def main():
                            "algorithmic_MB_per_request": round(load_bytes / R / 1e6, 1),
                            "achieved_GBs": round(load_bytes / (load_ms * 1e-3) / 1e9, 1),
                            "frac": round(load_bytes / (load_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-
-    out = {
-        "metric": METRIC,
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    return {
         "value": round(R * args.steps / elapsed, 2),
-        "unit": "req/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(1e3 * elapsed / args.steps, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic",
-        "config": {"workload": workload_text(cfg, shapes), "requests": R, "layers": cfg.n_layers,
-                   "ctx_len": cfg.ctx_len, "beam_width": cfg.beam_width, "levels": lv,
-                   "codebook": cfg.codebook, "items": cfg.n_items, "live_beams_per_level": n_live[0].tolist()},
+        "live_beams_per_level": n_live[0].tolist(),
         "step_us": {k: round(v, 1) for k, v in step_us.items()},
         "decode_ms": {"p10": round(float(np.percentile(decode_ms, 10)), 3),
                       "p50": round(float(np.percentile(decode_ms, 50)), 3),
@@ -550,13 +516,90 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
-    eng.close()
-    del eng
-    out["scoring"] = scoring_leg(cfg, args)
-    out["prefill"] = prefill_leg(cfg, args)
-    if not args.no_workloads:
-        out["workloads"] = {w: workload_leg(w) for w in ("ctx2k_beam30_r64", "ragged_r128")}
-        out["serving"] = serving_leg()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=None, help="workload name (default: the ctx-5000 beam-256 headline)")
+    ap.add_argument("--cpu-beams", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other two workloads (64 x ctx 2000 beam 30; ragged 128 in four waves)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the headline decode (one layer per launch): no other legs")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by request with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from synth.configs import HEADLINE
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.get_config(args.config or HEADLINE)
+    shapes = synth.request_shapes(cfg)
+    R, lv = cfg.n_requests, cfg.n_levels
+    log("workload", workload_text(cfg, shapes))
+    # the headline: one context-attention launch per layer at every level (the launch sequence
+    # of a model whose layers depend on each other)
+    head = decode_leg(cfg, args, per_layer=True)
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "req/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload_text(cfg, shapes), "requests": R, "layers": cfg.n_layers,
+                   "ctx_len": cfg.ctx_len, "beam_width": cfg.beam_width, "levels": lv,
+                   "codebook": cfg.codebook, "items": cfg.n_items,
+                   "live_beams_per_level": head["live_beams_per_level"],
+                   "launches": "one context-attention launch per layer at every level"},
+        "step_us": head["step_us"],
+        "decode_ms": head["decode_ms"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+    }
+    if not args.decode_only:
+        # labelled variant, not the headline: where every layer's query is an input (this model
+        # stand-in), the first level runs all layers in one launch and wide levels several
+        fused = decode_leg(cfg, args, per_layer=False)
+        out["fused_layers_variant"] = {
+            "note": ("several layers per context-attention launch (first level: all layers; wide levels: "
+                     "a group of layers): valid only because this model stand-in's layers are independent; "
+                     "not the headline"),
+            **{k: fused[k] for k in ("value", "ms_per_step", "step_us", "decode_ms", "roofline", "kernels")}}
+        out["scoring"] = scoring_leg(cfg, args)
+        out["prefill"] = prefill_leg(cfg, args)
+        if not args.no_workloads:
+            out["workloads"] = {w: workload_leg(w) for w in ("ctx2k_beam30_r64", "ragged_r128")}
+            out["workloads_fused_layers_variant"] = {w: workload_leg(w, per_layer=False)["req_per_s"]
+                                                     for w in ("ctx2k_beam30_r64", "ragged_r128")}
+            out["serving"] = serving_leg()
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_beams} beams ...")
         cb = cpu_baseline(cfg, args.cpu_beams)

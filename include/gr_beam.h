@@ -43,11 +43,12 @@
  *     and one stream at a time.
  *   - The caller owns every buffer it passes, including the workspace; the
  *     engine sub-allocates the workspace.  Its own allocations are a small ring
- *     of pinned host buffers for per-step work descriptors (at bind time), the
- *     prefill staging of gr_engine_set_prefill (a pinned token buffer, grown by
- *     gr_ctx_prefill when a longer context comes, and a small device area for
- *     the soft token), and a scheduler's pinned result buffers (gr_sched_create).
- *     No decode-step call allocates.
+ *     of pinned host buffers for per-step work descriptors, timing and ordering
+ *     events and three auxiliary streams (all at bind time), the prefill staging
+ *     of gr_engine_set_prefill (a pinned token buffer, grown by gr_ctx_prefill
+ *     when a longer context comes, and a small device area for the soft token),
+ *     and a scheduler's pinned result buffers (gr_sched_create).  No decode-step
+ *     call allocates.
  */
 #ifndef GR_BEAM_H
 #define GR_BEAM_H
@@ -104,6 +105,13 @@ typedef struct {
 } gr_item_set;
 
 #define GR_ENGINE_DEBUG_ATTN 1u /* keep every layer's attention output for gr_debug_attn_out */
+/* One context-attention launch per layer at every level, the launch sequence of a model whose
+ * layer l+1 reads layer l's output: no launch covers two layers (the first level included).  A
+ * layer whose row blocks fill the chip runs each block over the whole context; otherwise the
+ * context is split into token ranges whose partials the next layer's launch merges.  Without
+ * this flag the engine may run several layers in one launch where every layer's query is an
+ * input (the model stand-in above). */
+#define GR_ENGINE_PER_LAYER 2u
 
 typedef struct {
   int32_t max_requests;   /* requests loaded at once (slots), >= 1 */
@@ -113,10 +121,11 @@ typedef struct {
                              0 = only GR_LOAD_ADOPT loads */
   int32_t max_splits;     /* split-K partial slots per (request, kv head) at full beam width
                              (narrower steps may use proportionally more); 0 = 4 */
-  uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN */
+  uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN | GR_ENGINE_PER_LAYER */
   int32_t max_layers_per_launch; /* full-context steps: at most this many layers per
                              context-attention launch; 0 = automatic (about seven rounds of
-                             workgroups per launch, layers split evenly over the launches) */
+                             workgroups per launch, layers split evenly over the launches);
+                             GR_ENGINE_PER_LAYER forces 1 */
 } gr_engine_opts;
 
 /* ---- engine lifetime ------------------------------------------------------ */

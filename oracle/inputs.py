@@ -1,0 +1,40 @@
+"""The oracle's view of the seeded synthetic workloads (test infrastructure only).
+
+Builds the float64 model, the valid-prefix sets and per-request contexts from the input
+generators in `synth` (the only module the oracle and the HIP path both use)."""
+from __future__ import annotations
+
+import functools
+
+from . import beam
+from .beam import Model, PrefixSet, Request
+
+
+@functools.lru_cache(maxsize=8)
+def model_for(cfg) -> Model:
+    import synth
+    tq, tk, tv = synth.token_tables(cfg)
+    return Model.from_arrays(tq, tk, tv, synth.w_sid(cfg))
+
+
+@functools.lru_cache(maxsize=8)
+def prefixes_for(cfg) -> PrefixSet:
+    import synth
+    return PrefixSet(synth.items(cfg), cfg.codebook)
+
+
+def request_for(cfg, r: int, cache: bool = True) -> Request:
+    """The oracle's view of request r; context blocks are regenerated per layer on demand."""
+    import synth
+    store = {}
+
+    def ctx(l):
+        if cache and l in store:
+            return store[l]
+        k, v = synth.ctx_kv_block(cfg, r, l)
+        kv = (beam.as_f64(k), beam.as_f64(v))
+        if cache:
+            store[l] = kv
+        return kv
+
+    return Request(ctx=ctx, q_last=beam.as_f64(synth.q_last(cfg, r)))

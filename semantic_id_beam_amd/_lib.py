@@ -20,6 +20,7 @@ GR_OK, GR_E_INVALID_ARG, GR_E_OUT_OF_MEMORY, GR_E_BAD_STATE, GR_E_NOT_FOUND, GR_
 GR_DTYPE_F32, GR_DTYPE_BF16 = 0, 1
 GR_NORM_VALID, GR_NORM_FULL = 0, 1
 GR_ENGINE_DEBUG_ATTN = 1
+GR_ENGINE_PER_LAYER = 2
 GR_LOAD_ADOPT = 1
 
 STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "GR_E_BAD_STATE",

@@ -91,7 +91,7 @@ struct gr_engine {
 
   // split-K steps with several variant groups: each group's chain of layer launches depends
   // only on itself, so groups 1..3 (mod 4) run on their own streams, forked from and joined
-  // into the caller's stream (default priority, created at the first such step)
+  // into the caller's stream (default priority, created when the workspace is bound)
   hipStream_t aux[kAuxStreams] = {};
   hipEvent_t fork_ev = nullptr, join_ev[kAuxStreams] = {};
   std::vector<gr::StepReq *> pinned;
@@ -354,6 +354,7 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   if (o->max_ctx_tokens < 0) return fail(GR_E_INVALID_ARG, "max_ctx_tokens < 0");
   if (o->max_splits < 0 || o->max_splits > 64) return fail(GR_E_INVALID_ARG, "max_splits must be in [0, 64]");
   if (o->max_layers_per_launch < 0) return fail(GR_E_INVALID_ARG, "max_layers_per_launch must be >= 0");
+  if (o->flags & ~(GR_ENGINE_DEBUG_ATTN | GR_ENGINE_PER_LAYER)) return fail(GR_E_INVALID_ARG, "unknown engine flag");
 
   gr_engine *e = new gr_engine();
   e->model = *m;
@@ -427,6 +428,15 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
   e->prof_ev.assign(kProfPool, nullptr);
   for (auto &ev : e->prof_ev)
     if ((r = check_dev(e, hipEventCreate(&ev), "event")) != GR_OK) return r;
+  // streams (default priority) and fork/join events for steps with several variant groups
+  for (int i = 0; i < kAuxStreams; ++i) {
+    if ((r = check_dev(e, hipStreamCreateWithFlags(&e->aux[i], hipStreamNonBlocking), "stream create")) != GR_OK)
+      return r;
+    if ((r = check_dev(e, hipEventCreateWithFlags(&e->join_ev[i], hipEventDisableTiming), "event create")) != GR_OK)
+      return r;
+  }
+  if ((r = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
+    return r;
   gr::Dev &dv = e->dev;
   dv.dm = e->dm;
   dv.sl = e->sl;
@@ -481,20 +491,25 @@ gr_status gr_engine_set_prefill(gr_engine *e, const gr_prefill_desc *p) {
   gr_status r;
   if (!e->pf_ev && (r = check_dev(e, hipEventCreateWithFlags(&e->pf_ev, hipEventDisableTiming), "event")) != GR_OK)
     return r;
-  if (e->pf_soft) {
-    if ((r = check_dev(e, hipDeviceSynchronize(), "sync")) != GR_OK) return r;
-    (void)hipFree(e->pf_soft);
-    e->pf_soft = nullptr;
-  }
+  // the new soft-token staging first: on failure the engine keeps its previous tables and
+  // staging, which stay consistent with each other
+  float *soft = nullptr;
   if (p->user_dim > 0) {
     const size_t ct = (size_t)(e->dm.Hq + 2 * e->dm.Hkv) * e->dm.d;
     const size_t n = (size_t)gr::kSoftSplit * (p->embed_dim + e->dm.L * ct);
-    if (hipMalloc((void **)&e->pf_soft, n * sizeof(float)) != hipSuccess) {
-      e->pf_soft = nullptr;
+    if (hipMalloc((void **)&soft, n * sizeof(float)) != hipSuccess) {
       (void)hipGetLastError();
       return fail(GR_E_OUT_OF_MEMORY, "soft-token staging");
     }
   }
+  if (e->pf_soft) {
+    if ((r = check_dev(e, hipDeviceSynchronize(), "sync")) != GR_OK) {
+      if (soft) (void)hipFree(soft);
+      return r;
+    }
+    (void)hipFree(e->pf_soft);
+  }
+  e->pf_soft = soft;
   e->pf = *p;
   e->has_pf = true;
   return GR_OK;
@@ -714,7 +729,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   // A first-level step (every request at level 0) runs all layers' context attention in one
   // launch: each layer's query is an input there.  Needs room for every layer's partials in
   // one partial buffer and for the per-layer outputs in the other.
-  bool first_fused = d.dtype == 1 && d.d == 128 && d.L > 1 && (int64_t)d.L <= (int64_t)d.S_max * d.W_max;
+  const bool per_layer = (e->opts.flags & GR_ENGINE_PER_LAYER) != 0;  // no launch covers two layers
+  bool first_fused = !per_layer && d.dtype == 1 && d.d == 128 && d.L > 1 && (int64_t)d.L <= (int64_t)d.S_max * d.W_max;
   for (int i = 0; i < n && first_fused; ++i) first_fused = rs[(size_t)i]->level == 0;
   std::vector<int> kind((size_t)n);
   for (int i = 0; i < n; ++i)
@@ -725,7 +741,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   // and the partials are summed into h at the end.  Wide requests run on the 8-wave kernel;
   // every narrower one (level-0 beams included) on the two-wave stream kernel in 64-row
   // blocks, so a step that mixes levels (continuous batching) stays on this path.
-  const int lg_max = std::min(d.L, d.S_max);
+  const int lg_max = per_layer ? 1 : std::min(d.L, d.S_max);
   auto full_ctx_kind = [](int k) { return (k & 0xFF) == 8 ? k : (2 | gr::kCtxHiLo); };
   bool layered = d.dtype == 1 && d.d == 128 && !first_fused;
   double fill = 0.0;  // resident-workgroup rounds the step's row blocks fill over lg_max layers
@@ -781,6 +797,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       int64_t target =
           std::min<int64_t>(d.L, std::max<int64_t>(1, (7 * want + units - 1) / std::max<int64_t>(units, 1)));
       if (e->opts.max_layers_per_launch > 0) target = std::min<int64_t>(target, e->opts.max_layers_per_launch);
+      if (per_layer) target = 1;
       const int64_t launches = (d.L + target - 1) / target;
       lgroups = (int)((d.L + launches - 1) / launches);
       G.lgroups = lgroups;
@@ -865,16 +882,6 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   auto group_stream = [&](size_t gi) { return gi % (kAuxStreams + 1) == 0 ? st : e->aux[gi % (kAuxStreams + 1) - 1]; };
   auto fork = [&]() -> gr_status {
     gr_status q;
-    if (!e->fork_ev) {
-      for (int i = 0; i < kAuxStreams; ++i) {
-        if ((q = check_dev(e, hipStreamCreateWithFlags(&e->aux[i], hipStreamNonBlocking), "stream create")) != GR_OK)
-          return q;
-        if ((q = check_dev(e, hipEventCreateWithFlags(&e->join_ev[i], hipEventDisableTiming), "event create")) != GR_OK)
-          return q;
-      }
-      if ((q = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
-        return q;
-    }
     if ((q = check_dev(e, hipEventRecord(e->fork_ev, st), "stream fork")) != GR_OK) return q;
     for (int i = 0; i + 1 < nstreams; ++i)
       if ((q = check_dev(e, hipStreamWaitEvent(e->aux[i], e->fork_ev, 0), "stream fork")) != GR_OK) return q;

@@ -233,6 +233,7 @@ __global__ __launch_bounds__(256) void k_prefill_q(const T *__restrict__ tq, int
 hipError_t launch_soft_token(const float *u, const float *proj, int du, int de, const float *wq, const float *wk,
                              const float *wv, int L, int cq, int ckv, float *e_buf, float *part, hipStream_t st) {
   if (du < 1 || de < 1 || de > kMaxEmbed || L < 1 || cq < 1 || ckv < 1) return hipErrorInvalidValue;
+  if (!u || !proj || !wq || !wk || !wv || !e_buf || !part) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_soft_embed, dim3((unsigned)((de + 255) / 256), kSoftSplit), dim3(256), 0, st, u, proj, du, de,
                      e_buf);
   const int ct = cq + 2 * ckv;

@@ -33,7 +33,8 @@ class BeamEngine:
     def __init__(self, *, tok_q, tok_k, tok_v, w_sid, items, n_layers: int, n_q_heads: int, n_kv_heads: int,
                  head_dim: int, dtype: str = "bf16", norm: str = "valid", max_requests: int = 1,
                  max_beam_width: int = 256, max_ctx_tokens: int = 0, max_splits: int = 0,
-                 debug_attn: bool = False, max_layers_per_launch: int = 0, device="cuda"):
+                 debug_attn: bool = False, max_layers_per_launch: int = 0, per_layer: bool = False,
+                 device="cuda"):
         torch = _torch()
         self.device = device
         self.dtype = dtype
@@ -48,7 +49,8 @@ class BeamEngine:
                                self.tok_q.data_ptr(), self.tok_k.data_ptr(), self.tok_v.data_ptr(),
                                self.w_sid.data_ptr())
         opts = G.gr_engine_opts(max_requests, max_beam_width, max_ctx_tokens, max_splits,
-                                G.GR_ENGINE_DEBUG_ATTN if debug_attn else 0, max_layers_per_launch)
+                                (G.GR_ENGINE_DEBUG_ATTN if debug_attn else 0) |
+                                (G.GR_ENGINE_PER_LAYER if per_layer else 0), max_layers_per_launch)
         self.max_beam_width = max_beam_width
         self.eng = G.gr_engine_create(desc, np.asarray(items), opts)
         self.ws_bytes = G.gr_engine_workspace_bytes(self.eng)

@@ -34,6 +34,12 @@ class Config:
     waves: int = 1                   # admission waves (continuous batching)
     seed: int = 0
     shapes: Tuple[Tuple[int, int], ...] = ()   # explicit (ctx_len, beam_width) per request
+    # exact power-of-two scalings of the drawn values (large query and key norms, as a trained
+    # model's activations have them): queries (q_last and the query table) by 2^q_scale_log2,
+    # context keys by 2^k_scale_log2, the fed-back tokens' keys by 2^own_k_scale_log2
+    q_scale_log2: int = 0
+    k_scale_log2: int = 0
+    own_k_scale_log2: int = 0
     notes: str = field(default="", compare=False)
 
     @property

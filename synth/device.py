@@ -62,4 +62,9 @@ def request_tensors(cfg, r: int, device="cuda"):
         bf16_normal_into(v[l], _key(cfg, _T_CTX_V, r, l))
     q = torch.empty((L, Hq, d), dtype=torch.bfloat16, device=device)
     bf16_normal_into(q, _key(cfg, _T_QLAST, r))
+    # the workload's power-of-two scalings (exact in bf16 for the table's range)
+    if cfg.k_scale_log2:
+        k.mul_(2.0 ** cfg.k_scale_log2)
+    if cfg.q_scale_log2:
+        q.mul_(2.0 ** cfg.q_scale_log2)
     return k, v, q

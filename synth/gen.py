@@ -22,6 +22,23 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def times_pow2(x: np.ndarray, k: int) -> np.ndarray:
+    """x * 2^k exactly: bf16 bit patterns (uint16) or float32.  Raises if a value would leave
+    the exponent range (the product would not be exact)."""
+    if k == 0:
+        return x
+    if x.dtype == np.uint16:
+        f = bf16_bits_to_f32(x) * np.float32(2.0 ** k)
+        out = (f.view(np.uint32) >> 16).astype(np.uint16)
+        if not np.array_equal(bf16_bits_to_f32(out), f):
+            raise ValueError("power-of-two scaling is not exact in bf16")
+        return out
+    out = (x.astype(np.float32) * np.float32(2.0 ** k)).astype(np.float32)
+    if not np.array_equal(out * np.float32(2.0 ** -k), x.astype(np.float32)):
+        raise ValueError("power-of-two scaling is not exact in float32")
+    return out
+
+
 def _make_table() -> np.ndarray:
     u = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
     return _f32_to_bf16_bits(ndtri(u).astype(np.float32))
@@ -112,16 +129,17 @@ def ctx_kv_block(cfg: Config, r: int, l: int):
     shape = (n, cfg.n_kv_heads, cfg.head_dim)
     if cfg.dtype == "f32":
         t = _tiny_all(cfg)
-        return t["ctx_k"][l], t["ctx_v"][l]
-    return (_bf16_normal(_philox(cfg, _T_CTX_K, r, l), shape),
+        return times_pow2(t["ctx_k"][l], cfg.k_scale_log2), t["ctx_v"][l]
+    return (times_pow2(_bf16_normal(_philox(cfg, _T_CTX_K, r, l), shape), cfg.k_scale_log2),
             _bf16_normal(_philox(cfg, _T_CTX_V, r, l), shape))
 
 
 def q_last(cfg: Config, r: int):
     """Query of the last context token, [L][Hq][d] (stands in for the prefill's last query)."""
     if cfg.dtype == "f32":
-        return _tiny_all(cfg)["q_last"]
-    return _bf16_normal(_philox(cfg, _T_QLAST, r), (cfg.n_layers, cfg.n_q_heads, cfg.head_dim))
+        return times_pow2(_tiny_all(cfg)["q_last"], cfg.q_scale_log2)
+    return times_pow2(_bf16_normal(_philox(cfg, _T_QLAST, r), (cfg.n_layers, cfg.n_q_heads, cfg.head_dim)),
+                      cfg.q_scale_log2)
 
 
 def token_tables(cfg: Config):
@@ -131,7 +149,7 @@ def token_tables(cfg: Config):
     code c of level t back into the model."""
     if cfg.dtype == "f32":
         t = _tiny_all(cfg)
-        return t["tq"], t["tk"], t["tv"]
+        return times_pow2(t["tq"], cfg.q_scale_log2), times_pow2(t["tk"], cfg.own_k_scale_log2), t["tv"]
     L, T, V = cfg.n_layers, max(cfg.n_levels - 1, 0), cfg.codebook
     tq = np.empty((L, T, V, cfg.n_q_heads, cfg.head_dim), dtype=np.uint16)
     tk = np.empty((L, T, V, cfg.n_kv_heads, cfg.head_dim), dtype=np.uint16)
@@ -140,7 +158,7 @@ def token_tables(cfg: Config):
         tq[l] = _bf16_normal(_philox(cfg, _T_TQ, l), tq.shape[1:])
         tk[l] = _bf16_normal(_philox(cfg, _T_TK, l), tk.shape[1:])
         tv[l] = _bf16_normal(_philox(cfg, _T_TV, l), tv.shape[1:])
-    return tq, tk, tv
+    return times_pow2(tq, cfg.q_scale_log2), times_pow2(tk, cfg.own_k_scale_log2), tv
 
 
 def w_sid(cfg: Config) -> np.ndarray:

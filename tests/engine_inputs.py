@@ -1,65 +1,2 @@
-"""Engine construction and input upload from the seeded generators (no oracle here).
-
-Used by the GPU tests and by bench.py's GPU leg."""
-from __future__ import annotations
-
-import numpy as np
-
-import synth
-
-
-def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm="valid", max_ctx_tokens=None,
-                max_beam_width=None, max_layers_per_launch=0):
-    import semantic_id_beam_amd as sib
-    tq, tk, tv = synth.token_tables(cfg)
-    shapes = synth.request_shapes(cfg)
-    R = cfg.n_requests if max_requests is None else max_requests
-    if max_ctx_tokens is None:
-        max_ctx_tokens = sum(sib._lib.lib().gr_ctx_padded_len(n) for n, _ in shapes[:R])
-    W = max(w for _, w in shapes) if max_beam_width is None else max_beam_width
-    return sib.BeamEngine(tok_q=tq, tok_k=tk, tok_v=tv, w_sid=synth.w_sid(cfg), items=synth.items(cfg),
-                          n_layers=cfg.n_layers, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
-                          head_dim=cfg.head_dim, dtype=cfg.dtype, norm=norm, max_requests=R,
-                          max_beam_width=W, max_ctx_tokens=max_ctx_tokens, max_splits=max_splits,
-                          debug_attn=debug_attn, max_layers_per_launch=max_layers_per_launch)
-
-
-def request_tensors(cfg, r: int, device="cuda", host=False):
-    """Context K, V [L][N][Hkv][d] and q_last [L][Hq][d] of request r as device tensors.
-
-    bf16 workloads are generated on the device (synth.device: the host generators' values)
-    unless `host`; fp32 ones on the host."""
-    from semantic_id_beam_amd import to_device
-    if cfg.dtype == "bf16" and not host and str(device).startswith("cuda"):
-        from synth import device as synth_device
-        return synth_device.request_tensors(cfg, r, device)
-    ks, vs = [], []
-    for l in range(cfg.n_layers):
-        k, v = synth.ctx_kv_block(cfg, r, l)
-        ks.append(k)
-        vs.append(v)
-    return to_device(np.stack(ks), device), to_device(np.stack(vs), device), to_device(synth.q_last(cfg, r), device)
-
-
-def native_layout(k, v):
-    """[L][N][Hkv][d] -> (K [L][Hkv][Np][d], V^T [L][Hkv][d][Np]) zero-padded (test-side data prep)."""
-    import torch
-    L, N, Hkv, d = k.shape
-    Np = (N + 63) // 64 * 64
-    kn = torch.zeros((L, Hkv, Np, d), dtype=k.dtype, device=k.device)
-    vn = torch.zeros((L, Hkv, d, Np), dtype=v.dtype, device=v.device)
-    kn[:, :, :N, :] = k.permute(0, 2, 1, 3)
-    vn[:, :, :, :N] = v.permute(0, 2, 3, 1)
-    return kn.contiguous(), vn.contiguous(), N
-
-
-def load_request(eng, cfg, r: int, rid: int | None = None, adopt=False):
-    k, v, q = request_tensors(cfg, r)
-    N, W = synth.request_shapes(cfg)[r]
-    rid = r if rid is None else rid
-    if adopt:
-        kn, vn, _ = native_layout(k, v)
-        eng.load(rid, kn, vn, q, W, adopt=True, ctx_len=N)
-    else:
-        eng.load(rid, k, v, q, W)
-    return rid
+"""Engine construction and input upload from the seeded generators (no oracle here)."""
+from semantic_id_beam_amd.workloads import load_request, make_engine, native_layout, request_tensors  # noqa: F401

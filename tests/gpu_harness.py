@@ -106,3 +106,73 @@ def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
     num = np.max(np.abs(got - ref), axis=-1)
     den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
     return float(np.max(num / den))
+
+
+def check_beam_path(eng, rid, sets):
+    """BeamPath closure of a request's current beam set B_s.  sets[t] holds the code tuples of
+    B_{t+1} in slot order (t < s, the last entry is B_s).  For every beam j of B_s and level t,
+    anc[j][t] must be a slot of B_{t+1} whose tuple is beam j's prefix of length t+1, and the
+    newest entry anc[j][s-1] is j itself (a beam's token of the latest level sits in its own
+    slot)."""
+    anc = eng.path(rid)
+    cur, s = sets[-1], len(sets)
+    assert anc.shape[0] == len(cur), (anc.shape, len(cur))
+    for j, p in enumerate(cur):
+        assert int(anc[j, s - 1]) == j, f"beam {j}: newest ancestor slot {anc[j, s - 1]}"
+        for t in range(s):
+            slot = int(anc[j, t])
+            assert 0 <= slot < len(sets[t]), f"beam {j} level {t}: slot {slot} outside B_{t + 1}"
+            assert sets[t][slot] == p[: t + 1], f"beam {j} level {t}: slot {slot} holds {sets[t][slot]}, not {p[:t + 1]}"
+
+
+def run_checked(eng, cfg, steps, checked, attn=True, tfs=None):
+    """Runs batched steps (steps: one list of request ids per gr_beam_step; ids equal the
+    workload's request indices) and checks the requests in `checked` after each of their steps,
+    teacher-forced: every layer's attention output of every beam (attn; needs an engine with
+    debug_attn), the hidden vector, the beam set and scores, and BeamPath closure.  Returns
+    (TeacherForced per checked id, attention errors, final beam sets)."""
+    tfs = tfs if tfs is not None else {r: TeacherForced(cfg, r) for r in checked}
+    prev = {r: [()] for r in checked}
+    sets = {r: [] for r in checked}
+    tol = attn_tol(cfg)
+    errs = []
+    for step in steps:
+        eng.step(step)
+        for r in step:
+            if r not in tfs:
+                continue
+            tf = tfs[r]
+            after = gpu_beams(eng, r)
+            if attn:
+                for l in range(cfg.n_layers):
+                    got = eng.attn_out(r, l)
+                    assert got.shape[0] == len(prev[r])
+                    ref = np.stack([oracle.beam_layer_output(tf.req, tf.model, p, l) for p in prev[r]])
+                    errs.append(rel_err_rows(got, ref))
+                    assert errs[-1] <= tol, f"request {r} level {len(sets[r])} layer {l}: attention rel err {errs[-1]}"
+            h, _ = eng.hidden(r)
+            href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev[r]])
+            assert rel_err_rows(h, href) <= tol * max(1, cfg.n_layers)
+            tf.check_step(prev[r], after)
+            sets[r].append(after[0])
+            check_beam_path(eng, r, sets[r])
+            prev[r] = after[0]
+    return tfs, errs, prev
+
+
+def score_bound(cfg, r: int) -> float:
+    """(smallest, largest) over layers and kv heads of the Cauchy-Schwarz score bound at the
+    first level: the largest |q| of the head's queries times the largest context-key norm, times
+    log2(e)/sqrt(d) (the quantity the context kernels compare with their fixed-reference limit)."""
+    qs = oracle.beam.as_f64(synth.q_last(cfg, r))
+    g = cfg.group
+    lo, hi = np.inf, 0.0
+    for l in range(cfg.n_layers):
+        k, _ = synth.ctx_kv_block(cfg, r, l)
+        k = oracle.beam.as_f64(k)
+        for h in range(cfg.n_kv_heads):
+            kn = np.sqrt(np.max(np.sum(k[:, h, :] ** 2, axis=-1)))
+            qn = np.max(np.linalg.norm(qs[l, h * g:(h + 1) * g, :], axis=-1))
+            b = qn * kn * np.log2(np.e) / np.sqrt(cfg.head_dim)
+            lo, hi = min(lo, b), max(hi, b)
+    return float(lo), float(hi)

@@ -157,6 +157,13 @@ int main() {
     bo = opts(1, 4, 64);
     bo.max_layers_per_launch = -1;
     EXPECT(gr_engine_create(&m, &is, &bo, &e) != GR_OK && e == nullptr);
+    bo = opts(1, 4, 64);
+    bo.flags = 4u;  // not an engine flag
+    EXPECT(gr_engine_create(&m, &is, &bo, &e) == GR_E_INVALID_ARG && e == nullptr);
+    bo.flags = GR_ENGINE_PER_LAYER | GR_ENGINE_DEBUG_ATTN;
+    EXPECT(gr_engine_create(&m, &is, &bo, &e) == GR_OK && e != nullptr);
+    EXPECT(gr_engine_destroy(e) == GR_OK);
+    e = nullptr;
     it[5] = 16;  // code out of range
     EXPECT(gr_engine_create(&m, &is, &o, &e) != GR_OK && e == nullptr);
     gr_item_set none{0, it.data()};

@@ -1,39 +1,9 @@
-"""Builds oracle inputs from the seeded generators (test side only)."""
+"""Oracle inputs from the seeded generators (test side), and an independent dict trie."""
 from __future__ import annotations
-
-import functools
 
 import numpy as np
 
-import oracle
-import synth
-
-
-@functools.lru_cache(maxsize=8)
-def model_for(cfg) -> "oracle.Model":
-    tq, tk, tv = synth.token_tables(cfg)
-    return oracle.Model.from_arrays(tq, tk, tv, synth.w_sid(cfg))
-
-
-@functools.lru_cache(maxsize=8)
-def prefixes_for(cfg) -> "oracle.PrefixSet":
-    return oracle.PrefixSet(synth.items(cfg), cfg.codebook)
-
-
-def request_for(cfg, r: int, cache: bool = True) -> "oracle.Request":
-    """The oracle's view of request r; context blocks are regenerated per layer on demand."""
-    store = {}
-
-    def ctx(l):
-        if cache and l in store:
-            return store[l]
-        k, v = synth.ctx_kv_block(cfg, r, l)
-        kv = (oracle.beam.as_f64(k), oracle.beam.as_f64(v))
-        if cache:
-            store[l] = kv
-        return kv
-
-    return oracle.Request(ctx=ctx, q_last=oracle.beam.as_f64(synth.q_last(cfg, r)))
+from oracle.inputs import model_for, prefixes_for, request_for  # noqa: F401
 
 
 def dict_trie(items: np.ndarray):

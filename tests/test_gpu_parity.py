@@ -4,8 +4,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_harness import (SCORE_TOL, TeacherForced, attn_tol, gpu_beams, load_request, make_engine, rel_err_rows,
-                               save_report)
+from tests.gpu_harness import (SCORE_TOL, TeacherForced, attn_tol, check_beam_path, gpu_beams, load_request,
+                               make_engine, rel_err_rows, save_report)
 from tests.oracle_inputs import model_for, prefixes_for, request_for
 
 pytestmark = pytest.mark.gpu
@@ -262,6 +262,7 @@ def test_full_context_steps_mixing_levels_match_oracle():
     checked = (1, 10, 18, 22)
     tfs = {r: TeacherForced(cfg, r) for r in checked}
     prev = {r: [()] for r in rids}
+    sets = {r: [] for r in rids}
     level = {r: 0 for r in rids}
     tol = attn_tol(cfg)
     errs, report, admitted, mixed = [], [], [], 0
@@ -286,6 +287,8 @@ def test_full_context_steps_mixing_levels_match_oracle():
                 href = np.stack([oracle.beam_hidden(tf.req, tf.model, p) for p in prev[r]])
                 assert rel_err_rows(h, href) <= tol * cfg.n_layers
                 tf.check_step(prev[r], after)
+                sets[r].append(after[0])
+                check_beam_path(eng, r, sets[r])   # BeamPath closure in mixed-level steps
                 prev[r] = after[0]
             level[r] += 1
     G.gr_engine_set_profiling(eng.eng, False)
@@ -311,6 +314,7 @@ def test_max_beam_width_1024():
     rids = [load_request(eng, cfg, r) for r in range(cfg.n_requests)]
     tfs = {r: TeacherForced(cfg, r) for r in rids}
     prev = {r: [()] for r in rids}
+    sets = {r: [] for r in rids}
     tol = attn_tol(cfg)
     errs = []
     for s in range(cfg.n_levels):
@@ -324,6 +328,8 @@ def test_max_beam_width_1024():
                 errs.append(rel_err_rows(got, ref))
                 assert errs[-1] <= tol, f"request {r} step {s} layer {l}: attention rel err {errs[-1]}"
             tf.check_step(prev[r], after)
+            sets[r].append(after[0])
+            check_beam_path(eng, r, sets[r])   # BeamPath closure at 1024 beams
             prev[r] = after[0]
     assert max(len(p) for p in prev.values()) == 1024
     eng.close()

@@ -1,0 +1,143 @@
+"""Large query and key norms: parity of every bf16 context-attention variant on its
+running-max path.
+
+The context kernels take a fixed score reference when every row of a workgroup has the
+Cauchy-Schwarz bound B = |q| max|k| log2(e)/sqrt(d) <= 60, and otherwise track a running
+maximum with a lazy rescale (in the full-context kernels the beam's own tokens are then merged
+again from an empty state).  The other tests draw N(0, 1) queries and keys (B of about 15-25),
+which never reach that path; a trained model's activations do.  Here queries and context keys
+are scaled by exact powers of two (the search is then a different, sharper one, which the
+oracle recomputes from the same scaled inputs):
+
+  qk2    queries and context keys x2: B of about 75, softmax still spread over many tokens
+  qk8    x8 each: B of about 1200, attention close to one-hot (rescales along the loop)
+  ownk16 only the fed-back tokens' keys x16: B stays small (fixed reference), and the beam's
+         own tokens push the reference up from their online merge
+
+Each case is checked teacher-forced at every level with every layer's attention output of
+every beam, the hidden vector, the beam set and scores, and BeamPath closure."""
+import pytest
+
+import synth
+from tests.gpu_harness import load_request, make_engine, run_checked, save_report, score_bound
+
+pytestmark = pytest.mark.gpu
+
+MODES = {
+    "qk2": dict(q_scale_log2=1, k_scale_log2=1),
+    "qk8": dict(q_scale_log2=3, k_scale_log2=3),
+    "ownk16": dict(own_k_scale_log2=4),
+}
+
+
+def _premise(cfg, mode, r=0):
+    """The inputs take the intended path (checked on the host from the drawn values)."""
+    lo, hi = score_bound(cfg, r)
+    if mode == "ownk16":
+        assert hi <= 60.0, hi
+    else:
+        assert lo > 60.0, lo
+
+
+def _lockstep(cfg, rids):
+    return [list(rids)] * cfg.n_levels
+
+
+def _waves(cfg, waves):
+    """Admission waves: wave k joins before batched step k; each step holds every admitted,
+    unfinished request (each at its own level)."""
+    level = {}
+    steps = []
+    for k in range(len(waves) + cfg.n_levels - 1):
+        if k < len(waves):
+            for r in waves[k]:
+                level[r] = 0
+        step = [r for r in level if level[r] < cfg.n_levels]
+        for r in step:
+            level[r] += 1
+        steps.append(step)
+    return steps
+
+
+def _run(cfg, mode, steps, checked, **engine_kw):
+    _premise(cfg, mode, checked[0])
+    eng = make_engine(cfg, max_requests=cfg.n_requests, debug_attn=True, **engine_kw)
+    for r in range(cfg.n_requests):
+        load_request(eng, cfg, r)
+    tfs, errs, final = run_checked(eng, cfg, steps, checked)
+    for r in checked:
+        codes, scores = eng.beams(r)
+        assert [tuple(c) for c in codes.tolist()] == final[r]
+    eng.close()
+    save_report(cfg, [x for r in checked for x in tfs[r].report], attn_err=max(errs), mode=mode)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_fused_first_level_and_layered_wide(mode):
+    """Level 0: every layer of four requests in one launch (one-wave stream kernel, split
+    partials); levels 1-2: 200 beams x 2 heads = two 256-row blocks per kv head on the wide
+    kernel, each workgroup over the whole (ragged, 700-token) context of one layer, two-term P."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=4, n_layers=3, ctx_len=700, beam_width=200, n_items=50000,
+                           **MODES[mode])
+    _run(cfg, mode, _lockstep(cfg, range(4)), [0, 3])
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_layered_wide_single_bf16_p(mode):
+    """Contexts of 4100 tokens (>= 4096: P rounded once to bf16) on the full-context wide
+    kernel, 130 beams x 2 heads = a full and a nearly empty row block."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=8, n_layers=2, ctx_len=4100, beam_width=130, n_items=50000,
+                           **MODES[mode])
+    _run(cfg, mode, _lockstep(cfg, range(8)), [5])
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_split_k_variants(mode):
+    """One launch per layer and variant with split-K partials (the step does not fill the chip
+    with full-context workgroups): one-wave and two-wave stream kernels, the four-wave narrow
+    kernel, the wide kernel with two-term P (600 tokens) and single P (4100 tokens); the next
+    layer's launch finishes each layer, and the variant groups run on four streams."""
+    shapes = ((700, 8), (1500, 30), (900, 50), (600, 200), (4100, 66))
+    cfg = synth.get_config("ragged_r128", n_requests=5, n_layers=2, shapes=shapes, n_items=60000, waves=1,
+                           **MODES[mode])
+    _run(cfg, mode, _lockstep(cfg, range(5)), [0, 1, 2, 3, 4])
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_layered_stream_and_mixed_levels(mode):
+    """Continuous batching on the full-context path: narrow requests (30 and 5 beams, level-0
+    beams) on the two-wave stream kernel in 64-row blocks and 150-beam requests on the wide
+    kernel, admitted in two waves so that the middle steps mix levels 0, 1 and 2."""
+    wave = ((333, 30),) * 6 + ((333, 150), (129, 5))
+    shapes = wave + tuple((n + 40, w) for n, w in wave)
+    cfg = synth.get_config("ragged_r128", n_requests=len(shapes), n_layers=3, shapes=shapes, n_items=60000, waves=2,
+                           **MODES[mode])
+    steps = _waves(cfg, [list(range(8)), list(range(8, 16))])
+    _run(cfg, mode, steps, [1, 6, 7, 14], max_layers_per_launch=4)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_per_layer_launches(mode):
+    """The one-layer-per-launch engine (GR_ENGINE_PER_LAYER): level 0 on the one-wave stream
+    kernel with split partials, one launch per layer; wide levels with split-K (one layer's row
+    blocks do not fill the chip), each layer finished by the next layer's launch."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=4, n_layers=3, ctx_len=700, beam_width=200, n_items=50000,
+                           **MODES[mode])
+    _run(cfg, mode, _lockstep(cfg, range(4)), [1, 2], per_layer=True)
+
+
+D64_MODES = {"qk4": dict(q_scale_log2=2, k_scale_log2=2), "qk8": MODES["qk8"], "ownk16": MODES["ownk16"]}
+
+
+@pytest.mark.parametrize("mode", list(D64_MODES))
+@pytest.mark.parametrize("hq,hkv,W", [(16, 8, 64), (32, 4, 16)])
+def test_head_dim_64(mode, hq, hkv, W):
+    """head_dim 64 (the narrow register-staged kernels of one, two and four waves)."""
+    cfg = synth.get_config("ctx1k_beam256", n_q_heads=hq, n_kv_heads=hkv, head_dim=64, n_layers=2, ctx_len=500,
+                           beam_width=W, n_items=20000, **D64_MODES[mode])
+    _premise(cfg, "ownk16" if mode == "ownk16" else "qk")
+    eng = make_engine(cfg, max_requests=1, debug_attn=True)
+    load_request(eng, cfg, 0)
+    tfs, errs, _ = run_checked(eng, cfg, _lockstep(cfg, [0]), [0])
+    eng.close()
+    save_report(cfg, tfs[0].report, attn_err=max(errs), mode=mode)
