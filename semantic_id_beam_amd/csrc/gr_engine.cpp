@@ -256,8 +256,7 @@ void layout(gr_engine *e) {
   s.items = take(W * d.levels * 4);
   s.dbg_attn = d.debug_attn ? take((size_t)d.L * W * d.Hq * d.d * 4) : 0;
   const bool full_ctx = d.dtype == 1 && d.d == 128;  // full-context (layered) steps possible
-  s.hl = full_ctx ? take((size_t)d.L * W * d.Hq * d.d * 2) : 0;
-  s.hl_scale = full_ctx ? take((size_t)d.L * W * d.Hq * 4) : 0;
+  s.hl = full_ctx ? take((size_t)d.L * W * d.Hq * d.d * 4) : 0;
   s.slot_bytes = align_up(o, A);
 
   size_t w = 0;

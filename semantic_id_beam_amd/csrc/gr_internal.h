@@ -32,12 +32,12 @@ struct SlotLayout {
   size_t beamkv_k, beamkv_v;  // [L][levels-1][W_max][Hkv][d] elem
   size_t q_last;              // [L][Hq][d] elem
   size_t knmax;               // [L][Hkv] f32: largest context-key norm (bounds the scores)
-  size_t vscale;              // [L][Hkv] f32: power of two above the context's largest |v|
+  size_t vscale;              // [L][Hkv] f32: power of two above the context's largest |v| (taken at load)
   size_t h;                   // [W_max][Hq*d] f32
   size_t logits;              // [W_max][V] f32
   size_t logits_part;         // [kLogitsKS][W_max][V] f32 split-K partial sums
   size_t cand;                // [W_max][V] f32
-  size_t part_o[2];           // [part_rows][d] fp16 o/l*2^-e (bf16) or f32 o, row ((h*splits + sp)*rows_b + row); by layer parity
+  size_t part_o[2];           // [part_rows][d] f32 unnormalised o, row ((h*splits + sp)*rows_b + row); by layer parity
   size_t part_ml[2];          // [part_rows] float2 (m in log2 units, l)
   size_t codes[2];            // [W_max][levels] i32   (double-buffered by level parity)
   size_t score[2];            // [W_max] f32
@@ -47,8 +47,7 @@ struct SlotLayout {
   size_t n_live;              // i32[2]: n_live[s & 1] = beams of B_s
   size_t items;               // [W_max][levels] i32: the candidates of a scoring request
   size_t dbg_attn;            // [L][W_max][Hq][d] f32 (only with debug_attn)
-  size_t hl;                  // full-context steps: [L][W_max][Hq][d] fp16 o/l of each layer, times 2^-e of its row
-  size_t hl_scale;            // [L][W_max][Hq] f32: the row's 2^e (0 when bf16 head_dim-128 steps are impossible)
+  size_t hl;                  // full-context steps: [L][W_max][Hq][d] f32 o/l of each layer (0 when impossible)
 };
 
 struct Dev {
@@ -86,10 +85,10 @@ struct LaunchEv {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 // Context-attention variants: waves per workgroup (1, 2, 4 or 8; 32 query rows per wave)
-// in the low byte, kCtxHiLo when P is split into two bf16 terms.  1, 2 and 4 waves always
-// use the split (narrow steps: HBM- or latency-bound); 8 waves only for short contexts.
+// in the low byte; kCtxHiLo marks P split into two bf16 terms (p = p_hi + p_lo, relative error
+// about 2^-17), which every variant uses: a single bf16 P perturbs each weight by up to 2^-9,
+// and with a few dominant tokens (large query/key norms) that moved log-probs past 1e-3.
 constexpr int kCtxHiLo = 0x100;
-constexpr int kCtxLongContext = 4096;  // wide steps at least this long round P once to bf16
 hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                            int ctx_kind, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
@@ -160,7 +159,8 @@ inline int ctx_kind_for(int rows, int N, int d) {
   if (rows <= 32) return 1 | kCtxHiLo;
   if (rows <= 64 || d == 64) return (rows <= 64 ? 2 : 4) | kCtxHiLo;
   if (rows <= 128) return 4 | kCtxHiLo;
-  return N >= kCtxLongContext ? 8 : (8 | kCtxHiLo);
+  (void)N;
+  return 8 | kCtxHiLo;
 }
 
 }  // namespace gr

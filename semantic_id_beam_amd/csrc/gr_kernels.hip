@@ -46,7 +46,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 #define GR_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kNegInf = -__builtin_inff();
@@ -116,44 +115,23 @@ __device__ __forceinline__ uint8_t *slot_base(const Dev &dev, int slot) {
 // consecutive tokens per lane: no cross-lane shuffle between the two MFMAs.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Split partials of bf16 models: (m, l) in fp32, and the row's o divided by its own l in fp16.
-// o/l is a convex combination of value rows, so |o/l| <= max |v| of the context head; it is
-// stored times 2^-e, where 2^e is the head's value scale (vscale: the power of two just above
-// max |v|), which keeps it below 1 in magnitude whatever the values' range, with no rounding
-// from the scale.  fp16 rounds it to 2^-11 relative, an order below the bf16 rounding of P,
-// and halves the partials' traffic.  A reader weights split sp by exp2(m_sp - M) * l_sp * 2^e.
+// Split partials: (m, l) and the row's unnormalised o, all float32 (a reader weights split sp by
+// exp2(m_sp - M)).  Float32 keeps the merge exact to fp32 rounding whatever the attention's
+// sharpness: with a few dominant tokens o/l is close to one value row, the hidden vector and
+// the logits grow with it, and a 16-bit partial's rounding reached the 1e-3 log-prob bound.
 // Lane (row, hh) of an MFMA output tile holds features db*32 + 8a + 4hh .. +4.
 template <int DB>
 __device__ __forceinline__ void store_partial(uint8_t *slot, const SlotLayout &sl, int buf, size_t prow, float M,
-                                              float ltot, int hh, float vscale, const f32x16_t (&oacc)[DB]) {
+                                              float ltot, int hh, const f32x16_t (&oacc)[DB]) {
   constexpr int D = DB * 32;
   if (hh == 0) gst<f32x2_t>((float2 *)(slot + sl.part_ml[buf]) + prow, f32x2_t{M, ltot});
-  uint16_t *po = (uint16_t *)(slot + sl.part_o[buf]) + prow * D;
-  const float inv = (1.f / ltot) * (1.f / vscale);  // 1/vscale: exact, a power of two
+  float *po = (float *)(slot + sl.part_o[buf]) + prow * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const f16x2_t lo = {(_Float16)(oacc[db][4 * a] * inv), (_Float16)(oacc[db][4 * a + 1] * inv)};
-      const f16x2_t hi = {(_Float16)(oacc[db][4 * a + 2] * inv), (_Float16)(oacc[db][4 * a + 3] * inv)};
-      gst<u32x2_t>(po + db * 32 + 8 * a + 4 * hh,
-                   u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
-    }
-  }
-}
-__device__ __forceinline__ float head_vscale(const Dev &dev, const uint8_t *slot, int layer, int kv) {
-  return ((const float *)(slot + dev.sl.vscale))[layer * dev.dm.Hkv + kv];
-}
-
-// 8 features of a bf16 model's fp16 partial row
-// Each half is cut out of its word with integer ops before the conversion: per-element bit
-// casts of the loaded vector were folded into one 32-bit load that fed all eight features.
-__device__ __forceinline__ void f16x8_to_float(const u32x4_t &u, float *f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = u[i];
-    f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-    f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    for (int a = 0; a < 4; ++a)
+      gst<f32x4_t>(po + db * 32 + 8 * a + 4 * hh,
+                   f32x4_t{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]});
   }
 }
 
@@ -418,7 +396,7 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
   const float ltot = l + __shfl_xor(l, 32);
   if (wave_active && row_ok) {
     const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
+    store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, oacc);
   }
 
 }
@@ -775,7 +753,7 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
     const size_t lofs = FUSED ? (size_t)layer * dm.Hkv * R.splits * R.rows_b : 0;
     const int pb = FUSED ? 0 : layer & 1;
     const size_t prow = lofs + ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-    store_partial<DB>(slot, dev.sl, pb, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
+    store_partial<DB>(slot, dev.sl, pb, prow, M, ltot, hh, oacc);
   }
 }
 
@@ -890,11 +868,9 @@ __device__ __forceinline__ void wide_tail_merge(const Dev &dev, uint8_t *slot, i
 }
 
 // Layer output o/l of the lane's query row in the full-context kernels: to the debug rows, and
-// stored (never read back here) as the layer's fp16 partial of the hidden vector.  The row is
-// scaled by 2^-e, 2^e the power of two just above its largest |o/l| (kept beside it in fp32),
-// so the stored values lie in (-1, 1) for any value range and fp16 rounds them to 2^-11
-// relative; k_sum_hparts adds the layers' rows in layer order.  Lanes (row, hh) and
-// (row, hh ^ 1) hold the two halves of the row's features.
+// stored (never read back here) in float32 as the layer's partial of the hidden vector;
+// k_sum_hparts adds the layers' rows in layer order.  Lanes (row, hh) and (row, hh ^ 1) hold
+// the two halves of the row's features.
 template <int D>
 __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &R, uint8_t *slot, int layer, int j,
                                                  int hq, int hh, float ltot, const f32x16_t (&oacc)[D / 32],
@@ -902,30 +878,19 @@ __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &
   constexpr int DB = D / 32;
   const Dims &dm = dev.dm;
   const float inv = 1.f / ltot;
-  float mx = 0.f;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(oacc[db][i] * inv));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
   if (!row_ok) return;
-  int e = 0;
-  (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1); e = 0 for mx = 0
   const size_t row = ((size_t)layer * dm.W_max + j) * dm.Hq + hq;
-  uint32_t *hp = (uint32_t *)(slot + dev.sl.hl) + row * (D / 2);
-  if (hh == 0) ((float *)(slot + dev.sl.hl_scale))[row] = ldexpf(1.f, e);
+  float *hp = (float *)(slot + dev.sl.hl) + row * D;
   float *dg = dm.debug_attn ? (float *)(slot + dev.sl.dbg_attn) + row * D : nullptr;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int f0 = db * 32 + 8 * a + 4 * hh;
-      f32x4_t o = f32x4_t{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv, oacc[db][4 * a + 2] * inv,
-                          oacc[db][4 * a + 3] * inv};
+      const f32x4_t o = f32x4_t{oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv, oacc[db][4 * a + 2] * inv,
+                                oacc[db][4 * a + 3] * inv};
       if (dg) gst<f32x4_t>(dg + f0, o);
-      const f16x2_t h01 = {(_Float16)ldexpf(o[0], -e), (_Float16)ldexpf(o[1], -e)};
-      const f16x2_t h23 = {(_Float16)ldexpf(o[2], -e), (_Float16)ldexpf(o[3], -e)};
-      gst<u32x2_t>(hp + f0 / 2, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+      gst<f32x4_t>(hp + f0, o);
     }
 }
 
@@ -1296,7 +1261,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     if constexpr (!LAYERED) {
       if (wave_active && row_ok) {
         const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-        store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, head_vscale(dev, slot, layer, h), oacc);
+        store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, oacc);
       }
     } else {
       if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, true);
@@ -1476,13 +1441,11 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
       Mb = Mn;
     }
   }
-  // partials: fp16 o/l for bf16 models (weight exp2(m - Ms) * l), fp32 o for fp32 models
-  constexpr bool F16 = std::is_same<T, uint16_t>::value;
+  // split partials: unnormalised o in float32, weight exp2(m - Ms)
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[layer & 1]);
-  const uint8_t *po = slot + dev.sl.part_o[layer & 1];
+  const float *po = (const float *)(slot + dev.sl.part_o[layer & 1]);
   const int row = j * g + gi;
   const size_t pbase = (size_t)kv * R.splits * R.rows_b + row;
-  const float vs = F16 ? head_vscale(dev, slot, layer, kv) : 1.f;
   float Ms = Mb;
   for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
   const float fb = fast_exp2(Mb - Ms);
@@ -1494,21 +1457,13 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
     const f32x2_t ml = gld<f32x2_t>(pml + prow);
     const float f = fast_exp2(ml[0] - Ms);
     Ls = fmaf(ml[1], f, Ls);
-    float a[8];
-    if constexpr (F16) {
-      f16x8_to_float(gld<u32x4_t>((const uint16_t *)po + prow * D + c8 * 8), a);
-    } else {
-      const f32x4_t x = gld<f32x4_t>((const float *)po + prow * D + c8 * 8);
-      const f32x4_t y = gld<f32x4_t>((const float *)po + prow * D + c8 * 8 + 4);
+    const f32x4_t x = gld<f32x4_t>(po + prow * D + c8 * 8);
+    const f32x4_t y = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = x[i];
-        a[4 + i] = y[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      O[i] = fmaf(x[i], f, O[i]);
+      O[4 + i] = fmaf(y[i], f, O[4 + i]);
     }
-    const float wgt = F16 ? f * ml[1] * vs : f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], wgt, O[i]);
   }
   const float inv = 1.f / Ls;
 #pragma unroll
@@ -1543,8 +1498,7 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
   const float c2 = dm.scale_log2;
   const int total = (r1 - r0) * C8;
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[layer & 1]);
-  const uint16_t *po = (const uint16_t *)(slot + dev.sl.part_o[layer & 1]);  // fp16 o/l * 2^-e
-  const float vs = head_vscale(dev, slot, layer, kv);
+  const float *po = (const float *)(slot + dev.sl.part_o[layer & 1]);  // unnormalised o, float32
   const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
   const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
   uint16_t *bk = (uint16_t *)(slot + dev.sl.beamkv_k);
@@ -1569,18 +1523,20 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
     }
     // ---- phase 1: index-only loads
     f32x2_t ml0[E], ml1[E];
-    u32x4_t pa0[E], pa1[E];
+    f32x4_t pa0[E], pb0[E], pa1[E], pb1[E];
     f32x4_t ha[E], hc[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
       if (!ok[k]) continue;
       code[k] = s > 0 ? codes[j[k] * lvl + (s - 1)] : 0;
-      const uint16_t *p0 = po + pbase[k] * D + c8[k] * 8;
+      const float *p0 = po + pbase[k] * D + c8[k] * 8;
       ml0[k] = gld<f32x2_t>(pml + pbase[k]);
-      pa0[k] = gld<u32x4_t>(p0);
+      pa0[k] = gld<f32x4_t>(p0);
+      pb0[k] = gld<f32x4_t>(p0 + 4);
       if (S > 1) {
         ml1[k] = gld<f32x2_t>(pml + pbase[k] + R.rows_b);
-        pa1[k] = gld<u32x4_t>(p0 + (size_t)R.rows_b * D);
+        pa1[k] = gld<f32x4_t>(p0 + (size_t)R.rows_b * D);
+        pb1[k] = gld<f32x4_t>(p0 + (size_t)R.rows_b * D + 4);
       }
       if (layer > 0) {
         const float *hr = hb + ((size_t)j[k] * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8;
@@ -1676,28 +1632,33 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
       {
         const float f = fast_exp2(ml0[k][0] - Ms);
         Ls = fmaf(ml0[k][1], f, Ls);
-        float a[8];
-        f16x8_to_float(pa0[k], a);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml0[k][1] * vs, O[i]);
+        for (int i = 0; i < 4; ++i) {
+          O[i] = fmaf(pa0[k][i], f, O[i]);
+          O[4 + i] = fmaf(pb0[k][i], f, O[4 + i]);
+        }
       }
       if (S > 1) {
         const float f = fast_exp2(ml1[k][0] - Ms);
         Ls = fmaf(ml1[k][1], f, Ls);
-        float a[8];
-        f16x8_to_float(pa1[k], a);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml1[k][1] * vs, O[i]);
+        for (int i = 0; i < 4; ++i) {
+          O[i] = fmaf(pa1[k][i], f, O[i]);
+          O[4 + i] = fmaf(pb1[k][i], f, O[4 + i]);
+        }
       }
       for (int sp = 2; sp < S; ++sp) {
         const size_t prow = pbase[k] + (size_t)sp * R.rows_b;
         const f32x2_t ml = gld<f32x2_t>(pml + prow);
         const float f = fast_exp2(ml[0] - Ms);
         Ls = fmaf(ml[1], f, Ls);
-        float a[8];
-        f16x8_to_float(gld<u32x4_t>(po + prow * D + c8[k] * 8), a);
+        const f32x4_t x = gld<f32x4_t>(po + prow * D + c8[k] * 8);
+        const f32x4_t y = gld<f32x4_t>(po + prow * D + c8[k] * 8 + 4);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml[1] * vs, O[i]);
+        for (int i = 0; i < 4; ++i) {
+          O[i] = fmaf(x[i], f, O[i]);
+          O[4 + i] = fmaf(y[i], f, O[4 + i]);
+        }
       }
       const float inv = 1.f / Ls;
 #pragma unroll
@@ -1755,7 +1716,7 @@ __global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepR
   const Dims &dm = dev.dm;
   uint8_t *slot = slot_base(dev, R.slot);
   const float2 *pml = (const float2 *)(slot + dev.sl.part_ml[0]);
-  const uint16_t *po = (const uint16_t *)(slot + dev.sl.part_o[0]);  // fp16 o/l * 2^-e
+  const float *po = (const float *)(slot + dev.sl.part_o[0]);  // unnormalised o, float32
   float *tmp = (float *)(slot + dev.sl.part_o[1]);
   const size_t lofs = (size_t)layer * dm.Hkv * R.splits * R.rows_b;
   for (int e = threadIdx.x; e < dm.Hq * C8; e += blockDim.x) {
@@ -1763,7 +1724,6 @@ __global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepR
     const size_t pbase = lofs + (size_t)kv * R.splits * R.rows_b + row;
     float Ms = kNegInf;
     for (int sp = 0; sp < R.splits; ++sp) Ms = fmaxf(Ms, gld<f32x2_t>(pml + pbase + (size_t)sp * R.rows_b)[0]);
-    const float vs = head_vscale(dev, slot, layer, kv);
     float Ls = 0.f, O[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) O[i] = 0.f;
@@ -1772,10 +1732,13 @@ __global__ __launch_bounds__(256) void k_finish_first_level(Dev dev, const StepR
       const f32x2_t ml = gld<f32x2_t>(pml + prow);
       const float f = fast_exp2(ml[0] - Ms);
       Ls = fmaf(ml[1], f, Ls);
-      float a[8];
-      f16x8_to_float(gld<u32x4_t>(po + prow * D + c8 * 8), a);
+      const f32x4_t x = gld<f32x4_t>(po + prow * D + c8 * 8);
+      const f32x4_t y = gld<f32x4_t>(po + prow * D + c8 * 8 + 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) O[i] = fmaf(a[i], f * ml[1] * vs, O[i]);
+      for (int i = 0; i < 4; ++i) {
+        O[i] = fmaf(x[i], f, O[i]);
+        O[4 + i] = fmaf(y[i], f, O[4 + i]);
+      }
     }
     const float inv = 1.f / Ls;
     const f32x4_t a = f32x4_t{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
@@ -1806,8 +1769,7 @@ __global__ __launch_bounds__(256) void k_sum_layers(Dev dev, const StepReq *__re
 }
 
 // h of every live beam after a full-context step: the sum over layers, in layer order, of the
-// rows' stored fp16 o/l times their 2^e (an exact product).  One thread per 8 features of a
-// (beam, query head) row.
+// rows' stored float32 o/l.  One thread per 8 features of a (beam, query head) row.
 __global__ __launch_bounds__(256) void k_sum_hparts(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
   const StepReq R = reqs[blockIdx.y];
   if (R.lgroups < 1) return;
@@ -1817,20 +1779,14 @@ __global__ __launch_bounds__(256) void k_sum_hparts(Dev dev, const StepReq *__re
   const int per_row = dm.d / 8;
   const size_t n8 = (size_t)n_live * dm.Hq * per_row;
   const size_t lrows = (size_t)dm.W_max * dm.Hq;  // rows per layer
-  const u32x4_t *hp = (const u32x4_t *)(slot + dev.sl.hl);
-  const float *sc = (const float *)(slot + dev.sl.hl_scale);
+  const f32x4_t *hp = (const f32x4_t *)(slot + dev.sl.hl);
   f32x4_t *hb = (f32x4_t *)(slot + dev.sl.h);
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += (size_t)gridDim.x * blockDim.x) {
-    const size_t row = e / per_row;
-    f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+    f32x4_t a0 = gld<f32x4_t>(hp + 2 * e), a1 = gld<f32x4_t>(hp + 2 * e + 1);
 #pragma unroll 4
-    for (int l = 0; l < dm.L; ++l) {
-      const u32x4_t v = gld<u32x4_t>(hp + (size_t)l * lrows * per_row + e);
-      const float w = sc[(size_t)l * lrows + row];
-      float f[8];
-      f16x8_to_float(v, f);
-      a0 += w * f32x4_t{f[0], f[1], f[2], f[3]};
-      a1 += w * f32x4_t{f[4], f[5], f[6], f[7]};
+    for (int l = 1; l < dm.L; ++l) {
+      a0 += gld<f32x4_t>(hp + 2 * ((size_t)l * lrows * per_row + e));
+      a1 += gld<f32x4_t>(hp + 2 * ((size_t)l * lrows * per_row + e) + 1);
     }
     gst<f32x4_t>(hb + 2 * e, a0);
     gst<f32x4_t>(hb + 2 * e + 1, a1);
@@ -2533,13 +2489,10 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
     return hipGetLastError();
   }
   const int nw = ctx_kind & 0xFF;
-  const bool hilo = (ctx_kind & kCtxHiLo) != 0;
   const dim3 blk(nw * 64);
   if (dev.dm.d == 128) {
-    if (nw == 8 && hilo)
+    if (nw == 8)
       launch(k_ctx_attn_wide<4, true, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
-    else if (nw == 8)
-      launch(k_ctx_attn_wide<4, false, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 4)
       launch(k_ctx_attn_bf16_narrow<128, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 2)
@@ -2566,10 +2519,7 @@ hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_re
     return hipGetLastError();
   }
   if ((ctx_kind & 0xFF) != 8) return hipErrorInvalidValue;
-  if (ctx_kind & kCtxHiLo)
-    launch(k_ctx_attn_wide<4, true, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
-  else
-    launch(k_ctx_attn_wide<4, false, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
+  launch(k_ctx_attn_wide<4, true, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
   return hipGetLastError();
 }
 
