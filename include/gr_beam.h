@@ -233,6 +233,24 @@ gr_status gr_ctx_prefill(gr_engine *eng, int64_t request_id, const int32_t *toke
                          int32_t soft_pos, const float *user_vec, int32_t beam_width, void *k_native,
                          void *vt_native, void *q_last_out, void *stream);
 
+/* gr_ctx_prefill for callers that cannot allocate: code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc.  The same context, bounds and last query as
+ * gr_ctx_prefill (the same kernels), with two differences:
+ *   tokens_dev  device [ctx_len] int32 token ids (the entry at soft_pos is ignored).  They are
+ *               not checked on the host: an id outside [0, vocab) is clamped into it.
+ *   the soft token's partial sums go to a fixed device array of the library, 4 MiB
+ *               (kSoftSplit = 8 partial sums of embed_dim + n_layers * (Hq + 2 Hkv) * head_dim
+ *               floats must fit: 28 layers of 16/8 heads of 128 with embed_dim 2048 take 3.7 MB);
+ *               each GPU the library runs on holds one such array until the process ends.
+ * No call here runs hipMalloc, hipHostMalloc or hipFree (only the engine's host request table is
+ * updated).  Every call on one GPU shares that GPU's array and overwrites it: calls that overlap
+ * on one GPU (several streams or engines prefilling soft tokens at once) race.  Errors: those of
+ * gr_ctx_prefill except the token-id check, and GR_E_UNSUPPORTED when the soft token's partial
+ * sums exceed the array. */
+gr_status gr_ctx_prefill_noalloc(gr_engine *eng, int64_t request_id, const int32_t *tokens_dev, int32_t ctx_len,
+                                 int32_t soft_pos, const float *user_vec, int32_t beam_width, void *k_native,
+                                 void *vt_native, void *q_last_out, void *stream);
+
 /* Advances each listed request by one decode step (one semantic-ID level),
  * whatever level each one is at: requests at different levels can share a
  * call (continuous batching).  Enqueued on `stream`; returns without waiting.

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "
 #: every symbol include/gr_beam.h declares
 EXPORTS = [
     "gr_engine_create", "gr_engine_workspace_bytes", "gr_engine_bind_workspace", "gr_engine_destroy",
-    "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_engine_set_prefill", "gr_ctx_prefill",
+    "gr_engine_trie_nodes", "gr_ctx_padded_len", "gr_ctx_kv_load", "gr_engine_set_prefill", "gr_ctx_prefill", "gr_ctx_prefill_noalloc",
     "gr_beam_step", "gr_beams_get",
     "gr_beams_get_batch", "gr_beams_get_batch_async", "gr_beams_result_bytes", "gr_beams_unpack",
     "gr_request_release", "gr_request_reset", "gr_request_reset_batch", "gr_last_error", "gr_topk_select", "gr_debug_beam_state", "gr_debug_beam_path",
@@ -100,6 +100,7 @@ def lib() -> C.CDLL:
         "gr_ctx_kv_load": (i32, [vp, i64, i32, i32, vp, vp, vp, u32, vp]),
         "gr_engine_set_prefill": (i32, [vp, P(gr_prefill_desc)]),
         "gr_ctx_prefill": (i32, [vp, i64, vp, i32, i32, vp, i32, vp, vp, vp, vp]),
+        "gr_ctx_prefill_noalloc": (i32, [vp, i64, vp, i32, i32, vp, i32, vp, vp, vp, vp]),
         "gr_beam_step": (i32, [vp, P(i64), i32, vp]),
         "gr_beams_get": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
         "gr_beams_get_batch": (i32, [vp, P(i64), i32, i32, vp, vp, vp, vp]),
@@ -201,6 +202,13 @@ def gr_ctx_prefill(eng: int, rid: int, tokens, soft_pos: int, user_vec, beam_wid
     tok = np.ascontiguousarray(tokens, dtype=np.int32)
     _check(lib().gr_ctx_prefill(eng, rid, _host(tok), tok.shape[0], soft_pos, _ptr(user_vec), beam_width,
                                 _ptr(k_native), _ptr(vt_native), _ptr(q_last_out), stream))
+
+
+def gr_ctx_prefill_noalloc(eng: int, rid: int, tokens_dev, ctx_len: int, soft_pos: int, user_vec, beam_width: int,
+                           k_native=None, vt_native=None, q_last_out=None, stream: int = 0):
+    """tokens_dev: device int32 [ctx_len]; user_vec, k_native, vt_native, q_last_out: device pointers or None."""
+    _check(lib().gr_ctx_prefill_noalloc(eng, rid, _ptr(tokens_dev), ctx_len, soft_pos, _ptr(user_vec), beam_width,
+                                        _ptr(k_native), _ptr(vt_native), _ptr(q_last_out), stream))
 
 
 def gr_beam_step(eng: int, request_ids, stream: int = 0):

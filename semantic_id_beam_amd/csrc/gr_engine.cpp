@@ -109,6 +109,8 @@ struct gr_engine {
   float *pf_soft = nullptr;
   hipEvent_t pf_ev = nullptr;
   bool pf_ev_used = false;
+  // the allocation-free prefill's fixed device array on the engine's device (resolved at bind)
+  float *noalloc_scratch = nullptr;
 };
 
 namespace {
@@ -436,6 +438,7 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
   }
   if ((r = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
     return r;
+  if ((r = check_dev(e, gr::prefill_scratch(&e->noalloc_scratch), "scratch address")) != GR_OK) return r;
   gr::Dev &dv = e->dev;
   dv.dm = e->dm;
   dv.sl = e->sl;
@@ -589,7 +592,7 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
       return q;
     // the last query first: its launch also clears the maxima the context launch folds into
     const int last = (soft_pos == N - 1) ? -1 : tokens[N - 1];
-    if ((q = check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, last, part, L, Hq, Hkv, d, e->pf.vocab,
+    if ((q = check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, last, nullptr, part, L, Hq, Hkv, d, e->pf.vocab,
                                                sb + e->sl.q_last, q_out, (float *)(sb + e->sl.knmax),
                                                (float *)(sb + e->sl.vscale), st),
                        "prefill query")) != GR_OK)
@@ -601,6 +604,82 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
                                                (float *)(sb + e->sl.vscale), st),
                      "prefill");
   };
+  if ((r = run()) != GR_OK) {
+    if (!R.adopt) pool_free(e, R.pool_off, Np);
+    return r;
+  }
+  if ((r = check_dev(e, gr::launch_init_slots(e->dev, &R.slot, 1, st), "slot init")) != GR_OK) return r;
+  e->free_slots.pop_back();
+  e->reqs[rid] = R;
+  return GR_OK;
+}
+
+gr_status gr_ctx_prefill_noalloc(gr_engine *e, int64_t rid, const int32_t *tokens_dev, int32_t N, int32_t soft_pos,
+                                 const float *u, int32_t W, void *kn, void *vtn, void *q_out, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  if (!e->has_pf) return fail(GR_E_BAD_STATE, "no prefill tables (gr_engine_set_prefill)");
+  if (!tokens_dev) return fail(GR_E_INVALID_ARG, "null tokens");
+  if (N < 1) return fail(GR_E_INVALID_ARG, "ctx_len must be >= 1");
+  if (W < 1 || W > e->dm.W_max) return fail(GR_E_INVALID_ARG, "beam_width must be in [1, max_beam_width]");
+  if (soft_pos < -1 || soft_pos >= N) return fail(GR_E_INVALID_ARG, "soft_pos must be -1 or in [0, ctx_len)");
+  if (soft_pos >= 0 && e->pf.user_dim < 1) return fail(GR_E_BAD_STATE, "no soft-token projection set");
+  if (soft_pos >= 0 && !u) return fail(GR_E_INVALID_ARG, "null user vector");
+  if ((kn == nullptr) != (vtn == nullptr)) return fail(GR_E_INVALID_ARG, "k_native and vt_native go together");
+  if (((uintptr_t)kn | (uintptr_t)vtn) & 15u) return fail(GR_E_INVALID_ARG, "k_native and vt_native must be 16-byte aligned");
+  if (e->reqs.count(rid)) return fail(GR_E_INVALID_ARG, "request id already loaded");
+  if (e->free_slots.empty()) return fail(GR_E_OUT_OF_MEMORY, "no free request slot (max_requests)");
+  const int L = e->dm.L, Hq = e->dm.Hq, Hkv = e->dm.Hkv, d = e->dm.d;
+  float *part = nullptr;
+  if (soft_pos >= 0) {
+    const size_t need = (size_t)gr::kSoftSplit * ((size_t)e->pf.embed_dim + (size_t)L * (Hq + 2 * Hkv) * d);
+    if (need > gr::kPrefillScratchFloats)
+      return fail(GR_E_UNSUPPORTED, "the soft token's partial sums (" + std::to_string(need * 4) +
+                                        " bytes) exceed the fixed 4 MiB device array of the allocation-free prefill");
+    part = e->noalloc_scratch + (size_t)gr::kSoftSplit * e->pf.embed_dim;
+  }
+  const int Np = gr_ctx_padded_len(N);
+  hipStream_t st = (hipStream_t)stream;
+  gr_engine::Req R;
+  R.N = N;
+  R.Np = Np;
+  R.W = W;
+  if (kn) {
+    R.adopt = true;
+    R.k = kn;
+    R.vt = vtn;
+  } else {
+    int64_t off;
+    if (!pool_alloc(e, Np, &off)) return fail(GR_E_OUT_OF_MEMORY, "context pool exhausted (max_ctx_tokens)");
+    R.pool_off = off;
+    uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
+    R.k = dk;
+    R.vt = dk + (size_t)L * Hkv * Np * d * e->elem;
+  }
+  R.slot = e->free_slots.back();
+  uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
+  auto run = [&]() -> gr_status {
+    gr_status q;
+    if (soft_pos >= 0 &&
+        (q = check_dev(e, gr::launch_soft_token(u, e->pf.proj, e->pf.user_dim, e->pf.embed_dim, e->pf.w_q, e->pf.w_k,
+                                                e->pf.w_v, L, Hq * d, Hkv * d, e->noalloc_scratch, part, st),
+                       "soft token")) != GR_OK)
+      return q;
+    // the last query first (its id read on the device): it also clears the bound maxima
+    const bool soft_last = soft_pos == N - 1;
+    if ((q = check_dev(e, gr::launch_prefill_q(e->elem, e->pf.tok_q, -1, soft_last ? nullptr : tokens_dev + (N - 1),
+                                               part, L, Hq, Hkv, d, e->pf.vocab, sb + e->sl.q_last, q_out,
+                                               (float *)(sb + e->sl.knmax), (float *)(sb + e->sl.vscale), st),
+                       "prefill query")) != GR_OK)
+      return q;
+    return check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, tokens_dev, N, Np, soft_pos, part, L,
+                                               Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
+                                               const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
+                                               (float *)(sb + e->sl.vscale), st),
+                     "prefill");
+  };
+  gr_status r;
   if ((r = run()) != GR_OK) {
     if (!R.adopt) pool_free(e, R.pool_off, Np);
     return r;

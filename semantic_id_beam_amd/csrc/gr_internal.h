@@ -143,11 +143,20 @@ hipError_t launch_soft_token(const float *u, const float *proj, int du, int de, 
 hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, const int32_t *tok, int N, int Np,
                               int soft_pos, const float *part, int L, int Hq, int Hkv, int d, int vocab, void *nk,
                               void *nvt, float *knmax, float *vscale, hipStream_t st);
-// Query of the last position, [L][Hq][d]: row last_tok of tq [L][vocab][Hq][d], or the soft
-// token's q (last_tok < 0), into q_slot and (if set) q_out; clears knmax / vscale [L][Hkv]
-// for the launch_prefill_ctx that follows.
-hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const float *part, int L, int Hq, int Hkv,
-                            int d, int vocab, void *q_slot, void *q_out, float *knmax, float *vscale, hipStream_t st);
+// Query of the last position, [L][Hq][d]: row last_tok of tq [L][vocab][Hq][d] (or of the id
+// at last_dev, device memory, clamped into [0, vocab)), or the soft token's q (last_tok < 0 and
+// no last_dev), into q_slot and (if set) q_out; clears knmax / vscale [L][Hkv] for the
+// launch_prefill_ctx that follows.  Context token ids of launch_prefill_ctx outside [0, vocab)
+// are clamped the same way.
+hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const int32_t *last_dev, const float *part,
+                            int L, int Hq, int Hkv, int d, int vocab, void *q_slot, void *q_out, float *knmax,
+                            float *vscale, hipStream_t st);
+// The allocation-free prefill's fixed device array (soft-token partial sums), the same
+// kSoftSplit * (embed_dim + L * (Hq + 2 Hkv) d) floats as gr_engine_set_prefill's staging: at
+// most kPrefillScratchFloats.  prefill_scratch returns the current device's address of it
+// (hipGetSymbolAddress, once per device).
+constexpr size_t kPrefillScratchFloats = (size_t)1 << 20;  // 4 MiB
+hipError_t prefill_scratch(float **out);
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
 

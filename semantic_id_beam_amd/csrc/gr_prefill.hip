@@ -22,10 +22,19 @@
 // All of it is HBM-bound gather and GEMV work: no matrix cores.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <vector>
+
 #include "gr_internal.h"
 
 namespace gr {
 namespace {
+
+// Fixed device array for the soft token's partial sums of the allocation-free prefill
+// (gr_ctx_prefill_noalloc): every call on one GPU shares it.  Host code never passes its name
+// to a kernel (on the host the name is a stand-in, not the device address): the address of
+// each device's copy comes from hipGetSymbolAddress (prefill_scratch).
+static __device__ __align__(256) float scratch[kPrefillScratchFloats];
 
 constexpr int kPfTile = 64;    // tokens per prefill workgroup (the native layout pads to it)
 constexpr int kMaxEmbed = 8192;
@@ -165,7 +174,10 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(const T *__restrict__ tk, c
         __builtin_memcpy(&kc, kt, 16);
         __builtin_memcpy(&vc, vt, 16);
       } else {
-        const size_t row = (((size_t)l * vocab + (size_t)tok[n]) * Hkv + h) * d + (size_t)ch * EPC;
+        // ids from device memory (the allocation-free prefill) are not checked on the host:
+        // clamped into the table, so every read stays in bounds
+        const int id = min(max(tok[n], 0), vocab - 1);
+        const size_t row = (((size_t)l * vocab + (size_t)id) * Hkv + h) * d + (size_t)ch * EPC;
         kc = *reinterpret_cast<const uint4 *>(tk + row);
         vc = *reinterpret_cast<const uint4 *>(tv + row);
       }
@@ -209,8 +221,11 @@ __global__ __launch_bounds__(256) void k_prefill_ctx(const T *__restrict__ tk, c
 }
 
 // Also clears the key-norm / |v| maxima that k_prefill_ctx (launched after it) folds into.
+// The last token's id is last_tok, or (last_dev set) read from device memory and clamped into
+// the table; last_tok < 0 without last_dev: the soft token's query.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prefill_q(const T *__restrict__ tq, int last_tok,
+                                                   const int32_t *__restrict__ last_dev,
                                                    const float *__restrict__ part, int L, int Hq, int Hkv, int d,
                                                    int vocab, T *__restrict__ q_slot, T *__restrict__ q_out,
                                                    uint32_t *__restrict__ kn_bits, uint32_t *__restrict__ vm_bits) {
@@ -222,8 +237,9 @@ __global__ __launch_bounds__(256) void k_prefill_q(const T *__restrict__ tq, int
   }
   if (i >= L * cq) return;
   const int l = i / cq, c = i - l * cq;
-  const T v = last_tok >= 0 ? tq[((size_t)l * vocab + (size_t)last_tok) * cq + c]
-                            : from_f32<T>(soft_col(part, L, ct, l, c));
+  const int lt = last_dev ? min(max(*last_dev, 0), vocab - 1) : last_tok;
+  const T v = lt >= 0 ? tq[((size_t)l * vocab + (size_t)lt) * cq + c]
+                      : from_f32<T>(soft_col(part, L, ct, l, c));
   q_slot[i] = v;
   if (q_out) q_out[i] = v;
 }
@@ -261,19 +277,40 @@ hipError_t launch_prefill_ctx(int elem_bytes, const void *tk, const void *tv, co
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const float *part, int L, int Hq, int Hkv,
-                            int d, int vocab, void *q_slot, void *q_out, float *knmax, float *vscale, hipStream_t st) {
-  if (last_tok >= vocab || (last_tok < 0 && !part) || (elem_bytes != 2 && elem_bytes != 4) || Hkv > Hq * d)
+hipError_t launch_prefill_q(int elem_bytes, const void *tq, int last_tok, const int32_t *last_dev, const float *part,
+                            int L, int Hq, int Hkv, int d, int vocab, void *q_slot, void *q_out, float *knmax,
+                            float *vscale, hipStream_t st) {
+  if (last_tok >= vocab || (last_tok < 0 && !last_dev && !part) || (elem_bytes != 2 && elem_bytes != 4) ||
+      Hkv > Hq * d)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((size_t)L * Hq * d + 255) / 256));
   uint32_t *kb = (uint32_t *)knmax, *vb = (uint32_t *)vscale;
   if (elem_bytes == 2)
-    hipLaunchKernelGGL(k_prefill_q<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)tq, last_tok, part, L, Hq,
-                       Hkv, d, vocab, (uint16_t *)q_slot, (uint16_t *)q_out, kb, vb);
+    hipLaunchKernelGGL(k_prefill_q<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)tq, last_tok, last_dev, part,
+                       L, Hq, Hkv, d, vocab, (uint16_t *)q_slot, (uint16_t *)q_out, kb, vb);
   else
-    hipLaunchKernelGGL(k_prefill_q<float>, grid, dim3(256), 0, st, (const float *)tq, last_tok, part, L, Hq, Hkv, d,
-                       vocab, (float *)q_slot, (float *)q_out, kb, vb);
+    hipLaunchKernelGGL(k_prefill_q<float>, grid, dim3(256), 0, st, (const float *)tq, last_tok, last_dev, part, L, Hq,
+                       Hkv, d, vocab, (float *)q_slot, (float *)q_out, kb, vb);
   return hipGetLastError();
+}
+
+hipError_t prefill_scratch(float **out) {
+  // once per device, with that device current: the address of its copy of the array
+  static std::mutex mu;
+  static std::vector<float *> ptrs;
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= ptrs.size()) ptrs.resize((size_t)dev + 1, nullptr);
+  if (!ptrs[(size_t)dev]) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    ptrs[(size_t)dev] = static_cast<float *>(p);
+  }
+  *out = ptrs[(size_t)dev];
+  return hipSuccess;
 }
 
 }  // namespace gr

@@ -101,6 +101,15 @@ class BeamEngine:
         if k_native is not None:
             self._keep[rid] = (k_native, vt_native)
 
+    def prefill_noalloc(self, rid: int, tokens_dev, beam_width: int, soft_pos: int = -1, user_vec=None,
+                        k_native=None, vt_native=None, q_last_out=None):
+        """prefill() with the token ids in device memory (torch int32 tensor) and no allocation by
+        the library (gr_ctx_prefill_noalloc)."""
+        G.gr_ctx_prefill_noalloc(self.eng, rid, tokens_dev, int(tokens_dev.shape[0]), soft_pos, user_vec, beam_width,
+                                 k_native, vt_native, q_last_out, self.stream)
+        if k_native is not None:
+            self._keep[rid] = (k_native, vt_native)
+
     def step(self, rids):
         G.gr_beam_step(self.eng, rids, self.stream)
 

@@ -35,8 +35,9 @@ GR_STUB(launch_soft_token, const float *, const float *, int, int, const float *
         int, int, float *, float *, hipStream_t)
 GR_STUB(launch_prefill_ctx, int, const void *, const void *, const int32_t *, int, int, int, const float *, int, int,
         int, int, int, void *, void *, float *, float *, hipStream_t)
-GR_STUB(launch_prefill_q, int, const void *, int, const float *, int, int, int, int, int, void *, void *, float *,
-        float *, hipStream_t)
+GR_STUB(launch_prefill_q, int, const void *, int, const int32_t *, const float *, int, int, int, int, int, void *,
+        void *, float *, float *, hipStream_t)
+hipError_t prefill_scratch(float **) { std::abort(); }
 #undef GR_STUB
 }  // namespace gr
 
@@ -113,6 +114,10 @@ int main() {
     {
       const int32_t toks[3] = {0, 1, 2};
       EXPECT(gr_ctx_prefill(e, rid, toks, 3, -1, nullptr, 1, nullptr, nullptr, nullptr, nullptr) == GR_E_BAD_STATE);
+      EXPECT(gr_ctx_prefill_noalloc(e, rid, toks, 3, -1, nullptr, 1, nullptr, nullptr, nullptr, nullptr) ==
+             GR_E_BAD_STATE);
+      EXPECT(gr_ctx_prefill_noalloc(nullptr, rid, toks, 3, -1, nullptr, 1, nullptr, nullptr, nullptr, nullptr) ==
+             GR_E_INVALID_ARG);
       gr_prefill_desc pd{};
       EXPECT(gr_engine_set_prefill(e, &pd) == GR_E_INVALID_ARG);
       pd.vocab = 4;
