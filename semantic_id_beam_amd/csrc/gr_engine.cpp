@@ -832,6 +832,10 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   if (layered)
     for (int i = 0; i < n; ++i) kind[(size_t)i] = full_ctx_kind(kind[(size_t)i]);
   bool any_hparts = false;
+  // split-K steps of bf16 models finish layer l inside the launch of layer l+1 (the model
+  // stand-in's layers do not read each other's output); with one layer per launch every layer
+  // is finished by its own merge launch before the next layer starts
+  const bool defer = d.dtype == 1 && !per_layer;
   std::vector<int> order((size_t)n);
   for (int i = 0; i < n; ++i) order[(size_t)i] = i;
   // within a variant, longest context first: workgroups are dealt out in order as compute
@@ -840,11 +844,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     if (kind[(size_t)a] != kind[(size_t)b]) return kind[(size_t)a] < kind[(size_t)b];
     return rs[(size_t)a]->N > rs[(size_t)b]->N;
   });
-  struct Group { int kind, start, count, wgs, lgroups; };
+  struct Group { int kind, start, count, wgs, lgroups, merge0, merge_wgs, fin0, fin_wgs; };
   std::vector<Group> groups;
   for (int i = 0; i < n; ++i) {
     const int k = kind[(size_t)order[(size_t)i]];
-    if (groups.empty() || groups.back().kind != k) groups.push_back({k, i, 0, 0, 0});
+    if (groups.empty() || groups.back().kind != k) groups.push_back({k, i, 0, 0, 0, 0, 0, 0, 0});
     groups.back().count++;
   }
   const int slot_i = e->ring;
@@ -853,7 +857,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     if ((r = check_dev(e, hipEventSynchronize(e->events[slot_i]), "descriptor ring")) != GR_OK) return r;
   }
   gr::StepReq *hw = e->pinned[slot_i];
-  int wg_merge = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0;
+  int wg_merge = 0, wg_fin = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0;
   for (Group &G : groups) {
     const int nw = G.kind & 0xFF;
     const int rows_wg = d.dtype == 1 ? gr::ctx_rows_per_wg(G.kind) : 32;
@@ -911,6 +915,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       w.splits = S;
       w.tps = tps;
       w.lgroups = lgroups;
+      w.defer_finish = defer ? 1 : 0;
       w.wg_ctx = wg_ctx;
       if (layered)
         wg_ctx += (int)align_up((size_t)d.Hkv * lgroups, 8) * w.row_blocks;
@@ -919,7 +924,15 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       else
         wg_ctx += ceil_div((int64_t)d.Hkv * rows * S, 4);
       w.wg_merge = wg_merge;
+      if (i == G.start) G.merge0 = wg_merge;
+      G.merge_wgs += R->n_bound;
       wg_merge += R->n_bound;
+      // the bf16 layer finish: workgroups over (row block, kv head)
+      const int fin = d.Hkv * ceil_div(rows, gr::fin_rows_per_wg(d.d));
+      w.wg_fin = wg_fin;
+      if (i == G.start) G.fin0 = wg_fin;
+      G.fin_wgs += fin;
+      wg_fin += fin;
       w.wg_logits = wg_logits;
       wg_logits += ceil_div(R->n_bound, 64) * ceil_div(d.V, 64) * gr::kLogitsKS;
       w.wg_lsm = wg_lsm;
@@ -973,6 +986,13 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     }
     return GR_OK;
   };
+  // the finish of one layer for requests [i0, i0 + m) of the step (bf16: the phased finish
+  // kernel over row blocks; float32: one workgroup per beam)
+  auto finish = [&](int i0, int m, int layer, int fin_wgs, int fin0, int merge_wgs, int merge0, hipStream_t s,
+                    gr::LaunchEv ev) -> hipError_t {
+    if (d.dtype == 1) return gr::launch_finish_layer(e->dev, dw + i0, m, layer, fin_wgs, s, ev, fin0);
+    return gr::launch_beam_merge(e->dev, dw + i0, m, layer, merge_wgs, s, ev, merge0);
+  };
   auto marker = [&](int ev) -> gr_status {
     return ev >= 0 ? check_dev(e, hipEventRecord(e->prof_ev[(size_t)ev], st), "profiling event") : GR_OK;
   };
@@ -1003,7 +1023,9 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     }
   }
   // split-K steps with several groups: the same streams; layer l of a group is finished inside
-  // the group's launch of layer l+1, the last layer of every request after the join
+  // the group's launch of layer l+1 and the last layer of every request after the join, or (one
+  // layer per launch) by the group's own merge launch after each layer; the span record then
+  // holds the merges too
   const bool multi = !first_fused && !layered && nstreams > 1;
   if (multi) {
     const auto pc = prof_pair(e, pon);
@@ -1011,18 +1033,25 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     if ((r = marker(pc.first)) != GR_OK || (r = fork()) != GR_OK) return r;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group &G = groups[gi];
-      for (int l = 0; l < d.L; ++l)
+      for (int l = 0; l < d.L; ++l) {
         if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, group_stream(gi)),
                            "context attention")) != GR_OK)
           return r;
+        if (!defer && (r = check_dev(e, finish(G.start, G.count, l, G.fin_wgs, G.fin0, G.merge_wgs, G.merge0,
+                                               group_stream(gi), gr::LaunchEv{}),
+                                     "beam attention/merge")) != GR_OK)
+          return r;
+      }
     }
     if ((r = join()) != GR_OK || (r = marker(pc.second)) != GR_OK) return r;
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, d.L * (int)groups.size());
-    const auto pm = prof_pair(e, pon);
-    if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, d.L - 1, wg_merge, st, prof_ev(e, pm.first, pm.second)),
-                       "beam attention/merge")) != GR_OK)
-      return r;
-    prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
+    if (defer) {
+      const auto pm = prof_pair(e, pon);
+      if ((r = check_dev(e, finish(0, n, d.L - 1, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
+                         "beam attention/merge")) != GR_OK)
+        return r;
+      prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
+    }
   }
   for (int l = 0; l < (first_fused || layered || multi ? 0 : d.L); ++l) {
     const auto pc = prof_pair(e, pon);
@@ -1035,11 +1064,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
         return r;
     }
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, 1, (int)groups.size());
-    // float32: finish every layer separately; bf16: layer l is finished inside layer l+1's
-    // context kernel, and the last layer here
-    if (d.dtype == 0 || l == d.L - 1) {
+    // float32 (and one layer per launch): finish every layer separately; otherwise layer l is
+    // finished inside layer l+1's context kernel, and the last layer here
+    if (!defer || l == d.L - 1) {
       const auto pm = prof_pair(e, pon);
-      if ((r = check_dev(e, gr::launch_beam_merge(e->dev, dw, n, l, wg_merge, st, prof_ev(e, pm.first, pm.second)),
+      if ((r = check_dev(e, finish(0, n, l, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
                          "beam attention/merge")) != GR_OK)
         return r;
       prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);

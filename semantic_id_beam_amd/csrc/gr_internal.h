@@ -72,9 +72,11 @@ struct StepReq {
   int rows_b;           // n_bound * g: row stride of the split-K partials
   int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
   int lgroups;          // full-context steps: layers per launch (else 0)
+  int defer_finish;     // split-K steps: layer l is finished inside layer l+1's launch (else by a merge
+                        // launch after each layer)
   int n_items;          // > 0: scoring request, its n_items candidates' codes are forced (no top-K)
   int row_blocks;       // context-attention row blocks per kv head
-  int wg_ctx, wg_merge, wg_logits, wg_lsm;  // first workgroup of this request in each launch
+  int wg_ctx, wg_merge, wg_logits, wg_lsm, wg_fin;  // first workgroup of this request in each launch
 };
 
 // ---- launchers (gr_kernels.hip) ------------------------------------------
@@ -91,8 +93,16 @@ struct LaunchEv {
 constexpr int kCtxHiLo = 0x100;
 hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                            int ctx_kind, hipStream_t st, LaunchEv ev = {});
+// Finish of `layer` for reqs[0..n_reqs): one workgroup per beam (total_wgs of them); wg0 =
+// reqs[0].wg_merge when reqs starts past the step's first request.
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
-                             hipStream_t st, LaunchEv ev = {});
+                             hipStream_t st, LaunchEv ev = {}, int wg0 = 0);
+// The same finish for bf16 models with the phased loads of the deferred finish: workgroup
+// (request, row block of fin_rows_per_wg(d) rows, kv head); wg0 = reqs[0].wg_fin when reqs starts
+// past the step's first request.
+hipError_t launch_finish_layer(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
+                              hipStream_t st, LaunchEv ev = {}, int wg0 = 0);
+inline int fin_rows_per_wg(int d) { return 2 * 256 / (d / 8); }
 // A first-level step of head_dim-128 bf16 requests with every layer in one launch (grid
 // [total_wgs][L], partials of layer l at row offset l*Hkv*splits*rows_b of buffer 0), and its
 // finish: per-layer outputs into buffer 1, then h = sum over layers in order.

@@ -99,7 +99,8 @@ __device__ __forceinline__ int find_req(const StepReq *reqs, int n, int bid) {
     const int first = FIELD == 0   ? reqs[mid].wg_ctx
                       : FIELD == 1 ? reqs[mid].wg_merge
                       : FIELD == 2 ? reqs[mid].wg_logits
-                                   : reqs[mid].wg_lsm;
+                      : FIELD == 3 ? reqs[mid].wg_lsm
+                                   : reqs[mid].wg_fin;
     if (first <= bid) lo = mid; else hi = mid - 1;
   }
   return lo;
@@ -361,7 +362,7 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
 
   auto run = [&](auto fixed_tag) {
     gload(t0);
-    if (layer > 0) {
+    if (layer > 0 && R.defer_finish) {
       // finish the previous layer for this workgroup's share of the row block (its split
       // partials are complete: that layer's kernel has ended)
       int r0, r1;
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
   }
-  if (!FUSED && !LAYERED && layer > 0) {
+  if (!FUSED && !LAYERED && layer > 0 && R.defer_finish) {
     int r0, r1;
     finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, NT / (D / 8), r0, r1);
     finish_rows<D, 1>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
@@ -1229,7 +1230,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
     }
-    if (!LAYERED && layer > 0) {
+    if (!LAYERED && layer > 0 && R.defer_finish) {
       // finish the previous layer for this workgroup's share of the row block
       int r0, r1;
       finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
@@ -1686,12 +1687,13 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
 // thread = (query head, 8-feature chunk).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void k_beam_merge(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
-                                                    int layer) {
+                                                    int layer, int wg0) {
   constexpr int C8 = D / 8;
-  const int ri = find_req<1>(reqs, n_reqs, blockIdx.x);
+  const int bid = (int)blockIdx.x + wg0;  // reqs may start past the step's first request
+  const int ri = find_req<1>(reqs, n_reqs, bid);
   const StepReq R = reqs[ri];
   const Dims &dm = dev.dm;
-  const int j = blockIdx.x - R.wg_merge;
+  const int j = bid - R.wg_merge;
   uint8_t *slot = slot_base(dev, R.slot);
   const int n_live = ((const int *)(slot + dev.sl.n_live))[R.level & 1];
   if (j >= n_live) return;
@@ -1700,6 +1702,25 @@ __global__ __launch_bounds__(256) void k_beam_merge(Dev dev, const StepReq *__re
     const int hq = e / C8;
     merge_elem<D, T>(dev, R, slot, layer, j, hq % dm.g, hq / dm.g, e % C8);
   }
+}
+
+// Finish of one layer of a split-K step of a bf16 model as a launch of its own (the merge that
+// otherwise runs in the next layer's prologue): workgroup (request, 32- or 64-row block, kv
+// head), finish_rows with two elements per thread (BeamKV append, the beam's own tokens, the
+// split merge in split order, h += o).
+template <int D>
+__global__ __launch_bounds__(256) void k_finish_layer(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                      int layer, int wg0) {
+  constexpr int RPW = 2 * 256 / (D / 8);  // rows per workgroup
+  const int bid = (int)blockIdx.x + wg0;
+  const StepReq R = reqs[find_req<4>(reqs, n_reqs, bid)];
+  const Dims &dm = dev.dm;
+  const int local = bid - R.wg_fin;
+  const int kv = local % dm.Hkv, r0 = (local / dm.Hkv) * RPW;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int rows = ((const int *)(slot + dev.sl.n_live))[R.level & 1] * dm.g;
+  if (r0 >= rows) return;
+  finish_rows<D, 2>(dev, R, slot, layer, kv, r0, min(rows, r0 + RPW), (int)threadIdx.x, 256);
 }
 
 // Finish of a first-level step whose layers ran in one launch (k_ctx_attn_stream<.., true>).
@@ -2545,20 +2566,31 @@ hipError_t launch_finish_first_level(const Dev &dev, const StepReq *reqs, int n_
 }
 
 hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
-                             hipStream_t st, LaunchEv ev) {
+                             hipStream_t st, LaunchEv ev, int wg0) {
   if (total_wgs <= 0) return hipSuccess;
   const dim3 grid(total_wgs), blk(256);
   if (dev.dm.dtype == 0) {
     if (dev.dm.d == 64)
-      launch(k_beam_merge<64, float>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<64, float>, grid, blk, st, ev, dev, reqs, n_reqs, layer, wg0);
     else
-      launch(k_beam_merge<128, float>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<128, float>, grid, blk, st, ev, dev, reqs, n_reqs, layer, wg0);
   } else {
     if (dev.dm.d == 64)
-      launch(k_beam_merge<64, uint16_t>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<64, uint16_t>, grid, blk, st, ev, dev, reqs, n_reqs, layer, wg0);
     else
-      launch(k_beam_merge<128, uint16_t>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_beam_merge<128, uint16_t>, grid, blk, st, ev, dev, reqs, n_reqs, layer, wg0);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_layer(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
+                              hipStream_t st, LaunchEv ev, int wg0) {
+  if (total_wgs <= 0) return hipSuccess;
+  if (dev.dm.dtype != 1) return hipErrorInvalidValue;
+  if (dev.dm.d == 64)
+    launch(k_finish_layer<64>, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs, layer, wg0);
+  else
+    launch(k_finish_layer<128>, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs, layer, wg0);
   return hipGetLastError();
 }
 

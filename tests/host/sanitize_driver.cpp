@@ -18,7 +18,8 @@ namespace gr {
 #define GR_STUB(name, ...) \
   hipError_t name(__VA_ARGS__) { std::abort(); }
 GR_STUB(launch_ctx_attn, const Dev &, const StepReq *, int, int, int, int, hipStream_t, LaunchEv)
-GR_STUB(launch_beam_merge, const Dev &, const StepReq *, int, int, int, hipStream_t, LaunchEv)
+GR_STUB(launch_beam_merge, const Dev &, const StepReq *, int, int, int, hipStream_t, LaunchEv, int)
+GR_STUB(launch_finish_layer, const Dev &, const StepReq *, int, int, int, hipStream_t, LaunchEv, int)
 GR_STUB(launch_ctx_attn_first_level, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_ctx_attn_layered, const Dev &, const StepReq *, int, int, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_sum_hparts, const Dev &, const StepReq *, int, hipStream_t, LaunchEv)
