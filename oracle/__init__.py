@@ -33,6 +33,10 @@ GQA (kv = hq // g); log-softmax normalised over the valid codes (R2) or the
 whole codebook (R1); ties broken by flat index j*V + c ascending; the beam
 count after a step is min(W, number of valid candidates).
 
+* A real layer chain (``chain.py``): a Qwen3-1.7B-shaped pre-norm decoder whose layer l+1
+  reads layer l's output (RMSNorm, q/k/v/o projections, SwiGLU MLP, final RMSNorm), with the
+  bf16 rounding points of its projections' inputs stated as part of the model.
+
 * Prefill (``prefill.py``): the context K/V and first query from context
   token ids, one position optionally a soft token projected from a user
   vector (paper-daily article, section "Getting the user vector into the
@@ -58,3 +62,13 @@ from .beam import (  # noqa: F401
     step_candidates,
 )
 from .prefill import prefill_context, soft_embedding, soft_qkv  # noqa: F401
+from .chain import (  # noqa: F401
+    ChainModel,
+    ChainRequest,
+    beam_chain,
+    bf16_round,
+    chain_hidden,
+    chain_layer_outputs,
+    rms_norm,
+    silu,
+)

@@ -159,7 +159,10 @@ def beam_layer_output(req: Request, model: Model, prefix: Sequence[int], l: int)
 
 
 def beam_hidden(req: Request, model: Model, prefix: Sequence[int]) -> np.ndarray:
-    """Hidden vector of one beam: sum over layers of the attention outputs, head-major [Hq*d]."""
+    """Hidden vector of one beam: sum over layers of the attention outputs, head-major [Hq*d]
+    (a model with its own hidden_of, the layer chain of chain.py, computes it itself)."""
+    if hasattr(model, "hidden_of"):
+        return model.hidden_of(req, prefix)
     h = np.zeros(model.n_q_heads * model.head_dim)
     for l in range(model.n_layers):
         h += beam_layer_output(req, model, prefix, l).reshape(-1)

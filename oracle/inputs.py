@@ -38,3 +38,22 @@ def request_for(cfg, r: int, cache: bool = True) -> Request:
         return kv
 
     return Request(ctx=ctx, q_last=beam.as_f64(synth.q_last(cfg, r)))
+
+
+@functools.lru_cache(maxsize=4)
+def chain_model_for(cfg):
+    """The layer-chain model of a chain workload (every layer's weights on the host)."""
+    import synth
+
+    from .chain import ChainModel
+    return ChainModel.from_arrays(synth.chain_weights(cfg), synth.w_sid(cfg), cfg.n_q_heads, cfg.n_kv_heads)
+
+
+def chain_request_for(cfg, r: int, cache: bool = True):
+    """The chain oracle's view of request r: the context blocks and the last token's input."""
+    import synth
+
+    from .chain import ChainRequest
+    base = request_for(cfg, r, cache)
+    return ChainRequest(ctx=base.ctx, x_last=synth.x_last(cfg, r).astype("float64"))
+

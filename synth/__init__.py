@@ -32,7 +32,15 @@ Value recipes
 from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     BF16_NORMAL_TABLE,
+    CHAIN_MATS,
     bf16_bits_to_f32,
+    chain_embed,
+    chain_gains,
+    chain_matrix,
+    chain_scale,
+    chain_shapes,
+    chain_weights,
+    x_last,
     ctx_kv_block,
     items,
     prefill_tables,

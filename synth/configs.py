@@ -40,6 +40,11 @@ class Config:
     q_scale_log2: int = 0
     k_scale_log2: int = 0
     own_k_scale_log2: int = 0
+    # "tables": q/k/v of a fed-back code from per-(layer, level, code) tables, layers summed;
+    # "chain": a pre-norm decoder layer chain (RMSNorm, q/k/v/o projections, SwiGLU MLP of width
+    # `intermediate`) whose layer l+1 reads layer l's output
+    model: str = "tables"
+    intermediate: int = 0
     notes: str = field(default="", compare=False)
 
     @property
@@ -64,6 +69,9 @@ CONFIGS = {
                item_dist="zipf", notes="wide-request, narrow-beam mix"),
         Config("ragged_r128", 5, "bf16", 128, 28, 16, 8, 128, (500, 8000), (32, 128, 256), 3, 256,
                1_000_000, waves=4, notes="continuous-batching ragged mix in 4 admission waves"),
+        Config("chain_ctx5k_beam256_r8", 6, "bf16", 8, 28, 16, 8, 128, 5000, 256, 3, 256, 1_000_000,
+               model="chain", intermediate=6144,
+               notes="the headline shapes with a Qwen3-1.7B-shaped layer chain (hidden 2048, MLP 6144)"),
     ]
 }
 

@@ -246,3 +246,59 @@ def soft_token_weights(cfg: Config, user_dim: int, embed_dim: int):
     proj = (_philox(cfg, _T_PF_PROJ).standard_normal((user_dim, embed_dim)) * np.sqrt(1.0 / user_dim)).astype(np.float32)
     return (proj, g(0, (L, embed_dim, Hq * d), 1.0 / embed_dim), g(1, (L, embed_dim, Hkv * d), 1.0 / embed_dim),
             g(2, (L, embed_dim, Hkv * d), 1.0 / embed_dim))
+
+
+# ---------------------------------------------------------------- layer-chain weights
+_T_CH_EMBED, _T_CH_W, _T_CH_GAIN, _T_CH_XLAST = range(20, 24)
+CHAIN_MATS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def chain_shapes(cfg: Config) -> dict:
+    """(rows, cols) of each layer matrix (out x in) of the chain model."""
+    D, I = cfg.n_q_heads * cfg.head_dim, cfg.intermediate
+    kvd = cfg.n_kv_heads * cfg.head_dim
+    return {"wq": (D, D), "wk": (kvd, D), "wv": (kvd, D), "wo": (D, D), "wg": (I, D), "wu": (I, D), "wd": (D, I)}
+
+
+def chain_scale(cfg: Config, name: str) -> np.float32:
+    """1/sqrt(fan_in) as float32: a matrix entry is bf16(N(0,1) * scale), rounded to nearest even."""
+    return np.float32(1.0 / np.sqrt(chain_shapes(cfg)[name][1]))
+
+
+def chain_matrix(cfg: Config, name: str, l: int) -> np.ndarray:
+    """Layer l's matrix `name` (out x in), bf16 bit patterns: N(0, 1/fan_in)."""
+    i = CHAIN_MATS.index(name)
+    raw = _bf16_normal(_philox(cfg, _T_CH_W, i, l), chain_shapes(cfg)[name])
+    return _f32_to_bf16_bits(bf16_bits_to_f32(raw) * chain_scale(cfg, name))
+
+
+def chain_embed(cfg: Config) -> np.ndarray:
+    """Input vector of a fed-back code, [levels-1][V][D] bf16 bit patterns, N(0, 1)."""
+    D = cfg.n_q_heads * cfg.head_dim
+    return _bf16_normal(_philox(cfg, _T_CH_EMBED), (max(cfg.n_levels - 1, 0), cfg.codebook, D))
+
+
+def chain_gains(cfg: Config):
+    """RMSNorm gains (g_attn [L][D], g_mlp [L][D], g_final [D]) float32, 1 + 0.1 N(0, 1)."""
+    D, L = cfg.n_q_heads * cfg.head_dim, cfg.n_layers
+    rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, cfg.cfg_id, _T_CH_GAIN]))
+    g = (1.0 + 0.1 * rng.standard_normal((2 * L + 1, D))).astype(np.float32)
+    return g[:L], g[L:2 * L], g[2 * L]
+
+
+def chain_weights(cfg: Config, layers=None) -> dict:
+    """Every weight of the chain model (matrices of the listed layers, default all), host arrays:
+    bf16 bit patterns for embed and the matrices [L][out][in], float32 gains."""
+    layers = range(cfg.n_layers) if layers is None else layers
+    w = {"embed": chain_embed(cfg)}
+    for name in CHAIN_MATS:
+        w[name] = np.stack([chain_matrix(cfg, name, l) for l in layers])
+    w["g_attn"], w["g_mlp"], w["g_final"] = chain_gains(cfg)
+    return w
+
+
+def x_last(cfg: Config, r: int) -> np.ndarray:
+    """Input vector of request r's last context token, [D] float32, N(0, 1)."""
+    D = cfg.n_q_heads * cfg.head_dim
+    return _philox(cfg, _T_CH_XLAST, r).standard_normal(D).astype(np.float32)
+
