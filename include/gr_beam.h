@@ -80,6 +80,35 @@ typedef enum {
 
 typedef struct gr_engine gr_engine; /* opaque */
 
+/* The layer-chain model: a pre-norm decoder of the Qwen3-1.7B shape the pages run the decode on
+ * ([TRT] section "Performance"; [GR] section "语义ID生成式推荐专用推理框架"), with layer l+1's
+ * new-token query, key and value computed from layer l's output.  D = n_q_heads * head_dim.  Per
+ * step s and beam with codes c_0..c_{s-1}, the new token's input vector x is embed[s-1][c_{s-1}]
+ * (s >= 1) or the request's x_last (s = 0; that token's key and value are the context's last
+ * row, so it attends to the context only).  Per layer l, with RMSNorm(x, g) = x / sqrt(mean(x^2)
+ * + rms_eps) * g and b() rounding to bf16 (nearest even):
+ *   xn = b(RMSNorm(x, g_attn[l])); q = b(xn w_q[l]^T), k = b(xn w_k[l]^T), v = b(xn w_v[l]^T)
+ *   o  = attention of q over the context and the beam's own tokens (k, v of each at layer l)
+ *   x += b(o) w_o[l]^T
+ *   xm = b(RMSNorm(x, g_mlp[l])); x += b(silu(xm w_gate[l]^T) * (xm w_up[l]^T)) w_down[l]^T
+ * and the hidden vector is RMSNorm(x, g_final) (float32), projected by w_sid as in the stand-in.
+ * The projections run in float32 on bf16 inputs; the residual x is float32.  Every matrix is
+ * device memory, bf16, row-major "out x in" (K contiguous).  Limits: bf16; n_q_heads * head_dim
+ * and n_kv_heads * head_dim multiples of 128; intermediate a positive multiple of 64. */
+typedef struct {
+  int32_t intermediate;      /* MLP width I */
+  float rms_eps;             /* > 0 */
+  const void *embed;         /* device [n_levels-1][V][D] */
+  const void *w_q;           /* device [L][n_q_heads*head_dim][D] */
+  const void *w_k, *w_v;     /* device [L][n_kv_heads*head_dim][D] */
+  const void *w_o;           /* device [L][D][n_q_heads*head_dim] */
+  const void *w_gate, *w_up; /* device [L][I][D] */
+  const void *w_down;        /* device [L][D][I] */
+  const float *g_attn;       /* device [L][D] */
+  const float *g_mlp;        /* device [L][D] */
+  const float *g_final;      /* device [D] */
+} gr_chain_desc;
+
 /* Model description.  Limits: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
  * n_q_heads * head_dim a multiple of 128; 1 <= n_levels <= 8; 2 <= codebook_size <= 1024
  * and codebook_size**n_levels < 2**62.
@@ -91,10 +120,12 @@ typedef struct {
   int32_t n_levels, codebook_size;
   int32_t dtype; /* gr_dtype: ContextKV, BeamKV and token tables */
   int32_t norm;  /* gr_norm */
-  const void *tok_q;   /* device [L][n_levels-1][V][Hq][d]  */
+  const void *tok_q;   /* device [L][n_levels-1][V][Hq][d]  (the stand-in; unused by a chain) */
   const void *tok_k;   /* device [L][n_levels-1][V][Hkv][d] */
   const void *tok_v;   /* device [L][n_levels-1][V][Hkv][d] */
   const float *w_sid;  /* device [n_levels][Hq*d][V] float32 */
+  const gr_chain_desc *chain; /* host, read at gr_engine_create: the layer-chain model; NULL = the
+                                 table stand-in above */
 } gr_model_desc;
 
 /* The valid items: distinct code tuples (duplicates are tolerated and merged).
@@ -161,10 +192,12 @@ int32_t gr_ctx_padded_len(int32_t ctx_len);
 #define GR_LOAD_ADOPT 1u /* k/v already in the native layout: view them, copy nothing */
 
 /* Admits request `request_id` with its shared context and creates its root
- * beam (empty prefix, score 0).
+ * beam (empty prefix, score 0): the "long shared context loaded once" of [GR] section
+ * "语义ID生成式推荐专用推理框架" (ContextKV, shared by every beam of the request).
  *   ctx_len    N >= 1 context tokens;  beam_width 1 <= W <= max_beam_width.
  *   q_last     device [L][Hq][d] (dtype): query of the last context token,
- *              used at decode step 0; copied.
+ *              used at decode step 0; copied.  Layer-chain model: device [D] float32, the
+ *              last context token's input vector x_last.
  *   flags = 0: k, v are device [L][N][Hkv][d] (dtype); copied and re-laid-out
  *              into the engine's context pool (stream-ordered; the sources may be
  *              freed once the stream has passed this call).
@@ -253,14 +286,19 @@ gr_status gr_ctx_prefill_noalloc(gr_engine *eng, int64_t request_id, const int32
 
 /* Advances each listed request by one decode step (one semantic-ID level),
  * whatever level each one is at: requests at different levels can share a
- * call (continuous batching).  Enqueued on `stream`; returns without waiting.
+ * call (continuous batching, [GR] section "语义ID生成式推荐专用推理框架").  One step is the
+ * beam-search expansion of [TRT] section "Background": every beam attends to its request's
+ * ContextKV and to its own BeamKV tokens through BeamPath, its hidden vector is projected onto
+ * the level's codes, the item-constrained log-softmax and the top-K over beams x codes keep
+ * the best min(W, #valid) candidates, and BeamPath is updated (no KV copy).  Enqueued on `stream`; returns without waiting.
  * Errors: GR_E_INVALID_ARG (n_requests < 1, duplicate ids), GR_E_NOT_FOUND,
  * GR_E_BAD_STATE (a request already decoded all levels); nothing is enqueued
  * when an error is returned. */
 gr_status gr_beam_step(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, void *stream);
 
-/* Multi-beam return after all n_levels steps.  Writes n = min(W, #valid items
- * reachable) beams, best first: codes host [capacity][n_levels], scores host
+/* Multi-beam return after all n_levels steps ([TRT] section "Background": every surviving
+ * beam is returned, not only the best).  Writes n = min(W, #valid items reachable) beams,
+ * best first: codes host [capacity][n_levels], scores host
  * [capacity] (cumulative log-probability).  Synchronises `stream`.
  * Errors: GR_E_BAD_STATE before the last step, GR_E_INVALID_ARG when
  * capacity < n (then *n_beams still receives n). */
@@ -420,7 +458,9 @@ typedef enum {
   GR_PROF_BEAM_MERGE = 1, /* BeamKV append + beam attention + merge, or the sum of hidden-vector partials */
   GR_PROF_LOGITS = 2,     /* codebook logits (one per step) */
   GR_PROF_TOPK = 3,       /* constrained log-softmax + top-K + BeamPath update (one per step) */
-  GR_PROF_STEP = 4        /* a whole gr_beam_step, first launch to last */
+  GR_PROF_STEP = 4,       /* a whole gr_beam_step, first launch to last */
+  GR_PROF_GEMM = 5,       /* layer chain: one projection launch (q/k/v, o, gate/up, down) */
+  GR_PROF_NORM = 6        /* layer chain: input vectors, RMSNorms and the final norm */
 } gr_prof_kind;
 
 /* When enabled, gr_beam_step times each launch with HIP events carried by the
@@ -468,6 +508,18 @@ gr_status gr_debug_hidden(gr_engine *eng, int64_t request_id, int32_t capacity, 
  * step, host [cap][Hq][d] float32.  Needs GR_ENGINE_DEBUG_ATTN. */
 gr_status gr_debug_attn_out(gr_engine *eng, int64_t request_id, int32_t layer, int32_t capacity,
                             float *out, int32_t *n, void *stream);
+
+/* Layer chain, engines created with GR_ENGINE_DEBUG_ATTN: the rows of the last completed step
+ * that enter and leave each projection of layer `layer`, for the request's beams, as float32
+ * host [cap][width]: which = GR_CHAIN_X_IN (the residual entering the layer, D), GR_CHAIN_XN_ATTN
+ * (its norm, the q/k/v projection's input, D), GR_CHAIN_Q (Hq*d), GR_CHAIN_O (the attention
+ * output, the output projection's input, Hq*d), GR_CHAIN_X_MID (the residual after it, D),
+ * GR_CHAIN_XN_MLP (D), GR_CHAIN_ACT (the SwiGLU product, the down projection's input, I),
+ * GR_CHAIN_X_OUT (the residual leaving the layer, D).  bf16 rows are widened exactly. */
+enum { GR_CHAIN_X_IN = 0, GR_CHAIN_XN_ATTN = 1, GR_CHAIN_Q = 2, GR_CHAIN_O = 3, GR_CHAIN_X_MID = 4,
+       GR_CHAIN_XN_MLP = 5, GR_CHAIN_ACT = 6, GR_CHAIN_X_OUT = 7 };
+gr_status gr_debug_chain_rows(gr_engine *eng, int64_t request_id, int32_t layer, int32_t which, int32_t capacity,
+                              float *out, int32_t *n, void *stream);
 
 #ifdef __cplusplus
 }

@@ -36,9 +36,11 @@ EXPORTS = [
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
     "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
     "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
-    "gr_sched_completed", "gr_sched_result", "gr_sched_counts",
+    "gr_sched_completed", "gr_sched_result", "gr_sched_counts", "gr_debug_chain_rows",
 ]
-GR_PROF_CTX_ATTN, GR_PROF_BEAM_MERGE, GR_PROF_LOGITS, GR_PROF_TOPK, GR_PROF_STEP = range(5)
+GR_CHAIN_X_IN, GR_CHAIN_XN_ATTN, GR_CHAIN_Q, GR_CHAIN_O, GR_CHAIN_X_MID, GR_CHAIN_XN_MLP, GR_CHAIN_ACT, \
+    GR_CHAIN_X_OUT = range(8)
+GR_PROF_CTX_ATTN, GR_PROF_BEAM_MERGE, GR_PROF_LOGITS, GR_PROF_TOPK, GR_PROF_STEP, GR_PROF_GEMM, GR_PROF_NORM = range(7)
 
 
 class GrError(RuntimeError):
@@ -47,11 +49,19 @@ class GrError(RuntimeError):
         self.status = status
 
 
+class gr_chain_desc(C.Structure):
+    _fields_ = [("intermediate", C.c_int32), ("rms_eps", C.c_float), ("embed", C.c_void_p), ("w_q", C.c_void_p),
+                ("w_k", C.c_void_p), ("w_v", C.c_void_p), ("w_o", C.c_void_p), ("w_gate", C.c_void_p),
+                ("w_up", C.c_void_p), ("w_down", C.c_void_p), ("g_attn", C.c_void_p), ("g_mlp", C.c_void_p),
+                ("g_final", C.c_void_p)]
+
+
 class gr_model_desc(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("n_levels", C.c_int32), ("codebook_size", C.c_int32),
                 ("dtype", C.c_int32), ("norm", C.c_int32),
-                ("tok_q", C.c_void_p), ("tok_k", C.c_void_p), ("tok_v", C.c_void_p), ("w_sid", C.c_void_p)]
+                ("tok_q", C.c_void_p), ("tok_k", C.c_void_p), ("tok_v", C.c_void_p), ("w_sid", C.c_void_p),
+                ("chain", C.POINTER(gr_chain_desc))]
 
 
 class gr_item_set(C.Structure):
@@ -114,6 +124,7 @@ def lib() -> C.CDLL:
         "gr_topk_select": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "gr_debug_beam_state": (i32, [vp, i64, i32, vp, vp, vp, P(i32), P(i32), vp]),
         "gr_debug_beam_path": (i32, [vp, i64, i32, vp, P(i32), vp]),
+        "gr_debug_chain_rows": (i32, [vp, i64, i32, i32, i32, vp, P(i32), vp]),
         "gr_debug_hidden": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
         "gr_debug_attn_out": (i32, [vp, i64, i32, i32, vp, P(i32), vp]),
         "gr_engine_set_profiling": (i32, [vp, i32]),
@@ -313,6 +324,13 @@ def gr_debug_beam_path(eng: int, rid: int, capacity: int, n_levels: int, stream:
     n = C.c_int32()
     _check(lib().gr_debug_beam_path(eng, rid, capacity, _host(anc), C.byref(n), stream))
     return anc[: min(n.value, capacity)]
+
+
+def gr_debug_chain_rows(eng: int, rid: int, layer: int, which: int, capacity: int, width: int, stream: int = 0):
+    out = np.zeros((capacity, width), dtype=np.float32)
+    n = C.c_int32()
+    _check(lib().gr_debug_chain_rows(eng, rid, layer, which, capacity, _host(out), C.byref(n), stream))
+    return out[: min(n.value, capacity)]
 
 
 def gr_debug_hidden(eng: int, rid: int, capacity: int, hidden_dim: int, V: int, stream: int = 0):

@@ -8,7 +8,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = [os.path.join(PKG, "csrc", f) for f in ("gr_kernels.hip", "gr_prefill.hip", "gr_engine.cpp")]
+SRC = [os.path.join(PKG, "csrc", f) for f in ("gr_kernels.hip", "gr_prefill.hip", "gr_chain.hip", "gr_engine.cpp")]
 OUT = os.path.join(PKG, "libgr_beam.so")
 
 HIP_FLAGS = [

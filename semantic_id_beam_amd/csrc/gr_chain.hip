@@ -1,0 +1,422 @@
+// The layer chain of the decode step on gfx950 (MI355X): projections, norms and the SwiGLU MLP
+// between the attention layers, so that layer l+1's new-token query, key and value come from
+// layer l's output.  The pages run the decode on Qwen3-1.7B (paper-daily.com, "Advancing
+// Generative Recommendation Inference", section "Performance"; zhiding.cn recsys-examples
+// article, section "语义ID生成式推荐专用推理框架"); the layer is a pre-norm decoder layer of that
+// shape with synthetic weights.
+//
+// Rows.  A step's beams are packed row by row, request after request, each request's block
+// starting at a multiple of 32 (row0 of its descriptor) and padded up to the next multiple of
+// 32; the packed row count is padded to a multiple of 128.  Padding rows (beams past the live
+// count, the tail) start at zero and never reach BeamKV or the hidden vector.
+//
+//   k_chain_start   x = the new token's input vector (embed[s-1][code], or the request's x_last
+//                   at s = 0), float32; xn = bf16(RMSNorm(x) * g_attn[0])
+//   k_rmsnorm       xn = bf16(RMSNorm(x) * g)
+//   k_gemm<EPI>     C = A W^T with A [rows][K] bf16 and W [N][K] bf16 (a projection's weight,
+//                   out x in), fp32 accumulation on v_mfma_f32_32x32x16_bf16, and the epilogue:
+//                     EPI_QKV     q -> the step's q rows (bf16), k and v -> BeamKV slot
+//                                 [layer][s-1][beam] of the row's request (bf16)
+//                     EPI_RESID   x += C (float32 residual stream)
+//                     EPI_SWIGLU  act = bf16(silu(gate) * up); the tile's weight rows alternate
+//                                 32 gate rows and the 32 matching up rows
+//   k_chain_final   h = RMSNorm(x) * g_final (float32) into each request's hidden rows
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "gr_internal.h"
+
+namespace gr {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+#define GR_GLOBAL __attribute__((address_space(1)))
+
+template <typename T>
+__device__ __forceinline__ T gld(const void *p) {
+  return *(const GR_GLOBAL T *)(p);
+}
+template <typename T>
+__device__ __forceinline__ void gst(void *p, const T &v) {
+  *(GR_GLOBAL T *)(p) = v;
+}
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];  // the same order in every thread
+  return s;
+}
+
+// packed row -> request: reqs[] ordered by row0
+__device__ __forceinline__ int find_row_req(const StepReq *reqs, int n, int row) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (reqs[mid].row0 <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ uint8_t *slot_of(const Dev &dev, int slot) { return dev.slots + (size_t)slot * dev.sl.slot_bytes; }
+
+// RMSNorm of one float32 row of D into bf16: xn = bf16(x / sqrt(mean(x^2) + eps) * g).  One
+// workgroup of 256 per row, D a multiple of 4 (each thread a 4-element run at a time).
+__device__ __forceinline__ void norm_row(const float *x, const float *g, uint16_t *xn, int D, float eps, float *red) {
+  float ss = 0.f;
+  for (int i = 4 * (int)threadIdx.x; i < D; i += 4 * 256) {
+    const f32x4_t v = gld<f32x4_t>(x + i);
+    ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
+  }
+  const float r = rsqrtf(block_sum(ss, red) / (float)D + eps);
+  for (int i = 4 * (int)threadIdx.x; i < D; i += 4 * 256) {
+    const f32x4_t v = gld<f32x4_t>(x + i), w = gld<f32x4_t>(g + i);
+    gst<u32x2_t>(xn + i, u32x2_t{pack_bf16(v[0] * r * w[0], v[1] * r * w[1]), pack_bf16(v[2] * r * w[2], v[3] * r * w[3])});
+  }
+}
+
+__global__ __launch_bounds__(256) void k_chain_start(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  __shared__ float red[4];
+  const ChainDev &c = dev.ch;
+  const int row = blockIdx.x, D = c.D;
+  float *x = c.x + (size_t)row * D;
+  const StepReq R = reqs[find_row_req(reqs, n_reqs, row)];
+  const uint8_t *slot = slot_of(dev, R.slot);
+  const int s = R.level, j = row - R.row0;
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  const bool live = row >= R.row0 && j < n_live && j < R.n_bound;
+  const float *src = nullptr;
+  const uint16_t *emb = nullptr;
+  if (live) {
+    if (s == 0) {
+      src = (const float *)(slot + dev.sl.q_last);
+    } else {
+      const int code = ((const int *)(slot + dev.sl.codes[s & 1]))[j * dev.dm.levels + (s - 1)];
+      emb = c.embed + ((size_t)(s - 1) * dev.dm.V + code) * D;
+    }
+  }
+  for (int i = 4 * (int)threadIdx.x; i < D; i += 4 * 256) {
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (src) {
+      v = gld<f32x4_t>(src + i);
+    } else if (emb) {
+      const u32x2_t b = gld<u32x2_t>(emb + i);
+      v = f32x4_t{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xFFFF0000u), __uint_as_float(b[1] << 16),
+                  __uint_as_float(b[1] & 0xFFFF0000u)};
+    }
+    gst<f32x4_t>(x + i, v);
+  }
+  __syncthreads();
+  norm_row(x, c.g_attn, c.xn + (size_t)row * D, D, c.eps, red);
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, const float *__restrict__ g,
+                                                 uint16_t *__restrict__ xn, int D, float eps) {
+  __shared__ float red[4];
+  norm_row(x + (size_t)blockIdx.x * D, g, xn + (size_t)blockIdx.x * D, D, eps, red);
+}
+
+__global__ __launch_bounds__(256) void k_chain_final(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  __shared__ float red[4];
+  const ChainDev &c = dev.ch;
+  const int row = blockIdx.x, D = c.D;
+  const StepReq R = reqs[find_row_req(reqs, n_reqs, row)];
+  uint8_t *slot = slot_of(dev, R.slot);
+  const int j = row - R.row0;
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[R.level & 1];
+  if (row < R.row0 || j >= n_live || j >= R.n_bound) return;  // uniform over the workgroup
+  const float *x = c.x + (size_t)row * D;
+  float ss = 0.f;
+  for (int i = 4 * (int)threadIdx.x; i < D; i += 4 * 256) {
+    const f32x4_t v = gld<f32x4_t>(x + i);
+    ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
+  }
+  const float r = rsqrtf(block_sum(ss, red) / (float)D + c.eps);
+  float *h = (float *)(slot + dev.sl.h) + (size_t)j * D;
+  for (int i = 4 * (int)threadIdx.x; i < D; i += 4 * 256) {
+    const f32x4_t v = gld<f32x4_t>(x + i), w = gld<f32x4_t>(c.g_final + i);
+    gst<f32x4_t>(h + i, f32x4_t{v[0] * r * w[0], v[1] * r * w[1], v[2] * r * w[2], v[3] * r * w[3]});
+  }
+}
+
+// ---------------------------------------------------------------------------------------- GEMM
+// Workgroup: 256 threads, four waves in 2 x 2, a 128 (rows) x 128 (weight rows) tile; wave
+// (wm, wn) owns 64 x 64 as 2 x 2 MFMA blocks.  The K loop takes 64 columns per stage: the
+// stage's A and W tiles (16 KB each) go from global memory straight into LDS
+// (global_load_lds_dwordx4, 1 KB of consecutive LDS per wave instruction, 8 per lane and
+// stage), a ring of three stages with two in flight.  LDS rows are 128 bytes (8 chunks of 16);
+// chunk c of row r sits at c ^ (r & 7), so the 32 rows a half-wave reads for one operand hit
+// different banks.  The MFMA computes the transposed block D[n][m] = W_blk (32 x 16) x A_blk^T
+// (16 x 32): lane (m, hh) then holds output row m, columns 8a + 4hh + {0..3} of the block, so
+// each epilogue write is a run of four columns of one row.
+enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+constexpr int GBM = 128, GBN = 128, GBK = 64, GNST = 3;
+
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+struct GemmArgs {
+  const uint16_t *A;    // [rows][K] bf16
+  const uint16_t *W0;   // weight rows: EPI_QKV: q rows [0, n1), k rows [n1, n2), v rows [n2, N);
+  const uint16_t *W1;   //   EPI_SWIGLU: W0 gate [I][K], W1 up [I][K] (N = 2I); else W0 [N][K]
+  const uint16_t *W2;
+  int n1, n2, N, K;
+  int layer;            // EPI_QKV: BeamKV layer
+  float *x;             // EPI_RESID: residual [rows][N] float32
+  uint16_t *out;        // EPI_QKV: q rows [rows][n1]; EPI_SWIGLU: act [rows][N / 2]
+};
+
+// source row of weight-tile row r (tile columns n0 .. n0 + 127)
+template <int EPI>
+__device__ __forceinline__ const uint16_t *w_row(const GemmArgs &g, int n0, int r) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int b = r >> 5, i = n0 / 2 + (b >> 1) * 32 + (r & 31);
+    return ((b & 1) ? g.W1 : g.W0) + (size_t)i * g.K;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int n = n0 + r;
+    return n < g.n1 ? g.W0 + (size_t)n * g.K : n < g.n2 ? g.W1 + (size_t)(n - g.n1) * g.K : g.W2 + (size_t)(n - g.n2) * g.K;
+  } else {
+    return g.W0 + (size_t)(n0 + r) * g.K;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0 || N == 8, "unsupported wait");
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs, GemmArgs g,
+                                              int m_tiles) {
+  __shared__ bf16x8_t sA[GNST][GBM * 8];
+  __shared__ bf16x8_t sW[GNST][GBN * 8];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 1, wn = w >> 1;
+  const int mt = (int)blockIdx.x % m_tiles, nt = (int)blockIdx.x / m_tiles;
+  const int m0 = mt * GBM, n0 = nt * GBN;
+  const int KT = g.K / GBK;
+
+  // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane, row p >> 3, stored
+  // position p & 7 <- global chunk (p & 7) ^ (row & 7); rows 8(i*4+w) .. +7 share one weight block
+  const uint16_t *asrc[4], *wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+    asrc[i] = g.A + (size_t)(m0 + r) * g.K + c * 8;
+    wsrc[i] = w_row<EPI>(g, n0, r) + c * 8;
+  }
+  const uint32_t adst = lds_addr(&sA[0][0]) + w * 1024, wdst = lds_addr(&sW[0][0]) + w * 1024;
+  auto issue = [&](int kt) {
+    const int st = kt % GNST;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * 128) + i * 4096);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (GBN * 128) + i * 4096);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
+
+  issue(0);
+  if (KT > 1) issue(1);
+  const int rl = lane & 31, sw = rl & 7;
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) vm_wait_barrier<8>(); else vm_wait_barrier<0>();
+    if (kt + 2 < KT) issue(kt + 2);  // into the stage of tile kt-1, which every wave has left
+    const int st = kt % GNST;
+    const bf16x8_t *a = &sA[st][0], *b = &sW[st][0];
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      const int ch = (2 * ks + hh) ^ sw;
+      bf16x8_t af[2], wf[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) af[mb] = a[(wm * 64 + mb * 32 + rl) * 8 + ch];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) wf[nb] = b[(wn * 64 + nb * 32 + rl) * 8 + ch];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane (rl, hh) of block (nb, mb) holds row m0 + wm*64 + mb*32 + rl, columns
+  // n0 + wn*64 + nb*32 + 8a + 4hh + c, c = 0..3, in acc[nb][mb][4a + c]
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int row = m0 + wm * 64 + mb * 32 + rl;
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float *p = g.x + (size_t)row * g.N + n0 + wn * 64 + nb * 32 + 8 * a + 4 * hh;
+          const f32x4_t o = gld<f32x4_t>(p);
+          gst<f32x4_t>(p, f32x4_t{o[0] + acc[nb][mb][4 * a], o[1] + acc[nb][mb][4 * a + 1],
+                                  o[2] + acc[nb][mb][4 * a + 2], o[3] + acc[nb][mb][4 * a + 3]});
+        }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // block 0 of the wave holds gate columns, block 1 the matching up columns
+      const int i0 = (n0 + wn * 64) / 2;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float gt = acc[0][mb][4 * a + c], up = acc[1][mb][4 * a + c];
+          v[c] = gt / (1.f + expf(-gt)) * up;
+        }
+        gst<u32x2_t>(g.out + (size_t)row * (g.N / 2) + i0 + 8 * a + 4 * hh,
+                     u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+      }
+    } else {
+      // q columns -> the step's q rows; k, v columns -> BeamKV of the row's request (live beams
+      // at steps s >= 1 only).  The 32 rows of a block belong to one request.
+      const int nb0 = n0 + wn * 64;
+      if (nb0 < g.n1) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            gst<u32x2_t>(g.out + (size_t)row * g.n1 + nb0 + nb * 32 + 8 * a + 4 * hh,
+                         u32x2_t{pack_bf16(acc[nb][mb][4 * a], acc[nb][mb][4 * a + 1]),
+                                 pack_bf16(acc[nb][mb][4 * a + 2], acc[nb][mb][4 * a + 3])});
+      } else {
+        const int blk0 = m0 + wm * 64 + mb * 32;
+        const StepReq R = reqs[find_row_req(reqs, n_reqs, blk0)];
+        const int s = R.level, j = row - R.row0;
+        uint8_t *slot = slot_of(dev, R.slot);
+        const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+        if (s > 0 && blk0 >= R.row0 && j < n_live && j < R.n_bound) {
+          const Dims &dm = dev.dm;
+          const bool is_v = nb0 >= g.n2;
+          uint16_t *kv = (uint16_t *)(slot + (is_v ? dev.sl.beamkv_v : dev.sl.beamkv_k));
+          const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
+          uint16_t *dst = kv + (size_t)g.layer * (dm.levels - 1) * lvstride + (size_t)(s - 1) * lvstride +
+                          (size_t)j * wstride + (nb0 - (is_v ? g.n2 : g.n1));
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+              gst<u32x2_t>(dst + nb * 32 + 8 * a + 4 * hh,
+                           u32x2_t{pack_bf16(acc[nb][mb][4 * a], acc[nb][mb][4 * a + 1]),
+                                   pack_bf16(acc[nb][mb][4 * a + 2], acc[nb][mb][4 * a + 3])});
+        }
+      }
+    }
+  }
+}
+
+template <typename K, typename... Args>
+void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, LaunchEv ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
+}  // namespace
+
+hipError_t launch_chain_start(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
+                              LaunchEv ev) {
+  if (rows <= 0 || rows % 128 != 0 || dev.ch.D % 4 != 0) return hipErrorInvalidValue;
+  launch(k_chain_start, dim3(rows), dim3(256), st, ev, dev, reqs, n_reqs);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_norm(const Dev &dev, const float *g, int rows, hipStream_t st, LaunchEv ev) {
+  if (rows <= 0 || rows % 128 != 0 || dev.ch.D % 4 != 0) return hipErrorInvalidValue;
+  launch(k_rmsnorm, dim3(rows), dim3(256), st, ev, (const float *)dev.ch.x, g, dev.ch.xn, dev.ch.D, dev.ch.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_final(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
+                              LaunchEv ev) {
+  if (rows <= 0 || rows % 128 != 0 || dev.ch.D % 4 != 0) return hipErrorInvalidValue;
+  launch(k_chain_final, dim3(rows), dim3(256), st, ev, dev, reqs, n_reqs);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, int kind, int layer,
+                             hipStream_t st, LaunchEv ev) {
+  const ChainDev &c = dev.ch;
+  const Dims &dm = dev.dm;
+  if (rows <= 0 || rows % GBM != 0 || layer < 0 || layer >= dm.L) return hipErrorInvalidValue;
+  const size_t D = c.D, I = c.I, Dq = (size_t)dm.Hq * dm.d, Dkv = (size_t)dm.Hkv * dm.d;
+  GemmArgs g{};
+  g.layer = layer;
+  int epi;
+  if (kind == kChainQKV) {
+    epi = EPI_QKV;
+    g.A = c.xn;
+    g.W0 = c.wq + layer * Dq * D;
+    g.W1 = c.wk + layer * Dkv * D;
+    g.W2 = c.wv + layer * Dkv * D;
+    g.n1 = (int)Dq;
+    g.n2 = (int)(Dq + Dkv);
+    g.N = (int)(Dq + 2 * Dkv);
+    g.K = (int)D;
+    g.out = c.q;
+  } else if (kind == kChainO) {
+    epi = EPI_RESID;
+    g.A = c.o;
+    g.W0 = c.wo + layer * D * Dq;
+    g.N = (int)D;
+    g.K = (int)Dq;
+    g.x = c.x;
+  } else if (kind == kChainGateUp) {
+    epi = EPI_SWIGLU;
+    g.A = c.xn;
+    g.W0 = c.wg + layer * I * D;
+    g.W1 = c.wu + layer * I * D;
+    g.N = (int)(2 * I);
+    g.K = (int)D;
+    g.out = c.act;
+  } else if (kind == kChainDown) {
+    epi = EPI_RESID;
+    g.A = c.act;
+    g.W0 = c.wd + layer * D * I;
+    g.N = (int)D;
+    g.K = (int)I;
+    g.x = c.x;
+  } else {
+    return hipErrorInvalidValue;
+  }
+  if (g.N % GBN != 0 || g.K % GBK != 0) return hipErrorInvalidValue;
+  const int m_tiles = rows / GBM;
+  const dim3 grid((unsigned)(m_tiles * (g.N / GBN)));
+  if (epi == EPI_QKV) launch(k_gemm<EPI_QKV>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+  else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+  else launch(k_gemm<EPI_SWIGLU>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace gr

@@ -45,6 +45,7 @@ struct gr_engine {
   gr::Dev dev{};
   gr_model_desc model{};
   gr_engine_opts opts{};
+  gr_chain_desc chain{};  // the layer-chain model (dm.chain), copied at create
   int elem = 2;
 
   // trie, host copy: levels 0..n_levels-1 hold masks and first-child indices
@@ -55,6 +56,9 @@ struct gr_engine {
 
   // workspace layout (byte offsets)
   size_t off_mask = 0, off_child = 0, off_slots = 0, off_pool = 0, off_work = 0, off_out = 0, ws_need = 0;
+  size_t off_chain = 0, chain_bytes = 0;  // the layer chain's activation rows
+  size_t off_chain_dbg = 0, chain_dbg_layer = 0;  // debug copies of them, per layer
+  int chain_rows = 0;                     // rows of those buffers (a multiple of 128)
   size_t work_bytes = 0;  // one ring entry
   size_t out_bytes = 0;   // results of one request in the staging area (gr_beams_get_batch)
   uint8_t *out_host = nullptr;  // pinned copy of the staging area
@@ -71,6 +75,7 @@ struct gr_engine {
     int slot = -1;
     int N = 0, Np = 0, W = 0, level = 0, n_bound = 1;
     int n_items = 0;  // > 0 while the request scores given items (gr_score_items)
+    int last_row0 = 0;  // the layer chain: the request's first packed row in its last step
     bool adopt = false;
     int64_t pool_off = -1;
     const void *k = nullptr, *vt = nullptr;
@@ -85,9 +90,10 @@ struct gr_engine {
   int prof_next = 0;  // next unused event of the pool
   struct ProfRec { int kind, level, a, b, count, disp; };  // count: layer steps, disp: kernel dispatches
   std::vector<ProfRec> prof_pending;
-  double prof_ms[5][gr::kMaxLevels + 1] = {};
-  int64_t prof_n[5][gr::kMaxLevels + 1] = {};
-  int64_t prof_d[5][gr::kMaxLevels + 1] = {};
+  static constexpr int kProfKinds = GR_PROF_NORM + 1;
+  double prof_ms[kProfKinds][gr::kMaxLevels + 1] = {};
+  int64_t prof_n[kProfKinds][gr::kMaxLevels + 1] = {};
+  int64_t prof_d[kProfKinds][gr::kMaxLevels + 1] = {};
 
   // split-K steps with several variant groups: each group's chain of layer launches depends
   // only on itself, so groups 1..3 (mod 4) run on their own streams, forked from and joined
@@ -236,7 +242,7 @@ void layout(gr_engine *e) {
   const size_t kv = (size_t)d.L * (d.levels - 1) * W * d.Hkv * d.d * el;
   s.beamkv_k = take(kv);
   s.beamkv_v = take(kv);
-  s.q_last = take((size_t)d.L * d.Hq * d.d * el);
+  s.q_last = take(std::max((size_t)d.L * d.Hq * d.d * el, (size_t)d.Hq * d.d * 4));  // chain: x_last [D] f32
   s.knmax = take((size_t)d.L * d.Hkv * 4);
   s.vscale = take((size_t)d.L * d.Hkv * 4);
   s.h = take(W * d.Hq * d.d * 4);
@@ -279,6 +285,22 @@ void layout(gr_engine *e) {
   e->out_bytes = align_up(16 + W * d.levels * 4 + W * 4, A);
   e->off_out = w;
   w = align_up(w + e->out_bytes * (size_t)e->opts.max_requests, A);
+  if (d.chain) {
+    // every request's beams packed at 32-row boundaries, padded to 128: x f32 [D], xn bf16 [D],
+    // q and o bf16 [Hq d], act bf16 [I]
+    const size_t rows = align_up((size_t)e->opts.max_requests * align_up(W, 32), 128);
+    const size_t D = (size_t)d.Hq * d.d, I = (size_t)e->chain.intermediate;
+    e->chain_rows = (int)rows;
+    e->off_chain = w;
+    e->chain_bytes = align_up(rows * (D * 4 + D * 2 + 2 * D * 2 + I * 2), A);
+    w = align_up(w + e->chain_bytes, A);
+    if (d.debug_attn) {
+      // per layer, copies of the rows entering and leaving each projection (gr_debug_chain_rows)
+      e->off_chain_dbg = w;
+      e->chain_dbg_layer = align_up(rows * (4 * D * 4 + 2 * D * 2 + 2 * D * 2 + I * 2), A);
+      w = align_up(w + e->chain_dbg_layer * (size_t)d.L, A);
+    }
+  }
   e->ws_need = w;
 }
 
@@ -313,6 +335,23 @@ void pool_free(gr_engine *e, int64_t off, int64_t n) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// debug copy of chain rows `which` of layer l (layout of one layer: X_IN, X_MID, X_OUT f32 [rows][D];
+// XN_ATTN, XN_MLP bf16 [rows][D]; Q, O bf16 [rows][Hq d]; ACT bf16 [rows][I]; one spare f32 [rows][D])
+uint8_t *chain_dbg(gr_engine *e, int l, int which) {
+  const size_t rows = (size_t)e->chain_rows, D = (size_t)e->dm.Hq * e->dm.d;
+  uint8_t *b = e->ws + e->off_chain_dbg + e->chain_dbg_layer * (size_t)l;
+  switch (which) {
+    case GR_CHAIN_X_IN: return b;
+    case GR_CHAIN_X_MID: return b + rows * D * 4;
+    case GR_CHAIN_X_OUT: return b + 2 * rows * D * 4;
+    case GR_CHAIN_XN_ATTN: return b + 4 * rows * D * 4;
+    case GR_CHAIN_XN_MLP: return b + 4 * rows * D * 4 + rows * D * 2;
+    case GR_CHAIN_Q: return b + 4 * rows * D * 4 + 2 * rows * D * 2;
+    case GR_CHAIN_O: return b + 4 * rows * D * 4 + 3 * rows * D * 2;
+    default: return b + 4 * rows * D * 4 + 4 * rows * D * 2;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,8 +385,20 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   if (m->dtype != GR_DTYPE_F32 && m->dtype != GR_DTYPE_BF16) return fail(GR_E_INVALID_ARG, "dtype");
   if (m->norm != GR_NORM_VALID && m->norm != GR_NORM_FULL) return fail(GR_E_INVALID_ARG, "norm");
   if (!m->w_sid) return fail(GR_E_INVALID_ARG, "w_sid is null");
-  if (m->n_levels > 1 && (!m->tok_q || !m->tok_k || !m->tok_v))
+  if (m->chain) {
+    const gr_chain_desc *c = m->chain;
+    if (m->dtype != GR_DTYPE_BF16) return fail(GR_E_UNSUPPORTED, "the layer chain runs in bf16 only");
+    if ((m->n_q_heads * m->head_dim) % 128 != 0 || (m->n_kv_heads * m->head_dim) % 128 != 0)
+      return fail(GR_E_UNSUPPORTED, "the layer chain needs n_q_heads*head_dim and n_kv_heads*head_dim multiples of 128");
+    if (c->intermediate < 64 || c->intermediate % 64 != 0 || c->intermediate > (1 << 20))
+      return fail(GR_E_UNSUPPORTED, "intermediate must be a positive multiple of 64");
+    if (!(c->rms_eps > 0.f)) return fail(GR_E_INVALID_ARG, "rms_eps must be > 0");
+    if ((m->n_levels > 1 && !c->embed) || !c->w_q || !c->w_k || !c->w_v || !c->w_o || !c->w_gate || !c->w_up ||
+        !c->w_down || !c->g_attn || !c->g_mlp || !c->g_final)
+      return fail(GR_E_INVALID_ARG, "a layer-chain weight is null");
+  } else if (m->n_levels > 1 && (!m->tok_q || !m->tok_k || !m->tok_v)) {
     return fail(GR_E_INVALID_ARG, "token tables are null");
+  }
   if (items->n_items < 1 || !items->codes) return fail(GR_E_INVALID_ARG, "empty item set");
   if (o->max_requests < 1 || o->max_requests > 65536) return fail(GR_E_INVALID_ARG, "max_requests must be in [1, 65536]");
   if (o->max_beam_width < 1 || o->max_beam_width > gr::kMaxBeam)
@@ -360,6 +411,8 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   gr_engine *e = new gr_engine();
   e->model = *m;
   e->opts = *o;
+  if (m->chain) e->chain = *m->chain;
+  e->model.chain = nullptr;  // the description is copied: the caller's may go away
   if (e->opts.max_splits == 0) e->opts.max_splits = 4;
   e->elem = m->dtype == GR_DTYPE_BF16 ? 2 : 4;
   gr::Dims &d = e->dm;
@@ -377,6 +430,7 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   d.norm = m->norm == GR_NORM_FULL ? 1 : 0;
   d.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
   d.debug_attn = (o->flags & GR_ENGINE_DEBUG_ATTN) ? 1 : 0;
+  d.chain = m->chain ? 1 : 0;
   gr_status st = build_trie(e, items);
   if (st != GR_OK) {
     delete e;
@@ -450,6 +504,34 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
   dv.tok_k = e->model.tok_k;
   dv.tok_v = e->model.tok_v;
   dv.w_sid = e->model.w_sid;
+  if (e->dm.chain) {
+    gr::ChainDev &c = dv.ch;
+    const gr_chain_desc &cd = e->chain;
+    const size_t rows = (size_t)e->chain_rows, D = (size_t)e->dm.Hq * e->dm.d, I = (size_t)cd.intermediate;
+    c.D = (int)D;
+    c.I = (int)I;
+    c.eps = cd.rms_eps;
+    c.embed = (const uint16_t *)cd.embed;
+    c.wq = (const uint16_t *)cd.w_q;
+    c.wk = (const uint16_t *)cd.w_k;
+    c.wv = (const uint16_t *)cd.w_v;
+    c.wo = (const uint16_t *)cd.w_o;
+    c.wg = (const uint16_t *)cd.w_gate;
+    c.wu = (const uint16_t *)cd.w_up;
+    c.wd = (const uint16_t *)cd.w_down;
+    c.g_attn = cd.g_attn;
+    c.g_mlp = cd.g_mlp;
+    c.g_final = cd.g_final;
+    uint8_t *b = e->ws + e->off_chain;
+    c.x = (float *)b;
+    c.xn = (uint16_t *)(b + rows * D * 4);
+    c.q = c.xn + rows * D;
+    c.o = c.q + rows * D;
+    c.act = c.o + rows * D;
+    // padding rows are read by the projections: start every row at zero (finite)
+    if ((r = check_dev(e, hipMemsetAsync(b, 0, e->chain_bytes, st), "chain rows")) != GR_OK) return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "chain rows")) != GR_OK) return r;
+  }
   e->bound = true;
   return GR_OK;
 }
@@ -485,6 +567,7 @@ gr_status gr_engine_destroy(gr_engine *e) {
 gr_status gr_engine_set_prefill(gr_engine *e, const gr_prefill_desc *p) {
   if (!e || !p) return fail(GR_E_INVALID_ARG, "null engine or prefill description");
   if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
+  if (e->dm.chain) return fail(GR_E_UNSUPPORTED, "the layer chain takes its context from gr_ctx_kv_load");
   if (p->vocab < 1 || !p->tok_q || !p->tok_k || !p->tok_v) return fail(GR_E_INVALID_ARG, "need vocab >= 1 and three tables");
   if (p->user_dim < 0 || p->user_dim > 8192) return fail(GR_E_INVALID_ARG, "user_dim must be in [0, 8192]");
   if (p->user_dim > 0 && (p->embed_dim < 1 || p->embed_dim > 8192 || !p->proj || !p->w_q || !p->w_k || !p->w_v))
@@ -732,8 +815,9 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
     if (!adopt) pool_free(e, R.pool_off, Np);
     return r;
   }
-  if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem,
-                                       hipMemcpyDeviceToDevice, st), "q_last copy")) != GR_OK)
+  const size_t qbytes = e->dm.chain ? (size_t)e->dm.Hq * e->dm.d * 4 : (size_t)e->dm.L * e->dm.Hq * e->dm.d * e->elem;
+  if ((r = check_dev(e, hipMemcpyAsync(sb + e->sl.q_last, q_last, qbytes, hipMemcpyDeviceToDevice, st), "q_last copy")) !=
+      GR_OK)
     return r;
   if ((r = check_dev(e, gr::launch_init_slots(e->dev, &R.slot, 1, st), "slot init")) != GR_OK) return r;
   e->free_slots.pop_back();
@@ -807,7 +891,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   // A first-level step (every request at level 0) runs all layers' context attention in one
   // launch: each layer's query is an input there.  Needs room for every layer's partials in
   // one partial buffer and for the per-layer outputs in the other.
-  const bool per_layer = (e->opts.flags & GR_ENGINE_PER_LAYER) != 0;  // no launch covers two layers
+  // no launch covers two layers (the layer chain: every layer reads the previous one's output)
+  const bool per_layer = (e->opts.flags & GR_ENGINE_PER_LAYER) != 0 || d.chain;
   bool first_fused = !per_layer && d.dtype == 1 && d.d == 128 && d.L > 1 && (int64_t)d.L <= (int64_t)d.S_max * d.W_max;
   for (int i = 0; i < n && first_fused; ++i) first_fused = rs[(size_t)i]->level == 0;
   std::vector<int> kind((size_t)n);
@@ -821,7 +906,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   // blocks, so a step that mixes levels (continuous batching) stays on this path.
   const int lg_max = per_layer ? 1 : std::min(d.L, d.S_max);
   auto full_ctx_kind = [](int k) { return (k & 0xFF) == 8 ? k : (2 | gr::kCtxHiLo); };
-  bool layered = d.dtype == 1 && d.d == 128 && !first_fused;
+  bool layered = d.dtype == 1 && d.d == 128 && !first_fused && !d.chain;
   double fill = 0.0;  // resident-workgroup rounds the step's row blocks fill over lg_max layers
   for (int i = 0; i < n && layered; ++i) {
     const int k = full_ctx_kind(kind[(size_t)i]);
@@ -857,7 +942,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     if ((r = check_dev(e, hipEventSynchronize(e->events[slot_i]), "descriptor ring")) != GR_OK) return r;
   }
   gr::StepReq *hw = e->pinned[slot_i];
-  int wg_merge = 0, wg_fin = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0;
+  int wg_merge = 0, wg_fin = 0, wg_logits = 0, wg_lsm = 0, max_cand = 0, row_acc = 0;
   for (Group &G : groups) {
     const int nw = G.kind & 0xFF;
     const int rows_wg = d.dtype == 1 ? gr::ctx_rows_per_wg(G.kind) : 32;
@@ -916,6 +1001,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       w.tps = tps;
       w.lgroups = lgroups;
       w.defer_finish = defer ? 1 : 0;
+      w.row0 = row_acc;  // the layer chain's packed rows: each request at a multiple of 32
+      row_acc += (int)align_up((size_t)R->n_bound, 32);
       w.wg_ctx = wg_ctx;
       if (layered)
         wg_ctx += (int)align_up((size_t)d.Hkv * lgroups, 8) * w.row_blocks;
@@ -950,7 +1037,7 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   int plevel = rs[0]->level;
   for (auto *R : rs)
     if (R->level != plevel) plevel = d.levels;
-  const bool pon = prof_reserve(e, 2 * (2 * d.L + 2));
+  const bool pon = prof_reserve(e, 2 * ((d.chain ? 8 : 2) * d.L + 4));
   int step_start = -1;
   if (first_fused) {
     const auto pc = prof_pair(e, pon);
@@ -969,7 +1056,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
   // several variant groups: each group's launches depend only on that group's earlier ones,
   // so group gi runs on stream gi mod 4 (the caller's stream or an engine-owned one), forked
   // from and joined into the caller's stream; a span record then uses marker events on it
-  const int nstreams = d.dtype == 1 && !first_fused ? (int)std::min<size_t>(kAuxStreams + 1, groups.size()) : 1;
+  const int nstreams =
+      d.dtype == 1 && !first_fused && !d.chain ? (int)std::min<size_t>(kAuxStreams + 1, groups.size()) : 1;
   auto group_stream = [&](size_t gi) { return gi % (kAuxStreams + 1) == 0 ? st : e->aux[gi % (kAuxStreams + 1) - 1]; };
   auto fork = [&]() -> gr_status {
     gr_status q;
@@ -1053,7 +1141,88 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
     }
   }
-  for (int l = 0; l < (first_fused || layered || multi ? 0 : d.L); ++l) {
+  if (d.chain) {
+    // the layer chain, one layer after another: q/k/v projection (k, v into BeamKV), context
+    // attention (split-K, every variant group), the layer's finish (o rows), output projection
+    // into the residual, the MLP's norm, gate/up with SwiGLU, down into the residual, the next
+    // layer's norm; then the final norm into each request's hidden rows
+    const int rows = (int)align_up((size_t)row_acc, 128);
+    if (rows > e->chain_rows) return fail(GR_E_BAD_STATE, "step rows exceed the chain buffers");  // cannot happen
+    auto rec = [&](int kind, std::pair<int, int> ab) { prof_record(e, kind, plevel, ab); };
+    auto pn = prof_pair(e, pon);
+    step_start = pn.first;
+    if ((r = check_dev(e, gr::launch_chain_start(e->dev, dw, n, rows, st, prof_ev(e, pn.first, pn.second)),
+                       "chain start")) != GR_OK)
+      return r;
+    rec(GR_PROF_NORM, pn);
+    const size_t D = (size_t)d.Hq * d.d;
+    for (int l = 0; l < d.L; ++l) {
+      auto gemm = [&](int kind) -> gr_status {
+        const auto pg = prof_pair(e, pon);
+        gr_status q = check_dev(e, gr::launch_chain_gemm(e->dev, dw, n, rows, kind, l, st, prof_ev(e, pg.first, pg.second)),
+                                "chain projection");
+        if (q == GR_OK) rec(GR_PROF_GEMM, pg);
+        return q;
+      };
+      auto norm = [&](const float *g) -> gr_status {
+        const auto pq = prof_pair(e, pon);
+        gr_status q = check_dev(e, gr::launch_chain_norm(e->dev, g, rows, st, prof_ev(e, pq.first, pq.second)),
+                                "chain norm");
+        if (q == GR_OK) rec(GR_PROF_NORM, pq);
+        return q;
+      };
+      // debug engines keep a copy of the rows entering and leaving each projection
+      const size_t crow = (size_t)rows;
+      auto snap = [&](int which) -> gr_status {
+        if (!d.debug_attn) return GR_OK;
+        const gr::ChainDev &c = e->dev.ch;
+        const size_t Dq = D, I = (size_t)c.I;
+        const void *src = nullptr;
+        size_t bytes = 0;
+        switch (which) {
+          case GR_CHAIN_X_IN: case GR_CHAIN_X_MID: case GR_CHAIN_X_OUT: src = c.x; bytes = crow * D * 4; break;
+          case GR_CHAIN_XN_ATTN: case GR_CHAIN_XN_MLP: src = c.xn; bytes = crow * D * 2; break;
+          case GR_CHAIN_Q: src = c.q; bytes = crow * Dq * 2; break;
+          case GR_CHAIN_O: src = c.o; bytes = crow * Dq * 2; break;
+          default: src = c.act; bytes = crow * I * 2; break;
+        }
+        return check_dev(e, hipMemcpyAsync(chain_dbg(e, l, which), src, bytes, hipMemcpyDeviceToDevice, st), "debug copy");
+      };
+      if ((r = snap(GR_CHAIN_X_IN)) != GR_OK || (r = snap(GR_CHAIN_XN_ATTN)) != GR_OK) return r;
+      if ((r = gemm(gr::kChainQKV)) != GR_OK) return r;
+      if ((r = snap(GR_CHAIN_Q)) != GR_OK) return r;
+      const auto pc = prof_pair(e, pon);
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const Group &G = groups[gi];
+        const gr::LaunchEv ev = prof_ev(e, gi == 0 ? pc.first : -1, gi + 1 == groups.size() ? pc.second : -1);
+        if ((r = check_dev(e, gr::launch_ctx_attn(e->dev, dw + G.start, G.count, l, G.wgs, G.kind, st, ev),
+                           "context attention")) != GR_OK)
+          return r;
+      }
+      prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, 1, (int)groups.size());
+      const auto pm = prof_pair(e, pon);
+      if ((r = check_dev(e, finish(0, n, l, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
+                         "layer finish")) != GR_OK)
+        return r;
+      rec(GR_PROF_BEAM_MERGE, pm);
+      if ((r = snap(GR_CHAIN_O)) != GR_OK) return r;
+      if ((r = gemm(gr::kChainO)) != GR_OK) return r;
+      if ((r = snap(GR_CHAIN_X_MID)) != GR_OK) return r;
+      if ((r = norm(e->chain.g_mlp + (size_t)l * D)) != GR_OK) return r;
+      if ((r = snap(GR_CHAIN_XN_MLP)) != GR_OK) return r;
+      if ((r = gemm(gr::kChainGateUp)) != GR_OK) return r;
+      if ((r = snap(GR_CHAIN_ACT)) != GR_OK) return r;
+      if ((r = gemm(gr::kChainDown)) != GR_OK) return r;
+      if ((r = snap(GR_CHAIN_X_OUT)) != GR_OK) return r;
+      if (l + 1 < d.L && (r = norm(e->chain.g_attn + (size_t)(l + 1) * D)) != GR_OK) return r;
+    }
+    pn = prof_pair(e, pon);
+    if ((r = check_dev(e, gr::launch_chain_final(e->dev, dw, n, rows, st, prof_ev(e, pn.first, pn.second)),
+                       "chain final norm")) != GR_OK)
+      return r;
+    rec(GR_PROF_NORM, pn);
+  }
+  for (int l = 0; l < (first_fused || layered || multi || d.chain ? 0 : d.L); ++l) {
     const auto pc = prof_pair(e, pon);
     if (l == 0) step_start = pc.first;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
@@ -1086,6 +1255,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     return r;
   prof_record(e, GR_PROF_TOPK, plevel, pt);
   prof_record(e, GR_PROF_STEP, plevel, {step_start, pt.second});
+  for (int i = 0; i < n; ++i)  // descriptor i belongs to request order[i]
+    rs[(size_t)order[(size_t)i]]->last_row0 = hw[i].row0;
   for (auto *R : rs) {
     const int s = R->level;
     int64_t nb = std::min<int64_t>((int64_t)R->W, (int64_t)R->n_bound * d.V);
@@ -1331,6 +1502,45 @@ gr_status gr_debug_attn_out(gr_engine *e, int64_t rid, int32_t layer, int32_t ca
   return GR_OK;
 }
 
+gr_status gr_debug_chain_rows(gr_engine *e, int64_t rid, int32_t layer, int32_t which, int32_t cap, float *out,
+                              int32_t *n, void *stream) {
+  gr_engine::Req *R;
+  gr_status r = find_req(e, rid, &R);
+  if (r != GR_OK) return r;
+  if (!e->dm.chain || !e->dm.debug_attn) return fail(GR_E_BAD_STATE, "needs a layer-chain engine with GR_ENGINE_DEBUG_ATTN");
+  if (!out || !n || cap < 0) return fail(GR_E_INVALID_ARG, "null output");
+  if (layer < 0 || layer >= e->dm.L) return fail(GR_E_INVALID_ARG, "layer out of range");
+  if (which < GR_CHAIN_X_IN || which > GR_CHAIN_X_OUT) return fail(GR_E_INVALID_ARG, "unknown row kind");
+  if (R->level < 1) return fail(GR_E_BAD_STATE, "no step completed yet");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *sb = slot_ptr(e, R);
+  const int prev = (R->level - 1) & 1;
+  int32_t nl = 0;
+  if ((r = d2h(e, &nl, sb + e->sl.n_live + 4 * prev, 4, st)) != GR_OK) return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  *n = nl;
+  const int m = std::min(nl, cap);
+  const size_t D = (size_t)e->dm.Hq * e->dm.d;
+  const size_t width = which == GR_CHAIN_ACT ? (size_t)e->chain.intermediate : D;
+  const bool f32 = which == GR_CHAIN_X_IN || which == GR_CHAIN_X_MID || which == GR_CHAIN_X_OUT;
+  if (m > 0) {
+    const uint8_t *src = chain_dbg(e, layer, which) + (size_t)R->last_row0 * width * (f32 ? 4 : 2);
+    std::vector<uint8_t> raw((size_t)m * width * (f32 ? 4 : 2));
+    if ((r = d2h(e, raw.data(), src, raw.size(), st)) != GR_OK) return r;
+    if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+    if (f32) {
+      std::memcpy(out, raw.data(), raw.size());
+    } else {
+      for (size_t i = 0; i < (size_t)m * width; ++i) {
+        const uint32_t b = (uint32_t)raw[2 * i] | ((uint32_t)raw[2 * i + 1] << 8);
+        const uint32_t u = b << 16;
+        std::memcpy(out + i, &u, 4);
+      }
+    }
+  }
+  return GR_OK;
+}
+
 gr_status gr_engine_set_profiling(gr_engine *e, int32_t enable) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
@@ -1340,7 +1550,7 @@ gr_status gr_engine_set_profiling(gr_engine *e, int32_t enable) {
 
 gr_status gr_engine_profile_read(gr_engine *e, int32_t kind, int32_t level, double *total_ms, int64_t *launches) {
   if (!e || !total_ms || !launches) return fail(GR_E_INVALID_ARG, "null argument");
-  if (kind < 0 || kind > GR_PROF_STEP) return fail(GR_E_INVALID_ARG, "unknown profile kind");
+  if (kind < 0 || kind > GR_PROF_NORM) return fail(GR_E_INVALID_ARG, "unknown profile kind");
   if (level < -1 || level > e->dm.levels) return fail(GR_E_INVALID_ARG, "level out of range");
   gr_status r = prof_fold(e);
   if (r != GR_OK) return r;
@@ -1358,7 +1568,7 @@ gr_status gr_engine_profile_read(gr_engine *e, int32_t kind, int32_t level, doub
 
 gr_status gr_engine_profile_dispatches(gr_engine *e, int32_t kind, int32_t level, int64_t *dispatches) {
   if (!e || !dispatches) return fail(GR_E_INVALID_ARG, "null argument");
-  if (kind < 0 || kind > GR_PROF_STEP) return fail(GR_E_INVALID_ARG, "unknown profile kind");
+  if (kind < 0 || kind > GR_PROF_NORM) return fail(GR_E_INVALID_ARG, "unknown profile kind");
   if (level < -1 || level > e->dm.levels) return fail(GR_E_INVALID_ARG, "level out of range");
   gr_status r = prof_fold(e);
   if (r != GR_OK) return r;

@@ -24,6 +24,7 @@ struct Dims {
   int norm;    // 0 valid, 1 full
   float scale_log2;  // log2(e) / sqrt(d)
   int debug_attn;
+  int chain;         // 1: the layer-chain model (q of a step from the q rows, outputs to the o rows)
 };
 
 // Byte offsets of the arrays inside one request slot; slots are slot_bytes apart.
@@ -50,6 +51,20 @@ struct SlotLayout {
   size_t hl;                  // full-context steps: [L][W_max][Hq][d] f32 o/l of each layer (0 when impossible)
 };
 
+// The layer chain's weights and per-step activation rows (gr_chain.hip).  Rows: a step's beams
+// packed request after request (StepReq::row0), padded to a multiple of 128.
+struct ChainDev {
+  int D, I;          // hidden (= Hq * d) and MLP width
+  float eps;
+  const uint16_t *embed;                      // [levels-1][V][D] bf16
+  const uint16_t *wq, *wk, *wv, *wo;          // [L][Hq d][D], [L][Hkv d][D] x2, [L][D][Hq d]
+  const uint16_t *wg, *wu, *wd;               // [L][I][D] x2, [L][D][I]
+  const float *g_attn, *g_mlp, *g_final;      // [L][D], [L][D], [D]
+  float *x;                                   // residual rows [rows][D] float32
+  uint16_t *xn, *q, *o, *act;                 // bf16 rows: [rows][D], [rows][Hq d] x2, [rows][I]
+};
+enum { kChainQKV = 0, kChainO = 1, kChainGateUp = 2, kChainDown = 3 };
+
 struct Dev {
   Dims dm;
   SlotLayout sl;
@@ -59,6 +74,7 @@ struct Dev {
   int64_t trie_off[kMaxLevels + 1];  // node offset of level t
   const void *tok_q, *tok_k, *tok_v;
   const float *w_sid;
+  ChainDev ch;
 };
 
 // One request of one gr_beam_step call.
@@ -74,6 +90,7 @@ struct StepReq {
   int lgroups;          // full-context steps: layers per launch (else 0)
   int defer_finish;     // split-K steps: layer l is finished inside layer l+1's launch (else by a merge
                         // launch after each layer)
+  int row0;             // the layer chain: first packed row of this request (a multiple of 32)
   int n_items;          // > 0: scoring request, its n_items candidates' codes are forced (no top-K)
   int row_blocks;       // context-attention row blocks per kv head
   int wg_ctx, wg_merge, wg_logits, wg_lsm, wg_fin;  // first workgroup of this request in each launch
@@ -169,6 +186,18 @@ constexpr size_t kPrefillScratchFloats = (size_t)1 << 20;  // 4 MiB
 hipError_t prefill_scratch(float **out);
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat,
                               float *out_score, int32_t *n_out_dev, hipStream_t st);
+
+// The layer chain (gr_chain.hip), over `rows` packed rows (a multiple of 128): the new tokens'
+// input vectors and their first norm; a norm of the residual rows with gain g; a projection
+// (kChainQKV, kChainO, kChainGateUp, kChainDown) of layer `layer` with its epilogue; the final
+// norm into each request's hidden rows.
+hipError_t launch_chain_start(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
+                              LaunchEv ev = {});
+hipError_t launch_chain_norm(const Dev &dev, const float *g, int rows, hipStream_t st, LaunchEv ev = {});
+hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, int kind, int layer,
+                             hipStream_t st, LaunchEv ev = {});
+hipError_t launch_chain_final(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
+                              LaunchEv ev = {});
 
 // rows per context workgroup for a given variant
 inline int ctx_rows_per_wg(int kind) { return (kind & 0xFF) * 32; }

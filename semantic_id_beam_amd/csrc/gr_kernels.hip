@@ -64,6 +64,15 @@ __device__ __forceinline__ void gst(void *p, const T &v) {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// float -> bf16 bits, round to nearest even (NaN kept quiet); two of them in one word
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -214,7 +223,9 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
     const uint16_t *qsrc = nullptr;
     if (row_ok) {
       const int j = q_row / dm.g, hq = h * dm.g + q_row % dm.g;
-      if (s == 0) {
+      if (dm.chain) {
+        qsrc = dev.ch.q + ((size_t)(R.row0 + j) * dm.Hq + hq) * D;
+      } else if (s == 0) {
         qsrc = (const uint16_t *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq) * D;
       } else {
         const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
@@ -612,7 +623,9 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
   {
     // a row past the live beams reads the request's own q_last row and is zeroed
     const uint16_t *qsrc = (const uint16_t *)(slot + dev.sl.q_last) + (size_t)layer * dm.Hq * D;
-    if (row_ok)
+    if (dm.chain)
+      qsrc = dev.ch.q + ((size_t)(R.row0 + (row_ok ? j_row : 0)) * dm.Hq + (row_ok ? hq_row : 0)) * D;
+    else if (row_ok)
       qsrc = s == 0 ? qsrc + (size_t)hq_row * D
                     : (const uint16_t *)dev.tok_q +
                           ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
@@ -1194,7 +1207,9 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     {
       // a row past the live beams reads the request's own q_last row and is zeroed
       const uint16_t *qsrc = (const uint16_t *)(slot + dev.sl.q_last) + (size_t)layer * dm.Hq * D;
-      if (row_ok)
+      if (dm.chain)
+        qsrc = dev.ch.q + ((size_t)(R.row0 + (row_ok ? j_row : 0)) * dm.Hq + (row_ok ? hq_row : 0)) * D;
+      else if (row_ok)
         qsrc = s == 0 ? qsrc + (size_t)hq_row * D
                       : (const uint16_t *)dev.tok_q +
                             ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
@@ -1539,7 +1554,7 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
         pa1[k] = gld<f32x4_t>(p0 + (size_t)R.rows_b * D);
         pb1[k] = gld<f32x4_t>(p0 + (size_t)R.rows_b * D + 4);
       }
-      if (layer > 0) {
+      if (layer > 0 && !dm.chain) {
         const float *hr = hb + ((size_t)j[k] * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8;
         ha[k] = gld<f32x4_t>(hr);
         hc[k] = gld<f32x4_t>(hr + 4);
@@ -1559,6 +1574,15 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         if (!ok[k]) continue;
+        if (dm.chain) {
+          // the layer chain: the step's q row, and the newest token's key and value already in
+          // BeamKV slot [layer][s-1][j] (written by the q/k/v projection)
+          const size_t own = lbase + (size_t)(s - 1) * lvstride + (size_t)j[k] * wstride + c8[k] * 8;
+          rq[k].load(dev.ch.q + ((size_t)(R.row0 + j[k]) * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8);
+          kn[k].load(bk + own);
+          vn[k].load(bv + own);
+          continue;
+        }
         const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code[k];
         rq[k].load((const uint16_t *)dev.tok_q + (trow * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8);
         kn[k].load((const uint16_t *)dev.tok_k + (trow * dm.Hkv + kv) * D + c8[k] * 8);
@@ -1568,7 +1592,7 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         rq[k].to_float(q[k]);
-        if (ok[k] && gi[k] == 0) {
+        if (ok[k] && gi[k] == 0 && !dm.chain) {
           const size_t dst = lbase + (size_t)(s - 1) * lvstride + (size_t)j[k] * wstride + c8[k] * 8;
           kn[k].store(bk + dst);
           vn[k].store(bv + dst);
@@ -1671,6 +1695,13 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
         float *dg = (float *)(slot + dev.sl.dbg_attn) + (((size_t)layer * dm.W_max + j[k]) * dm.Hq + hq) * D + c8[k] * 8;
         gst<f32x4_t>(dg, a);
         gst<f32x4_t>(dg + 4, b);
+      }
+      if (dm.chain) {
+        // the attention output, rounded to bf16, is the output projection's input row
+        gst<u32x4_t>(dev.ch.o + ((size_t)(R.row0 + j[k]) * dm.Hq + hq) * D + c8[k] * 8,
+                     u32x4_t{pack_bf16(O[0], O[1]), pack_bf16(O[2], O[3]), pack_bf16(O[4], O[5]),
+                             pack_bf16(O[6], O[7])});
+        continue;
       }
       if (layer > 0) {
         a += ha[k];

@@ -5,6 +5,8 @@ the decode runs in libgr_beam.so.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import numpy as np
 
 from . import _lib as G
@@ -28,26 +30,39 @@ class BeamEngine:
     """One engine: model tables, item trie, workspace.
 
     tok_q/tok_k/tok_v/w_sid are numpy arrays (bf16 bit patterns as uint16, or float32) or torch
-    device tensors; items is a [n_items][n_levels] integer array."""
+    device tensors; items is a [n_items][n_levels] integer array.  chain: the layer-chain model's
+    weights, a dict (embed, wq, wk, wv, wo, wg, wu, wd as bf16 [..][out][in], g_attn, g_mlp,
+    g_final float32; numpy or torch device tensors) with "intermediate" and "eps"; the token
+    tables are then unused (None)."""
 
     def __init__(self, *, tok_q, tok_k, tok_v, w_sid, items, n_layers: int, n_q_heads: int, n_kv_heads: int,
                  head_dim: int, dtype: str = "bf16", norm: str = "valid", max_requests: int = 1,
                  max_beam_width: int = 256, max_ctx_tokens: int = 0, max_splits: int = 0,
                  debug_attn: bool = False, max_layers_per_launch: int = 0, per_layer: bool = False,
-                 device="cuda"):
+                 chain=None, device="cuda"):
         torch = _torch()
         self.device = device
         self.dtype = dtype
-        conv = (lambda x: x) if isinstance(tok_q, torch.Tensor) else (lambda x: to_device(x, device))
+        conv = lambda x: x if (x is None or isinstance(x, torch.Tensor)) else to_device(x, device)
         self.tok_q, self.tok_k, self.tok_v = conv(tok_q), conv(tok_k), conv(tok_v)
+        self._chain = None
+        self._chain_I = chain["intermediate"] if chain is not None else 0
+        chain_desc = None
+        if chain is not None:
+            self._chain = {k: conv(v) for k, v in chain.items() if k not in ("intermediate", "eps")}
+            c = self._chain
+            chain_desc = G.gr_chain_desc(int(chain["intermediate"]), float(chain["eps"]),
+                                         *(c[k].data_ptr() for k in ("embed", "wq", "wk", "wv", "wo", "wg", "wu",
+                                                                     "wd", "g_attn", "g_mlp", "g_final")))
+        ptr = lambda t: t.data_ptr() if t is not None else None
         self.w_sid = conv(np.asarray(w_sid, dtype=np.float32)) if not isinstance(w_sid, torch.Tensor) else w_sid
         self.n_layers, self.n_levels, self.V = int(n_layers), int(self.w_sid.shape[0]), int(self.w_sid.shape[2])
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
         desc = G.gr_model_desc(self.n_layers, n_q_heads, n_kv_heads, head_dim, self.n_levels, self.V,
                                G.GR_DTYPE_BF16 if dtype == "bf16" else G.GR_DTYPE_F32,
                                G.GR_NORM_VALID if norm == "valid" else G.GR_NORM_FULL,
-                               self.tok_q.data_ptr(), self.tok_k.data_ptr(), self.tok_v.data_ptr(),
-                               self.w_sid.data_ptr())
+                               ptr(self.tok_q), ptr(self.tok_k), ptr(self.tok_v), self.w_sid.data_ptr(),
+                               C.pointer(chain_desc) if chain_desc is not None else None)
         opts = G.gr_engine_opts(max_requests, max_beam_width, max_ctx_tokens, max_splits,
                                 (G.GR_ENGINE_DEBUG_ATTN if debug_attn else 0) |
                                 (G.GR_ENGINE_PER_LAYER if per_layer else 0), max_layers_per_launch)
@@ -166,6 +181,11 @@ class BeamEngine:
 
     def path(self, rid: int):
         return G.gr_debug_beam_path(self.eng, rid, self.max_beam_width, self.n_levels, self.stream)
+
+    def chain_rows(self, rid: int, layer: int, which: int):
+        """Rows of the layer chain's last step (debug engines): which = G.GR_CHAIN_*."""
+        width = int(self._chain_I) if which == G.GR_CHAIN_ACT else self.Hq * self.d
+        return G.gr_debug_chain_rows(self.eng, rid, layer, which, self.max_beam_width, width, self.stream)
 
     def hidden(self, rid: int):
         return G.gr_debug_hidden(self.eng, rid, self.max_beam_width, self.Hq * self.d, self.V, self.stream)

@@ -15,7 +15,12 @@ def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm=
 
     from .engine import BeamEngine
     from ._lib import lib
-    tq, tk, tv = synth.token_tables(cfg)
+    chain = None
+    if cfg.model == "chain":
+        tq = tk = tv = None
+        chain = chain_weights(cfg)
+    else:
+        tq, tk, tv = synth.token_tables(cfg)
     shapes = synth.request_shapes(cfg)
     R = cfg.n_requests if max_requests is None else max_requests
     if max_ctx_tokens is None:
@@ -25,7 +30,21 @@ def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm=
                       n_layers=cfg.n_layers, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                       head_dim=cfg.head_dim, dtype=cfg.dtype, norm=norm, max_requests=R,
                       max_beam_width=W, max_ctx_tokens=max_ctx_tokens, max_splits=max_splits,
-                      debug_attn=debug_attn, max_layers_per_launch=max_layers_per_launch, per_layer=per_layer)
+                      debug_attn=debug_attn, max_layers_per_launch=max_layers_per_launch, per_layer=per_layer,
+                      chain=chain)
+
+
+def chain_weights(cfg, device="cuda", eps: float = 1e-6) -> dict:
+    """The layer chain's weights of a chain workload as device tensors (drawn on the device for
+    large models), with its MLP width and norm epsilon."""
+    import synth
+    n_params = cfg.n_layers * sum(r * c for r, c in synth.chain_shapes(cfg).values())
+    if n_params > (1 << 26) and str(device).startswith("cuda"):
+        from synth import device as synth_device
+        w = synth_device.chain_weights(cfg, device)
+    else:
+        w = synth.chain_weights(cfg)
+    return {**w, "intermediate": cfg.intermediate, "eps": eps}
 
 
 def request_tensors(cfg, r: int, device="cuda", host=False):
@@ -38,13 +57,17 @@ def request_tensors(cfg, r: int, device="cuda", host=False):
     from .engine import to_device
     if cfg.dtype == "bf16" and not host and str(device).startswith("cuda"):
         from synth import device as synth_device
-        return synth_device.request_tensors(cfg, r, device)
+        k, v, q = synth_device.request_tensors(cfg, r, device)
+        if cfg.model == "chain":   # the last context token's input vector instead of per-layer queries
+            q = to_device(synth.x_last(cfg, r), device)
+        return k, v, q
     ks, vs = [], []
     for l in range(cfg.n_layers):
         k, v = synth.ctx_kv_block(cfg, r, l)
         ks.append(k)
         vs.append(v)
-    return to_device(np.stack(ks), device), to_device(np.stack(vs), device), to_device(synth.q_last(cfg, r), device)
+    q = synth.x_last(cfg, r) if cfg.model == "chain" else synth.q_last(cfg, r)
+    return to_device(np.stack(ks), device), to_device(np.stack(vs), device), to_device(q, device)
 
 
 def native_layout(k, v):

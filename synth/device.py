@@ -10,7 +10,8 @@ import os
 
 import numpy as np
 
-from .gen import _T_CTX_K, _T_CTX_V, _T_QLAST, BF16_NORMAL_TABLE, _key, request_shapes
+from .gen import (_T_CH_EMBED, _T_CH_W, _T_CTX_K, _T_CTX_V, _T_QLAST, BF16_NORMAL_TABLE, CHAIN_MATS, _key,
+                  chain_gains, chain_scale, chain_shapes, request_shapes)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth_gen.so")
 _lib = None
@@ -68,3 +69,30 @@ def request_tensors(cfg, r: int, device="cuda"):
     if cfg.q_scale_log2:
         q.mul_(2.0 ** cfg.q_scale_log2)
     return k, v, q
+
+
+def chain_weights(cfg, device="cuda") -> dict:
+    """The layer chain's weights as device tensors (gen.chain_weights' values, bit for bit): each
+    matrix is drawn on the device from its Philox block, multiplied by its float32 scale and
+    rounded to bf16 (nearest even), as the host generator does."""
+    import torch
+    L = cfg.n_layers
+    D = cfg.n_q_heads * cfg.head_dim
+    w = {}
+    emb = torch.empty((max(cfg.n_levels - 1, 0), cfg.codebook, D), dtype=torch.bfloat16, device=device)
+    if emb.numel():
+        bf16_normal_into(emb, _key(cfg, _T_CH_EMBED))
+    w["embed"] = emb
+    for i, name in enumerate(CHAIN_MATS):
+        rows, cols = chain_shapes(cfg)[name]
+        out = torch.empty((L, rows, cols), dtype=torch.bfloat16, device=device)
+        tmp = torch.empty((rows, cols), dtype=torch.bfloat16, device=device)
+        scale = float(chain_scale(cfg, name))
+        for l in range(L):
+            bf16_normal_into(tmp, _key(cfg, _T_CH_W, i, l))
+            out[l] = (tmp.float() * scale).to(torch.bfloat16)
+        w[name] = out
+    ga, gm, gf = chain_gains(cfg)
+    w["g_attn"], w["g_mlp"], w["g_final"] = (torch.from_numpy(a).to(device) for a in (ga, gm, gf))
+    return w
+

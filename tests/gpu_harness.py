@@ -34,10 +34,12 @@ def gpu_beams(eng, rid):
 class TeacherForced:
     """Oracle bookkeeping for one request: scores of every prefix the oracle has expanded."""
 
-    def __init__(self, cfg, r: int, norm="valid"):
+    def __init__(self, cfg, r: int, norm="valid", model=None, req=None, score_tol=None, tau=None):
         self.cfg, self.r, self.norm = cfg, r, norm
-        self.model = model_for(cfg)
-        self.req = request_for(cfg, r)
+        self.score_tol = SCORE_TOL if score_tol is None else score_tol
+        self.tau = TAU if tau is None else tau
+        self.model = model if model is not None else model_for(cfg)
+        self.req = req if req is not None else request_for(cfg, r)
         self.ps = prefixes_for(cfg)
         self.score_of = {(): 0.0}
         self.W = synth.request_shapes(cfg)[r][1]
@@ -60,18 +62,18 @@ class TeacherForced:
         # must-have / must-not sets outside the tie band
         for i in range(sc.shape[0]):
             p = prev_prefixes[js[i]] + (int(cs[i]),)
-            if sc[i] > o_w + TAU:
+            if sc[i] > o_w + self.tau:
                 assert p in chosen, f"missing beam {p} (score {sc[i]:.6f}, cutoff {o_w:.6f})"
-            if sc[i] < o_w - TAU:
+            if sc[i] < o_w - self.tau:
                 assert p not in chosen, f"extra beam {p} (score {sc[i]:.6f}, cutoff {o_w:.6f})"
         osc = np.array([self.score_of[p] for p in pref])
         dmax = float(np.max(np.abs(osc - gsc))) if len(pref) else 0.0
-        assert dmax <= SCORE_TOL, f"score error {dmax}"
+        assert dmax <= self.score_tol, f"score error {dmax}"
         # slot order sorted up to the band; parents consistent with prefixes
-        assert np.all(osc[:-1] >= osc[1:] - TAU), "slot order not sorted by score"
+        assert np.all(osc[:-1] >= osc[1:] - self.tau), "slot order not sorted by score"
         for i, p in enumerate(pref):
             assert prev_prefixes[par[i]] == p[:-1], "parent slot does not hold the prefix"
-        in_band = int(np.sum(np.abs(sc - o_w) <= TAU))
+        in_band = int(np.sum(np.abs(sc - o_w) <= self.tau))
         exact = [prev_prefixes[js[i]] + (int(cs[i]),) for i in order] == list(pref)
         self.report.append({"n": n_exp, "max_dscore": dmax, "in_band": in_band, "exact_order": exact})
         return self.report[-1]

@@ -39,6 +39,10 @@ GR_STUB(launch_prefill_ctx, int, const void *, const void *, const int32_t *, in
 GR_STUB(launch_prefill_q, int, const void *, int, const int32_t *, const float *, int, int, int, int, int, void *,
         void *, float *, float *, hipStream_t)
 hipError_t prefill_scratch(float **) { std::abort(); }
+GR_STUB(launch_chain_start, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
+GR_STUB(launch_chain_norm, const Dev &, const float *, int, hipStream_t, LaunchEv)
+GR_STUB(launch_chain_gemm, const Dev &, const StepReq *, int, int, int, int, hipStream_t, LaunchEv)
+GR_STUB(launch_chain_final, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 #undef GR_STUB
 }  // namespace gr
 

@@ -32,3 +32,17 @@ def test_request_tensors_equal_host(name, r):
     for a, b in ((dk, hk), (dv, hv), (dq, hq)):
         assert a.shape == b.shape and a.dtype == b.dtype
         assert np.array_equal(_bits(a), _bits(b))
+
+
+def test_chain_weights_equal_host():
+    """The layer chain's weights drawn on the device (scaled and rounded to bf16 there) equal the
+    host generator's, bit for bit, at Qwen3-1.7B's layer shape."""
+    from synth import device as sd
+    cfg = synth.get_config("chain_ctx5k_beam256_r8", n_layers=2)
+    dw = sd.chain_weights(cfg)
+    hw = synth.chain_weights(cfg)
+    for k in ("embed",) + synth.CHAIN_MATS:
+        assert tuple(dw[k].shape) == hw[k].shape, k
+        assert np.array_equal(_bits(dw[k]), hw[k]), k
+    for k in ("g_attn", "g_mlp", "g_final"):
+        assert np.array_equal(dw[k].cpu().numpy(), hw[k]), k
