@@ -311,6 +311,86 @@ def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 40
             "points": points}
 
 
+def chain_leg(args, name: str = "chain_ctx5k_beam256_r8", reps: int = 5):
+    """The decode with a real layer chain (28 Qwen3-1.7B-shaped pre-norm decoder layers: q/k/v/o
+    projections, RMSNorm, SwiGLU MLP of 6144) on the headline's requests: one launch per kernel
+    and layer.  HIP events carried by the dispatches time every kernel; the projections'
+    algorithmic work is 2 x live beams x (weights per layer) flops."""
+    import numpy as np
+    import torch
+
+    import synth
+    from semantic_id_beam_amd import _lib as G
+    from semantic_id_beam_amd.workloads import make_engine, request_tensors
+    cfg = synth.get_config(name)
+    shapes = synth.request_shapes(cfg)
+    R, lv, L = cfg.n_requests, cfg.n_levels, cfg.n_layers
+    t = time.time()
+    eng = make_engine(cfg, max_requests=R)
+    log(f"chain engine ready ({time.time() - t:.1f} s)")
+    for r in range(R):
+        k, v, x = request_tensors(cfg, r)
+        eng.load(r, k, v, x, shapes[r][1])
+        del k, v, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    rids = list(range(R))
+    n_live = np.zeros((R, lv), dtype=np.int64)
+    n_live[:, 0] = 1
+    for s_ in range(lv):
+        eng.step(rids)
+        if s_ + 1 < lv:
+            for r in rids:
+                n_live[r, s_ + 1] = eng.state(r)["n"]
+    eng.beams_batch(rids)
+
+    def decode_all():
+        eng.reset_batch(rids)
+        for _ in range(lv):
+            eng.step(rids)
+        return eng.beams_batch(rids)
+
+    decode_all()
+    torch.cuda.synchronize()
+    G.gr_engine_profile_reset(eng.eng)
+    G.gr_engine_set_profiling(eng.eng, True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        decode_all()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    G.gr_engine_set_profiling(eng.eng, False)
+    prof = {k: {s_: G.gr_engine_profile_read(eng.eng, kind, s_) for s_ in range(lv)}
+            for kind, k in [(G.GR_PROF_GEMM, "gemm"), (G.GR_PROF_CTX_ATTN, "attn"), (G.GR_PROF_BEAM_MERGE, "finish"),
+                            (G.GR_PROF_NORM, "norm"), (G.GR_PROF_LOGITS, "logits"), (G.GR_PROF_TOPK, "topk")]}
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    D, I = cfg.n_q_heads * cfg.head_dim, cfg.intermediate
+    Dkv = cfg.n_kv_heads * cfg.head_dim
+    w_layer = D * (D + 2 * Dkv) + D * D + 2 * D * I + I * D       # weights per layer
+    N = np.array([n for n, _ in shapes], dtype=np.float64)
+    out = {"workload": workload_text(cfg, shapes) + f", layer chain (MLP {I})", "reps": reps,
+           "req_per_s": round(R * reps / dt, 1), "ms_per_decode": round(1e3 * dt / reps, 3), "levels": {}}
+    for s_ in range(lv):
+        rows = float(n_live[:, s_].sum())
+        g_ms, g_n = prof["gemm"][s_]
+        a_ms, a_n = prof["attn"][s_]
+        gemm_flops = 2 * rows * w_layer * L * reps
+        attn_flops = float(np.sum(cfg.n_kv_heads * n_live[:, s_] * cfg.group * N * cfg.head_dim * 4)) * L * reps
+        out["levels"][f"level{s_}"] = {
+            "rows": int(rows),
+            "gemm_ms": round(g_ms / reps, 3), "gemm_TFLOPs": round(gemm_flops / (g_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_bf16_peak": round(gemm_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gemm_weight_GBs": round(2 * w_layer * L * reps / (g_ms * 1e-3) / 1e9, 1),
+            "attn_ms": round(a_ms / reps, 3), "attn_us_per_layer": round(1e3 * a_ms / max(a_n, 1), 2),
+            "attn_TFLOPs": round(attn_flops / (a_ms * 1e-3) / 1e12, 1),
+            "finish_ms": round(prof["finish"][s_][0] / reps, 3), "norm_ms": round(prof["norm"][s_][0] / reps, 3),
+            "logits_topk_ms": round((prof["logits"][s_][0] + prof["topk"][s_][0]) / reps, 3)}
+    log(f"chain: {out['req_per_s']} req/s, {out['ms_per_decode']} ms per decode")
+    return out
+
+
 def cpu_baseline(cfg, n_beams: int):
     """The oracle, timed on the host cores on a bounded sample of the same workload."""
     import numpy as np
@@ -530,6 +610,7 @@ def main():
                     help="skip the other two workloads (64 x ctx 2000 beam 30; ragged 128 in four waves)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the headline decode (one layer per launch): no other legs")
+    ap.add_argument("--chain-only", action="store_true", help="only the layer-chain leg (prints its JSON)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -554,6 +635,9 @@ def main():
     from synth.configs import HEADLINE
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.chain_only:
+        print(json.dumps({"chain": chain_leg(args)}), flush=True)
+        return
     cfg = synth.get_config(args.config or HEADLINE)
     shapes = synth.request_shapes(cfg)
     R, lv = cfg.n_requests, cfg.n_levels
@@ -593,6 +677,7 @@ def main():
                      "a group of layers): valid only because this model stand-in's layers are independent; "
                      "not the headline"),
             **{k: fused[k] for k in ("value", "ms_per_step", "step_us", "decode_ms", "roofline", "kernels")}}
+        out["chain"] = chain_leg(args)
         out["scoring"] = scoring_leg(cfg, args)
         out["prefill"] = prefill_leg(cfg, args)
         if not args.no_workloads:

@@ -158,16 +158,18 @@ __global__ __launch_bounds__(256) void k_chain_final(Dev dev, const StepReq *__r
 
 // ---------------------------------------------------------------------------------------- GEMM
 // Workgroup: 256 threads, four waves in 2 x 2, a 128 (rows) x 128 (weight rows) tile; wave
-// (wm, wn) owns 64 x 64 as 2 x 2 MFMA blocks.  The K loop takes 64 columns per stage: the
-// stage's A and W tiles (16 KB each) go from global memory straight into LDS
-// (global_load_lds_dwordx4, 1 KB of consecutive LDS per wave instruction, 8 per lane and
-// stage), a ring of three stages with two in flight.  LDS rows are 128 bytes (8 chunks of 16);
-// chunk c of row r sits at c ^ (r & 7), so the 32 rows a half-wave reads for one operand hit
-// different banks.  The MFMA computes the transposed block D[n][m] = W_blk (32 x 16) x A_blk^T
-// (16 x 32): lane (m, hh) then holds output row m, columns 8a + 4hh + {0..3} of the block, so
-// each epilogue write is a run of four columns of one row.
+// (wm, wn) owns 64 x 64 as 2 x 2 MFMA blocks.  The K loop takes 32 columns per stage: the
+// stage's A and W tiles (8 KB each) go from global memory straight into LDS
+// (global_load_lds_dwordx4, 1 KB of consecutive LDS per wave instruction, 4 per lane and
+// stage), a ring of four stages with three in flight; 64 KB of LDS, so two workgroups share a
+// compute unit (two waves per SIMD).  LDS rows are 64 bytes (4 chunks of 16); chunk c of row r
+// sits at c ^ ((r >> 2) & 3): the LDS serves 16 lanes (16 rows, one chunk each) over its 64
+// banks at a time, and rows r, r+4, r+8, r+12 (same banks otherwise) then take the four
+// different chunk positions.  The MFMA computes the transposed block D[n][m] = W_blk (32 x 16)
+// x A_blk^T (16 x 32): lane (m, hh) then holds output row m, columns 8a + 4hh + {0..3} of the
+// block, so each epilogue write is a run of four columns of one row.
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
-constexpr int GBM = 128, GBN = 128, GBK = 64, GNST = 3;
+constexpr int GBM = 128, GBN = 128, GBK = 32, GNST = 4;
 
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
@@ -204,28 +206,46 @@ __device__ __forceinline__ const uint16_t *w_row(const GemmArgs &g, int n0, int 
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 0 || N == 8, "unsupported wait");
+  else static_assert(N == 0 || N == 4 || N == 8, "unsupported wait");
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs, GemmArgs g,
-                                              int m_tiles) {
-  __shared__ bf16x8_t sA[GNST][GBM * 8];
-  __shared__ bf16x8_t sW[GNST][GBN * 8];
+__global__ __launch_bounds__(256, 2) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs, GemmArgs g,
+                                                 int m_tiles) {
+  constexpr int CPR = GBK / 8;                 // 16-byte chunks per LDS row
+  constexpr int NI = GBM * CPR / 256;          // DMA instructions per lane and operand per stage
+  constexpr int P = GNST - 1;                  // stages in flight
+  static_assert(GBM == GBN && CPR == 4 && NI == 2 && P == 3, "tile shape");
+  __shared__ bf16x8_t sA[GNST][GBM * CPR];
+  __shared__ bf16x8_t sW[GNST][GBN * CPR];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;
-  const int mt = (int)blockIdx.x % m_tiles, nt = (int)blockIdx.x / m_tiles;
+  // workgroups are dealt round-robin over the 8 XCDs (blockIdx % 8): when the weight tiles split
+  // evenly, XCD x takes weight tiles x, x+8, ... and runs every row tile of each, so a weight tile
+  // is fetched into one XCD's L2 only (the smaller activation rows are what each XCD re-reads)
+  const int n_tiles = g.N / GBN;
+  int mt, nt;
+  if ((n_tiles & 7) == 0) {
+    const int xcd = (int)blockIdx.x & 7, idx = (int)blockIdx.x >> 3;
+    mt = idx % m_tiles;
+    nt = (idx / m_tiles) * 8 + xcd;
+  } else {
+    mt = (int)blockIdx.x % m_tiles;
+    nt = (int)blockIdx.x / m_tiles;
+  }
   const int m0 = mt * GBM, n0 = nt * GBN;
   const int KT = g.K / GBK;
 
-  // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane, row p >> 3, stored
-  // position p & 7 <- global chunk (p & 7) ^ (row & 7); rows 8(i*4+w) .. +7 share one weight block
-  const uint16_t *asrc[4], *wsrc[4];
+  // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane: row p / CPR, stored
+  // position p % CPR <- global chunk (p % CPR) ^ ((row >> 2) & 3); the 16 rows of one instruction
+  // lie in one 32-row weight block
+  const uint16_t *asrc[NI], *wsrc[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+  for (int i = 0; i < NI; ++i) {
+    const int p = (i * 4 + w) * 64 + lane, r = p / CPR, c = (p % CPR) ^ ((r >> 2) & 3);
     asrc[i] = g.A + (size_t)(m0 + r) * g.K + c * 8;
     wsrc[i] = w_row<EPI>(g, n0, r) + c * 8;
   }
@@ -233,9 +253,9 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
   auto issue = [&](int kt) {
     const int st = kt % GNST;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * 128) + i * 4096);
+    for (int i = 0; i < NI; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * CPR * 16) + i * 4096);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (GBN * 128) + i * 4096);
+    for (int i = 0; i < NI; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (GBN * CPR * 16) + i * 4096);
   };
 
   f32x16_t acc[2][2];
@@ -244,12 +264,15 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
 
-  issue(0);
-  if (KT > 1) issue(1);
-  const int rl = lane & 31, sw = rl & 7;
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+    if (k < KT) issue(k);
+  const int rl = lane & 31, sw = (rl >> 2) & 3;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) vm_wait_barrier<8>(); else vm_wait_barrier<0>();
-    if (kt + 2 < KT) issue(kt + 2);  // into the stage of tile kt-1, which every wave has left
+    // stage kt has landed once at most the copies of the stages issued after it remain
+    const int ahead = min(P - 1, KT - 1 - kt);
+    if (ahead >= 2) vm_wait_barrier<4 * NI>(); else if (ahead == 1) vm_wait_barrier<2 * NI>(); else vm_wait_barrier<0>();
+    if (kt + P < KT) issue(kt + P);  // into the stage of tile kt-1, which every wave has left
     const int st = kt % GNST;
     const bf16x8_t *a = &sA[st][0], *b = &sW[st][0];
 #pragma unroll
@@ -257,9 +280,9 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
       const int ch = (2 * ks + hh) ^ sw;
       bf16x8_t af[2], wf[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[mb] = a[(wm * 64 + mb * 32 + rl) * 8 + ch];
+      for (int mb = 0; mb < 2; ++mb) af[mb] = a[(wm * 64 + mb * 32 + rl) * CPR + ch];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) wf[nb] = b[(wn * 64 + nb * 32 + rl) * 8 + ch];
+      for (int nb = 0; nb < 2; ++nb) wf[nb] = b[(wn * 64 + nb * 32 + rl) * CPR + ch];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
