@@ -104,9 +104,11 @@ struct LaunchEv {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 // Context-attention variants: waves per workgroup (1, 2, 4 or 8; 32 query rows per wave)
-// in the low byte; kCtxHiLo marks P split into two bf16 terms (p = p_hi + p_lo, relative error
-// about 2^-17), which every variant uses: a single bf16 P perturbs each weight by up to 2^-9,
-// and with a few dominant tokens (large query/key norms) that moved log-probs past 1e-3.
+// in the low byte.  kCtxHiLo marks P split into two bf16 terms (p = p_hi + p_lo, relative
+// error about 2^-17), which the one-, two- and four-wave variants use; the eight-wave (wide)
+// kernel takes P as one float16 term against float16 V (relative error 2^-11).  A single bf16
+// P perturbs each weight by up to 2^-8, and with a few dominant tokens (large query/key norms)
+// that moved log-probs past 1e-3.
 constexpr int kCtxHiLo = 0x100;
 hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                            int ctx_kind, hipStream_t st, LaunchEv ev = {});
@@ -208,7 +210,7 @@ inline int ctx_kind_for(int rows, int N, int d) {
   if (rows <= 64 || d == 64) return (rows <= 64 ? 2 : 4) | kCtxHiLo;
   if (rows <= 128) return 4 | kCtxHiLo;
   (void)N;
-  return 8 | kCtxHiLo;
+  return 8;
 }
 
 }  // namespace gr

@@ -41,6 +41,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -72,6 +74,10 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return u >> 16;
 }
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+// two floats as float16 (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)a, (_Float16)b});
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -461,6 +467,14 @@ __device__ __forceinline__ void vm_wait_barrier() {
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0 || N == 4 || N == 8, "unsupported wait");
+}
+
+// as vm_wait_barrier, and this wave's LDS writes done before the barrier
+template <int N>
+__device__ __forceinline__ void vm_lgkm_wait_barrier() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0 || N == 4, "unsupported wait");
 }
 
 template <int N>
@@ -908,27 +922,35 @@ __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &
     }
 }
 
+// The wide context kernel: 8 waves x 32 query rows (256 rows of one kv head) against K and V^T
+// tiles of 64 tokens that go from HBM straight into LDS through a ring of five stages.  Each
+// V^T tile is rewritten in place, once it has landed, as float16 of v / vscale, where vscale =
+// 2^e is the power of two above the head's largest |v| (taken at load); a bf16 value converts
+// exactly while |v| >= 2^-14 vscale, and below that to within 2^-25 vscale.  P is then a single
+// float16 term (relative rounding 2^-11) and PV one f16 MFMA per 16 tokens.  The softmax keeps
+// a running maximum with a lazy rescale: only when a row's maximum grows by more than 8 in log2
+// units, so every p stays within (0, 2^8].  A tile is converted while its predecessor is in
+// use, one barrier before its first PV.
+//
 // LAYERED: a launch covers layers layer_arg .. layer_arg + lgroups - 1, and a workgroup owns its
 // row block over the whole context of one of them, layer_arg + g (every layer's query comes
 // from the token tables or the request, never from another layer's output).  It then finishes
 // its rows itself, with no split partials: the beam's own tokens are merged into (m, l, o) in
 // the prologue (the newest one appended to BeamKV), the context loop continues from that
-// state, and o/l is stored as the layer's fp16 hidden partial (k_sum_hparts adds the layers
+// state, and o/l is stored as the layer's float32 hidden partial (k_sum_hparts adds the layers
 // in order at the end).  Otherwise: one layer, one token range, split partials out, and the
-// previous layer finished in the prologue.
-template <int NST, bool HILO, bool LAYERED>
+// previous layer finished in the prologue when the step defers it.
+template <bool LAYERED>
 __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                        int layer_arg) {
-  constexpr int D = 128, NW = 8, TT = 64, KB = D / 16, DB = D / 32, NT = NW * 64;
-  constexpr int P = NST - 2;                          // tiles in flight beyond the one in use
+  constexpr int D = 128, NW = 8, TT = 64, KB = D / 16, DB = D / 32, NT = NW * 64, NST = 5;
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
   constexpr int KI = KCH / NT, VI = VCH / NT;        // DMA instructions per wave and tile
   constexpr int LPT = KI + VI;
-  static_assert(NST >= 3 && NST <= 5, "ring of three to five stages");
+  static_assert(LPT == 4, "wait immediates assume four copies per lane and tile");
   static_assert(TT == kTileTok, "tiles never cross the zero-padded end of the context");
   __shared__ bf16x8_t sK[NST][KCH];   // [token row swap23(r)][column c ^ (row & 15)]
-  __shared__ bf16x8_t sV[NST][VCH];   // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
-  __shared__ float sBound[NW];        // per-wave score bounds of the current layer
+  __shared__ u32x4_t sV[NST][VCH];    // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
   const int kx = lane & 15, vx = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of this lane's operand row
@@ -956,7 +978,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const int rows = n_live * dm.g;
   if (row0 >= rows) return;  // whole workgroup idle
 
-  const bool wave_active = wrow < rows;
+  const bool wave_active = wrow < rows;  // an idle wave still copies and converts its share
   const bool row_ok = q_row < rows;
 
   const int t0 = LAYERED ? 0 : sp * R.tps;
@@ -965,7 +987,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const int nsub = (t1 - t0 + 31) / 32;
   const int layer = layer_arg + (LAYERED ? sp : 0);
   if (layer >= dm.L) return;  // past the last layer of the last launch
-  const uint16_t *gK = nullptr, *gV = nullptr;  // the current layer's K and V^T of kv head h
+  const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
+  const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
+  const float vs = ((const float *)(slot + dev.sl.vscale))[layer * dm.Hkv + h];
+  const float ivs = 1.f / vs;  // exact: vs is a power of two
 
   // per-lane DMA sources (elements from the tile's first token) for this wave's chunks
   uint32_t koff[KI], voff[VI];
@@ -990,9 +1015,22 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 #pragma unroll
     for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + i * 1024);
   };
+  // V^T of a landed tile -> float16 of v / vscale, in place (each thread two 16-byte chunks)
+  auto convert_v = [&](int tile) {
+    u32x4_t *sv = &sV[tile % NST][0];
+#pragma unroll
+    for (int i = 0; i < VCH / NT; ++i) {
+      const u32x4_t x = sv[i * NT + tid];
+      u32x4_t y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = pack_f16(__uint_as_float(x[e] << 16) * ivs, __uint_as_float(x[e] & 0xFFFF0000u) * ivs);
+      sv[i * NT + tid] = y;
+    }
+  };
   const float c2 = dm.scale_log2;
   bf16x8_t qf[KB];  // B operand of QK^T: lane holds Q[q_row][kb*16 + 8*hh .. +8]
-  float M, l;
+  float M = kNegInf, l = 0.f;
   f32x16_t oacc[DB];
 
   auto qk = [&](int tile, int sub) {
@@ -1003,95 +1041,75 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[(kb * 2 + hh) ^ kx], qf[kb], acc, 0, 0, 0);
     return acc;
   };
-  // softmax of sub-tile u (first token t0 + 32u) and PV with its tile's V^T
-  auto soft_pv = [&](f32x16_t sacc, int u, auto mask_tag, auto fixed_tag) {
+  // lazy rescale before the sub-tile whose row maxima (x log2 e / sqrt(d)) are mxs
+  auto rescale = [&](float mx) {
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxs = mx * c2;
+    if (__ballot(mxs > M + 8.f) != 0ull) {  // uniform over the wave
+      const float Mn = fmaxf(M, mxs);
+      const float f = fast_exp2(M - Mn);  // 0 before the first sub-tile (M = -inf)
+      l *= f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= f;
+      M = Mn;
+    }
+  };
+  auto smax = [&](const f32x16_t &sc) {
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    return mx;
+  };
+  const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // softmax of sub-tile u (first token t0 + 32u) and PV with its tile's V^T (tail sub-tiles)
+  auto soft_pv = [&](f32x16_t sacc, int u, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool FIXED = decltype(fixed_tag)::value;
     if constexpr (MASK) {
       const int tbase = t0 + u * 32 + 8 * hh;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (tbase + 16 * (i >> 3) + (i & 7) >= t1) sacc[i] = kNegInf;
     }
-    if constexpr (!FIXED) {
-      float mx = sacc[0];
+    rescale(smax(sacc));
+    f16x8_t pf[2];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = mx * c2;
-      if (__ballot(mxs > M + 8.f) != 0ull) {
-        const float Mn = fmaxf(M, mxs);
-        const float f = fast_exp2(M - Mn);
-        l *= f;
+    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (_Float16)fast_exp2(fmaf(sacc[i], c2, -M));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= f;
-        M = Mn;
-      }
-    }
-    bf16x8_t pf[2], pl[2];
-    if constexpr (HILO) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(sacc[i], c2, -M));
-        const __bf16 ph = (__bf16)p;
-        pf[i >> 3][i & 7] = ph;
-        pl[i >> 3][i & 7] = (__bf16)(p - (float)ph);
-        l += p;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (__bf16)fast_exp2(fmaf(sacc[i], c2, -M));
-      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 0, 1), ones, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 2, 3), ones, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 4, 5), ones, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[pp], pf[pp], 6, 7), ones, l, false);
-      }
-    }
+    for (int i = 0; i < 16; i += 2)
+      l = __builtin_amdgcn_fdot2(f16x2_t{pf[i >> 3][i & 7], pf[i >> 3][(i & 7) + 1]}, ones, l, false);
     const int tile = u >> 1, sub = u & 1;
-    const bf16x8_t *vr = &sV[tile % NST][(lane & 31) * (TT / 8)];
+    const u32x4_t *vr = &sV[tile % NST][(lane & 31) * (TT / 8)];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        const bf16x8_t vf = vr[db * 32 * (TT / 8) + ((sub * 4 + pp * 2 + hh) ^ vx)];
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pp], oacc[db], 0, 0, 0);
-        if constexpr (HILO) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[pp], oacc[db], 0, 0, 0);
+        const f16x8_t vf = __builtin_bit_cast(f16x8_t, vr[db * 32 * (TT / 8) + ((sub * 4 + pp * 2 + hh) ^ vx)]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[pp], oacc[db], 0, 0, 0);
       }
-    }
   };
-  // Steady-state step with the fixed reference, sub-tile u unmasked: QK^T of sub-tile u+1
-  // and softmax + PV of sub-tile u, interleaved by hand.  Issue is in order within a wave, so
-  // the softmax is spread over this wave's own MFMAs, giving each wave independent VALU work
-  // between its MFMAs (the two waves of a SIMD then keep the matrix core fed): element k
-  // (k < 8) after the k-th QK^T MFMA, elements 8..15 two at a time after the first four PV
-  // MFMAs (those use the first eight only).  LDS operands are fetched two MFMAs ahead (a
-  // deeper prefetch measured no faster); sched_barrier keeps the order.
-  // kr: the K rows of the QK^T sub-tile, vr: the V^T tile of the PV sub-tile spv.  With
-  // compile-time stages (block_fixed_st) every operand address is a per-lane register plus
-  // an immediate offset.
-  auto block_fixed_p = [&](const bf16x8_t *kr, const bf16x8_t *vr, int spv, const f32x16_t &sc) {
+  // Steady-state step, sub-tile u unmasked: QK^T of sub-tile u+1 and softmax + PV of sub-tile
+  // u, interleaved by hand.  Issue is in order within a wave, so the softmax is spread over the
+  // wave's own MFMAs, giving each wave independent VALU work between its MFMAs (the two waves of
+  // a SIMD then keep the matrix core fed): element k (k < 8) after the k-th QK^T MFMA, elements
+  // 8..15 two at a time after the first four PV MFMAs (those use the first eight only), and the
+  // row maxima of sub-tile u+1 over the last four, for its lazy rescale at the end.  LDS
+  // operands are fetched two MFMAs ahead; sched_barrier keeps the order.  kr: the K rows of the
+  // QK^T sub-tile, vr: the V^T tile of the PV sub-tile spv.  With compile-time stages
+  // (block_st) every operand address is a per-lane register plus an immediate offset.
+  auto block_p = [&](const bf16x8_t *kr, const u32x4_t *vr, int spv, const f32x16_t &sc) {
     auto kfrag = [&](int kb) { return kr[(kb * 2 + hh) ^ kx]; };
     auto vfrag = [&](int j) {  // j = pp*4 + db
-      return vr[(j & 3) * 32 * (TT / 8) + ((spv * 4 + (j >> 2) * 2 + hh) ^ vx)];
+      return __builtin_bit_cast(f16x8_t, vr[(j & 3) * 32 * (TT / 8) + ((spv * 4 + (j >> 2) * 2 + hh) ^ vx)]);
     };
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x8_t kf[3], vf[3], pf[2], pl[2];
-    float pr[8];
-    // the pair (i, i+1) of P: bf16 term(s) and its share of l
+    bf16x8_t kf[3];
+    f16x8_t vf[3], pf[2];
+    float pr[8], mx = 0.f;
+    // the pair (i, i+1) of P and its share of l (exactly the float16 weights the MFMAs use)
     auto pair = [&](float p0, float p1, int i) {
-      const bf16x2_t h2 = {(__bf16)p0, (__bf16)p1};
+      const f16x2_t h2 = {(_Float16)p0, (_Float16)p1};
       pf[i >> 3][i & 7] = h2[0];
       pf[i >> 3][(i + 1) & 7] = h2[1];
-      if constexpr (HILO) {
-        pl[i >> 3][i & 7] = (__bf16)(p0 - (float)h2[0]);
-        pl[i >> 3][(i + 1) & 7] = (__bf16)(p1 - (float)h2[1]);
-        l += p0 + p1;
-      } else {
-        l = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, l, false);
-      }
+      l = __builtin_amdgcn_fdot2(h2, ones, l, false);
     };
     kf[0] = kfrag(0);
     kf[1] = kfrag(1);
@@ -1108,180 +1126,140 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j + 2 < 8) vf[(j + 2) % 3] = vfrag(j + 2);
-      oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % 3], pf[j >> 2], oacc[j & 3], 0, 0, 0);
-      if constexpr (HILO)
-        oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % 3], pl[j >> 2], oacc[j & 3], 0, 0, 0);
-      if (j < 4)
+      oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[j % 3], pf[j >> 2], oacc[j & 3], 0, 0, 0);
+      if (j < 4) {
         pair(fast_exp2(fmaf(sc[8 + 2 * j], c2, -M)), fast_exp2(fmaf(sc[9 + 2 * j], c2, -M)), 8 + 2 * j);
+      } else {
+        const int b = 4 * (j - 4);
+        const float m4 = fmaxf(fmaxf(acc[b], acc[b + 1]), fmaxf(acc[b + 2], acc[b + 3]));
+        mx = j == 4 ? m4 : fmaxf(mx, m4);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    rescale(mx);
     return acc;
   };
-  auto block_fixed = [&](int u, const f32x16_t &sc) {
+  static_assert(KB == 8, "the interleave assumes eight QK^T MFMAs per sub-tile");
+  auto block = [&](int u, const f32x16_t &sc) {
     const int tq = (u + 1) >> 1, sq = (u + 1) & 1, tp = u >> 1;
-    return block_fixed_p(&sK[tq % NST][(sq * 32 + (lane & 31)) * (D / 8)], &sV[tp % NST][(lane & 31) * (TT / 8)], u & 1,
-                         sc);
+    return block_p(&sK[tq % NST][(sq * 32 + (lane & 31)) * (D / 8)], &sV[tp % NST][(lane & 31) * (TT / 8)], u & 1,
+                   sc);
   };
   // sub-tile u = 2*it + SPV with it % NST == ST (QK^T of sub-tile u+1, PV of sub-tile u)
-  auto block_fixed_st = [&](auto st_tag, auto spv_tag, const f32x16_t &sc) {
+  auto block_st = [&](auto st_tag, auto spv_tag, const f32x16_t &sc) {
     constexpr int ST = decltype(st_tag)::value, SPV = decltype(spv_tag)::value;
     constexpr int KST = SPV ? (ST + 1) % NST : ST, SQ = SPV ? 0 : 1;
-    return block_fixed_p(&sK[KST][(SQ * 32 + (lane & 31)) * (D / 8)], &sV[ST][(lane & 31) * (TT / 8)], SPV, sc);
-  };
-  static_assert(KB == 8, "the interleave assumes eight QK^T MFMAs per sub-tile");
-
-  // before the first QK^T of tile it (it >= 1): tile it landed, then the barrier, then tile
-  // it+P goes into the stage of tile it-2
-  auto advance = [&](int it) {
-    const int ahead = min(P - 1, ntiles - 1 - it);  // own tiles issued after tile it
-    if (ahead >= 2) vm_wait_barrier<2 * LPT>();
-    else if (ahead == 1) vm_wait_barrier<LPT>();
-    else vm_wait_barrier<0>();
-    if (it + P < ntiles) issue(it + P);
+    return block_p(&sK[KST][(SQ * 32 + (lane & 31)) * (D / 8)], &sV[ST][(lane & 31) * (TT / 8)], SPV, sc);
   };
 
-  auto run = [&](auto fixed_tag) {
-    using F = decltype(fixed_tag);
-    if (P < ntiles) issue(P);  // stage P was never used
-    // s0 holds the scores of even sub-tiles, s1 of odd ones
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-    if (wave_active) s0 = qk(0, 0);
-    // steady state: both sub-tiles of tile it are unmasked and tile it+1 exists; NST tiles
-    // at a time with compile-time stages on the fixed path, then one at a time
-    int it = 0;
-    if constexpr (F::value) {
-      auto step = [&](auto st_tag) {
-        if (wave_active) s1 = block_fixed_st(st_tag, std::integral_constant<int, 0>{}, s0);
-        advance(it + 1);
-        if (wave_active) s0 = block_fixed_st(st_tag, std::integral_constant<int, 1>{}, s1);
-        ++it;
-      };
-      static_assert(NST == 4, "the unrolled steady loop walks a ring of four stages");
-      while (2 * (it + NST - 1) + 2 < nsub) {
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
-        step(std::integral_constant<int, 3>{});
-      }
-    }
-    for (; 2 * it + 2 < nsub; ++it) {
-      if (wave_active) {
-        if constexpr (F::value) {
-          s1 = block_fixed(2 * it, s0);
-        } else {
-          s1 = qk(it, 1);
-          soft_pv(s0, 2 * it, std::false_type{}, F{});
-        }
-      }
-      advance(it + 1);
-      if (wave_active) {
-        if constexpr (F::value) {
-          s0 = block_fixed(2 * it + 1, s1);
-        } else {
-          s0 = qk(it + 1, 0);
-          soft_pv(s1, 2 * it + 1, std::false_type{}, F{});
-        }
-      }
-    }
-    // tail: one or two sub-tiles of the last tile; only the very last one can be partial
-    const bool partial = ((t1 - t0) & 31) != 0;
-    if (wave_active) {
-      if (2 * it + 1 < nsub) {
-        s1 = qk(it, 1);
-        soft_pv(s0, 2 * it, std::false_type{}, F{});
-        if (partial)
-          soft_pv(s1, nsub - 1, std::true_type{}, F{});
-        else
-          soft_pv(s1, nsub - 1, std::false_type{}, F{});
-      } else if (partial) {
-        soft_pv(s0, nsub - 1, std::true_type{}, F{});
-      } else {
-        soft_pv(s0, nsub - 1, std::false_type{}, F{});
-      }
-    }
+  // between the blocks of sub-tiles 2T-2 and 2T-1 (T >= 1): tile T+1 has landed (only tile T+2
+  // may still be in flight), then the barrier (every wave is past sub-tile 2T-3, the last use
+  // of tile T-2, and the V^T of tile T, converted before, is visible), tile T+3 goes into the
+  // stage of tile T-2, and tile T+1's V^T is converted
+  auto advance = [&](int T) {
+    if (T + 2 < ntiles) vm_lgkm_wait_barrier<LPT>();
+    else vm_lgkm_wait_barrier<0>();
+    if (T + 3 < ntiles) issue(T + 3);
+    if (T + 1 < ntiles) convert_v(T + 1);
   };
+
   {
-    gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
-    gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
-    const float kn = ((const float *)(slot + dev.sl.knmax))[layer * dm.Hkv + h];
-    {
-      // a row past the live beams reads the request's own q_last row and is zeroed
-      const uint16_t *qsrc = (const uint16_t *)(slot + dev.sl.q_last) + (size_t)layer * dm.Hq * D;
-      if (dm.chain)
-        qsrc = dev.ch.q + ((size_t)(R.row0 + (row_ok ? j_row : 0)) * dm.Hq + (row_ok ? hq_row : 0)) * D;
-      else if (row_ok)
-        qsrc = s == 0 ? qsrc + (size_t)hq_row * D
-                      : (const uint16_t *)dev.tok_q +
-                            ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
-      u32x4_t qr[KB];
+    // a row past the live beams reads the request's own q_last row and is zeroed
+    const uint16_t *qsrc = (const uint16_t *)(slot + dev.sl.q_last) + (size_t)layer * dm.Hq * D;
+    if (dm.chain)
+      qsrc = dev.ch.q + ((size_t)(R.row0 + (row_ok ? j_row : 0)) * dm.Hq + (row_ok ? hq_row : 0)) * D;
+    else if (row_ok)
+      qsrc = s == 0 ? qsrc + (size_t)hq_row * D
+                    : (const uint16_t *)dev.tok_q +
+                          ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
+    u32x4_t qr[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
-      // the tiles the ring holds ahead of the first one, in flight with the query
+    for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
+    // the first four tiles, in flight with the query
 #pragma unroll
-      for (int k = 0; k < P; ++k)
-        if (k < ntiles) issue(k);
+    for (int k = 0; k < NST - 1; ++k)
+      if (k < ntiles) issue(k);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? qr[kb] : u32x4_t{0, 0, 0, 0});
-    }
-    l = 0.f;  // oacc: zero, or set by the first own token
-    // fixed score reference from the Cauchy-Schwarz bound, as in ctx_attn_body
-    {
-      float qn = 0.f;
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? qr[kb] : u32x4_t{0, 0, 0, 0});
+  }
+  if (LAYERED && s > 0) {
+    // the beam's own tokens (the first sets (M, l, o)), then o in units of vscale like the
+    // context's contributions
+    wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, true, qf, M, l, oacc, true);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int db = 0; db < DB; ++db) oacc[db] *= ivs;
+  } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[kb][e], (float)qf[kb][e], qn);
-      qn += __shfl_xor(qn, 32);
-      const float B = row_ok ? sqrtf(qn) * kn * c2 * 1.001f + 1e-3f : 0.f;
-      M = B - 60.f;
-      const float bw = wave_max(B);
-      if (lane == 0) sBound[w] = bw;
-    }
-    if (LAYERED && s > 0) {
-      // the beam's own tokens, against the fixed reference (redone below if the workgroup
-      // takes the lazy path)
-      wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, true, qf, M, l, oacc, true);
-    } else {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
-    }
-    if (!LAYERED && layer > 0 && R.defer_finish) {
-      // finish the previous layer for this workgroup's share of the row block
-      int r0, r1;
-      finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
-      finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
-    }
-    // the first P tiles have landed (explicitly: the compiler does not count the copies) and
-    // sBound is visible
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    float bmax = 0.f;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) bmax = fmaxf(bmax, sBound[i]);
-    const bool fixed_ref = bmax <= 60.f;  // uniform over the workgroup
-    if (!fixed_ref) {
-      M = kNegInf;
-      if (LAYERED) {
-        l = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
-        wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, false, qf, M, l, oacc, false);
-      }
-    }
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  }
+  if (!LAYERED && layer > 0 && R.defer_finish) {
+    // finish the previous layer for this workgroup's share of the row block
+    int r0, r1;
+    finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
+    finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
+  }
+  // the first tiles have landed (explicitly: the compiler does not count the copies); tiles 0
+  // and 1 are converted here, every later one in advance()
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  convert_v(0);
+  if (ntiles > 1) convert_v(1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    if (fixed_ref)
-      run(std::true_type{});
-    else
-      run(std::false_type{});
-
-    float ltot = l + __shfl_xor(l, 32);
-    if constexpr (!LAYERED) {
-      if (wave_active && row_ok) {
-        const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
-        store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, oacc);
-      }
+  // s0 holds the scores of even sub-tiles, s1 of odd ones
+  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+  if (wave_active) {
+    s0 = qk(0, 0);
+    rescale(smax(s0));
+  }
+  // steady state: both sub-tiles of tile it are unmasked and tile it+1 exists; NST tiles at a
+  // time with compile-time stages, then one at a time
+  int it = 0;
+  auto step = [&](auto st_tag) {
+    if (wave_active) s1 = block_st(st_tag, std::integral_constant<int, 0>{}, s0);
+    advance(it + 1);
+    if (wave_active) s0 = block_st(st_tag, std::integral_constant<int, 1>{}, s1);
+    ++it;
+  };
+  while (2 * (it + NST - 1) + 2 < nsub) {
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+  }
+  for (; 2 * it + 2 < nsub; ++it) {
+    if (wave_active) s1 = block(2 * it, s0);
+    advance(it + 1);
+    if (wave_active) s0 = block(2 * it + 1, s1);
+  }
+  // tail: one or two sub-tiles of the last tile; only the very last one can be partial
+  const bool partial = ((t1 - t0) & 31) != 0;
+  if (wave_active) {
+    if (2 * it + 1 < nsub) {
+      s1 = qk(it, 1);
+      soft_pv(s0, 2 * it, std::false_type{});
+      if (partial)
+        soft_pv(s1, nsub - 1, std::true_type{});
+      else
+        soft_pv(s1, nsub - 1, std::false_type{});
+    } else if (partial) {
+      soft_pv(s0, nsub - 1, std::true_type{});
     } else {
-      if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, true);
+      soft_pv(s0, nsub - 1, std::false_type{});
     }
+  }
+
+  // back to units of v
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] *= vs;
+  const float ltot = l + __shfl_xor(l, 32);
+  if constexpr (!LAYERED) {
+    if (wave_active && row_ok) {
+      const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
+      store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, oacc);
+    }
+  } else {
+    if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, true);
   }
 }
 
@@ -2544,7 +2522,7 @@ hipError_t launch_ctx_attn(const Dev &dev, const StepReq *reqs, int n_reqs, int 
   const dim3 blk(nw * 64);
   if (dev.dm.d == 128) {
     if (nw == 8)
-      launch(k_ctx_attn_wide<4, true, false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
+      launch(k_ctx_attn_wide<false>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 4)
       launch(k_ctx_attn_bf16_narrow<128, 4, 64>, grid, blk, st, ev, dev, reqs, n_reqs, layer);
     else if (nw == 2)
@@ -2571,7 +2549,7 @@ hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_re
     return hipGetLastError();
   }
   if ((ctx_kind & 0xFF) != 8) return hipErrorInvalidValue;
-  launch(k_ctx_attn_wide<4, true, true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
+  launch(k_ctx_attn_wide<true>, dim3(total_wgs), dim3(512), st, ev, dev, reqs, n_reqs, layer0);
   return hipGetLastError();
 }
 

@@ -199,7 +199,7 @@ def test_layered_stream_steps_match_oracle():
 def test_mixed_variant_steps_match_oracle():
     """Continuous batching over every context-attention variant at once: six requests whose
     (context, beam width) pick the one-wave and two-wave streaming kernels, the four-wave
-    narrow kernel, and the wide kernel with two-term and single-term P; the second half is
+    narrow kernel, and the wide kernel (short and long contexts); the second half is
     admitted one step later, so the middle steps mix levels and variants (five groups, each
     group's chain of layer launches on its own stream, the fifth sharing the first's).  Each
     request is checked teacher-forced after each of its steps, with every layer's attention

@@ -1,18 +1,22 @@
 """Large query and key norms: parity of every bf16 context-attention variant on its
 running-max path.
 
-The context kernels take a fixed score reference when every row of a workgroup has the
-Cauchy-Schwarz bound B = |q| max|k| log2(e)/sqrt(d) <= 60, and otherwise track a running
-maximum with a lazy rescale (in the full-context kernels the beam's own tokens are then merged
-again from an empty state).  The other tests draw N(0, 1) queries and keys (B of about 15-25),
-which never reach that path; a trained model's activations do.  Here queries and context keys
-are scaled by exact powers of two (the search is then a different, sharper one, which the
-oracle recomputes from the same scaled inputs):
+The one-, two- and four-wave context kernels take a fixed score reference when every row of a
+workgroup has the Cauchy-Schwarz bound B = |q| max|k| log2(e)/sqrt(d) <= 60, and otherwise track
+a running maximum with a lazy rescale (in the full-context kernels the beam's own tokens are
+then merged again from an empty state); the eight-wave (wide) kernel always keeps a running
+maximum, with P as one float16 term against float16 V.  The other tests draw N(0, 1) queries
+and keys (B of about 15-25), which never reach the running-max path of the narrow kernels; a
+trained model's activations do.  Here queries and context keys are scaled by exact powers of
+two (the search is then a different, sharper one, which the oracle recomputes from the same
+scaled inputs):
 
   qk2    queries and context keys x2: B of about 75, softmax still spread over many tokens
   qk8    x8 each: B of about 1200, attention close to one-hot (rescales along the loop)
   ownk16 only the fed-back tokens' keys x16: B stays small (fixed reference), and the beam's
          own tokens push the reference up from their online merge
+  q2     queries x2: B of about 40 (fixed reference), attention twice as sharp as N(0, 1)
+         scores give
 
 Each case is checked teacher-forced at every level with every layer's attention output of
 every beam, the hidden vector, the beam set and scores, and BeamPath closure."""
@@ -27,13 +31,15 @@ MODES = {
     "qk2": dict(q_scale_log2=1, k_scale_log2=1),
     "qk8": dict(q_scale_log2=3, k_scale_log2=3),
     "ownk16": dict(own_k_scale_log2=4),
+    "q2": dict(q_scale_log2=1),
 }
+FIXED_REF = ("ownk16", "q2")
 
 
 def _premise(cfg, mode, r=0):
     """The inputs take the intended path (checked on the host from the drawn values)."""
     lo, hi = score_bound(cfg, r)
-    if mode == "ownk16":
+    if mode in FIXED_REF:
         assert hi <= 60.0, hi
     else:
         assert lo > 60.0, lo
@@ -76,7 +82,7 @@ def _run(cfg, mode, steps, checked, **engine_kw):
 def test_fused_first_level_and_layered_wide(mode):
     """Level 0: every layer of four requests in one launch (one-wave stream kernel, split
     partials); levels 1-2: 200 beams x 2 heads = two 256-row blocks per kv head on the wide
-    kernel, each workgroup over the whole (ragged, 700-token) context of one layer, two-term P."""
+    kernel, each workgroup over the whole (ragged, 700-token) context of one layer."""
     cfg = synth.get_config("ctx1k_beam256", n_requests=4, n_layers=3, ctx_len=700, beam_width=200, n_items=50000,
                            **MODES[mode])
     _run(cfg, mode, _lockstep(cfg, range(4)), [0, 3])
@@ -84,7 +90,7 @@ def test_fused_first_level_and_layered_wide(mode):
 
 @pytest.mark.parametrize("mode", list(MODES))
 def test_layered_wide_single_bf16_p(mode):
-    """Contexts of 4100 tokens (>= 4096: P rounded once to bf16) on the full-context wide
+    """Contexts of 4100 tokens (65 tiles: the five-stage ring wraps many times) on the full-context wide
     kernel, 130 beams x 2 heads = a full and a nearly empty row block."""
     cfg = synth.get_config("ctx1k_beam256", n_requests=8, n_layers=2, ctx_len=4100, beam_width=130, n_items=50000,
                            **MODES[mode])
@@ -95,7 +101,7 @@ def test_layered_wide_single_bf16_p(mode):
 def test_split_k_variants(mode):
     """One launch per layer and variant with split-K partials (the step does not fill the chip
     with full-context workgroups): one-wave and two-wave stream kernels, the four-wave narrow
-    kernel, the wide kernel with two-term P (600 tokens) and single P (4100 tokens); the next
+    kernel, the wide kernel on 600- and 4100-token contexts; the next
     layer's launch finishes each layer, and the variant groups run on four streams."""
     shapes = ((700, 8), (1500, 30), (900, 50), (600, 200), (4100, 66))
     cfg = synth.get_config("ragged_r128", n_requests=5, n_layers=2, shapes=shapes, n_items=60000, waves=1,
