@@ -24,6 +24,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gr_internal.h"
 
 namespace gr {
@@ -157,19 +159,20 @@ __global__ __launch_bounds__(256) void k_chain_final(Dev dev, const StepReq *__r
 }
 
 // ---------------------------------------------------------------------------------------- GEMM
-// Workgroup: 256 threads, four waves in 2 x 2, a 128 (rows) x 128 (weight rows) tile; wave
-// (wm, wn) owns 64 x 64 as 2 x 2 MFMA blocks.  The K loop takes 32 columns per stage: the
-// stage's A and W tiles (8 KB each) go from global memory straight into LDS
-// (global_load_lds_dwordx4, 1 KB of consecutive LDS per wave instruction, 4 per lane and
-// stage), a ring of four stages with three in flight; 64 KB of LDS, so two workgroups share a
-// compute unit (two waves per SIMD).  LDS rows are 64 bytes (4 chunks of 16); chunk c of row r
-// sits at c ^ ((r >> 2) & 3): the LDS serves 16 lanes (16 rows, one chunk each) over its 64
-// banks at a time, and rows r, r+4, r+8, r+12 (same banks otherwise) then take the four
-// different chunk positions.  The MFMA computes the transposed block D[n][m] = W_blk (32 x 16)
-// x A_blk^T (16 x 32): lane (m, hh) then holds output row m, columns 8a + 4hh + {0..3} of the
-// block, so each epilogue write is a run of four columns of one row.
+// Workgroup: 256 threads, four waves in 2 x 2 over a 128 (rows) x 2*WN (weight rows) tile; wave
+// (wm, wn) owns 64 x WN as 2 x (WN/32) MFMA blocks (WN = 128 for the wide projections: six
+// fragment reads per eight MFMAs).  The K loop takes 64 columns per stage: the stage's A tile
+// (16 KB) and W tile (WN/2 KB) go from global memory straight into LDS (global_load_lds_dwordx4,
+// 1 KB of consecutive LDS per wave instruction), a ring of three stages with two in flight and
+// one barrier per stage (4 k-steps of 16, 8 * (WN/32) MFMAs per wave between barriers); each
+// k-step's fragments are read while the previous k-step's MFMAs run.  LDS rows are 128 bytes
+// (8 chunks of 16): chunk c of row r sits at c ^ (r & 7) ^ ((r >> 3) & 1), so each group of 16
+// lanes (16 rows, one chunk each) covers the 64 banks once.  The MFMA computes the transposed
+// block D[n][m] = W_blk (32 x 16) x A_blk^T (16 x 32): lane (m, hh) then holds output row m,
+// columns 8a + 4hh + {0..3} of the block, so each epilogue write is a run of four columns of one
+// row.
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
-constexpr int GBM = 128, GBN = 128, GBK = 32, GNST = 4;
+constexpr int GBM = 128, GBK = 64, GNST = 3;
 
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
@@ -177,6 +180,7 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 struct GemmArgs {
   const uint16_t *A;    // [rows][K] bf16
@@ -189,7 +193,8 @@ struct GemmArgs {
   uint16_t *out;        // EPI_QKV: q rows [rows][n1]; EPI_SWIGLU: act [rows][N / 2]
 };
 
-// source row of weight-tile row r (tile columns n0 .. n0 + 127)
+// source row of weight-tile row r (tile columns n0 ..); SwiGLU tiles alternate 32 gate rows and
+// the matching 32 up rows
 template <int EPI>
 __device__ __forceinline__ const uint16_t *w_row(const GemmArgs &g, int n0, int r) {
   if constexpr (EPI == EPI_SWIGLU) {
@@ -206,27 +211,27 @@ __device__ __forceinline__ const uint16_t *w_row(const GemmArgs &g, int n0, int 
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 0 || N == 4 || N == 8, "unsupported wait");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0 || N == 8 || N == 12, "unsupported wait");
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs, GemmArgs g,
-                                                 int m_tiles) {
-  constexpr int CPR = GBK / 8;                 // 16-byte chunks per LDS row
-  constexpr int NI = GBM * CPR / 256;          // DMA instructions per lane and operand per stage
-  constexpr int P = GNST - 1;                  // stages in flight
-  static_assert(GBM == GBN && CPR == 4 && NI == 2 && P == 3, "tile shape");
-  __shared__ bf16x8_t sA[GNST][GBM * CPR];
-  __shared__ bf16x8_t sW[GNST][GBN * CPR];
+template <int EPI, int WN>
+__global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs, GemmArgs g,
+                                              int m_tiles) {
+  constexpr int BN = 2 * WN;                            // weight rows per tile
+  constexpr int NB = WN / 32;                           // MFMA blocks along the weight rows per wave
+  constexpr int AI = GBM * 8 / 256, WI = BN * 8 / 256;  // DMA instructions per lane and stage
+  static_assert(GNST == 3 && (WN == 64 || WN == 128), "tile shape");
+  __shared__ bf16x8_t sA[GNST][GBM * 8];
+  __shared__ bf16x8_t sW[GNST][BN * 8];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;
   // workgroups are dealt round-robin over the 8 XCDs (blockIdx % 8): when the weight tiles split
   // evenly, XCD x takes weight tiles x, x+8, ... and runs every row tile of each, so a weight tile
   // is fetched into one XCD's L2 only (the smaller activation rows are what each XCD re-reads)
-  const int n_tiles = g.N / GBN;
+  const int n_tiles = g.N / BN;
   int mt, nt;
   if ((n_tiles & 7) == 0) {
     const int xcd = (int)blockIdx.x & 7, idx = (int)blockIdx.x >> 3;
@@ -236,100 +241,113 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Dev dev, const StepReq *__restr
     mt = (int)blockIdx.x % m_tiles;
     nt = (int)blockIdx.x / m_tiles;
   }
-  const int m0 = mt * GBM, n0 = nt * GBN;
+  const int m0 = mt * GBM, n0 = nt * BN;
   const int KT = g.K / GBK;
 
-  // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane: row p / CPR, stored
-  // position p % CPR <- global chunk (p % CPR) ^ ((row >> 2) & 3); the 16 rows of one instruction
-  // lie in one 32-row weight block
-  const uint16_t *asrc[NI], *wsrc[NI];
+  // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane: row p >> 3, stored
+  // position p & 7 <- global chunk (p & 7) ^ swz(row); the 8 rows of one instruction lie in one
+  // 32-row weight block
+  const uint16_t *asrc[AI], *wsrc[WI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int p = (i * 4 + w) * 64 + lane, r = p / CPR, c = (p % CPR) ^ ((r >> 2) & 3);
+  for (int i = 0; i < AI; ++i) {
+    const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
     asrc[i] = g.A + (size_t)(m0 + r) * g.K + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
     wsrc[i] = w_row<EPI>(g, n0, r) + c * 8;
   }
   const uint32_t adst = lds_addr(&sA[0][0]) + w * 1024, wdst = lds_addr(&sW[0][0]) + w * 1024;
   auto issue = [&](int kt) {
     const int st = kt % GNST;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * CPR * 16) + i * 4096);
+    for (int i = 0; i < AI; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * 128) + i * 4096);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (GBN * CPR * 16) + i * 4096);
+    for (int i = 0; i < WI; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (BN * 128) + i * 4096);
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[NB][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NB; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
 
-#pragma unroll
-  for (int k = 0; k < P; ++k)
-    if (k < KT) issue(k);
-  const int rl = lane & 31, sw = (rl >> 2) & 3;
+  issue(0);
+  if (KT > 1) issue(1);
+  const int rl = lane & 31, sw = swz(rl);
   for (int kt = 0; kt < KT; ++kt) {
-    // stage kt has landed once at most the copies of the stages issued after it remain
-    const int ahead = min(P - 1, KT - 1 - kt);
-    if (ahead >= 2) vm_wait_barrier<4 * NI>(); else if (ahead == 1) vm_wait_barrier<2 * NI>(); else vm_wait_barrier<0>();
-    if (kt + P < KT) issue(kt + P);  // into the stage of tile kt-1, which every wave has left
+    // stage kt has landed once at most the copies of stage kt+1 remain in flight
+    if (kt + 1 < KT) vm_wait_barrier<AI + WI>(); else vm_wait_barrier<0>();
+    if (kt + 2 < KT) issue(kt + 2);  // into the stage of tile kt-1, which every wave has left
     const int st = kt % GNST;
-    const bf16x8_t *a = &sA[st][0], *b = &sW[st][0];
+    const bf16x8_t *a = &sA[st][(wm * 64 + rl) * 8], *b = &sW[st][(wn * WN + rl) * 8];
+    bf16x8_t af[2][2], wf[2][NB];
+    auto frags = [&](int ks, int buf) {
+      const int ch = (2 * ks + hh) ^ sw;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) af[buf][mb] = a[mb * 32 * 8 + ch];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wf[buf][nb] = b[nb * 32 * 8 + ch];
+    };
+    frags(0, 0);
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      const int ch = (2 * ks + hh) ^ sw;
-      bf16x8_t af[2], wf[2];
+      // the next k-step's reads are issued ahead of this k-step's MFMAs (kept in that order)
+      if (ks + 1 < GBK / 16) frags(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[mb] = a[(wm * 64 + mb * 32 + rl) * CPR + ch];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) wf[nb] = b[(wn * 64 + nb * 32 + rl) * CPR + ch];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[mb], acc[nb][mb], 0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][nb], af[ks & 1][mb], acc[nb][mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- epilogue: lane (rl, hh) of block (nb, mb) holds row m0 + wm*64 + mb*32 + rl, columns
-  // n0 + wn*64 + nb*32 + 8a + 4hh + c, c = 0..3, in acc[nb][mb][4a + c]
+  // n0 + wn*WN + nb*32 + 8a + 4hh + c, c = 0..3, in acc[nb][mb][4a + c]
+  const int ncol0 = n0 + wn * WN;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int row = m0 + wm * 64 + mb * 32 + rl;
     if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          float *p = g.x + (size_t)row * g.N + n0 + wn * 64 + nb * 32 + 8 * a + 4 * hh;
+          float *p = g.x + (size_t)row * g.N + ncol0 + nb * 32 + 8 * a + 4 * hh;
           const f32x4_t o = gld<f32x4_t>(p);
           gst<f32x4_t>(p, f32x4_t{o[0] + acc[nb][mb][4 * a], o[1] + acc[nb][mb][4 * a + 1],
                                   o[2] + acc[nb][mb][4 * a + 2], o[3] + acc[nb][mb][4 * a + 3]});
         }
     } else if constexpr (EPI == EPI_SWIGLU) {
-      // block 0 of the wave holds gate columns, block 1 the matching up columns
-      const int i0 = (n0 + wn * 64) / 2;
+      // blocks 2p and 2p+1 of the wave hold gate columns and the matching up columns
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float v[4];
+      for (int pr = 0; pr < NB / 2; ++pr) {
+        const int i0 = ncol0 / 2 + pr * 32;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float gt = acc[0][mb][4 * a + c], up = acc[1][mb][4 * a + c];
-          v[c] = gt / (1.f + expf(-gt)) * up;
+        for (int a = 0; a < 4; ++a) {
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float gt = acc[2 * pr][mb][4 * a + c], up = acc[2 * pr + 1][mb][4 * a + c];
+            v[c] = gt / (1.f + expf(-gt)) * up;
+          }
+          gst<u32x2_t>(g.out + (size_t)row * (g.N / 2) + i0 + 8 * a + 4 * hh,
+                       u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
         }
-        gst<u32x2_t>(g.out + (size_t)row * (g.N / 2) + i0 + 8 * a + 4 * hh,
-                     u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
       }
     } else {
       // q columns -> the step's q rows; k, v columns -> BeamKV of the row's request (live beams
-      // at steps s >= 1 only).  The 32 rows of a block belong to one request.
-      const int nb0 = n0 + wn * 64;
-      if (nb0 < g.n1) {
+      // at steps s >= 1 only).  The 32 rows of a block belong to one request; the WN columns of
+      // a wave to one of q, k, v.
+      if (ncol0 < g.n1) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int a = 0; a < 4; ++a)
-            gst<u32x2_t>(g.out + (size_t)row * g.n1 + nb0 + nb * 32 + 8 * a + 4 * hh,
+            gst<u32x2_t>(g.out + (size_t)row * g.n1 + ncol0 + nb * 32 + 8 * a + 4 * hh,
                          u32x2_t{pack_bf16(acc[nb][mb][4 * a], acc[nb][mb][4 * a + 1]),
                                  pack_bf16(acc[nb][mb][4 * a + 2], acc[nb][mb][4 * a + 3])});
       } else {
@@ -340,13 +358,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Dev dev, const StepReq *__restr
         const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
         if (s > 0 && blk0 >= R.row0 && j < n_live && j < R.n_bound) {
           const Dims &dm = dev.dm;
-          const bool is_v = nb0 >= g.n2;
+          const bool is_v = ncol0 >= g.n2;
           uint16_t *kv = (uint16_t *)(slot + (is_v ? dev.sl.beamkv_v : dev.sl.beamkv_k));
           const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
           uint16_t *dst = kv + (size_t)g.layer * (dm.levels - 1) * lvstride + (size_t)(s - 1) * lvstride +
-                          (size_t)j * wstride + (nb0 - (is_v ? g.n2 : g.n1));
+                          (size_t)j * wstride + (ncol0 - (is_v ? g.n2 : g.n1));
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int a = 0; a < 4; ++a)
               gst<u32x2_t>(dst + nb * 32 + 8 * a + 4 * hh,
@@ -433,12 +451,22 @@ hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, in
   } else {
     return hipErrorInvalidValue;
   }
-  if (g.N % GBN != 0 || g.K % GBK != 0) return hipErrorInvalidValue;
+  if (g.K % GBK != 0) return hipErrorInvalidValue;
+  // 256 weight rows per tile where the q / k / v (or gate / up) ranges allow it and the tiles
+  // still fill the chip, else 128
   const int m_tiles = rows / GBM;
-  const dim3 grid((unsigned)(m_tiles * (g.N / GBN)));
-  if (epi == EPI_QKV) launch(k_gemm<EPI_QKV>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
-  else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
-  else launch(k_gemm<EPI_SWIGLU>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+  const bool wide = g.N % 256 == 0 && (epi != EPI_QKV || (g.n1 % 256 == 0 && (g.n2 - g.n1) % 256 == 0)) &&
+                    (long)m_tiles * (g.N / 256) >= 256;
+  if (!wide && g.N % 128 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(m_tiles * (g.N / (wide ? 256 : 128))));
+  auto go = [&](auto wn) {
+    constexpr int WN = decltype(wn)::value;
+    if (epi == EPI_QKV) launch(k_gemm<EPI_QKV, WN>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+    else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID, WN>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+    else launch(k_gemm<EPI_SWIGLU, WN>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+  };
+  if (wide) go(std::integral_constant<int, 128>{});
+  else go(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 
