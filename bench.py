@@ -29,18 +29,16 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # HBM bytes per layer of the context-attention kernels on this workload, from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
-# the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000), and
-# divided by the layers one dispatch covers (one with one layer per launch; 14 for the wide
-# kernel and all 28 for the first-level launch of the multi-layer variant);
+# the same counters read for a 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000); one
+# dispatch covers one layer in the headline's launch sequence;
 # profiles/hbm_traffic_ctx5k_beam256_r8.md.  They belong to the kernel code they were taken on
 # (source_digest of gr_kernels.hip: comments excluded); with any other code, or a variant not
-# measured, the traffic is reported as null.
+# measured (the several-layers-per-launch variant), the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "f1d6bdc3eb22b130a9eb529ffe81b5297ef79a44b9b0e97c9e9e01fecf4fc08a",
-    "fused": {"k_ctx_attn_wide": {"read": 181454927, "written": 21535287},
-              "k_ctx_attn_stream": {"read": 166624539, "written": 278601}},
-    "per_layer": {},
+    "source_sha256": "fc1f08c327049cb076fdd6e36ee7bc77d4f5ddc8f519a42ca326013e6414f5fb",
+    "per_layer": {"k_ctx_attn_wide": {"read": 168465599, "written": 34078720},
+                  "k_ctx_attn_stream": {"read": 165734766, "written": 540672}},
 }
 
 
@@ -541,10 +539,10 @@ def decode_leg(cfg, args, per_layer: bool):
     achieved_gbs0 = ctx_bytes(0) * n_0 / (ms_0 * 1e-3) / 1e9 if ms_0 > 0 else 0.0
     step_us = {f"level{s}": 1e3 * prof["step"][s][0] / max(prof["step"][s][1], 1) for s in range(lv)}
 
-    # the unit is one layer of one step over every request: a dispatch covers one layer (one layer
-    # per launch) or several.  The kernel also finishes a layer (beam tokens, BeamKV append, the
-    # split merge, h += o): that time is in the denominator, those bytes are not in the
-    # algorithmic count.
+    # the unit is one layer of one step over every request: a dispatch covers one layer (the
+    # headline's launch sequence) or several (the multi-layer variant, whose kernel also merges
+    # the beam's own tokens and stores the layer's hidden partial: that time is in its
+    # denominator, those bytes are not in the algorithmic count)
     wide = cfg.dtype == "bf16" and cfg.head_dim == 128
     d_m = sum(G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, s) for s in levels_mfma)
     d_0 = G.gr_engine_profile_dispatches(eng.eng, G.GR_PROF_CTX_ATTN, 0)
