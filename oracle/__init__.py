@@ -23,7 +23,10 @@ What it computes (one request, one beam-search decode):
   valid item prefix are candidates.
 * Candidate scoring (paper-daily article, section "Background": given
   candidates are ranked by the model): an item's log-probability is the sum
-  of its per-level constrained log-probabilities at its own prefixes.
+  of its per-level constrained log-probabilities at its own prefixes; and by
+  label tokens (sections "Background" and "Scoring many candidates at once"):
+  the label log-probabilities read from each candidate's last token, the
+  candidate seeing the context and itself only (``label_scores``).
 
 Readings where the pages are silent (each is a choice, see ``beam.py``):
 query of step 0 is the last context token's query; a fed-back code's q/k/v
@@ -57,6 +60,7 @@ from .beam import (  # noqa: F401
     beam_search,
     codebook_logits,
     constrained_log_softmax,
+    label_scores,
     score_items,
     select_topk,
     step_candidates,

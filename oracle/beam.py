@@ -247,6 +247,28 @@ def score_items(req: Request, model: Model, prefixes: PrefixSet, items, norm: st
     return out
 
 
+def label_scores(req: Request, model: Model, items, w_label: np.ndarray) -> np.ndarray:
+    """Label-token log-probabilities of given candidates (paper-daily article, sections
+    "Background" and "Scoring many candidates at once": the candidates go into the prompt, each
+    sees only the shared prefix and itself, and the model's log-probabilities of label tokens
+    such as "yes" and "no", read after each candidate, rank them).
+
+    Each candidate (c_0 .. c_{T-1}) is its own sequence: the context followed by its T code
+    tokens (the model's tables hold a token for every level, T = n_levels); h is the hidden
+    vector of its last token, whose query reads the context and all T tokens (beam_hidden of the
+    full tuple); z = h @ w_label ([Hq*d][n_labels]) and the result row is z - logsumexp(z).
+    Returns [n][n_labels]."""
+    items = np.asarray(items, dtype=np.int64)
+    w_label = np.asarray(w_label, dtype=np.float64)
+    out = np.empty((items.shape[0], w_label.shape[1]))
+    for i in range(items.shape[0]):
+        h = beam_hidden(req, model, tuple(int(c) for c in items[i]))
+        z = h @ w_label
+        m = z.max()
+        out[i] = z - (m + np.log(np.sum(np.exp(z - m))))
+    return out
+
+
 def beam_search(req: Request, model: Model, prefixes: PrefixSet, W: int, norm: str = "valid"):
     """Full decode of one request: n_levels steps from the empty prefix ([BG]).
 

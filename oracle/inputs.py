@@ -18,6 +18,14 @@ def model_for(cfg) -> Model:
 
 
 @functools.lru_cache(maxsize=8)
+def label_model_for(cfg) -> Model:
+    """The model with the label level's token tables appended (candidate scoring by labels)."""
+    import synth
+    tq, tk, tv = synth.token_tables_with_labels(cfg)
+    return Model.from_arrays(tq, tk, tv, synth.w_sid(cfg))
+
+
+@functools.lru_cache(maxsize=8)
 def prefixes_for(cfg) -> PrefixSet:
     import synth
     return PrefixSet(synth.items(cfg), cfg.codebook)

@@ -43,12 +43,15 @@ from .gen import (  # noqa: F401
     x_last,
     ctx_kv_block,
     items,
+    label_token_tables,
     prefill_tables,
     prefill_tokens,
     q_last,
     request_shapes,
     soft_token_weights,
     token_tables,
+    token_tables_with_labels,
     user_vector,
+    w_label,
     w_sid,
 )

@@ -161,6 +161,43 @@ def token_tables(cfg: Config):
     return times_pow2(tq, cfg.q_scale_log2), times_pow2(tk, cfg.own_k_scale_log2), tv
 
 
+_T_LB_Q, _T_LB_K, _T_LB_V, _T_LB_W = range(30, 34)
+
+
+def label_token_tables(cfg: Config):
+    """Tables of the last level's codes as tokens (the label read of candidate scoring):
+    (TQ [L][V][Hq][d], TK [L][V][Hkv][d], TV same as TK), drawn like token_tables (bf16: a Philox
+    stream per tensor and layer; f32: normals from a stream of their own)."""
+    L, V, Hq, Hkv, d = cfg.n_layers, cfg.codebook, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    if cfg.dtype == "f32":
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, cfg.cfg_id, _T_LB_Q]))
+        tq = rng.standard_normal((L, V, Hq, d)).astype(np.float32)
+        tk = rng.standard_normal((L, V, Hkv, d)).astype(np.float32)
+        tv = rng.standard_normal((L, V, Hkv, d)).astype(np.float32)
+        return times_pow2(tq, cfg.q_scale_log2), times_pow2(tk, cfg.own_k_scale_log2), tv
+    tq = np.empty((L, V, Hq, d), dtype=np.uint16)
+    tk = np.empty((L, V, Hkv, d), dtype=np.uint16)
+    tv = np.empty_like(tk)
+    for l in range(L):
+        tq[l] = _bf16_normal(_philox(cfg, _T_LB_Q, l), tq.shape[1:])
+        tk[l] = _bf16_normal(_philox(cfg, _T_LB_K, l), tk.shape[1:])
+        tv[l] = _bf16_normal(_philox(cfg, _T_LB_V, l), tv.shape[1:])
+    return times_pow2(tq, cfg.q_scale_log2), times_pow2(tk, cfg.own_k_scale_log2), tv
+
+
+def token_tables_with_labels(cfg: Config):
+    """token_tables with the label level appended: [L][n_levels][V][H][d] each."""
+    base, last = token_tables(cfg), label_token_tables(cfg)
+    return tuple(np.concatenate([b, x[:, None]], axis=1) for b, x in zip(base, last))
+
+
+def w_label(cfg: Config, n_labels: int) -> np.ndarray:
+    """Label head [Hq*d][n_labels] float32, N(0, 1/(Hq*d)) (variance), like w_sid."""
+    rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, cfg.cfg_id, _T_LB_W, n_labels]))
+    H = cfg.n_q_heads * cfg.head_dim
+    return (rng.standard_normal((H, n_labels)) * np.sqrt(1.0 / H)).astype(np.float32)
+
+
 def w_sid(cfg: Config) -> np.ndarray:
     """Codebook projection [levels][Hq*d][V] float32, N(0, 1/(Hq*d)) (variance)."""
     if cfg.dtype == "f32":
