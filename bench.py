@@ -80,7 +80,9 @@ def workload_text(cfg, shapes):
 def scoring_leg(cfg, args, per_layer=True):
     """Candidate scoring on the same contexts: 500 given items per request per call (the pages'
     scoring workload), items of the set drawn with repeats; every request of the workload in
-    one call (gr_score_items_batch), calls timed end to end (each call synchronises)."""
+    one call, calls timed end to end (each call synchronises): by the item log-likelihood
+    (gr_score_items_batch), and by two label tokens read after each candidate
+    (gr_score_items_labels: the same steps plus the label step)."""
     import numpy as np
     import torch
 
@@ -88,7 +90,7 @@ def scoring_leg(cfg, args, per_layer=True):
     from semantic_id_beam_amd.workloads import make_engine, request_tensors
     n_cand, n_calls = 500, max(4, args.steps // 2)
     R = cfg.n_requests
-    eng = make_engine(cfg, max_requests=R, max_beam_width=512, per_layer=per_layer)
+    eng = make_engine(cfg, max_requests=R, max_beam_width=512, per_layer=per_layer, n_labels=2)
     for r in range(R):
         k, v, q = request_tensors(cfg, r)
         eng.load(r, k, v, q, synth.request_shapes(cfg)[r][1])
@@ -97,19 +99,26 @@ def scoring_leg(cfg, args, per_layer=True):
     rng = np.random.default_rng(11)
     cands = np.stack([items[rng.integers(0, items.shape[0], size=n_cand)] for _ in range(R)]).astype(np.int32)
     rids = list(range(R))
-    for _ in range(2):
-        eng.score_items_batch(rids, cands)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(n_calls):
-        sc = eng.score_items_batch(rids, cands)
-    dt = time.perf_counter() - t0
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_calls):
+            out = fn()
+        return time.perf_counter() - t0, out
+
+    dt, sc = timed(lambda: eng.score_items_batch(rids, cands))
+    dl, (_, lab) = timed(lambda: eng.score_items_labels(rids, cands))
     eng.close()
-    log(f"scoring: {n_calls} calls of {R} x {n_cand} candidates in {dt:.3f} s")
-    assert np.all(np.isfinite(sc))
+    log(f"scoring: {n_calls} calls of {R} x {n_cand} candidates in {dt:.3f} s; with labels {dl:.3f} s")
+    assert np.all(np.isfinite(sc)) and np.all(np.isfinite(lab))
     return {"requests_per_call": R, "candidates_per_request": n_cand, "calls": n_calls,
             "ms_per_call": round(1e3 * dt / n_calls, 3),
-            "candidates_per_s": round(R * n_cand * n_calls / dt, 1)}
+            "candidates_per_s": round(R * n_cand * n_calls / dt, 1),
+            "labels": {"n_labels": 2, "ms_per_call": round(1e3 * dl / n_calls, 3),
+                       "candidates_per_s": round(R * n_cand * n_calls / dl, 1)}}
 
 
 def prefill_leg(cfg, args, vocab: int = 32768, user_dim: int = 256, embed_dim: int = 2048, reps: int = 5):

@@ -109,6 +109,20 @@ typedef struct {
   const float *g_final;      /* device [D] */
 } gr_chain_desc;
 
+/* The label head for scoring given candidates by label tokens ([TRT] sections "Background" and
+ * "Scoring many candidates at once": the candidates go into the prompt, each sees only the shared
+ * prefix and itself, and the model's log-probabilities of label tokens such as "yes" and "no",
+ * read after each candidate, rank them).  With a label head the token tables hold n_levels levels
+ * instead of n_levels - 1: level n_levels - 1 gives a candidate's last code its query, key and
+ * value, so that code runs as a token (attending to the context, the candidate's earlier codes and
+ * itself), and its hidden vector h (as the step's hidden vector: the sum over layers of the
+ * attention outputs) gives z_c = h . w_label[:, c] and the label log-probabilities z_c -
+ * logsumexp(z) over the n_labels outputs.  Limits: 1 <= n_labels <= 16; not with a layer chain. */
+typedef struct {
+  int32_t n_labels;
+  const float *w_label; /* device [n_q_heads*head_dim][n_labels] float32 */
+} gr_label_desc;
+
 /* Model description.  Limits: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0;
  * n_q_heads * head_dim a multiple of 128; 1 <= n_levels <= 8; 2 <= codebook_size <= 1024
  * and codebook_size**n_levels < 2**62.
@@ -120,12 +134,14 @@ typedef struct {
   int32_t n_levels, codebook_size;
   int32_t dtype; /* gr_dtype: ContextKV, BeamKV and token tables */
   int32_t norm;  /* gr_norm */
-  const void *tok_q;   /* device [L][n_levels-1][V][Hq][d]  (the stand-in; unused by a chain) */
-  const void *tok_k;   /* device [L][n_levels-1][V][Hkv][d] */
-  const void *tok_v;   /* device [L][n_levels-1][V][Hkv][d] */
+  const void *tok_q;   /* device [L][T][V][Hq][d]  (the stand-in; unused by a chain); T = n_levels-1,
+                          or n_levels with a label head */
+  const void *tok_k;   /* device [L][T][V][Hkv][d] */
+  const void *tok_v;   /* device [L][T][V][Hkv][d] */
   const float *w_sid;  /* device [n_levels][Hq*d][V] float32 */
   const gr_chain_desc *chain; /* host, read at gr_engine_create: the layer-chain model; NULL = the
                                  table stand-in above */
+  const gr_label_desc *label; /* host, read at gr_engine_create: the label head; NULL = none */
 } gr_model_desc;
 
 /* The valid items: distinct code tuples (duplicates are tolerated and merged).
@@ -363,6 +379,17 @@ gr_status gr_score_items(gr_engine *eng, int64_t request_id, const int32_t *item
  * GR_E_INVALID_ARG for n_requests outside 1..max_requests or a duplicate id. */
 gr_status gr_score_items_batch(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, const int32_t *items,
                                int32_t n, float *scores, void *stream);
+
+/* Candidate scoring by label tokens ([TRT] "Background", "Scoring many candidates at once"):
+ * runs gr_score_items_batch (scores[i][k]: candidate k's item log-likelihood, as there), then one
+ * more step in which each candidate's last code runs as a token over the context and the
+ * candidate's earlier codes (each candidate sees the shared context and itself only), and the
+ * label head on its hidden vector.  label_logp: host [n_requests][n][n_labels] float32, the label
+ * log-probabilities of candidate k of request i.  Needs an engine with a label head
+ * (GR_E_BAD_STATE otherwise); same argument rules as gr_score_items_batch.  Synchronises
+ * `stream`. */
+gr_status gr_score_items_labels(gr_engine *eng, const int64_t *request_ids, int32_t n_requests, const int32_t *items,
+                                int32_t n, float *scores, float *label_logp, void *stream);
 
 /* Releases a request's slot and pool space (host bookkeeping only; later work
  * on the same stream may reuse them).  Errors: GR_E_NOT_FOUND. */

@@ -36,7 +36,7 @@ EXPORTS = [
     "gr_debug_hidden", "gr_debug_attn_out", "gr_engine_set_profiling", "gr_engine_profile_read",
     "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
     "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
-    "gr_sched_completed", "gr_sched_result", "gr_sched_counts", "gr_debug_chain_rows",
+    "gr_sched_completed", "gr_sched_result", "gr_sched_counts", "gr_debug_chain_rows", "gr_score_items_labels",
 ]
 GR_CHAIN_X_IN, GR_CHAIN_XN_ATTN, GR_CHAIN_Q, GR_CHAIN_O, GR_CHAIN_X_MID, GR_CHAIN_XN_MLP, GR_CHAIN_ACT, \
     GR_CHAIN_X_OUT = range(8)
@@ -56,12 +56,16 @@ class gr_chain_desc(C.Structure):
                 ("g_final", C.c_void_p)]
 
 
+class gr_label_desc(C.Structure):
+    _fields_ = [("n_labels", C.c_int32), ("w_label", C.c_void_p)]
+
+
 class gr_model_desc(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("n_levels", C.c_int32), ("codebook_size", C.c_int32),
                 ("dtype", C.c_int32), ("norm", C.c_int32),
                 ("tok_q", C.c_void_p), ("tok_k", C.c_void_p), ("tok_v", C.c_void_p), ("w_sid", C.c_void_p),
-                ("chain", C.POINTER(gr_chain_desc))]
+                ("chain", C.POINTER(gr_chain_desc)), ("label", C.POINTER(gr_label_desc))]
 
 
 class gr_item_set(C.Structure):
@@ -132,6 +136,7 @@ def lib() -> C.CDLL:
         "gr_engine_profile_dispatches": (i32, [vp, i32, i32, P(i64)]),
         "gr_score_items": (i32, [vp, i64, vp, i32, vp, vp]),
         "gr_score_items_batch": (i32, [vp, vp, i32, vp, i32, vp, vp]),
+        "gr_score_items_labels": (i32, [vp, vp, i32, vp, i32, vp, vp, vp]),
         "gr_engine_profile_reset": (i32, [vp]),
         "gr_sched_create": (i32, [vp, i32, vp, P(vp)]),
         "gr_sched_destroy": (i32, [vp]),
@@ -284,6 +289,18 @@ def gr_score_items_batch(eng: int, request_ids, items, stream: int = 0) -> np.nd
     _check(lib().gr_score_items_batch(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), ids.shape[0], _host(it),
                                       it.shape[1], _host(scores), stream))
     return scores
+
+
+def gr_score_items_labels(eng: int, request_ids, items, n_labels: int, stream: int = 0):
+    """Item log-likelihoods [n_requests][n] and label log-probabilities [n_requests][n][n_labels]
+    of items [n_requests][n][n_levels] (engines with a label head)."""
+    ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+    it = np.ascontiguousarray(items, dtype=np.int32)
+    scores = np.zeros((ids.shape[0], it.shape[1]), dtype=np.float32)
+    labels = np.zeros((ids.shape[0], it.shape[1], n_labels), dtype=np.float32)
+    _check(lib().gr_score_items_labels(eng, ids.ctypes.data_as(C.POINTER(C.c_int64)), ids.shape[0], _host(it),
+                                       it.shape[1], _host(scores), _host(labels), stream))
+    return scores, labels
 
 
 def gr_request_release(eng: int, rid: int):

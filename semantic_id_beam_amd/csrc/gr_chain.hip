@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
           const bool is_v = ncol0 >= g.n2;
           uint16_t *kv = (uint16_t *)(slot + (is_v ? dev.sl.beamkv_v : dev.sl.beamkv_k));
           const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
-          uint16_t *dst = kv + (size_t)g.layer * (dm.levels - 1) * lvstride + (size_t)(s - 1) * lvstride +
+          uint16_t *dst = kv + (size_t)g.layer * dm.tl * lvstride + (size_t)(s - 1) * lvstride +
                           (size_t)j * wstride + (ncol0 - (is_v ? g.n2 : g.n1));
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)

@@ -46,6 +46,7 @@ struct gr_engine {
   gr_model_desc model{};
   gr_engine_opts opts{};
   gr_chain_desc chain{};  // the layer-chain model (dm.chain), copied at create
+  gr_label_desc label{};  // the label head (dm.n_labels > 0), copied at create
   int elem = 2;
 
   // trie, host copy: levels 0..n_levels-1 hold masks and first-child indices
@@ -57,6 +58,7 @@ struct gr_engine {
   // workspace layout (byte offsets)
   size_t off_mask = 0, off_child = 0, off_slots = 0, off_pool = 0, off_work = 0, off_out = 0, ws_need = 0;
   size_t off_chain = 0, chain_bytes = 0;  // the layer chain's activation rows
+  size_t off_label = 0;                   // label-step log-probs [max_requests][W_max][n_labels] f32
   size_t off_chain_dbg = 0, chain_dbg_layer = 0;  // debug copies of them, per layer
   int chain_rows = 0;                     // rows of those buffers (a multiple of 128)
   size_t work_bytes = 0;  // one ring entry
@@ -239,7 +241,7 @@ void layout(gr_engine *e) {
     o = align_up(o + bytes, A);
     return r;
   };
-  const size_t kv = (size_t)d.L * (d.levels - 1) * W * d.Hkv * d.d * el;
+  const size_t kv = (size_t)d.L * d.tl * W * d.Hkv * d.d * el;
   s.beamkv_k = take(kv);
   s.beamkv_v = take(kv);
   s.q_last = take(std::max((size_t)d.L * d.Hq * d.d * el, (size_t)d.Hq * d.d * 4));  // chain: x_last [D] f32
@@ -285,6 +287,10 @@ void layout(gr_engine *e) {
   e->out_bytes = align_up(16 + W * d.levels * 4 + W * 4, A);
   e->off_out = w;
   w = align_up(w + e->out_bytes * (size_t)e->opts.max_requests, A);
+  if (d.n_labels > 0) {
+    e->off_label = w;
+    w = align_up(w + (size_t)e->opts.max_requests * W * d.n_labels * 4, A);
+  }
   if (d.chain) {
     // every request's beams packed at 32-row boundaries, padded to 128: x f32 [D], xn bf16 [D],
     // q and o bf16 [Hq d], act bf16 [I]
@@ -396,8 +402,13 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
     if ((m->n_levels > 1 && !c->embed) || !c->w_q || !c->w_k || !c->w_v || !c->w_o || !c->w_gate || !c->w_up ||
         !c->w_down || !c->g_attn || !c->g_mlp || !c->g_final)
       return fail(GR_E_INVALID_ARG, "a layer-chain weight is null");
-  } else if (m->n_levels > 1 && (!m->tok_q || !m->tok_k || !m->tok_v)) {
+  } else if ((m->n_levels > 1 || m->label) && (!m->tok_q || !m->tok_k || !m->tok_v)) {
     return fail(GR_E_INVALID_ARG, "token tables are null");
+  }
+  if (m->label) {
+    if (m->chain) return fail(GR_E_UNSUPPORTED, "a label head needs the table model, not a layer chain");
+    if (m->label->n_labels < 1 || m->label->n_labels > 16) return fail(GR_E_UNSUPPORTED, "n_labels must be in [1, 16]");
+    if (!m->label->w_label) return fail(GR_E_INVALID_ARG, "w_label is null");
   }
   if (items->n_items < 1 || !items->codes) return fail(GR_E_INVALID_ARG, "empty item set");
   if (o->max_requests < 1 || o->max_requests > 65536) return fail(GR_E_INVALID_ARG, "max_requests must be in [1, 65536]");
@@ -412,7 +423,9 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   e->model = *m;
   e->opts = *o;
   if (m->chain) e->chain = *m->chain;
-  e->model.chain = nullptr;  // the description is copied: the caller's may go away
+  if (m->label) e->label = *m->label;
+  e->model.chain = nullptr;  // the descriptions are copied: the caller's may go away
+  e->model.label = nullptr;
   if (e->opts.max_splits == 0) e->opts.max_splits = 4;
   e->elem = m->dtype == GR_DTYPE_BF16 ? 2 : 4;
   gr::Dims &d = e->dm;
@@ -431,6 +444,8 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   d.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
   d.debug_attn = (o->flags & GR_ENGINE_DEBUG_ATTN) ? 1 : 0;
   d.chain = m->chain ? 1 : 0;
+  d.n_labels = m->label ? m->label->n_labels : 0;
+  d.tl = d.levels - 1 + (d.n_labels > 0 ? 1 : 0);
   gr_status st = build_trie(e, items);
   if (st != GR_OK) {
     delete e;
@@ -504,6 +519,8 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
   dv.tok_k = e->model.tok_k;
   dv.tok_v = e->model.tok_v;
   dv.w_sid = e->model.w_sid;
+  dv.w_label = e->dm.n_labels > 0 ? e->label.w_label : nullptr;
+  dv.label_out = e->dm.n_labels > 0 ? (float *)(e->ws + e->off_label) : nullptr;
   if (e->dm.chain) {
     gr::ChainDev &c = dv.ch;
     const gr_chain_desc &cd = e->chain;
@@ -866,7 +883,12 @@ gr_status gr_request_reset(gr_engine *e, int64_t rid, void *stream) {
   return gr_request_reset_batch(e, &rid, 1, stream);
 }
 
-gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream) {
+namespace {
+// One decode step (label_order == nullptr), or the label step of gr_score_items_labels: every
+// listed request at level n_levels, its beams' last codes run as tokens and the label head
+// instead of logits and selection; *label_order receives the request index of each descriptor
+// (the row order of the label output).
+gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, std::vector<int> *label_order) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (e->poisoned) return fail(GR_E_DEVICE, "engine poisoned by an earlier device error");
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
@@ -880,7 +902,8 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       if (!seen.insert(ids[i]).second) return fail(GR_E_INVALID_ARG, "duplicate request id in one step");
       auto it = e->reqs.find(ids[i]);
       if (it == e->reqs.end()) return fail(GR_E_NOT_FOUND, "unknown request id");
-      if (it->second.level >= d.levels) return fail(GR_E_BAD_STATE, "request already decoded every level");
+      if (label_order ? it->second.level != d.levels : it->second.level >= d.levels)
+        return fail(GR_E_BAD_STATE, label_order ? "the label step follows the last level" : "request already decoded every level");
       rs[(size_t)i] = &it->second;
     }
   }
@@ -1243,6 +1266,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
       prof_record(e, GR_PROF_BEAM_MERGE, plevel, pm);
     }
   }
+  if (label_order) {
+    if ((r = check_dev(e, gr::launch_label_head(e->dev, dw, n, wg_merge, st), "label head")) != GR_OK) return r;
+    label_order->assign(order.begin(), order.end());
+    return GR_OK;
+  }
   const auto pl = prof_pair(e, pon);
   if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st, prof_ev(e, pl.first, pl.second)),
                      "logits")) != GR_OK)
@@ -1266,6 +1294,11 @@ gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream
     R->level = s + 1;
   }
   return GR_OK;
+}
+}  // namespace
+
+gr_status gr_beam_step(gr_engine *e, const int64_t *ids, int32_t n, void *stream) {
+  return step_impl(e, ids, n, stream, nullptr);
 }
 
 namespace {
@@ -1405,6 +1438,28 @@ gr_status gr_score_items_batch(gr_engine *e, const int64_t *ids, int32_t n_req, 
 
 gr_status gr_score_items(gr_engine *e, int64_t rid, const int32_t *items, int32_t n, float *scores, void *stream) {
   return gr_score_items_batch(e, &rid, 1, items, n, scores, stream);
+}
+
+gr_status gr_score_items_labels(gr_engine *e, const int64_t *ids, int32_t n_req, const int32_t *items, int32_t n,
+                                float *scores, float *label_logp, void *stream) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (e->dm.n_labels < 1) return fail(GR_E_BAD_STATE, "the engine has no label head");
+  if (!label_logp) return fail(GR_E_INVALID_ARG, "null label_logp");
+  gr_status r = gr_score_items_batch(e, ids, n_req, items, n, scores, stream);  // validates, synchronises
+  if (r != GR_OK) return r;
+  std::vector<int> order;
+  if ((r = step_impl(e, ids, n_req, stream, &order)) != GR_OK) return r;
+  const int nl = e->dm.n_labels, W = e->dm.W_max;
+  std::vector<float> out((size_t)n_req * W * nl);
+  hipStream_t st = (hipStream_t)stream;
+  if ((r = check_dev(e, hipMemcpyAsync(out.data(), e->ws + e->off_label, out.size() * 4, hipMemcpyDeviceToHost, st),
+                     "label copy")) != GR_OK)
+    return r;
+  if ((r = check_dev(e, hipStreamSynchronize(st), "sync")) != GR_OK) return r;
+  for (int i = 0; i < n_req; ++i)  // descriptor i holds request order[i]
+    std::memcpy(label_logp + (size_t)order[(size_t)i] * n * nl, out.data() + (size_t)i * W * nl,
+                (size_t)n * nl * sizeof(float));
+  return GR_OK;
 }
 
 gr_status gr_debug_beam_state(gr_engine *e, int64_t rid, int32_t cap, int32_t *parent, int32_t *codes,

@@ -25,12 +25,15 @@ struct Dims {
   float scale_log2;  // log2(e) / sqrt(d)
   int debug_attn;
   int chain;         // 1: the layer-chain model (q of a step from the q rows, outputs to the o rows)
+  int tl;            // token-table and BeamKV levels: levels - 1, or levels with a label head (the
+                     // last level's codes are then tokens too, read by the label step s = levels)
+  int n_labels;      // label head outputs (0: none)
 };
 
 // Byte offsets of the arrays inside one request slot; slots are slot_bytes apart.
 struct SlotLayout {
   size_t slot_bytes;
-  size_t beamkv_k, beamkv_v;  // [L][levels-1][W_max][Hkv][d] elem
+  size_t beamkv_k, beamkv_v;  // [L][tl][W_max][Hkv][d] elem
   size_t q_last;              // [L][Hq][d] elem
   size_t knmax;               // [L][Hkv] f32: largest context-key norm (bounds the scores)
   size_t vscale;              // [L][Hkv] f32: power of two above the context's largest |v| (taken at load)
@@ -72,8 +75,10 @@ struct Dev {
   const uint32_t *trie_mask;       // concatenated levels: [nodes_t][MW]
   const int32_t *trie_child;       // concatenated levels: [nodes_t]
   int64_t trie_off[kMaxLevels + 1];  // node offset of level t
-  const void *tok_q, *tok_k, *tok_v;
+  const void *tok_q, *tok_k, *tok_v;  // [L][tl][V][H][d]
   const float *w_sid;
+  const float *w_label;  // [Hq*d][n_labels] f32 (label head), or null
+  float *label_out;      // [max_requests][W_max][n_labels] f32: a label step's log-probs
   ChainDev ch;
 };
 
@@ -195,6 +200,11 @@ hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32
 // norm into each request's hidden rows.
 hipError_t launch_chain_start(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
                               LaunchEv ev = {});
+// The label head after a label step (s = levels): per live beam row of each request, the
+// log-softmax over n_labels of h . w_label, to label_out[i][j][c] (i = the request's index in
+// reqs).  One workgroup per (request, beam); total_wgs = the sum of the requests' n_bound.
+hipError_t launch_label_head(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
+                             LaunchEv ev = {});
 hipError_t launch_chain_norm(const Dev &dev, const float *g, int rows, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, int kind, int layer,
                              hipStream_t st, LaunchEv ev = {});

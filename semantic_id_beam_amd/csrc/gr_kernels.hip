@@ -237,7 +237,7 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
         const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
         const int code = codes[j * dm.levels + (s - 1)];
         qsrc = (const uint16_t *)dev.tok_q +
-               ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
+               ((((size_t)layer * dm.tl + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
       }
     }
 #pragma unroll
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
     else if (row_ok)
       qsrc = s == 0 ? qsrc + (size_t)hq_row * D
                     : (const uint16_t *)dev.tok_q +
-                          ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
+                          ((((size_t)layer * dm.tl + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
     u32x4_t qr[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
@@ -800,8 +800,8 @@ __device__ __forceinline__ void tail_load_pair(const Dev &dev, uint8_t *slot, in
   const int lvl = dm.levels;
   const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
   const size_t lvstride = (size_t)dm.W_max * wstride;
-  const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
-  const size_t tbase = (size_t)layer * (lvl - 1) * dm.V * dm.Hkv + kv;  // token-table row, level 0, code 0
+  const size_t lbase = (size_t)layer * dm.tl * lvstride + (size_t)kv * D;
+  const size_t tbase = (size_t)layer * dm.tl * dm.V * dm.Hkv + kv;  // token-table row, level 0, code 0
 #pragma unroll
   for (int e = 0; e < NTOK; ++e) {
     const int t = t0 + e;
@@ -839,7 +839,7 @@ __device__ __forceinline__ void tail_merge_pair(const Dev &dev, uint8_t *slot, i
   uint16_t *bv = (uint16_t *)(slot + dev.sl.beamkv_v);
   const size_t wstride = (size_t)dm.Hkv * D;
   const size_t lvstride = (size_t)dm.W_max * wstride;
-  const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
+  const size_t lbase = (size_t)layer * dm.tl * lvstride + (size_t)kv * D;
 #pragma unroll
   for (int e = 0; e < NTOK; ++e) {
     const int t = t0 + e;
@@ -1171,7 +1171,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     else if (row_ok)
       qsrc = s == 0 ? qsrc + (size_t)hq_row * D
                     : (const uint16_t *)dev.tok_q +
-                          ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
+                          ((((size_t)layer * dm.tl + (s - 1)) * dm.V + bi.code) * dm.Hq + hq_row) * D;
     u32x4_t qr[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
@@ -1291,7 +1291,7 @@ __global__ __launch_bounds__(256) void k_ctx_attn_f32(Dev dev, const StepReq *__
     q = (const float *)(slot + dev.sl.q_last) + ((size_t)layer * dm.Hq + hq) * D;
   } else {
     const int code = ((const int *)(slot + dev.sl.codes[s & 1]))[j * dm.levels + (s - 1)];
-    q = (const float *)dev.tok_q + ((((size_t)layer * (dm.levels - 1) + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
+    q = (const float *)dev.tok_q + ((((size_t)layer * dm.tl + (s - 1)) * dm.V + code) * dm.Hq + hq) * D;
   }
   const float *gK = (const float *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const float *gV = (const float *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
@@ -1388,7 +1388,7 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
     const int *codes = (const int *)(slot + dev.sl.codes[s & 1]);
     const int *anc = (const int *)(slot + dev.sl.anc[s & 1]);
     const int code = codes[j * lvl + (s - 1)];
-    const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code;
+    const size_t trow = ((size_t)layer * dm.tl + (s - 1)) * dm.V + code;
     float q[8];
     {
       Raw8<T> rq;
@@ -1402,7 +1402,7 @@ __device__ __forceinline__ void merge_elem(const Dev &dev, const StepReq &R, uin
     T *bv = (T *)(slot + dev.sl.beamkv_v);
     const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
     const size_t lvstride = (size_t)dm.W_max * wstride;
-    const size_t base = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D + c8 * 8;
+    const size_t base = (size_t)layer * dm.tl * lvstride + (size_t)kv * D + c8 * 8;
     if (gi == 0) {
       kn.store(bk + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
       vn.store(bv + base + (size_t)(s - 1) * lvstride + (size_t)j * wstride);
@@ -1500,7 +1500,7 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
   float *hb = (float *)(slot + dev.sl.h);
   const size_t wstride = (size_t)dm.Hkv * D;  // one BeamKV slot
   const size_t lvstride = (size_t)dm.W_max * wstride;
-  const size_t lbase = (size_t)layer * (lvl - 1) * lvstride + (size_t)kv * D;
+  const size_t lbase = (size_t)layer * dm.tl * lvstride + (size_t)kv * D;
   for (int e0 = tid; e0 < total; e0 += E * nthreads) {
     int j[E], gi[E], c8[E], code[E];
     bool ok[E];
@@ -1561,7 +1561,7 @@ __device__ __forceinline__ void finish_rows(const Dev &dev, const StepReq &R, ui
           vn[k].load(bv + own);
           continue;
         }
-        const size_t trow = ((size_t)layer * (lvl - 1) + (s - 1)) * dm.V + code[k];
+        const size_t trow = ((size_t)layer * dm.tl + (s - 1)) * dm.V + code[k];
         rq[k].load((const uint16_t *)dev.tok_q + (trow * dm.Hq + kv * g + gi[k]) * D + c8[k] * 8);
         kn[k].load((const uint16_t *)dev.tok_k + (trow * dm.Hkv + kv) * D + c8[k] * 8);
         vn[k].load((const uint16_t *)dev.tok_v + (trow * dm.Hkv + kv) * D + c8[k] * 8);
@@ -1822,6 +1822,55 @@ __global__ __launch_bounds__(256) void k_sum_hparts(Dev dev, const StepReq *__re
     gst<f32x4_t>(hb + 2 * e + 1, a1);
   }
 }
+
+// Label head ([TRT] "Background" and "Scoring many candidates at once": given candidates are
+// ranked by the log-probabilities of label tokens read after each candidate).  After a label
+// step (s = levels: each candidate's last code run as a token), beam j of request i has the
+// hidden vector h_j; z_c = h_j . w_label[:, c] in float32 and label_out[i][j][c] = z_c -
+// logsumexp(z).  One workgroup per (request, beam), workgroups numbered as the merge launch's.
+constexpr int kMaxLabels = 16;
+__global__ __launch_bounds__(256) void k_label_head(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  const int ri = find_req<1>(reqs, n_reqs, blockIdx.x);
+  const StepReq R = reqs[ri];
+  const Dims &dm = dev.dm;
+  const int j = (int)blockIdx.x - R.wg_merge;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[R.level & 1];
+  if (j >= n_live) return;
+  const int D = dm.Hq * dm.d, nl = dm.n_labels;
+  const float *h = (const float *)(slot + dev.sl.h) + (size_t)j * D;
+  float acc[kMaxLabels];
+#pragma unroll
+  for (int c = 0; c < kMaxLabels; ++c) acc[c] = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const float hv = h[i];
+    const float *w = dev.w_label + (size_t)i * nl;
+#pragma unroll
+    for (int c = 0; c < kMaxLabels; ++c)
+      if (c < nl) acc[c] = fmaf(hv, w[c], acc[c]);
+  }
+  __shared__ float red[kMaxLabels][4];
+#pragma unroll
+  for (int c = 0; c < kMaxLabels; ++c) {
+    if (c >= nl) break;
+    const float v = wave_sum(acc[c]);
+    if ((threadIdx.x & 63) == 0) red[c][threadIdx.x >> 6] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float z[kMaxLabels], m = kNegInf;
+    for (int c = 0; c < nl; ++c) {
+      z[c] = (red[c][0] + red[c][1]) + (red[c][2] + red[c][3]);
+      m = fmaxf(m, z[c]);
+    }
+    float se = 0.f;
+    for (int c = 0; c < nl; ++c) se += expf(z[c] - m);
+    const float lse = m + logf(se);
+    float *out = dev.label_out + ((size_t)ri * dm.W_max + j) * nl;
+    for (int c = 0; c < nl; ++c) out[c] = z[c] - lse;
+  }
+}
+
 
 // --------------------------------------------------------------------------------------
 // logits_part[ks][j][c] = sum over the ks-th quarter of the hidden dim of h[j][k] w_sid[level][k][c]
@@ -2607,6 +2656,15 @@ hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int to
                          LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
   launch(k_logits, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
+  return hipGetLastError();
+}
+
+hipError_t launch_label_head(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
+                             LaunchEv ev) {
+  if (total_wgs <= 0) return hipSuccess;
+  if (dev.dm.n_labels < 1 || dev.dm.n_labels > kMaxLabels || !dev.w_label || !dev.label_out)
+    return hipErrorInvalidValue;
+  launch(k_label_head, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 

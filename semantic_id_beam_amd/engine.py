@@ -33,13 +33,15 @@ class BeamEngine:
     device tensors; items is a [n_items][n_levels] integer array.  chain: the layer-chain model's
     weights, a dict (embed, wq, wk, wv, wo, wg, wu, wd as bf16 [..][out][in], g_attn, g_mlp,
     g_final float32; numpy or torch device tensors) with "intermediate" and "eps"; the token
-    tables are then unused (None)."""
+    tables are then unused (None).  w_label: the label head [Hq*d][n_labels] float32 (numpy or a
+    torch device tensor); the token tables then hold n_levels levels, the last one for a
+    candidate's last code."""
 
     def __init__(self, *, tok_q, tok_k, tok_v, w_sid, items, n_layers: int, n_q_heads: int, n_kv_heads: int,
                  head_dim: int, dtype: str = "bf16", norm: str = "valid", max_requests: int = 1,
                  max_beam_width: int = 256, max_ctx_tokens: int = 0, max_splits: int = 0,
                  debug_attn: bool = False, max_layers_per_launch: int = 0, per_layer: bool = False,
-                 chain=None, device="cuda"):
+                 chain=None, w_label=None, device="cuda"):
         torch = _torch()
         self.device = device
         self.dtype = dtype
@@ -55,6 +57,10 @@ class BeamEngine:
                                          *(c[k].data_ptr() for k in ("embed", "wq", "wk", "wv", "wo", "wg", "wu",
                                                                      "wd", "g_attn", "g_mlp", "g_final")))
         ptr = lambda t: t.data_ptr() if t is not None else None
+        self.w_label, label_desc = None, None
+        if w_label is not None:
+            self.w_label = w_label if isinstance(w_label, torch.Tensor) else conv(np.asarray(w_label, dtype=np.float32))
+            label_desc = G.gr_label_desc(int(self.w_label.shape[1]), self.w_label.data_ptr())
         self.w_sid = conv(np.asarray(w_sid, dtype=np.float32)) if not isinstance(w_sid, torch.Tensor) else w_sid
         self.n_layers, self.n_levels, self.V = int(n_layers), int(self.w_sid.shape[0]), int(self.w_sid.shape[2])
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
@@ -62,7 +68,8 @@ class BeamEngine:
                                G.GR_DTYPE_BF16 if dtype == "bf16" else G.GR_DTYPE_F32,
                                G.GR_NORM_VALID if norm == "valid" else G.GR_NORM_FULL,
                                ptr(self.tok_q), ptr(self.tok_k), ptr(self.tok_v), self.w_sid.data_ptr(),
-                               C.pointer(chain_desc) if chain_desc is not None else None)
+                               C.pointer(chain_desc) if chain_desc is not None else None,
+                               C.pointer(label_desc) if label_desc is not None else None)
         opts = G.gr_engine_opts(max_requests, max_beam_width, max_ctx_tokens, max_splits,
                                 (G.GR_ENGINE_DEBUG_ATTN if debug_attn else 0) |
                                 (G.GR_ENGINE_PER_LAYER if per_layer else 0), max_layers_per_launch)
@@ -165,6 +172,11 @@ class BeamEngine:
     def score_items_batch(self, rids, items):
         """[len(rids)][n] log-probabilities; items [len(rids)][n][n_levels]."""
         return G.gr_score_items_batch(self.eng, rids, items, self.stream)
+
+    def score_items_labels(self, rids, items):
+        """Item log-likelihoods [len(rids)][n] and label log-probabilities [len(rids)][n][n_labels]
+        of items [len(rids)][n][n_levels] (an engine with a label head)."""
+        return G.gr_score_items_labels(self.eng, rids, items, int(self.w_label.shape[1]), self.stream)
 
     def reset(self, rid: int):
         G.gr_request_reset(self.eng, rid, self.stream)

@@ -26,6 +26,7 @@ GR_STUB(launch_sum_hparts, const Dev &, const StepReq *, int, hipStream_t, Launc
 GR_STUB(launch_finish_first_level, const Dev &, const StepReq *, int, hipStream_t, LaunchEv)
 GR_STUB(launch_logits, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_lsm, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
+GR_STUB(launch_label_head, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_topk, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_init_slots, const Dev &, const int32_t *, int, hipStream_t)
 GR_STUB(launch_gather_results, const Dev &, const int32_t *, int, int, uint8_t *, size_t, hipStream_t)

@@ -208,3 +208,55 @@ def test_result_records_unpack_and_async_checks():
     ids = np.zeros(1, np.int64)
     assert L.gr_beams_get_batch_async(None, ids.ctypes.data_as(C.POINTER(C.c_int64)), 1, buf.ctypes.data,
                                       None) == G.GR_E_INVALID_ARG
+
+
+def _label_desc(n_labels=2, w=FAKE, chain=None):
+    import ctypes as C
+    lab = G.gr_label_desc(n_labels, w)
+    d = _desc()
+    d.label = C.pointer(lab)
+    if chain is not None:
+        d.chain = C.pointer(chain)
+    return d, lab
+
+
+def test_label_head_grows_beamkv_and_adds_its_output():
+    """A label head adds one level to BeamKV (the last code's key and value) and the label output
+    rows; the engine keeps its own copy of the description."""
+    plain = G.gr_engine_create(_desc(), _items(), _opts(R=2, W=8))
+    d, lab = _label_desc(n_labels=5)
+    labelled = G.gr_engine_create(d, _items(), _opts(R=2, W=8))
+    wp, wl = G.gr_engine_workspace_bytes(plain), G.gr_engine_workspace_bytes(labelled)
+    # per slot: K and V of one more level, L * W * Hkv * d * 4 bytes each (f32 model)
+    assert wl - wp >= 2 * (2 * 1 * 8 * 2 * 64 * 4) + 2 * 8 * 5 * 4
+    G.gr_engine_destroy(plain)
+    G.gr_engine_destroy(labelled)
+
+
+@pytest.mark.parametrize("n_labels,w,status", [(0, FAKE, "GR_E_UNSUPPORTED"), (17, FAKE, "GR_E_UNSUPPORTED"),
+                                               (2, None, "GR_E_INVALID_ARG")])
+def test_label_head_limits(n_labels, w, status):
+    d, lab = _label_desc(n_labels=n_labels, w=w)
+    with pytest.raises(G.GrError, match=status):
+        G.gr_engine_create(d, _items(), _opts())
+
+
+def test_label_head_is_not_for_the_layer_chain():
+    chain = G.gr_chain_desc(64, 1e-6, *([FAKE] * 11))
+    d, lab = _label_desc(chain=chain)
+    d.dtype = G.GR_DTYPE_BF16
+    d.n_q_heads, d.n_kv_heads, d.head_dim = 2, 1, 128
+    with pytest.raises(G.GrError, match="GR_E_UNSUPPORTED"):
+        G.gr_engine_create(d, _items(), _opts())
+
+
+def test_label_scoring_needs_a_bound_engine_with_a_label_head():
+    eng = G.gr_engine_create(_desc(), _items(), _opts())
+    with pytest.raises(G.GrError, match="GR_E_BAD_STATE"):
+        G.gr_score_items_labels(eng, [1], np.zeros((1, 2, 3), np.int32), 2)
+    G.gr_engine_destroy(eng)
+    d, lab = _label_desc()
+    eng = G.gr_engine_create(d, _items(), _opts())
+    with pytest.raises(G.GrError, match="GR_E_BAD_STATE"):
+        G.gr_score_items_labels(eng, [1], np.zeros((1, 2, 3), np.int32), 2)
+    G.gr_engine_destroy(eng)
