@@ -251,7 +251,7 @@ def workload_leg(name: str, reps: int = 3, per_layer: bool = True):
 
 
 def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 4000, 5000, 6000),
-                n_req: int = 1000, max_active: int = 64, seed: int = 0, per_layer: bool = True):
+                n_req: int = 1000, max_active: int = 64, seed: int = 0, per_layer: bool = True, graph: bool = False):
     """Latency against offered load through the continuous-batching scheduler (gr_sched_*):
     Poisson arrivals at each offered rate, n_req requests per rate, at most max_active decoding
     at once, the way the paper-daily TensorRT-LLM summary reads its beam-search chart
@@ -275,7 +275,7 @@ def serving_leg(name: str = "ctx2k_beam30_r64", rates=(500, 1000, 2000, 3000, 40
         kn, vn, _ = native_layout(k, v)
         del k, v
         tens.append((kn, vn, q))
-    eng = make_engine(cfg, max_requests=max_active + 2, max_ctx_tokens=0, per_layer=per_layer)
+    eng = make_engine(cfg, max_requests=max_active + 2, max_ctx_tokens=0, per_layer=per_layer, graph=graph)
     torch.cuda.synchronize()
     points, base = [], 0
     for lam in rates:
@@ -440,6 +440,51 @@ def cpu_baseline(cfg, n_beams: int):
                    f"({dt:.1f} s); extrapolated to {evals} beam evaluations per request decode"),
         "seconds": dt,
     }
+
+
+def graph_leg(cfg, args):
+    """The headline decode (one launch per layer) launched directly and as replayed graphs
+    (GR_ENGINE_GRAPH): the same engine options, no profiling, contexts resident, each decode
+    (every level of every request, beam sets fetched) timed by HIP events on the stream."""
+    import torch
+
+    import synth
+    from semantic_id_beam_amd import _lib as G
+    from semantic_id_beam_amd.workloads import make_engine, request_tensors
+    shapes = synth.request_shapes(cfg)
+    R, lv = cfg.n_requests, cfg.n_levels
+    out = {}
+    for graph in (False, True):
+        eng = make_engine(cfg, max_requests=R, per_layer=True, graph=graph)
+        for r in range(R):
+            k, v, q = request_tensors(cfg, r)
+            eng.load(r, k, v, q, shapes[r][1])
+            del k, v, q
+        rids = list(range(R))
+
+        def decode():
+            eng.reset_batch(rids)
+            for _ in range(lv):
+                eng.step(rids)
+            eng.beams_batch(rids)
+
+        for _ in range(max(1, args.warmup)):
+            decode()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            decode()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        key = "graph" if graph else "direct"
+        out[key] = {"ms_per_decode": round(ms, 3), "req_per_s": round(R / (ms * 1e-3), 1)}
+        if graph:
+            out[key]["captures"], out[key]["replays"] = G.gr_engine_graph_stats(eng.eng)
+        eng.close()
+    log(f"graph replay: direct {out['direct']['req_per_s']} req/s, graphs {out['graph']['req_per_s']} req/s")
+    return out
 
 
 def decode_leg(cfg, args, per_layer: bool):
@@ -618,6 +663,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the headline decode (one layer per launch): no other legs")
     ap.add_argument("--chain-only", action="store_true", help="only the layer-chain leg (prints its JSON)")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="only the headline decode launched directly and as replayed graphs (prints its JSON)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -646,6 +693,9 @@ def main():
         print(json.dumps({"chain": chain_leg(args)}), flush=True)
         return
     cfg = synth.get_config(args.config or HEADLINE)
+    if args.graph_only:
+        print(json.dumps({"graph_replay": graph_leg(cfg, args)}), flush=True)
+        return
     shapes = synth.request_shapes(cfg)
     R, lv = cfg.n_requests, cfg.n_levels
     log("workload", workload_text(cfg, shapes))
@@ -684,6 +734,7 @@ def main():
                      "a group of layers): valid only because this model stand-in's layers are independent; "
                      "not the headline"),
             **{k: fused[k] for k in ("value", "ms_per_step", "step_us", "decode_ms", "roofline", "kernels")}}
+        out["graph_replay"] = graph_leg(cfg, args)
         out["chain"] = chain_leg(args)
         out["scoring"] = scoring_leg(cfg, args)
         out["prefill"] = prefill_leg(cfg, args)
@@ -692,6 +743,7 @@ def main():
             out["workloads_fused_layers_variant"] = {w: workload_leg(w, per_layer=False)["req_per_s"]
                                                      for w in ("ctx2k_beam30_r64", "ragged_r128")}
             out["serving"] = serving_leg()
+            out["serving_graph"] = serving_leg(graph=True)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_beams} beams ...")
         cb = cpu_baseline(cfg, args.cpu_beams)

@@ -159,6 +159,15 @@ typedef struct {
  * this flag the engine may run several layers in one launch where every layer's query is an
  * input (the model stand-in above). */
 #define GR_ENGINE_PER_LAYER 2u
+/* Graph replay of decode steps ([GR] section "语义ID生成式推荐专用推理框架": the runtime replays
+ * captured graphs over views of the KV pool): gr_beam_step captures the launch sequence of each
+ * step shape (the request count and the per-request parameters that set every launch) once, on
+ * an engine-owned stream, as a HIP graph, and replays it for every later step of that shape; the
+ * step's descriptors are uploaded to one fixed device area before each replay.  A new shape costs
+ * a capture and an instantiation (host time and a little device memory; up to 64 shapes are kept,
+ * the oldest dropped first).  Steps with profiling enabled, debug engines and the label step are
+ * launched directly.  Results are the same as without the flag, bit for bit. */
+#define GR_ENGINE_GRAPH 4u
 
 typedef struct {
   int32_t max_requests;   /* requests loaded at once (slots), >= 1 */
@@ -168,7 +177,7 @@ typedef struct {
                              0 = only GR_LOAD_ADOPT loads */
   int32_t max_splits;     /* split-K partial slots per (request, kv head) at full beam width
                              (narrower steps may use proportionally more); 0 = 4 */
-  uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN | GR_ENGINE_PER_LAYER */
+  uint32_t flags;         /* GR_ENGINE_DEBUG_ATTN | GR_ENGINE_PER_LAYER | GR_ENGINE_GRAPH */
   int32_t max_layers_per_launch; /* full-context steps: at most this many layers per
                              context-attention launch; 0 = automatic (about seven rounds of
                              workgroups per launch, layers split evenly over the launches);
@@ -511,6 +520,10 @@ gr_status gr_engine_profile_dispatches(gr_engine *eng, int32_t kind, int32_t lev
 
 /* Clears every bucket (pending events are folded first). */
 gr_status gr_engine_profile_reset(gr_engine *eng);
+
+/* Graph replay counters of a GR_ENGINE_GRAPH engine: steps that captured a new graph and steps
+ * that replayed a kept one. */
+gr_status gr_engine_graph_stats(const gr_engine *eng, int64_t *captures, int64_t *replays);
 
 /* ---- inspection (tests and debugging; each synchronises `stream`) --------- */
 

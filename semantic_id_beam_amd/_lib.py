@@ -21,6 +21,7 @@ GR_DTYPE_F32, GR_DTYPE_BF16 = 0, 1
 GR_NORM_VALID, GR_NORM_FULL = 0, 1
 GR_ENGINE_DEBUG_ATTN = 1
 GR_ENGINE_PER_LAYER = 2
+GR_ENGINE_GRAPH = 4
 GR_LOAD_ADOPT = 1
 
 STATUS_NAMES = {0: "GR_OK", 1: "GR_E_INVALID_ARG", 2: "GR_E_OUT_OF_MEMORY", 3: "GR_E_BAD_STATE",
@@ -37,6 +38,7 @@ EXPORTS = [
     "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
     "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
     "gr_sched_completed", "gr_sched_result", "gr_sched_counts", "gr_debug_chain_rows", "gr_score_items_labels",
+    "gr_engine_graph_stats",
 ]
 GR_CHAIN_X_IN, GR_CHAIN_XN_ATTN, GR_CHAIN_Q, GR_CHAIN_O, GR_CHAIN_X_MID, GR_CHAIN_XN_MLP, GR_CHAIN_ACT, \
     GR_CHAIN_X_OUT = range(8)
@@ -138,6 +140,7 @@ def lib() -> C.CDLL:
         "gr_score_items_batch": (i32, [vp, vp, i32, vp, i32, vp, vp]),
         "gr_score_items_labels": (i32, [vp, vp, i32, vp, i32, vp, vp, vp]),
         "gr_engine_profile_reset": (i32, [vp]),
+        "gr_engine_graph_stats": (i32, [vp, vp, vp]),
         "gr_sched_create": (i32, [vp, i32, vp, P(vp)]),
         "gr_sched_destroy": (i32, [vp]),
         "gr_sched_submit": (i32, [vp, i64, i32, i32, vp, vp, vp, u32]),
@@ -380,6 +383,13 @@ def gr_engine_profile_dispatches(eng: int, kind: int, level: int = -1) -> int:
     n = C.c_int64()
     _check(lib().gr_engine_profile_dispatches(eng, kind, level, C.byref(n)))
     return n.value
+
+
+def gr_engine_graph_stats(eng: int):
+    """(captures, replays) of a graph-replay engine."""
+    a, b = C.c_int64(0), C.c_int64(0)
+    _check(lib().gr_engine_graph_stats(eng, C.byref(a), C.byref(b)))
+    return a.value, b.value
 
 
 def gr_engine_profile_reset(eng: int):

@@ -102,6 +102,15 @@ struct gr_engine {
   // into the caller's stream (default priority, created when the workspace is bound)
   hipStream_t aux[kAuxStreams] = {};
   hipEvent_t fork_ev = nullptr, join_ev[kAuxStreams] = {};
+  // graph replay (GR_ENGINE_GRAPH): one executable graph per step shape (the launch sequence's
+  // every parameter), captured on cap_st; the descriptors of graph steps go to one fixed
+  // device area (gdesc), and gdone_ev marks the last graph launch's end for the next upload
+  hipStream_t cap_st = nullptr;
+  hipEvent_t gdone_ev = nullptr;
+  bool gdone_used = false;
+  std::map<std::vector<int64_t>, hipGraphExec_t> graphs;
+  std::deque<std::vector<int64_t>> graph_fifo;
+  int64_t graph_hits = 0, graph_captures = 0;
   std::vector<gr::StepReq *> pinned;
   std::vector<hipEvent_t> events;
   std::vector<bool> event_used;
@@ -282,7 +291,7 @@ void layout(gr_engine *e) {
   w = align_up(w + (size_t)e->pool_tokens * e->pool_tok_bytes, A);
   e->work_bytes = align_up(sizeof(gr::StepReq) * (size_t)e->opts.max_requests, A);
   e->off_work = w;
-  w = align_up(w + e->work_bytes * kRing, A);
+  w = align_up(w + e->work_bytes * (kRing + 1), A);  // the ring, then the graph steps' area
   // result staging: per request n_live (16-byte header), codes [W][levels], scores [W]
   e->out_bytes = align_up(16 + W * d.levels * 4 + W * 4, A);
   e->off_out = w;
@@ -417,7 +426,8 @@ gr_status gr_engine_create(const gr_model_desc *m, const gr_item_set *items, con
   if (o->max_ctx_tokens < 0) return fail(GR_E_INVALID_ARG, "max_ctx_tokens < 0");
   if (o->max_splits < 0 || o->max_splits > 64) return fail(GR_E_INVALID_ARG, "max_splits must be in [0, 64]");
   if (o->max_layers_per_launch < 0) return fail(GR_E_INVALID_ARG, "max_layers_per_launch must be >= 0");
-  if (o->flags & ~(GR_ENGINE_DEBUG_ATTN | GR_ENGINE_PER_LAYER)) return fail(GR_E_INVALID_ARG, "unknown engine flag");
+  if (o->flags & ~(GR_ENGINE_DEBUG_ATTN | GR_ENGINE_PER_LAYER | GR_ENGINE_GRAPH))
+    return fail(GR_E_INVALID_ARG, "unknown engine flag");
 
   gr_engine *e = new gr_engine();
   e->model = *m;
@@ -507,6 +517,12 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
   }
   if ((r = check_dev(e, hipEventCreateWithFlags(&e->fork_ev, hipEventDisableTiming), "event create")) != GR_OK)
     return r;
+  if (e->opts.flags & GR_ENGINE_GRAPH) {
+    if ((r = check_dev(e, hipStreamCreateWithFlags(&e->cap_st, hipStreamNonBlocking), "stream create")) != GR_OK)
+      return r;
+    if ((r = check_dev(e, hipEventCreateWithFlags(&e->gdone_ev, hipEventDisableTiming), "event create")) != GR_OK)
+      return r;
+  }
   if ((r = check_dev(e, gr::prefill_scratch(&e->noalloc_scratch), "scratch address")) != GR_OK) return r;
   gr::Dev &dv = e->dev;
   dv.dm = e->dm;
@@ -566,6 +582,9 @@ gr_status gr_engine_destroy(gr_engine *e) {
       if (e->join_ev[i]) (void)hipEventDestroy(e->join_ev[i]);
     }
     if (e->fork_ev) (void)hipEventDestroy(e->fork_ev);
+    for (auto &kv : e->graphs) (void)hipGraphExecDestroy(kv.second);
+    if (e->cap_st) (void)hipStreamDestroy(e->cap_st);
+    if (e->gdone_ev) (void)hipEventDestroy(e->gdone_ev);
     for (auto *p : e->pinned)
       if (p) (void)hipHostFree(p);
     if (e->out_host) (void)hipHostFree(e->out_host);
@@ -1051,12 +1070,30 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     }
     G.wgs = wg_ctx;
   }
-  gr::StepReq *dw = (gr::StepReq *)(e->ws + e->off_work + e->work_bytes * (size_t)slot_i);
+  const bool graph = (e->opts.flags & GR_ENGINE_GRAPH) && !e->prof && !d.debug_attn && !label_order;
+  gr::StepReq *dw = (gr::StepReq *)(e->ws + e->off_work + e->work_bytes * (size_t)(graph ? kRing : slot_i));
+  if (graph && e->gdone_used &&
+      (r = check_dev(e, hipStreamWaitEvent(st, e->gdone_ev, 0), "graph order")) != GR_OK)
+    return r;
   if ((r = check_dev(e, hipMemcpyAsync(dw, hw, sizeof(gr::StepReq) * (size_t)n, hipMemcpyHostToDevice, st),
                      "descriptor upload")) != GR_OK)
     return r;
   if ((r = check_dev(e, hipEventRecord(e->events[slot_i], st), "descriptor ring")) != GR_OK) return r;
   e->event_used[slot_i] = true;
+  // graph replay: the step's shape (every value the launch sequence below depends on)
+  std::vector<int64_t> key;
+  hipGraphExec_t exec = nullptr;
+  if (graph) {
+    key = {n, first_fused, layered, per_layer, defer, any_hparts, d.chain, wg_merge, wg_fin, wg_logits, wg_lsm,
+           max_cand, row_acc, (int64_t)groups.size()};
+    for (const Group &G : groups)
+      key.insert(key.end(), {G.kind, G.start, G.count, G.wgs, G.lgroups, G.merge0, G.merge_wgs, G.fin0, G.fin_wgs});
+    auto it = e->graphs.find(key);
+    if (it != e->graphs.end()) exec = it->second;
+  }
+  // the launch sequence, enqueued on `st` (the caller's stream, or the capture stream)
+  auto enqueue = [&](hipStream_t st) -> gr_status {
+  gr_status r;
   int plevel = rs[0]->level;
   for (auto *R : rs)
     if (R->level != plevel) plevel = d.levels;
@@ -1283,6 +1320,45 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     return r;
   prof_record(e, GR_PROF_TOPK, plevel, pt);
   prof_record(e, GR_PROF_STEP, plevel, {step_start, pt.second});
+  return GR_OK;
+  };
+  if (!graph) {
+    if ((r = enqueue(st)) != GR_OK || label_order) return r;
+  } else {
+    if (!exec) {
+      // capture this shape once on the engine's own stream, then keep its executable graph
+      if ((r = check_dev(e, hipStreamBeginCapture(e->cap_st, hipStreamCaptureModeThreadLocal), "graph capture")) !=
+          GR_OK)
+        return r;
+      const gr_status q = enqueue(e->cap_st);
+      hipGraph_t g = nullptr;
+      const hipError_t ce = hipStreamEndCapture(e->cap_st, &g);
+      if (q != GR_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return q;
+      }
+      if ((r = check_dev(e, ce, "graph capture")) != GR_OK) return r;
+      const hipError_t ie = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(g);
+      if ((r = check_dev(e, ie, "graph instantiate")) != GR_OK) return r;
+      if (e->graph_fifo.size() >= 64) {
+        auto old = e->graphs.find(e->graph_fifo.front());
+        if (old != e->graphs.end()) {
+          (void)hipGraphExecDestroy(old->second);
+          e->graphs.erase(old);
+        }
+        e->graph_fifo.pop_front();
+      }
+      e->graphs[key] = exec;
+      e->graph_fifo.push_back(key);
+      ++e->graph_captures;
+    } else {
+      ++e->graph_hits;
+    }
+    if ((r = check_dev(e, hipGraphLaunch(exec, st), "graph launch")) != GR_OK) return r;
+    if ((r = check_dev(e, hipEventRecord(e->gdone_ev, st), "graph order")) != GR_OK) return r;
+    e->gdone_used = true;
+  }
   for (int i = 0; i < n; ++i)  // descriptor i belongs to request order[i]
     rs[(size_t)order[(size_t)i]]->last_row0 = hw[i].row0;
   for (auto *R : rs) {
@@ -1631,6 +1707,13 @@ gr_status gr_engine_profile_dispatches(gr_engine *e, int32_t kind, int32_t level
   for (int l = 0; l <= e->dm.levels; ++l)
     if (level < 0 || l == level) n += e->prof_d[kind][l];
   *dispatches = n;
+  return GR_OK;
+}
+
+gr_status gr_engine_graph_stats(const gr_engine *e, int64_t *captures, int64_t *replays) {
+  if (!e || !captures || !replays) return fail(GR_E_INVALID_ARG, "null argument");
+  *captures = e->graph_captures;
+  *replays = e->graph_hits;
   return GR_OK;
 }
 

@@ -41,7 +41,7 @@ class BeamEngine:
                  head_dim: int, dtype: str = "bf16", norm: str = "valid", max_requests: int = 1,
                  max_beam_width: int = 256, max_ctx_tokens: int = 0, max_splits: int = 0,
                  debug_attn: bool = False, max_layers_per_launch: int = 0, per_layer: bool = False,
-                 chain=None, w_label=None, device="cuda"):
+                 chain=None, w_label=None, graph=False, device="cuda"):
         torch = _torch()
         self.device = device
         self.dtype = dtype
@@ -72,7 +72,8 @@ class BeamEngine:
                                C.pointer(label_desc) if label_desc is not None else None)
         opts = G.gr_engine_opts(max_requests, max_beam_width, max_ctx_tokens, max_splits,
                                 (G.GR_ENGINE_DEBUG_ATTN if debug_attn else 0) |
-                                (G.GR_ENGINE_PER_LAYER if per_layer else 0), max_layers_per_launch)
+                                (G.GR_ENGINE_PER_LAYER if per_layer else 0) | (G.GR_ENGINE_GRAPH if graph else 0),
+                                max_layers_per_launch)
         self.max_beam_width = max_beam_width
         self.eng = G.gr_engine_create(desc, np.asarray(items), opts)
         self.ws_bytes = G.gr_engine_workspace_bytes(self.eng)

@@ -10,7 +10,7 @@ import numpy as np
 
 
 def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm="valid", max_ctx_tokens=None,
-                max_beam_width=None, max_layers_per_launch=0, per_layer=False, n_labels=0):
+                max_beam_width=None, max_layers_per_launch=0, per_layer=False, n_labels=0, graph=False):
     """An engine for a synthetic workload; n_labels > 0 adds a label head (and the label level of
     the token tables) for candidate scoring by label tokens."""
     import synth
@@ -35,7 +35,7 @@ def make_engine(cfg, *, max_requests=None, max_splits=0, debug_attn=False, norm=
                       head_dim=cfg.head_dim, dtype=cfg.dtype, norm=norm, max_requests=R,
                       max_beam_width=W, max_ctx_tokens=max_ctx_tokens, max_splits=max_splits,
                       debug_attn=debug_attn, max_layers_per_launch=max_layers_per_launch, per_layer=per_layer,
-                      chain=chain, w_label=synth.w_label(cfg, n_labels) if n_labels > 0 else None)
+                      chain=chain, w_label=synth.w_label(cfg, n_labels) if n_labels > 0 else None, graph=graph)
 
 
 def chain_weights(cfg, device="cuda", eps: float = 1e-6) -> dict:

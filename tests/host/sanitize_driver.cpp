@@ -169,9 +169,9 @@ int main() {
     bo.max_layers_per_launch = -1;
     EXPECT(gr_engine_create(&m, &is, &bo, &e) != GR_OK && e == nullptr);
     bo = opts(1, 4, 64);
-    bo.flags = 4u;  // not an engine flag
+    bo.flags = 8u;  // not an engine flag
     EXPECT(gr_engine_create(&m, &is, &bo, &e) == GR_E_INVALID_ARG && e == nullptr);
-    bo.flags = GR_ENGINE_PER_LAYER | GR_ENGINE_DEBUG_ATTN;
+    bo.flags = GR_ENGINE_PER_LAYER | GR_ENGINE_DEBUG_ATTN | GR_ENGINE_GRAPH;
     EXPECT(gr_engine_create(&m, &is, &bo, &e) == GR_OK && e != nullptr);
     EXPECT(gr_engine_destroy(e) == GR_OK);
     e = nullptr;
