@@ -506,6 +506,9 @@ typedef enum {
  * Buckets are keyed by kind and by the decode level of the step (0..n_levels-1;
  * steps whose requests are at different levels go to bucket n_levels). */
 gr_status gr_engine_set_profiling(gr_engine *eng, int32_t enable);
+/* As gr_engine_set_profiling, for the kinds whose bit (1u << GR_PROF_*) is set in `kinds` only (0:
+ * off): a timed run can carry events on the launches it reports and none on the others. */
+gr_status gr_engine_set_profiling_kinds(gr_engine *eng, uint32_t kinds);
 
 /* Waits for every recorded event, folds the elapsed times into the buckets and
  * returns one bucket: total milliseconds and number of launches, where a launch that

@@ -88,6 +88,7 @@ struct gr_engine {
   // profiling: timing events carried by the launches themselves (no marker packets between
   // kernels), folded into [kind][level] buckets.  A record spans two events of the pool.
   bool prof = false;
+  uint32_t prof_mask = ~0u;  // the kinds (bit 1 << GR_PROF_*) profiled while prof is on
   std::vector<hipEvent_t> prof_ev;
   int prof_next = 0;  // next unused event of the pool
   struct ProfRec { int kind, level, a, b, count, disp; };  // count: layer steps, disp: kernel dispatches
@@ -1098,16 +1099,17 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
   for (auto *R : rs)
     if (R->level != plevel) plevel = d.levels;
   const bool pon = prof_reserve(e, 2 * ((d.chain ? 8 : 2) * d.L + 4));
+  auto pk = [&](int kind) { return pon && ((e->prof_mask >> kind) & 1u) != 0; };  // this kind is timed
   int step_start = -1;
   if (first_fused) {
-    const auto pc = prof_pair(e, pon);
+    const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
     step_start = pc.first;
     if ((r = check_dev(e, gr::launch_ctx_attn_first_level(e->dev, dw, n, groups[0].wgs, st,
                                                           prof_ev(e, pc.first, pc.second)),
                        "context attention")) != GR_OK)
       return r;
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L);
-    const auto pm = prof_pair(e, pon);
+    const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
     if ((r = check_dev(e, gr::launch_finish_first_level(e->dev, dw, n, st, prof_ev(e, pm.first, pm.second)),
                        "first-level finish")) != GR_OK)
       return r;
@@ -1145,7 +1147,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     return ev >= 0 ? check_dev(e, hipEventRecord(e->prof_ev[(size_t)ev], st), "profiling event") : GR_OK;
   };
   if (layered) {
-    const auto pc = prof_pair(e, pon);
+    const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
     step_start = pc.first;
     if (nstreams > 1 && ((r = marker(pc.first)) != GR_OK || (r = fork()) != GR_OK)) return r;
     int disp = 0;
@@ -1163,7 +1165,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     if (nstreams > 1 && ((r = join()) != GR_OK || (r = marker(pc.second)) != GR_OK)) return r;
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, disp);
     if (any_hparts) {
-      const auto pm = prof_pair(e, pon);
+      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
       if ((r = check_dev(e, gr::launch_sum_hparts(e->dev, dw, n, st, prof_ev(e, pm.first, pm.second)),
                          "layer-group sum")) != GR_OK)
         return r;
@@ -1176,7 +1178,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
   // holds the merges too
   const bool multi = !first_fused && !layered && nstreams > 1;
   if (multi) {
-    const auto pc = prof_pair(e, pon);
+    const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
     step_start = pc.first;
     if ((r = marker(pc.first)) != GR_OK || (r = fork()) != GR_OK) return r;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
@@ -1194,7 +1196,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     if ((r = join()) != GR_OK || (r = marker(pc.second)) != GR_OK) return r;
     prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, d.L, d.L * (int)groups.size());
     if (defer) {
-      const auto pm = prof_pair(e, pon);
+      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
       if ((r = check_dev(e, finish(0, n, d.L - 1, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
                          "beam attention/merge")) != GR_OK)
         return r;
@@ -1209,7 +1211,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     const int rows = (int)align_up((size_t)row_acc, 128);
     if (rows > e->chain_rows) return fail(GR_E_BAD_STATE, "step rows exceed the chain buffers");  // cannot happen
     auto rec = [&](int kind, std::pair<int, int> ab) { prof_record(e, kind, plevel, ab); };
-    auto pn = prof_pair(e, pon);
+    auto pn = prof_pair(e, pk(GR_PROF_NORM));
     step_start = pn.first;
     if ((r = check_dev(e, gr::launch_chain_start(e->dev, dw, n, rows, st, prof_ev(e, pn.first, pn.second)),
                        "chain start")) != GR_OK)
@@ -1218,14 +1220,14 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     const size_t D = (size_t)d.Hq * d.d;
     for (int l = 0; l < d.L; ++l) {
       auto gemm = [&](int kind) -> gr_status {
-        const auto pg = prof_pair(e, pon);
+        const auto pg = prof_pair(e, pk(GR_PROF_GEMM));
         gr_status q = check_dev(e, gr::launch_chain_gemm(e->dev, dw, n, rows, kind, l, st, prof_ev(e, pg.first, pg.second)),
                                 "chain projection");
         if (q == GR_OK) rec(GR_PROF_GEMM, pg);
         return q;
       };
       auto norm = [&](const float *g) -> gr_status {
-        const auto pq = prof_pair(e, pon);
+        const auto pq = prof_pair(e, pk(GR_PROF_NORM));
         gr_status q = check_dev(e, gr::launch_chain_norm(e->dev, g, rows, st, prof_ev(e, pq.first, pq.second)),
                                 "chain norm");
         if (q == GR_OK) rec(GR_PROF_NORM, pq);
@@ -1251,7 +1253,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       if ((r = snap(GR_CHAIN_X_IN)) != GR_OK || (r = snap(GR_CHAIN_XN_ATTN)) != GR_OK) return r;
       if ((r = gemm(gr::kChainQKV)) != GR_OK) return r;
       if ((r = snap(GR_CHAIN_Q)) != GR_OK) return r;
-      const auto pc = prof_pair(e, pon);
+      const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
       for (size_t gi = 0; gi < groups.size(); ++gi) {
         const Group &G = groups[gi];
         const gr::LaunchEv ev = prof_ev(e, gi == 0 ? pc.first : -1, gi + 1 == groups.size() ? pc.second : -1);
@@ -1260,7 +1262,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
           return r;
       }
       prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, 1, (int)groups.size());
-      const auto pm = prof_pair(e, pon);
+      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
       if ((r = check_dev(e, finish(0, n, l, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
                          "layer finish")) != GR_OK)
         return r;
@@ -1276,14 +1278,14 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       if ((r = snap(GR_CHAIN_X_OUT)) != GR_OK) return r;
       if (l + 1 < d.L && (r = norm(e->chain.g_attn + (size_t)(l + 1) * D)) != GR_OK) return r;
     }
-    pn = prof_pair(e, pon);
+    pn = prof_pair(e, pk(GR_PROF_NORM));
     if ((r = check_dev(e, gr::launch_chain_final(e->dev, dw, n, rows, st, prof_ev(e, pn.first, pn.second)),
                        "chain final norm")) != GR_OK)
       return r;
     rec(GR_PROF_NORM, pn);
   }
   for (int l = 0; l < (first_fused || layered || multi || d.chain ? 0 : d.L); ++l) {
-    const auto pc = prof_pair(e, pon);
+    const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
     if (l == 0) step_start = pc.first;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group &G = groups[gi];
@@ -1296,7 +1298,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     // float32 (and one layer per launch): finish every layer separately; otherwise layer l is
     // finished inside layer l+1's context kernel, and the last layer here
     if (!defer || l == d.L - 1) {
-      const auto pm = prof_pair(e, pon);
+      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
       if ((r = check_dev(e, finish(0, n, l, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
                          "beam attention/merge")) != GR_OK)
         return r;
@@ -1308,18 +1310,18 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     label_order->assign(order.begin(), order.end());
     return GR_OK;
   }
-  const auto pl = prof_pair(e, pon);
+  const auto pl = prof_pair(e, pk(GR_PROF_LOGITS));
   if ((r = check_dev(e, gr::launch_logits(e->dev, dw, n, wg_logits, st, prof_ev(e, pl.first, pl.second)),
                      "logits")) != GR_OK)
     return r;
   prof_record(e, GR_PROF_LOGITS, plevel, pl);
-  const auto pt = prof_pair(e, pon);
+  const auto pt = prof_pair(e, pk(GR_PROF_TOPK));
   if ((r = check_dev(e, gr::launch_lsm(e->dev, dw, n, wg_lsm, st, prof_ev(e, pt.first, -1)), "log-softmax")) != GR_OK)
     return r;
   if ((r = check_dev(e, gr::launch_topk(e->dev, dw, n, max_cand, st, prof_ev(e, -1, pt.second)), "top-k")) != GR_OK)
     return r;
   prof_record(e, GR_PROF_TOPK, plevel, pt);
-  prof_record(e, GR_PROF_STEP, plevel, {step_start, pt.second});
+  if (step_start >= 0 && pt.second >= 0 && pk(GR_PROF_STEP)) prof_record(e, GR_PROF_STEP, plevel, {step_start, pt.second});
   return GR_OK;
   };
   if (!graph) {
@@ -1676,6 +1678,15 @@ gr_status gr_engine_set_profiling(gr_engine *e, int32_t enable) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
   e->prof = enable != 0;
+  e->prof_mask = ~0u;
+  return GR_OK;
+}
+
+gr_status gr_engine_set_profiling_kinds(gr_engine *e, uint32_t kinds) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
+  e->prof = kinds != 0;
+  e->prof_mask = kinds;
   return GR_OK;
 }
 
