@@ -925,8 +925,9 @@ __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &
 // The wide context kernel: 8 waves x 32 query rows (256 rows of one kv head) against K and V^T
 // tiles of 64 tokens that go from HBM straight into LDS through a ring of five stages.  Each
 // V^T tile is rewritten in place, once it has landed, as float16 of v / vscale, where vscale =
-// 2^e is the power of two above the head's largest |v| (taken at load); a bf16 value converts
-// exactly while |v| >= 2^-14 vscale, and below that to within 2^-25 vscale.  P is then a single
+// 2^e is the power of two above the head's largest |v| (taken at load; 1 when that lies in
+// [2^-10, 2^15], where float16 of v itself is as good); a bf16 value converts exactly while
+// |v| >= 2^-14 vscale, and below that to within 2^-25 vscale.  P is then a single
 // float16 term (relative rounding 2^-11) and PV one f16 MFMA per 16 tokens.  The softmax keeps
 // a running maximum with a lazy rescale: only when a row's maximum grows by more than 8 in log2
 // units, so every p stays within (0, 2^8].  A tile is converted while its predecessor is in
@@ -989,7 +990,12 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   if (layer >= dm.L) return;  // past the last layer of the last launch
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
-  const float vs = ((const float *)(slot + dev.sl.vscale))[layer * dm.Hkv + h];
+  // with the head's values between 2^-11 and 2^15 in magnitude (vscale = 2^e above max|v| in
+  // [2^-10, 2^15]) float16 of v itself is exact for |v| >= 2^-14 and within 2^-25 below, so the
+  // scaling is skipped; otherwise V is taken in units of vscale
+  const float vsc = ((const float *)(slot + dev.sl.vscale))[layer * dm.Hkv + h];
+  const bool vraw = vsc >= 0x1p-10f && vsc <= 0x1p15f;
+  const float vs = vraw ? 1.f : vsc;
   const float ivs = 1.f / vs;  // exact: vs is a power of two
 
   // per-lane DMA sources (elements from the tile's first token) for this wave's chunks
@@ -1022,9 +1028,14 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     for (int i = 0; i < VCH / NT; ++i) {
       const u32x4_t x = sv[i * NT + tid];
       u32x4_t y;
+      if (vraw) {  // uniform over the workgroup
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        y[e] = pack_f16(__uint_as_float(x[e] << 16) * ivs, __uint_as_float(x[e] & 0xFFFF0000u) * ivs);
+        for (int e = 0; e < 4; ++e) y[e] = pack_f16(__uint_as_float(x[e] << 16), __uint_as_float(x[e] & 0xFFFF0000u));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[e] = pack_f16(__uint_as_float(x[e] << 16) * ivs, __uint_as_float(x[e] & 0xFFFF0000u) * ivs);
+      }
       sv[i * NT + tid] = y;
     }
   };
@@ -1041,11 +1052,12 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[(kb * 2 + hh) ^ kx], qf[kb], acc, 0, 0, 0);
     return acc;
   };
-  // lazy rescale before the sub-tile whose row maxima (x log2 e / sqrt(d)) are mxs
+  // lazy rescale before the sub-tile whose lane maxima of the scores are mx: a row's maximum
+  // (x log2 e / sqrt(d)) outgrows M + 8 exactly when one of its two lanes' does, so the lanes
+  // exchange their maxima only on that (rare) path
   auto rescale = [&](float mx) {
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * c2;
-    if (__ballot(mxs > M + 8.f) != 0ull) {  // uniform over the wave
+    if (__ballot(mx * c2 > M + 8.f) != 0ull) {  // uniform over the wave
+      const float mxs = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
       const float Mn = fmaxf(M, mxs);
       const float f = fast_exp2(M - Mn);  // 0 before the first sub-tile (M = -inf)
       l *= f;
@@ -1186,8 +1198,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     // the beam's own tokens (the first sets (M, l, o)), then o in units of vscale like the
     // context's contributions
     wide_tail_merge<D>(dev, slot, layer, h, s, row_ok, j_row, gi_row, bi, hh, c2, true, qf, M, l, oacc, true);
+    if (!vraw) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= ivs;
+      for (int db = 0; db < DB; ++db) oacc[db] *= ivs;
+    }
   } else {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
@@ -1250,8 +1264,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   }
 
   // back to units of v
+  if (!vraw) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] *= vs;
+    for (int db = 0; db < DB; ++db) oacc[db] *= vs;
+  }
   const float ltot = l + __shfl_xor(l, 32);
   if constexpr (!LAYERED) {
     if (wave_active && row_ok) {
