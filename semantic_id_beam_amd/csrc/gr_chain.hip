@@ -191,7 +191,17 @@ struct GemmArgs {
   int layer;            // EPI_QKV: BeamKV layer
   float *x;             // EPI_RESID: residual [rows][N] float32
   uint16_t *out;        // EPI_QKV: q rows [rows][n1]; EPI_SWIGLU: act [rows][N / 2]
+  int ksplit;           // > 1: K in ksplit ranges, raw sums of the live rows to part[ks][row][col]
+  float *part;          //   (SwiGLU columns in logical order: gate i at i, up i at N/2 + i)
 };
+
+// a packed row's request and whether the row is a live beam of it
+__device__ __forceinline__ bool row_live(const Dev &dev, const StepReq *reqs, int n_reqs, int row) {
+  const StepReq &R = reqs[find_row_req(reqs, n_reqs, row)];
+  const int j = row - R.row0;
+  const int n_live = ((const int *)(slot_of(dev, R.slot) + dev.sl.n_live))[R.level & 1];
+  return row >= R.row0 && j < n_live && j < R.n_bound;
+}
 
 // source row of weight-tile row r (tile columns n0 ..); SwiGLU tiles alternate 32 gate rows and
 // the matching 32 up rows
@@ -232,17 +242,19 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
   // evenly, XCD x takes weight tiles x, x+8, ... and runs every row tile of each, so a weight tile
   // is fetched into one XCD's L2 only (the smaller activation rows are what each XCD re-reads)
   const int n_tiles = g.N / BN;
+  // split-K: range ks of K, the tile index the rest (ranges outermost)
+  const int tile = (int)blockIdx.x % (m_tiles * n_tiles), ks = (int)blockIdx.x / (m_tiles * n_tiles);
   int mt, nt;
   if ((n_tiles & 7) == 0) {
-    const int xcd = (int)blockIdx.x & 7, idx = (int)blockIdx.x >> 3;
+    const int xcd = tile & 7, idx = tile >> 3;
     mt = idx % m_tiles;
     nt = (idx / m_tiles) * 8 + xcd;
   } else {
-    mt = (int)blockIdx.x % m_tiles;
-    nt = (int)blockIdx.x / m_tiles;
+    mt = tile % m_tiles;
+    nt = tile / m_tiles;
   }
   const int m0 = mt * GBM, n0 = nt * BN;
-  const int KT = g.K / GBK;
+  const int KT = g.K / GBK / g.ksplit, k0 = ks * KT * GBK;
 
   // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane: row p >> 3, stored
   // position p & 7 <- global chunk (p & 7) ^ swz(row); the 8 rows of one instruction lie in one
@@ -251,12 +263,12 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
-    asrc[i] = g.A + (size_t)(m0 + r) * g.K + c * 8;
+    asrc[i] = g.A + (size_t)(m0 + r) * g.K + k0 + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
-    wsrc[i] = w_row<EPI>(g, n0, r) + c * 8;
+    wsrc[i] = w_row<EPI>(g, n0, r) + k0 + c * 8;
   }
   const uint32_t adst = lds_addr(&sA[0][0]) + w * 1024, wdst = lds_addr(&sW[0][0]) + w * 1024;
   auto issue = [&](int kt) {
@@ -308,6 +320,25 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
   // ---- epilogue: lane (rl, hh) of block (nb, mb) holds row m0 + wm*64 + mb*32 + rl, columns
   // n0 + wn*WN + nb*32 + 8a + 4hh + c, c = 0..3, in acc[nb][mb][4a + c]
   const int ncol0 = n0 + wn * WN;
+  if (g.ksplit > 1) {
+    // raw sums of the live rows to this range's partials; k_gemm_reduce adds the ranges
+    float *part = g.part + (size_t)ks * m_tiles * GBM * g.N;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = m0 + wm * 64 + mb * 32 + rl;
+      if (!row_live(dev, reqs, n_reqs, row)) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        int col = ncol0 + nb * 32;
+        if constexpr (EPI == EPI_SWIGLU) col = (nb & 1 ? g.N / 2 : 0) + ncol0 / 2 + (nb >> 1) * 32;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          gst<f32x4_t>(part + (size_t)row * g.N + col + 8 * a + 4 * hh,
+                       f32x4_t{acc[nb][mb][4 * a], acc[nb][mb][4 * a + 1], acc[nb][mb][4 * a + 2], acc[nb][mb][4 * a + 3]});
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int row = m0 + wm * 64 + mb * 32 + rl;
@@ -371,6 +402,63 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
                            u32x2_t{pack_bf16(acc[nb][mb][4 * a], acc[nb][mb][4 * a + 1]),
                                    pack_bf16(acc[nb][mb][4 * a + 2], acc[nb][mb][4 * a + 3])});
         }
+      }
+    }
+  }
+}
+
+// The split-K ranges of one row added in range order, then the projection's epilogue (as in
+// k_gemm): one workgroup per packed row (dead rows return at once), four columns per thread and
+// iteration.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_reduce(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                     GemmArgs g, int rows) {
+  const int row = blockIdx.x;
+  const StepReq R = reqs[find_row_req(reqs, n_reqs, row)];
+  uint8_t *slot = slot_of(dev, R.slot);
+  const int s = R.level, j = row - R.row0;
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  if (!(row >= R.row0 && j < n_live && j < R.n_bound)) return;
+  const size_t rstride = (size_t)rows * g.N;
+  const float *p = g.part + (size_t)row * g.N;
+  auto sum4 = [&](int col) {
+    f32x4_t acc = gld<f32x4_t>(p + col);
+    for (int k = 1; k < g.ksplit; ++k) {
+      const f32x4_t v = gld<f32x4_t>(p + k * rstride + col);
+      acc = f32x4_t{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+    }
+    return acc;
+  };
+  if constexpr (EPI == EPI_RESID) {
+    for (int col = 4 * (int)threadIdx.x; col < g.N; col += 4 * 256) {
+      const f32x4_t a = sum4(col);
+      float *xp = g.x + (size_t)row * g.N + col;
+      const f32x4_t o = gld<f32x4_t>(xp);
+      gst<f32x4_t>(xp, f32x4_t{o[0] + a[0], o[1] + a[1], o[2] + a[2], o[3] + a[3]});
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int I = g.N / 2;
+    for (int i = 4 * (int)threadIdx.x; i < I; i += 4 * 256) {
+      const f32x4_t gt = sum4(i), up = sum4(I + i);
+      float v[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = gt[c] / (1.f + expf(-gt[c])) * up[c];
+      gst<u32x2_t>(g.out + (size_t)row * I + i, u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+    }
+  } else {
+    const Dims &dm = dev.dm;
+    const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
+    for (int col = 4 * (int)threadIdx.x; col < g.N; col += 4 * 256) {
+      const f32x4_t a = sum4(col);
+      const u32x2_t b = u32x2_t{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
+      if (col < g.n1) {
+        gst<u32x2_t>(g.out + (size_t)row * g.n1 + col, b);
+      } else if (s > 0) {
+        const bool is_v = col >= g.n2;
+        uint16_t *kv = (uint16_t *)(slot + (is_v ? dev.sl.beamkv_v : dev.sl.beamkv_k));
+        gst<u32x2_t>(kv + (size_t)g.layer * dm.tl * lvstride + (size_t)(s - 1) * lvstride + (size_t)j * wstride +
+                         (col - (is_v ? g.n2 : g.n1)),
+                     b);
       }
     }
   }
@@ -458,15 +546,32 @@ hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, in
   const bool wide = g.N % 256 == 0 && (epi != EPI_QKV || (g.n1 % 256 == 0 && (g.n2 - g.n1) % 256 == 0)) &&
                     (long)m_tiles * (g.N / 256) >= 256;
   if (!wide && g.N % 128 != 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(m_tiles * (g.N / (wide ? 256 : 128))));
+  const int tiles = m_tiles * (g.N / (wide ? 256 : 128));
+  // few rows (the first level: one beam per request): the tiles alone leave most compute units
+  // without a weight stream, so K is split into up to 8 ranges (at least 4 stages each) whose
+  // partial sums a second launch adds in order (deterministic) before the epilogue
+  g.ksplit = 1;
+  const int KT = g.K / GBK;
+  while (g.ksplit < 8 && tiles * g.ksplit < 256 && KT % (2 * g.ksplit) == 0 && KT / (2 * g.ksplit) >= 4 &&
+         (size_t)2 * g.ksplit * rows * g.N <= c.part_floats)
+    g.ksplit *= 2;
+  g.part = c.part;
+  const dim3 grid((unsigned)(tiles * g.ksplit));
+  const LaunchEv e1{ev.start, g.ksplit > 1 ? nullptr : ev.stop};
   auto go = [&](auto wn) {
     constexpr int WN = decltype(wn)::value;
-    if (epi == EPI_QKV) launch(k_gemm<EPI_QKV, WN>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
-    else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID, WN>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
-    else launch(k_gemm<EPI_SWIGLU, WN>, grid, dim3(256), st, ev, dev, reqs, n_reqs, g, m_tiles);
+    if (epi == EPI_QKV) launch(k_gemm<EPI_QKV, WN>, grid, dim3(256), st, e1, dev, reqs, n_reqs, g, m_tiles);
+    else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID, WN>, grid, dim3(256), st, e1, dev, reqs, n_reqs, g, m_tiles);
+    else launch(k_gemm<EPI_SWIGLU, WN>, grid, dim3(256), st, e1, dev, reqs, n_reqs, g, m_tiles);
   };
   if (wide) go(std::integral_constant<int, 128>{});
   else go(std::integral_constant<int, 64>{});
+  if (g.ksplit > 1) {
+    const LaunchEv e2{nullptr, ev.stop};
+    if (epi == EPI_QKV) launch(k_gemm_reduce<EPI_QKV>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
+    else if (epi == EPI_RESID) launch(k_gemm_reduce<EPI_RESID>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
+    else launch(k_gemm_reduce<EPI_SWIGLU>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
+  }
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ constexpr int kRing = 16;  // per-step descriptor buffers in flight
 }  // namespace
 
 constexpr int kAuxStreams = 3;
+constexpr size_t kChainPartFloats = size_t(8) << 20;  // split-K partials of the chain projections
 
 struct gr_engine {
   gr::Dims dm{};
@@ -308,7 +309,8 @@ void layout(gr_engine *e) {
     const size_t D = (size_t)d.Hq * d.d, I = (size_t)e->chain.intermediate;
     e->chain_rows = (int)rows;
     e->off_chain = w;
-    e->chain_bytes = align_up(rows * (D * 4 + D * 2 + 2 * D * 2 + I * 2), A);
+    // + the split-K partial sums of the few-row projections (32 MiB)
+    e->chain_bytes = align_up(rows * (D * 4 + D * 2 + 2 * D * 2 + I * 2), A) + kChainPartFloats * 4;
     w = align_up(w + e->chain_bytes, A);
     if (d.debug_attn) {
       // per layer, copies of the rows entering and leaving each projection (gr_debug_chain_rows)
@@ -562,6 +564,8 @@ gr_status gr_engine_bind_workspace(gr_engine *e, void *ws, size_t bytes, void *s
     c.q = c.xn + rows * D;
     c.o = c.q + rows * D;
     c.act = c.o + rows * D;
+    c.part = (float *)(b + align_up(rows * (D * 4 + D * 2 + 2 * D * 2 + I * 2), 256));
+    c.part_floats = kChainPartFloats;
     // padding rows are read by the projections: start every row at zero (finite)
     if ((r = check_dev(e, hipMemsetAsync(b, 0, e->chain_bytes, st), "chain rows")) != GR_OK) return r;
     if ((r = check_dev(e, hipStreamSynchronize(st), "chain rows")) != GR_OK) return r;

@@ -65,6 +65,8 @@ struct ChainDev {
   const float *g_attn, *g_mlp, *g_final;      // [L][D], [L][D], [D]
   float *x;                                   // residual rows [rows][D] float32
   uint16_t *xn, *q, *o, *act;                 // bf16 rows: [rows][D], [rows][Hq d] x2, [rows][I]
+  float *part;                                // split-K partial sums of a projection over few rows
+  size_t part_floats;                         // capacity of part
 };
 enum { kChainQKV = 0, kChainO = 1, kChainGateUp = 2, kChainDown = 3 };
 
