@@ -1187,12 +1187,21 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     u32x4_t qr[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
-    // the first four tiles, in flight with the query
+    // tiles 0 and 1, in flight with the query; once both have landed (with the query) tiles
+    // 2 and 3 go out: at the start of a launch every workgroup waits only for its first two
+    // tiles, not for the whole chip's first four
 #pragma unroll
-    for (int k = 0; k < NST - 1; ++k)
+    for (int k = 0; k < 2; ++k)
       if (k < ntiles) issue(k);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? qr[kb] : u32x4_t{0, 0, 0, 0});
+    for (int kb = 0; kb < KB; ++kb) {
+      qf[kb] = __builtin_bit_cast(bf16x8_t, row_ok ? qr[kb] : u32x4_t{0, 0, 0, 0});
+      asm volatile("" ::"v"(qf[kb]));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 2; k < NST - 1; ++k)
+      if (k < ntiles) issue(k);
   }
   if (LAYERED && s > 0) {
     // the beam's own tokens (the first sets (M, l, o)), then o in units of vscale like the
@@ -1212,9 +1221,13 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
     finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
   }
-  // the first tiles have landed (explicitly: the compiler does not count the copies); tiles 0
-  // and 1 are converted here, every later one in advance()
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // every wave's tiles 0 and 1 have landed (tiles 2 and 3 may be in flight; after prologue
+  // work with memory accesses of its own, everything is waited for, so that the ring's waits
+  // count copies only) and are converted here, every later one in advance()
+  if (LAYERED ? s > 0 : layer > 0 && R.defer_finish)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   convert_v(0);
   if (ntiles > 1) convert_v(1);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
