@@ -2092,18 +2092,10 @@ __device__ void block_sort_desc(uint64_t *a, int n) {
   __syncthreads();
 }
 
-__device__ void scan_cands(const float *__restrict__ cand, int total, SelectSmem &sm) {
+// Block reduction of the per-thread statistics of the finite (> -inf) candidates into
+// sm.nvalid / vmin / vmax.
+__device__ void reduce_stats(int cnt, float mn, float mx, SelectSmem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int cnt = 0;
-  float mn = __builtin_inff(), mx = kNegInf;
-  for (int i = tid; i < total; i += kTopkThreads) {
-    const float v = gld<float>(cand + i);
-    if (v > kNegInf) {
-      ++cnt;
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     cnt += __shfl_xor(cnt, o);
@@ -2131,38 +2123,71 @@ __device__ void scan_cands(const float *__restrict__ cand, int total, SelectSmem
   __syncthreads();
 }
 
-// Top-k of cand[0..total), total <= 1024*CPT (second pass; scan_cands ran first and
-// 1 <= k <= nvalid).  A monotone linear map of the score to 2048 bins is kept in
-// registers as packed 16-bit bin numbers; the histogram picks the bin holding the k-th
-// best, everything above it is selected, and the candidates of that bin are ordered
-// exactly by their 64-bit keys.  When the cut bin holds more than kTieCap candidates
-// the exact streaming radix select runs instead.  Leaves the k best keys, sorted
-// descending, in sm.sel[0..k).
+// Streaming statistics of cand[0..total): eight loads in flight per thread at a time.
+__device__ void scan_cands(const float *__restrict__ cand, int total, SelectSmem &sm) {
+  const int tid = threadIdx.x;
+  int cnt = 0;
+  float mn = __builtin_inff(), mx = kNegInf;
+  for (int base = 0; base < total; base += 8 * kTopkThreads) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + tid + u * kTopkThreads;
+      x[u] = i < total ? gld<float>(cand + i) : kNegInf;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (x[u] > kNegInf) {
+        ++cnt;
+        mn = fminf(mn, x[u]);
+        mx = fmaxf(mx, x[u]);
+      }
+  }
+  reduce_stats(cnt, mn, mx, sm);
+}
+
+// Candidates tid + 1024*m of cand[0..total) into v[m], -inf past the end: every
+// load is issued before the first is used (one round trip, not CPT), then their statistics.
 template <int CPT>
-__device__ void select_bins(const float *__restrict__ cand, int total, int k, SelectSmem &sm) {
+__device__ void load_cands(const float *__restrict__ cand, int total, float (&v)[CPT], SelectSmem &sm) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int i = tid + kTopkThreads * m;
+    const float x = total > 0 ? gld<float>(cand + min(i, total - 1)) : kNegInf;
+    v[m] = i < total ? x : kNegInf;
+  }
+  int cnt = 0;
+  float mn = __builtin_inff(), mx = kNegInf;
+#pragma unroll
+  for (int m = 0; m < CPT; ++m)
+    if (v[m] > kNegInf) {
+      ++cnt;
+      mn = fminf(mn, v[m]);
+      mx = fmaxf(mx, v[m]);
+    }
+  reduce_stats(cnt, mn, mx, sm);
+}
+
+// Top-k of the candidates that load_cands left in v (1 <= k <= nvalid).  A monotone linear
+// map of the score to 2048 bins; the histogram picks the bin holding the k-th best,
+// everything above it is selected, and the candidates of that bin are ordered exactly by
+// their 64-bit keys.  When the cut bin holds more than kTieCap candidates the exact
+// streaming radix select runs instead.  Leaves the k best keys, sorted descending, in
+// sm.sel[0..k).
+template <int CPT>
+__device__ void select_bins(const float *__restrict__ cand, int total, const float (&v)[CPT], int k,
+                            SelectSmem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float vmin = sm.vmin, span = sm.vmax - sm.vmin;
   float scale = (float)(kBins - 1) / span;
   if (!(scale > 0.f) || !(scale < 3.0e38f)) scale = 0.f;
+  auto bin = [&](float x) { return min(kBins - 1, (int)((x - vmin) * scale)); };
   for (int b = tid; b < kBins; b += kTopkThreads) sm.hist[b] = 0;
   __syncthreads();
-  uint32_t pb[CPT / 2];  // bin of candidate tid + 1024*m in half m%2 of pb[m/2]; 0xFFFF = invalid
 #pragma unroll
-  for (int m2 = 0; m2 < CPT / 2; ++m2) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int hsel = 0; hsel < 2; ++hsel) {
-      const int i = tid + kTopkThreads * (2 * m2 + hsel);
-      const float v = i < total ? gld<float>(cand + i) : kNegInf;
-      uint32_t b = 0xFFFFu;
-      if (v > kNegInf) {
-        b = (uint32_t)min(kBins - 1, (int)((v - vmin) * scale));
-        atomicAdd(&sm.hist[b], 1);
-      }
-      packed |= b << (16 * hsel);
-    }
-    pb[m2] = packed;
-  }
+  for (int m = 0; m < CPT; ++m)
+    if (v[m] > kNegInf) atomicAdd(&sm.hist[bin(v[m])], 1);
   __syncthreads();
   // suffix sums: thread t owns bins 2t and 2t+1
   const int h0 = sm.hist[2 * tid], h1 = sm.hist[2 * tid + 1];
@@ -2197,10 +2222,10 @@ __device__ void select_bins(const float *__restrict__ cand, int total, int k, Se
   }
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
-    const int b = (int)((pb[m >> 1] >> (16 * (m & 1))) & 0xFFFFu);
-    if (b != 0xFFFF && b >= cut) {
-      const int i = tid + kTopkThreads * m;
-      const uint64_t key = cand_key(gld<float>(cand + i), (uint32_t)i);
+    if (!(v[m] > kNegInf)) continue;
+    const int b = bin(v[m]);
+    if (b >= cut) {
+      const uint64_t key = cand_key(v[m], (uint32_t)(tid + kTopkThreads * m));
       if (b > cut)
         sm.sel[atomicAdd(&sm.cnt, 1)] = key;
       else
@@ -2225,11 +2250,19 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, int k
     const int shift = 56 - 8 * pass;
     for (int b = tid; b < 256; b += kTopkThreads) sm.hist[b] = 0;
     __syncthreads();
-    for (int i = tid; i < n_total; i += kTopkThreads) {
-      const float v = cand[i];
-      if (!(v > kNegInf)) continue;
-      const uint64_t key = cand_key(v, (uint32_t)i);
-      if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255], 1);
+    for (int base = 0; base < n_total; base += 8 * kTopkThreads) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + tid + u * kTopkThreads;
+        x[u] = i < n_total ? gld<float>(cand + i) : kNegInf;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!(x[u] > kNegInf)) continue;
+        const uint64_t key = cand_key(x[u], (uint32_t)(base + tid + u * kTopkThreads));
+        if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255], 1);
+      }
     }
     __syncthreads();
     if (tid == 0) {
@@ -2251,11 +2284,19 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, int k
   }
   if (tid == 0) sm.cnt = 0;
   __syncthreads();
-  for (int i = tid; i < n_total; i += kTopkThreads) {
-    const float v = cand[i];
-    if (!(v > kNegInf)) continue;
-    const uint64_t key = cand_key(v, (uint32_t)i);
-    if (key >= prefix) sm.sel[atomicAdd(&sm.cnt, 1)] = key;
+  for (int base = 0; base < n_total; base += 8 * kTopkThreads) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + tid + u * kTopkThreads;
+      x[u] = i < n_total ? gld<float>(cand + i) : kNegInf;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!(x[u] > kNegInf)) continue;
+      const uint64_t key = cand_key(x[u], (uint32_t)(base + tid + u * kTopkThreads));
+      if (key >= prefix) sm.sel[atomicAdd(&sm.cnt, 1)] = key;
+    }
   }
   __syncthreads();
   block_sort_desc(sm.sel, k);
@@ -2321,13 +2362,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_select(Dev dev, const StepReq 
   const int cur = s & 1, nxt = cur ^ 1;
   const int n = ((const int *)(slot + dev.sl.n_live))[cur];
   const float *cand = (const float *)(slot + dev.sl.cand);
-  scan_cands(cand, n * V, sm);
-  const int k = min(R.W, sm.nvalid);
-  if (k > 0) {
-    if constexpr (REGS)
-      select_bins<kSelectCPT>(cand, n * V, k, sm);
-    else
-      select_stream(cand, n * V, k, sm);
+  int k;
+  if constexpr (REGS) {
+    float v[kSelectCPT];
+    load_cands<kSelectCPT>(cand, n * V, v, sm);
+    k = min(R.W, sm.nvalid);
+    if (k > 0) select_bins<kSelectCPT>(cand, n * V, v, k, sm);
+  } else {
+    scan_cands(cand, n * V, sm);
+    k = min(R.W, sm.nvalid);
+    if (k > 0) select_stream(cand, n * V, k, sm);
   }
   __syncthreads();
   const int *node_cur = (const int *)(slot + dev.sl.node[cur]);
@@ -2369,13 +2413,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float *__res
   __shared__ SelectSmem sm;
   const int tid = threadIdx.x;
   const int n_total = n_rows * V;
-  scan_cands(cand, n_total, sm);
-  const int ke = min(k, sm.nvalid);
-  if (ke > 0) {
-    if constexpr (REGS)
-      select_bins<kSelectCPT>(cand, n_total, ke, sm);
-    else
-      select_stream(cand, n_total, ke, sm);
+  int ke;
+  if constexpr (REGS) {
+    float v[kSelectCPT];
+    load_cands<kSelectCPT>(cand, n_total, v, sm);
+    ke = min(k, sm.nvalid);
+    if (ke > 0) select_bins<kSelectCPT>(cand, n_total, v, ke, sm);
+  } else {
+    scan_cands(cand, n_total, sm);
+    ke = min(k, sm.nvalid);
+    if (ke > 0) select_stream(cand, n_total, ke, sm);
   }
   __syncthreads();
   for (int i = tid; i < ke; i += kTopkThreads) {
