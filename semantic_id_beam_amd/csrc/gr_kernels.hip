@@ -2075,20 +2075,34 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, int k
 static_assert(kMaxBeam <= kTopkThreads && kTieCap <= kTopkThreads, "one key per thread");
 __device__ void block_sort_desc(uint64_t *a, int n) {
   // n <= kTopkThreads distinct keys (each holds its candidate's flat index): a key's place in
-  // descending order is the number of keys above it, so the places form a permutation.  Every
-  // thread reads the same a[j] at once (an LDS broadcast); two barriers in all.
+  // descending order is the number of keys above it, so the places form a permutation.  With
+  // n <= kTopkThreads / 4 four adjacent lanes count a key's rank over a quarter of the keys
+  // each; the reads a[j] are LDS broadcasts.  Two barriers in all.
   const int tid = threadIdx.x;
   uint64_t key = 0;
   int rank = 0;
-  if (tid < n) {
-    key = a[tid];
-    int j = 0;
-    for (; j + 4 <= n; j += 4)
-      rank += (int)(a[j] > key) + (int)(a[j + 1] > key) + (int)(a[j + 2] > key) + (int)(a[j + 3] > key);
-    for (; j < n; ++j) rank += (int)(a[j] > key);
+  if (n <= kTopkThreads / 4) {
+    const int me = tid >> 2, q = tid & 3;
+    if (me < n) {
+      key = a[me];
+      const int j0 = q * ((n + 3) >> 2), j1 = min(n, j0 + ((n + 3) >> 2));
+      for (int j = j0; j < j1; ++j) rank += (int)(a[j] > key);
+    }
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    __syncthreads();
+    if (me < n && q == 0) a[rank] = key;
+  } else {
+    if (tid < n) {
+      key = a[tid];
+      int j = 0;
+      for (; j + 4 <= n; j += 4)
+        rank += (int)(a[j] > key) + (int)(a[j + 1] > key) + (int)(a[j + 2] > key) + (int)(a[j + 3] > key);
+      for (; j < n; ++j) rank += (int)(a[j] > key);
+    }
+    __syncthreads();
+    if (tid < n) a[rank] = key;
   }
-  __syncthreads();
-  if (tid < n) a[rank] = key;
   __syncthreads();
 }
 
@@ -2146,16 +2160,28 @@ __device__ void scan_cands(const float *__restrict__ cand, int total, SelectSmem
   reduce_stats(cnt, mn, mx, sm);
 }
 
-// Candidates tid + 1024*m of cand[0..total) into v[m], -inf past the end: every
-// load is issued before the first is used (one round trip, not CPT), then their statistics.
+// Flat index of a thread's m-th register candidate: four consecutive candidates per 16-byte
+// load, 4096 apart between loads.
+__device__ __forceinline__ int reg_cand(int m) { return 4 * (int)threadIdx.x + 4 * kTopkThreads * (m >> 2) + (m & 3); }
+
+// cand[0..total) into the registers v[m] (flat index reg_cand(m)), -inf past the end: every
+// load is issued before the first is used (one round trip, not CPT/4), then their statistics.
+// total is a multiple of 4 (rows x codebook with 4 | codebook) or the loads of the last
+// group go element by element.
 template <int CPT>
 __device__ void load_cands(const float *__restrict__ cand, int total, float (&v)[CPT], SelectSmem &sm) {
-  const int tid = threadIdx.x;
+  static_assert(CPT % 4 == 0, "four candidates per load");
 #pragma unroll
-  for (int m = 0; m < CPT; ++m) {
-    const int i = tid + kTopkThreads * m;
-    const float x = total > 0 ? gld<float>(cand + min(i, total - 1)) : kNegInf;
-    v[m] = i < total ? x : kNegInf;
+  for (int m4 = 0; m4 < CPT / 4; ++m4) {
+    const int i = reg_cand(4 * m4);
+    if (i + 4 <= total) {
+      const f32x4_t x = gld<f32x4_t>(cand + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * m4 + e] = x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * m4 + e] = i + e < total ? gld<float>(cand + i + e) : kNegInf;
+    }
   }
   int cnt = 0;
   float mn = __builtin_inff(), mx = kNegInf;
@@ -2225,7 +2251,7 @@ __device__ void select_bins(const float *__restrict__ cand, int total, const flo
     if (!(v[m] > kNegInf)) continue;
     const int b = bin(v[m]);
     if (b >= cut) {
-      const uint64_t key = cand_key(v[m], (uint32_t)(tid + kTopkThreads * m));
+      const uint64_t key = cand_key(v[m], (uint32_t)reg_cand(m));
       if (b > cut)
         sm.sel[atomicAdd(&sm.cnt, 1)] = key;
       else
@@ -2761,7 +2787,8 @@ hipError_t launch_topk(const Dev &dev, const StepReq *reqs, int n_reqs, int max_
 
 hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32_t *out_flat, float *out_score,
                               int32_t *n_out_dev, hipStream_t st) {
-  if ((int64_t)n_rows * V <= (int64_t)kTopkThreads * kSelectCPT)
+  // the register path reads 16-byte groups: the array must start on a 16-byte boundary
+  if ((int64_t)n_rows * V <= (int64_t)kTopkThreads * kSelectCPT && ((uintptr_t)cand & 15) == 0)
     hipLaunchKernelGGL(k_topk_select<true>, dim3(1), dim3(kTopkThreads), 0, st, cand, n_rows, V, k, out_flat,
                        out_score, n_out_dev);
   else

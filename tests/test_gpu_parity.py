@@ -537,7 +537,8 @@ def test_topk_select_bit_exact_vs_lexsort():
     rng = np.random.default_rng(5)
     cases = [(1, 16, 4, "r"), (7, 33, 20, "r"), (256, 256, 256, "r"), (30, 256, 30, "r"), (3, 1000, 1024, "r"),
              (64, 5, 300, "r"), (300, 256, 100, "r"),         # > 65536 candidates: streaming select
-             (40, 128, 50, "eq"), (256, 256, 256, "n"), (1, 1024, 1024, "n")]
+             (40, 128, 50, "eq"), (256, 256, 256, "n"), (1, 1024, 1024, "n"),
+             (16, 256, 64, "off")]                           # array not on a 16-byte boundary
     for n_rows, V, k, kind in cases:
         if kind == "eq":                                     # one value: every candidate ties
             x = np.full((n_rows, V), -1.5, dtype=np.float32)
@@ -548,7 +549,12 @@ def test_topk_select_bit_exact_vs_lexsort():
         x[rng.random((n_rows, V)) < 0.3] = -np.inf
         x[0, 0] = 0.0
         x[-1, -1] = -0.0
-        cand = torch.from_numpy(x).cuda()
+        if kind == "off":
+            buf = torch.zeros(n_rows * V + 1, dtype=torch.float32, device="cuda")
+            buf[1:] = torch.from_numpy(x.reshape(-1)).cuda()
+            cand = buf[1:]
+        else:
+            cand = torch.from_numpy(x).cuda()
         of = torch.empty(k, dtype=torch.int32, device="cuda")
         os_ = torch.empty(k, dtype=torch.float32, device="cuda")
         no = torch.zeros(1, dtype=torch.int32, device="cuda")
