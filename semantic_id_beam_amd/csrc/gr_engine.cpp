@@ -262,6 +262,8 @@ void layout(gr_engine *e) {
   s.logits = take(W * d.V * 4);
   s.logits_part = take((size_t)gr::kLogitsKS * W * d.V * 4);
   s.cand = take(W * d.V * 4);
+  s.lkeys = take((size_t)((W + gr::kLsmRows - 1) / gr::kLsmRows) * W * 8);
+  s.lcnt = take((size_t)((W + gr::kLsmRows - 1) / gr::kLsmRows) * 4);
   for (int b = 0; b < 2; ++b) {
     s.part_o[b] = take((size_t)d.Hkv * d.S_max * W * d.g * d.d * 4);
     s.part_ml[b] = take((size_t)d.Hkv * d.S_max * W * d.g * 8);
@@ -1070,7 +1072,10 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       w.wg_logits = wg_logits;
       wg_logits += ceil_div(R->n_bound, 64) * ceil_div(d.V, 64) * gr::kLogitsKS;
       w.wg_lsm = wg_lsm;
-      wg_lsm += ceil_div(R->n_bound, 4);
+      wg_lsm += ceil_div(R->n_bound, gr::kLsmRows);
+      // two-stage top-K when the chunks' kept keys fit the second stage's registers
+      w.sel2 = R->n_items == 0 &&
+               (int64_t)ceil_div(R->n_bound, gr::kLsmRows) * R->W <= (int64_t)gr::kTopkThreads * gr::kSel2CPT;
       max_cand = std::max(max_cand, R->n_bound * d.V);
     }
     G.wgs = wg_ctx;

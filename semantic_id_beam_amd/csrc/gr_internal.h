@@ -14,6 +14,8 @@ constexpr int kTopkThreads = 1024;
 constexpr int kMaxBeam = 1024;
 constexpr int kLogitsKS = 4;          // split of the hidden dimension in the logits GEMM
 constexpr int kSelectCPT = 64;        // candidates per thread kept in registers by the selection
+constexpr int kLsmRows = 16;          // beam rows per log-softmax workgroup (one wave each): a top-K chunk
+constexpr int kSel2CPT = 16;          // kept keys per thread in the second top-K stage (chunks x W <= 16384)
 constexpr int kTieCap = 1024;         // candidates sharing the cut bin that the fast selection sorts
 constexpr int kGatherMax = 64;        // slots per result-gather / root-beam launch
 
@@ -41,6 +43,8 @@ struct SlotLayout {
   size_t logits;              // [W_max][V] f32
   size_t logits_part;         // [kLogitsKS][W_max][V] f32 split-K partial sums
   size_t cand;                // [W_max][V] f32
+  size_t lkeys;               // [ceil(W_max / kLsmRows)][W] u64: each chunk's largest candidate keys
+  size_t lcnt;                // [ceil(W_max / kLsmRows)] i32: keys kept per chunk
   size_t part_o[2];           // [part_rows][d] f32 unnormalised o, row ((h*splits + sp)*rows_b + row); by layer parity
   size_t part_ml[2];          // [part_rows] float2 (m in log2 units, l)
   size_t codes[2];            // [W_max][levels] i32   (double-buffered by level parity)
@@ -99,6 +103,8 @@ struct StepReq {
                         // launch after each layer)
   int row0;             // the layer chain: first packed row of this request (a multiple of 32)
   int n_items;          // > 0: scoring request, its n_items candidates' codes are forced (no top-K)
+  int sel2;             // top-K in two stages: k_lsm keeps each chunk's W largest keys, k_select
+                        // selects over them (chunks x W <= kTopkThreads * kSel2CPT)
   int row_blocks;       // context-attention row blocks per kv head
   int wg_ctx, wg_merge, wg_logits, wg_lsm, wg_fin;  // first workgroup of this request in each launch
 };

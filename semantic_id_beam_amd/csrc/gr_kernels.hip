@@ -26,7 +26,8 @@
 //                                 (BeamKV append, beam tokens, merge, h += o) and
 //                                 k_beam_merge the last one
 //   k_ctx_attn_f32    split-K context attention on the vector ALU for float32 models
-//   k_logits          h @ w_sid[level], fp32 MFMA, split over the hidden dim
+//   k_logits          h @ w_sid[level], fp32 MFMA, split over the hidden dim (float32 models);
+//                     k_logits_x3 the same on bf16 MFMA with three-term bf16 operands
 //   k_lsm             sums the split logits, trie-masked log-softmax, candidates
 //   k_select          top-K over beams x codes, BeamPath update
 #include <hip/hip_ext.h>
@@ -1985,61 +1986,6 @@ __global__ __launch_bounds__(256) void k_logits(Dev dev, const StepReq *__restri
 }
 
 // --------------------------------------------------------------------------------------
-// Per beam row (one wave): logits = sum of the split partials (fixed order), trie mask of
-// the beam's node, log-softmax over the valid codes (or the whole codebook), candidates
-// cand[j][c] = score_j + logit - lse (valid) or -inf.
-__global__ __launch_bounds__(256) void k_lsm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
-  constexpr int MAXC = 1024 / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int ri = find_req<3>(reqs, n_reqs, blockIdx.x);
-  const StepReq R = reqs[ri];
-  const Dims &dm = dev.dm;
-  const int j = (blockIdx.x - R.wg_lsm) * 4 + w;
-  uint8_t *slot = slot_base(dev, R.slot);
-  const int s = R.level, cur = s & 1, V = dm.V;
-  const int n = ((const int *)(slot + dev.sl.n_live))[cur];
-  if (j >= n) return;
-  const uint32_t *mrow = dev.trie_mask + (dev.trie_off[s] + ((const int *)(slot + dev.sl.node[cur]))[j]) * dm.MW;
-  const float sc = ((const float *)(slot + dev.sl.score[cur]))[j];
-  const float *part = (const float *)(slot + dev.sl.logits_part);
-  const size_t pstride = (size_t)dm.W_max * V;
-  float *logits = (float *)(slot + dev.sl.logits);
-  float *cand = (float *)(slot + dev.sl.cand);
-  float xs[MAXC];
-  uint32_t vbits = 0;
-  float mx = kNegInf;
-#pragma unroll
-  for (int e = 0; e < MAXC; ++e) {
-    const int c = lane + 64 * e;
-    xs[e] = 0.f;
-    if (c < V) {
-      float x = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < kLogitsKS; ++ks) x += gld<float>(part + ks * pstride + (size_t)j * V + c);
-      xs[e] = x;
-      gst<float>(logits + (size_t)j * V + c, x);
-      const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
-      vbits |= (uint32_t)valid << e;
-      if (dm.norm == 1 || valid) mx = fmaxf(mx, x);
-    }
-  }
-  mx = wave_max(mx);
-  float sum = 0.f;
-#pragma unroll
-  for (int e = 0; e < MAXC; ++e) {
-    const int c = lane + 64 * e;
-    if (c < V && (dm.norm == 1 || ((vbits >> e) & 1u))) sum += expf(xs[e] - mx);
-  }
-  sum = wave_sum(sum);
-  const float lse = mx + logf(sum);
-#pragma unroll
-  for (int e = 0; e < MAXC; ++e) {
-    const int c = lane + 64 * e;
-    if (c < V) gst<float>(cand + (size_t)j * V + c, ((vbits >> e) & 1u) ? sc + (xs[e] - lse) : kNegInf);
-  }
-}
-
-// --------------------------------------------------------------------------------------
 // Top-K selection over a candidate array.  Keys are unique 64-bit integers
 //   key = order-preserving bits of the score << 32 | (0xFFFFFFFF - flat index)
 // so "larger key" = higher score, then lower flat index; -0 is folded to +0 first.
@@ -2069,7 +2015,7 @@ struct SelectSmem {
   float vmin, vmax;
 };
 
-__device__ void select_stream(const float *__restrict__ cand, int n_total, int k, SelectSmem &sm);
+__device__ void select_stream(const float *__restrict__ cand, int n_total, uint32_t ibase, int k, SelectSmem &sm);
 
 // Sorts a[0..n) descending (n <= 1024); every thread of the workgroup calls it.
 static_assert(kMaxBeam <= kTopkThreads && kTieCap <= kTopkThreads, "one key per thread");
@@ -2195,15 +2141,16 @@ __device__ void load_cands(const float *__restrict__ cand, int total, float (&v)
   reduce_stats(cnt, mn, mx, sm);
 }
 
-// Top-k of the candidates that load_cands left in v (1 <= k <= nvalid).  A monotone linear
-// map of the score to 2048 bins; the histogram picks the bin holding the k-th best,
-// everything above it is selected, and the candidates of that bin are ordered exactly by
-// their 64-bit keys.  When the cut bin holds more than kTieCap candidates the exact
-// streaming radix select runs instead.  Leaves the k best keys, sorted descending, in
-// sm.sel[0..k).
-template <int CPT>
-__device__ void select_bins(const float *__restrict__ cand, int total, const float (&v)[CPT], int k,
-                            SelectSmem &sm) {
+// Top-k of the candidates a thread holds in v[m] (flat index idx(m); -inf = none) with their
+// statistics in sm (1 <= k <= nvalid).  A monotone linear map of the score to 2048 bins;
+// the histogram picks the bin holding the k-th best, everything above it is selected, and the
+// candidates of that bin are ordered exactly by their 64-bit keys.  When the cut bin holds
+// more than kTieCap candidates the exact streaming radix select runs instead, over the same
+// candidates in memory: cand[0..total), flat index ibase + i.  Leaves the k best keys in
+// sm.sel[0..k), sorted descending when `sorted` (the streaming select always sorts).
+template <int CPT, typename IDX>
+__device__ void select_bins(const float *__restrict__ cand, int total, uint32_t ibase, const float (&v)[CPT], IDX idx,
+                            int k, bool sorted, SelectSmem &sm) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float vmin = sm.vmin, span = sm.vmax - sm.vmin;
   float scale = (float)(kBins - 1) / span;
@@ -2243,7 +2190,7 @@ __device__ void select_bins(const float *__restrict__ cand, int total, const flo
   const int cut = sm.cut, need = sm.need, cutcnt = sm.hist[cut];
   __syncthreads();  // every thread has read hist[cut] before anything reuses hist
   if (cutcnt > kTieCap) {  // uniform branch
-    select_stream(cand, total, k, sm);
+    select_stream(cand, total, ibase, k, sm);
     return;
   }
 #pragma unroll
@@ -2251,7 +2198,7 @@ __device__ void select_bins(const float *__restrict__ cand, int total, const flo
     if (!(v[m] > kNegInf)) continue;
     const int b = bin(v[m]);
     if (b >= cut) {
-      const uint64_t key = cand_key(v[m], (uint32_t)reg_cand(m));
+      const uint64_t key = cand_key(v[m], (uint32_t)idx(m));
       if (b > cut)
         sm.sel[atomicAdd(&sm.cnt, 1)] = key;
       else
@@ -2263,12 +2210,13 @@ __device__ void select_bins(const float *__restrict__ cand, int total, const flo
   if (ntie > 1) block_sort_desc(sm.tie, ntie);
   for (int i = tid; i < need; i += kTopkThreads) sm.sel[base + i] = sm.tie[i];
   __syncthreads();
-  block_sort_desc(sm.sel, k);
+  if (sorted) block_sort_desc(sm.sel, k);
 }
 
 // Streaming variant for candidate arrays larger than the registers hold: exact radix
-// select reading the array from memory each pass.  Leaves the k largest keys sorted.
-__device__ void select_stream(const float *__restrict__ cand, int n_total, int k, SelectSmem &sm) {
+// select reading the array from memory each pass (flat index ibase + i).  Leaves the k largest
+// keys sorted.
+__device__ void select_stream(const float *__restrict__ cand, int n_total, uint32_t ibase, int k, SelectSmem &sm) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   int need = k;
@@ -2286,7 +2234,7 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, int k
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (!(x[u] > kNegInf)) continue;
-        const uint64_t key = cand_key(x[u], (uint32_t)(base + tid + u * kTopkThreads));
+        const uint64_t key = cand_key(x[u], ibase + (uint32_t)(base + tid + u * kTopkThreads));
         if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255], 1);
       }
     }
@@ -2320,12 +2268,201 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, int k
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (!(x[u] > kNegInf)) continue;
-      const uint64_t key = cand_key(x[u], (uint32_t)(base + tid + u * kTopkThreads));
+      const uint64_t key = cand_key(x[u], ibase + (uint32_t)(base + tid + u * kTopkThreads));
       if (key >= prefix) sm.sel[atomicAdd(&sm.cnt, 1)] = key;
     }
   }
   __syncthreads();
   block_sort_desc(sm.sel, k);
+}
+
+// --------------------------------------------------------------------------------------
+// The same logit partials for bf16 models, on the bf16 matrix cores: each fp32 operand is
+// split into bf16 terms x = hi + lo + r (hi and lo rounded to nearest, |r| <= 2^-18 |x|) and
+// the product taken as hi*hi + hi*lo + lo*hi with fp32 accumulation (the dropped lo*lo and
+// the residuals leave about 3 * 2^-18 relative error per product, 2e-5 on logits of rms 1, far
+// below the decode's 1e-3 log-prob bound).  Tiles as in k_logits; chunks of 32 hidden
+// features are staged through LDS already split, A as [row][k] and B transposed to [col][k],
+// so every MFMA operand is one 16-byte read.
+__global__ __launch_bounds__(256) void k_logits_x3(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  constexpr int KC = 32, LS = KC + 8;  // chunk of hidden features, LDS row stride (elements)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ri = find_req<2>(reqs, n_reqs, blockIdx.x);
+  const StepReq R = reqs[ri];
+  const Dims &dm = dev.dm;
+  const int V = dm.V, H = dm.Hq * dm.d, KSL = H / kLogitsKS;
+  const int nct = (V + 63) / 64;
+  int local = blockIdx.x - R.wg_logits;
+  const int ks = local % kLogitsKS;
+  local /= kLogitsKS;
+  const int ct = local % nct, rt = local / nct;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int s = R.level;
+  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  const int row0 = rt * 64;
+  if (row0 >= n_live) return;
+  const float *hb = (const float *)(slot + dev.sl.h);
+  const float *Wt = dev.w_sid + (size_t)s * H * V;
+  const int k0 = ks * KSL;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][2][64 * LS];  // [buf][hi, lo][row][k]
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][2][64 * LS];  // [buf][hi, lo][col][k]
+  // staging: A row ar, features ak..ak+8; B column bc, features bk..bk+8
+  const int ar = tid >> 2, ak = (tid & 3) * 8;
+  const int bc = tid & 63, bk = w * 8;
+  const bool a_ok = row0 + ar < n_live, b_ok = ct * 64 + bc < V;
+  f32x4_t ra[2];
+  float rb[8];
+  auto gl = [&](int kc) {
+    const float *ap = hb + (size_t)(row0 + (a_ok ? ar : 0)) * H + k0 + kc + ak;
+    ra[0] = a_ok ? gld<f32x4_t>(ap) : f32x4_t{};
+    ra[1] = a_ok ? gld<f32x4_t>(ap + 4) : f32x4_t{};
+    const float *bp = Wt + (size_t)(k0 + kc + bk) * V + ct * 64 + (b_ok ? bc : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rb[i] = b_ok ? gld<float>(bp + (size_t)i * V) : 0.f;
+  };
+  // x -> (hi, lo) bf16, eight at a time, as two 16-byte words
+  auto split8 = [](const float (&x)[8], u32x4_t &hi, u32x4_t &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t v = {x[2 * i], x[2 * i + 1]};
+      const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+      const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
+      const bf16x2_t l = __builtin_convertvector(v - hf, bf16x2_t);
+      hi[i] = __builtin_bit_cast(uint32_t, h);
+      lo[i] = __builtin_bit_cast(uint32_t, l);
+    }
+  };
+  auto ls = [&](int buf) {
+    float a8[8] = {ra[0][0], ra[0][1], ra[0][2], ra[0][3], ra[1][0], ra[1][1], ra[1][2], ra[1][3]};
+    u32x4_t h, l;
+    split8(a8, h, l);
+    *(u32x4_t *)&sA[buf][0][ar * LS + ak] = h;
+    *(u32x4_t *)&sA[buf][1][ar * LS + ak] = l;
+    split8(rb, h, l);
+    *(u32x4_t *)&sB[buf][0][bc * LS + bk] = h;
+    *(u32x4_t *)&sB[buf][1][bc * LS + bk] = l;
+  };
+  const int rbk = w >> 1, cbk = w & 1;
+  const int ao = (rbk * 32 + (lane & 31)) * LS + 8 * (lane >> 5);
+  const int bo = (cbk * 32 + (lane & 31)) * LS + 8 * (lane >> 5);
+  f32x16_t acc = f32x16_t{};
+  gl(0);
+  ls(0);
+  __syncthreads();
+  for (int kc = 0, it = 0; kc < KSL; kc += KC, ++it) {
+    const int buf = it & 1;
+    if (kc + KC < KSL) gl(kc + KC);
+#pragma unroll
+    for (int kb = 0; kb < KC / 16; ++kb) {
+      const bf16x8_t ah = *(const bf16x8_t *)&sA[buf][0][ao + 16 * kb];
+      const bf16x8_t al = *(const bf16x8_t *)&sA[buf][1][ao + 16 * kb];
+      const bf16x8_t bh = *(const bf16x8_t *)&sB[buf][0][bo + 16 * kb];
+      const bf16x8_t bl = *(const bf16x8_t *)&sB[buf][1][bo + 16 * kb];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+    }
+    if (kc + KC < KSL) ls(buf ^ 1);
+    __syncthreads();
+  }
+  float *out = (float *)(slot + dev.sl.logits_part) + (size_t)ks * dm.W_max * V;
+  const int col = ct * 64 + cbk * 32 + (lane & 31);
+  if (col < V) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = row0 + rbk * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (row < n_live) gst<float>(out + (size_t)row * V + col, acc[i]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// Per beam row (one wave, kLsmRows rows per workgroup): logits = sum of the split partials
+// (fixed order), trie mask of the beam's node, log-softmax over the valid codes (or the whole
+// codebook), candidates cand[j][c] = score_j + logit - lse (valid) or -inf.  For a request
+// whose top-K runs in two stages (StepReq::sel2) the workgroup then keeps the W largest
+// candidate keys of its rows (a chunk) in lkeys[chunk][0..lcnt[chunk]): keys are unique, so
+// the request's W largest are among the union of its chunks' W largest, and k_select selects
+// over those.
+__global__ __launch_bounds__(kTopkThreads) void k_lsm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
+  constexpr int MAXC = 1024 / 64;
+  static_assert(kLsmRows * 64 == kTopkThreads, "one wave per row");
+  __shared__ SelectSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ri = find_req<3>(reqs, n_reqs, blockIdx.x);
+  const StepReq R = reqs[ri];
+  const Dims &dm = dev.dm;
+  const int chunk = blockIdx.x - R.wg_lsm, row0 = chunk * kLsmRows, j = row0 + w;
+  uint8_t *slot = slot_base(dev, R.slot);
+  const int s = R.level, cur = s & 1, V = dm.V;
+  const int n = ((const int *)(slot + dev.sl.n_live))[cur];
+  if (row0 >= n) return;  // the whole chunk past the live beams
+  float *cand = (float *)(slot + dev.sl.cand);
+  float cv[MAXC];  // this lane's candidates (codes lane + 64 e); -inf: invalid, or no row
+#pragma unroll
+  for (int e = 0; e < MAXC; ++e) cv[e] = kNegInf;
+  if (j < n) {
+    const uint32_t *mrow = dev.trie_mask + (dev.trie_off[s] + ((const int *)(slot + dev.sl.node[cur]))[j]) * dm.MW;
+    const float sc = ((const float *)(slot + dev.sl.score[cur]))[j];
+    const float *part = (const float *)(slot + dev.sl.logits_part);
+    const size_t pstride = (size_t)dm.W_max * V;
+    float *logits = (float *)(slot + dev.sl.logits);
+    float xs[MAXC];
+    uint32_t vbits = 0;
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < MAXC; ++e) {
+      const int c = lane + 64 * e;
+      xs[e] = 0.f;
+      if (c < V) {
+        float x = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kLogitsKS; ++ks) x += gld<float>(part + ks * pstride + (size_t)j * V + c);
+        xs[e] = x;
+        gst<float>(logits + (size_t)j * V + c, x);
+        const bool valid = (mrow[c >> 5] >> (c & 31)) & 1u;
+        vbits |= (uint32_t)valid << e;
+        if (dm.norm == 1 || valid) mx = fmaxf(mx, x);
+      }
+    }
+    mx = wave_max(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < MAXC; ++e) {
+      const int c = lane + 64 * e;
+      if (c < V && (dm.norm == 1 || ((vbits >> e) & 1u))) sum += expf(xs[e] - mx);
+    }
+    sum = wave_sum(sum);
+    const float lse = mx + logf(sum);
+#pragma unroll
+    for (int e = 0; e < MAXC; ++e) {
+      const int c = lane + 64 * e;
+      if (c < V) {
+        cv[e] = ((vbits >> e) & 1u) ? sc + (xs[e] - lse) : kNegInf;
+        gst<float>(cand + (size_t)j * V + c, cv[e]);
+      }
+    }
+  }
+  if (!R.sel2) return;  // uniform over the workgroup
+  int cnt = 0;
+  float mn = __builtin_inff(), mxv = kNegInf;
+#pragma unroll
+  for (int e = 0; e < MAXC; ++e)
+    if (cv[e] > kNegInf) {
+      ++cnt;
+      mn = fminf(mn, cv[e]);
+      mxv = fmaxf(mxv, cv[e]);
+    }
+  reduce_stats(cnt, mn, mxv, sm);  // its barriers also publish the chunk's cand stores
+  const int k = min(R.W, sm.nvalid);
+  if (k > 0) {
+    const int rows = min(kLsmRows, n - row0);
+    select_bins<MAXC>(cand + (size_t)row0 * V, rows * V, (uint32_t)(row0 * V), cv,
+                      [&](int e) { return j * V + lane + 64 * e; }, k, false, sm);
+    uint64_t *lk = (uint64_t *)(slot + dev.sl.lkeys) + (size_t)chunk * R.W;
+    for (int i = tid; i < k; i += kTopkThreads) lk[i] = sm.sel[i];
+  }
+  if (tid == 0) ((int *)(slot + dev.sl.lcnt))[chunk] = k;
 }
 
 // Scoring step: candidate i (of the n_items given) takes its own code at level s instead of a
@@ -2389,15 +2526,42 @@ __global__ __launch_bounds__(kTopkThreads) void k_select(Dev dev, const StepReq 
   const int n = ((const int *)(slot + dev.sl.n_live))[cur];
   const float *cand = (const float *)(slot + dev.sl.cand);
   int k;
-  if constexpr (REGS) {
+  if (R.sel2) {
+    // second stage: the chunks' kept keys (chunk g's at lkeys[g * W], lcnt[g] of them); the
+    // streaming fallback runs over the whole candidate array
+    const int G = (n + kLsmRows - 1) / kLsmRows, P = G * R.W;
+    const uint64_t *lk = (const uint64_t *)(slot + dev.sl.lkeys);
+    const int *lc = (const int *)(slot + dev.sl.lcnt);
+    float v[kSel2CPT];
+    uint32_t ix[kSel2CPT];
+    int cnt = 0;
+    float mn = __builtin_inff(), mx = kNegInf;
+#pragma unroll
+    for (int m = 0; m < kSel2CPT; ++m) {
+      const int p = tid + kTopkThreads * m, g = p / R.W;
+      v[m] = kNegInf;
+      ix[m] = 0;
+      if (p < P && p - g * R.W < lc[g]) {
+        const uint64_t key = lk[p];
+        v[m] = ord2f((uint32_t)(key >> 32));
+        ix[m] = 0xFFFFFFFFu - (uint32_t)key;
+        ++cnt;
+        mn = fminf(mn, v[m]);
+        mx = fmaxf(mx, v[m]);
+      }
+    }
+    reduce_stats(cnt, mn, mx, sm);
+    k = min(R.W, sm.nvalid);
+    if (k > 0) select_bins<kSel2CPT>(cand, n * V, 0u, v, [&](int m) { return ix[m]; }, k, true, sm);
+  } else if constexpr (REGS) {
     float v[kSelectCPT];
     load_cands<kSelectCPT>(cand, n * V, v, sm);
     k = min(R.W, sm.nvalid);
-    if (k > 0) select_bins<kSelectCPT>(cand, n * V, v, k, sm);
+    if (k > 0) select_bins<kSelectCPT>(cand, n * V, 0u, v, [](int m) { return reg_cand(m); }, k, true, sm);
   } else {
     scan_cands(cand, n * V, sm);
     k = min(R.W, sm.nvalid);
-    if (k > 0) select_stream(cand, n * V, k, sm);
+    if (k > 0) select_stream(cand, n * V, 0u, k, sm);
   }
   __syncthreads();
   const int *node_cur = (const int *)(slot + dev.sl.node[cur]);
@@ -2444,11 +2608,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float *__res
     float v[kSelectCPT];
     load_cands<kSelectCPT>(cand, n_total, v, sm);
     ke = min(k, sm.nvalid);
-    if (ke > 0) select_bins<kSelectCPT>(cand, n_total, v, ke, sm);
+    if (ke > 0) select_bins<kSelectCPT>(cand, n_total, 0u, v, [](int m) { return reg_cand(m); }, ke, true, sm);
   } else {
     scan_cands(cand, n_total, sm);
     ke = min(k, sm.nvalid);
-    if (ke > 0) select_stream(cand, n_total, ke, sm);
+    if (ke > 0) select_stream(cand, n_total, 0u, ke, sm);
   }
   __syncthreads();
   for (int i = tid; i < ke; i += kTopkThreads) {
@@ -2757,7 +2921,10 @@ hipError_t launch_finish_layer(const Dev &dev, const StepReq *reqs, int n_reqs, 
 hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
                          LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
-  launch(k_logits, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
+  if (dev.dm.dtype == 1)
+    launch(k_logits_x3, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
+  else
+    launch(k_logits, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
@@ -2772,7 +2939,7 @@ hipError_t launch_label_head(const Dev &dev, const StepReq *reqs, int n_reqs, in
 
 hipError_t launch_lsm(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st, LaunchEv ev) {
   if (total_wgs <= 0) return hipSuccess;
-  launch(k_lsm, dim3(total_wgs), dim3(256), st, ev, dev, reqs, n_reqs);
+  launch(k_lsm, dim3(total_wgs), dim3(kTopkThreads), st, ev, dev, reqs, n_reqs);
   return hipGetLastError();
 }
 
