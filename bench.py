@@ -42,6 +42,11 @@ MEASURED_TRAFFIC = {
 }
 
 
+# per-layer launch sequences: the timed region's context-attention events sit on every fourth
+# layer's launch (each carrying dispatch costs about 3 us of the stream's time)
+PROF_STRIDE = 4
+
+
 def source_digest(path):
     """SHA-256 of a C/HIP source with its // comments and blank lines removed (a comment edit
     does not change the code the counters ran)."""
@@ -114,11 +119,25 @@ def scoring_leg(cfg, args, per_layer=True):
     eng.close()
     log(f"scoring: {n_calls} calls of {R} x {n_cand} candidates in {dt:.3f} s; with labels {dl:.3f} s")
     assert np.all(np.isfinite(sc)) and np.all(np.isfinite(lab))
+    # shared-context attention flops of one call (QK^T and PV, 4 d flops per query row and
+    # context token): every candidate's query rows at levels 1..levels-1 (level 0 has one
+    # beam), plus the label step's; the whole call's time (every kernel) against the bf16
+    # matrix peak
+    N = sum(n for n, _ in synth.request_shapes(cfg))
+    per_level = 4.0 * cfg.n_layers * n_cand * cfg.n_q_heads * cfg.head_dim * N
+    f_items = per_level * (cfg.n_levels - 1 + 1.0 / n_cand)
+    f_labels = f_items + per_level
+
+    def roof(flops, sec):
+        ach = flops * n_calls / sec / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                "frac": round(ach / 2500.0, 4), "scope": "whole call (every kernel), context-attention flops"}
+
     return {"requests_per_call": R, "candidates_per_request": n_cand, "calls": n_calls,
             "ms_per_call": round(1e3 * dt / n_calls, 3),
-            "candidates_per_s": round(R * n_cand * n_calls / dt, 1),
+            "candidates_per_s": round(R * n_cand * n_calls / dt, 1), "roofline": roof(f_items, dt),
             "labels": {"n_labels": 2, "ms_per_call": round(1e3 * dl / n_calls, 3),
-                       "candidates_per_s": round(R * n_cand * n_calls / dl, 1)}}
+                       "candidates_per_s": round(R * n_cand * n_calls / dl, 1), "roofline": roof(f_labels, dl)}}
 
 
 def prefill_leg(cfg, args, vocab: int = 32768, user_dim: int = 256, embed_dim: int = 2048, reps: int = 5):
@@ -552,10 +571,12 @@ def decode_leg(cfg, args, per_layer: bool):
     for i in range(args.warmup):
         decode_all()
     torch.cuda.synchronize()
-    # the timed region: the context-attention launches carry HIP events (the roofline's
-    # durations), the other launches none
+    # the timed region: the context-attention launches of every PROF_STRIDE-th layer carry HIP
+    # events (the roofline's durations: the same kernel on the same work at every layer), the
+    # other launches none
     G.gr_engine_profile_reset(eng.eng)
     G.gr_engine_set_profiling_kinds(eng.eng, 1 << G.GR_PROF_CTX_ATTN)
+    G.gr_engine_set_profiling_stride(eng.eng, PROF_STRIDE)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
@@ -567,6 +588,7 @@ def decode_leg(cfg, args, per_layer: bool):
     t1 = time.perf_counter()
     decode_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     G.gr_engine_set_profiling(eng.eng, False)
+    G.gr_engine_set_profiling_stride(eng.eng, 1)
     elapsed = t1 - t0
     log(f"timed {args.steps} decodes in {elapsed:.3f} s")
 
@@ -623,6 +645,8 @@ def decode_leg(cfg, args, per_layer: bool):
         "dispatches": int(d_m),
         "avg_us_per_dispatch": round(1e3 * ms_m / max(d_m, 1), 2),
         "algorithmic_per_layer": f"{ctx_flops(levels_mfma[-1]) / 1e9:.2f} GFLOP" if levels_mfma else None,
+        "timed_launches": (f"every {PROF_STRIDE}th layer's launch of the timed decodes" if per_layer
+                           else "every launch of the timed decodes"),
     }
     kernels = {
         "ctx_attn_level0": {"kernel": "k_ctx_attn_stream" if wide else "k_ctx_attn",
@@ -638,7 +662,13 @@ def decode_leg(cfg, args, per_layer: bool):
         tot = sum(prof[name][s][0] for s in range(lv))
         n = sum(prof[name][s][1] for s in range(lv))
         kernels[name] = {"avg_launch_us": round(1e3 * tot / max(n, 1), 2), "ms_per_decode": round(tot / args.steps, 3)}
-    kernels["ctx_attn"] = {"ms_per_decode": round(sum(prof["ctx_attn"][s][0] for s in range(lv)) / args.steps, 3)}
+    # per-layer launches: the timed (sampled) launches' average duration times the layers of a
+    # decode; otherwise every launch was timed
+    if per_layer:
+        ctx_ms = sum(prof["ctx_attn"][s][0] / max(prof["ctx_attn"][s][1], 1) * cfg.n_layers for s in range(lv))
+    else:
+        ctx_ms = sum(prof["ctx_attn"][s][0] for s in range(lv)) / args.steps
+    kernels["ctx_attn"] = {"ms_per_decode": round(ctx_ms, 3)}
     # context loading (gr_ctx_kv_load), outside the timed decodes: caller K/V read, native
     # K/V^T written (padding included); the key norms and value scales add no traffic
     kernels["ctx_load"] = {"kernel": "k_load_ctx", "bound": "hbm", "ms_per_request": round(load_ms / R, 3),

@@ -509,6 +509,12 @@ gr_status gr_engine_set_profiling(gr_engine *eng, int32_t enable);
 /* As gr_engine_set_profiling, for the kinds whose bit (1u << GR_PROF_*) is set in `kinds` only (0:
  * off): a timed run can carry events on the launches it reports and none on the others. */
 gr_status gr_engine_set_profiling_kinds(gr_engine *eng, uint32_t kinds);
+/* In launch sequences of one launch per layer (the split-K steps' context attention and merge,
+ * the layer chain's projections, norms, attention and finish), only the launches of layers l
+ * with l % stride == 0 carry events while profiling is on; the buckets then average the timed
+ * launches only.  stride >= 1 (1, the default, times every launch), else GR_E_INVALID_ARG.  A
+ * timed run can so sample a kernel's duration with fewer events in its stream. */
+gr_status gr_engine_set_profiling_stride(gr_engine *eng, int32_t stride);
 
 /* Waits for every recorded event, folds the elapsed times into the buckets and
  * returns one bucket: total milliseconds and number of launches, where a launch that

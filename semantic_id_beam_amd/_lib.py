@@ -38,7 +38,7 @@ EXPORTS = [
     "gr_engine_profile_dispatches", "gr_engine_profile_reset", "gr_score_items", "gr_score_items_batch",
     "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
     "gr_sched_completed", "gr_sched_result", "gr_sched_counts", "gr_debug_chain_rows", "gr_score_items_labels",
-    "gr_engine_graph_stats", "gr_engine_set_profiling_kinds",
+    "gr_engine_graph_stats", "gr_engine_set_profiling_kinds", "gr_engine_set_profiling_stride",
 ]
 GR_CHAIN_X_IN, GR_CHAIN_XN_ATTN, GR_CHAIN_Q, GR_CHAIN_O, GR_CHAIN_X_MID, GR_CHAIN_XN_MLP, GR_CHAIN_ACT, \
     GR_CHAIN_X_OUT = range(8)
@@ -142,6 +142,7 @@ def lib() -> C.CDLL:
         "gr_engine_profile_reset": (i32, [vp]),
         "gr_engine_graph_stats": (i32, [vp, vp, vp]),
         "gr_engine_set_profiling_kinds": (i32, [vp, C.c_uint32]),
+        "gr_engine_set_profiling_stride": (i32, [vp, i32]),
         "gr_sched_create": (i32, [vp, i32, vp, P(vp)]),
         "gr_sched_destroy": (i32, [vp]),
         "gr_sched_submit": (i32, [vp, i64, i32, i32, vp, vp, vp, u32]),
@@ -388,6 +389,10 @@ def gr_engine_profile_dispatches(eng: int, kind: int, level: int = -1) -> int:
 
 def gr_engine_set_profiling_kinds(eng: int, kinds: int):
     _check(lib().gr_engine_set_profiling_kinds(eng, kinds))
+
+
+def gr_engine_set_profiling_stride(eng: int, stride: int):
+    _check(lib().gr_engine_set_profiling_stride(eng, stride))
 
 
 def gr_engine_graph_stats(eng: int):

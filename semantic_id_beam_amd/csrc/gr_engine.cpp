@@ -90,6 +90,7 @@ struct gr_engine {
   // kernels), folded into [kind][level] buckets.  A record spans two events of the pool.
   bool prof = false;
   uint32_t prof_mask = ~0u;  // the kinds (bit 1 << GR_PROF_*) profiled while prof is on
+  int prof_stride = 1;       // one-launch-per-layer sequences: only layers l % prof_stride == 0 are timed
   std::vector<hipEvent_t> prof_ev;
   int prof_next = 0;  // next unused event of the pool
   struct ProfRec { int kind, level, a, b, count, disp; };  // count: layer steps, disp: kernel dispatches
@@ -1228,15 +1229,16 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     rec(GR_PROF_NORM, pn);
     const size_t D = (size_t)d.Hq * d.d;
     for (int l = 0; l < d.L; ++l) {
+      const bool lp = l % e->prof_stride == 0;  // this layer's launches are timed
       auto gemm = [&](int kind) -> gr_status {
-        const auto pg = prof_pair(e, pk(GR_PROF_GEMM));
+        const auto pg = prof_pair(e, pk(GR_PROF_GEMM) && lp);
         gr_status q = check_dev(e, gr::launch_chain_gemm(e->dev, dw, n, rows, kind, l, st, prof_ev(e, pg.first, pg.second)),
                                 "chain projection");
         if (q == GR_OK) rec(GR_PROF_GEMM, pg);
         return q;
       };
       auto norm = [&](const float *g) -> gr_status {
-        const auto pq = prof_pair(e, pk(GR_PROF_NORM));
+        const auto pq = prof_pair(e, pk(GR_PROF_NORM) && lp);
         gr_status q = check_dev(e, gr::launch_chain_norm(e->dev, g, rows, st, prof_ev(e, pq.first, pq.second)),
                                 "chain norm");
         if (q == GR_OK) rec(GR_PROF_NORM, pq);
@@ -1262,7 +1264,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       if ((r = snap(GR_CHAIN_X_IN)) != GR_OK || (r = snap(GR_CHAIN_XN_ATTN)) != GR_OK) return r;
       if ((r = gemm(gr::kChainQKV)) != GR_OK) return r;
       if ((r = snap(GR_CHAIN_Q)) != GR_OK) return r;
-      const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
+      const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN) && lp);
       for (size_t gi = 0; gi < groups.size(); ++gi) {
         const Group &G = groups[gi];
         const gr::LaunchEv ev = prof_ev(e, gi == 0 ? pc.first : -1, gi + 1 == groups.size() ? pc.second : -1);
@@ -1271,7 +1273,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
           return r;
       }
       prof_record(e, GR_PROF_CTX_ATTN, plevel, pc, 1, (int)groups.size());
-      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
+      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE) && lp);
       if ((r = check_dev(e, finish(0, n, l, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
                          "layer finish")) != GR_OK)
         return r;
@@ -1294,7 +1296,8 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     rec(GR_PROF_NORM, pn);
   }
   for (int l = 0; l < (first_fused || layered || multi || d.chain ? 0 : d.L); ++l) {
-    const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN));
+    const bool lp = l % e->prof_stride == 0;  // this layer's launches are timed
+    const auto pc = prof_pair(e, pk(GR_PROF_CTX_ATTN) && lp);
     if (l == 0) step_start = pc.first;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group &G = groups[gi];
@@ -1307,7 +1310,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
     // float32 (and one layer per launch): finish every layer separately; otherwise layer l is
     // finished inside layer l+1's context kernel, and the last layer here
     if (!defer || l == d.L - 1) {
-      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE));
+      const auto pm = prof_pair(e, pk(GR_PROF_BEAM_MERGE) && lp);
       if ((r = check_dev(e, finish(0, n, l, wg_fin, 0, wg_merge, 0, st, prof_ev(e, pm.first, pm.second)),
                          "beam attention/merge")) != GR_OK)
         return r;
@@ -1696,6 +1699,13 @@ gr_status gr_engine_set_profiling_kinds(gr_engine *e, uint32_t kinds) {
   if (!e->bound) return fail(GR_E_BAD_STATE, "workspace not bound");
   e->prof = kinds != 0;
   e->prof_mask = kinds;
+  return GR_OK;
+}
+
+gr_status gr_engine_set_profiling_stride(gr_engine *e, int32_t stride) {
+  if (!e) return fail(GR_E_INVALID_ARG, "null engine");
+  if (stride < 1) return fail(GR_E_INVALID_ARG, "profiling stride must be >= 1");
+  e->prof_stride = stride;
   return GR_OK;
 }
 

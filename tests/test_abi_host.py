@@ -146,8 +146,20 @@ def test_null_engine_is_rejected():
     assert L.gr_engine_profile_dispatches(None, 0, -1, None) == G.GR_E_INVALID_ARG
     assert L.gr_score_items(None, 0, None, 1, None, None) == G.GR_E_INVALID_ARG
     assert L.gr_score_items_batch(None, None, 1, None, 1, None, None) == G.GR_E_INVALID_ARG
+    assert L.gr_engine_set_profiling_stride(None, 4) == G.GR_E_INVALID_ARG
     assert L.gr_engine_destroy(None) == G.GR_OK
     assert L.gr_engine_workspace_bytes(None) == 0
+
+
+def test_profiling_stride_must_be_positive():
+    eng = G.gr_engine_create(_desc(), _items(), _opts())
+    G.gr_engine_set_profiling_stride(eng, 4)
+    G.gr_engine_set_profiling_stride(eng, 1)
+    for bad in (0, -3):
+        with pytest.raises(G.GrError) as ei:
+            G.gr_engine_set_profiling_stride(eng, bad)
+        assert ei.value.status == G.GR_E_INVALID_ARG
+    G.gr_engine_destroy(eng)
 
 
 def test_scheduler_host_checks():

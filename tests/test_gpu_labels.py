@@ -4,7 +4,8 @@ Each candidate's codes run as its own tokens after the shared context (it sees t
 itself only); the last code's hidden vector gives the label log-probabilities through the label
 head.  Checked: the label log-probabilities against oracle.label_scores (1e-5 absolute on the
 float32 model, 1e-3 on bf16, the log-prob bound of the decode), the item log-likelihoods of the
-same call against oracle.score_items, and agreement between a batched call and single calls."""
+same call against oracle.score_items, and agreement between a batched call and single calls, up
+to the pages' 500 candidates per request."""
 import numpy as np
 import pytest
 
@@ -76,6 +77,19 @@ def test_labels_bf16_batch(per_layer):
         np.testing.assert_allclose(l1[0], labels[r], rtol=0, atol=2 * SCORE_TOL)
     eng.close()
     save_report(cfg, [], label_err=err, per_layer=per_layer)
+
+
+def test_labels_500_candidates():
+    """The pages' scoring workload shape: 500 candidates (20 outside the item set) of one
+    request in one call, bf16, four labels, one launch per layer; every candidate against the
+    oracle."""
+    cfg = synth.get_config("ctx1k_beam256", n_requests=1, n_layers=3, ctx_len=400, beam_width=64, n_items=50000)
+    eng = make_engine(cfg, max_requests=1, max_beam_width=512, per_layer=True, n_labels=4)
+    rid = load_request(eng, cfg, 0)
+    cands = _candidates(cfg, 500, 20, seed=77)[None]
+    _, _, err = _check(cfg, eng, [rid], cands, 4, SCORE_TOL, [0])
+    eng.close()
+    save_report(cfg, [], label_err=err, n_candidates=500)
 
 
 def test_labels_need_a_label_head():
