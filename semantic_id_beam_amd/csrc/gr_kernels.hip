@@ -2278,10 +2278,10 @@ __device__ void select_stream(const float *__restrict__ cand, int n_total, uint3
 
 // --------------------------------------------------------------------------------------
 // The same logit partials for bf16 models, on the bf16 matrix cores: each fp32 operand is
-// split into bf16 terms x = hi + lo + r (hi and lo rounded to nearest, |r| <= 2^-18 |x|) and
+// split into bf16 terms x = hi + lo + r (hi and lo rounded to nearest, |r| <= 2^-16 |x|) and
 // the product taken as hi*hi + hi*lo + lo*hi with fp32 accumulation (the dropped lo*lo and
-// the residuals leave about 3 * 2^-18 relative error per product, 2e-5 on logits of rms 1, far
-// below the decode's 1e-3 log-prob bound).  Tiles as in k_logits; chunks of 32 hidden
+// the residuals leave at most 3 * 2^-16 relative error per product, typically 2e-5 on a
+// 2048-term logit of rms 1, far below the decode's 1e-3 log-prob bound).  Tiles as in k_logits; chunks of 32 hidden
 // features are staged through LDS already split, A as [row][k] and B transposed to [col][k],
 // so every MFMA operand is one 16-byte read.
 __global__ __launch_bounds__(256) void k_logits_x3(Dev dev, const StepReq *__restrict__ reqs, int n_reqs) {
