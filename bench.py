@@ -69,6 +69,19 @@ def measured_traffic(cfg, kernel, variant):
     return None if t is None else t["read"] + t["written"]
 
 
+def ctx_load_bytes(cfg, n):
+    """HBM bytes of one copy load of an n-token context: the caller's K and V read, native K and
+    V^T written (padded to a multiple of 64 tokens); for bf16 models with head_dim 128 also the
+    native V^T read again and its float16 copy written."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    np_ = (n + 63) // 64 * 64
+    row = cfg.n_layers * cfg.n_kv_heads * cfg.head_dim
+    b = 2 * row * el * (n + np_)
+    if cfg.dtype == "bf16" and cfg.head_dim == 128:
+        b += 2 * row * 2 * np_
+    return b
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -259,9 +272,7 @@ def workload_leg(name: str, reps: int = 3, per_layer: bool = True):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     eng.close()
-    el = 2 if cfg.dtype == "bf16" else 4
-    load_bytes = sum(2 * cfg.n_layers * cfg.n_kv_heads * cfg.head_dim * el * (n + (n + 63) // 64 * 64)
-                     for n, _ in shapes)
+    load_bytes = sum(ctx_load_bytes(cfg, n) for n, _ in shapes)
     log(f"{name}: {reps} schedules in {dt:.3f} s")
     return {"workload": workload_text(cfg, shapes), "req_per_s": round(R * reps / dt, 1),
             "ms_per_schedule": round(1e3 * dt / reps, 3), "batched_steps": batch_sizes,
@@ -545,9 +556,7 @@ def decode_leg(cfg, args, per_layer: bool):
         del batch
         log(f"loaded {min(R, r0 + 8)}/{R} contexts ({time.time() - t:.1f} s)")
     torch.cuda.empty_cache()
-    el_load = 2 if cfg.dtype == "bf16" else 4
-    load_bytes = sum(2 * cfg.n_layers * cfg.n_kv_heads * cfg.head_dim * el_load * (n + G.gr_ctx_padded_len(n))
-                     for n, _ in shapes)
+    load_bytes = sum(ctx_load_bytes(cfg, n) for n, _ in shapes)
 
     # live beams per level, measured once
     n_live = np.zeros((R, lv), dtype=np.int64)

@@ -232,7 +232,12 @@ int32_t gr_ctx_padded_len(int32_t ctx_len);
  *              buffers must stay alive and unchanged until gr_request_release.
  *   k and v are 16-byte aligned in both cases.  Either way one pass over the
  *   context also takes, per (layer, kv head), the largest key norm and the
- *   largest |v| (bounds that the attention kernels use).
+ *   largest |v| (bounds that the attention kernels use).  A copy load of a bf16
+ *   model with head_dim 128 also keeps V^T as float16, in the units the wide
+ *   attention kernel computes in, so that kernel reads it without converting
+ *   (the pool then takes 3*L*Hkv*d*2 bytes per token, else 2*L*Hkv*d*dtype
+ *   size); adopted contexts are converted inside the kernel, with the same
+ *   result.
  * Errors: GR_E_INVALID_ARG (bad sizes, duplicate id, misaligned k or v),
  * GR_E_OUT_OF_MEMORY (no free slot or pool space), GR_E_BAD_STATE (workspace not
  * bound). */

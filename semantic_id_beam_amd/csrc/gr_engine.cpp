@@ -72,6 +72,7 @@ struct gr_engine {
   // context pool: padded tokens, first fit
   int64_t pool_tokens = 0;
   size_t pool_tok_bytes = 0;
+  bool v16 = false;  // loaded contexts also keep V^T as float16 for the eight-wave kernel (bf16, head_dim 128)
   std::map<int64_t, int64_t> pool_free;  // offset -> length
 
   struct Req {
@@ -82,6 +83,7 @@ struct gr_engine {
     bool adopt = false;
     int64_t pool_off = -1;
     const void *k = nullptr, *vt = nullptr;
+    const void *vt16 = nullptr;  // float16 copy of V^T (pool contexts of v16 engines), else null
   };
   std::unordered_map<int64_t, Req> reqs;
   std::vector<int> free_slots;
@@ -290,7 +292,8 @@ void layout(gr_engine *e) {
   w = align_up(w + e->h_child.size() * 4, A);
   e->off_slots = w;
   w = align_up(w + s.slot_bytes * (size_t)e->opts.max_requests, A);
-  e->pool_tok_bytes = (size_t)2 * d.L * d.Hkv * d.d * el;
+  e->v16 = d.dtype == 1 && d.d == 128;
+  e->pool_tok_bytes = (size_t)(e->v16 ? 3 : 2) * d.L * d.Hkv * d.d * el;
   e->pool_tokens = e->opts.max_ctx_tokens;
   e->off_pool = w;
   w = align_up(w + (size_t)e->pool_tokens * e->pool_tok_bytes, A);
@@ -700,6 +703,7 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
     uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
     R.k = dk;
     R.vt = dk + (size_t)e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
+    if (e->v16) R.vt16 = dk + (size_t)2 * e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
   }
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
@@ -725,11 +729,16 @@ gr_status gr_ctx_prefill(gr_engine *e, int64_t rid, const int32_t *tokens, int32
                        "prefill query")) != GR_OK)
       return q;
     // the context in the native layout, with its key-norm bounds and value scales
-    return check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, e->pf_tok_dev, N, Np, soft_pos,
-                                               part, L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
-                                               const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
-                                               (float *)(sb + e->sl.vscale), st),
-                     "prefill");
+    if ((q = check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, e->pf_tok_dev, N, Np, soft_pos,
+                                                 part, L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
+                                                 const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
+                                                 (float *)(sb + e->sl.vscale), st),
+                       "prefill")) != GR_OK)
+      return q;
+    return R.vt16 ? check_dev(e, gr::launch_load_v16(R.vt, const_cast<void *>(R.vt16), (float *)(sb + e->sl.vscale), L,
+                                                     Hkv, d, Np, st),
+                              "float16 V")
+                  : GR_OK;
   };
   if ((r = run()) != GR_OK) {
     if (!R.adopt) pool_free(e, R.pool_off, Np);
@@ -783,6 +792,7 @@ gr_status gr_ctx_prefill_noalloc(gr_engine *e, int64_t rid, const int32_t *token
     uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
     R.k = dk;
     R.vt = dk + (size_t)L * Hkv * Np * d * e->elem;
+    if (e->v16) R.vt16 = dk + (size_t)2 * L * Hkv * Np * d * e->elem;
   }
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
@@ -800,11 +810,16 @@ gr_status gr_ctx_prefill_noalloc(gr_engine *e, int64_t rid, const int32_t *token
                                                (float *)(sb + e->sl.knmax), (float *)(sb + e->sl.vscale), st),
                        "prefill query")) != GR_OK)
       return q;
-    return check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, tokens_dev, N, Np, soft_pos, part, L,
-                                               Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
-                                               const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
-                                               (float *)(sb + e->sl.vscale), st),
-                     "prefill");
+    if ((q = check_dev(e, gr::launch_prefill_ctx(e->elem, e->pf.tok_k, e->pf.tok_v, tokens_dev, N, Np, soft_pos, part,
+                                                 L, Hq, Hkv, d, e->pf.vocab, const_cast<void *>(R.k),
+                                                 const_cast<void *>(R.vt), (float *)(sb + e->sl.knmax),
+                                                 (float *)(sb + e->sl.vscale), st),
+                       "prefill")) != GR_OK)
+      return q;
+    return R.vt16 ? check_dev(e, gr::launch_load_v16(R.vt, const_cast<void *>(R.vt16), (float *)(sb + e->sl.vscale), L,
+                                                     Hkv, d, Np, st),
+                              "float16 V")
+                  : GR_OK;
   };
   gr_status r;
   if ((r = run()) != GR_OK) {
@@ -848,6 +863,7 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
     uint8_t *dk = e->ws + e->off_pool + (size_t)off * e->pool_tok_bytes;
     R.k = dk;
     R.vt = dk + (size_t)e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
+    if (e->v16) R.vt16 = dk + (size_t)2 * e->dm.L * e->dm.Hkv * Np * e->dm.d * e->elem;
   }
   R.slot = e->free_slots.back();
   uint8_t *sb = e->ws + e->off_slots + (size_t)R.slot * e->sl.slot_bytes;
@@ -855,7 +871,10 @@ gr_status gr_ctx_kv_load(gr_engine *e, int64_t rid, int32_t N, int32_t W, const 
   if ((r = check_dev(e, gr::launch_load_ctx(k, v, const_cast<void *>(R.k), const_cast<void *>(R.vt), !adopt,
                                             e->dm.L, e->dm.Hkv, N, Np, e->dm.d, e->elem, (float *)(sb + e->sl.knmax),
                                             (float *)(sb + e->sl.vscale), st),
-                     "context load")) != GR_OK) {
+                     "context load")) != GR_OK ||
+      (R.vt16 && (r = check_dev(e, gr::launch_load_v16(R.vt, const_cast<void *>(R.vt16), (float *)(sb + e->sl.vscale),
+                                                       e->dm.L, e->dm.Hkv, e->dm.d, Np, st),
+                                "float16 V")) != GR_OK)) {
     if (!adopt) pool_free(e, R.pool_off, Np);
     return r;
   }
@@ -1027,6 +1046,7 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       std::memset(&w, 0, sizeof(w));
       w.ctx_k = R->k;
       w.ctx_vt = R->vt;
+      w.ctx_vt16 = R->vt16;
       w.ctx_lstride = (int64_t)d.Hkv * R->Np * d.d;
       w.N = R->N;
       w.Np = R->Np;

@@ -92,6 +92,7 @@ struct Dev {
 struct StepReq {
   const void *ctx_k;    // native K [L][Hkv][Np][d]
   const void *ctx_vt;   // native V^T [L][Hkv][d][Np]
+  const void *ctx_vt16; // its float16 copy (launch_load_v16), or null: the wide kernel converts V^T itself
   int64_t ctx_lstride;  // elements per layer = Hkv*Np*d
   int N, Np;
   int slot, level, W;
@@ -169,6 +170,12 @@ hipError_t launch_gather_results(const Dev &dev, const int32_t *slots, int n, in
 // scale, the power of two 2^e with max |v| < 2^e over the first N tokens -> vscale [L][Hkv].
 hipError_t launch_load_ctx(const void *src_k, const void *src_v, void *nk, void *nvt, bool copy, int L, int Hkv,
                            int N, int Np, int d, int elem_bytes, float *knmax, float *vscale, hipStream_t st);
+// The float16 copy of a bf16 context's V^T that the eight-wave attention kernel reads: nvt16
+// [L][Hkv][d][Np] = float16 of v in the units that kernel computes in (v / vscale, or v itself
+// when the head's vscale lies in [2^-10, 2^15]), the same rounding as its in-LDS conversion.
+// It must follow the launch that wrote vscale, on the same stream.
+hipError_t launch_load_v16(const void *nvt, void *nvt16, const float *vscale, int L, int Hkv, int d, int Np,
+                           hipStream_t st);
 // Prefill (gr_prefill.hip).  Soft token: e = u * proj [du][de] as kSoftSplit partial sums
 // over the user vector in e_buf [kSoftSplit][de], then the
 // per-layer projections of e in kSoftSplit partial sums over the embedding dimension,

@@ -942,6 +942,15 @@ __device__ __forceinline__ void wide_store_layer(const Dev &dev, const StepReq &
 // state, and o/l is stored as the layer's float32 hidden partial (k_sum_hparts adds the layers
 // in order at the end).  Otherwise: one layer, one token range, split partials out, and the
 // previous layer finished in the prologue when the step defers it.
+// Units of V in the eight-wave kernel's float16 PV: with the head's values between 2^-11 and
+// 2^15 in magnitude (vscale = 2^e above max|v| in [2^-10, 2^15]) float16 of v itself is exact
+// for |v| >= 2^-14 and within 2^-25 below, so v is taken as it is (raw); otherwise in units of
+// vscale.  Returns the factor v is multiplied by (1, or 1/vscale: exact, a power of two).
+__device__ __forceinline__ float v16_factor(float vsc, bool &raw) {
+  raw = vsc >= 0x1p-10f && vsc <= 0x1p15f;
+  return raw ? 1.f : 1.f / vsc;
+}
+
 template <bool LAYERED>
 __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                        int layer_arg) {
@@ -989,15 +998,16 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const int nsub = (t1 - t0 + 31) / 32;
   const int layer = layer_arg + (LAYERED ? sp : 0);
   if (layer >= dm.L) return;  // past the last layer of the last launch
+  // V^T as float16 in the kernel's units when the context has that copy (v16), else bf16
+  // converted in LDS after each tile lands
+  const bool v16 = R.ctx_vt16 != nullptr;  // uniform
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
-  const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
-  // with the head's values between 2^-11 and 2^15 in magnitude (vscale = 2^e above max|v| in
-  // [2^-10, 2^15]) float16 of v itself is exact for |v| >= 2^-14 and within 2^-25 below, so the
-  // scaling is skipped; otherwise V is taken in units of vscale
+  const uint16_t *gV = (const uint16_t *)(v16 ? R.ctx_vt16 : R.ctx_vt) + (size_t)layer * R.ctx_lstride +
+                       (size_t)h * D * R.Np;
   const float vsc = ((const float *)(slot + dev.sl.vscale))[layer * dm.Hkv + h];
-  const bool vraw = vsc >= 0x1p-10f && vsc <= 0x1p15f;
+  bool vraw;
+  const float ivs = v16_factor(vsc, vraw);
   const float vs = vraw ? 1.f : vsc;
-  const float ivs = 1.f / vs;  // exact: vs is a power of two
 
   // per-lane DMA sources (elements from the tile's first token) for this wave's chunks
   uint32_t koff[KI], voff[VI];
@@ -1173,7 +1183,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     if (T + 2 < ntiles) vm_lgkm_wait_barrier<LPT>();
     else vm_lgkm_wait_barrier<0>();
     if (T + 3 < ntiles) issue(T + 3);
-    if (T + 1 < ntiles) convert_v(T + 1);
+    if (!v16 && T + 1 < ntiles) convert_v(T + 1);
   };
 
   {
@@ -1229,9 +1239,11 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  convert_v(0);
-  if (ntiles > 1) convert_v(1);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (!v16) {
+    convert_v(0);
+    if (ntiles > 1) convert_v(1);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
 
   // s0 holds the scores of even sub-tiles, s1 of odd ones
   f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
@@ -2760,6 +2772,25 @@ __global__ void k_load_init(uint32_t *kn_bits, uint32_t *vm_bits, int n) {
 
 // In place: kn = sqrt(largest squared key norm); vs = 2^e with max|v| < 2^e (frexp: max|v| =
 // m 2^e, m in [0.5, 1)), kept a normal float.
+// V^T [L][Hkv][d][Np] bf16 -> its float16 copy in the wide kernel's units (v16_factor), one
+// 16-byte chunk per thread; grid (chunks of one (layer, kv head), L*Hkv).
+__global__ __launch_bounds__(256) void k_load_v16(const u32x4_t *__restrict__ vt, u32x4_t *__restrict__ vt16,
+                                                  const float *__restrict__ vscale, int chunks) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const size_t i = (size_t)blockIdx.y * chunks + c;
+  bool raw;
+  const float f = v16_factor(vscale[blockIdx.y], raw);
+  const u32x4_t x = vt[i];
+  u32x4_t y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = __uint_as_float(x[e] << 16), b = __uint_as_float(x[e] & 0xFFFF0000u);
+    y[e] = raw ? pack_f16(a, b) : pack_f16(a * f, b * f);
+  }
+  vt16[i] = y;
+}
+
 __global__ void k_load_finish(float *kn, float *vs, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -2961,6 +2992,15 @@ hipError_t launch_topk_select(const float *cand, int n_rows, int V, int k, int32
   else
     hipLaunchKernelGGL(k_topk_select<false>, dim3(1), dim3(kTopkThreads), 0, st, cand, n_rows, V, k, out_flat,
                        out_score, n_out_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_load_v16(const void *nvt, void *nvt16, const float *vscale, int L, int Hkv, int d, int Np,
+                           hipStream_t st) {
+  if (Np % kLoadTile != 0 || Np < kLoadTile || d != 128 || L < 1 || Hkv < 1) return hipErrorInvalidValue;
+  const int chunks = d * Np / 8;  // 16-byte chunks of one (layer, kv head)
+  hipLaunchKernelGGL(k_load_v16, dim3((unsigned)((chunks + 255) / 256), (unsigned)(L * Hkv)), dim3(256), 0, st,
+                     (const u32x4_t *)nvt, (u32x4_t *)nvt16, vscale, chunks);
   return hipGetLastError();
 }
 

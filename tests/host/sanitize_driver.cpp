@@ -32,6 +32,7 @@ GR_STUB(launch_init_slots, const Dev &, const int32_t *, int, hipStream_t)
 GR_STUB(launch_gather_results, const Dev &, const int32_t *, int, int, uint8_t *, size_t, hipStream_t)
 GR_STUB(launch_load_ctx, const void *, const void *, void *, void *, bool, int, int, int, int, int, int, float *,
         float *, hipStream_t)
+GR_STUB(launch_load_v16, const void *, void *, const float *, int, int, int, int, hipStream_t)
 GR_STUB(launch_topk_select, const float *, int, int, int, int32_t *, float *, int32_t *, hipStream_t)
 GR_STUB(launch_soft_token, const float *, const float *, int, int, const float *, const float *, const float *, int,
         int, int, float *, float *, hipStream_t)
