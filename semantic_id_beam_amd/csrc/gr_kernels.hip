@@ -1198,11 +1198,11 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     u32x4_t qr[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
-    // tiles 0 and 1, in flight with the query; once both have landed (with the query) tiles
-    // 2 and 3 go out: at the start of a launch every workgroup waits only for its first two
-    // tiles, not for the whole chip's first four
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
+    // the tiles the prologue needs in flight with the query (tile 0, and tile 1 when its V^T is
+    // converted here); the rest of the ring's tiles once those have landed: at the start of a
+    // launch every workgroup waits only for its first tiles, not for the whole chip's first four
+    const int first = v16 ? 1 : 2;
+    for (int k = 0; k < first; ++k)
       if (k < ntiles) issue(k);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -1210,8 +1210,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
       asm volatile("" ::"v"(qf[kb]));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int k = 2; k < NST - 1; ++k)
+    for (int k = first; k < NST - 1; ++k)
       if (k < ntiles) issue(k);
   }
   if (LAYERED && s > 0) {
@@ -1232,9 +1231,12 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     finish_share(row0, min(rows, row0 + NW * 32) - row0, R.splits, sp, 2 * NT / (D / 8), r0, r1);
     finish_rows<D, 2>(dev, R, slot, layer - 1, h, r0, r1, tid, NT);
   }
-  // every wave's tiles 0 and 1 have landed (tiles 2 and 3 may be in flight; after prologue
-  // work with memory accesses of its own, everything is waited for, so that the ring's waits
-  // count copies only) and are converted here, every later one in advance()
+  // every wave's first tiles have landed (tile 0, and tile 1 when it is converted here; the
+  // later ones may be in flight; after prologue work with memory accesses of its own,
+  // everything is waited for, so that the ring's waits count copies only); the barrier makes
+  // every wave's copies visible.  Tiles 0 and 1 are converted here (without the float16 copy),
+  // every later one in advance(); tile 1 is in LDS by the first advance() (which waits for tile
+  // 2), before sub-tile 2 reads it
   if (LAYERED ? s > 0 : layer > 0 && R.defer_finish)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else
