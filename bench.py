@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # measured (the several-layers-per-launch variant), the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "fa679ef59286d6a4305eb145acf0727e73cb421b0c69e95e9008f5cfcdb77dcf",
-    "per_layer": {"k_ctx_attn_wide": {"read": 168611021, "written": 34078822},
-                  "k_ctx_attn_stream": {"read": 165741158, "written": 540672}},
+    "source_sha256": "a29cdfb0cef74ca106f7d688928e069d20ba8dce8504e61ea0486a65db9a5da1",
+    "per_layer": {"k_ctx_attn_wide": {"read": 168459059, "written": 34080666},
+                  "k_ctx_attn_stream": {"read": 165722726, "written": 540672}},
 }
 
 
