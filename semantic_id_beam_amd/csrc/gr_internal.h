@@ -135,7 +135,7 @@ hipError_t launch_beam_merge(const Dev &dev, const StepReq *reqs, int n_reqs, in
 // past the step's first request.
 hipError_t launch_finish_layer(const Dev &dev, const StepReq *reqs, int n_reqs, int layer, int total_wgs,
                               hipStream_t st, LaunchEv ev = {}, int wg0 = 0);
-inline int fin_rows_per_wg(int d) { return 2 * 256 / (d / 8); }
+inline int fin_rows_per_wg(int d) { return 256 / (d / 8); }
 // A first-level step of head_dim-128 bf16 requests with every layer in one launch (grid
 // [total_wgs][L], partials of layer l at row offset l*Hkv*splits*rows_b of buffer 0), and its
 // finish: per-layer outputs into buffer 1, then h = sum over layers in order.

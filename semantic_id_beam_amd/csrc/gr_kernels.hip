@@ -1758,13 +1758,15 @@ __global__ __launch_bounds__(256) void k_beam_merge(Dev dev, const StepReq *__re
 }
 
 // Finish of one layer of a split-K step of a bf16 model as a launch of its own (the merge that
-// otherwise runs in the next layer's prologue): workgroup (request, 32- or 64-row block, kv
-// head), finish_rows with two elements per thread (BeamKV append, the beam's own tokens, the
-// split merge in split order, h += o).
+// otherwise runs in the next layer's prologue): workgroup (request, 16- or 32-row block, kv
+// head), finish_rows with one element per thread (BeamKV append, the beam's own tokens, the
+// split merge in split order, h += o).  Its time is the round trips of its dependent loads;
+// many small workgroups keep more of them in flight (one element per thread: 13.6 us per
+// layer of the 256-beam headline, two: 16.0).
 template <int D>
 __global__ __launch_bounds__(256) void k_finish_layer(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                       int layer, int wg0) {
-  constexpr int RPW = 2 * 256 / (D / 8);  // rows per workgroup
+  constexpr int RPW = 256 / (D / 8);  // rows per workgroup
   const int bid = (int)blockIdx.x + wg0;
   const StepReq R = reqs[find_req<4>(reqs, n_reqs, bid)];
   const Dims &dm = dev.dm;
@@ -1773,7 +1775,7 @@ __global__ __launch_bounds__(256) void k_finish_layer(Dev dev, const StepReq *__
   uint8_t *slot = slot_base(dev, R.slot);
   const int rows = ((const int *)(slot + dev.sl.n_live))[R.level & 1] * dm.g;
   if (r0 >= rows) return;
-  finish_rows<D, 2>(dev, R, slot, layer, kv, r0, min(rows, r0 + RPW), (int)threadIdx.x, 256);
+  finish_rows<D, 1>(dev, R, slot, layer, kv, r0, min(rows, r0 + RPW), (int)threadIdx.x, 256);
 }
 
 // Finish of a first-level step whose layers ran in one launch (k_ctx_attn_stream<.., true>).
