@@ -1067,6 +1067,14 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       if (first_fused) S = std::max(1, std::min<int>(S, (int)((int64_t)d.S_max * d.W_max * d.g / ((int64_t)d.L * rows))));
       int tps = (int)align_up((size_t)ceil_div(R->N, S), gr::kTileTok);
       S = ceil_div(R->N, tps);
+      if (S > 1) {
+        // the last range takes the rest: of the two tile multiples around N/S, the one whose
+        // longest range has fewer 32-token sub-tiles (5000 tokens in two: 2496 + 2504, not
+        // 2560 + 2440), each range keeping at least two tiles
+        const int lo = R->N / S / gr::kTileTok * gr::kTileTok;
+        auto longest = [&](int t) { return std::max(ceil_div(t, 32), ceil_div(R->N - (int64_t)(S - 1) * t, 32)); };
+        if (lo >= 2 * gr::kTileTok && longest(lo) < longest(tps)) tps = lo;
+      }
       w.splits = S;
       w.tps = tps;
       w.lgroups = lgroups;

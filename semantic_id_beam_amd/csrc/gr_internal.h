@@ -98,7 +98,8 @@ struct StepReq {
   int slot, level, W;
   int n_bound;          // upper bound of n_s known on the host (device holds the exact n_s)
   int rows_b;           // n_bound * g: row stride of the split-K partials
-  int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64)
+  int splits, tps;      // split-K: number of token ranges, tokens per range (multiple of 64); range
+                        // sp covers [sp*tps, (sp+1)*tps), the last one [(splits-1)*tps, N)
   int lgroups;          // full-context steps: layers per launch (else 0)
   int defer_finish;     // split-K steps: layer l is finished inside layer l+1's launch (else by a merge
                         // launch after each layer)

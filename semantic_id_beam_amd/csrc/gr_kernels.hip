@@ -247,7 +247,7 @@ __device__ __forceinline__ void ctx_attn_body(const Dev &dev, const StepReq *__r
   }
 
   const int t0 = sp * R.tps;
-  const int t1 = min(R.N, t0 + R.tps);
+  const int t1 = (sp == R.splits - 1 ? R.N : t0 + R.tps);
   const int ntiles = (t1 - t0 + TT - 1) / TT;
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_stream(Dev dev, const Step
   const bool row_ok = q_row < rows;
 
   const int t0 = LAYERED ? 0 : sp * R.tps;
-  const int t1 = LAYERED ? R.N : min(R.N, t0 + R.tps);
+  const int t1 = LAYERED ? R.N : (sp == R.splits - 1 ? R.N : t0 + R.tps);
   const int ntiles = (t1 - t0 + TT - 1) / TT;
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
@@ -993,7 +993,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const bool row_ok = q_row < rows;
 
   const int t0 = LAYERED ? 0 : sp * R.tps;
-  const int t1 = LAYERED ? R.N : min(R.N, t0 + R.tps);
+  const int t1 = LAYERED ? R.N : (sp == R.splits - 1 ? R.N : t0 + R.tps);
   const int ntiles = (t1 - t0 + TT - 1) / TT;
   const int nsub = (t1 - t0 + 31) / 32;
   const int layer = layer_arg + (LAYERED ? sp : 0);
@@ -1339,7 +1339,7 @@ __global__ __launch_bounds__(256) void k_ctx_attn_f32(Dev dev, const StepReq *__
   }
   const float *gK = (const float *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const float *gV = (const float *)R.ctx_vt + (size_t)layer * R.ctx_lstride + (size_t)h * D * R.Np;
-  const int t0 = sp * R.tps, t1 = min(R.N, t0 + R.tps);
+  const int t0 = sp * R.tps, t1 = (sp == R.splits - 1 ? R.N : t0 + R.tps);
   const float c2 = dm.scale_log2;
   float M = kNegInf, l = 0.f, o[DPL];
 #pragma unroll
