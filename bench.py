@@ -424,7 +424,35 @@ def chain_leg(args, name: str = "chain_ctx5k_beam256_r8", reps: int = 5):
             "attn_TFLOPs": round(attn_flops / (a_ms * 1e-3) / 1e12, 1),
             "finish_ms": round(prof["finish"][s_][0] / reps, 3), "norm_ms": round(prof["norm"][s_][0] / reps, 3),
             "logits_topk_ms": round((prof["logits"][s_][0] + prof["topk"][s_][0]) / reps, 3)}
+    out["library_reference"] = gemm_library_reference(int(n_live[:, -1].sum()), D, Dkv, I)
     log(f"chain: {out['req_per_s']} req/s, {out['ms_per_decode']} ms per decode")
+    return out
+
+
+def gemm_library_reference(rows, D, Dkv, I, reps: int = 50):
+    """Context for the chain's projections, not part of the path: torch.matmul (hipBLASLt) on the
+    same bf16 shapes (rows x out x in), each timed back to back with warm caches."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {"note": "torch.matmul (hipBLASLt) on the projection shapes, back to back; context only"}
+    for name, n, k in (("qkv", D + 2 * Dkv, D), ("o", D, D), ("gate_up", 2 * I, D), ("down", D, I)):
+        a = torch.randn(rows, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        w = torch.randn(n, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(5):
+            c = a @ w.t()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            c = a @ w.t()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = 2.0 * rows * n * k / (us * 1e-6) / 1e12
+        out[name] = {"shape": [rows, n, k], "us": round(us, 2), "TFLOPs": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del a, w, c
+    torch.cuda.empty_cache()
     return out
 
 

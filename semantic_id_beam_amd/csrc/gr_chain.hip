@@ -159,13 +159,15 @@ __global__ __launch_bounds__(256) void k_chain_final(Dev dev, const StepReq *__r
 }
 
 // ---------------------------------------------------------------------------------------- GEMM
-// Workgroup: 256 threads, four waves in 2 x 2 over a 128 (rows) x 2*WN (weight rows) tile; wave
-// (wm, wn) owns 64 x WN as 2 x (WN/32) MFMA blocks (WN = 128 for the wide projections: six
-// fragment reads per eight MFMAs).  The K loop takes 64 columns per stage: the stage's A tile
-// (16 KB) and W tile (WN/2 KB) go from global memory straight into LDS (global_load_lds_dwordx4,
-// 1 KB of consecutive LDS per wave instruction), a ring of three stages with two in flight and
-// one barrier per stage (4 k-steps of 16, 8 * (WN/32) MFMAs per wave between barriers); each
-// k-step's fragments are read while the previous k-step's MFMAs run.  LDS rows are 128 bytes
+// Workgroup: 2 x NWN waves over a 128 (rows) x NWN*WN (weight rows) tile; wave (wm, wn) owns
+// 64 x WN as 2 x (WN/32) MFMA blocks.  The 256-row tiles of the wide projections run eight waves
+// of 64 x 64 (two waves per SIMD; the 128 x 128 tiles four of 64 x 64): against four waves of
+// 64 x 128, the gate/up and q/k/v projections at 2,048 rows took about 4 % less time.  The K
+// loop takes 64 columns per stage: the stage's A tile (16 KB) and W tile (BN/8 KB) go from
+// global memory straight into LDS (global_load_lds_dwordx4, 1 KB of consecutive LDS per wave
+// instruction), a ring of three stages with two in flight and one barrier per stage (4 k-steps
+// of 16 between barriers); each k-step's fragments are read while the previous k-step's MFMAs
+// run.  LDS rows are 128 bytes
 // (8 chunks of 16): chunk c of row r sits at c ^ (r & 7) ^ ((r >> 3) & 1), so each group of 16
 // lanes (16 rows, one chunk each) covers the 64 banks once.  The MFMA computes the transposed
 // block D[n][m] = W_blk (32 x 16) x A_blk^T (16 x 32): lane (m, hh) then holds output row m,
@@ -173,6 +175,7 @@ __global__ __launch_bounds__(256) void k_chain_final(Dev dev, const StepReq *__r
 // row.
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 constexpr int GBM = 128, GBK = 64, GNST = 3;
+constexpr int kWideNWN = 4;  // waves along the weight rows of a 256-row tile
 
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
@@ -221,18 +224,22 @@ __device__ __forceinline__ const uint16_t *w_row(const GemmArgs &g, int n0, int 
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 0 || N == 8 || N == 12, "unsupported wait");
+  else static_assert(N == 0 || N == 4 || N == 6 || N == 8 || N == 12, "unsupported wait");
 }
 
-template <int EPI, int WN>
-__global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs, GemmArgs g,
-                                              int m_tiles) {
-  constexpr int BN = 2 * WN;                            // weight rows per tile
-  constexpr int NB = WN / 32;                           // MFMA blocks along the weight rows per wave
-  constexpr int AI = GBM * 8 / 256, WI = BN * 8 / 256;  // DMA instructions per lane and stage
-  static_assert(GNST == 3 && (WN == 64 || WN == 128), "tile shape");
+template <int EPI, int WN, int NWN>
+__global__ __launch_bounds__(128 * NWN) void k_gemm(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                    GemmArgs g, int m_tiles) {
+  constexpr int NW = 2 * NWN;                                     // waves: 2 along rows x NWN
+  constexpr int BN = NWN * WN;                                    // weight rows per tile
+  constexpr int NB = WN / 32;                                     // MFMA blocks along the weight rows per wave
+  constexpr int AI = GBM * 8 / (64 * NW), WI = BN * 8 / (64 * NW);  // DMA instructions per lane and stage
+  static_assert(GNST == 3 && (WN == 32 || WN == 64 || WN == 128) && (BN == 128 || BN == 256), "tile shape");
+  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0, "a wave holds gate and up blocks in pairs");
   __shared__ bf16x8_t sA[GNST][GBM * 8];
   __shared__ bf16x8_t sW[GNST][BN * 8];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
@@ -256,27 +263,27 @@ __global__ __launch_bounds__(256) void k_gemm(Dev dev, const StepReq *__restrict
   const int m0 = mt * GBM, n0 = nt * BN;
   const int KT = g.K / GBK / g.ksplit, k0 = ks * KT * GBK;
 
-  // DMA: instruction i of wave w fills LDS chunks p = (i * 4 + w) * 64 + lane: row p >> 3, stored
+  // DMA: instruction i of wave w fills LDS chunks p = (i * NW + w) * 64 + lane: row p >> 3, stored
   // position p & 7 <- global chunk (p & 7) ^ swz(row); the 8 rows of one instruction lie in one
   // 32-row weight block
   const uint16_t *asrc[AI], *wsrc[WI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
+    const int p = (i * NW + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
     asrc[i] = g.A + (size_t)(m0 + r) * g.K + k0 + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
+    const int p = (i * NW + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ swz(r);
     wsrc[i] = w_row<EPI>(g, n0, r) + k0 + c * 8;
   }
   const uint32_t adst = lds_addr(&sA[0][0]) + w * 1024, wdst = lds_addr(&sW[0][0]) + w * 1024;
   auto issue = [&](int kt) {
     const int st = kt % GNST;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * 128) + i * 4096);
+    for (int i = 0; i < AI; ++i) dma16(asrc[i] + kt * GBK, adst + st * (GBM * 128) + i * NW * 1024);
 #pragma unroll
-    for (int i = 0; i < WI; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (BN * 128) + i * 4096);
+    for (int i = 0; i < WI; ++i) dma16(wsrc[i] + kt * GBK, wdst + st * (BN * 128) + i * NW * 1024);
   };
 
   f32x16_t acc[NB][2];
@@ -558,14 +565,15 @@ hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, in
   g.part = c.part;
   const dim3 grid((unsigned)(tiles * g.ksplit));
   const LaunchEv e1{ev.start, g.ksplit > 1 ? nullptr : ev.stop};
-  auto go = [&](auto wn) {
-    constexpr int WN = decltype(wn)::value;
-    if (epi == EPI_QKV) launch(k_gemm<EPI_QKV, WN>, grid, dim3(256), st, e1, dev, reqs, n_reqs, g, m_tiles);
-    else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID, WN>, grid, dim3(256), st, e1, dev, reqs, n_reqs, g, m_tiles);
-    else launch(k_gemm<EPI_SWIGLU, WN>, grid, dim3(256), st, e1, dev, reqs, n_reqs, g, m_tiles);
+  auto go = [&](auto wn, auto nwn) {
+    constexpr int WN = decltype(wn)::value, NWN = decltype(nwn)::value;
+    const dim3 blk(128 * NWN);
+    if (epi == EPI_QKV) launch(k_gemm<EPI_QKV, WN, NWN>, grid, blk, st, e1, dev, reqs, n_reqs, g, m_tiles);
+    else if (epi == EPI_RESID) launch(k_gemm<EPI_RESID, WN, NWN>, grid, blk, st, e1, dev, reqs, n_reqs, g, m_tiles);
+    else launch(k_gemm<EPI_SWIGLU, WN, NWN>, grid, blk, st, e1, dev, reqs, n_reqs, g, m_tiles);
   };
-  if (wide) go(std::integral_constant<int, 128>{});
-  else go(std::integral_constant<int, 64>{});
+  if (wide) go(std::integral_constant<int, 256 / kWideNWN>{}, std::integral_constant<int, kWideNWN>{});
+  else go(std::integral_constant<int, 64>{}, std::integral_constant<int, 2>{});
   if (g.ksplit > 1) {
     const LaunchEv e2{nullptr, ev.stop};
     if (epi == EPI_QKV) launch(k_gemm_reduce<EPI_QKV>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
