@@ -985,6 +985,17 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
   layered = layered && fill >= 0.75;
   if (layered)
     for (int i = 0; i < n; ++i) kind[(size_t)i] = full_ctx_kind(kind[(size_t)i]);
+  // a split-K step of first-level requests only (one beam each, head_dim 128) runs on the
+  // 8-wave kernel too: its 64-token tiles fetch whole 128-byte lines of V^T, and a quarter of
+  // the ranges halves the merge (headline level 0, same box: 37.5 against 38.2 us per layer,
+  // layer finish 13.2 against 13.7 us); steps that mix levels keep the one-wave kernel in a
+  // group of its own
+  if (!layered && !first_fused && d.dtype == 1 && d.d == 128) {
+    bool all_first = true;
+    for (int i = 0; i < n; ++i) all_first = all_first && rs[(size_t)i]->level == 0 && (kind[(size_t)i] & 0xFF) == 1;
+    if (all_first)
+      for (int i = 0; i < n; ++i) kind[(size_t)i] = 8;
+  }
   bool any_hparts = false;
   // split-K steps of bf16 models finish layer l inside the launch of layer l+1 (the model
   // stand-in's layers do not read each other's output); with one layer per launch every layer
