@@ -106,18 +106,28 @@ __device__ __forceinline__ float row16_sum(float v) {
   return dpp_add<0x140>(v);  // row_mirror
 }
 
-// Workgroup -> request: reqs[] is ordered by each first-workgroup field.
+// Workgroup -> request: reqs[] is ordered by each first-workgroup field.  Up to 8 requests, the
+// fields of requests 1..7 are loaded at once (one round trip instead of a binary search's three);
+// more, a binary search.
+template <int FIELD>
+__device__ __forceinline__ int req_first(const StepReq &r) {
+  return FIELD == 0 ? r.wg_ctx : FIELD == 1 ? r.wg_merge : FIELD == 2 ? r.wg_logits : FIELD == 3 ? r.wg_lsm : r.wg_fin;
+}
 template <int FIELD>
 __device__ __forceinline__ int find_req(const StepReq *reqs, int n, int bid) {
+  if (n <= 8) {
+    int f[7];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) f[i - 1] = req_first<FIELD>(reqs[min(i, n - 1)]);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) cnt += (i < n && f[i - 1] <= bid) ? 1 : 0;
+    return cnt;
+  }
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int first = FIELD == 0   ? reqs[mid].wg_ctx
-                      : FIELD == 1 ? reqs[mid].wg_merge
-                      : FIELD == 2 ? reqs[mid].wg_logits
-                      : FIELD == 3 ? reqs[mid].wg_lsm
-                                   : reqs[mid].wg_fin;
-    if (first <= bid) lo = mid; else hi = mid - 1;
+    if (req_first<FIELD>(reqs[mid]) <= bid) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -951,6 +961,28 @@ __device__ __forceinline__ float v16_factor(float vsc, bool &raw) {
   return raw ? 1.f : 1.f / vsc;
 }
 
+// Loads of a beam code and of the live-beam count, then the four copies of a wave's share of a
+// tile (two K, two V^T chunks of 1 KB), and a wait for the two loads only (vmcnt counts
+// outstanding vector memory operations, which complete in issue order): one block, so the two
+// results are complete when it ends and the compiler, which does not see the copies, keeps no
+// wait of its own on them.  The copies are waited for by the caller.
+__device__ __forceinline__ void idx_and_tile0(const uint32_t *code_p, const int *nl_p, const uint16_t *k0,
+                                              const uint16_t *k1, const uint16_t *v0, const uint16_t *v1,
+                                              uint32_t lk0, uint32_t lk1, uint32_t lv0, uint32_t lv1,
+                                              uint32_t &code, uint32_t &nl) {
+  asm volatile(
+      "global_load_dword %0, %2, off\n\t"
+      "global_load_dword %1, %3, off\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, off\n\t"
+      "s_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, off\n\t"
+      "s_mov_b32 m0, %10\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, off\n\t"
+      "s_mov_b32 m0, %11\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, off\n\t"
+      "s_waitcnt vmcnt(4)"
+      : "=&v"(code), "=&v"(nl)
+      : "v"(code_p), "v"(nl_p), "v"(k0), "v"(k1), "v"(v0), "v"(v1), "s"(lk0), "s"(lk1), "s"(lv0), "s"(lv1)
+      : "memory", "m0");
+}
+
 template <bool LAYERED>
 __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
                                                        int layer_arg) {
@@ -958,16 +990,26 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   constexpr int KCH = TT * D / 8, VCH = D * TT / 8;  // 16-byte chunks per stage
   constexpr int KI = KCH / NT, VI = VCH / NT;        // DMA instructions per wave and tile
   constexpr int LPT = KI + VI;
-  static_assert(LPT == 4, "wait immediates assume four copies per lane and tile");
+  static_assert(LPT == 4 && KI == 2 && VI == 2, "wait immediates assume four copies per lane and tile");
   static_assert(TT == kTileTok, "tiles never cross the zero-padded end of the context");
   __shared__ bf16x8_t sK[NST][KCH];   // [token row swap23(r)][column c ^ (row & 15)]
   __shared__ u32x4_t sV[NST][VCH];    // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
   const int kx = lane & 15, vx = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of this lane's operand row
+  // the model's and then the descriptor's fields that the prologue reads, in SGPRs at once (the
+  // first with the request lookup's own loads): a round trip each, not a chain of loads each
+  // behind the branch that first needs it
+  const Dims &dm = dev.dm;
+  asm volatile("" ::"s"(dm.L), "s"(dm.Hq), "s"(dm.Hkv), "s"(dm.g), "s"(dm.levels), "s"(dm.V), "s"(dm.W_max),
+               "s"(dm.chain), "s"(dm.tl), "s"(dm.scale_log2), "s"(dev.slots), "s"(dev.sl.slot_bytes),
+               "s"(dev.sl.n_live), "s"(dev.sl.codes[0]), "s"(dev.sl.codes[1]), "s"(dev.sl.vscale),
+               "s"(dev.sl.q_last), "s"(dev.tok_q), "s"(dev.ch.q));
   const int ri = find_req<0>(reqs, n_reqs, blockIdx.x);
   const StepReq R = reqs[ri];
-  const Dims &dm = dev.dm;
+  asm volatile("" ::"s"(R.ctx_k), "s"(R.ctx_vt), "s"(R.ctx_vt16), "s"(R.ctx_lstride), "s"(R.N), "s"(R.Np),
+               "s"(R.slot), "s"(R.level), "s"(R.rows_b), "s"(R.splits), "s"(R.tps), "s"(R.lgroups),
+               "s"(R.defer_finish), "s"(R.row0), "s"(R.row_blocks), "s"(R.wg_ctx));
   const int local = blockIdx.x - R.wg_ctx;
   const int rest = local >> 3;
   const int rb = rest % R.row_blocks;
@@ -984,17 +1026,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   // the row's beam j, query head hq and latest code (its query token at steps s >= 1), and
   // the BeamKV slots of its older tokens: loaded before the live-beam count is known
   const int j_row = q_row / dm.g, gi_row = q_row % dm.g, hq_row = h * dm.g + gi_row;
-  const BeamIdx bi = load_beam_idx<LAYERED>(dev, slot, s, j_row);
-  const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
-  const int rows = n_live * dm.g;
-  if (row0 >= rows) return;  // whole workgroup idle
-
-  const bool wave_active = wrow < rows;  // an idle wave still copies and converts its share
-  const bool row_ok = q_row < rows;
 
   const int t0 = LAYERED ? 0 : sp * R.tps;
   const int t1 = LAYERED ? R.N : (sp == R.splits - 1 ? R.N : t0 + R.tps);
-  const int ntiles = (t1 - t0 + TT - 1) / TT;
+  const int ntiles = (t1 - t0 + TT - 1) / TT;  // at least one
   const int nsub = (t1 - t0 + 31) / 32;
   const int layer = layer_arg + (LAYERED ? sp : 0);
   if (layer >= dm.L) return;  // past the last layer of the last launch
@@ -1004,10 +1039,6 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   const uint16_t *gK = (const uint16_t *)R.ctx_k + (size_t)layer * R.ctx_lstride + (size_t)h * R.Np * D;
   const uint16_t *gV = (const uint16_t *)(v16 ? R.ctx_vt16 : R.ctx_vt) + (size_t)layer * R.ctx_lstride +
                        (size_t)h * D * R.Np;
-  const float vsc = ((const float *)(slot + dev.sl.vscale))[layer * dm.Hkv + h];
-  bool vraw;
-  const float ivs = v16_factor(vsc, vraw);
-  const float vs = vraw ? 1.f : vsc;
 
   // per-lane DMA sources (elements from the tile's first token) for this wave's chunks
   uint32_t koff[KI], voff[VI];
@@ -1032,6 +1063,36 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
 #pragma unroll
     for (int i = 0; i < VI; ++i) dma16(vb + voff[i], vdst + st * (VCH * 16) + i * 1024);
   };
+  // the row's beam index and the live-beam count; per-layer launches load them with tile 0's
+  // copies right behind, waiting for the two loads only, so the query gather that depends on
+  // them overlaps the tile's fetch
+  BeamIdx bi;
+  int n_live;
+  if constexpr (LAYERED) {
+    bi = load_beam_idx<true>(dev, slot, s, j_row);
+    n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
+  } else {
+    const int jj = min(j_row, dm.W_max - 1);
+    const size_t codes = (s & 1) ? dev.sl.codes[1] : dev.sl.codes[0];  // both in SGPRs already
+    const uint32_t *cp = (const uint32_t *)(slot + codes) + jj * dm.levels + max(s - 1, 0);
+    uint32_t code, nl;
+    idx_and_tile0(cp, (const int *)(slot + dev.sl.n_live) + (s & 1), gK + t0 * D + koff[0], gK + t0 * D + koff[1],
+                  gV + t0 + voff[0], gV + t0 + voff[1], kdst, kdst + 1024, vdst, vdst + 1024, code, nl);
+    bi.code = s > 0 ? code : 0u;
+    bi.anc0 = 0u;
+    n_live = __builtin_amdgcn_readfirstlane((int)nl);
+  }
+  const int rows = n_live * dm.g;
+  if (row0 >= rows) {  // whole workgroup idle; tile 0 lands before the LDS is released
+    if (!LAYERED) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+  const bool wave_active = wrow < rows;  // an idle wave still copies and converts its share
+  const bool row_ok = q_row < rows;
+  const float vsc = ((const float *)(slot + dev.sl.vscale))[layer * dm.Hkv + h];
+  bool vraw;
+  const float ivs = v16_factor(vsc, vraw);
+  const float vs = vraw ? 1.f : vsc;
   // V^T of a landed tile -> float16 of v / vscale, in place (each thread two 16-byte chunks)
   auto convert_v = [&](int tile) {
     u32x4_t *sv = &sV[tile % NST][0];
@@ -1198,11 +1259,12 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     u32x4_t qr[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qr[kb] = gld<u32x4_t>(qsrc + kb * 16 + 8 * hh);
-    // the tiles the prologue needs in flight with the query (tile 0, and tile 1 when its V^T is
-    // converted here); the rest of the ring's tiles once those have landed: at the start of a
-    // launch every workgroup waits only for its first tiles, not for the whole chip's first four
+    // the tiles the prologue needs in flight with the query (tile 0, out already in per-layer
+    // launches, and tile 1 when its V^T is converted here); the rest of the ring's tiles once
+    // those have landed: at the start of a launch every workgroup waits only for its first
+    // tiles, not for the whole chip's first four
     const int first = v16 ? 1 : 2;
-    for (int k = 0; k < first; ++k)
+    for (int k = LAYERED ? 0 : 1; k < first; ++k)
       if (k < ntiles) issue(k);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
