@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 METRIC = "beam-decode req/s + step µs at ctx 5000, beam 256; % MFMA peak, HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 
 # HBM bytes per layer of the context-attention kernels on this workload, from rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this benchmark (one counter per run), scaled by what
@@ -728,6 +729,29 @@ def decode_leg(cfg, args, per_layer: bool):
     }
 
 
+def rate_probe_leg(timeout: int = 120):
+    """Measured ceilings next to the published peaks: the package's rate probe (a child process,
+    started before this process touches the GPU) times dense bf16 and f16 MFMA with no memory
+    traffic, and the fp32 FMA and exp2 issue rates, on the whole chip."""
+    import subprocess
+    probe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "semantic_id_beam_amd", "rate_probe")
+    if not os.path.exists(probe):
+        raise RuntimeError(f"{probe} is missing: build the package first (semantic_id_beam_amd/build.py)")
+    res = subprocess.run([probe], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=timeout)
+    if res.returncode != 0:
+        raise RuntimeError(f"rate probe failed ({res.returncode}): {res.stderr.strip()}")
+    r = json.loads(res.stdout.strip().splitlines()[-1])
+    r["mfma_bf16_frac_of_peak"] = round(r["mfma_bf16_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+    r["mfma_f16_frac_of_peak"] = round(r["mfma_f16_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+    r["fma_f32_frac_of_peak"] = round(r["fma_f32_TFLOPs"] / PEAK_FP32_TFLOPS, 4)
+    r["exp2_per_fma"] = round(r["exp2_f32_wave_instr_per_ns"] / r["fma_f32_wave_instr_per_ns"], 3)
+    r["note"] = ("register-only loops, 4 waves per SIMD on every compute unit; the MFMA figures are the "
+                 "sustained dense rate under full matrix-core load (the chip clocks down), not a target")
+    log(f"rate probe: bf16 MFMA {r['mfma_bf16_TFLOPs']} TFLOP/s ({r['mfma_bf16_frac_of_peak']:.2f} of peak), "
+        f"fp32 FMA {r['fma_f32_TFLOPs']} TFLOP/s, exp2 at {r['exp2_per_fma']} of the FMA issue rate")
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -743,9 +767,18 @@ def main():
     ap.add_argument("--chain-only", action="store_true", help="only the layer-chain leg (prints its JSON)")
     ap.add_argument("--graph-only", action="store_true",
                     help="only the headline decode launched directly and as replayed graphs (prints its JSON)")
+    ap.add_argument("--rate-probe", action="store_true",
+                    help="only the unit-rate probe (MFMA, FMA, exp2 ceilings; prints its JSON)")
+    ap.add_argument("--no-rate-probe", action="store_true", help="skip the unit-rate probe")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.rate_probe:
+        print(json.dumps({"rate_probe": rate_probe_leg()}), flush=True)
+        return
+    # before this process touches the GPU: the probe runs as a child process
+    ceilings = None if (args.no_rate_probe or args.decode_only or args.chain_only or args.graph_only
+                        or args.copy_probe or args.gpus != 1) else rate_probe_leg()
     if args.copy_probe:
         import torch
         n = args.copy_probe << 20
@@ -803,6 +836,12 @@ def main():
         "roofline": head["roofline"],
         "kernels": head["kernels"],
     }
+    if ceilings is not None:
+        ceil_tf = min(ceilings["mfma_bf16_TFLOPs"], ceilings["mfma_f16_TFLOPs"])  # QK^T bf16, PV f16
+        out["roofline"]["measured_ceiling"] = {
+            "TFLOPs": ceil_tf, "frac": round(out["roofline"]["achieved"] / ceil_tf, 4),
+            "note": "the rate probe's sustained dense MFMA rate on this box (the lower of bf16 and f16); context only"}
+        out["rate_probe"] = ceilings
     if not args.decode_only:
         # labelled variant, not the headline: where every layer's query is an input (this model
         # stand-in), the first level runs all layers in one launch and wide levels several

@@ -41,7 +41,28 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, OUT)
+    build_rate_probe(verbose)
     return OUT
+
+
+PROBE_SRC = os.path.join(PKG, "csrc", "rate_probe.hip")
+PROBE_OUT = os.path.join(PKG, "rate_probe")
+
+
+def build_rate_probe(verbose: bool = False) -> str:
+    """The unit-rate probe (a stand-alone executable: MFMA, FMA and exp2 issue rates measured on
+    the GPU, the ceilings that `bench.py --rate-probe` reports next to the published peaks)."""
+    tmp = PROBE_OUT + ".tmp"
+    flags = [f for f in HIP_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [hipcc(), *flags, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the rate probe ({res.returncode}):\n{out}")
+    os.replace(tmp, PROBE_OUT)
+    return PROBE_OUT
 
 
 if __name__ == "__main__":
