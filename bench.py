@@ -37,15 +37,17 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 # measured (the several-layers-per-launch variant), the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "a29cdfb0cef74ca106f7d688928e069d20ba8dce8504e61ea0486a65db9a5da1",
-    "per_layer": {"k_ctx_attn_wide": {"read": 168459059, "written": 34080666},
-                  "k_ctx_attn_stream": {"read": 165722726, "written": 540672}},
+    "source_sha256": "14cb9900af0768e6db64975a579a5f24ce741e5f717b0753a404499f1211d898",
+    "per_layer": {"k_ctx_attn_wide": {"read": 168464956, "written": 34079438},
+                  "k_ctx_attn_wide_level0": {"read": 166435378, "written": 270336}},
 }
 
 
-# per-layer launch sequences: the timed region's context-attention events sit on every fourth
-# layer's launch (each carrying dispatch costs about 3 us of the stream's time)
-PROF_STRIDE = 4
+# per-layer launch sequences: the timed region's context-attention events sit on every seventh
+# layer's launch, four per level (each carrying dispatch costs the stream a few us: on one box
+# 1,028 req/s with events on every layer, 1,052-1,058 on every fourth, 1,061-1,063 on the first
+# only)
+PROF_STRIDE = 7
 
 
 def source_digest(path):
@@ -687,14 +689,16 @@ def decode_leg(cfg, args, per_layer: bool):
                            else "every launch of the timed decodes"),
     }
     kernels = {
-        "ctx_attn_level0": {"kernel": "k_ctx_attn_stream" if wide else "k_ctx_attn",
+        # the first level of the one-layer-per-launch sequence runs on the 8-wave kernel (4 token
+        # ranges); several layers per launch, on the streaming kernel
+        "ctx_attn_level0": {"kernel": ("k_ctx_attn_wide" if per_layer else "k_ctx_attn_stream") if wide else "k_ctx_attn",
                             "bound": "hbm", "achieved_GBs": round(achieved_gbs0, 1), "peak_GBs": PEAK_HBM_GBS,
                             "frac": round(achieved_gbs0 / PEAK_HBM_GBS, 4),
                             "avg_us_per_layer": round(1e3 * ms_0 / max(n_0, 1), 2),
                             "avg_us_per_dispatch": round(1e3 * ms_0 / max(d_0, 1), 2),
                             "dispatches": int(d_0),
                             "algorithmic_MB_per_layer": round(ctx_bytes(0) / 1e6, 2),
-                            "traffic": measured_traffic(cfg, "k_ctx_attn_stream", variant) if wide else None},
+                            "traffic": measured_traffic(cfg, "k_ctx_attn_wide_level0", variant) if wide else None},
     }
     for name in ("beam_merge", "logits", "topk"):
         tot = sum(prof[name][s][0] for s in range(lv))
