@@ -749,10 +749,14 @@ def rate_probe_leg(timeout: int = 120):
     r["mfma_f16_frac_of_peak"] = round(r["mfma_f16_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
     r["fma_f32_frac_of_peak"] = round(r["fma_f32_TFLOPs"] / PEAK_FP32_TFLOPS, 4)
     r["exp2_per_fma"] = round(r["exp2_f32_wave_instr_per_ns"] / r["fma_f32_wave_instr_per_ns"], 3)
+    r["hbm_read_164MiB_frac_of_peak"] = round(r["hbm_read_164MiB_TBs"] * 1e3 / PEAK_HBM_GBS, 4)
+    r["hbm_read_1GiB_frac_of_peak"] = round(r["hbm_read_1GiB_TBs"] * 1e3 / PEAK_HBM_GBS, 4)
     r["note"] = ("register-only loops, 4 waves per SIMD on every compute unit; the MFMA figures are the "
-                 "sustained dense rate under full matrix-core load (the chip clocks down), not a target")
+                 "sustained dense rate under full matrix-core load (the chip clocks down), not a target; "
+                 "HBM: one read pass (16-byte loads, 4096 workgroups) over 164 MiB and over 1 GiB")
     log(f"rate probe: bf16 MFMA {r['mfma_bf16_TFLOPs']} TFLOP/s ({r['mfma_bf16_frac_of_peak']:.2f} of peak), "
-        f"fp32 FMA {r['fma_f32_TFLOPs']} TFLOP/s, exp2 at {r['exp2_per_fma']} of the FMA issue rate")
+        f"fp32 FMA {r['fma_f32_TFLOPs']} TFLOP/s, exp2 at {r['exp2_per_fma']} of the FMA issue rate, "
+        f"HBM read {r['hbm_read_164MiB_TBs']} TB/s (164 MiB) / {r['hbm_read_1GiB_TBs']} TB/s (1 GiB)")
     return r
 
 
@@ -846,6 +850,11 @@ def main():
             "TFLOPs": ceil_tf, "frac": round(out["roofline"]["achieved"] / ceil_tf, 4),
             "note": "the rate probe's sustained dense MFMA rate on this box (the lower of bf16 and f16); context only"}
         out["rate_probe"] = ceilings
+        lv0 = out["kernels"]["ctx_attn_level0"]
+        lv0["measured_ceiling"] = {
+            "GBs": round(ceilings["hbm_read_164MiB_TBs"] * 1e3, 1),
+            "frac": round(lv0["achieved_GBs"] / (ceilings["hbm_read_164MiB_TBs"] * 1e3), 4),
+            "note": "the rate probe's read pass over 164 MiB (one layer's K and V) on this box; context only"}
     if not args.decode_only:
         # labelled variant, not the headline: where every layer's query is an input (this model
         # stand-in), the first level runs all layers in one launch and wide levels several

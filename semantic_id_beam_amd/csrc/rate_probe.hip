@@ -1,8 +1,10 @@
-// Sustained issue rates of the gfx950 units the decode kernels lean on, as a measured ceiling
-// next to the published peaks: dense bf16 and f16 MFMA (v_mfma_f32_32x32x16_*: 32,768 flop each)
-// with no memory traffic, and the vector ALU's fp32 FMA and exp2 (v_exp_f32) rates.  Each thread
-// runs `iters` iterations of independent operations on registers and writes one float, so the
-// grid touches only its own output array.  Prints one JSON object.
+// Sustained rates of the gfx950 units the decode kernels lean on, as measured ceilings next to
+// the published peaks: dense bf16 and f16 MFMA (v_mfma_f32_32x32x16_*: 32,768 flop each) with no
+// memory traffic, the vector ALU's fp32 FMA and exp2 (v_exp_f32) rates, and HBM read bandwidth
+// (one pass over a 164 MiB buffer, the size of one headline layer's K and V, and over 1 GiB).
+// The ALU loops run `iters` iterations of independent operations on registers and write one
+// float per thread; the read pass sums 16-byte loads and writes one word per thread.  Prints
+// one JSON object.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -13,6 +15,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 
 enum { kMfmaBf16 = 0, kMfmaF16 = 1, kFma = 2, kExp = 3 };
 constexpr int kAcc = 8;  // independent accumulators per wave
@@ -60,6 +63,26 @@ __global__ __launch_bounds__(256) void k_rate(float *out, int iters, float seed)
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// every thread sums its grid-stride share of n 16-byte words, U loads in flight
+template <int U>
+__global__ __launch_bounds__(256) void k_read(const u32x4_t *p, size_t n, unsigned *out) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x, nt = (size_t)gridDim.x * blockDim.x;
+  unsigned acc = 0;
+  size_t i = tid;
+  for (; i + (U - 1) * nt < n; i += U * nt) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * nt);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n; i += nt) {
+    const u32x4_t v = p[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[tid] = acc;
+}
+
 bool ok(hipError_t e, const char *what) {
   if (e != hipSuccess) {
     fprintf(stderr, "rate_probe: %s: %s\n", what, hipGetErrorString(e));
@@ -101,9 +124,35 @@ int main(int argc, char **argv) {
     else
       rate[mode] = threads / 64 * iters * 16 / sec / 1e9;  // wave instructions per ns (x64 lanes)
   }
+  // HBM reads: 4096 workgroups of 256 threads, best of 4 passes after a warm-up pass
+  const size_t rbytes[2] = {(size_t)164 << 20, (size_t)1 << 30};
+  const int rgrid = 4096;
+  u32x4_t *buf = nullptr;
+  unsigned *rout = nullptr;
+  if (!ok(hipMalloc(&buf, rbytes[1]), "hipMalloc") || !ok(hipMemset(buf, 1, rbytes[1]), "hipMemset") ||
+      !ok(hipMalloc(&rout, sizeof(unsigned) * rgrid * 256), "hipMalloc"))
+    return 1;
+  double tbs[2];
+  for (int b = 0; b < 2; ++b) {
+    float best = 1e30f;
+    for (int rep = 0; rep < 5; ++rep) {
+      if (!ok(hipEventRecord(e0), "record")) return 1;
+      k_read<8><<<rgrid, 256>>>(buf, rbytes[b] / 16, rout);
+      if (!ok(hipGetLastError(), "launch") || !ok(hipEventRecord(e1), "record") ||
+          !ok(hipEventSynchronize(e1), "sync"))
+        return 1;
+      float ms = 0.f;
+      if (!ok(hipEventElapsedTime(&ms, e0, e1), "elapsed")) return 1;
+      if (rep > 0 && ms < best) best = ms;
+    }
+    tbs[b] = rbytes[b] / (best * 1e-3) / 1e12;
+  }
   printf("{\"mfma_bf16_TFLOPs\": %.1f, \"mfma_f16_TFLOPs\": %.1f, \"fma_f32_wave_instr_per_ns\": %.2f, "
-         "\"exp2_f32_wave_instr_per_ns\": %.2f, \"fma_f32_TFLOPs\": %.1f, \"iters\": %d}\n",
-         rate[0], rate[1], rate[2], rate[3], rate[2] * 64 * 2 / 1e3, iters);
+         "\"exp2_f32_wave_instr_per_ns\": %.2f, \"fma_f32_TFLOPs\": %.1f, \"iters\": %d, "
+         "\"hbm_read_164MiB_TBs\": %.2f, \"hbm_read_1GiB_TBs\": %.2f}\n",
+         rate[0], rate[1], rate[2], rate[3], rate[2] * 64 * 2 / 1e3, iters, tbs[0], tbs[1]);
+  hipFree(rout);
+  hipFree(buf);
   hipFree(out);
   return 0;
 }
