@@ -175,6 +175,7 @@ __global__ __launch_bounds__(256) void k_chain_final(Dev dev, const StepReq *__r
 // row.
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 constexpr int GBM = 128, GBK = 64, GNST = 3;
+constexpr int kMaxKSplit = 8;  // K ranges of a split-K projection
 constexpr int kWideNWN = 4;  // waves along the weight rows of a 256-row tile
 
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
@@ -414,48 +415,48 @@ __global__ __launch_bounds__(128 * NWN) void k_gemm(Dev dev, const StepReq *__re
   }
 }
 
-// The split-K ranges of one row added in range order, then the projection's epilogue (as in
-// k_gemm): one workgroup per packed row (dead rows return at once), four columns per thread and
-// iteration.
+// The split-K ranges of a row added in range order, then the projection's epilogue (as in
+// k_gemm): one workgroup per (request, block of 1024 columns), the request's live rows in turn,
+// four columns per thread; every range's four values are loaded before the first is added.
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_reduce(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
-                                                     GemmArgs g, int rows) {
-  const int row = blockIdx.x;
-  const StepReq R = reqs[find_row_req(reqs, n_reqs, row)];
+__global__ __launch_bounds__(256) void k_gemm_reduce(Dev dev, const StepReq *__restrict__ reqs, GemmArgs g, int rows) {
+  const StepReq R = reqs[blockIdx.x];
   uint8_t *slot = slot_of(dev, R.slot);
-  const int s = R.level, j = row - R.row0;
+  const int s = R.level;
   const int n_live = ((const int *)(slot + dev.sl.n_live))[s & 1];
-  if (!(row >= R.row0 && j < n_live && j < R.n_bound)) return;
+  const int nr = min(n_live, R.n_bound);
+  const int ncols = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
+  const int col = (int)blockIdx.y * 1024 + 4 * (int)threadIdx.x;
+  if (col >= ncols) return;
   const size_t rstride = (size_t)rows * g.N;
-  const float *p = g.part + (size_t)row * g.N;
-  auto sum4 = [&](int col) {
-    f32x4_t acc = gld<f32x4_t>(p + col);
-    for (int k = 1; k < g.ksplit; ++k) {
-      const f32x4_t v = gld<f32x4_t>(p + k * rstride + col);
-      acc = f32x4_t{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
-    }
-    return acc;
-  };
-  if constexpr (EPI == EPI_RESID) {
-    for (int col = 4 * (int)threadIdx.x; col < g.N; col += 4 * 256) {
+  for (int j = 0; j < nr; ++j) {
+    const int row = R.row0 + j;
+    const float *p = g.part + (size_t)row * g.N;
+    auto sum4 = [&](int c) {
+      f32x4_t v[kMaxKSplit];
+#pragma unroll
+      for (int k = 0; k < kMaxKSplit; ++k)
+        if (k < g.ksplit) v[k] = gld<f32x4_t>(p + k * rstride + c);
+      f32x4_t acc = v[0];
+#pragma unroll
+      for (int k = 1; k < kMaxKSplit; ++k)
+        if (k < g.ksplit) acc = f32x4_t{acc[0] + v[k][0], acc[1] + v[k][1], acc[2] + v[k][2], acc[3] + v[k][3]};
+      return acc;
+    };
+    if constexpr (EPI == EPI_RESID) {
       const f32x4_t a = sum4(col);
       float *xp = g.x + (size_t)row * g.N + col;
       const f32x4_t o = gld<f32x4_t>(xp);
       gst<f32x4_t>(xp, f32x4_t{o[0] + a[0], o[1] + a[1], o[2] + a[2], o[3] + a[3]});
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    const int I = g.N / 2;
-    for (int i = 4 * (int)threadIdx.x; i < I; i += 4 * 256) {
-      const f32x4_t gt = sum4(i), up = sum4(I + i);
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t gt = sum4(col), up = sum4(ncols + col);
       float v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) v[c] = gt[c] / (1.f + expf(-gt[c])) * up[c];
-      gst<u32x2_t>(g.out + (size_t)row * I + i, u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
-    }
-  } else {
-    const Dims &dm = dev.dm;
-    const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
-    for (int col = 4 * (int)threadIdx.x; col < g.N; col += 4 * 256) {
+      gst<u32x2_t>(g.out + (size_t)row * ncols + col, u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+    } else {
+      const Dims &dm = dev.dm;
+      const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
       const f32x4_t a = sum4(col);
       const u32x2_t b = u32x2_t{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
       if (col < g.n1) {
@@ -559,7 +560,7 @@ hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, in
   // partial sums a second launch adds in order (deterministic) before the epilogue
   g.ksplit = 1;
   const int KT = g.K / GBK;
-  while (g.ksplit < 8 && tiles * g.ksplit < 256 && KT % (2 * g.ksplit) == 0 && KT / (2 * g.ksplit) >= 4 &&
+  while (g.ksplit < kMaxKSplit && tiles * g.ksplit < 256 && KT % (2 * g.ksplit) == 0 && KT / (2 * g.ksplit) >= 4 &&
          (size_t)2 * g.ksplit * rows * g.N <= c.part_floats)
     g.ksplit *= 2;
   g.part = c.part;
@@ -576,9 +577,11 @@ hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, in
   else go(std::integral_constant<int, 64>{}, std::integral_constant<int, 2>{});
   if (g.ksplit > 1) {
     const LaunchEv e2{nullptr, ev.stop};
-    if (epi == EPI_QKV) launch(k_gemm_reduce<EPI_QKV>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
-    else if (epi == EPI_RESID) launch(k_gemm_reduce<EPI_RESID>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
-    else launch(k_gemm_reduce<EPI_SWIGLU>, dim3(rows), dim3(256), st, e2, dev, reqs, n_reqs, g, rows);
+    const int ncols = epi == EPI_SWIGLU ? g.N / 2 : g.N;
+    const dim3 rgrid((unsigned)n_reqs, (unsigned)((ncols + 1023) / 1024));
+    if (epi == EPI_QKV) launch(k_gemm_reduce<EPI_QKV>, rgrid, dim3(256), st, e2, dev, reqs, g, rows);
+    else if (epi == EPI_RESID) launch(k_gemm_reduce<EPI_RESID>, rgrid, dim3(256), st, e2, dev, reqs, g, rows);
+    else launch(k_gemm_reduce<EPI_SWIGLU>, rgrid, dim3(256), st, e2, dev, reqs, g, rows);
   }
   return hipGetLastError();
 }
