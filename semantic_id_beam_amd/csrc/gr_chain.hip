@@ -472,6 +472,99 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(Dev dev, const StepReq *__r
   }
 }
 
+// ------------------------------------------------------------------- few-row projections
+// Steps whose every request has one live row (the first level: one beam each) and at most
+// kGemvRows requests: C = A W^T for those rows only, each weight streamed once.  One wave per
+// output unit (a weight row; SwiGLU: gate row i and up row i), the unit's weights KL 16-byte
+// loads per lane issued before anything waits (across the grid the whole matrix is in flight at
+// once); the requests' A rows staged in LDS ([request][K] bf16, conflict-free 16-byte reads);
+// products on v_dot2_f32_bf16, each request's sum reduced over the wave's lanes, then lane r
+// applies the projection's epilogue for request r.
+constexpr int kGemvRows = 8, kGemvWaves = 8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+template <int EPI, int KL>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv(Dev dev, const StepReq *__restrict__ reqs, int n_reqs,
+                                                          GemmArgs g, int units) {
+  constexpr int K = KL * 512, NU = EPI == EPI_SWIGLU ? 2 : 1;
+  __shared__ u32x4_t sA[kGemvRows][K / 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int unit = (int)blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool active = unit < units;  // uniform over the wave
+  u32x4_t wr[NU][KL];
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const uint16_t *wp = EPI == EPI_SWIGLU ? (u ? g.W1 : g.W0) + (size_t)unit * K : w_row<EPI>(g, 0, unit);
+#pragma unroll
+      for (int i = 0; i < KL; ++i) wr[u][i] = gld<u32x4_t>(wp + i * 512 + lane * 8);
+    }
+  }
+  for (int c = tid; c < n_reqs * (K / 8); c += 64 * kGemvWaves) {
+    const int r = c / (K / 8), k8 = c % (K / 8);
+    sA[r][k8] = gld<u32x4_t>(g.A + (size_t)reqs[r].row0 * K + k8 * 8);
+  }
+  __syncthreads();
+  if (!active) return;
+  float acc[NU][kGemvRows];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) acc[u][r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < KL; ++i)
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      if (r >= n_reqs) break;  // uniform
+      // (pairs taken from whole 8-element vectors: a bit cast of one element of a 4 x 32-bit
+      // vector compiled to element 0 for every index)
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, sA[r][i * 64 + lane]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, wr[u][i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[u][r] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{wv[2 * e], wv[2 * e + 1]},
+                                                      bf16x2_t{a[2 * e], a[2 * e + 1]}, acc[u][r], false);
+      }
+    }
+  float mine[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    mine[u] = 0.f;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      float v = acc[u][r];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == r) mine[u] = v;
+    }
+  }
+  if (lane >= n_reqs) return;
+  const StepReq &R = reqs[lane];
+  const int row = R.row0;
+  if constexpr (EPI == EPI_RESID) {
+    float *xp = g.x + (size_t)row * g.N + unit;
+    gst<float>(xp, gld<float>(xp) + mine[0]);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const float gt = mine[0], up = mine[NU - 1];
+    gst<uint16_t>(g.out + (size_t)row * (g.N / 2) + unit, (uint16_t)bf16_bits(gt / (1.f + expf(-gt)) * up));
+  } else {
+    const uint16_t b = (uint16_t)bf16_bits(mine[0]);
+    if (unit < g.n1) {
+      gst<uint16_t>(g.out + (size_t)row * g.n1 + unit, b);
+    } else if (R.level > 0) {
+      const Dims &dm = dev.dm;
+      const int s = R.level;
+      const size_t wstride = (size_t)dm.Hkv * dm.d, lvstride = (size_t)dm.W_max * wstride;
+      const bool is_v = unit >= g.n2;
+      uint16_t *kv = (uint16_t *)(slot_of(dev, R.slot) + (is_v ? dev.sl.beamkv_v : dev.sl.beamkv_k));
+      gst<uint16_t>(kv + (size_t)g.layer * dm.tl * lvstride + (size_t)(s - 1) * lvstride + (unit - (is_v ? g.n2 : g.n1)),
+                    b);
+    }
+  }
+}
+
 template <typename K, typename... Args>
 void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, LaunchEv ev, Args... args) {
   if (ev.start || ev.stop)
@@ -503,7 +596,7 @@ hipError_t launch_chain_final(const Dev &dev, const StepReq *reqs, int n_reqs, i
 }
 
 hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, int kind, int layer,
-                             hipStream_t st, LaunchEv ev) {
+                             int few, hipStream_t st, LaunchEv ev) {
   const ChainDev &c = dev.ch;
   const Dims &dm = dev.dm;
   if (rows <= 0 || rows % GBM != 0 || layer < 0 || layer >= dm.L) return hipErrorInvalidValue;
@@ -548,6 +641,21 @@ hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, in
     return hipErrorInvalidValue;
   }
   if (g.K % GBK != 0) return hipErrorInvalidValue;
+  // one live row per request, at most kGemvRows requests: the rows alone, each weight streamed
+  // once (a first-level step's q/k/v projection computes q only: its k and v are never stored)
+  if (few > 0 && n_reqs <= kGemvRows && (g.K == 2048 || g.K == 6144)) {
+    const int units = epi == EPI_SWIGLU ? g.N / 2 : (epi == EPI_QKV && few == 2 ? g.n1 : g.N);
+    const dim3 grid((unsigned)((units + kGemvWaves - 1) / kGemvWaves)), blk(64 * kGemvWaves);
+    auto go = [&](auto kl) {
+      constexpr int KL = decltype(kl)::value;
+      if (epi == EPI_QKV) launch(k_gemv<EPI_QKV, KL>, grid, blk, st, ev, dev, reqs, n_reqs, g, units);
+      else if (epi == EPI_RESID) launch(k_gemv<EPI_RESID, KL>, grid, blk, st, ev, dev, reqs, n_reqs, g, units);
+      else launch(k_gemv<EPI_SWIGLU, KL>, grid, blk, st, ev, dev, reqs, n_reqs, g, units);
+    };
+    if (g.K == 2048) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, 12>{});
+    return hipGetLastError();
+  }
   // 256 weight rows per tile where the q / k / v (or gate / up) ranges allow it and the tiles
   // still fill the chip, else 128
   const int m_tiles = rows / GBM;

@@ -1267,12 +1267,19 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       return r;
     rec(GR_PROF_NORM, pn);
     const size_t D = (size_t)d.Hq * d.d;
+    // one live row per request (the first level): the projections' few-row kernel
+    int few = 2;
+    for (int i = 0; i < n && few > 0; ++i) {
+      if (rs[(size_t)i]->n_bound != 1) few = 0;
+      else if (rs[(size_t)i]->level != 0) few = 1;
+    }
     for (int l = 0; l < d.L; ++l) {
       const bool lp = l % e->prof_stride == 0;  // this layer's launches are timed
       auto gemm = [&](int kind) -> gr_status {
         const auto pg = prof_pair(e, pk(GR_PROF_GEMM) && lp);
-        gr_status q = check_dev(e, gr::launch_chain_gemm(e->dev, dw, n, rows, kind, l, st, prof_ev(e, pg.first, pg.second)),
-                                "chain projection");
+        gr_status q = check_dev(
+            e, gr::launch_chain_gemm(e->dev, dw, n, rows, kind, l, few, st, prof_ev(e, pg.first, pg.second)),
+            "chain projection");
         if (q == GR_OK) rec(GR_PROF_GEMM, pg);
         return q;
       };

@@ -222,8 +222,10 @@ hipError_t launch_chain_start(const Dev &dev, const StepReq *reqs, int n_reqs, i
 hipError_t launch_label_head(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
                              LaunchEv ev = {});
 hipError_t launch_chain_norm(const Dev &dev, const float *g, int rows, hipStream_t st, LaunchEv ev = {});
+// few: 0 any step; 1 every request has one live row (n_bound 1); 2 as 1 and every request at
+// the first level (the q/k/v projection then computes q only)
 hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, int kind, int layer,
-                             hipStream_t st, LaunchEv ev = {});
+                             int few, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_chain_final(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
                               LaunchEv ev = {});
 

@@ -43,7 +43,7 @@ GR_STUB(launch_prefill_q, int, const void *, int, const int32_t *, const float *
 hipError_t prefill_scratch(float **) { std::abort(); }
 GR_STUB(launch_chain_start, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_chain_norm, const Dev &, const float *, int, hipStream_t, LaunchEv)
-GR_STUB(launch_chain_gemm, const Dev &, const StepReq *, int, int, int, int, hipStream_t, LaunchEv)
+GR_STUB(launch_chain_gemm, const Dev &, const StepReq *, int, int, int, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_chain_final, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 #undef GR_STUB
 }  // namespace gr
