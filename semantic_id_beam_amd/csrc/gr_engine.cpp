@@ -1267,12 +1267,10 @@ gr_status step_impl(gr_engine *e, const int64_t *ids, int32_t n, void *stream, s
       return r;
     rec(GR_PROF_NORM, pn);
     const size_t D = (size_t)d.Hq * d.d;
-    // one live row per request (the first level): the projections' few-row kernel
+    // every request at the first level (one live row each): the projections' few-row kernel
     int few = 2;
-    for (int i = 0; i < n && few > 0; ++i) {
-      if (rs[(size_t)i]->n_bound != 1) few = 0;
-      else if (rs[(size_t)i]->level != 0) few = 1;
-    }
+    for (int i = 0; i < n && few > 0; ++i)
+      if (rs[(size_t)i]->n_bound != 1 || rs[(size_t)i]->level != 0) few = 0;
     for (int l = 0; l < d.L; ++l) {
       const bool lp = l % e->prof_stride == 0;  // this layer's launches are timed
       auto gemm = [&](int kind) -> gr_status {

@@ -222,8 +222,9 @@ hipError_t launch_chain_start(const Dev &dev, const StepReq *reqs, int n_reqs, i
 hipError_t launch_label_head(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,
                              LaunchEv ev = {});
 hipError_t launch_chain_norm(const Dev &dev, const float *g, int rows, hipStream_t st, LaunchEv ev = {});
-// few: 0 any step; 1 every request has one live row (n_bound 1); 2 as 1 and every request at
-// the first level (the q/k/v projection then computes q only)
+// few: 0 any step; 2 every request at the first level with one live row (n_bound 1): the
+// few-row kernel, and the q/k/v projection computes q only (1, one live row per request at any
+// level, is accepted by the kernel but not produced by the engine)
 hipError_t launch_chain_gemm(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, int kind, int layer,
                              int few, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_chain_final(const Dev &dev, const StepReq *reqs, int n_reqs, int rows, hipStream_t st,
