@@ -149,16 +149,17 @@ def _run_full(cfg, sampled, schedule=None, n_parents=2, n_final=3):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.timeout(900)
 def test_headline_ctx5k_beam256_r8_full():
     cfg = synth.get_config("ctx5k_beam256_r8")
-    steps = _run_full(cfg, sampled=[0, 5])
+    steps = _run_full(cfg, sampled=[0, 2, 5, 7], n_parents=4, n_final=4)
     assert steps == cfg.n_levels
 
 
 @pytest.mark.timeout(900)
 def test_ctx2k_beam30_r64_zipf_full():
     cfg = synth.get_config("ctx2k_beam30_r64")
-    steps = _run_full(cfg, sampled=[3, 41], n_parents=3)
+    steps = _run_full(cfg, sampled=[3, 17, 41, 60], n_parents=3)
     assert steps == cfg.n_levels
 
 
