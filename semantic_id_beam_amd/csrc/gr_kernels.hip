@@ -1144,20 +1144,46 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
     return mx;
   };
+  // The token loop carries a sub-tile's scores as exponent arguments a = s x log2 e / sqrt(d) - M
+  // (converted once, right after the QK^T: the maximum is then taken over arithmetic results,
+  // which need no quieting, three at a time).  The lazy rescale on arguments whose lane maximum
+  // is mx: a row whose arguments exceed 8 moves M up by its largest argument, its l and o scale
+  // by exp2 of the difference, and its arguments shift by the same difference.
+  auto rescale_args = [&](float mx, f32x16_t &a) {
+    if (__ballot(mx > 8.f) != 0ull) {  // uniform over the wave
+      const float Mn = M + fmaxf(fmaxf(mx, __shfl_xor(mx, 32)), 0.f);
+      const float e = M - Mn;
+      const float f = fast_exp2(e);
+      l *= f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a[i] += e;
+      M = Mn;
+    }
+  };
+  auto to_args = [&](f32x16_t &a) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = fmaf(a[i], c2, -M);
+  };
   const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-  // softmax of sub-tile u (first token t0 + 32u) and PV with its tile's V^T (tail sub-tiles)
-  auto soft_pv = [&](f32x16_t sacc, int u, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // softmax of sub-tile u (first token t0 + 32u) and PV with its tile's V^T (tail sub-tiles);
+  // sacc holds exponent arguments (ARGS, rescaled already) or raw scores
+  auto soft_pv = [&](f32x16_t sacc, int u, auto mask_tag, auto args_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value, ARGS = decltype(args_tag)::value;
     if constexpr (MASK) {
       const int tbase = t0 + u * 32 + 8 * hh;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (tbase + 16 * (i >> 3) + (i & 7) >= t1) sacc[i] = kNegInf;
     }
-    rescale(smax(sacc));
+    if constexpr (!ARGS) {
+      rescale(smax(sacc));
+      to_args(sacc);
+    }
     f16x8_t pf[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (_Float16)fast_exp2(fmaf(sacc[i], c2, -M));
+    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (_Float16)fast_exp2(sacc[i]);
 #pragma unroll
     for (int i = 0; i < 16; i += 2)
       l = __builtin_amdgcn_fdot2(f16x2_t{pf[i >> 3][i & 7], pf[i >> 3][(i & 7) + 1]}, ones, l, false);
@@ -1175,8 +1201,9 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   // u, interleaved by hand.  Issue is in order within a wave, so the softmax is spread over the
   // wave's own MFMAs, giving each wave independent VALU work between its MFMAs (the two waves of
   // a SIMD then keep the matrix core fed): element k (k < 8) after the k-th QK^T MFMA, elements
-  // 8..15 two at a time after the first four PV MFMAs (those use the first eight only), and the
-  // row maxima of sub-tile u+1 over the last four, for its lazy rescale at the end.  LDS
+  // 8..15 two at a time after the first four PV MFMAs (those use the first eight only), and
+  // sub-tile u+1's scores turned into arguments, with their maxima, over the last four, for its
+  // lazy rescale at the end.  LDS
   // operands are fetched two MFMAs ahead; sched_barrier keeps the order.  kr: the K rows of the
   // QK^T sub-tile, vr: the V^T tile of the PV sub-tile spv.  With compile-time stages
   // (block_st) every operand address is a per-lane register plus an immediate offset.
@@ -1203,7 +1230,7 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
       if (kb + 2 < KB) kf[(kb + 2) % 3] = kfrag(kb + 2);
       else vf[(kb + 2 - KB) % 3] = vfrag(kb + 2 - KB);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb % 3], qf[kb], acc, 0, 0, 0);
-      pr[kb] = fast_exp2(fmaf(sc[kb], c2, -M));
+      pr[kb] = fast_exp2(sc[kb]);
       if (kb & 1) pair(pr[kb - 1], pr[kb], kb - 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1212,15 +1239,18 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
       if (j + 2 < 8) vf[(j + 2) % 3] = vfrag(j + 2);
       oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[j % 3], pf[j >> 2], oacc[j & 3], 0, 0, 0);
       if (j < 4) {
-        pair(fast_exp2(fmaf(sc[8 + 2 * j], c2, -M)), fast_exp2(fmaf(sc[9 + 2 * j], c2, -M)), 8 + 2 * j);
+        pair(fast_exp2(sc[8 + 2 * j]), fast_exp2(sc[9 + 2 * j]), 8 + 2 * j);
       } else {
+        // sub-tile u+1's scores to arguments, four per step, and their maximum
         const int b = 4 * (j - 4);
+#pragma unroll
+        for (int i = b; i < b + 4; ++i) acc[i] = fmaf(acc[i], c2, -M);
         const float m4 = fmaxf(fmaxf(acc[b], acc[b + 1]), fmaxf(acc[b + 2], acc[b + 3]));
         mx = j == 4 ? m4 : fmaxf(mx, m4);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    rescale(mx);
+    rescale_args(mx, acc);
     return acc;
   };
   static_assert(KB == 8, "the interleave assumes eight QK^T MFMAs per sub-tile");
@@ -1309,11 +1339,12 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
-  // s0 holds the scores of even sub-tiles, s1 of odd ones
+  // s0 holds the exponent arguments of even sub-tiles, s1 of odd ones
   f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
   if (wave_active) {
     s0 = qk(0, 0);
     rescale(smax(s0));
+    to_args(s0);
   }
   // steady state: both sub-tiles of tile it are unmasked and tile it+1 exists; NST tiles at a
   // time with compile-time stages, then one at a time
@@ -1341,15 +1372,15 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   if (wave_active) {
     if (2 * it + 1 < nsub) {
       s1 = qk(it, 1);
-      soft_pv(s0, 2 * it, std::false_type{});
+      soft_pv(s0, 2 * it, std::false_type{}, std::true_type{});
       if (partial)
-        soft_pv(s1, nsub - 1, std::true_type{});
+        soft_pv(s1, nsub - 1, std::true_type{}, std::false_type{});
       else
-        soft_pv(s1, nsub - 1, std::false_type{});
+        soft_pv(s1, nsub - 1, std::false_type{}, std::false_type{});
     } else if (partial) {
-      soft_pv(s0, nsub - 1, std::true_type{});
+      soft_pv(s0, nsub - 1, std::true_type{}, std::true_type{});
     } else {
-      soft_pv(s0, nsub - 1, std::false_type{});
+      soft_pv(s0, nsub - 1, std::false_type{}, std::true_type{});
     }
   }
 
