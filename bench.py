@@ -37,9 +37,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 # measured (the several-layers-per-launch variant), the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "14cb9900af0768e6db64975a579a5f24ce741e5f717b0753a404499f1211d898",
-    "per_layer": {"k_ctx_attn_wide": {"read": 168464956, "written": 34079438},
-                  "k_ctx_attn_wide_level0": {"read": 166435378, "written": 270336}},
+    "source_sha256": "ff8838c229c72fb80f6f09c6849e69b6380a32dde5b742d0be5a9e7d2bbcc2bd",
+    "per_layer": {"k_ctx_attn_wide": {"read": 168474171, "written": 34079236},
+                  "k_ctx_attn_wide_level0": {"read": 166446164, "written": 270336}},
 }
 
 
