@@ -751,12 +751,16 @@ def rate_probe_leg(timeout: int = 120):
     r["exp2_per_fma"] = round(r["exp2_f32_wave_instr_per_ns"] / r["fma_f32_wave_instr_per_ns"], 3)
     r["hbm_read_164MiB_frac_of_peak"] = round(r["hbm_read_164MiB_TBs"] * 1e3 / PEAK_HBM_GBS, 4)
     r["hbm_read_1GiB_frac_of_peak"] = round(r["hbm_read_1GiB_TBs"] * 1e3 / PEAK_HBM_GBS, 4)
+    r["mfma_bf16_lds_operand_frac_of_peak"] = round(r["mfma_bf16_lds_operand_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
     r["note"] = ("register-only loops, 4 waves per SIMD on every compute unit; the MFMA figures are the "
                  "sustained dense rate under full matrix-core load (the chip clocks down), not a target; "
-                 "HBM: one read pass (16-byte loads, 4096 workgroups) over 164 MiB and over 1 GiB")
+                 "HBM: one read pass (16-byte loads, 4096 workgroups) over 164 MiB and over 1 GiB; LDS: "
+                 "8 waves per compute unit reading 1 KB per ds_read_b128, and bf16 MFMA taking one such "
+                 "read as its A operand per instruction (the context-attention loop's operand path)")
     log(f"rate probe: bf16 MFMA {r['mfma_bf16_TFLOPs']} TFLOP/s ({r['mfma_bf16_frac_of_peak']:.2f} of peak), "
         f"fp32 FMA {r['fma_f32_TFLOPs']} TFLOP/s, exp2 at {r['exp2_per_fma']} of the FMA issue rate, "
-        f"HBM read {r['hbm_read_164MiB_TBs']} TB/s (164 MiB) / {r['hbm_read_1GiB_TBs']} TB/s (1 GiB)")
+        f"HBM read {r['hbm_read_164MiB_TBs']} TB/s (164 MiB) / {r['hbm_read_1GiB_TBs']} TB/s (1 GiB), "
+        f"LDS read {r['lds_read_TBs']} TB/s, MFMA with LDS operands {r['mfma_bf16_lds_operand_TFLOPs']} TFLOP/s")
     return r
 
 

@@ -1,7 +1,9 @@
 // Sustained rates of the gfx950 units the decode kernels lean on, as measured ceilings next to
 // the published peaks: dense bf16 and f16 MFMA (v_mfma_f32_32x32x16_*: 32,768 flop each) with no
 // memory traffic, the vector ALU's fp32 FMA and exp2 (v_exp_f32) rates, and HBM read bandwidth
-// (one pass over a 164 MiB buffer, the size of one headline layer's K and V, and over 1 GiB).
+// (one pass over a 164 MiB buffer, the size of one headline layer's K and V, and over 1 GiB),
+// LDS read bandwidth, and MFMA fed by one LDS read per instruction (the attention loop's
+// operand path).
 // The ALU loops run `iters` iterations of independent operations on registers and write one
 // float per thread; the read pass sums 16-byte loads and writes one word per thread.  Prints
 // one JSON object.
@@ -83,6 +85,67 @@ __global__ __launch_bounds__(256) void k_read(const u32x4_t *p, size_t n, unsign
   out[tid] = acc;
 }
 
+// LDS read bandwidth: 8 waves per workgroup, one workgroup per compute unit; each wave reads
+// 1 KB per ds_read_b128 (64 lanes x 16 consecutive bytes, no bank conflicts) from a 64 KB
+// buffer, 8 reads per iteration (8 consecutive 1 KB rows, immediate offsets), and folds the
+// words with three-input adds (two VALU instructions per read).
+__global__ __launch_bounds__(512) void k_lds_read(unsigned *out, int iters) {
+  __shared__ u32x4_t buf[4096];
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = u32x4_t{(unsigned)i, (unsigned)i + 1, 7u, 9u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  unsigned a0 = 0, a1 = 0;
+  for (int it = 0; it < iters; ++it) {
+    const u32x4_t *row = buf + ((it + w) & 7) * 512 + lane;  // 8 rows of 1 KB, immediate offsets
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = row[u * 64];  // all 8 reads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a0 = a0 + v[u][0] + v[u][1];  // v_add3_u32
+      a1 = a1 + v[u][2] + v[u][3];
+    }
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = a0 ^ a1;
+}
+
+// The context-attention loop's shape: each v_mfma_f32_32x32x16_bf16 takes its A operand from
+// one ds_read_b128 (1 KB per wave), B from registers; 8 waves per workgroup (2 per SIMD), one
+// workgroup per compute unit, 4 accumulators per wave.
+__global__ __launch_bounds__(512) void k_mfma_lds(float *out, int iters) {
+  __shared__ u32x4_t buf[4096];
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = u32x4_t{0x3c003c00u, 0x3b003b00u, 0x3c003c00u, 0x3a003a00u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  bf16x8_t b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = (__bf16)((float)(lane + i) * 1e-4f);
+  f32x16_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16_t{};
+  // software-pipelined: the next iteration's 8 operand reads are in flight during this one's MFMAs
+  u32x4_t cur[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) cur[u] = buf[(w & 7) * 512 + lane + u * 64];
+  for (int it = 0; it < iters; ++it) {
+    const u32x4_t *row = buf + ((it + 1 + w) & 7) * 512 + lane;
+    u32x4_t nxt[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) nxt[u] = row[u * 64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur[u]), b, acc[u & 3], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[j][i];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 bool ok(hipError_t e, const char *what) {
   if (e != hipSuccess) {
     fprintf(stderr, "rate_probe: %s: %s\n", what, hipGetErrorString(e));
@@ -124,6 +187,28 @@ int main(int argc, char **argv) {
     else
       rate[mode] = threads / 64 * iters * 16 / sec / 1e9;  // wave instructions per ns (x64 lanes)
   }
+  // LDS: 256 workgroups of 512 threads (one per compute unit), best of 2 after a warm-up
+  double lds_tbs = 0, mfma_lds = 0;
+  {
+    const int lgrid = 256, lblock = 512, liters = iters / 4;
+    for (int mode = 0; mode < 2; ++mode) {
+      float best = 1e30f;
+      for (int rep = 0; rep < 3; ++rep) {
+        if (!ok(hipEventRecord(e0), "record")) return 1;
+        if (mode == 0) k_lds_read<<<lgrid, lblock>>>(reinterpret_cast<unsigned *>(out), liters);
+        if (mode == 1) k_mfma_lds<<<lgrid, lblock>>>(out, liters);
+        if (!ok(hipGetLastError(), "launch") || !ok(hipEventRecord(e1), "record") ||
+            !ok(hipEventSynchronize(e1), "sync"))
+          return 1;
+        float ms = 0.f;
+        if (!ok(hipEventElapsedTime(&ms, e0, e1), "elapsed")) return 1;
+        if (rep > 0 && ms < best) best = ms;
+      }
+      const double waves = (double)lgrid * lblock / 64, sec = best * 1e-3;
+      if (mode == 0) lds_tbs = waves * liters * 8 * 1024.0 / sec / 1e12;
+      else mfma_lds = waves * liters * 8 * 32768.0 / sec / 1e12;
+    }
+  }
   // HBM reads: 4096 workgroups of 256 threads, best of 4 passes after a warm-up pass
   const size_t rbytes[2] = {(size_t)164 << 20, (size_t)1 << 30};
   const int rgrid = 4096;
@@ -149,8 +234,9 @@ int main(int argc, char **argv) {
   }
   printf("{\"mfma_bf16_TFLOPs\": %.1f, \"mfma_f16_TFLOPs\": %.1f, \"fma_f32_wave_instr_per_ns\": %.2f, "
          "\"exp2_f32_wave_instr_per_ns\": %.2f, \"fma_f32_TFLOPs\": %.1f, \"iters\": %d, "
-         "\"hbm_read_164MiB_TBs\": %.2f, \"hbm_read_1GiB_TBs\": %.2f}\n",
-         rate[0], rate[1], rate[2], rate[3], rate[2] * 64 * 2 / 1e3, iters, tbs[0], tbs[1]);
+         "\"hbm_read_164MiB_TBs\": %.2f, \"hbm_read_1GiB_TBs\": %.2f, \"lds_read_TBs\": %.1f, "
+         "\"mfma_bf16_lds_operand_TFLOPs\": %.1f}\n",
+         rate[0], rate[1], rate[2], rate[3], rate[2] * 64 * 2 / 1e3, iters, tbs[0], tbs[1], lds_tbs, mfma_lds);
   hipFree(rout);
   hipFree(buf);
   hipFree(out);
