@@ -37,9 +37,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 # measured (the several-layers-per-launch variant), the traffic is reported as null.
 MEASURED_TRAFFIC = {
     "workload": "ctx5k_beam256_r8",
-    "source_sha256": "ff8838c229c72fb80f6f09c6849e69b6380a32dde5b742d0be5a9e7d2bbcc2bd",
-    "per_layer": {"k_ctx_attn_wide": {"read": 168474171, "written": 34079236},
-                  "k_ctx_attn_wide_level0": {"read": 166446164, "written": 270336}},
+    "source_sha256": "ac741b57f9f3e38438b441a907e6a5bf045b9564788febaecedcb087398301a7",
+    "per_layer": {"k_ctx_attn_wide": {"read": 168466022, "written": 34079130},
+                  "k_ctx_attn_wide_level0": {"read": 166437478, "written": 270336}},
 }
 
 
@@ -764,6 +764,88 @@ def rate_probe_leg(timeout: int = 120):
     return r
 
 
+def wave_times_child(cfg, level: int = 1, layer: int = 13, decodes: int = 3):
+    """Runs inside the wave-timeline build (GR_BEAM_LIB_VARIANT=timed): the headline decode with
+    one context-attention launch per layer, recording the launch of (level, layer); returns the
+    per-wave breakdown of that launch (prologue, token loop, epilogue, copy waits and barriers
+    inside the loop, the spread between XCDs)."""
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    import synth
+    from semantic_id_beam_amd import _lib as G
+    from semantic_id_beam_amd.workloads import make_engine, request_tensors
+
+    if not G.LIB_PATH.endswith("libgr_beam_timed.so"):
+        raise RuntimeError("the wave timeline needs the timed library (GR_BEAM_LIB_VARIANT=timed)")
+    shapes = synth.request_shapes(cfg)
+    R = cfg.n_requests
+    eng = make_engine(cfg, max_requests=R, per_layer=True)
+    for r in range(R):
+        k, v, q = request_tensors(cfg, r)
+        eng.load(r, k, v, q, shapes[r][1])
+        del k, v, q
+    torch.cuda.synchronize()
+    L = G.lib()
+    if L.gr_wave_times_select(level, layer) != 0:
+        raise RuntimeError("gr_wave_times_select failed")
+    rids = list(range(R))
+    for _ in range(decodes):
+        eng.reset_batch(rids)
+        for _s in range(cfg.n_levels):
+            eng.step(rids)
+        eng.beams_batch(rids)
+    torch.cuda.synchronize()
+    n = 1024 * 8 * 8
+    buf = np.zeros(n, dtype=np.int64)
+    if L.gr_wave_times_read(buf.ctypes.data_as(C.POINTER(C.c_int64)), n) != 0:
+        raise RuntimeError("gr_wave_times_read failed")
+    t = buf.reshape(1024, 8, 8)
+    rec = t[:, :, 0] != 0
+    if not rec.any():
+        raise RuntimeError("no wave recorded")
+    entry, lstart, lend, done = (t[:, :, f][rec] for f in range(4))
+    wait, barrier, loop, nbar = (t[:, :, f][rec].astype(float) for f in range(4, 8))
+    us = lambda x: round(float(x) / 100.0, 2)  # 100 MHz stamps
+    wg_end = np.where(rec, t[:, :, 3], 0).max(axis=1)
+    wg_ids = np.nonzero(rec.any(axis=1))[0]
+    xcd_end = [float(np.median(wg_end[[i for i in wg_ids if i % 8 == x]] - entry.min())) / 100.0
+               for x in range(8) if any(i % 8 == x for i in wg_ids)]
+    return {
+        "launch": f"level {level}, layer {layer}, last of {decodes} decodes",
+        "workgroups": int(len(wg_ids)), "waves": int(rec.sum()),
+        "span_us": us(done.max() - entry.min()),
+        "entry_spread_us": us(entry.max() - entry.min()),
+        "prologue_us": {"median": us(np.median(lstart - entry)), "max": us((lstart - entry).max())},
+        "loop_us": {"median": us(np.median(lend - lstart)), "min": us((lend - lstart).min()),
+                    "max": us((lend - lstart).max())},
+        "epilogue_us": {"median": us(np.median(done - lend)), "max": us((done - lend).max())},
+        "xcd_median_end_us": [round(x, 2) for x in xcd_end],
+        "xcd_spread_us": round(max(xcd_end) - min(xcd_end), 2),
+        "loop_copy_wait_frac": round(float(wait.sum() / loop.sum()), 4),
+        "loop_barrier_frac": round(float(barrier.sum() / loop.sum()), 4),
+        "barriers_per_wave": float(np.median(nbar)),
+        "memtime_ticks_per_ns": round(float(loop.sum() / ((lend - lstart).sum() * 10.0)), 3),
+        "note": "s_memrealtime stamps (entry, token-loop start and end, partial stores done) and "
+                "s_memtime cycles of the copy waits and barriers inside the token loop, per wave; "
+                "a separate build of the library (libgr_beam_timed.so), the product kernel has none",
+    }
+
+
+def wave_times_leg(timeout: int = 300):
+    """The wave timeline of one headline context-attention launch, from a child process that
+    loads the wave-timeline build of the library."""
+    import subprocess
+    env = dict(os.environ, GR_BEAM_LIB_VARIANT="timed")
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--wave-times-child"], env=env,
+                         stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=timeout)
+    if res.returncode != 0:
+        raise RuntimeError(f"wave timeline failed ({res.returncode}): {res.stderr.strip()[-2000:]}")
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -782,9 +864,21 @@ def main():
     ap.add_argument("--rate-probe", action="store_true",
                     help="only the unit-rate probe (MFMA, FMA, exp2 ceilings; prints its JSON)")
     ap.add_argument("--no-rate-probe", action="store_true", help="skip the unit-rate probe")
+    ap.add_argument("--wave-times", action="store_true",
+                    help="only the wave timeline of one headline context-attention launch (a child process "
+                         "with the wave-timeline build; prints its JSON)")
+    ap.add_argument("--wave-times-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.wave_times_child:
+        import synth
+        from synth.configs import HEADLINE
+        print(json.dumps(wave_times_child(synth.get_config(args.config or HEADLINE))), flush=True)
+        return
+    if args.wave_times:
+        print(json.dumps({"wave_times": wave_times_leg()}), flush=True)
+        return
     if args.rate_probe:
         print(json.dumps({"rate_probe": rate_probe_leg()}), flush=True)
         return

@@ -521,6 +521,19 @@ gr_status gr_engine_set_profiling_kinds(gr_engine *eng, uint32_t kinds);
  * timed run can so sample a kernel's duration with fewer events in its stream. */
 gr_status gr_engine_set_profiling_stride(gr_engine *eng, int32_t stride);
 
+/* Wave timeline of the context-attention kernel (measurement, not part of any decode).  Only the
+ * separately built libgr_beam_timed.so records it; the product library returns
+ * GR_E_UNSUPPORTED from gr_wave_times_read.  gr_wave_times_select(level, layer) picks the launch
+ * to record (-1, -1: none, the default): from then on, every launch of that decode level and
+ * layer overwrites the record.  gr_wave_times_read copies it to host memory the caller owns:
+ * count must be 1024 x 8 x 8 = 65536 values, [workgroup][wave][field] with the fields entry,
+ * token-loop start, token-loop end and partial stores done (100 MHz real-time stamps), then
+ * over the token loop the shader-clock cycles spent in copy waits, in barriers and in the whole
+ * loop, and the number of barriers; waves with no rows and workgroups past 1024 keep zeros.
+ * Synchronous (the default stream).  Errors: GR_E_INVALID_ARG, GR_E_UNSUPPORTED, GR_E_DEVICE. */
+gr_status gr_wave_times_select(int32_t level, int32_t layer);
+gr_status gr_wave_times_read(int64_t *host, size_t count);
+
 /* Waits for every recorded event, folds the elapsed times into the buckets and
  * returns one bucket: total milliseconds and number of launches, where a launch that
  * covers several layers counts once per layer (so total_ms / launches is the time per

@@ -14,7 +14,10 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgr_beam.so")
+# GR_BEAM_LIB_VARIANT=timed loads the wave-timeline measurement build instead (bench.py
+# --wave-times starts a child process with it); nothing else selects it
+LIB_PATH = os.path.join(_HERE, "libgr_beam_timed.so" if os.environ.get("GR_BEAM_LIB_VARIANT") == "timed"
+                        else "libgr_beam.so")
 
 GR_OK, GR_E_INVALID_ARG, GR_E_OUT_OF_MEMORY, GR_E_BAD_STATE, GR_E_NOT_FOUND, GR_E_DEVICE, GR_E_UNSUPPORTED = range(7)
 GR_DTYPE_F32, GR_DTYPE_BF16 = 0, 1
@@ -39,6 +42,7 @@ EXPORTS = [
     "gr_sched_create", "gr_sched_destroy", "gr_sched_submit", "gr_sched_advance", "gr_sched_flush",
     "gr_sched_completed", "gr_sched_result", "gr_sched_counts", "gr_debug_chain_rows", "gr_score_items_labels",
     "gr_engine_graph_stats", "gr_engine_set_profiling_kinds", "gr_engine_set_profiling_stride",
+    "gr_wave_times_select", "gr_wave_times_read",
 ]
 GR_CHAIN_X_IN, GR_CHAIN_XN_ATTN, GR_CHAIN_Q, GR_CHAIN_O, GR_CHAIN_X_MID, GR_CHAIN_XN_MLP, GR_CHAIN_ACT, \
     GR_CHAIN_X_OUT = range(8)
@@ -118,6 +122,8 @@ def lib() -> C.CDLL:
         "gr_ctx_prefill": (i32, [vp, i64, vp, i32, i32, vp, i32, vp, vp, vp, vp]),
         "gr_ctx_prefill_noalloc": (i32, [vp, i64, vp, i32, i32, vp, i32, vp, vp, vp, vp]),
         "gr_beam_step": (i32, [vp, P(i64), i32, vp]),
+        "gr_wave_times_select": (i32, [i32, i32]),
+        "gr_wave_times_read": (i32, [P(i64), sz]),
         "gr_beams_get": (i32, [vp, i64, i32, vp, vp, P(i32), vp]),
         "gr_beams_get_batch": (i32, [vp, P(i64), i32, i32, vp, vp, vp, vp]),
         "gr_beams_get_batch_async": (i32, [vp, P(i64), i32, vp, vp]),

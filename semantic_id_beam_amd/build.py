@@ -41,8 +41,29 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, OUT)
+    build_timed(verbose)
     build_rate_probe(verbose)
     return OUT
+
+
+TIMED_OUT = os.path.join(PKG, "libgr_beam_timed.so")
+
+
+def build_timed(verbose: bool = False) -> str:
+    """The same library with the context-attention wave timeline compiled in (GR_WAVE_TIMES):
+    a measurement build that `bench.py --wave-times` loads in a child process; the product
+    library has none of it."""
+    tmp = TIMED_OUT + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-DGR_WAVE_TIMES", "-I", os.path.join(ROOT, "include"), "-I",
+           os.path.join(PKG, "csrc"), *SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the wave-timeline build ({res.returncode}):\n{out}")
+    os.replace(tmp, TIMED_OUT)
+    return TIMED_OUT
 
 
 PROBE_SRC = os.path.join(PKG, "csrc", "rate_probe.hip")

@@ -1746,6 +1746,20 @@ gr_status gr_engine_set_profiling_kinds(gr_engine *e, uint32_t kinds) {
   return GR_OK;
 }
 
+gr_status gr_wave_times_select(int32_t level, int32_t layer) {
+  if (level < -1 || layer < -1) return fail(GR_E_INVALID_ARG, "level and layer must be >= -1");
+  const hipError_t err = gr::wave_times_select(level, layer);
+  return err == hipSuccess ? GR_OK : fail(GR_E_DEVICE, hipGetErrorString(err));
+}
+
+gr_status gr_wave_times_read(int64_t *host, size_t count) {
+  const size_t full = (size_t)gr::kWaveTimesWgs * 8 * gr::kWaveTimesFields;
+  if (!host || count != full) return fail(GR_E_INVALID_ARG, "host buffer of kWaveTimesWgs x 8 x 8 values");
+  const hipError_t err = gr::wave_times_read(reinterpret_cast<long long *>(host), count);
+  if (err == hipErrorNotSupported) return fail(GR_E_UNSUPPORTED, "not a wave-timeline build");
+  return err == hipSuccess ? GR_OK : fail(GR_E_DEVICE, hipGetErrorString(err));
+}
+
 gr_status gr_engine_set_profiling_stride(gr_engine *e, int32_t stride) {
   if (!e) return fail(GR_E_INVALID_ARG, "null engine");
   if (stride < 1) return fail(GR_E_INVALID_ARG, "profiling stride must be >= 1");

@@ -10,6 +10,8 @@ namespace gr {
 constexpr int kMaxLevels = 8;
 constexpr int kMaxGroup = 8;      // query heads per kv head handled by the beam kernel
 constexpr int kTileTok = 64;      // context tokens per split granule / padding unit
+constexpr int kWaveTimesWgs = 1024;  // workgroups whose waves a GR_WAVE_TIMES build records
+constexpr int kWaveTimesFields = 8;  // values per wave
 constexpr int kTopkThreads = 1024;
 constexpr int kMaxBeam = 1024;
 constexpr int kLogitsKS = 4;          // split of the hidden dimension in the logits GEMM
@@ -149,6 +151,11 @@ hipError_t launch_ctx_attn_first_level(const Dev &dev, const StepReq *reqs, int 
 hipError_t launch_ctx_attn_layered(const Dev &dev, const StepReq *reqs, int n_reqs, int layer0, int total_wgs,
                                    int ctx_kind, hipStream_t st, LaunchEv ev = {});
 hipError_t launch_sum_hparts(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st, LaunchEv ev = {});
+// The context-attention wave timeline of a GR_WAVE_TIMES build (gr_kernels.hip): select the
+// (level, layer) whose launch is recorded; read kWaveTimesWgs x 8 waves x kWaveTimesFields
+// values (hipErrorNotSupported in the product library).
+hipError_t wave_times_select(int level, int layer);
+hipError_t wave_times_read(long long *host, size_t count);
 hipError_t launch_finish_first_level(const Dev &dev, const StepReq *reqs, int n_reqs, hipStream_t st,
                                      LaunchEv ev = {});
 hipError_t launch_logits(const Dev &dev, const StepReq *reqs, int n_reqs, int total_wgs, hipStream_t st,

@@ -468,6 +468,21 @@ __global__ __launch_bounds__(NW * 64) void k_ctx_attn_bf16_narrow(Dev dev, const
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr) : "memory", "m0");
 }
+// Wave timeline of the context-attention launch (a build option: GR_WAVE_TIMES, the library
+// libgr_beam_timed.so; the product library compiles none of it).  For the launch of the selected
+// (level, layer) of each request batch, every wave of the first kWaveTimesWgs workgroups
+// writes kWaveTimesFields values: its entry, token-loop start, token-loop end and
+// partial-stores-done stamps (s_memrealtime, 100 MHz), and over the token loop the shader-clock
+// cycles (s_memtime) spent in the copy waits, in the barriers and in the whole loop, and the
+// number of barriers.  The last matching launch's values stay.
+#ifdef GR_WAVE_TIMES
+constexpr bool kWaveTimes = true;
+#else
+constexpr bool kWaveTimes = false;
+#endif
+__device__ long long g_wave_times[kWaveTimes ? kWaveTimesWgs * 8 * kWaveTimesFields : 1];
+__device__ int g_wave_times_sel[2] = {-1, -1};
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -995,6 +1010,8 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   __shared__ bf16x8_t sK[NST][KCH];   // [token row swap23(r)][column c ^ (row & 15)]
   __shared__ u32x4_t sV[NST][VCH];    // [feature row][token column c ^ (row & 7) ^ (row >> 3 & 1)]
 
+  long long wt[kWaveTimesFields] = {};  // the wave timeline (GR_WAVE_TIMES builds only)
+  if constexpr (kWaveTimes) wt[0] = wall_clock64();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5;
   const int kx = lane & 15, vx = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of this lane's operand row
   // the model's and then the descriptor's fields that the prologue reads, in SGPRs at once (the
@@ -1271,8 +1288,20 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
   // of tile T-2, and the V^T of tile T, converted before, is visible), tile T+3 goes into the
   // stage of tile T-2, and tile T+1's V^T is converted
   auto advance = [&](int T) {
-    if (T + 2 < ntiles) vm_lgkm_wait_barrier<LPT>();
-    else vm_lgkm_wait_barrier<0>();
+    if constexpr (kWaveTimes) {
+      const long long ta = __builtin_amdgcn_s_memtime();
+      if (T + 2 < ntiles) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      const long long tb = __builtin_amdgcn_s_memtime();
+      asm volatile("s_barrier" ::: "memory");
+      wt[4] += tb - ta;
+      wt[5] += __builtin_amdgcn_s_memtime() - tb;
+      wt[7] += 1;
+    } else if (T + 2 < ntiles) {
+      vm_lgkm_wait_barrier<LPT>();
+    } else {
+      vm_lgkm_wait_barrier<0>();
+    }
     if (T + 3 < ntiles) issue(T + 3);
     if (!v16 && T + 1 < ntiles) convert_v(T + 1);
   };
@@ -1339,6 +1368,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
+  if constexpr (kWaveTimes) {
+    wt[1] = wall_clock64();
+    wt[6] = __builtin_amdgcn_s_memtime();
+  }
   // s0 holds the exponent arguments of even sub-tiles, s1 of odd ones
   f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
   if (wave_active) {
@@ -1384,6 +1417,10 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     }
   }
 
+  if constexpr (kWaveTimes) {
+    wt[2] = wall_clock64();
+    wt[6] = __builtin_amdgcn_s_memtime() - wt[6];
+  }
   // back to units of v
   if (!vraw) {
 #pragma unroll
@@ -1394,6 +1431,16 @@ __global__ __launch_bounds__(512) void k_ctx_attn_wide(Dev dev, const StepReq *_
     if (wave_active && row_ok) {
       const size_t prow = ((size_t)h * R.splits + sp) * R.rows_b + q_row;
       store_partial<DB>(slot, dev.sl, layer & 1, prow, M, ltot, hh, oacc);
+    }
+    if constexpr (kWaveTimes) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wt[3] = wall_clock64();
+      if (lane == 0 && wave_active && s == g_wave_times_sel[0] && layer == g_wave_times_sel[1] &&
+          blockIdx.x < kWaveTimesWgs) {
+        long long *o = g_wave_times + ((size_t)blockIdx.x * 8 + w) * kWaveTimesFields;
+#pragma unroll
+        for (int f = 0; f < kWaveTimesFields; ++f) o[f] = wt[f];
+      }
     }
   } else {
     if (row_ok) wide_store_layer<D>(dev, R, slot, layer, j_row, hq_row, hh, ltot, oacc, true);
@@ -3147,6 +3194,17 @@ hipError_t launch_init_slots(const Dev &dev, const int32_t *slots, int n, hipStr
   for (int i = 0; i < n; ++i) gs.slot[i] = slots[i];
   hipLaunchKernelGGL(k_init_slot, dim3(n), dim3(64), 0, st, dev, gs, n);
   return hipGetLastError();
+}
+
+
+hipError_t wave_times_select(int level, int layer) {
+  const int sel[2] = {level, layer};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_wave_times_sel), sel, sizeof sel, 0, hipMemcpyHostToDevice);
+}
+
+hipError_t wave_times_read(long long *host, size_t count) {
+  if (!kWaveTimes) return hipErrorNotSupported;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_wave_times), count * sizeof(long long), 0, hipMemcpyDeviceToHost);
 }
 
 }  // namespace gr

@@ -23,6 +23,8 @@ GR_STUB(launch_finish_layer, const Dev &, const StepReq *, int, int, int, hipStr
 GR_STUB(launch_ctx_attn_first_level, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_ctx_attn_layered, const Dev &, const StepReq *, int, int, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_sum_hparts, const Dev &, const StepReq *, int, hipStream_t, LaunchEv)
+GR_STUB(wave_times_select, int, int)
+GR_STUB(wave_times_read, long long *, size_t)
 GR_STUB(launch_finish_first_level, const Dev &, const StepReq *, int, hipStream_t, LaunchEv)
 GR_STUB(launch_logits, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)
 GR_STUB(launch_lsm, const Dev &, const StepReq *, int, int, hipStream_t, LaunchEv)

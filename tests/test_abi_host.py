@@ -30,6 +30,25 @@ def test_library_exports_every_declared_symbol():
     assert sorted(G.EXPORTS) == decl
 
 
+def test_wave_timeline_build_exports_the_same_symbols():
+    # the measurement build (context-attention wave timeline compiled in) keeps the whole ABI
+    path = os.path.join(os.path.dirname(G.__file__), "libgr_beam_timed.so")
+    if not os.path.exists(path):
+        pytest.skip("libgr_beam_timed.so not built")
+    T = C.CDLL(path)
+    for name in _declared():
+        assert hasattr(T, name), name
+
+
+def test_product_library_records_no_wave_timeline():
+    L = sib.lib()
+    buf = np.zeros(1024 * 8 * 8, dtype=np.int64)
+    assert L.gr_wave_times_read(buf.ctypes.data_as(C.POINTER(C.c_int64)), 5) == G.GR_E_INVALID_ARG
+    assert L.gr_wave_times_select(-2, 0) == G.GR_E_INVALID_ARG
+    # the product library compiles no recorder: refused before any device call
+    assert L.gr_wave_times_read(buf.ctypes.data_as(C.POINTER(C.c_int64)), buf.size) == G.GR_E_UNSUPPORTED
+
+
 def _desc(L=1, Hq=4, Hkv=2, d=64, lv=3, V=16, dtype=G.GR_DTYPE_F32, norm=G.GR_NORM_VALID):
     return G.gr_model_desc(L, Hq, Hkv, d, lv, V, dtype, norm, FAKE, FAKE, FAKE, FAKE)
 
