@@ -868,6 +868,7 @@ def main():
                     help="only the wave timeline of one headline context-attention launch (a child process "
                          "with the wave-timeline build; prints its JSON)")
     ap.add_argument("--wave-times-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-wave-times", action="store_true", help="skip the wave timeline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -885,6 +886,8 @@ def main():
     # before this process touches the GPU: the probe runs as a child process
     ceilings = None if (args.no_rate_probe or args.decode_only or args.chain_only or args.graph_only
                         or args.copy_probe or args.gpus != 1) else rate_probe_leg()
+    timeline = None if (args.no_wave_times or args.decode_only or args.chain_only or args.graph_only
+                        or args.copy_probe or args.gpus != 1 or args.config is not None) else wave_times_leg()
     if args.copy_probe:
         import torch
         n = args.copy_probe << 20
@@ -953,6 +956,8 @@ def main():
             "GBs": round(ceilings["hbm_read_164MiB_TBs"] * 1e3, 1),
             "frac": round(lv0["achieved_GBs"] / (ceilings["hbm_read_164MiB_TBs"] * 1e3), 4),
             "note": "the rate probe's read pass over 164 MiB (one layer's K and V) on this box; context only"}
+    if timeline is not None:
+        out["wave_times"] = timeline
     if not args.decode_only:
         # labelled variant, not the headline: where every layer's query is an input (this model
         # stand-in), the first level runs all layers in one launch and wide levels several
