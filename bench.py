@@ -834,12 +834,13 @@ def wave_times_child(cfg, level: int = 1, layer: int = 13, decodes: int = 3):
     }
 
 
-def wave_times_leg(timeout: int = 300):
-    """The wave timeline of one headline context-attention launch, from a child process that
-    loads the wave-timeline build of the library."""
+def wave_times_leg(level: int = 1, timeout: int = 300):
+    """The wave timeline of one headline context-attention launch (layer 13 of the given decode
+    level), from a child process that loads the wave-timeline build of the library."""
     import subprocess
     env = dict(os.environ, GR_BEAM_LIB_VARIANT="timed")
-    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--wave-times-child"], env=env,
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--wave-times-child", "--wave-level",
+                          str(level)], env=env,
                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=timeout)
     if res.returncode != 0:
         raise RuntimeError(f"wave timeline failed ({res.returncode}): {res.stderr.strip()[-2000:]}")
@@ -869,16 +870,18 @@ def main():
                          "with the wave-timeline build; prints its JSON)")
     ap.add_argument("--wave-times-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--no-wave-times", action="store_true", help="skip the wave timeline")
+    ap.add_argument("--wave-level", type=int, default=1, help="decode level of the recorded launch (default 1)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.wave_times_child:
         import synth
         from synth.configs import HEADLINE
-        print(json.dumps(wave_times_child(synth.get_config(args.config or HEADLINE))), flush=True)
+        print(json.dumps(wave_times_child(synth.get_config(args.config or HEADLINE), level=args.wave_level)),
+              flush=True)
         return
     if args.wave_times:
-        print(json.dumps({"wave_times": wave_times_leg()}), flush=True)
+        print(json.dumps({"wave_times": wave_times_leg(args.wave_level)}), flush=True)
         return
     if args.rate_probe:
         print(json.dumps({"rate_probe": rate_probe_leg()}), flush=True)
