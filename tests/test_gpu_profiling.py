@@ -36,3 +36,29 @@ def test_profiling_stride_times_every_kth_layer():
         assert np.array_equal(ca, cb) and np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
     plain.close()
     prof.close()
+
+
+def test_wave_timeline_build_records_every_wave_in_order():
+    # bench.py --wave-times: a child process with the wave-timeline build records one headline
+    # launch (level 1, layer 13); every wave's stamps must be present and ordered
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if not os.path.exists(os.path.join(root, "semantic_id_beam_amd", "libgr_beam_timed.so")):
+        pytest.fail("libgr_beam_timed.so is missing: build the package first")
+    print("wave timeline: bench.py --wave-times (headline, level 1, layer 13)", flush=True)
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--wave-times"], cwd=root,
+                         stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=110)
+    assert res.returncode == 0, res.stderr[-2000:]
+    wt = json.loads(res.stdout.strip().splitlines()[-1])["wave_times"]
+    assert wt["workgroups"] == 256 and wt["waves"] == 2048  # 8 requests x 8 kv heads x 2 splits x 2 row blocks
+    assert 0 < wt["prologue_us"]["median"] <= wt["prologue_us"]["max"]
+    assert 0 < wt["loop_us"]["min"] <= wt["loop_us"]["median"] <= wt["loop_us"]["max"]
+    assert 0 < wt["epilogue_us"]["median"] <= wt["epilogue_us"]["max"]
+    assert wt["span_us"] >= wt["loop_us"]["max"]
+    assert len(wt["xcd_median_end_us"]) == 8
+    assert 0 < wt["loop_copy_wait_frac"] < 1 and 0 < wt["loop_barrier_frac"] < 1
+    assert wt["loop_copy_wait_frac"] + wt["loop_barrier_frac"] < 1
+    assert wt["barriers_per_wave"] >= 30  # about one per 64-token tile of a 2,500-token range
